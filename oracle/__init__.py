@@ -1,0 +1,212 @@
+"""ctypes wrapper of the plain C reference of CSA2 sparse attention.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It shares no code with the GPU
+library (``sparse_attention_shared_amd``) and neither imports the other; both
+take their inputs from ``synth``.
+
+Every function here marshals numpy arrays into ``csa2_oracle.c``; all of the
+arithmetic is in that file, in double precision.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "csa2_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FULL, REINDEX, REUSE = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                               "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.orc_fp4_pack.argtypes = [P, i64, i32, P, P]
+        L.orc_fp4_unpack.argtypes = [P, P, i64, i32, P]
+        L.orc_scores.argtypes = [P, P, i64, P]
+        L.orc_scores.restype = None
+        L.orc_block_scores.argtypes = [P, i64, i32, P]
+        L.orc_block_scores.restype = None
+        L.orc_topk.argtypes = [P, P, i64, i32, P]
+        L.orc_topk.restype = i32
+        L.orc_attention.argtypes = [P, P, P, i64, dbl, P]
+        L.orc_attention.restype = None
+        L.orc_layer.argtypes = [i32, P, P, i32, i32, i64, P, P, P, P, P, P, P, P,
+                                i32, i32, i32, i32, i32, i32, P, P, dbl, P]
+        L.orc_attend.argtypes = [i32, P, P, i32, i64, P, P, P, P, P, i32, P, P,
+                                 i32, i32, i32, dbl, P]
+        L.orc_stack.argtypes = [i32, P, i32, P, i32, i64, P, P, P, P, P, P, P, P,
+                                i32, i32, i32, i32, i32, i32, dbl, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def fp4_pack(x_bf16: np.ndarray):
+    """[..., dim] bf16 bits -> (codes [..., dim/2] u8, scales [..., dim/32] u8)."""
+    x = _c(x_bf16, np.uint16)
+    dim = x.shape[-1]
+    rows = x.size // dim
+    codes = np.empty(x.shape[:-1] + (dim // 2,), np.uint8)
+    scales = np.empty(x.shape[:-1] + (dim // 32,), np.uint8)
+    rc = lib().orc_fp4_pack(_p(x), rows, dim, _p(codes), _p(scales))
+    if rc:
+        raise ValueError("orc_fp4_pack rc=%d" % rc)
+    return codes, scales
+
+
+def fp4_unpack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    s = _c(scales, np.uint8)
+    dim = c.shape[-1] * 2
+    rows = c.size // c.shape[-1]
+    out = np.empty(c.shape[:-1] + (dim,), np.float64)
+    rc = lib().orc_fp4_unpack(_p(c), _p(s), rows, dim, _p(out))
+    if rc:
+        raise ValueError("orc_fp4_unpack rc=%d" % rc)
+    return out
+
+
+def scores(q_idx: np.ndarray, k_idx: np.ndarray) -> np.ndarray:
+    q = _c(q_idx, np.uint16)
+    k = _c(k_idx, np.uint16)
+    n = k.shape[0]
+    s = np.empty(n, np.float32)
+    lib().orc_scores(_p(q), _p(k), n, _p(s))
+    return s
+
+
+def block_scores(s: np.ndarray, block: int) -> np.ndarray:
+    s = _c(s, np.float32)
+    out = np.empty((s.size + block - 1) // block, np.float32)
+    lib().orc_block_scores(_p(s), s.size, block, _p(out))
+    return out
+
+
+def topk(s: np.ndarray, k: int, ids: np.ndarray | None = None) -> np.ndarray:
+    s = _c(s, np.float32)
+    idp = None if ids is None else _c(ids, np.int32)
+    out = np.empty(k, np.int32)
+    lib().orc_topk(_p(s), _p(idp), s.size, k, _p(out))
+    return out
+
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    q = _c(q, np.uint16)
+    K = _c(K, np.float64)
+    V = _c(V, np.float64)
+    out = np.empty((16, 128), np.float64)
+    lib().orc_attention(_p(q), _p(K), _p(V), K.shape[0], scale, _p(out))
+    return out
+
+
+class Cache:
+    """The global cache of every sequence as the oracle reads it.
+
+    For FP4 the oracle quantises the bf16 rows with its own packer.
+    """
+
+    def __init__(self, kv_bf16: np.ndarray, k_idx: np.ndarray, fp4: bool):
+        self.t_cap = kv_bf16.shape[1]
+        self.fp4 = bool(fp4)
+        self.k_idx = _c(k_idx, np.uint16)
+        if self.fp4:
+            self.kv = None
+            self.codes, self.scales = fp4_pack(kv_bf16)
+        else:
+            self.kv = _c(kv_bf16, np.uint16)
+            self.codes = self.scales = None
+
+    def args(self):
+        return (int(self.fp4), self.t_cap, _p(self.kv), _p(self.codes), _p(self.scales))
+
+
+def layer(cache: Cache, q_pos, q_seq, mode, q, q_idx, lk, lv, window, lo, k,
+          pool=0, block=1, pool_io=None, sel_io=None, scale=128 ** -0.5):
+    """One layer for nq queries; returns (out [nq][16][128] f64, sel, pool)."""
+    q_pos = _c(q_pos, np.int32)
+    q_seq = _c(q_seq, np.int32)
+    nq = q_pos.size
+    q = _c(q, np.uint16)
+    q_idx = _c(q_idx, np.uint16)
+    lk = _c(lk, np.uint16)
+    lv = _c(lv, np.uint16)
+    cap = lk.shape[-2]
+    pool_io = (np.full((nq, max(pool, 0)), -1, np.int32) if pool_io is None
+               else _c(pool_io, np.int32).copy())
+    sel_io = np.full((nq, k), -1, np.int32) if sel_io is None else _c(sel_io, np.int32).copy()
+    out = np.empty((nq, 16, 128), np.float64)
+    rc = lib().orc_layer(nq, _p(q_pos), _p(q_seq), mode, *cache.args(), _p(cache.k_idx),
+                         _p(q), _p(q_idx), _p(lk), _p(lv), cap, window, lo, k, pool, block,
+                         _p(pool_io), _p(sel_io), scale, _p(out))
+    if rc:
+        raise ValueError("orc_layer rc=%d" % rc)
+    return out, sel_io, pool_io
+
+
+def attend(cache: Cache, q_pos, q_seq, q, sel, lk, lv, window, lo, scale=128 ** -0.5):
+    q_pos = _c(q_pos, np.int32)
+    q_seq = _c(q_seq, np.int32)
+    nq = q_pos.size
+    q = _c(q, np.uint16)
+    sel = _c(sel, np.int32)
+    lk = _c(lk, np.uint16)
+    lv = _c(lv, np.uint16)
+    out = np.empty((nq, 16, 128), np.float64)
+    rc = lib().orc_attend(nq, _p(q_pos), _p(q_seq), *cache.args(), _p(q), _p(sel), sel.shape[-1],
+                          _p(lk), _p(lv), lk.shape[-2], window, lo, scale, _p(out))
+    if rc:
+        raise ValueError("orc_attend rc=%d" % rc)
+    return out
+
+
+def stack(cache: Cache, modes, q_pos, q, q_idx, lk, lv, window, lo, k, pool, block=1,
+          scale=128 ** -0.5):
+    """Decoder stack, one query per sequence; returns (out, sel [L][S][k], pool)."""
+    modes = _c(modes, np.int32)
+    q_pos = _c(q_pos, np.int32)
+    L = modes.size
+    S = q_pos.size
+    q = _c(q, np.uint16)
+    q_idx = _c(q_idx, np.uint16)
+    lk = _c(lk, np.uint16)
+    lv = _c(lv, np.uint16)
+    sel = np.full((L, S, k), -1, np.int32)
+    pool_out = np.full((S, max(pool, 0)), -1, np.int32)
+    out = np.empty((L, S, 16, 128), np.float64)
+    rc = lib().orc_stack(L, _p(modes), S, _p(q_pos), *cache.args(), _p(cache.k_idx),
+                         _p(q), _p(q_idx), _p(lk), _p(lv), lk.shape[-2], window, lo, k, pool,
+                         block, scale, _p(sel), _p(pool_out), _p(out))
+    if rc:
+        raise ValueError("orc_stack rc=%d" % rc)
+    return out, sel, pool_out
