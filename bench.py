@@ -1,0 +1,226 @@
+"""CSA2 decode benchmark on one MI355X.
+
+Workload: a 20-layer decoder stack sharing one FP4 global KV cache; batch 4,
+context 131072 tokens per sequence, 16 query heads over one KV head
+(head_dim 128); layer 0 Full builds an 8192-position candidate pool and keeps
+top-2048, then [Reindex, Reuse, Reuse, Reuse] repeats; every layer attends to
+its 2048 selected entries plus a 128-position local window.
+
+One step = one decode token for every sequence through all 20 layers (index
+scoring, top-k, gather + FP4 dequant, attention), launched through the C ABI
+(csa2_stack_run).  Inputs are resident in HBM before the timed region; the
+timed steps rotate over several copies of the cache so that consecutive steps
+do not find it in the 256 MB Infinity Cache.
+
+Prints one JSON line (see the repository's design doc for the fields).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA2 decode tokens/s + achieved HBM GB/s (% peak) at 128k ctx, FP4 shared KV"
+PEAK_HBM_GBPS = 8000.0
+SCAN_KERNEL_SRC = os.path.join(ROOT, "sparse_attention_shared_amd", "csrc", "k_score.hip")
+
+
+def algorithmic_bytes(schedule, B, T, k, P, W):
+    """Bytes the method must move per step (selected rows, the scans the
+    indexer needs, window, queries, outputs and index lists); the dense
+    attention it avoids is not counted."""
+    row = 136            # FP4 K+V codes (128 B) + E8M0 scales (8 B)
+    kidx = 128           # bf16 indexer key
+    win = W * 2 * 128 * 2
+    qio = 16 * 128 * 2 * 2  # main Q in + output
+    total = 0
+    for m in schedule:
+        b = k * row + win + qio + k * 4          # gather, window, q/out, read sel
+        if m == 0:
+            b += T * kidx + 64 * 2 + (P + k) * 4  # full scan, q_I, write pool + sel
+        elif m == 1:
+            b += P * kidx + 64 * 2 + (P + k) * 4  # pool rescore, q_I, read pool, write sel
+        total += b
+    return total * B
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(launch_units):
+    """HBM bytes per launch of the scan kernel from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", "score_scan_config3_counters.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_src_sha256_16") != src_hash(SCAN_KERNEL_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle (plain C, one thread) on a bounded sample of the same
+    workload: whole 20-layer stacks of single sequences until the budget."""
+    import numpy as np
+    import oracle
+    import synth
+    sp = synth.config(3)
+    sp1 = synth.Spec(**{**sp.__dict__, "n_seq": 1, "q_pos": [sp.q_pos[0]], "q_seq": [0]})
+    x = synth.make_inputs(sp1)
+    c = oracle.Cache(x.kv, x.k_idx, fp4=True)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.stack(c, sp1.schedule, x.q_pos, x.q, x.q_idx, x.local_k, x.local_v, sp1.window, 0,
+                     sp1.k, sp1.pool)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 64:
+            break
+    return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d single-sequence 20-layer decode steps of the same workload "
+                      "(T=131072, FP4, pool 8192, k=2048, W=128) in %.1f s, one thread" % (n, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", choices=["repeat", "page"], default="repeat")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(a sharding plan is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import sparse_attention_shared_amd as csa2
+
+    torch.cuda.set_device(0)
+    csa2.device_check()
+    sp = synth.config(3)
+    if args.schedule == "page":
+        sp = synth.Spec(**{**sp.__dict__, "schedule": synth.page_schedule_20()})
+    B, T, L = sp.n_seq, sp.t_cap, sp.n_layers
+    print("generating inputs ...", file=sys.stderr, flush=True)
+    x = synth.make_inputs(sp)
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    kv = d16(x.kv)
+    k_idx0 = d16(x.k_idx)
+    codes0, scales0 = csa2.pack_fp4(kv)
+    del kv
+    caches = []
+    for i in range(args.copies):
+        if i == 0:
+            codes, scales, k_idx = codes0, scales0, k_idx0
+        else:
+            codes, scales, k_idx = codes0.clone(), scales0.clone(), k_idx0.clone()
+        caches.append(csa2.Cache(codes, k_idx, scales))
+    q_pos = torch.from_numpy(x.q_pos).cuda()
+    q = [d16(x.q[l]) for l in range(L)]
+    q_idx = [d16(x.q_idx[l]) if sp.schedule[l] != synth.REUSE else None for l in range(L)]
+    local = [csa2.Local(d16(x.local_k[l]), d16(x.local_v[l]), sp.window) for l in range(L)]
+    out = [torch.empty((B, 16, 128), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    ws = torch.empty(1, dtype=torch.uint8, device="cuda")
+    # size the workspace once
+    _, _, _ = csa2.stack_run(caches[0], sp.schedule, q_pos, q, q_idx, local, sp.k, sp.pool,
+                             want_sel=False, out=out)
+    torch.cuda.synchronize()
+    from sparse_attention_shared_amd._lib import _StackArgs, stack_workspace
+    need = stack_workspace(_StackArgs(caches[0], sp.schedule, q_pos, q, q_idx, local, out, sp.k,
+                                      sp.pool, 1, 128 ** -0.5, None, None))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    n_ev = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_ev)]
+    for a, b in ev:  # create the underlying HIP events
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+
+    def step(i, events=None):
+        csa2.stack_run(caches[i % len(caches)], sp.schedule, q_pos, q, q_idx, local, sp.k,
+                       sp.pool, want_sel=False, ws=ws, out=out, scan_events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_start.elapsed_time(t_end) / args.steps
+    scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+
+    step_bytes = algorithmic_bytes(sp.schedule, B, T, sp.k, sp.pool, sp.window)
+    scan_bytes = B * T * 128
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": B / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "20-layer CSA2 decode stack over one shared FP4 (E2M1 + E8M0/32) global "
+                        "KV cache: batch 4, context 131072, 16 q heads / 1 KV head, head_dim "
+                        "128, indexer dim 64, Full pool 8192 then [Reindex, Reuse x3]*, "
+                        "top-k 2048, SWA 128",
+            "batch": B, "context": T, "layers": L,
+            "schedule": "".join("FIU"[m] for m in sp.schedule),
+            "k": sp.k, "pool": sp.pool, "window": sp.window,
+            "cache_copies_rotated": args.copies,
+        },
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
+        "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "wall_s_timed_region": wall,
+        "roofline": {
+            "kernel": "k_score_dense<1> (layer-0 Full indexer scan)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic_from_profile(B * T),
+            "launch_ms": scan_ms,
+            "algorithmic_bytes_per_launch": scan_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("timing the oracle on the host ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,225 @@
+/*
+ * csa2.h -- C ABI of an MI355X (gfx950) library for CSA2 sparse attention of
+ * decoder queries over one global KV cache shared by every decoder layer, as
+ * used by a Causal Encoder-Decoder (YOCO-style) model.
+ *
+ * Source of the operations: "CED: Continuing Context with a Causal Encoder and
+ * Decoder" (ai-systems-engineering.com):
+ *   - "One Token Sequence and Causal Access", Fig. 2: a query at position t
+ *     may read positions <= t (its own included), never later ones;
+ *   - "Shared Global KV and Per-Layer Local KV", Fig. 3: the global main KV
+ *     and indexer keys are produced once and read by every decoder layer;
+ *     Main Q, indexer Q and the local KV are per layer;
+ *   - "Selecting Positions and Reading Values with Attention", Fig. 4: the
+ *     indexer (indexer Q against indexer K) picks top-k positions; their
+ *     global entries are gathered, joined with the local sliding window and
+ *     attended by Main Q in one softmax; a position may appear in both parts;
+ *   - "What Full, Reindex, and Reuse Share", Fig. 5: per-layer modes fixed in
+ *     advance; Full scores every causal position, Reindex rescores only the
+ *     candidate pool built by the first Full layer, Reuse takes the previous
+ *     layer's selection; every layer recomputes attention with its own Main Q
+ *     and local KV.
+ * FP4 main cache: E2M1 elements ("DeepSeek-V4.1 Flash Pushes KV Cache
+ * Compression for Agent Workloads", draft article), here with one E8M0
+ * (power-of-two) scale per 32 elements.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns and
+ *     allocates every buffer (inputs, outputs and workspace); the library
+ *     allocates nothing except inside a stack plan object.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns; nothing synchronises and no device
+ *     data is read on the host.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is enqueued.  Kernel faults surface at the caller's
+ *     next synchronisation.  No C++ exception crosses this ABI.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Shapes: 16 query heads share one KV head (MQA); head_dim 128 for K and
+ *     V; indexer vectors have 64 elements.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_VERSION 100
+#define CSA2_HEADS 16
+#define CSA2_HEAD_DIM 128
+#define CSA2_INDEX_DIM 64
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_ERR_INVALID_ARG = 1, /* null pointer, negative size, unknown enum, misaligned pointer */
+    CSA2_ERR_SHAPE = 2,       /* sizes that do not fit together */
+    CSA2_ERR_SCHEDULE = 3,    /* a layer schedule the modes do not allow */
+    CSA2_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the size query returned */
+    CSA2_ERR_UNSUPPORTED = 5, /* current device is not gfx950 */
+    CSA2_ERR_NO_DEVICE = 6,   /* no HIP device visible */
+    CSA2_ERR_HIP = 7          /* the HIP runtime refused a launch */
+} csa2_status;
+
+typedef enum { CSA2_MODE_FULL = 0, CSA2_MODE_REINDEX = 1, CSA2_MODE_REUSE = 2 } csa2_mode;
+
+typedef enum { CSA2_KV_BF16 = 0, CSA2_KV_FP4 = 1 } csa2_kv_format;
+
+/* The global cache shared by all decoder layers (Fig. 3).
+ *   BF16: data = uint16 [n_seq][t_cap][256]; channels 0..127 are K, 128..255 V.
+ *   FP4:  data = uint8 codes [n_seq][t_cap][128]: bytes 0..63 hold K, 64..127
+ *         hold V, two elements per byte, low nibble = even channel;
+ *         scales = uint8 E8M0 [n_seq][t_cap][8]: bytes 0..3 scale the four
+ *         32-channel blocks of K, bytes 4..7 those of V.
+ *         This is exactly what csa2_pack_fp4 writes for rows of 256 (K | V).
+ *   k_idx = indexer keys, bf16 [n_seq][t_cap][64].
+ * data, scales and k_idx must be 16-byte aligned. */
+typedef struct {
+    int32_t format;           /* csa2_kv_format */
+    int32_t n_seq;
+    int64_t t_cap;            /* rows per sequence */
+    const void *data;
+    const uint8_t *scales;    /* FP4 only; NULL for BF16 */
+    const uint16_t *k_idx;
+} csa2_cache;
+
+/* A layer's local (sliding-window) KV, a ring of `cap` slots per sequence:
+ * position p is held in slot p % cap.  k, v: bf16 [n_seq][cap][128].
+ * The window of a query at t is positions [max(t - window + 1, lo, 0), t]
+ * (Fig. 4: the recent positions including t).  0 <= window <= cap. */
+typedef struct {
+    const uint16_t *k;
+    const uint16_t *v;
+    int32_t cap;
+    int32_t window;
+    int32_t lo;
+} csa2_local;
+
+int csa2_version(void);
+const char *csa2_status_str(csa2_status s);
+
+/* CSA2_OK when a HIP device is current and it is gfx950. */
+csa2_status csa2_device_check(void);
+
+/* ------------------------------------------------------------------ FP4 */
+
+/* Quantise rows of bf16 to FP4 (E2M1 + E8M0 per 32 elements).
+ * x: bf16 [rows][dim], dim % 32 == 0; codes: [rows][dim/2] (low nibble =
+ * even channel); scales: [rows][dim/32].  For each 32-element block with
+ * largest magnitude a: E = clamp(floor(log2 a) - 2, -127, 127) (E = -127
+ * when a = 0), scale byte = E + 127, and each element x becomes the E2M1
+ * value nearest to x * 2^-E (ties to the even code, magnitudes above 6 give
+ * 6, the sign bit is kept, so -0 gives code 8).  x and codes 16-byte aligned.
+ * Also used for the decode append of one row per sequence. */
+csa2_status csa2_pack_fp4(const uint16_t *x, int64_t rows, int32_t dim, uint8_t *codes,
+                          uint8_t *scales, void *stream);
+
+/* Exact dequantisation: out[i] = (-1)^s * e2m1(c) * 2^(byte - 127) as fp32
+ * (exact for scale bytes 0..253).  out: float [rows][dim], 16-byte aligned. */
+csa2_status csa2_unpack_fp4(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                            int32_t dim, float *out, void *stream);
+
+/* -------------------------------------------------------------- indexer */
+
+/* Indexer scores (Fig. 4: indexer Q of the layer against indexer K of the
+ * global cache), a plain 64-element dot product accumulated in fp32.
+ *   q_idx: bf16 [nq][64]; q_pos, q_seq: int32 [nq] (position and sequence of
+ *   each query; q_seq may be NULL, then query i reads sequence i).  A query
+ *   whose sequence id is out of range reads nothing (all scores -inf).
+ *   nq <= 65535.
+ * Dense (cand == NULL): scores[i][b] for b < ceil(t_cap / block): with block
+ *   1 the score of position b; with block > 1 the max of the scores of the
+ *   positions of block b (positions [b*block, b*block + block)).  Positions
+ *   after q_pos[i] are masked (Fig. 2): their score is -inf and a block with
+ *   none left is -inf.
+ * Candidates (cand != NULL, block must be 1): scores[i][c] = score of
+ *   position cand[i][c] (cand: int32 [nq][n_cand]); -inf for slots < 0 or
+ *   after q_pos[i].
+ * scores: float with row stride ld_scores (elements). */
+csa2_status csa2_index_score(const csa2_cache *cache, const uint16_t *q_idx, const int32_t *q_pos,
+                             const int32_t *q_seq, int32_t nq, const int32_t *cand, int64_t n_cand,
+                             int32_t block, float *scores, int64_t ld_scores, void *stream);
+
+/* Top-k selection (Fig. 4) of each row of scores: float [nq][n] with row
+ * stride ld.  Order: higher score first, equal scores by lower position
+ * (-0 equals +0).  Entries equal to -inf, and slots whose id is < 0, are
+ * never chosen.  ids (nullable, int32 [nq][n]) maps slot c to its position;
+ * its non-negative entries must be ascending within a row (every pool this
+ * library writes is).  out: int32 [nq][k], the chosen positions ascending,
+ * padded with -1 when fewer than k can be chosen.  When out2 != NULL the
+ * first k2 >= k under the same order are also written to out2 [nq][k2]
+ * (the Full layer's candidate pool, Fig. 5).  ws: at least the size returned
+ * by csa2_topk_workspace (may be 0). */
+csa2_status csa2_topk(const float *scores, int32_t nq, int64_t n, int64_t ld, const int32_t *ids,
+                      int32_t k, int32_t *out, int32_t k2, int32_t *out2, void *ws,
+                      size_t ws_bytes, void *stream);
+csa2_status csa2_topk_workspace(int32_t nq, int64_t n, int32_t k, int32_t k2, size_t *bytes);
+
+/* Positions of chosen blocks: tokens[i][c*block + r] = blocks[i][c]*block + r
+ * when blocks[i][c] >= 0 and that position is <= q_pos[i], else -1.
+ * blocks: int32 [nq][nb] ascending (as csa2_topk writes them). */
+csa2_status csa2_expand_blocks(const int32_t *blocks, int32_t nq, int32_t nb, int32_t block,
+                               const int32_t *q_pos, int32_t *tokens, void *stream);
+
+/* ------------------------------------------------------------ attention */
+
+/* Sparse attention (Fig. 4): for each query i and head h, one softmax over
+ * the global entries listed in sel[i] (int32 [nq][k]; slots < 0 or after
+ * q_pos[i] are skipped) followed by the local window of q_pos[i]; logits are
+ * sm_scale * (q . K); entries are not de-duplicated.  FP4 entries are
+ * dequantised exactly.  q: bf16 [nq][16][128]; out: bf16 [nq][16][128]
+ * (fp32 accumulation, rounded to nearest even).  A query with no entry at
+ * all gets zeros.  q_seq may be NULL (query i reads sequence i).  nq <= 65535.
+ * ws: at least csa2_sparse_attn_workspace bytes. */
+csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, const int32_t *q_pos,
+                             const int32_t *q_seq, int32_t nq, const int32_t *sel, int32_t k,
+                             const csa2_local *local, float sm_scale, uint16_t *out, void *ws,
+                             size_t ws_bytes, void *stream);
+csa2_status csa2_sparse_attn_workspace(int32_t nq, int32_t k, int32_t window, size_t *bytes);
+
+/* ------------------------------------------------------------ layer stack */
+
+/* A decoder stack over one shared global cache with one decode query per
+ * sequence (query b belongs to sequence b), modes fixed per layer (Fig. 5):
+ *   Full    dense indexer scores, top-k selection and, with pool > 0, the
+ *           candidate pool of the top `pool` positions (layer 0 is Full; a
+ *           later Full layer builds a new pool).  With
+ *           block > 1 the pool is every position of the top pool/block
+ *           blocks by block score (max of its tokenwise scores) and the top-k
+ *           is chosen tokenwise inside it.
+ *   Reindex: its own indexer query rescores the pool; top-k inside it.
+ *   Reuse:  the previous layer's selection, unchanged.
+ * Every layer then runs csa2_sparse_attn with its own q and local KV.
+ * All per-layer arrays are HOST arrays of n_layers device pointers. */
+typedef struct {
+    int32_t n_layers;
+    const int32_t *modes;              /* host [n_layers], csa2_mode */
+    const csa2_cache *cache;           /* host pointer */
+    const int32_t *q_pos;              /* device int32 [n_seq] */
+    int32_t k;                         /* selected global entries per layer */
+    int32_t pool;                      /* pool size in positions (0: no Reindex layers) */
+    int32_t block;                     /* 1: tokenwise Full scoring; >1 blockwise */
+    float sm_scale;
+    const uint16_t *const *q;          /* [l] -> bf16 [n_seq][16][128] */
+    const uint16_t *const *q_idx;      /* [l] -> bf16 [n_seq][64]; unused (may be NULL) for Reuse */
+    const csa2_local *local;           /* host [n_layers] */
+    uint16_t *const *out;              /* [l] -> bf16 [n_seq][16][128] */
+    int32_t *const *sel_out;           /* NULL, or [l] -> int32 [n_seq][k] (entries may be NULL) */
+    int32_t *pool_out;                 /* NULL, or int32 [n_seq][pool] */
+    void *scan_events[2];              /* optional timing hook: two hipEvent_t the caller
+                                          created, recorded on `stream` right before and
+                                          after layer 0's indexer scan kernel; NULL skips */
+} csa2_stack_desc;
+
+csa2_status csa2_stack_workspace(const csa2_stack_desc *desc, size_t *bytes);
+/* Run every layer in order on `stream`.  Validates the schedule: layer 0 must
+ * be Full and Reindex needs pool > 0; k <= pool when pool > 0; with block > 1,
+ * pool > 0 and pool % block == 0. */
+csa2_status csa2_stack_run(const csa2_stack_desc *desc, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

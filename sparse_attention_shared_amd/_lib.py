@@ -1,0 +1,296 @@
+"""ctypes marshalling of the libcsa2 C ABI (include/csa2.h).
+
+Tensors are torch tensors on the current HIP device; bf16 data may be passed as
+``torch.bfloat16`` or as 16-bit integer bit patterns.  Every call enqueues on
+``torch.cuda.current_stream()`` and returns without synchronising.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libcsa2.so")
+
+FULL, REINDEX, REUSE = 0, 1, 2
+KV_BF16, KV_FP4 = 0, 1
+HEADS, HEAD_DIM, INDEX_DIM = 16, 128, 64
+
+_P = ctypes.c_void_p
+_i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class csa2_cache(ctypes.Structure):
+    _fields_ = [("format", _i32), ("n_seq", _i32), ("t_cap", _i64), ("data", _P),
+                ("scales", _P), ("k_idx", _P)]
+
+
+class csa2_local(ctypes.Structure):
+    _fields_ = [("k", _P), ("v", _P), ("cap", _i32), ("window", _i32), ("lo", _i32)]
+
+
+class csa2_stack_desc(ctypes.Structure):
+    _fields_ = [("n_layers", _i32), ("modes", ctypes.POINTER(_i32)),
+                ("cache", ctypes.POINTER(csa2_cache)), ("q_pos", _P), ("k", _i32),
+                ("pool", _i32), ("block", _i32), ("sm_scale", _f32),
+                ("q", ctypes.POINTER(_P)), ("q_idx", ctypes.POINTER(_P)),
+                ("local", ctypes.POINTER(csa2_local)), ("out", ctypes.POINTER(_P)),
+                ("sel_out", ctypes.POINTER(_P)), ("pool_out", _P), ("scan_events", _P * 2)]
+
+
+class Csa2Error(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcsa2.so (built by ``sparse_attention_shared_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError("libcsa2.so is not built (%s); run __graft_entry__.build()" % lib_path)
+        L = ctypes.CDLL(lib_path)
+        L.csa2_version.restype = ctypes.c_int
+        L.csa2_status_str.restype = ctypes.c_char_p
+        L.csa2_status_str.argtypes = [ctypes.c_int]
+        L.csa2_device_check.restype = ctypes.c_int
+        L.csa2_pack_fp4.argtypes = [_P, _i64, _i32, _P, _P, _P]
+        L.csa2_unpack_fp4.argtypes = [_P, _P, _i64, _i32, _P, _P]
+        L.csa2_index_score.argtypes = [ctypes.POINTER(csa2_cache), _P, _P, _P, _i32, _P, _i64,
+                                       _i32, _P, _i64, _P]
+        L.csa2_topk.argtypes = [_P, _i32, _i64, _i64, _P, _i32, _P, _i32, _P, _P, _sz, _P]
+        L.csa2_topk_workspace.argtypes = [_i32, _i64, _i32, _i32, ctypes.POINTER(_sz)]
+        L.csa2_expand_blocks.argtypes = [_P, _i32, _i32, _i32, _P, _P, _P]
+        L.csa2_sparse_attn.argtypes = [ctypes.POINTER(csa2_cache), _P, _P, _P, _i32, _P, _i32,
+                                       ctypes.POINTER(csa2_local), _f32, _P, _P, _sz, _P]
+        L.csa2_sparse_attn_workspace.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_sz)]
+        L.csa2_stack_workspace.argtypes = [ctypes.POINTER(csa2_stack_desc), ctypes.POINTER(_sz)]
+        L.csa2_stack_run.argtypes = [ctypes.POINTER(csa2_stack_desc), _P, _sz, _P]
+        for f in ("csa2_pack_fp4", "csa2_unpack_fp4", "csa2_index_score", "csa2_topk",
+                  "csa2_topk_workspace", "csa2_expand_blocks", "csa2_sparse_attn",
+                  "csa2_sparse_attn_workspace", "csa2_stack_workspace", "csa2_stack_run"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(name: str, st: int) -> None:
+    if st != 0:
+        raise Csa2Error("%s: %s (status %d)" % (name, lib().csa2_status_str(st).decode(), st))
+
+
+def version() -> int:
+    return lib().csa2_version()
+
+
+def device_check() -> None:
+    _check("csa2_device_check", lib().csa2_device_check())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _bits16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return t
+    raise TypeError("expected bf16 data (bfloat16 or 16-bit bit patterns), got %s" % t.dtype)
+
+
+def _i32t(t: Optional[torch.Tensor]):
+    if t is not None and t.dtype != torch.int32:
+        raise TypeError("expected int32, got %s" % t.dtype)
+    return t
+
+
+class Cache:
+    """The global cache shared by all decoder layers.
+
+    BF16: ``data`` bf16 [n_seq][t_cap][256] (K | V).  FP4: ``data`` uint8 codes
+    [n_seq][t_cap][128] and ``scales`` uint8 [n_seq][t_cap][8] as written by
+    :func:`pack_fp4` on rows of 256.  ``k_idx`` bf16 [n_seq][t_cap][64].
+    """
+
+    def __init__(self, data: torch.Tensor, k_idx: torch.Tensor,
+                 scales: Optional[torch.Tensor] = None):
+        self.fp4 = scales is not None
+        self.data, self.scales, self.k_idx = data, scales, _bits16(k_idx)
+        self.n_seq, self.t_cap = int(k_idx.shape[0]), int(k_idx.shape[1])
+        if self.fp4:
+            assert data.dtype == torch.uint8 and tuple(data.shape) == (self.n_seq, self.t_cap, 128)
+            assert scales.dtype == torch.uint8 and tuple(scales.shape) == (self.n_seq, self.t_cap, 8)
+        else:
+            _bits16(data)
+            assert tuple(data.shape) == (self.n_seq, self.t_cap, 256)
+        self.c = csa2_cache(KV_FP4 if self.fp4 else KV_BF16, self.n_seq, self.t_cap,
+                            _ptr(data), _ptr(scales) if self.fp4 else None, _ptr(self.k_idx))
+
+
+class Local:
+    """A layer's local KV ring: k, v bf16 [n_seq][cap][128]; position p in slot p % cap."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, window: int, lo: int = 0):
+        self.k, self.v = _bits16(k), _bits16(v)
+        self.cap = int(k.shape[1])
+        self.c = csa2_local(_ptr(self.k), _ptr(self.v), self.cap, int(window), int(lo))
+
+
+def pack_fp4(x: torch.Tensor):
+    """bf16 [..., dim] -> (codes uint8 [..., dim/2], scales uint8 [..., dim/32])."""
+    x = _bits16(x)
+    dim = int(x.shape[-1])
+    rows = x.numel() // dim if dim else 0
+    codes = torch.empty(tuple(x.shape[:-1]) + (dim // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(tuple(x.shape[:-1]) + (dim // 32,), dtype=torch.uint8, device=x.device)
+    _check("csa2_pack_fp4", lib().csa2_pack_fp4(_ptr(x), rows, dim, _ptr(codes), _ptr(scales),
+                                                _stream()))
+    return codes, scales
+
+
+def unpack_fp4(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    dim = int(codes.shape[-1]) * 2
+    rows = codes.numel() // (dim // 2) if dim else 0
+    out = torch.empty(tuple(codes.shape[:-1]) + (dim,), dtype=torch.float32, device=codes.device)
+    _check("csa2_unpack_fp4", lib().csa2_unpack_fp4(_ptr(codes), _ptr(scales), rows, dim,
+                                                    _ptr(out), _stream()))
+    return out
+
+
+def index_score(cache: Cache, q_idx: torch.Tensor, q_pos: torch.Tensor,
+                q_seq: Optional[torch.Tensor] = None, cand: Optional[torch.Tensor] = None,
+                block: int = 1, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    nq = int(q_pos.shape[0])
+    if cand is not None:
+        n = int(cand.shape[1])
+    else:
+        n = (cache.t_cap + block - 1) // block
+    if out is None:
+        out = torch.empty((nq, n), dtype=torch.float32, device=q_pos.device)
+    _check("csa2_index_score", lib().csa2_index_score(
+        ctypes.byref(cache.c), _ptr(_bits16(q_idx)), _ptr(_i32t(q_pos)), _ptr(_i32t(q_seq)), nq,
+        _ptr(_i32t(cand)), n if cand is not None else 0, block, _ptr(out), int(out.stride(0)),
+        _stream()))
+    return out
+
+
+def topk(scores: torch.Tensor, k: int, ids: Optional[torch.Tensor] = None, k2: int = 0):
+    """Returns (out [nq][k], out2 [nq][k2] or None); positions ascending, -1 padded."""
+    nq, n = int(scores.shape[0]), int(scores.shape[1])
+    out = torch.empty((nq, k), dtype=torch.int32, device=scores.device)
+    out2 = torch.empty((nq, k2), dtype=torch.int32, device=scores.device) if k2 else None
+    ws_n = _sz()
+    _check("csa2_topk_workspace", lib().csa2_topk_workspace(nq, n, k, k2, ctypes.byref(ws_n)))
+    ws = torch.empty(max(ws_n.value, 1), dtype=torch.uint8, device=scores.device)
+    _check("csa2_topk", lib().csa2_topk(_ptr(scores), nq, n, int(scores.stride(0)),
+                                        _ptr(_i32t(ids)), k, _ptr(out), k2, _ptr(out2), _ptr(ws),
+                                        ws_n.value, _stream()))
+    return out, out2
+
+
+def expand_blocks(blocks: torch.Tensor, block: int, q_pos: torch.Tensor) -> torch.Tensor:
+    nq, nb = int(blocks.shape[0]), int(blocks.shape[1])
+    out = torch.empty((nq, nb * block), dtype=torch.int32, device=blocks.device)
+    _check("csa2_expand_blocks", lib().csa2_expand_blocks(_ptr(_i32t(blocks)), nq, nb, block,
+                                                          _ptr(_i32t(q_pos)), _ptr(out), _stream()))
+    return out
+
+
+def sparse_attn_workspace(nq: int, k: int, window: int) -> int:
+    n = _sz()
+    _check("csa2_sparse_attn_workspace", lib().csa2_sparse_attn_workspace(nq, k, window,
+                                                                          ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, q_seq: Optional[torch.Tensor],
+                sel: torch.Tensor, local: Local, sm_scale: float = HEAD_DIM ** -0.5,
+                out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    nq = int(q_pos.shape[0])
+    k = int(sel.shape[1]) if sel is not None else 0
+    if out is None:
+        out = torch.empty((nq, HEADS, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    need = sparse_attn_workspace(nq, k, local.c.window)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check("csa2_sparse_attn", lib().csa2_sparse_attn(
+        ctypes.byref(cache.c), _ptr(_bits16(q)), _ptr(_i32t(q_pos)), _ptr(_i32t(q_seq)), nq,
+        _ptr(_i32t(sel)), k, ctypes.byref(local.c), float(sm_scale), _ptr(out), _ptr(ws),
+        ws.numel(), _stream()))
+    return out
+
+
+class _StackArgs:
+    """Keeps the ctypes arrays of one stack descriptor alive."""
+
+    def __init__(self, cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
+                 q: Sequence[torch.Tensor], q_idx: Sequence[Optional[torch.Tensor]],
+                 local: Sequence[Local], out: Sequence[torch.Tensor], k: int, pool: int,
+                 block: int, sm_scale: float, sel_out: Optional[Sequence[torch.Tensor]],
+                 pool_out: Optional[torch.Tensor], scan_events=None):
+        L = len(modes)
+        self.refs = (cache, q_pos, list(q), list(q_idx), list(local), list(out), sel_out, pool_out)
+        self.modes = (_i32 * L)(*modes)
+        self.q = (_P * L)(*[t.data_ptr() for t in q])
+        self.q_idx = (_P * L)(*[(t.data_ptr() if t is not None else None) for t in q_idx])
+        self.local = (csa2_local * L)(*[l.c for l in local])
+        self.out = (_P * L)(*[t.data_ptr() for t in out])
+        self.sel = (_P * L)(*[t.data_ptr() for t in sel_out]) if sel_out is not None else None
+        self.desc = csa2_stack_desc(
+            L, self.modes, ctypes.pointer(cache.c), _ptr(_i32t(q_pos)), k, pool, block,
+            float(sm_scale), self.q, self.q_idx, self.local, self.out,
+            self.sel if self.sel is not None else None,
+            _ptr(pool_out) if pool_out is not None else None,
+            (_P * 2)(*(scan_events or (None, None))))
+
+
+def stack_workspace(args: _StackArgs) -> int:
+    n = _sz()
+    _check("csa2_stack_workspace", lib().csa2_stack_workspace(ctypes.byref(args.desc),
+                                                              ctypes.byref(n)))
+    return n.value
+
+
+def stack_run(cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
+              q: Sequence[torch.Tensor], q_idx: Sequence[Optional[torch.Tensor]],
+              local: Sequence[Local], k: int, pool: int = 0, block: int = 1,
+              sm_scale: float = HEAD_DIM ** -0.5, want_sel: bool = True,
+              ws: Optional[torch.Tensor] = None, out: Optional[Sequence[torch.Tensor]] = None,
+              scan_events=None):
+    """Run a decoder stack (one decode query per sequence).
+
+    Returns (out list of bf16 [n_seq][16][128], sel list or None, pool or None).
+    ``scan_events``: optional pair of ``torch.cuda.Event(enable_timing=True)``
+    recorded around layer 0's indexer scan.
+    """
+    S = int(q_pos.shape[0])
+    dev = q_pos.device
+    if out is None:
+        out = [torch.empty((S, HEADS, HEAD_DIM), dtype=torch.bfloat16, device=dev) for _ in modes]
+    sel = [torch.empty((S, k), dtype=torch.int32, device=dev) for _ in modes] if want_sel else None
+    pool_out = torch.empty((S, pool), dtype=torch.int32, device=dev) if pool > 0 else None
+    ev = None
+    if scan_events is not None:
+        ev = tuple(ctypes.c_void_p(e.cuda_event) for e in scan_events)
+    args = _StackArgs(cache, modes, q_pos, q, q_idx, local, out, k, pool, block, sm_scale, sel,
+                      pool_out, ev)
+    need = stack_workspace(args)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("csa2_stack_run", lib().csa2_stack_run(ctypes.byref(args.desc), _ptr(ws), ws.numel(),
+                                                  _stream()))
+    return out, sel, pool_out

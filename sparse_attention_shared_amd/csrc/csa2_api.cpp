@@ -1,0 +1,344 @@
+// csa2_api.cpp -- the C ABI of libcsa2 (declared in include/csa2.h): argument
+// validation, workspace sizing and dispatch to the gfx950 kernels, plus the
+// layer-stack driver that applies a Full / Reindex / Reuse schedule ("CED:
+// Continuing Context with a Causal Encoder and Decoder", section "What Full,
+// Reindex, and Reuse Share", Fig. 5).
+//
+// Every entry point validates on the host before enqueuing anything, reads no
+// device memory, allocates nothing and never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <vector>
+
+#include "csa2.h"
+#include "csa2_kernels.h"
+
+using namespace csa2;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other (a memo, not state)
+
+csa2_status device_ok() {
+    int dev = -1;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return CSA2_ERR_NO_DEVICE;
+    }
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return CSA2_ERR_NO_DEVICE;
+    }
+    if (dev < kMaxDevices) {
+        const int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (v) return v == 1 ? CSA2_OK : CSA2_ERR_UNSUPPORTED;
+    }
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return CSA2_ERR_NO_DEVICE;
+    }
+    const bool ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? CSA2_OK : CSA2_ERR_UNSUPPORTED;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+csa2_status from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+csa2_status check_cache(const csa2_cache* c, bool need_kv, bool need_idx, CacheView* v) {
+    if (!c) return CSA2_ERR_INVALID_ARG;
+    if (c->format != CSA2_KV_BF16 && c->format != CSA2_KV_FP4) return CSA2_ERR_INVALID_ARG;
+    if (c->n_seq <= 0 || c->t_cap <= 0 || c->t_cap > (int64_t)INT32_MAX) return CSA2_ERR_SHAPE;
+    if (need_kv) {
+        if (!c->data || !aligned16(c->data)) return CSA2_ERR_INVALID_ARG;
+        if (c->format == CSA2_KV_FP4 && !c->scales) return CSA2_ERR_INVALID_ARG;
+    }
+    if (need_idx && (!c->k_idx || !aligned16(c->k_idx))) return CSA2_ERR_INVALID_ARG;
+    v->fp4 = c->format == CSA2_KV_FP4;
+    v->n_seq = c->n_seq;
+    v->t_cap = c->t_cap;
+    v->data = c->data;
+    v->scales = c->scales;
+    v->k_idx = c->k_idx;
+    return CSA2_OK;
+}
+
+csa2_status check_local(const csa2_local* l, LocalView* v) {
+    if (!l) return CSA2_ERR_INVALID_ARG;
+    if (l->window < 0 || l->lo < 0 || l->cap < 0) return CSA2_ERR_SHAPE;
+    if (l->window > l->cap) return CSA2_ERR_SHAPE;
+    if (l->window > 0 && (!l->k || !l->v || !aligned16(l->k) || !aligned16(l->v)))
+        return CSA2_ERR_INVALID_ARG;
+    v->k = l->k;
+    v->v = l->v;
+    v->cap = l->cap;
+    v->window = l->window;
+    v->lo = l->lo;
+    return CSA2_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace of one stack run: scores, block scores / block ids, pool scores,
+// pool, the current selection, top-k and attention scratch.
+struct StackWs {
+    size_t scores, bscores, blocks, pscores, pool, sel0, topk, attn, total;
+};
+
+StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, int32_t block,
+                        int32_t max_window) {
+    StackWs w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    const int64_t nb = block > 1 ? (t_cap + block - 1) / block : 0;
+    const int32_t nbsel = block > 1 ? pool / block : 0;
+    w.scores = take((size_t)n_seq * t_cap * sizeof(float));
+    w.bscores = take((size_t)n_seq * (nb > 0 ? nb : 1) * sizeof(float));
+    w.blocks = take((size_t)n_seq * (nbsel > 0 ? nbsel : 1) * sizeof(int32_t));
+    w.pscores = take((size_t)n_seq * (pool > 0 ? pool : 1) * sizeof(float));
+    w.pool = take((size_t)n_seq * (pool > 0 ? pool : 1) * sizeof(int32_t));
+    w.sel0 = take((size_t)n_seq * k * sizeof(int32_t));
+    size_t tk = topk_ws_bytes(n_seq, t_cap, k, pool);
+    if (block > 1) tk = std::max(tk, topk_ws_bytes(n_seq, nb, nbsel, 0));
+    if (pool > 0) tk = std::max(tk, topk_ws_bytes(n_seq, pool, k, 0));
+    w.topk = take(tk > 0 ? tk : 1);
+    w.attn = take(attn_ws_bytes(n_seq, k, max_window));
+    w.total = off;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa2_version(void) { return CSA2_VERSION; }
+
+const char* csa2_status_str(csa2_status s) {
+    switch (s) {
+        case CSA2_OK: return "ok";
+        case CSA2_ERR_INVALID_ARG: return "invalid argument";
+        case CSA2_ERR_SHAPE: return "inconsistent shape";
+        case CSA2_ERR_SCHEDULE: return "invalid layer schedule";
+        case CSA2_ERR_WORKSPACE: return "workspace too small";
+        case CSA2_ERR_UNSUPPORTED: return "device is not gfx950";
+        case CSA2_ERR_NO_DEVICE: return "no HIP device";
+        case CSA2_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+csa2_status csa2_device_check(void) { return device_ok(); }
+
+csa2_status csa2_pack_fp4(const uint16_t* x, int64_t rows, int32_t dim, uint8_t* codes,
+                          uint8_t* scales, void* stream) {
+    if (rows < 0 || dim <= 0) return CSA2_ERR_SHAPE;
+    if (dim % 32) return CSA2_ERR_SHAPE;
+    if (rows > 0 && (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)))
+        return CSA2_ERR_INVALID_ARG;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_pack_fp4(x, rows * (dim / 32), codes, scales, (hipStream_t)stream));
+}
+
+csa2_status csa2_unpack_fp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t dim,
+                            float* out, void* stream) {
+    if (rows < 0 || dim <= 0 || dim % 32) return CSA2_ERR_SHAPE;
+    if (rows > 0 && (!codes || !scales || !out || !aligned16(codes) || !aligned16(out)))
+        return CSA2_ERR_INVALID_ARG;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_unpack_fp4(codes, scales, rows * (dim / 32), out, (hipStream_t)stream));
+}
+
+csa2_status csa2_index_score(const csa2_cache* cache, const uint16_t* q_idx, const int32_t* q_pos,
+                             const int32_t* q_seq, int32_t nq, const int32_t* cand, int64_t n_cand,
+                             int32_t block, float* scores, int64_t ld_scores, void* stream) {
+    CacheView cv;
+    if (csa2_status st = check_cache(cache, false, true, &cv)) return st;
+    if (nq < 0) return CSA2_ERR_SHAPE;
+    if (nq > 0 && (!q_idx || !q_pos || !scores || !aligned16(q_idx)))
+        return CSA2_ERR_INVALID_ARG;
+    if (nq > 65535) return CSA2_ERR_SHAPE;
+    if (cand) {
+        if (block != 1 || n_cand < 0 || ld_scores < n_cand) return CSA2_ERR_SHAPE;
+    } else {
+        if (block != 1 && block != 64) return CSA2_ERR_SHAPE;
+        const int64_t n_out = (cv.t_cap + block - 1) / block;
+        if (ld_scores < n_out) return CSA2_ERR_SHAPE;
+    }
+    if (csa2_status st = device_ok()) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (cand)
+        return from_hip(launch_score_cand(cv, q_idx, q_pos, q_seq, nq, cand, n_cand, scores,
+                                          ld_scores, s));
+    return from_hip(launch_score_dense(cv, q_idx, q_pos, q_seq, nq, block, scores, ld_scores, s));
+}
+
+csa2_status csa2_topk_workspace(int32_t nq, int64_t n, int32_t k, int32_t k2, size_t* bytes) {
+    if (!bytes) return CSA2_ERR_INVALID_ARG;
+    if (nq < 0 || n < 0 || k <= 0 || k2 < 0) return CSA2_ERR_SHAPE;
+    *bytes = topk_ws_bytes(nq, n, k, k2);
+    return CSA2_OK;
+}
+
+csa2_status csa2_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, const int32_t* ids,
+                      int32_t k, int32_t* out, int32_t k2, int32_t* out2, void* ws,
+                      size_t ws_bytes, void* stream) {
+    if (nq < 0 || n < 0 || ld < n || k <= 0 || n > (int64_t)INT32_MAX) return CSA2_ERR_SHAPE;
+    if (out2 && k2 < k) return CSA2_ERR_SHAPE;
+    if (nq > 0 && (!scores || !out)) return CSA2_ERR_INVALID_ARG;
+    const size_t need = topk_ws_bytes(nq, n, k, out2 ? k2 : 0);
+    if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_topk(scores, nq, n, ld, ids, k, out, out2 ? k2 : 0, out2, ws,
+                                (hipStream_t)stream));
+}
+
+csa2_status csa2_expand_blocks(const int32_t* blocks, int32_t nq, int32_t nb, int32_t block,
+                               const int32_t* q_pos, int32_t* tokens, void* stream) {
+    if (nq < 0 || nb < 0 || block <= 0) return CSA2_ERR_SHAPE;
+    if ((int64_t)nb * block > (int64_t)INT32_MAX) return CSA2_ERR_SHAPE;
+    if (nq > 0 && nb > 0 && (!blocks || !q_pos || !tokens)) return CSA2_ERR_INVALID_ARG;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_expand_blocks(blocks, nq, nb, block, q_pos, tokens, (hipStream_t)stream));
+}
+
+csa2_status csa2_sparse_attn_workspace(int32_t nq, int32_t k, int32_t window, size_t* bytes) {
+    if (!bytes) return CSA2_ERR_INVALID_ARG;
+    if (nq < 0 || k < 0 || window < 0) return CSA2_ERR_SHAPE;
+    *bytes = attn_ws_bytes(nq, k, window);
+    return CSA2_OK;
+}
+
+csa2_status csa2_sparse_attn(const csa2_cache* cache, const uint16_t* q, const int32_t* q_pos,
+                             const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,
+                             const csa2_local* local, float sm_scale, uint16_t* out, void* ws,
+                             size_t ws_bytes, void* stream) {
+    CacheView cv;
+    LocalView lv;
+    if (csa2_status st = check_cache(cache, true, false, &cv)) return st;
+    if (csa2_status st = check_local(local, &lv)) return st;
+    if (nq < 0 || k < 0 || nq > 65535) return CSA2_ERR_SHAPE;
+    if (nq > 0 && (!q || !q_pos || !out || !aligned16(q))) return CSA2_ERR_INVALID_ARG;
+    if (nq > 0 && k > 0 && !sel) return CSA2_ERR_INVALID_ARG;
+    const size_t need = attn_ws_bytes(nq, k, lv.window);
+    if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_sparse_attn(cv, q, q_pos, q_seq, nq, sel, k, lv, sm_scale, out, ws,
+                                       (hipStream_t)stream));
+}
+
+static csa2_status check_stack(const csa2_stack_desc* d, CacheView* cv, int32_t* max_window) {
+    if (!d || !d->modes || !d->cache || !d->q_pos || !d->q || !d->local || !d->out)
+        return CSA2_ERR_INVALID_ARG;
+    if (d->n_layers <= 0) return CSA2_ERR_SHAPE;
+    if (csa2_status st = check_cache(d->cache, true, true, cv)) return st;
+    if (cv->n_seq > 65535) return CSA2_ERR_SHAPE;
+    if (d->k <= 0 || d->pool < 0 || d->block <= 0) return CSA2_ERR_SHAPE;
+    if (d->block != 1 && d->block != 64) return CSA2_ERR_SHAPE;
+    if (d->pool > 0 && d->pool < d->k) return CSA2_ERR_SHAPE;
+    if (d->block > 1 && (d->pool <= 0 || d->pool % d->block)) return CSA2_ERR_SHAPE;
+    if (d->modes[0] != CSA2_MODE_FULL) return CSA2_ERR_SCHEDULE;
+    int32_t mw = 0;
+    for (int32_t l = 0; l < d->n_layers; ++l) {
+        const int32_t m = d->modes[l];
+        if (m != CSA2_MODE_FULL && m != CSA2_MODE_REINDEX && m != CSA2_MODE_REUSE)
+            return CSA2_ERR_SCHEDULE;
+        if (m == CSA2_MODE_REINDEX && d->pool <= 0) return CSA2_ERR_SCHEDULE;
+        if (!d->q[l] || !d->out[l] || !aligned16(d->q[l])) return CSA2_ERR_INVALID_ARG;
+        if (m != CSA2_MODE_REUSE && (!d->q_idx || !d->q_idx[l] || !aligned16(d->q_idx[l])))
+            return CSA2_ERR_INVALID_ARG;
+        LocalView lv;
+        if (csa2_status st = check_local(&d->local[l], &lv)) return st;
+        mw = std::max(mw, lv.window);
+    }
+    *max_window = mw;
+    return CSA2_OK;
+}
+
+csa2_status csa2_stack_workspace(const csa2_stack_desc* d, size_t* bytes) {
+    if (!bytes) return CSA2_ERR_INVALID_ARG;
+    CacheView cv;
+    int32_t mw;
+    if (csa2_status st = check_stack(d, &cv, &mw)) return st;
+    *bytes = stack_ws_layout(cv.n_seq, cv.t_cap, d->k, d->pool, d->block, mw).total;
+    return CSA2_OK;
+}
+
+csa2_status csa2_stack_run(const csa2_stack_desc* d, void* ws, size_t ws_bytes, void* stream) {
+    CacheView cv;
+    int32_t mw;
+    if (csa2_status st = check_stack(d, &cv, &mw)) return st;
+    const StackWs W = stack_ws_layout(cv.n_seq, cv.t_cap, d->k, d->pool, d->block, mw);
+    if (!ws || ws_bytes < W.total) return CSA2_ERR_WORKSPACE;
+    if (csa2_status st = device_ok()) return st;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(base + W.scores);
+    float* bscores = reinterpret_cast<float*>(base + W.bscores);
+    int32_t* blocks = reinterpret_cast<int32_t*>(base + W.blocks);
+    float* pscores = reinterpret_cast<float*>(base + W.pscores);
+    int32_t* pool = d->pool_out ? d->pool_out : reinterpret_cast<int32_t*>(base + W.pool);
+    int32_t* selbuf = reinterpret_cast<int32_t*>(base + W.sel0);
+    void* tkws = base + W.topk;
+    void* atws = base + W.attn;
+    const int32_t* q_seq = nullptr;  // query b reads sequence b
+    const int32_t S = cv.n_seq, k = d->k, P = d->pool, B = d->block;
+    const int32_t* cur = nullptr;
+    for (int32_t l = 0; l < d->n_layers; ++l) {
+        const int32_t m = d->modes[l];
+        int32_t* sel_l = (d->sel_out && d->sel_out[l]) ? d->sel_out[l] : nullptr;
+        hipError_t e = hipSuccess;
+        if (m == CSA2_MODE_FULL || m == CSA2_MODE_REINDEX) {
+            int32_t* dst = sel_l ? sel_l : selbuf;
+            const bool timed = l == 0 && d->scan_events[0] && d->scan_events[1];
+            if (timed) e = hipEventRecord((hipEvent_t)d->scan_events[0], s);
+            if (e != hipSuccess) return CSA2_ERR_HIP;
+            if (m == CSA2_MODE_FULL && B == 1) {
+                e = launch_score_dense(cv, d->q_idx[l], d->q_pos, q_seq, S, 1, scores, cv.t_cap, s);
+                if (timed && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
+                if (e == hipSuccess)
+                    e = launch_topk(scores, S, cv.t_cap, cv.t_cap, nullptr, k, dst, P, P ? pool : nullptr,
+                                    tkws, s);
+            } else if (m == CSA2_MODE_FULL) {
+                const int64_t nb = (cv.t_cap + B - 1) / B;
+                const int32_t nbsel = P / B;
+                e = launch_score_dense(cv, d->q_idx[l], d->q_pos, q_seq, S, B, bscores, nb, s);
+                if (timed && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
+                if (e == hipSuccess)
+                    e = launch_topk(bscores, S, nb, nb, nullptr, nbsel, blocks, 0, nullptr, tkws, s);
+                if (e == hipSuccess) e = launch_expand_blocks(blocks, S, nbsel, B, d->q_pos, pool, s);
+                if (e == hipSuccess)
+                    e = launch_score_cand(cv, d->q_idx[l], d->q_pos, q_seq, S, pool, P, pscores, P, s);
+                if (e == hipSuccess)
+                    e = launch_topk(pscores, S, P, P, pool, k, dst, 0, nullptr, tkws, s);
+            } else {
+                e = launch_score_cand(cv, d->q_idx[l], d->q_pos, q_seq, S, pool, P, pscores, P, s);
+                if (timed && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
+                if (e == hipSuccess)
+                    e = launch_topk(pscores, S, P, P, pool, k, dst, 0, nullptr, tkws, s);
+            }
+            cur = dst;
+        } else if (sel_l) {
+            e = hipMemcpyAsync(sel_l, cur, sizeof(int32_t) * S * k, hipMemcpyDeviceToDevice, s);
+        }
+        if (e != hipSuccess) return CSA2_ERR_HIP;
+        LocalView lv;
+        check_local(&d->local[l], &lv);
+        e = launch_sparse_attn(cv, d->q[l], d->q_pos, q_seq, S, cur, k, lv, d->sm_scale, d->out[l],
+                               atws, s);
+        if (e != hipSuccess) return CSA2_ERR_HIP;
+    }
+    return CSA2_OK;
+}
+
+}  // extern "C"

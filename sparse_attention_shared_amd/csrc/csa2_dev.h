@@ -1,0 +1,106 @@
+// csa2_dev.h -- device helpers shared by the gfx950 kernels of libcsa2.
+// Internal header: not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kHeads = 16;
+constexpr int kHeadDim = 128;
+constexpr int kIdxDim = 64;
+constexpr int kRowBf16 = 256;   // K | V channels of one global row
+constexpr int kRowCodes = 128;  // FP4 code bytes of one global row
+constexpr int kRowScales = 8;   // E8M0 bytes of one global row
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Exact fp32 value of code c under block exponent E, built from bits.
+// Magnitude codes 1..7 are (1 + f/2) * 2^ec with (ec, f) = (-1,0) (0,0) (0,1)
+// (1,0) (1,1) (2,0) (2,1).
+__device__ __forceinline__ float fp4_exact(uint32_t c, int E) {
+    const uint32_t mag = c & 7u, sign = (c & 8u) << 28;
+    if (mag == 0) return __uint_as_float(sign);
+    const int ec = (mag == 1) ? -1 : (int)(mag >> 1) - 1;
+    const uint32_t f = (mag == 1) ? 0u : (mag & 1u);
+    const int be = ec + E + 127;
+    uint32_t bits;
+    if (be >= 255) bits = 0x7F800000u;
+    else if (be >= 1) bits = ((uint32_t)be << 23) | (f << 22);
+    else bits = (2u + f) << (ec + E + 148);  // subnormal
+    return __uint_as_float(bits | sign);
+}
+
+// Order-preserving unsigned key of a score: a larger score gives a larger key;
+// -0 and +0 give the same key.  Finite scores and +inf give keys >= 0x00800000;
+// -inf gives 0x007FFFFF.  Key 0 is kept free to mark "not selectable".
+__device__ __forceinline__ uint32_t score_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr uint32_t kNegInfKey = 0x007FFFFFu;
+
+// Sum over groups of 8 consecutive lanes (every lane of the group gets it).
+__device__ __forceinline__ float sum8(float v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    return v;
+}
+
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Exclusive scan over a whole workgroup of NT threads (NT % 64 == 0, NT <= 4096).
+// `tmp` needs NT/64 + 1 ints of LDS.  Returns the exclusive prefix; *total gets
+// the sum.  Contains barriers: every thread must call it.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int inc = wave_incl_scan(v);
+    if (lane == 63) tmp[w] = inc;
+    __syncthreads();
+    if (w == 0) {
+        int x = lane < NW ? tmp[lane] : 0;
+        int xi = wave_incl_scan(x);
+        if (lane < NW) tmp[lane] = xi - x;
+        if (lane == NW - 1) tmp[NW] = xi;
+    }
+    __syncthreads();
+    int r = tmp[w] + inc - v;
+    *total = tmp[NW];
+    __syncthreads();
+    return r;
+}
+
+// XCD-aware remap of a flat workgroup id: the hardware deals consecutive ids
+// round-robin over the 8 XCDs; this makes each XCD own a contiguous range of
+// logical ids, so neighbouring tiles share an L2.  `n` is the grid size.
+__device__ __forceinline__ uint32_t xcd_swizzle(uint32_t id, uint32_t n) {
+    constexpr uint32_t X = 8;
+    uint32_t per = n / X;
+    if (id >= per * X) return id;  // ragged tail keeps its id
+    return (id % X) * per + id / X;
+}
+
+}  // namespace csa2

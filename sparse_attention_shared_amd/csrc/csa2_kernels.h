@@ -1,0 +1,54 @@
+// csa2_kernels.h -- host-side launchers of the gfx950 kernels (internal).
+// Each launcher only enqueues on `s`; shapes are validated by the caller
+// (csa2_api.cpp) before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+struct CacheView {
+    int32_t fp4;            // 1: FP4 codes + scales, 0: bf16 rows
+    int32_t n_seq;
+    int64_t t_cap;
+    const void* data;       // bf16 [n_seq][t_cap][256] or codes [n_seq][t_cap][128]
+    const uint8_t* scales;  // [n_seq][t_cap][8]
+    const uint16_t* k_idx;  // [n_seq][t_cap][64]
+};
+
+struct LocalView {
+    const uint16_t* k;
+    const uint16_t* v;
+    int32_t cap, window, lo;
+};
+
+hipError_t launch_pack_fp4(const uint16_t* x, int64_t nblk, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s);
+hipError_t launch_unpack_fp4(const uint8_t* codes, const uint8_t* scales, int64_t nblk, float* out,
+                             hipStream_t s);
+
+// Dense indexer scores: scores[i][b], b < ceil(t_cap / block), block in {1, 64}.
+hipError_t launch_score_dense(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
+                              const int32_t* q_seq, int32_t nq, int32_t block, float* scores,
+                              int64_t ld, hipStream_t s);
+// Candidate scores: scores[i][j] = score of position cand[i][j].
+hipError_t launch_score_cand(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
+                             const int32_t* q_seq, int32_t nq, const int32_t* cand, int64_t n_cand,
+                             float* scores, int64_t ld, hipStream_t s);
+
+size_t topk_ws_bytes(int32_t nq, int64_t n, int32_t k, int32_t k2);
+hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, const int32_t* ids,
+                       int32_t k, int32_t* out, int32_t k2, int32_t* out2, void* ws, hipStream_t s);
+
+hipError_t launch_expand_blocks(const int32_t* blocks, int32_t nq, int32_t nb, int32_t block,
+                                const int32_t* q_pos, int32_t* tokens, hipStream_t s);
+
+size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window);
+hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
+                              const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,
+                              const LocalView& loc, float sm_scale, uint16_t* out, void* ws,
+                              hipStream_t s);
+
+}  // namespace csa2

@@ -1,0 +1,169 @@
+// k_score.hip -- indexer scores: the layer's 64-element indexer query against
+// the indexer keys of the shared global cache ("CED: Continuing Context with a
+// Causal Encoder and Decoder", section "Selecting Positions and Reading Values
+// with Attention", Fig. 4), causally masked (same page, Fig. 2: a query at t
+// reads positions <= t only).
+//
+// Decode scoring is a GEMV over T keys of 128 B each: pure HBM streaming at
+// about one flop per byte, so it runs on the vector ALUs, not MFMA.  Eight
+// lanes share one key: each lane loads 16 contiguous bytes, so every load
+// instruction of a wave reads 1 KB of consecutive memory (8 keys), and the
+// eight partial dots are summed with three lane exchanges.
+#include "csa2_dev.h"
+#include "csa2_kernels.h"
+
+namespace csa2 {
+
+constexpr int kScoreTile = 256;  // keys per workgroup (4 waves x 64)
+
+__device__ __forceinline__ float dot8(const float* q, uint4 k) {
+    float a = q[0] * bf16_lo(k.x);
+    a = fmaf(q[1], bf16_hi(k.x), a);
+    a = fmaf(q[2], bf16_lo(k.y), a);
+    a = fmaf(q[3], bf16_hi(k.y), a);
+    a = fmaf(q[4], bf16_lo(k.z), a);
+    a = fmaf(q[5], bf16_hi(k.z), a);
+    a = fmaf(q[6], bf16_lo(k.w), a);
+    a = fmaf(q[7], bf16_hi(k.w), a);
+    return a;
+}
+
+__device__ __forceinline__ void load_q8(const uint16_t* q, float* qf) {
+    const uint4 v = *reinterpret_cast<const uint4*>(q);
+    qf[0] = bf16_lo(v.x); qf[1] = bf16_hi(v.x);
+    qf[2] = bf16_lo(v.y); qf[3] = bf16_hi(v.y);
+    qf[4] = bf16_lo(v.z); qf[5] = bf16_hi(v.z);
+    qf[6] = bf16_lo(v.w); qf[7] = bf16_hi(v.w);
+}
+
+// Select s[r] for a run-time r in [0, 8) without spilling the array.
+__device__ __forceinline__ float pick8(const float* s, int r) {
+    float v = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) v = (r == i) ? s[i] : v;
+    return v;
+}
+
+// grid: (ceil(t_cap / 256), nq).  Lane (grp, sub) of a wave handles bytes
+// [16 sub, 16 sub + 16) of key base + 8 r + grp in round r.
+template <int BLOCK>
+__global__ __launch_bounds__(256) void k_score_dense(const uint16_t* __restrict__ k_idx,
+                                                     int32_t n_seq, int64_t t_cap,
+                                                     const uint16_t* __restrict__ q_idx,
+                                                     const int32_t* __restrict__ q_pos,
+                                                     const int32_t* __restrict__ q_seq,
+                                                     float* __restrict__ scores, int64_t ld) {
+    const int qi = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane & 7, grp = lane >> 3;
+    const int64_t base = (int64_t)blockIdx.x * kScoreTile + wave * 64;
+    float* srow = scores + (int64_t)qi * ld;
+    const int32_t seq = q_seq ? q_seq[qi] : qi;
+    int64_t t = q_pos[qi];
+    if (seq < 0 || seq >= n_seq) t = -1;  // a bad sequence id reads nothing
+    if (t >= t_cap) t = t_cap - 1;
+    if (base >= t_cap) return;
+    const float NEG = -__builtin_inff();
+    if (base > t) {  // the whole wave is after the query: masked
+        if (BLOCK == 1) {
+            if (base + lane < t_cap) srow[base + lane] = NEG;
+        } else if (lane == 0) {
+            srow[base / 64] = NEG;
+        }
+        return;
+    }
+    float qf[8];
+    load_q8(q_idx + (int64_t)qi * kIdxDim + sub * 8, qf);
+    const uint4* kb = reinterpret_cast<const uint4*>(k_idx) + (int64_t)seq * t_cap * 8;
+    uint4 kv[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int64_t tok = base + r * 8 + grp;
+        kv[r] = (tok <= t) ? kb[tok * 8 + sub] : make_uint4(0, 0, 0, 0);
+    }
+    float s[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) s[r] = sum8(dot8(qf, kv[r]));
+    if (BLOCK == 1) {
+        // lane (grp, sub) stores key base + 8 sub + grp: one 256 B coalesced store
+        const int64_t tok = base + sub * 8 + grp;
+        const float v = pick8(s, sub);
+        if (tok < t_cap) srow[tok] = (tok <= t) ? v : NEG;
+    } else {
+        float m = NEG;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            if (base + r * 8 + grp <= t) m = fmaxf(m, s[r]);
+        m = fmaxf(m, __shfl_xor(m, 8, 64));
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (lane == 0) srow[base / 64] = m;
+    }
+}
+
+// grid: (ceil(n_cand / 256), nq).  Same lane layout; key c of the tile is
+// position cand[qi][c].
+__global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__ k_idx,
+                                                    int32_t n_seq, int64_t t_cap,
+                                                    const uint16_t* __restrict__ q_idx,
+                                                    const int32_t* __restrict__ q_pos,
+                                                    const int32_t* __restrict__ q_seq,
+                                                    const int32_t* __restrict__ cand,
+                                                    int64_t n_cand, float* __restrict__ scores,
+                                                    int64_t ld) {
+    const int qi = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane & 7, grp = lane >> 3;
+    const int64_t base = (int64_t)blockIdx.x * kScoreTile + wave * 64;
+    if (base >= n_cand) return;
+    float* srow = scores + (int64_t)qi * ld;
+    const int32_t* crow = cand + (int64_t)qi * n_cand;
+    const int32_t seq = q_seq ? q_seq[qi] : qi;
+    int64_t t = q_pos[qi];
+    if (seq < 0 || seq >= n_seq) t = -1;
+    if (t >= t_cap) t = t_cap - 1;
+    float qf[8];
+    load_q8(q_idx + (int64_t)qi * kIdxDim + sub * 8, qf);
+    const uint4* kb = reinterpret_cast<const uint4*>(k_idx) + (int64_t)(seq < 0 ? 0 : seq) * t_cap * 8;
+    uint4 kv[8];
+    bool ok[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int64_t c = base + r * 8 + grp;
+        const int64_t tok = (c < n_cand) ? crow[c] : -1;
+        ok[r] = tok >= 0 && tok <= t;
+        kv[r] = ok[r] ? kb[tok * 8 + sub] : make_uint4(0, 0, 0, 0);
+    }
+    float s[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) s[r] = ok[r] ? sum8(dot8(qf, kv[r])) : -__builtin_inff();
+    const int64_t c = base + sub * 8 + grp;
+    const float v = pick8(s, sub);
+    if (c < n_cand) srow[c] = v;
+}
+
+hipError_t launch_score_dense(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
+                              const int32_t* q_seq, int32_t nq, int32_t block, float* scores,
+                              int64_t ld, hipStream_t s) {
+    if (nq == 0 || c.t_cap == 0) return hipSuccess;
+    dim3 grid((uint32_t)((c.t_cap + kScoreTile - 1) / kScoreTile), (uint32_t)nq);
+    if (block == 1)
+        hipLaunchKernelGGL(k_score_dense<1>, grid, dim3(256), 0, s, c.k_idx, c.n_seq, c.t_cap,
+                           q_idx, q_pos, q_seq, scores, ld);
+    else
+        hipLaunchKernelGGL(k_score_dense<64>, grid, dim3(256), 0, s, c.k_idx, c.n_seq, c.t_cap,
+                           q_idx, q_pos, q_seq, scores, ld);
+    return hipGetLastError();
+}
+
+hipError_t launch_score_cand(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
+                             const int32_t* q_seq, int32_t nq, const int32_t* cand, int64_t n_cand,
+                             float* scores, int64_t ld, hipStream_t s) {
+    if (nq == 0 || n_cand == 0) return hipSuccess;
+    dim3 grid((uint32_t)((n_cand + kScoreTile - 1) / kScoreTile), (uint32_t)nq);
+    hipLaunchKernelGGL(k_score_cand, grid, dim3(256), 0, s, c.k_idx, c.n_seq, c.t_cap, q_idx,
+                       q_pos, q_seq, cand, n_cand, scores, ld);
+    return hipGetLastError();
+}
+
+}  // namespace csa2

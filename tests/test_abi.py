@@ -1,0 +1,131 @@
+"""The C ABI library loads, exports every function include/csa2.h declares, and
+validates arguments on the host (these cases fail before any device work, so
+they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import sparse_attention_shared_amd as csa2
+from sparse_attention_shared_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INVALID, SHAPE, SCHEDULE, WORKSPACE, UNSUPPORTED, NO_DEVICE, HIP = range(8)
+
+
+def declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in os.listdir(inc):
+        if f.endswith(".h"):
+            src = open(os.path.join(inc, f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(csa2_\w+)\s*\(", src))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    L = csa2.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert csa2.version() == 100
+
+
+def test_status_strings():
+    L = csa2.lib()
+    for s in range(8):
+        assert L.csa2_status_str(s)
+    assert L.csa2_status_str(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails validation
+FAKE_ODD = ctypes.c_void_p(0x10004)  # misaligned
+
+
+def test_pack_validation():
+    L = csa2.lib()
+    assert L.csa2_pack_fp4(FAKE, 4, 48, FAKE, FAKE, None) == SHAPE
+    assert L.csa2_pack_fp4(FAKE, -1, 32, FAKE, FAKE, None) == SHAPE
+    assert L.csa2_pack_fp4(None, 4, 32, FAKE, FAKE, None) == INVALID
+    assert L.csa2_pack_fp4(FAKE_ODD, 4, 32, FAKE, FAKE, None) == INVALID
+    assert L.csa2_unpack_fp4(FAKE, FAKE, 4, 40, FAKE, None) == SHAPE
+
+
+def _cache(fmt=csa2.KV_FP4, n_seq=2, t_cap=100, data=FAKE, scales=FAKE, k_idx=FAKE):
+    return _lib.csa2_cache(fmt, n_seq, t_cap, data, scales, k_idx)
+
+
+def test_score_topk_attn_validation():
+    L = csa2.lib()
+    c = _cache()
+    bp = ctypes.byref
+    # block must be 1 or 64 on the dense path, 1 with candidates
+    assert L.csa2_index_score(bp(c), FAKE, FAKE, None, 2, None, 0, 7, FAKE, 100, None) == SHAPE
+    assert L.csa2_index_score(bp(c), FAKE, FAKE, None, 2, FAKE, 10, 64, FAKE, 100, None) == SHAPE
+    assert L.csa2_index_score(bp(c), FAKE, FAKE, None, 2, None, 0, 1, FAKE, 99, None) == SHAPE
+    assert L.csa2_index_score(bp(_cache(fmt=5)), FAKE, FAKE, None, 2, None, 0, 1, FAKE, 100,
+                              None) == INVALID
+    assert L.csa2_index_score(bp(_cache(k_idx=None)), FAKE, FAKE, None, 2, None, 0, 1, FAKE, 100,
+                              None) == INVALID
+    # top-k: k >= 1, k2 >= k, ld >= n
+    assert L.csa2_topk(FAKE, 2, 100, 100, None, 0, FAKE, 0, None, None, 0, None) == SHAPE
+    assert L.csa2_topk(FAKE, 2, 100, 100, None, 8, FAKE, 4, FAKE, None, 0, None) == SHAPE
+    assert L.csa2_topk(FAKE, 2, 100, 50, None, 8, FAKE, 0, None, None, 0, None) == SHAPE
+    # attention: window <= cap, FP4 cache needs scales
+    loc = _lib.csa2_local(FAKE, FAKE, 64, 128, 0)
+    assert L.csa2_sparse_attn(bp(c), FAKE, FAKE, None, 2, FAKE, 8, bp(loc), 0.1, FAKE, FAKE,
+                              1 << 20, None) == SHAPE
+    loc = _lib.csa2_local(FAKE, FAKE, 128, 128, 0)
+    assert L.csa2_sparse_attn(bp(_cache(scales=None)), FAKE, FAKE, None, 2, FAKE, 8, bp(loc), 0.1,
+                              FAKE, FAKE, 1 << 20, None) == INVALID
+    n = _lib._sz()
+    assert L.csa2_sparse_attn_workspace(2, 8, 128, ctypes.byref(n)) == OK and n.value > 0
+    assert L.csa2_sparse_attn(bp(c), FAKE, FAKE, None, 2, FAKE, 8, bp(loc), 0.1, FAKE, FAKE,
+                              n.value - 1, None) == WORKSPACE
+
+
+def _desc(modes, k=8, pool=16, block=1, cache=None):
+    Lr = len(modes)
+    keep = {}
+    keep["cache"] = cache or _cache()
+    keep["modes"] = (ctypes.c_int32 * Lr)(*modes)
+    ptrs = (ctypes.c_void_p * Lr)(*([0x10000] * Lr))
+    keep["ptrs"] = ptrs
+    keep["loc"] = (_lib.csa2_local * Lr)(*[_lib.csa2_local(FAKE, FAKE, 128, 128, 0)] * Lr)
+    d = _lib.csa2_stack_desc(Lr, keep["modes"], ctypes.pointer(keep["cache"]), FAKE, k, pool, block,
+                             0.1, ptrs, ptrs, keep["loc"], ptrs, None, None)
+    return d, keep
+
+
+@pytest.mark.parametrize("modes,pool,block,k,want", [
+    ([2, 0], 16, 1, 8, SCHEDULE),        # Reuse first
+    ([1, 2], 16, 1, 8, SCHEDULE),        # Reindex first
+    ([0, 1], 0, 1, 8, SCHEDULE),         # Reindex without a pool
+    ([0, 7], 16, 1, 8, SCHEDULE),        # unknown mode
+    ([0, 1], 4, 1, 8, SHAPE),            # pool smaller than k
+    ([0], 100, 64, 8, SHAPE),            # blockwise pool not a multiple of the block
+    ([0], 0, 64, 8, SHAPE),              # blockwise without a pool
+    ([0], 16, 3, 8, SHAPE),              # unsupported block size
+])
+def test_stack_schedule_validation(modes, pool, block, k, want):
+    d, keep = _desc(modes, k=k, pool=pool, block=block)
+    n = _lib._sz()
+    assert csa2.lib().csa2_stack_workspace(ctypes.byref(d), ctypes.byref(n)) == want
+    assert csa2.lib().csa2_stack_run(ctypes.byref(d), FAKE, 1 << 30, None) == want
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
+def test_valid_arguments_without_a_device_report_no_device():
+    L = csa2.lib()
+    assert L.csa2_device_check() == NO_DEVICE
+    # valid shapes, validation passes, then the device check refuses: nothing is launched
+    assert L.csa2_pack_fp4(FAKE, 4, 32, FAKE, FAKE, None) == NO_DEVICE
+    d, keep = _desc([0, 1, 2, 2])
+    n = _lib._sz()
+    assert L.csa2_stack_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert L.csa2_stack_run(ctypes.byref(d), FAKE, n.value, None) == NO_DEVICE
