@@ -145,7 +145,7 @@ def main():
     from sparse_attention_shared_amd._lib import _StackArgs, stack_workspace
     need = stack_workspace(_StackArgs(caches[0], sp.schedule, q_pos, q, q_idx, local, out, sp.k,
                                       sp.pool, 1, 128 ** -0.5, None, None))
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
 
     n_ev = args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

@@ -75,7 +75,7 @@ typedef enum { CSA2_KV_BF16 = 0, CSA2_KV_FP4 = 1 } csa2_kv_format;
  *         32-channel blocks of K, bytes 4..7 those of V.
  *         This is exactly what csa2_pack_fp4 writes for rows of 256 (K | V).
  *   k_idx = indexer keys, bf16 [n_seq][t_cap][64].
- * data, scales and k_idx must be 16-byte aligned. */
+ * data, scales and k_idx must be 16-byte aligned; t_cap <= 2^24. */
 typedef struct {
     int32_t format;           /* csa2_kv_format */
     int32_t n_seq;
@@ -150,8 +150,10 @@ csa2_status csa2_index_score(const csa2_cache *cache, const uint16_t *q_idx, con
  * library writes is).  out: int32 [nq][k], the chosen positions ascending,
  * padded with -1 when fewer than k can be chosen.  When out2 != NULL the
  * first k2 >= k under the same order are also written to out2 [nq][k2]
- * (the Full layer's candidate pool, Fig. 5).  ws: at least the size returned
- * by csa2_topk_workspace (may be 0). */
+ * (the Full layer's candidate pool, Fig. 5).  n <= 2^24.  ws: at least the
+ * size returned by csa2_topk_workspace (may be 0); it holds counters that
+ * reset themselves, so it must be zero-filled before its first use, every
+ * call leaves it zero-filled, and calls sharing a workspace must not overlap. */
 csa2_status csa2_topk(const float *scores, int32_t nq, int64_t n, int64_t ld, const int32_t *ids,
                       int32_t k, int32_t *out, int32_t k2, int32_t *out2, void *ws,
                       size_t ws_bytes, void *stream);
@@ -172,7 +174,9 @@ csa2_status csa2_expand_blocks(const int32_t *blocks, int32_t nq, int32_t nb, in
  * dequantised exactly.  q: bf16 [nq][16][128]; out: bf16 [nq][16][128]
  * (fp32 accumulation, rounded to nearest even).  A query with no entry at
  * all gets zeros.  q_seq may be NULL (query i reads sequence i).  nq <= 65535.
- * ws: at least csa2_sparse_attn_workspace bytes. */
+ * ws: at least csa2_sparse_attn_workspace bytes (0 when one workgroup covers
+ * a query); it holds per-query counters that reset themselves, so it must be
+ * zero-filled before its first use and calls sharing it must not overlap. */
 csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, const int32_t *q_pos,
                              const int32_t *q_seq, int32_t nq, const int32_t *sel, int32_t k,
                              const csa2_local *local, float sm_scale, uint16_t *out, void *ws,
@@ -213,6 +217,8 @@ typedef struct {
                                           after layer 0's indexer scan kernel; NULL skips */
 } csa2_stack_desc;
 
+/* Workspace of csa2_stack_run; like the top-k workspace it must be
+ * zero-filled before its first use and is left zero-filled by every run. */
 csa2_status csa2_stack_workspace(const csa2_stack_desc *desc, size_t *bytes);
 /* Run every layer in order on `stream`.  Validates the schedule: layer 0 must
  * be Full and Reindex needs pool > 0; k <= pool when pool > 0; with block > 1,

@@ -195,7 +195,7 @@ def topk(scores: torch.Tensor, k: int, ids: Optional[torch.Tensor] = None, k2: i
     out2 = torch.empty((nq, k2), dtype=torch.int32, device=scores.device) if k2 else None
     ws_n = _sz()
     _check("csa2_topk_workspace", lib().csa2_topk_workspace(nq, n, k, k2, ctypes.byref(ws_n)))
-    ws = torch.empty(max(ws_n.value, 1), dtype=torch.uint8, device=scores.device)
+    ws = torch.zeros(max(ws_n.value, 1), dtype=torch.uint8, device=scores.device)
     _check("csa2_topk", lib().csa2_topk(_ptr(scores), nq, n, int(scores.stride(0)),
                                         _ptr(_i32t(ids)), k, _ptr(out), k2, _ptr(out2), _ptr(ws),
                                         ws_n.value, _stream()))
@@ -226,7 +226,7 @@ def sparse_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, q_seq: Optio
         out = torch.empty((nq, HEADS, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
     need = sparse_attn_workspace(nq, k, local.c.window)
     if ws is None:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     _check("csa2_sparse_attn", lib().csa2_sparse_attn(
         ctypes.byref(cache.c), _ptr(_bits16(q)), _ptr(_i32t(q_pos)), _ptr(_i32t(q_seq)), nq,
         _ptr(_i32t(sel)), k, ctypes.byref(local.c), float(sm_scale), _ptr(out), _ptr(ws),
@@ -290,7 +290,7 @@ def stack_run(cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
                       pool_out, ev)
     need = stack_workspace(args)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     _check("csa2_stack_run", lib().csa2_stack_run(ctypes.byref(args.desc), _ptr(ws), ws.numel(),
                                                   _stream()))
     return out, sel, pool_out

@@ -55,10 +55,11 @@ csa2_status from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR
 csa2_status check_cache(const csa2_cache* c, bool need_kv, bool need_idx, CacheView* v) {
     if (!c) return CSA2_ERR_INVALID_ARG;
     if (c->format != CSA2_KV_BF16 && c->format != CSA2_KV_FP4) return CSA2_ERR_INVALID_ARG;
-    if (c->n_seq <= 0 || c->t_cap <= 0 || c->t_cap > (int64_t)INT32_MAX) return CSA2_ERR_SHAPE;
+    if (c->n_seq <= 0 || c->t_cap <= 0 || c->t_cap > ((int64_t)1 << 24)) return CSA2_ERR_SHAPE;
     if (need_kv) {
         if (!c->data || !aligned16(c->data)) return CSA2_ERR_INVALID_ARG;
-        if (c->format == CSA2_KV_FP4 && !c->scales) return CSA2_ERR_INVALID_ARG;
+        if (c->format == CSA2_KV_FP4 && (!c->scales || !aligned16(c->scales)))
+            return CSA2_ERR_INVALID_ARG;
     }
     if (need_idx && (!c->k_idx || !aligned16(c->k_idx))) return CSA2_ERR_INVALID_ARG;
     v->fp4 = c->format == CSA2_KV_FP4;
@@ -87,9 +88,10 @@ csa2_status check_local(const csa2_local* l, LocalView* v) {
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of one stack run: scores, block scores / block ids, pool scores,
-// pool, the current selection, top-k and attention scratch.
+// pool, the current selection, per-sequence counters, top-k and attention
+// scratch.  Counters reset themselves: the workspace must start zero-filled.
 struct StackWs {
-    size_t scores, bscores, blocks, pscores, pool, sel0, topk, attn, total;
+    size_t scores, bscores, blocks, pscores, pool, sel0, ctr, topk, attn, total;
 };
 
 StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, int32_t block,
@@ -109,6 +111,7 @@ StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, i
     w.pscores = take((size_t)n_seq * (pool > 0 ? pool : 1) * sizeof(float));
     w.pool = take((size_t)n_seq * (pool > 0 ? pool : 1) * sizeof(int32_t));
     w.sel0 = take((size_t)n_seq * k * sizeof(int32_t));
+    w.ctr = take((size_t)n_seq * sizeof(uint32_t));
     size_t tk = topk_ws_bytes(n_seq, t_cap, k, pool);
     if (block > 1) tk = std::max(tk, topk_ws_bytes(n_seq, nb, nbsel, 0));
     if (pool > 0) tk = std::max(tk, topk_ws_bytes(n_seq, pool, k, 0));
@@ -193,7 +196,7 @@ csa2_status csa2_topk_workspace(int32_t nq, int64_t n, int32_t k, int32_t k2, si
 csa2_status csa2_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, const int32_t* ids,
                       int32_t k, int32_t* out, int32_t k2, int32_t* out2, void* ws,
                       size_t ws_bytes, void* stream) {
-    if (nq < 0 || n < 0 || ld < n || k <= 0 || n > (int64_t)INT32_MAX) return CSA2_ERR_SHAPE;
+    if (nq < 0 || n < 0 || ld < n || k <= 0 || n > ((int64_t)1 << 24)) return CSA2_ERR_SHAPE;
     if (out2 && k2 < k) return CSA2_ERR_SHAPE;
     if (nq > 0 && (!scores || !out)) return CSA2_ERR_INVALID_ARG;
     const size_t need = topk_ws_bytes(nq, n, k, out2 ? k2 : 0);
@@ -289,10 +292,20 @@ csa2_status csa2_stack_run(const csa2_stack_desc* d, void* ws, size_t ws_bytes, 
     float* pscores = reinterpret_cast<float*>(base + W.pscores);
     int32_t* pool = d->pool_out ? d->pool_out : reinterpret_cast<int32_t*>(base + W.pool);
     int32_t* selbuf = reinterpret_cast<int32_t*>(base + W.sel0);
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(base + W.ctr);
     void* tkws = base + W.topk;
     void* atws = base + W.attn;
     const int32_t* q_seq = nullptr;  // query b reads sequence b
     const int32_t S = cv.n_seq, k = d->k, P = d->pool, B = d->block;
+    // score the pool with layer l's indexer query and keep the top k
+    auto rescore_pool = [&](int32_t l, int32_t* dst) -> hipError_t {
+        if (P <= kFusedSelectMax)
+            return launch_score_select(cv, d->q_idx[l], d->q_pos, q_seq, S, pool, P, pscores, ctr,
+                                       k, dst, s);
+        hipError_t e = launch_score_cand(cv, d->q_idx[l], d->q_pos, q_seq, S, pool, P, pscores, P, s);
+        if (e == hipSuccess) e = launch_topk(pscores, S, P, P, pool, k, dst, 0, nullptr, tkws, s);
+        return e;
+    };
     const int32_t* cur = nullptr;
     for (int32_t l = 0; l < d->n_layers; ++l) {
         const int32_t m = d->modes[l];
@@ -317,15 +330,10 @@ csa2_status csa2_stack_run(const csa2_stack_desc* d, void* ws, size_t ws_bytes, 
                 if (e == hipSuccess)
                     e = launch_topk(bscores, S, nb, nb, nullptr, nbsel, blocks, 0, nullptr, tkws, s);
                 if (e == hipSuccess) e = launch_expand_blocks(blocks, S, nbsel, B, d->q_pos, pool, s);
-                if (e == hipSuccess)
-                    e = launch_score_cand(cv, d->q_idx[l], d->q_pos, q_seq, S, pool, P, pscores, P, s);
-                if (e == hipSuccess)
-                    e = launch_topk(pscores, S, P, P, pool, k, dst, 0, nullptr, tkws, s);
+                if (e == hipSuccess) e = rescore_pool(l, dst);
             } else {
-                e = launch_score_cand(cv, d->q_idx[l], d->q_pos, q_seq, S, pool, P, pscores, P, s);
+                e = rescore_pool(l, dst);
                 if (timed && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
-                if (e == hipSuccess)
-                    e = launch_topk(pscores, S, P, P, pool, k, dst, 0, nullptr, tkws, s);
             }
             cur = dst;
         } else if (sel_l) {

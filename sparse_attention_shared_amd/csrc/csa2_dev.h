@@ -59,16 +59,20 @@ __device__ __forceinline__ float sum8(float v) {
     return v;
 }
 
-// Inclusive scan over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
-    }
-    return v;
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS traffic).
+__device__ __forceinline__ int wave_scan_dpp(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
 }
+
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) { return wave_scan_dpp(v); }
 
 // Exclusive scan over a whole workgroup of NT threads (NT % 64 == 0, NT <= 4096).
 // `tmp` needs NT/64 + 1 ints of LDS.  Returns the exclusive prefix; *total gets

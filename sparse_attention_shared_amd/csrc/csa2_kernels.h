@@ -38,6 +38,14 @@ hipError_t launch_score_cand(const CacheView& c, const uint16_t* q_idx, const in
                              const int32_t* q_seq, int32_t nq, const int32_t* cand, int64_t n_cand,
                              float* scores, int64_t ld, hipStream_t s);
 
+// Candidate scores + top-k among them in one launch (n_cand <= 16384); `ctr`
+// is nq counters that must be zero and are left zero.
+hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
+                               const int32_t* q_seq, int32_t nq, const int32_t* cand,
+                               int64_t n_cand, float* scores, uint32_t* ctr, int32_t k,
+                               int32_t* sel, hipStream_t s);
+constexpr int64_t kFusedSelectMax = 16384;
+
 size_t topk_ws_bytes(int32_t nq, int64_t n, int32_t k, int32_t k2);
 hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, const int32_t* ids,
                        int32_t k, int32_t* out, int32_t k2, int32_t* out2, void* ws, hipStream_t s);

@@ -5,64 +5,108 @@
 // from the shared cache, window entries from the layer's own local KV,
 // section "Shared Global KV and Per-Layer Local KV", Fig. 3).
 //
-// Split-K: the entry list of a query (k selected slots, then the window) is
-// cut into chunks of 64; one workgroup per (chunk, query) gathers its rows,
-// dequantises FP4 exactly into LDS, and writes an unnormalised partial
-// (max, sum, P.V) per head; a merge kernel combines the chunks in a fixed
+// All 16 heads read the same K/V row (one KV head), so per entry block the
+// work is two small dense products: S = K Q^T (16 entries x 16 heads, K = 128
+// dims) and O += P V (16 heads x 16 dims, K = 32 entries).  Both run on
+// v_mfma_f32_16x16x32_bf16.  FP4 codes become bf16 of the unscaled E2M1 value
+// (exact); each MFMA k-step covers exactly one 32-element scale block, so the
+// power-of-two scales are applied exactly in fp32: on S per (entry, block),
+// and on P per (entry, V block) before P feeds the second product.
+//
+// Work split: a wave takes 32 entries, a workgroup 8 waves (256 entries).  A
+// query with more entries is cut into chunks, one workgroup each; every chunk
+// writes its partial (max, sum, unnormalised O per head) to the workspace and
+// the last chunk to finish (a per-query counter) combines all of them in chunk
 // order, so results do not depend on scheduling.
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
 
 namespace csa2 {
 
-constexpr int kAttnChunk = 64;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBlk = 32;                  // entries per wave
+constexpr int kWgEntries = kWaves * kBlk;  // entries per workgroup
+constexpr int kVtStride = kBlk + 4;       // padded row of the V^T tile (bf16), 8-byte aligned
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ void store32(float* dst, const float* v) {
-#pragma unroll
-    for (int i = 0; i < 32; i += 4)
-        *reinterpret_cast<float4*>(dst + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+// 8 FP4 codes (one dword, element i in nibble i) -> 8 bf16 of the unscaled
+// E2M1 value, packed two per dword (element 2i in the low half of out[i/2]...).
+// bf16 of the magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}: high bytes
+// 00 3F 3F 3F 40 40 40 40, low bytes 00 00 80 C0 00 40 80 C0; the sign bit of
+// the code becomes bit 7 of the high byte.  v_perm_b32 does the table lookups.
+__device__ __forceinline__ void fp4x8_bf16(uint32_t w, uint32_t* out) {
+    constexpr uint32_t HI_03 = 0x3F3F3F00u, HI_47 = 0x40404040u;
+    constexpr uint32_t LO_03 = 0xC0800000u, LO_47 = 0xC0804000u;
+    const uint32_t ev = w & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6
+    const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
+    const uint32_t me = ev & 0x07070707u, mo = od & 0x07070707u;
+    const uint32_t he = __builtin_amdgcn_perm(HI_47, HI_03, me) | ((ev & 0x08080808u) << 4);
+    const uint32_t le = __builtin_amdgcn_perm(LO_47, LO_03, me);
+    const uint32_t ho = __builtin_amdgcn_perm(HI_47, HI_03, mo) | ((od & 0x08080808u) << 4);
+    const uint32_t lo = __builtin_amdgcn_perm(LO_47, LO_03, mo);
+    const uint32_t x01 = __builtin_amdgcn_perm(he, le, 0x05010400u);  // e0 | e2 << 16
+    const uint32_t x23 = __builtin_amdgcn_perm(he, le, 0x07030602u);  // e4 | e6 << 16
+    const uint32_t y01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u);  // e1 | e3 << 16
+    const uint32_t y23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);  // e5 | e7 << 16
+    out[0] = __builtin_amdgcn_perm(y01, x01, 0x05040100u);            // e0 | e1 << 16
+    out[1] = __builtin_amdgcn_perm(y01, x01, 0x07060302u);            // e2 | e3 << 16
+    out[2] = __builtin_amdgcn_perm(y23, x23, 0x05040100u);            // e4 | e5 << 16
+    out[3] = __builtin_amdgcn_perm(y23, x23, 0x07060302u);            // e6 | e7 << 16
 }
 
-// 32 bf16 (64 B) -> 32 floats
-__device__ __forceinline__ void bf16x32(const uint16_t* src, float* v) {
-    const uint4* p = reinterpret_cast<const uint4*>(src);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint4 w = p[i];
-        v[8 * i + 0] = bf16_lo(w.x); v[8 * i + 1] = bf16_hi(w.x);
-        v[8 * i + 2] = bf16_lo(w.y); v[8 * i + 3] = bf16_hi(w.y);
-        v[8 * i + 4] = bf16_lo(w.z); v[8 * i + 5] = bf16_hi(w.z);
-        v[8 * i + 6] = bf16_lo(w.w); v[8 * i + 7] = bf16_hi(w.w);
-    }
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+    u32x4_t v = {a, b, c, d};
+    return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// 32 FP4 codes (16 B) under one E8M0 scale -> 32 floats, exact
-__device__ __forceinline__ void fp4x32(const uint8_t* codes, uint8_t scale, float* v) {
-    const uint4 c = *reinterpret_cast<const uint4*>(codes);
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    const int E = (int)scale - 127;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[8 * i + j] = fp4_exact((w[i] >> (4 * j)) & 15u, E);
+// 2^(byte - 127) as fp32 (exact; byte 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t byte) {
+    return __uint_as_float(byte ? (byte << 23) : 0x00400000u);
 }
 
-// grid: (n_split, nq), 256 threads.
-__global__ __launch_bounds__(256) void k_attn_split(CacheView c, const uint16_t* __restrict__ q,
-                                                    const int32_t* __restrict__ q_pos,
-                                                    const int32_t* __restrict__ q_seq,
-                                                    const int32_t* __restrict__ sel, int32_t k,
-                                                    LocalView loc, float sm_scale, int32_t n_split,
-                                                    float* __restrict__ ws_o,
-                                                    float* __restrict__ ws_ml) {
-    __shared__ float qs[kHeads][kHeadDim];
-    __shared__ float Ks[kAttnChunk][kHeadDim + 1];
-    __shared__ float Vs[kAttnChunk][kHeadDim];
-    __shared__ float P[kHeads][kAttnChunk];
-    __shared__ int valid[kAttnChunk];
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return (uint32_t)f_to_bf16(a) | ((uint32_t)f_to_bf16(b) << 16);
+}
 
-    const int qi = blockIdx.y, split = blockIdx.x, tid = threadIdx.x;
+struct WaveTile {
+    uint16_t vt[kHeadDim][kVtStride];  // V^T of the wave's 32 entries (bf16 bits)
+    float sk[kBlk][4];                 // K scale of each 32-dim block
+    float sv[kBlk][4];                 // V scale of each 32-dim block
+    int valid[kBlk];
+};
+
+struct AttnLds {
+    union {
+        WaveTile w[kWaves];
+        float obuf[kWaves][kHeads][kHeadDim + 4];  // after the V^T tiles are consumed
+    } u;
+    float m[kWaves][kHeads];
+    float l[kWaves][kHeads];
+    int last;
+};
+
+// grid: (n_chunk, nq), kThreads threads.
+__global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint16_t* __restrict__ q,
+                                                         const int32_t* __restrict__ q_pos,
+                                                         const int32_t* __restrict__ q_seq,
+                                                         const int32_t* __restrict__ sel, int32_t k,
+                                                         LocalView loc, float sm_scale,
+                                                         int32_t n_chunk, float* __restrict__ ws_o,
+                                                         float* __restrict__ ws_ml,
+                                                         uint32_t* __restrict__ ctr,
+                                                         uint16_t* __restrict__ out) {
+    __shared__ AttnLds sh;
+
+    const int qi = blockIdx.y, chunk = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n16 = lane & 15, g = lane >> 4;
+    WaveTile& W = sh.u.w[wave];
+
     const int32_t seq = q_seq ? q_seq[qi] : qi;
     int64_t t = q_pos[qi];
     if (seq < 0 || seq >= c.n_seq) t = -1;
@@ -72,133 +116,267 @@ __global__ __launch_bounds__(256) void k_attn_split(CacheView c, const uint16_t*
     if (w0 < 0) w0 = 0;
     const int64_t nw = (loc.window > 0 && t >= w0) ? t - w0 + 1 : 0;
 
-    // Main Q of this query -> LDS
+    // Q^T as the B operand of S: head n16, dims 32 kb + 8 g .. +8 at step kb
+    bf16x8_t qf[4];
     {
-        const uint16_t* qrow = q + (int64_t)qi * kHeads * kHeadDim;
-        const uint4 w = reinterpret_cast<const uint4*>(qrow)[tid];
-        float* d = &qs[0][0] + tid * 8;
-        d[0] = bf16_lo(w.x); d[1] = bf16_hi(w.x); d[2] = bf16_lo(w.y); d[3] = bf16_hi(w.y);
-        d[4] = bf16_lo(w.z); d[5] = bf16_hi(w.z); d[6] = bf16_lo(w.w); d[7] = bf16_hi(w.w);
+        const uint4* qr = reinterpret_cast<const uint4*>(q + ((int64_t)qi * kHeads + n16) * kHeadDim);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const uint4 v = qr[4 * kb + g];
+            qf[kb] = as_bf16x8(v.x, v.y, v.z, v.w);
+        }
     }
-    // Gather + dequantise: thread -> (entry e, 32-channel part p) of K and V
-    {
-        const int e = tid >> 2, p = tid & 3;
-        const int64_t ge = (int64_t)split * kAttnChunk + e;
-        float kv[32], vv[32];
-        bool ok = false;
+
+    // ---- gather: this lane loads entry (tile tau, row n16) of the wave
+    bf16x8_t kf[2][4];
+    const int64_t e_base = (int64_t)chunk * kWgEntries + wave * kBlk;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+        const int eslot = tau * 16 + n16;
+        const int64_t ge = e_base + eslot;
+        int kind = 0;  // 0 none, 1 global FP4, 2 global bf16, 3 local bf16
+        int64_t row = 0;
         if (ge < k) {
             const int64_t j = sel[(int64_t)qi * k + ge];
             if (j >= 0 && j <= t) {
-                ok = true;
-                const int64_t row = (int64_t)seq * c.t_cap + j;
-                if (c.fp4) {
-                    const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row * kRowCodes;
-                    const uint8_t* sr = c.scales + row * kRowScales;
-                    fp4x32(cr + 16 * p, sr[p], kv);
-                    fp4x32(cr + 64 + 16 * p, sr[4 + p], vv);
-                } else {
-                    const uint16_t* br = static_cast<const uint16_t*>(c.data) + row * kRowBf16;
-                    bf16x32(br + 32 * p, kv);
-                    bf16x32(br + kHeadDim + 32 * p, vv);
-                }
+                kind = c.fp4 ? 1 : 2;
+                row = (int64_t)seq * c.t_cap + j;
             }
         } else if (ge - k < nw) {
-            ok = true;
-            const int64_t pos = w0 + (ge - k);
-            const int64_t slot = (int64_t)seq * loc.cap + pos % loc.cap;
-            bf16x32(loc.k + slot * kHeadDim + 32 * p, kv);
-            bf16x32(loc.v + slot * kHeadDim + 32 * p, vv);
+            kind = 3;
+            row = (int64_t)seq * loc.cap + (w0 + (ge - k)) % loc.cap;
         }
-        if (!ok) {
+        uint32_t vb[16];
+        float skv[4] = {1.f, 1.f, 1.f, 1.f}, svv[4] = {1.f, 1.f, 1.f, 1.f};
+        if (kind == 1) {
+            const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row * kRowCodes;
+            const uint32_t* kw = reinterpret_cast<const uint32_t*>(cr);
+            uint32_t kd[4];
 #pragma unroll
-            for (int i = 0; i < 32; ++i) kv[i] = vv[i] = 0.f;
+            for (int kb = 0; kb < 4; ++kb) kd[kb] = kw[4 * kb + g];  // dims 32kb + 8g .. +8
+            const uint4 vv = *reinterpret_cast<const uint4*>(cr + 64 + 16 * g);  // dims 32g .. +32
+            const uint2 sc = *reinterpret_cast<const uint2*>(c.scales + row * kRowScales);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                uint32_t o[4];
+                fp4x8_bf16(kd[kb], o);
+                kf[tau][kb] = as_bf16x8(o[0], o[1], o[2], o[3]);
+            }
+            fp4x8_bf16(vv.x, vb + 0);
+            fp4x8_bf16(vv.y, vb + 4);
+            fp4x8_bf16(vv.z, vb + 8);
+            fp4x8_bf16(vv.w, vb + 12);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                skv[b] = e8m0_value((sc.x >> (8 * b)) & 0xFFu);
+                svv[b] = e8m0_value((sc.y >> (8 * b)) & 0xFFu);
+            }
+        } else if (kind >= 2) {
+            const uint16_t* kr;
+            const uint16_t* vr;
+            if (kind == 2) {
+                kr = static_cast<const uint16_t*>(c.data) + row * kRowBf16;
+                vr = kr + kHeadDim;
+            } else {
+                kr = loc.k + row * kHeadDim;
+                vr = loc.v + row * kHeadDim;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const uint4 v = *reinterpret_cast<const uint4*>(kr + 32 * kb + 8 * g);
+                kf[tau][kb] = as_bf16x8(v.x, v.y, v.z, v.w);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 v = *reinterpret_cast<const uint4*>(vr + 32 * g + 8 * i);
+                vb[4 * i + 0] = v.x;
+                vb[4 * i + 1] = v.y;
+                vb[4 * i + 2] = v.z;
+                vb[4 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) kf[tau][kb] = as_bf16x8(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) vb[i] = 0u;
         }
+        // V^T tile: dims 32 g + j of entry eslot
 #pragma unroll
-        for (int i = 0; i < 32; ++i) Ks[e][32 * p + i] = kv[i];
-        store32(&Vs[e][32 * p], vv);
-        if (p == 0) valid[e] = ok;
+        for (int i = 0; i < 16; ++i) {
+            W.vt[32 * g + 2 * i][eslot] = (uint16_t)(vb[i] & 0xFFFFu);
+            W.vt[32 * g + 2 * i + 1][eslot] = (uint16_t)(vb[i] >> 16);
+        }
+        if (g == 0) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                W.sk[eslot][b] = skv[b];
+                W.sv[eslot][b] = svv[b];
+            }
+            W.valid[eslot] = kind != 0;
+        }
     }
     __syncthreads();
 
-    // Logits and chunk softmax: wave hg owns heads 4hg..4hg+3, lane = entry.
-    const int lane = tid & 63, hg = tid >> 6;
+    // ---- S^T = K Q^T: lane holds head n16, entries 4g + r of each tile
     const float zs = sm_scale * kLog2e;
-    float z[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int d = 0; d < kHeadDim; ++d) {
-        const float kd = Ks[lane][d];
+    float s[2][4];
+    bool ok[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = fmaf(qs[4 * hg + i][d], kd, z[i]);
-    }
-    const bool ok = valid[lane];
-    float mh[4], lh[4];
+    for (int tau = 0; tau < 2; ++tau) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float zi = ok ? z[i] * zs : -__builtin_inff();
-        float m = zi;
+        for (int kb = 0; kb < 4; ++kb) {
+            f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tau][kb], qf[kb], z, 0, 0, 0);
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        const float pi = (ok && m != -__builtin_inff()) ? exp2f(zi - m) : 0.f;
-        float l = pi;
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(z[r], W.sk[tau * 16 + 4 * g + r][kb], acc[r]);
+        }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
-        P[4 * hg + i][lane] = pi;
-        mh[i] = m;
-        lh[i] = l;
-    }
-    if (lane == 0) {
-        float* ml = ws_ml + (((int64_t)qi * n_split + split) * kHeads + 4 * hg) * 2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ml[2 * i] = mh[i];
-            ml[2 * i + 1] = lh[i];
+        for (int r = 0; r < 4; ++r) {
+            ok[tau][r] = W.valid[tau * 16 + 4 * g + r] != 0;
+            s[tau][r] = ok[tau][r] ? acc[r] * zs : -__builtin_inff();
         }
     }
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, s[tau][r]);
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float p[2][4];
+    float lsum = 0.f;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p[tau][r] = (ok[tau][r] && m != -__builtin_inff()) ? exp2f(s[tau][r] - m) : 0.f;
+            lsum += p[tau][r];
+        }
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (g == 0) {
+        sh.m[wave][n16] = m;
+        sh.l[wave][n16] = lsum;
+    }
+
+    // ---- O = P V: A = P (head n16, entry slots 8g + j), one variant per V block
+    bf16x8_t pf[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            v[r] = p[0][r] * W.sv[4 * g + r][b];
+            v[4 + r] = p[1][r] * W.sv[16 + 4 * g + r][b];
+        }
+        pf[b] = as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+    f32x4_t o[8];
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8) {
+        const uint16_t* vr = &W.vt[16 * t8 + n16][0];
+        const uint2 a = *reinterpret_cast<const uint2*>(vr + 4 * g);
+        const uint2 b2 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
+        const bf16x8_t vf = as_bf16x8(a.x, a.y, b2.x, b2.y);
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[t8 >> 1], vf, z, 0, 0, 0);
+    }
+    __syncthreads();  // every wave is done with its V^T tile
+    // O tile: lane holds dim 16 t8 + n16, heads 4 g + r
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sh.u.obuf[wave][4 * g + r][16 * t8 + n16] = o[t8][r];
     __syncthreads();
 
-    // P.V: thread -> channel d, heads 8hh..8hh+7
-    const int d = tid & 127, hh = tid >> 7;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int e = 0; e < kAttnChunk; ++e) {
-        const float v = Vs[e][d];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(P[8 * hh + i][e], v, acc[i]);
-    }
-    float* o = ws_o + (((int64_t)qi * n_split + split) * kHeads + 8 * hh) * kHeadDim + d;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i * kHeadDim] = acc[i];
-}
-
-// grid: (8, nq), 256 threads: two heads per workgroup, one channel per thread.
-__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ ws_o,
-                                                    const float* __restrict__ ws_ml,
-                                                    int32_t n_split, uint16_t* __restrict__ out) {
-    const int qi = blockIdx.y, h = blockIdx.x * 2 + (threadIdx.x >> 7), d = threadIdx.x & 127;
-    const float* ml = ws_ml + (int64_t)qi * n_split * kHeads * 2;
+    // ---- combine the waves: thread -> head h, 4 dims
+    const int h = tid >> 5, d0 = (tid & 31) * 4;
     float M = -__builtin_inff();
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[(s * kHeads + h) * 2]);
-    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.m[w][h]);
+    float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (M != -__builtin_inff()) {
-        for (int s = 0; s < n_split; ++s) {
-            const float m = ml[(s * kHeads + h) * 2];
-            if (m == -__builtin_inff()) continue;
-            const float f = exp2f(m - M);
-            L = fmaf(ml[(s * kHeads + h) * 2 + 1], f, L);
-            O = fmaf(ws_o[(((int64_t)qi * n_split + s) * kHeads + h) * kHeadDim + d], f, O);
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = sh.m[w][h];
+            const float f = (mw == -__builtin_inff()) ? 0.f : exp2f(mw - M);
+            L = fmaf(sh.l[w][h], f, L);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fmaf(sh.u.obuf[w][h][d0 + i], f, acc[i]);
         }
     }
-    const float r = L > 0.f ? O / L : 0.f;
-    out[((int64_t)qi * kHeads + h) * kHeadDim + d] = f_to_bf16(r);
+    uint16_t* orow = out + ((int64_t)qi * kHeads + h) * kHeadDim + d0;
+    if (n_chunk == 1) {  // the whole query in one workgroup
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        *reinterpret_cast<uint2*>(orow) =
+            make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+        return;
+    }
+    const int64_t part0 = (int64_t)qi * n_chunk;
+    *reinterpret_cast<float4*>(ws_o + ((part0 + chunk) * kHeads + h) * kHeadDim + d0) =
+        make_float4(acc[0], acc[1], acc[2], acc[3]);
+    if ((tid & 31) == 0)
+        *reinterpret_cast<float2*>(ws_ml + ((part0 + chunk) * kHeads + h) * 2) = make_float2(M, L);
+    __syncthreads();  // the workgroup's stores are ordered before thread 0's release
+    if (tid == 0) {
+        __threadfence();
+        sh.last = atomicAdd(&ctr[qi], 1u) == (uint32_t)(n_chunk - 1);
+    }
+    __syncthreads();
+    if (!sh.last) return;
+    if (tid == 0) __threadfence();  // acquire for the whole workgroup
+    __syncthreads();
+    // ---- the last chunk of the query merges all chunks in order
+    float Mq = -__builtin_inff();
+    for (int j0 = 0; j0 < n_chunk; j0 += 16) {
+        float mv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            mv[u] = (j0 + u < n_chunk) ? ws_ml[((part0 + j0 + u) * kHeads + h) * 2] : -__builtin_inff();
+#pragma unroll
+        for (int u = 0; u < 16; ++u) Mq = fmaxf(Mq, mv[u]);
+    }
+    float Lq = 0.f, aq[4] = {0.f, 0.f, 0.f, 0.f};
+    if (Mq != -__builtin_inff()) {
+        for (int j0 = 0; j0 < n_chunk; j0 += 8) {
+            float2 ml[8];
+            float4 ov[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t pj = part0 + j0 + u;
+                const bool in = j0 + u < n_chunk;
+                ml[u] = in ? *reinterpret_cast<const float2*>(ws_ml + (pj * kHeads + h) * 2)
+                           : make_float2(-__builtin_inff(), 0.f);
+                ov[u] = in ? *reinterpret_cast<const float4*>(ws_o + (pj * kHeads + h) * kHeadDim + d0)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float f = (ml[u].x == -__builtin_inff()) ? 0.f : exp2f(ml[u].x - Mq);
+                Lq = fmaf(ml[u].y, f, Lq);
+                aq[0] = fmaf(ov[u].x, f, aq[0]);
+                aq[1] = fmaf(ov[u].y, f, aq[1]);
+                aq[2] = fmaf(ov[u].z, f, aq[2]);
+                aq[3] = fmaf(ov[u].w, f, aq[3]);
+            }
+        }
+    }
+    const float inv = Lq > 0.f ? 1.f / Lq : 0.f;
+    *reinterpret_cast<uint2*>(orow) =
+        make_uint2(pack_bf16x2(aq[0] * inv, aq[1] * inv), pack_bf16x2(aq[2] * inv, aq[3] * inv));
+    if (tid == 0) ctr[qi] = 0u;  // ready for the next call
 }
 
-static int32_t attn_splits(int32_t k, int32_t window) {
-    return (k + window + kAttnChunk - 1) / kAttnChunk;
+static int32_t attn_chunks(int32_t k, int32_t window) {
+    return (k + window + kWgEntries - 1) / kWgEntries;
 }
 
 size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window) {
-    const int64_t ns = attn_splits(k, window);
-    return (size_t)nq * ns * kHeads * (kHeadDim + 2) * sizeof(float);
+    const int64_t nc = attn_chunks(k, window);
+    if (nc <= 1) return 0;
+    return (size_t)nq * nc * kHeads * (kHeadDim + 2) * sizeof(float) + (size_t)nq * sizeof(uint32_t);
 }
 
 hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
@@ -206,13 +384,13 @@ hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32
                               const LocalView& loc, float sm_scale, uint16_t* out, void* ws,
                               hipStream_t s) {
     if (nq == 0) return hipSuccess;
-    const int32_t ns = attn_splits(k, loc.window);
+    int32_t nc = attn_chunks(k, loc.window);
+    if (nc < 1) nc = 1;
     float* ws_o = static_cast<float*>(ws);
-    float* ws_ml = ws_o + (size_t)nq * ns * kHeads * kHeadDim;
-    if (ns > 0)
-        hipLaunchKernelGGL(k_attn_split, dim3((uint32_t)ns, (uint32_t)nq), dim3(256), 0, s, c, q,
-                           q_pos, q_seq, sel, k, loc, sm_scale, ns, ws_o, ws_ml);
-    hipLaunchKernelGGL(k_attn_merge, dim3(8, (uint32_t)nq), dim3(256), 0, s, ws_o, ws_ml, ns, out);
+    float* ws_ml = nc > 1 ? ws_o + (size_t)nq * nc * kHeads * kHeadDim : nullptr;
+    uint32_t* ctr = nc > 1 ? reinterpret_cast<uint32_t*>(ws_ml + (size_t)nq * nc * kHeads * 2) : nullptr;
+    hipLaunchKernelGGL(k_attn_chunk, dim3((uint32_t)nc, (uint32_t)nq), dim3(kThreads), 0, s, c, q,
+                       q_pos, q_seq, sel, k, loc, sm_scale, nc, ws_o, ws_ml, ctr, out);
     return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@
 // eight partial dots are summed with three lane exchanges.
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
+#include "csa2_select.h"
 
 namespace csa2 {
 
@@ -140,6 +141,89 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__
     const int64_t c = base + sub * 8 + grp;
     const float v = pick8(s, sub);
     if (c < n_cand) srow[c] = v;
+}
+
+// Candidate scoring fused with the selection among the candidates, for the
+// Reindex layers (rescore the Full layer's pool with the layer's own indexer
+// query and keep the top k, "What Full, Reindex, and Reuse Share", Fig. 5).
+// grid: (ceil(n_cand / 256), nq).  Every workgroup scores 256 candidates into
+// `scores`; the last one of a query to finish (per-query counter `ctr`, reset
+// on exit) selects the top k of all n_cand <= kSelMaxCand candidates in LDS.
+constexpr int kSelMaxCand = 16384;
+
+__global__ __launch_bounds__(256) void k_score_select(const uint16_t* __restrict__ k_idx,
+                                                      int32_t n_seq, int64_t t_cap,
+                                                      const uint16_t* __restrict__ q_idx,
+                                                      const int32_t* __restrict__ q_pos,
+                                                      const int32_t* __restrict__ q_seq,
+                                                      const int32_t* __restrict__ cand,
+                                                      int64_t n_cand, float* __restrict__ scores,
+                                                      uint32_t* __restrict__ ctr, int32_t k,
+                                                      int32_t* __restrict__ sel) {
+    __shared__ uint32_t keys[kSelMaxCand];
+    __shared__ int hist[256];
+    __shared__ int wtmp[2 * 256 / 64];
+    __shared__ int res[4];
+    __shared__ int last;
+    const int qi = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane & 7, grp = lane >> 3;
+    const int64_t base = (int64_t)blockIdx.x * kScoreTile + wave * 64;
+    float* srow = scores + (int64_t)qi * n_cand;
+    const int32_t* crow = cand + (int64_t)qi * n_cand;
+    const int32_t seq = q_seq ? q_seq[qi] : qi;
+    int64_t t = q_pos[qi];
+    if (seq < 0 || seq >= n_seq) t = -1;
+    if (t >= t_cap) t = t_cap - 1;
+    if (base < n_cand) {
+        float qf[8];
+        load_q8(q_idx + (int64_t)qi * kIdxDim + sub * 8, qf);
+        const uint4* kb =
+            reinterpret_cast<const uint4*>(k_idx) + (int64_t)(seq < 0 ? 0 : seq) * t_cap * 8;
+        uint4 kv[8];
+        bool ok[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int64_t c = base + r * 8 + grp;
+            const int64_t tok = (c < n_cand) ? crow[c] : -1;
+            ok[r] = tok >= 0 && tok <= t;
+            kv[r] = ok[r] ? kb[tok * 8 + sub] : make_uint4(0, 0, 0, 0);
+        }
+        float sc[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) sc[r] = ok[r] ? sum8(dot8(qf, kv[r])) : -__builtin_inff();
+        const int64_t c = base + sub * 8 + grp;
+        if (c < n_cand) srow[c] = pick8(sc, sub);
+    }
+    __syncthreads();  // the workgroup's stores are ordered before thread 0's release
+    if (threadIdx.x == 0) {
+        __threadfence();
+        last = atomicAdd(&ctr[qi], 1u) == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    if (threadIdx.x == 0) __threadfence();  // acquire for the whole workgroup
+    __syncthreads();
+    stage_keys<256>(srow, crow, n_cand, keys);
+    __syncthreads();
+    uint32_t tau;
+    int need;
+    lds_kth<256>(keys, (int)n_cand, k, 0, hist, res, tau, need);
+    ordered_write<256>([&](int64_t i) { return keys[i]; }, n_cand, tau, need, crow, k,
+                       sel + (int64_t)qi * k, wtmp);
+    if (threadIdx.x == 0) ctr[qi] = 0u;
+}
+
+hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
+                               const int32_t* q_seq, int32_t nq, const int32_t* cand,
+                               int64_t n_cand, float* scores, uint32_t* ctr, int32_t k,
+                               int32_t* sel, hipStream_t s) {
+    if (nq == 0 || n_cand == 0) return hipSuccess;
+    if (n_cand > kSelMaxCand) return hipErrorInvalidValue;
+    dim3 grid((uint32_t)((n_cand + kScoreTile - 1) / kScoreTile), (uint32_t)nq);
+    hipLaunchKernelGGL(k_score_select, grid, dim3(256), 0, s, c.k_idx, c.n_seq, c.t_cap, q_idx,
+                       q_pos, q_seq, cand, n_cand, scores, ctr, k, sel);
+    return hipGetLastError();
 }
 
 hipError_t launch_score_dense(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,

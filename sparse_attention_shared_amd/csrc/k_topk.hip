@@ -1,141 +1,464 @@
 // k_topk.hip -- top-k selection of indexer scores ("CED: Continuing Context with
 // a Causal Encoder and Decoder", section "Selecting Positions and Reading
 // Values with Attention", Fig. 4: the indexer keeps the positions with the
-// highest scores), with the Full layer's wider candidate pool from the same
-// ranking (section "What Full, Reindex, and Reuse Share", Fig. 5).
+// highest scores), with the Full layer's wider candidate pool taken from the
+// same ranking (section "What Full, Reindex, and Reuse Share", Fig. 5).
 //
 // Order: higher score first, equal scores by lower slot.  Scores become
-// order-preserving 32-bit keys; an exact radix select (four 8-bit digits, most
-// significant first) finds the k-th key tau and how many keys equal to tau
-// are taken; an ordered compaction then writes the chosen slots ascending.
-// One 1024-thread workgroup per row; rows of up to 32768 slots keep their keys
-// in LDS, longer rows re-read their scores for each pass.
+// order-preserving 32-bit keys (key 0 = not selectable).  A selection is the
+// pair (tau, need): every key > tau is chosen, plus the first `need` keys equal
+// to tau in slot order; an ordered compaction then writes the chosen slots
+// ascending.  tau is found by an exact radix select on 12 + 12 + 8 bit digits
+// that stops as soon as a whole bucket is taken.
+//
+// Short rows (<= 32768 slots): one 1024-thread workgroup per row, keys in LDS.
+// Long rows: three multi-workgroup kernels per row set --
+//   hist:  12-bit histogram of the top digit (LDS, then device atomics); the
+//          last workgroup of a row picks the boundary bucket of each target;
+//   cand:  every chunk counts its keys above the bucket and appends the keys of
+//          the bucket to a small candidate list; the last workgroup resolves
+//          (tau, need) exactly on the candidates and turns per-chunk counts
+//          into output offsets;
+//   write: each chunk writes its chosen slots at its offset, in order.
+// The workspace's counters and histogram reset themselves, so it must be
+// zero-filled before its first use and is left zero-filled by every call.
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
+#include "csa2_select.h"
 
 namespace csa2 {
 
-constexpr int kTkThreads = 1024;
-constexpr int kTkLdsKeys = 32768;
+constexpr int kSmallNT = 1024;
+constexpr int kSmallMax = 32768;  // slots kept in LDS by the one-workgroup path
+constexpr int kLongNT = 512;
+constexpr int kChunk = 8192;      // slots per workgroup on the long path
+constexpr int kCandCap = 4096;    // candidates per row and target
+constexpr int kMaxTargets = 2;
 
-struct RowKeys {
-    const float* s;
-    const int32_t* ids;
-    const uint32_t* lds;  // non-null: keys already staged in LDS
-    __device__ __forceinline__ uint32_t from_global(int64_t i) const {
-        if (ids && ids[i] < 0) return 0u;
-        const uint32_t k = score_key(s[i]);
-        return k == kNegInfKey ? 0u : k;
-    }
-    __device__ __forceinline__ uint32_t operator()(int64_t i) const {
-        return lds ? lds[i] : from_global(i);
-    }
-};
-
-struct TkShared {
-    int hist[256];
-    int scan[kTkThreads / 64 + 1];
-    uint32_t bucket;
-    int above;
-};
-
-// Writes the first kk slots of the row under the order (ascending slots,
-// mapped through ids, -1 padded) to dst.
-__device__ void select_row(const RowKeys& K, int64_t n, int n_valid, const int32_t* ids,
-                           int32_t kk, int32_t* dst, TkShared& sh) {
-    const int tid = threadIdx.x;
-    uint32_t tau = 0;
-    int need = 0;
-    if (n_valid > kk) {
-        uint32_t prefix = 0, mask = 0;
-        int rem = kk;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            if (tid < 256) sh.hist[tid] = 0;
-            __syncthreads();
-            for (int64_t i = tid; i < n; i += kTkThreads) {
-                const uint32_t key = K(i);
-                if (key && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1);
-            }
-            __syncthreads();
-            const int v = tid < 256 ? sh.hist[255 - tid] : 0;
-            int tot;
-            const int ex = block_excl_scan<kTkThreads>(v, sh.scan, &tot);
-            if (tid < 256 && ex < rem && ex + v >= rem) {
-                sh.bucket = 255u - (uint32_t)tid;
-                sh.above = ex;
-            }
-            __syncthreads();
-            prefix |= sh.bucket << shift;
-            mask |= 0xFFu << shift;
-            rem -= sh.above;
-            __syncthreads();
-        }
-        tau = prefix;
-        need = rem;
-    }
-    // ordered compaction over contiguous per-thread chunks
-    const int64_t chunk = (n + kTkThreads - 1) / kTkThreads;
-    const int64_t i0 = min(n, (int64_t)tid * chunk), i1 = min(n, i0 + chunk);
-    int gt = 0, eq = 0;
-    for (int64_t i = i0; i < i1; ++i) {
-        const uint32_t key = K(i);
-        gt += key > tau;
-        eq += key == tau;
-    }
-    int tot;
-    const int eq_before = block_excl_scan<kTkThreads>(eq, sh.scan, &tot);
-    const int take_eq = min(max(need - eq_before, 0), eq);
-    int total;
-    int off = block_excl_scan<kTkThreads>(gt + take_eq, sh.scan, &total);
-    int e = eq_before;
-    for (int64_t i = i0; i < i1; ++i) {
-        const uint32_t key = K(i);
-        bool take = key > tau;
-        if (key == tau) {
-            take = e < need;
-            ++e;
-        }
-        if (take && off < kk) dst[off++] = ids ? ids[i] : (int32_t)i;
-    }
-    for (int i = total + tid; i < kk; i += kTkThreads) dst[i] = -1;
-    __syncthreads();
-}
-
-template <bool IN_LDS>
-__global__ __launch_bounds__(kTkThreads) void k_topk(const float* __restrict__ scores, int64_t n,
-                                                     int64_t ld, const int32_t* __restrict__ ids,
-                                                     int32_t k, int32_t* __restrict__ out,
-                                                     int32_t k2, int32_t* __restrict__ out2) {
-    __shared__ TkShared sh;
-    __shared__ uint32_t keys[IN_LDS ? kTkLdsKeys : 1];
+// ---------------------------------------------------------------- short rows
+__global__ __launch_bounds__(kSmallNT) void k_topk_small(const float* __restrict__ scores,
+                                                         int64_t n, int64_t ld,
+                                                         const int32_t* __restrict__ ids,
+                                                         int32_t k, int32_t* __restrict__ out,
+                                                         int32_t k2, int32_t* __restrict__ out2) {
+    __shared__ uint32_t keys[kSmallMax];
+    __shared__ int hist[256];
+    __shared__ int wtmp[2 * kSmallNT / 64];
+    __shared__ int res[4];
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
-    RowKeys K{scores + row * ld, ids ? ids + row * n : nullptr, nullptr};
-    int nv = 0;
-    for (int64_t i = tid; i < n; i += kTkThreads) {
-        const uint32_t key = K.from_global(i);
-        if (IN_LDS) keys[i] = key;
-        nv += key != 0u;
-    }
-    if (IN_LDS) K.lds = keys;
-    int n_valid;
-    block_excl_scan<kTkThreads>(nv, sh.scan, &n_valid);
+    const float* s = scores + row * ld;
     const int32_t* irow = ids ? ids + row * n : nullptr;
-    select_row(K, n, n_valid, irow, k, out + row * k, sh);
-    if (out2) select_row(K, n, n_valid, irow, k2, out2 + row * k2, sh);
+    stage_keys<kSmallNT>(s, irow, n, keys);
+    __syncthreads();
+    auto K = [&](int64_t i) { return keys[i]; };
+    for (int t = 0; t < 2; ++t) {
+        const int32_t kk = t ? k2 : k;
+        int32_t* dst = t ? (out2 ? out2 + row * k2 : nullptr) : out + row * k;
+        if (!dst || kk <= 0) continue;
+        uint32_t tau;
+        int need;
+        lds_kth<kSmallNT>(keys, (int)n, kk, 0, hist, res, tau, need);
+        ordered_write<kSmallNT>(K, n, tau, need, irow, kk, dst, wtmp);
+    }
 }
 
-size_t topk_ws_bytes(int32_t, int64_t, int32_t, int32_t) { return 0; }
+// ----------------------------------------------------------------- long rows
+// Per-row workspace of the long path.
+struct RowState {
+    uint32_t hist[kHistBins];
+    uint32_t ctr_hist, ctr_cand;
+    uint32_t bucket[kMaxTargets];  // top digit of the boundary bucket
+    int32_t rem[kMaxTargets];      // rank still needed inside that bucket
+    uint32_t ncand[kMaxTargets];
+    uint32_t tau[kMaxTargets];
+    int32_t need[kMaxTargets];
+    int32_t total[kMaxTargets];
+    int32_t pad[2];
+};
+struct Cand {
+    uint32_t key;
+    int32_t slot;
+};
+// chunk records: [row][target][chunk] {above-bucket count, output offset, tau-equal keys before}
+struct ChunkRec {
+    int32_t gt, off, eq_before, pad;
+};
+
+struct LongWs {
+    RowState* st;   // [nq]
+    Cand* cand;     // [nq][targets][kCandCap]
+    ChunkRec* rec;  // [nq][targets][n_chunk]
+};
+
+__device__ __forceinline__ int64_t chunk_begin(int c) { return (int64_t)c * kChunk; }
+
+// grid (n_chunk, nq)
+__global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__ scores, int64_t n,
+                                                       int64_t ld, const int32_t* __restrict__ ids,
+                                                       int32_t k, int32_t k2, LongWs ws) {
+    __shared__ int hist[kHistBins];
+    __shared__ int tmp[kLongNT / 64 + 1];
+    __shared__ int last;
+    const int c = blockIdx.x, nc = gridDim.x;
+    const int64_t row = blockIdx.y;
+    const int tid = threadIdx.x;
+    const float* s = scores + row * ld;
+    const int32_t* irow = ids ? ids + row * n : nullptr;
+    RowState* st = ws.st + row;
+    for (int i = tid; i < kHistBins; i += kLongNT) hist[i] = 0;
+    __syncthreads();
+    constexpr int kPer = kChunk / kLongNT;
+    const int64_t b0 = chunk_begin(c);
+    uint32_t kr[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int64_t i = b0 + tid + (int64_t)j * kLongNT;
+        kr[j] = i < n ? load_key(s, irow, i) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        if (kr[j]) atomicAdd(&hist[kr[j] >> 20], 1);
+    __syncthreads();
+    for (int i = tid; i < kHistBins; i += kLongNT)
+        if (hist[i]) atomicAdd(&st->hist[i], (uint32_t)hist[i]);
+    __syncthreads();  // the workgroup's stores are ordered before thread 0's release
+    if (tid == 0) {
+        __threadfence();
+        last = atomicAdd(&st->ctr_hist, 1u) == (uint32_t)(nc - 1);
+    }
+    __syncthreads();
+    if (!last) return;
+    if (tid == 0) __threadfence();  // acquire for the whole workgroup
+    __syncthreads();
+    // the last workgroup of the row: boundary bucket of each target
+    {
+        constexpr int kB = kHistBins / kLongNT;
+        uint32_t hv[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+            hv[u] = __hip_atomic_load(&st->hist[tid + u * kLongNT], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            hist[tid + u * kLongNT] = (int)hv[u];
+            st->hist[tid + u * kLongNT] = 0u;
+        }
+    }
+    __syncthreads();
+    constexpr int per = kHistBins / kLongNT;
+    const int hi = kHistBins - tid * per, lo = hi - per;
+    int mine = 0;
+    for (int b = hi - 1; b >= lo; --b) mine += hist[b];
+    int total;
+    const int before = block_excl_scan<kLongNT>(mine, tmp, &total);
+    for (int t = 0; t < kMaxTargets; ++t) {
+        const int kk = t ? k2 : k;
+        if (kk <= 0) continue;
+        if (total <= kk) {  // every selectable key is taken
+            if (tid == 0) {
+                st->bucket[t] = 0u;
+                st->rem[t] = -1;
+            }
+            continue;
+        }
+        if (before < kk && before + mine >= kk) {
+            int acc = before;
+            for (int b = hi - 1; b >= lo; --b) {
+                if (acc + hist[b] >= kk) {
+                    st->bucket[t] = (uint32_t)b;
+                    st->rem[t] = kk - acc;
+                    break;
+                }
+                acc += hist[b];
+            }
+        }
+    }
+    if (tid == 0) st->ctr_hist = 0u;
+}
+
+// grid (n_chunk, nq)
+__global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__ scores, int64_t n,
+                                                       int64_t ld, const int32_t* __restrict__ ids,
+                                                       int32_t k, int32_t k2, LongWs ws) {
+    __shared__ uint32_t ckeys[kCandCap];
+    __shared__ int32_t cslot[kCandCap];
+    __shared__ int hist[kHistBins];
+    __shared__ int tmp[kLongNT / 64 + 1];
+    __shared__ int res[4];
+    __shared__ int cnt_gt[kMaxTargets], cnt_cand[kMaxTargets], cbase[kMaxTargets];
+    __shared__ int last;
+    const int c = blockIdx.x, nc = gridDim.x;
+    const int64_t row = blockIdx.y;
+    const int tid = threadIdx.x;
+    const float* s = scores + row * ld;
+    const int32_t* irow = ids ? ids + row * n : nullptr;
+    RowState* st = ws.st + row;
+    const int nt = k2 > 0 ? 2 : 1;
+    uint32_t bucket[kMaxTargets];
+    int rem[kMaxTargets];
+    for (int t = 0; t < nt; ++t) {
+        bucket[t] = st->bucket[t];
+        rem[t] = st->rem[t];
+    }
+    if (tid < kMaxTargets) {
+        cnt_gt[tid] = 0;
+        cnt_cand[tid] = 0;
+    }
+    __syncthreads();
+    // this chunk's keys stay in registers for the two passes below
+    constexpr int kPer = kChunk / kLongNT;
+    const int64_t b0 = chunk_begin(c);
+    uint32_t kr[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int64_t i = b0 + tid + (int64_t)j * kLongNT;
+        kr[j] = i < n ? load_key(s, irow, i) : 0u;
+    }
+    int gt[kMaxTargets] = {0, 0}, nca[kMaxTargets] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const uint32_t key = kr[j];
+        if (!key) continue;
+        const uint32_t d = key >> 20;
+        for (int t = 0; t < nt; ++t) {
+            if (rem[t] < 0 || d > bucket[t]) gt[t] += 1;
+            else if (d == bucket[t]) nca[t] += 1;
+        }
+    }
+    for (int t = 0; t < nt; ++t) {
+        if (nca[t]) atomicAdd(&cnt_cand[t], nca[t]);
+    }
+    __syncthreads();
+    if (tid < nt) {
+        // one device atomic per chunk reserves its range of the candidate list
+        cbase[tid] = (int)atomicAdd(&st->ncand[tid], (uint32_t)cnt_cand[tid]);
+        cnt_cand[tid] = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const uint32_t key = kr[j];
+        if (!key) continue;
+        const uint32_t d = key >> 20;
+        for (int t = 0; t < nt; ++t) {
+            if (rem[t] >= 0 && d == bucket[t]) {
+                const int pos = cbase[t] + atomicAdd(&cnt_cand[t], 1);
+                if (pos < kCandCap) {
+                    Cand* cb = ws.cand + ((int64_t)row * kMaxTargets + t) * kCandCap;
+                    cb[pos].key = key;
+                    cb[pos].slot = (int32_t)(tid + (int64_t)j * kLongNT + b0);
+                }
+            }
+        }
+    }
+    for (int t = 0; t < nt; ++t) atomicAdd(&cnt_gt[t], gt[t]);
+    __syncthreads();
+    if (tid < nt) ws.rec[((int64_t)row * kMaxTargets + tid) * nc + c].gt = cnt_gt[tid];
+    __syncthreads();  // the workgroup's stores are ordered before thread 0's release
+    if (tid == 0) {
+        __threadfence();
+        last = atomicAdd(&st->ctr_cand, 1u) == (uint32_t)(nc - 1);
+    }
+    __syncthreads();
+    if (!last) return;
+    if (tid == 0) __threadfence();  // acquire for the whole workgroup
+    __syncthreads();
+    // ---- last workgroup of the row: exact (tau, need) and chunk offsets
+    for (int t = 0; t < nt; ++t) {
+        const int kk = t ? k2 : k;
+        ChunkRec* rec = ws.rec + ((int64_t)row * kMaxTargets + t) * nc;
+        const uint32_t m = __hip_atomic_load(&st->ncand[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t tau;
+        int need;
+        bool exact = true;
+        if (rem[t] < 0) {
+            tau = 0u;  // all selectable keys
+            need = 0;
+        } else if (m <= (uint32_t)kCandCap) {
+            const Cand* cb = ws.cand + ((int64_t)row * kMaxTargets + t) * kCandCap;
+            for (int i0 = tid; i0 < (int)m; i0 += 8 * kLongNT) {
+                Cand cv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = i0 + u * kLongNT;
+                    if (i < (int)m) cv[u] = cb[i];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = i0 + u * kLongNT;
+                    if (i < (int)m) {
+                        ckeys[i] = cv[u].key;
+                        cslot[i] = cv[u].slot;
+                    }
+                }
+            }
+            __syncthreads();
+            lds_kth<kLongNT>(ckeys, (int)m, rem[t], 12, hist, res, tau, need);
+        } else {
+            exact = false;  // bucket too large for LDS: resolve below over the row
+            tau = 0u;
+            need = 0;
+        }
+        if (!exact) {
+            // Radix over the whole row (rare): prefix = bucket, three more digits.
+            uint32_t prefix = bucket[t] << 20, mask = 0xFFF00000u;
+            int r = rem[t];
+            for (int shift = 8; shift >= 0; shift -= 8) {
+                const int bits = shift == 8 ? 12 : 8;
+                const int nb = 1 << bits;
+                const uint32_t bm = (uint32_t)nb - 1u;
+                for (int i = tid; i < nb; i += kLongNT) hist[i] = 0;
+                __syncthreads();
+                for (int64_t i = tid; i < n; i += kLongNT) {
+                    const uint32_t key = load_key(s, irow, i);
+                    if (key && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & bm], 1);
+                }
+                __syncthreads();
+                if (tid == 0) {
+                    int acc = 0;
+                    for (int b = nb - 1; b >= 0; --b) {
+                        if (acc + hist[b] >= r) {
+                            res[0] = b;
+                            res[1] = acc;
+                            break;
+                        }
+                        acc += hist[b];
+                    }
+                }
+                __syncthreads();
+                prefix |= (uint32_t)res[0] << shift;
+                mask |= bm << shift;
+                r -= res[1];
+                __syncthreads();
+            }
+            tau = prefix;
+            need = r;
+        }
+        // per-chunk counts of keys > tau inside the bucket and of keys == tau
+        // (reuse hist as two int arrays of nc entries)
+        int* cgt = hist;
+        int* ceq = hist + 2048;
+        for (int i = tid; i < nc; i += kLongNT) {
+            cgt[i] = 0;
+            ceq[i] = 0;
+        }
+        __syncthreads();
+        if (rem[t] >= 0) {
+            if (exact) {
+                for (int i = tid; i < (int)m; i += kLongNT) {
+                    const int ch = cslot[i] / kChunk;
+                    if (ckeys[i] > tau) atomicAdd(&cgt[ch], 1);
+                    else if (ckeys[i] == tau && need > 0) atomicAdd(&ceq[ch], 1);
+                }
+            } else {
+                for (int64_t i = tid; i < n; i += kLongNT) {
+                    const uint32_t key = load_key(s, irow, i);
+                    if ((key >> 20) != bucket[t]) continue;
+                    if (key > tau) atomicAdd(&cgt[i / kChunk], 1);
+                    else if (key == tau && need > 0) atomicAdd(&ceq[i / kChunk], 1);
+                }
+            }
+        }
+        __syncthreads();
+        {
+            // chunk offsets: each thread owns a run of consecutive chunks
+            const int per = (nc + kLongNT - 1) / kLongNT;
+            const int c0 = min(nc, tid * per), c1 = min(nc, c0 + per);
+            int gtv[4], eqsum = 0;  // nc <= 2048 chunks: per <= 4
+#pragma unroll
+            for (int u = 0; u < 4; ++u) gtv[u] = (c0 + u < c1) ? rec[c0 + u].gt : 0;
+            for (int ch = c0; ch < c1; ++ch) eqsum += ceq[ch];
+            int tot;
+            int eqb = block_excl_scan<kLongNT>(eqsum, tmp, &tot);
+            int selsum = 0, e2 = eqb;
+            for (int ch = c0; ch < c1; ++ch) {
+                selsum += gtv[ch - c0] + cgt[ch] + min(max(need - e2, 0), ceq[ch]);
+                e2 += ceq[ch];
+            }
+            int total;
+            int off = block_excl_scan<kLongNT>(selsum, tmp, &total);
+            for (int ch = c0; ch < c1; ++ch) {
+                rec[ch].off = off;
+                rec[ch].eq_before = eqb;
+                off += gtv[ch - c0] + cgt[ch] + min(max(need - eqb, 0), ceq[ch]);
+                eqb += ceq[ch];
+            }
+            if (tid == 0) {
+                st->tau[t] = tau;
+                st->need[t] = need;
+                st->total[t] = total;
+                st->ncand[t] = 0u;
+            }
+        }
+        __syncthreads();
+    }
+    if (tid == 0) st->ctr_cand = 0u;
+}
+
+// grid (n_chunk, nq)
+__global__ __launch_bounds__(kLongNT) void k_topk_write(const float* __restrict__ scores, int64_t n,
+                                                        int64_t ld, const int32_t* __restrict__ ids,
+                                                        int32_t k, int32_t* __restrict__ out,
+                                                        int32_t k2, int32_t* __restrict__ out2,
+                                                        LongWs ws) {
+    __shared__ uint32_t keys[kChunk];
+    __shared__ int wtmp[2 * kLongNT / 64];
+    const int c = blockIdx.x, nc = gridDim.x;
+    const int64_t row = blockIdx.y;
+    const int tid = threadIdx.x;
+    const float* s = scores + row * ld;
+    const int32_t* irow = ids ? ids + row * n : nullptr;
+    const RowState* st = ws.st + row;
+    const int64_t b0 = chunk_begin(c), b1 = min(n, b0 + kChunk);
+    const int64_t len = b1 - b0;
+    stage_keys<kLongNT>(s + b0, irow ? irow + b0 : nullptr, len, keys);
+    __syncthreads();
+    const int nt = out2 ? 2 : 1;
+    for (int t = 0; t < nt; ++t) {
+        const int32_t kk = t ? k2 : k;
+        int32_t* dst = (t ? out2 + row * k2 : out + row * k);
+        const ChunkRec r = ws.rec[((int64_t)row * kMaxTargets + t) * nc + c];
+        const uint32_t tau = st->tau[t];
+        const int need = st->need[t];
+        const int32_t* ich = irow ? irow + b0 : nullptr;
+        ordered_write<kLongNT>([&](int64_t i) { return keys[i]; }, len, tau, need, ich, kk, dst,
+                               wtmp, r.off, r.eq_before, false, b0);
+        if (c == nc - 1)
+            for (int i = st->total[t] + tid; i < kk; i += kLongNT) dst[i] = -1;
+        __syncthreads();
+    }
+}
+
+static int32_t long_chunks(int64_t n) { return (int32_t)((n + kChunk - 1) / kChunk); }
+
+size_t topk_ws_bytes(int32_t nq, int64_t n, int32_t, int32_t) {
+    if (n <= kSmallMax) return 0;
+    const size_t nc = (size_t)long_chunks(n);
+    return (size_t)nq * (sizeof(RowState) + kMaxTargets * kCandCap * sizeof(Cand) +
+                         kMaxTargets * nc * sizeof(ChunkRec)) + 256;
+}
 
 hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, const int32_t* ids,
-                       int32_t k, int32_t* out, int32_t k2, int32_t* out2, void*, hipStream_t s) {
+                       int32_t k, int32_t* out, int32_t k2, int32_t* out2, void* ws, hipStream_t s) {
     if (nq == 0) return hipSuccess;
-    if (n <= kTkLdsKeys)
-        hipLaunchKernelGGL(k_topk<true>, dim3((uint32_t)nq), dim3(kTkThreads), 0, s, scores, n, ld,
+    if (n <= kSmallMax) {
+        hipLaunchKernelGGL(k_topk_small, dim3((uint32_t)nq), dim3(kSmallNT), 0, s, scores, n, ld,
                            ids, k, out, k2, out2);
-    else
-        hipLaunchKernelGGL(k_topk<false>, dim3((uint32_t)nq), dim3(kTkThreads), 0, s, scores, n,
-                           ld, ids, k, out, k2, out2);
+        return hipGetLastError();
+    }
+    const int32_t nc = long_chunks(n);
+    char* base = static_cast<char*>(ws);
+    LongWs w;
+    w.st = reinterpret_cast<RowState*>(base);
+    w.cand = reinterpret_cast<Cand*>(base + (size_t)nq * sizeof(RowState));
+    w.rec = reinterpret_cast<ChunkRec*>(reinterpret_cast<char*>(w.cand) +
+                                        (size_t)nq * kMaxTargets * kCandCap * sizeof(Cand));
+    const int32_t kk2 = out2 ? k2 : 0;
+    dim3 grid((uint32_t)nc, (uint32_t)nq);
+    hipLaunchKernelGGL(k_topk_hist, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, kk2, w);
+    hipLaunchKernelGGL(k_topk_cand, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, kk2, w);
+    hipLaunchKernelGGL(k_topk_write, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
+                       out2, w);
     return hipGetLastError();
 }
 
