@@ -51,11 +51,12 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 }
 constexpr uint32_t kNegInfKey = 0x007FFFFFu;
 
-// Sum over groups of 8 consecutive lanes (every lane of the group gets it).
+// Sum over groups of 8 consecutive lanes (every lane of the group gets it),
+// with DPP: swap neighbours, swap pairs, then mirror within the half-row.
 __device__ __forceinline__ float sum8(float v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
     return v;
 }
 

@@ -33,15 +33,64 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Padded histogram index: one spare word every 64 bins, so that 64 lanes
+// reading 64 consecutive bins each hit 64 different LDS banks.
+__device__ __forceinline__ int hidx(int b) { return b + (b >> 6); }
+constexpr int kHistWords = 4096 + 64;  // LDS ints a 12-bit digit needs
+
+// Bucket search by one wave over nb bins (descending): finds the bin where the
+// running count from the top first reaches rem.  Phase A: lane l sums bins
+// [nb - per(l+1), nb - per l); a DPP scan finds the lane of the crossing.
+// Phase B: that lane's bins are spread over the wave and scanned again.
+// Writes res[0] = bin, res[1] = keys in higher bins, res[2] = keys in the
+// bin, res[3] = total keys.  Call from all 64 lanes of one wave.
+__device__ __forceinline__ void wave_find_bucket(const int* hist, int nb, int rem, int* res) {
+    const int lane = threadIdx.x & 63;
+    const int per = nb >> 6;  // 64 bins per lane for 12-bit digits, 4 for 8-bit
+    const int top = nb - 1 - per * lane;
+    int sa = 0;
+    for (int j = 0; j < per; j += 4) {
+        const int v0 = hist[hidx(top - j)], v1 = hist[hidx(top - j - 1)];
+        const int v2 = hist[hidx(top - j - 2)], v3 = hist[hidx(top - j - 3)];
+        sa += v0 + v1 + v2 + v3;
+    }
+    const int incl = wave_scan_dpp(sa);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const uint64_t hit = __ballot(incl >= rem);
+    if (total < rem || hit == 0) {
+        if (lane == 0) {
+            res[0] = 0;
+            res[1] = 0;
+            res[2] = 0;
+            res[3] = total;
+        }
+        return;
+    }
+    const int L = __builtin_ctzll(hit);
+    const int above_l = __builtin_amdgcn_readlane(incl - sa, L);
+    const int topL = nb - 1 - per * L;
+    const int c = lane < per ? hist[hidx(topL - lane)] : 0;
+    const int ib = wave_scan_dpp(c);
+    const uint64_t hit2 = __ballot(lane < per && above_l + ib >= rem);
+    const int J = __builtin_ctzll(hit2);
+    if (lane == J) {
+        res[0] = topL - J;
+        res[1] = above_l + ib - c;
+        res[2] = c;
+        res[3] = total;
+    }
+}
+
 // Exact (tau, need) of the kk-th key among the selectable keys keys[0..m) in
 // LDS.  The top `known` bits (0 or 12) are shared by every key that can reach
 // the kk-th place (the caller already resolved them); the remaining bits are
-// resolved 8 at a time, highest first.  hist needs 256 ints, res 4 ints of
-// LDS.  NT threads; every thread returns the same result.
+// resolved in digits of 12, 12 and 8 bits, highest first, stopping as soon as
+// a whole bucket is taken.  hist needs kHistWords ints, res 4 ints of LDS.
+// NT threads; every thread returns the same result.
 template <int NT>
 __device__ void lds_kth(const uint32_t* keys, int m, int kk, int known, int* hist, int* res,
                         uint32_t& tau, int& need) {
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     tau = 0u;
     need = 0;
     if (m <= 0 || kk <= 0) return;
@@ -51,47 +100,34 @@ __device__ void lds_kth(const uint32_t* keys, int m, int kk, int known, int* his
         prefix = keys[0] & mask;
     }
     int rem = kk;
-    for (int hi_bit = 32 - known; hi_bit > 0; hi_bit -= 8) {
-        const int bits = hi_bit >= 8 ? 8 : hi_bit;
+    for (int hi_bit = 32 - known; hi_bit > 0;) {
+        const int bits = hi_bit > 8 ? 12 : 8;
         const int shift = hi_bit - bits;
-        const uint32_t dm = (1u << bits) - 1u;
-        if (tid < 256) hist[tid] = 0;
+        const int nb = 1 << bits;
+        const uint32_t dm = (uint32_t)nb - 1u;
+        for (int i = tid; i < hidx(nb); i += NT) hist[i] = 0;
         __syncthreads();
-        for (int i = tid; i < m; i += NT) {
-            const uint32_t key = keys[i];
-            if (key && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dm], 1);
+        for (int i0 = tid; i0 < m; i0 += 4 * NT) {
+            uint32_t kv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kv[u] = (i0 + u * NT < m) ? keys[i0 + u * NT] : 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (kv[u] && (kv[u] & mask) == prefix)
+                    atomicAdd(&hist[hidx((int)((kv[u] >> shift) & dm))], 1);
         }
         __syncthreads();
-        if (tid < 64) {
-            // lane l holds bins 255-4l .. 252-4l (highest bins first)
-            const int b0 = 255 - 4 * lane;
-            const int c0 = hist[b0], c1 = hist[b0 - 1], c2 = hist[b0 - 2], c3 = hist[b0 - 3];
-            const int s = c0 + c1 + c2 + c3;
-            const int incl = wave_scan_dpp(s);
-            const int total = __builtin_amdgcn_readlane(incl, 63);
-            const int excl = incl - s;
-            if (lane == 0) res[3] = total;
-            if (excl < rem && incl >= rem) {
-                int acc = excl, b = b0, c = c0;
-                if (acc + c0 < rem) { acc += c0; b = b0 - 1; c = c1;
-                    if (acc + c1 < rem) { acc += c1; b = b0 - 2; c = c2;
-                        if (acc + c2 < rem) { acc += c2; b = b0 - 3; c = c3; } } }
-                res[0] = b;
-                res[1] = acc;
-                res[2] = c;
-            }
-        }
+        if (tid < 64) wave_find_bucket(hist, nb, rem, res);
         __syncthreads();
         const int total = res[3];
-        if (total < rem) {  // fewer selectable keys than kk under this prefix: take all
-            tau = prefix ? prefix - 1u : 0u;
-            need = 0;
-            __syncthreads();
-            return;
-        }
         const uint32_t bucket = (uint32_t)res[0];
         const int above = res[1], cnt = res[2];
         __syncthreads();
+        if (total < rem) {  // fewer selectable keys than kk under this prefix: take all
+            tau = prefix ? prefix - 1u : 0u;
+            need = 0;
+            return;
+        }
         prefix |= bucket << shift;
         mask |= dm << shift;
         rem -= above;
@@ -100,6 +136,7 @@ __device__ void lds_kth(const uint32_t* keys, int m, int kk, int known, int* his
             need = 0;
             return;
         }
+        hi_bit = shift;
     }
     tau = prefix;
     need = rem;
@@ -122,10 +159,15 @@ __device__ int ordered_write(KeyFn K, int64_t n, uint32_t tau, int need, const i
     const int64_t per = ((n + NW - 1) / NW + 63) / 64 * 64;
     const int64_t r0 = min(n, (int64_t)w * per), r1 = min(n, r0 + per);
     int gt = 0, eq = 0;
-    for (int64_t i = r0 + lane; i < r1; i += 64) {
-        const uint32_t key = K(i);
-        gt += key > tau;
-        eq += (key == tau) & (need > 0);
+    for (int64_t i0 = r0 + lane; i0 < r1; i0 += 4 * 64) {
+        uint32_t kv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kv[u] = (i0 + u * 64 < r1) ? K(i0 + u * 64) : 0u;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            gt += kv[u] > tau;
+            eq += (kv[u] == tau) & (need > 0) & (i0 + u * 64 < r1);
+        }
     }
     gt = wave_sum_dpp(gt);
     eq = wave_sum_dpp(eq);
@@ -146,23 +188,187 @@ __device__ int ordered_write(KeyFn K, int64_t n, uint32_t tau, int need, const i
         total += take;
         eqrun += e;
     }
-    for (int64_t i0 = r0; i0 < r1; i0 += 64) {
-        const int64_t i = i0 + lane;
-        const uint32_t key = i < r1 ? K(i) : 0u;
-        const bool eqf = i < r1 && need > 0 && key == tau;
-        const uint64_t em = __ballot(eqf);
-        const int er = eqb + lanes_below(em);
-        const bool take = i < r1 && (key > tau || (eqf && er < need));
-        const uint64_t sm = __ballot(take);
-        const int pos = selb + lanes_below(sm);
-        if (take && pos < kk) dst[pos] = ids ? ids[i] : (int32_t)(slot0 + i);
-        eqb += __popcll(em);
-        selb += __popcll(sm);
+    for (int64_t j0 = r0; j0 < r1; j0 += 4 * 64) {
+        uint32_t kv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = j0 + u * 64 + lane;
+            kv[u] = i < r1 ? K(i) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = j0 + u * 64 + lane;
+            const bool in = i < r1;
+            const bool eqf = in && need > 0 && kv[u] == tau;
+            const uint64_t em = __ballot(eqf);
+            const int er = eqb + lanes_below(em);
+            const bool take = in && (kv[u] > tau || (eqf && er < need));
+            const uint64_t sm = __ballot(take);
+            const int pos = selb + lanes_below(sm);
+            if (take && pos < kk) dst[pos] = ids ? ids[i] : (int32_t)(slot0 + i);
+            eqb += __popcll(em);
+            selb += __popcll(sm);
+        }
     }
     if (pad)
         for (int i = off0 + total + tid; i < kk; i += NT) dst[i] = -1;
     __syncthreads();
     return total;
+}
+
+// LDS of reg_select.
+template <int NT, int CAP>
+struct RegSelShared {
+    int hist[kHistWords];
+    alignas(16) uint32_t cand[CAP + 4];
+    int tmp[NT / 64 + 1];
+    int res[4];
+    int ncand;
+};
+
+// Top-kk of one row of n <= NT * PER slots by one workgroup, keys in
+// registers: thread t owns slots [t*PER, t*PER + PER); slot i is written as
+// ids[i] when IDS (ids non-null, 16-byte aligned rows), else as i.  A 12-bit histogram
+// finds the boundary bucket; the keys of that bucket (at most CAP) are
+// resolved exactly in LDS; one block scan of packed (greater, equal) counts
+// then places every chosen slot, ascending.  Writes dst[0..kk), -1 padded.
+template <int NT, int PER, int CAP, bool IDS>
+__device__ void reg_select(const float* s, const int32_t* ids, int n, int kk, int32_t* dst,
+                           RegSelShared<NT, CAP>& sh) {
+    static_assert(PER % 4 == 0, "PER must be a multiple of 4");
+    const int tid = threadIdx.x;
+    const int s0 = tid * PER;
+    uint32_t key[PER];
+    int32_t id[PER];
+    // every load of the row is issued before any is used
+#pragma unroll
+    for (int j = 0; j < PER; j += 4) {
+        float4 f = make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(),
+                               -__builtin_inff());
+        int4 iv = make_int4(s0 + j, s0 + j + 1, s0 + j + 2, s0 + j + 3);
+        if (s0 + j + 3 < n) {
+            f = *reinterpret_cast<const float4*>(s + s0 + j);
+            if (IDS) iv = *reinterpret_cast<const int4*>(ids + s0 + j);
+        } else {
+            if (s0 + j < n) { f.x = s[s0 + j]; if (IDS) iv.x = ids[s0 + j]; }
+            if (s0 + j + 1 < n) { f.y = s[s0 + j + 1]; if (IDS) iv.y = ids[s0 + j + 1]; }
+            if (s0 + j + 2 < n) { f.z = s[s0 + j + 2]; if (IDS) iv.z = ids[s0 + j + 2]; }
+        }
+        const float v[4] = {f.x, f.y, f.z, f.w};
+        const int32_t w[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t k = score_key(v[u]);
+            key[j + u] = (k == kNegInfKey || (IDS && w[u] < 0)) ? 0u : k;
+            if (IDS) id[j + u] = w[u];
+        }
+    }
+    for (int i = tid; i < kHistWords; i += NT) sh.hist[i] = 0;
+    if (tid == 0) sh.ncand = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (key[j]) atomicAdd(&sh.hist[hidx((int)(key[j] >> 20))], 1);
+    __syncthreads();
+    if (tid < 64) wave_find_bucket(sh.hist, kHistBins, kk, sh.res);
+    __syncthreads();
+    const int total_valid = sh.res[3];
+    const uint32_t b1 = (uint32_t)sh.res[0];
+    const int rem = kk - sh.res[1], cnt = sh.res[2];
+    uint32_t tau = 0u;
+    int need = 0;
+    if (total_valid > kk && cnt != rem) {
+        // keys of the boundary bucket -> LDS (one LDS atomic per wave)
+        const int lane = tid & 63;
+        int mine = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) mine += key[j] && (key[j] >> 20) == b1;
+        const int incl = wave_scan_dpp(mine);
+        int base = 0;
+        if (lane == 63 && incl) base = atomicAdd(&sh.ncand, incl);  // one LDS atomic per wave
+        int pos = __builtin_amdgcn_readlane(base, 63) + incl - mine;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            if (key[j] && (key[j] >> 20) == b1) {
+                if (pos < CAP) sh.cand[pos] = key[j];
+                ++pos;
+            }
+        }
+        __syncthreads();
+        const int m = sh.ncand;
+        if (m <= NT && m + 4 <= CAP + 4) {
+            // small bucket: the rem-th largest key by counting, one candidate per thread
+            if (tid < 4) sh.cand[m + tid] = 0u;  // pad to whole uint4 reads (key 0 counts for nothing)
+            __syncthreads();
+            const uint32_t mine = tid < m ? sh.cand[tid] : 0u;
+            int gt = 0, ge = 0;
+            const uint4* c4 = reinterpret_cast<const uint4*>(sh.cand);
+#pragma unroll 4
+            for (int j = 0; j < (m + 3) / 4; ++j) {
+                const uint4 o = c4[j];
+                gt += (o.x > mine) + (o.y > mine) + (o.z > mine) + (o.w > mine);
+                ge += (o.x >= mine) + (o.y >= mine) + (o.z >= mine) + (o.w >= mine);
+            }
+            if (tid == 0) sh.res[0] = 0;
+            __syncthreads();
+            if (tid < m && gt < rem && ge >= rem) {
+                sh.res[0] = (int)mine;  // every thread holding this key writes the same
+                sh.res[1] = rem - gt;
+            }
+            __syncthreads();
+            tau = (uint32_t)sh.res[0];
+            need = sh.res[1];
+        } else if (m <= CAP) {
+            lds_kth<NT>(sh.cand, m, rem, 12, sh.hist, sh.res, tau, need);
+        } else {
+            // the bucket does not fit: refine over the register keys, 12 then 8 bits
+            uint32_t prefix = b1 << 20, mask = 0xFFF00000u;
+            int r = rem;
+            for (int shift = 8; shift >= 0; shift -= 8) {
+                const int bits = shift ? 12 : 8;
+                const uint32_t dm = (1u << bits) - 1u;
+                for (int i = tid; i < kHistWords; i += NT) sh.hist[i] = 0;
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < PER; ++j)
+                    if (key[j] && (key[j] & mask) == prefix)
+                        atomicAdd(&sh.hist[hidx((int)((key[j] >> shift) & dm))], 1);
+                __syncthreads();
+                if (tid < 64) wave_find_bucket(sh.hist, 1 << bits, r, sh.res);
+                __syncthreads();
+                prefix |= (uint32_t)sh.res[0] << shift;
+                mask |= dm << shift;
+                r -= sh.res[1];
+                __syncthreads();
+            }
+            tau = prefix;
+            need = r;
+        }
+    } else if (total_valid > kk) {
+        tau = (b1 << 20) - 1u;  // the whole boundary bucket is taken
+    }
+    // ordered write: packed counts (greater in the low 16 bits, equal in the high)
+    int packed = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        packed += key[j] > tau;
+        packed += ((need > 0) & (key[j] == tau)) << 16;
+    }
+    int total;
+    const int before = block_excl_scan<NT>(packed, sh.tmp, &total);
+    int e = (int)((uint32_t)before >> 16);  // packed sums wrap like unsigned
+    int pos = (int)((uint32_t)before & 0xFFFFu) + min(need, e);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        bool take = key[j] > tau;
+        if (need > 0 && key[j] == tau) {
+            take = e < need;
+            ++e;
+        }
+        if (take && pos < kk) dst[pos++] = IDS ? id[j] : s0 + j;
+    }
+    const int chosen = (int)((uint32_t)total & 0xFFFFu) + min(need, (int)((uint32_t)total >> 16));
+    for (int i = chosen + tid; i < kk; i += NT) dst[i] = -1;
 }
 
 // Stage the keys of slots [0, n) of a row into LDS; global loads are issued

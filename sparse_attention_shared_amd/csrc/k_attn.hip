@@ -127,73 +127,83 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
         }
     }
 
-    // ---- gather: this lane loads entry (tile tau, row n16) of the wave
+    // ---- gather: this lane loads entry (tile tau, row n16) of the wave.  The
+    // selection slots of both tiles are read first, then every row load of
+    // both tiles is issued, then the rows are decoded.
     bf16x8_t kf[2][4];
     const int64_t e_base = (int64_t)chunk * kWgEntries + wave * kBlk;
+    int kind[2];     // 0 none, 1 global FP4, 2 global bf16, 3 local bf16
+    int64_t row[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-        const int eslot = tau * 16 + n16;
-        const int64_t ge = e_base + eslot;
-        int kind = 0;  // 0 none, 1 global FP4, 2 global bf16, 3 local bf16
-        int64_t row = 0;
+        const int64_t ge = e_base + tau * 16 + n16;
+        kind[tau] = 0;
+        row[tau] = 0;
         if (ge < k) {
             const int64_t j = sel[(int64_t)qi * k + ge];
             if (j >= 0 && j <= t) {
-                kind = c.fp4 ? 1 : 2;
-                row = (int64_t)seq * c.t_cap + j;
+                kind[tau] = c.fp4 ? 1 : 2;
+                row[tau] = (int64_t)seq * c.t_cap + j;
             }
         } else if (ge - k < nw) {
-            kind = 3;
-            row = (int64_t)seq * loc.cap + (w0 + (ge - k)) % loc.cap;
+            kind[tau] = 3;
+            row[tau] = (int64_t)seq * loc.cap + (w0 + (ge - k)) % loc.cap;
         }
-        uint32_t vb[16];
-        float skv[4] = {1.f, 1.f, 1.f, 1.f}, svv[4] = {1.f, 1.f, 1.f, 1.f};
-        if (kind == 1) {
-            const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row * kRowCodes;
+    }
+    uint32_t rk[2][16], rv[2][16];
+    uint2 rsc[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+        rsc[tau] = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);  // scale 1 for bf16 rows
+        if (kind[tau] == 1) {
+            const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row[tau] * kRowCodes;
             const uint32_t* kw = reinterpret_cast<const uint32_t*>(cr);
-            uint32_t kd[4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) kd[kb] = kw[4 * kb + g];  // dims 32kb + 8g .. +8
+            for (int kb = 0; kb < 4; ++kb) rk[tau][kb] = kw[4 * kb + g];  // dims 32kb + 8g .. +8
             const uint4 vv = *reinterpret_cast<const uint4*>(cr + 64 + 16 * g);  // dims 32g .. +32
-            const uint2 sc = *reinterpret_cast<const uint2*>(c.scales + row * kRowScales);
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                uint32_t o[4];
-                fp4x8_bf16(kd[kb], o);
-                kf[tau][kb] = as_bf16x8(o[0], o[1], o[2], o[3]);
-            }
-            fp4x8_bf16(vv.x, vb + 0);
-            fp4x8_bf16(vv.y, vb + 4);
-            fp4x8_bf16(vv.z, vb + 8);
-            fp4x8_bf16(vv.w, vb + 12);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                skv[b] = e8m0_value((sc.x >> (8 * b)) & 0xFFu);
-                svv[b] = e8m0_value((sc.y >> (8 * b)) & 0xFFu);
-            }
-        } else if (kind >= 2) {
-            const uint16_t* kr;
-            const uint16_t* vr;
-            if (kind == 2) {
-                kr = static_cast<const uint16_t*>(c.data) + row * kRowBf16;
-                vr = kr + kHeadDim;
-            } else {
-                kr = loc.k + row * kHeadDim;
-                vr = loc.v + row * kHeadDim;
-            }
+            rv[tau][0] = vv.x; rv[tau][1] = vv.y; rv[tau][2] = vv.z; rv[tau][3] = vv.w;
+            rsc[tau] = *reinterpret_cast<const uint2*>(c.scales + row[tau] * kRowScales);
+        } else if (kind[tau] >= 2) {
+            const uint16_t* kr = kind[tau] == 2
+                                     ? static_cast<const uint16_t*>(c.data) + row[tau] * kRowBf16
+                                     : loc.k + row[tau] * kHeadDim;
+            const uint16_t* vr = kind[tau] == 2 ? kr + kHeadDim : loc.v + row[tau] * kHeadDim;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const uint4 v = *reinterpret_cast<const uint4*>(kr + 32 * kb + 8 * g);
-                kf[tau][kb] = as_bf16x8(v.x, v.y, v.z, v.w);
+                rk[tau][4 * kb] = v.x; rk[tau][4 * kb + 1] = v.y;
+                rk[tau][4 * kb + 2] = v.z; rk[tau][4 * kb + 3] = v.w;
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint4 v = *reinterpret_cast<const uint4*>(vr + 32 * g + 8 * i);
-                vb[4 * i + 0] = v.x;
-                vb[4 * i + 1] = v.y;
-                vb[4 * i + 2] = v.z;
-                vb[4 * i + 3] = v.w;
+                rv[tau][4 * i] = v.x; rv[tau][4 * i + 1] = v.y;
+                rv[tau][4 * i + 2] = v.z; rv[tau][4 * i + 3] = v.w;
             }
+        }
+    }
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+        const int eslot = tau * 16 + n16;
+        uint32_t vb[16];
+        if (kind[tau] == 1) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                uint32_t o[4];
+                fp4x8_bf16(rk[tau][kb], o);
+                kf[tau][kb] = as_bf16x8(o[0], o[1], o[2], o[3]);
+            }
+            fp4x8_bf16(rv[tau][0], vb + 0);
+            fp4x8_bf16(rv[tau][1], vb + 4);
+            fp4x8_bf16(rv[tau][2], vb + 8);
+            fp4x8_bf16(rv[tau][3], vb + 12);
+        } else if (kind[tau] >= 2) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                kf[tau][kb] = as_bf16x8(rk[tau][4 * kb], rk[tau][4 * kb + 1], rk[tau][4 * kb + 2],
+                                        rk[tau][4 * kb + 3]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) vb[i] = rv[tau][i];
         } else {
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) kf[tau][kb] = as_bf16x8(0u, 0u, 0u, 0u);
@@ -209,10 +219,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
         if (g == 0) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                W.sk[eslot][b] = skv[b];
-                W.sv[eslot][b] = svv[b];
+                W.sk[eslot][b] = e8m0_value((rsc[tau].x >> (8 * b)) & 0xFFu);
+                W.sv[eslot][b] = e8m0_value((rsc[tau].y >> (8 * b)) & 0xFFu);
             }
-            W.valid[eslot] = kind != 0;
+            W.valid[eslot] = kind[tau] != 0;
         }
     }
     __syncthreads();
@@ -329,39 +339,37 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     if (tid == 0) __threadfence();  // acquire for the whole workgroup
     __syncthreads();
     // ---- the last chunk of the query merges all chunks in order
-    float Mq = -__builtin_inff();
+    float Mq = -__builtin_inff(), Lq = 0.f, aq[4] = {0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < n_chunk; j0 += 16) {
-        float mv[16];
+        // all loads of up to 16 chunks are issued before any is used
+        float2 ml[16];
+        float4 ov[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-            mv[u] = (j0 + u < n_chunk) ? ws_ml[((part0 + j0 + u) * kHeads + h) * 2] : -__builtin_inff();
-#pragma unroll
-        for (int u = 0; u < 16; ++u) Mq = fmaxf(Mq, mv[u]);
-    }
-    float Lq = 0.f, aq[4] = {0.f, 0.f, 0.f, 0.f};
-    if (Mq != -__builtin_inff()) {
-        for (int j0 = 0; j0 < n_chunk; j0 += 8) {
-            float2 ml[8];
-            float4 ov[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int64_t pj = part0 + j0 + u;
-                const bool in = j0 + u < n_chunk;
-                ml[u] = in ? *reinterpret_cast<const float2*>(ws_ml + (pj * kHeads + h) * 2)
-                           : make_float2(-__builtin_inff(), 0.f);
-                ov[u] = in ? *reinterpret_cast<const float4*>(ws_o + (pj * kHeads + h) * kHeadDim + d0)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float f = (ml[u].x == -__builtin_inff()) ? 0.f : exp2f(ml[u].x - Mq);
-                Lq = fmaf(ml[u].y, f, Lq);
-                aq[0] = fmaf(ov[u].x, f, aq[0]);
-                aq[1] = fmaf(ov[u].y, f, aq[1]);
-                aq[2] = fmaf(ov[u].z, f, aq[2]);
-                aq[3] = fmaf(ov[u].w, f, aq[3]);
-            }
+        for (int u = 0; u < 16; ++u) {
+            const int64_t pj = part0 + j0 + u;
+            const bool in = j0 + u < n_chunk;
+            ml[u] = in ? *reinterpret_cast<const float2*>(ws_ml + (pj * kHeads + h) * 2)
+                       : make_float2(-__builtin_inff(), 0.f);
+            ov[u] = in ? *reinterpret_cast<const float4*>(ws_o + (pj * kHeads + h) * kHeadDim + d0)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        float Mn = Mq;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) Mn = fmaxf(Mn, ml[u].x);
+        if (Mn == -__builtin_inff()) continue;
+        const float rs = (Mq == -__builtin_inff()) ? 0.f : exp2f(Mq - Mn);
+        Lq *= rs;
+        aq[0] *= rs; aq[1] *= rs; aq[2] *= rs; aq[3] *= rs;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const float f = (ml[u].x == -__builtin_inff()) ? 0.f : exp2f(ml[u].x - Mn);
+            Lq = fmaf(ml[u].y, f, Lq);
+            aq[0] = fmaf(ov[u].x, f, aq[0]);
+            aq[1] = fmaf(ov[u].y, f, aq[1]);
+            aq[2] = fmaf(ov[u].z, f, aq[2]);
+            aq[3] = fmaf(ov[u].w, f, aq[3]);
+        }
+        Mq = Mn;
     }
     const float inv = Lq > 0.f ? 1.f / Lq : 0.f;
     *reinterpret_cast<uint2*>(orow) =

@@ -37,14 +37,6 @@ __device__ __forceinline__ void load_q8(const uint16_t* q, float* qf) {
     qf[6] = bf16_lo(v.w); qf[7] = bf16_hi(v.w);
 }
 
-// Select s[r] for a run-time r in [0, 8) without spilling the array.
-__device__ __forceinline__ float pick8(const float* s, int r) {
-    float v = s[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) v = (r == i) ? s[i] : v;
-    return v;
-}
-
 // grid: (ceil(t_cap / 256), nq).  Lane (grp, sub) of a wave handles bytes
 // [16 sub, 16 sub + 16) of key base + 8 r + grp in round r.
 template <int BLOCK>
@@ -87,8 +79,10 @@ __global__ __launch_bounds__(256) void k_score_dense(const uint16_t* __restrict_
     for (int r = 0; r < 8; ++r) s[r] = sum8(dot8(qf, kv[r]));
     if (BLOCK == 1) {
         // lane (grp, sub) stores key base + 8 sub + grp: one 256 B coalesced store
+        float v = s[0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r) v = (sub == r) ? s[r] : v;
         const int64_t tok = base + sub * 8 + grp;
-        const float v = pick8(s, sub);
         if (tok < t_cap) srow[tok] = (tok <= t) ? v : NEG;
     } else {
         float m = NEG;
@@ -138,8 +132,10 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__
     float s[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) s[r] = ok[r] ? sum8(dot8(qf, kv[r])) : -__builtin_inff();
+    float v = s[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) v = (sub == r) ? s[r] : v;
     const int64_t c = base + sub * 8 + grp;
-    const float v = pick8(s, sub);
     if (c < n_cand) srow[c] = v;
 }
 
@@ -150,25 +146,23 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__
 // `scores`; the last one of a query to finish (per-query counter `ctr`, reset
 // on exit) selects the top k of all n_cand <= kSelMaxCand candidates in LDS.
 constexpr int kSelMaxCand = 16384;
+constexpr int kSelNT = 512;
 
-__global__ __launch_bounds__(256) void k_score_select(const uint16_t* __restrict__ k_idx,
-                                                      int32_t n_seq, int64_t t_cap,
-                                                      const uint16_t* __restrict__ q_idx,
-                                                      const int32_t* __restrict__ q_pos,
-                                                      const int32_t* __restrict__ q_seq,
-                                                      const int32_t* __restrict__ cand,
-                                                      int64_t n_cand, float* __restrict__ scores,
-                                                      uint32_t* __restrict__ ctr, int32_t k,
-                                                      int32_t* __restrict__ sel) {
-    __shared__ uint32_t keys[kSelMaxCand];
-    __shared__ int hist[256];
-    __shared__ int wtmp[2 * 256 / 64];
-    __shared__ int res[4];
+__global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restrict__ k_idx,
+                                                         int32_t n_seq, int64_t t_cap,
+                                                         const uint16_t* __restrict__ q_idx,
+                                                         const int32_t* __restrict__ q_pos,
+                                                         const int32_t* __restrict__ q_seq,
+                                                         const int32_t* __restrict__ cand,
+                                                         int64_t n_cand, float* __restrict__ scores,
+                                                         uint32_t* __restrict__ ctr, int32_t k,
+                                                         int32_t* __restrict__ sel) {
+    __shared__ RegSelShared<kSelNT, 4096> sh;
     __shared__ int last;
     const int qi = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane & 7, grp = lane >> 3;
-    const int64_t base = (int64_t)blockIdx.x * kScoreTile + wave * 64;
+    const int64_t base = (int64_t)blockIdx.x * (kSelNT / 4) * 4 + wave * 64;
     float* srow = scores + (int64_t)qi * n_cand;
     const int32_t* crow = cand + (int64_t)qi * n_cand;
     const int32_t seq = q_seq ? q_seq[qi] : qi;
@@ -189,11 +183,14 @@ __global__ __launch_bounds__(256) void k_score_select(const uint16_t* __restrict
             ok[r] = tok >= 0 && tok <= t;
             kv[r] = ok[r] ? kb[tok * 8 + sub] : make_uint4(0, 0, 0, 0);
         }
-        float sc[8];
+        float my = -__builtin_inff();
 #pragma unroll
-        for (int r = 0; r < 8; ++r) sc[r] = ok[r] ? sum8(dot8(qf, kv[r])) : -__builtin_inff();
+        for (int r = 0; r < 8; ++r) {
+            const float sc = ok[r] ? sum8(dot8(qf, kv[r])) : -__builtin_inff();
+            if (sub == r) my = sc;
+        }
         const int64_t c = base + sub * 8 + grp;
-        if (c < n_cand) srow[c] = pick8(sc, sub);
+        if (c < n_cand) srow[c] = my;
     }
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
     if (threadIdx.x == 0) {
@@ -204,13 +201,8 @@ __global__ __launch_bounds__(256) void k_score_select(const uint16_t* __restrict
     if (!last) return;
     if (threadIdx.x == 0) __threadfence();  // acquire for the whole workgroup
     __syncthreads();
-    stage_keys<256>(srow, crow, n_cand, keys);
-    __syncthreads();
-    uint32_t tau;
-    int need;
-    lds_kth<256>(keys, (int)n_cand, k, 0, hist, res, tau, need);
-    ordered_write<256>([&](int64_t i) { return keys[i]; }, n_cand, tau, need, crow, k,
-                       sel + (int64_t)qi * k, wtmp);
+    reg_select<kSelNT, kSelMaxCand / kSelNT, 4096, true>(srow, crow, (int)n_cand, k,
+                                                   sel + (int64_t)qi * k, sh);
     if (threadIdx.x == 0) ctr[qi] = 0u;
 }
 
@@ -220,8 +212,8 @@ hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const 
                                int32_t* sel, hipStream_t s) {
     if (nq == 0 || n_cand == 0) return hipSuccess;
     if (n_cand > kSelMaxCand) return hipErrorInvalidValue;
-    dim3 grid((uint32_t)((n_cand + kScoreTile - 1) / kScoreTile), (uint32_t)nq);
-    hipLaunchKernelGGL(k_score_select, grid, dim3(256), 0, s, c.k_idx, c.n_seq, c.t_cap, q_idx,
+    dim3 grid((uint32_t)((n_cand + kSelNT - 1) / kSelNT), (uint32_t)nq);
+    hipLaunchKernelGGL(k_score_select, grid, dim3(kSelNT), 0, s, c.k_idx, c.n_seq, c.t_cap, q_idx,
                        q_pos, q_seq, cand, n_cand, scores, ctr, k, sel);
     return hipGetLastError();
 }

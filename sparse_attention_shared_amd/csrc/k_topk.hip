@@ -36,29 +36,22 @@ constexpr int kCandCap = 4096;    // candidates per row and target
 constexpr int kMaxTargets = 2;
 
 // ---------------------------------------------------------------- short rows
+template <bool IDS, int PER>
 __global__ __launch_bounds__(kSmallNT) void k_topk_small(const float* __restrict__ scores,
                                                          int64_t n, int64_t ld,
                                                          const int32_t* __restrict__ ids,
                                                          int32_t k, int32_t* __restrict__ out,
                                                          int32_t k2, int32_t* __restrict__ out2) {
-    __shared__ uint32_t keys[kSmallMax];
-    __shared__ int hist[256];
-    __shared__ int wtmp[2 * kSmallNT / 64];
-    __shared__ int res[4];
+    __shared__ RegSelShared<kSmallNT, 8192> sh;
     const int64_t row = blockIdx.x;
     const float* s = scores + row * ld;
-    const int32_t* irow = ids ? ids + row * n : nullptr;
-    stage_keys<kSmallNT>(s, irow, n, keys);
-    __syncthreads();
-    auto K = [&](int64_t i) { return keys[i]; };
-    for (int t = 0; t < 2; ++t) {
+    const int32_t* irow = IDS ? ids + row * n : nullptr;
+#pragma unroll 1
+    for (int t = 0; t < (out2 ? 2 : 1); ++t) {
+        if (t) __syncthreads();
         const int32_t kk = t ? k2 : k;
-        int32_t* dst = t ? (out2 ? out2 + row * k2 : nullptr) : out + row * k;
-        if (!dst || kk <= 0) continue;
-        uint32_t tau;
-        int need;
-        lds_kth<kSmallNT>(keys, (int)n, kk, 0, hist, res, tau, need);
-        ordered_write<kSmallNT>(K, n, tau, need, irow, kk, dst, wtmp);
+        int32_t* dst = t ? out2 + row * k2 : out + row * k;
+        reg_select<kSmallNT, PER, 8192, IDS>(s, irow, (int)n, kk, dst, sh);
     }
 }
 
@@ -96,8 +89,8 @@ __device__ __forceinline__ int64_t chunk_begin(int c) { return (int64_t)c * kChu
 __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__ scores, int64_t n,
                                                        int64_t ld, const int32_t* __restrict__ ids,
                                                        int32_t k, int32_t k2, LongWs ws) {
-    __shared__ int hist[kHistBins];
-    __shared__ int tmp[kLongNT / 64 + 1];
+    __shared__ int hist[kHistWords];
+    __shared__ int res[4];
     __shared__ int last;
     const int c = blockIdx.x, nc = gridDim.x;
     const int64_t row = blockIdx.y;
@@ -105,7 +98,7 @@ __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__
     const float* s = scores + row * ld;
     const int32_t* irow = ids ? ids + row * n : nullptr;
     RowState* st = ws.st + row;
-    for (int i = tid; i < kHistBins; i += kLongNT) hist[i] = 0;
+    for (int i = tid; i < kHistWords; i += kLongNT) hist[i] = 0;
     __syncthreads();
     constexpr int kPer = kChunk / kLongNT;
     const int64_t b0 = chunk_begin(c);
@@ -117,10 +110,12 @@ __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__
     }
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-        if (kr[j]) atomicAdd(&hist[kr[j] >> 20], 1);
+        if (kr[j]) atomicAdd(&hist[hidx((int)(kr[j] >> 20))], 1);
     __syncthreads();
-    for (int i = tid; i < kHistBins; i += kLongNT)
-        if (hist[i]) atomicAdd(&st->hist[i], (uint32_t)hist[i]);
+    for (int i = tid; i < kHistBins; i += kLongNT) {
+        const int v = hist[hidx(i)];
+        if (v) atomicAdd(&st->hist[i], (uint32_t)v);
+    }
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
     if (tid == 0) {
         __threadfence();
@@ -140,38 +135,26 @@ __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__
                                       __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-            hist[tid + u * kLongNT] = (int)hv[u];
+            hist[hidx(tid + u * kLongNT)] = (int)hv[u];
             st->hist[tid + u * kLongNT] = 0u;
         }
     }
     __syncthreads();
-    constexpr int per = kHistBins / kLongNT;
-    const int hi = kHistBins - tid * per, lo = hi - per;
-    int mine = 0;
-    for (int b = hi - 1; b >= lo; --b) mine += hist[b];
-    int total;
-    const int before = block_excl_scan<kLongNT>(mine, tmp, &total);
     for (int t = 0; t < kMaxTargets; ++t) {
         const int kk = t ? k2 : k;
         if (kk <= 0) continue;
-        if (total <= kk) {  // every selectable key is taken
-            if (tid == 0) {
+        if (tid < 64) wave_find_bucket(hist, kHistBins, kk, res);
+        __syncthreads();
+        if (tid == 0) {
+            if (res[3] <= kk) {  // every selectable key is taken
                 st->bucket[t] = 0u;
                 st->rem[t] = -1;
-            }
-            continue;
-        }
-        if (before < kk && before + mine >= kk) {
-            int acc = before;
-            for (int b = hi - 1; b >= lo; --b) {
-                if (acc + hist[b] >= kk) {
-                    st->bucket[t] = (uint32_t)b;
-                    st->rem[t] = kk - acc;
-                    break;
-                }
-                acc += hist[b];
+            } else {
+                st->bucket[t] = (uint32_t)res[0];
+                st->rem[t] = kk - res[1];
             }
         }
+        __syncthreads();
     }
     if (tid == 0) st->ctr_hist = 0u;
 }
@@ -182,7 +165,7 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
                                                        int32_t k, int32_t k2, LongWs ws) {
     __shared__ uint32_t ckeys[kCandCap];
     __shared__ int32_t cslot[kCandCap];
-    __shared__ int hist[kHistBins];
+    __shared__ int hist[kHistWords];
     __shared__ int tmp[kLongNT / 64 + 1];
     __shared__ int res[4];
     __shared__ int cnt_gt[kMaxTargets], cnt_cand[kMaxTargets], cbase[kMaxTargets];
@@ -442,8 +425,14 @@ hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, c
                        int32_t k, int32_t* out, int32_t k2, int32_t* out2, void* ws, hipStream_t s) {
     if (nq == 0) return hipSuccess;
     if (n <= kSmallMax) {
-        hipLaunchKernelGGL(k_topk_small, dim3((uint32_t)nq), dim3(kSmallNT), 0, s, scores, n, ld,
-                           ids, k, out, k2, out2);
+        const dim3 g((uint32_t)nq), b(kSmallNT);
+        if (n <= 16 * kSmallNT) {
+            if (ids) hipLaunchKernelGGL((k_topk_small<true, 16>), g, b, 0, s, scores, n, ld, ids, k, out, k2, out2);
+            else hipLaunchKernelGGL((k_topk_small<false, 16>), g, b, 0, s, scores, n, ld, ids, k, out, k2, out2);
+        } else {
+            if (ids) hipLaunchKernelGGL((k_topk_small<true, 32>), g, b, 0, s, scores, n, ld, ids, k, out, k2, out2);
+            else hipLaunchKernelGGL((k_topk_small<false, 32>), g, b, 0, s, scores, n, ld, ids, k, out, k2, out2);
+        }
         return hipGetLastError();
     }
     const int32_t nc = long_chunks(n);
