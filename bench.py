@@ -57,7 +57,7 @@ def src_hash(path):
 def traffic_from_profile(launch_units):
     """HBM bytes per launch of the scan kernel from the committed counter
     summary, or None when the kernel source changed since it was taken."""
-    p = os.path.join(ROOT, "profiles", "score_scan_config3_counters.json")
+    p = os.path.join(ROOT, "profiles", "k_score_dense_b4_t131072_counters.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["repeat", "page"], default="repeat")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -111,6 +113,15 @@ def main():
 
     torch.cuda.set_device(0)
     csa2.device_check()
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 18  # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("calibration copy: %d MiB x3" % args.calib_copy_mib, file=sys.stderr, flush=True)
+        del src, dst
     sp = synth.config(3)
     if args.schedule == "page":
         sp = synth.Spec(**{**sp.__dict__, "schedule": synth.page_schedule_20()})
