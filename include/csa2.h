@@ -142,6 +142,33 @@ csa2_status csa2_index_score(const csa2_cache *cache, const uint16_t *q_idx, con
                              const int32_t *q_seq, int32_t nq, const int32_t *cand, int64_t n_cand,
                              int32_t block, float *scores, int64_t ld_scores, void *stream);
 
+/* Dense indexer scores of a prefill chunk: nq queries, all on sequence `seq`,
+ * each at its own position q_pos[i] ("CED...", "Why Prefill Recomputes a
+ * Recent Segment", Fig. 6: the recent positions pass through the decoder
+ * again; each one selects like a decode query).  scores[i][t] for t < t_cap,
+ * -inf for t > q_pos[i].  The product Q_I K_I^T runs on MFMA (bf16 in, fp32
+ * accumulation); q_idx: bf16 [nq][64]; scores: float, row stride ld_scores
+ * >= t_cap. */
+csa2_status csa2_prefill_score(const csa2_cache *cache, int32_t seq, const uint16_t *q_idx,
+                               const int32_t *q_pos, int32_t nq, float *scores, int64_t ld_scores,
+                               void *stream);
+
+/* Indexer top-k of a prefill chunk ("CED...", "Why Prefill Recomputes a
+ * Recent Segment", Fig. 6, with the selection of "Selecting Positions and
+ * Reading Values with Attention", Fig. 4): nq queries on sequence `seq`, query
+ * i at position q_pos[i], choose the k positions p <= q_pos[i] with the largest
+ * q_idx[i] . k_idx[seq][p] (ties: lower position first), written ascending to
+ * sel[i][0..k), -1 padded.  The same selection as csa2_index_score followed by
+ * csa2_topk on each row, computed without materialising the score rows: the
+ * product runs on MFMA and only a candidate superset of the top-k is kept.
+ * Limits: 1 <= k <= 2048, t_cap <= 262144 (else CSA2_ERR_SHAPE).  ws: at least
+ * csa2_prefill_topk_workspace() bytes, no initial contents needed; q_pos
+ * outside [0, t_cap) is clamped to t_cap - 1, negative gives an all -1 row. */
+csa2_status csa2_prefill_topk_workspace(int32_t nq, int64_t t_cap, int32_t k, size_t *bytes);
+csa2_status csa2_prefill_topk(const csa2_cache *cache, int32_t seq, const uint16_t *q_idx,
+                              const int32_t *q_pos, int32_t nq, int32_t k, int32_t *sel, void *ws,
+                              size_t ws_bytes, void *stream);
+
 /* Top-k selection (Fig. 4) of each row of scores: float [nq][n] with row
  * stride ld.  Order: higher score first, equal scores by lower position
  * (-0 equals +0).  Entries equal to -inf, and slots whose id is < 0, are

@@ -63,6 +63,11 @@ def lib() -> ctypes.CDLL:
         L.csa2_unpack_fp4.argtypes = [_P, _P, _i64, _i32, _P, _P]
         L.csa2_index_score.argtypes = [ctypes.POINTER(csa2_cache), _P, _P, _P, _i32, _P, _i64,
                                        _i32, _P, _i64, _P]
+        L.csa2_prefill_score.argtypes = [ctypes.POINTER(csa2_cache), _i32, _P, _P, _i32, _P, _i64,
+                                         _P]
+        L.csa2_prefill_topk.argtypes = [ctypes.POINTER(csa2_cache), _i32, _P, _P, _i32, _i32, _P,
+                                        _P, _sz, _P]
+        L.csa2_prefill_topk_workspace.argtypes = [_i32, _i64, _i32, ctypes.POINTER(_sz)]
         L.csa2_topk.argtypes = [_P, _i32, _i64, _i64, _P, _i32, _P, _i32, _P, _P, _sz, _P]
         L.csa2_topk_workspace.argtypes = [_i32, _i64, _i32, _i32, ctypes.POINTER(_sz)]
         L.csa2_expand_blocks.argtypes = [_P, _i32, _i32, _i32, _P, _P, _P]
@@ -71,7 +76,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_sparse_attn_workspace.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_sz)]
         L.csa2_stack_workspace.argtypes = [ctypes.POINTER(csa2_stack_desc), ctypes.POINTER(_sz)]
         L.csa2_stack_run.argtypes = [ctypes.POINTER(csa2_stack_desc), _P, _sz, _P]
-        for f in ("csa2_pack_fp4", "csa2_unpack_fp4", "csa2_index_score", "csa2_topk",
+        for f in ("csa2_pack_fp4", "csa2_unpack_fp4", "csa2_index_score", "csa2_prefill_score",
+                  "csa2_prefill_topk", "csa2_prefill_topk_workspace", "csa2_topk",
                   "csa2_topk_workspace", "csa2_expand_blocks", "csa2_sparse_attn",
                   "csa2_sparse_attn_workspace", "csa2_stack_workspace", "csa2_stack_run"):
             getattr(L, f).restype = ctypes.c_int
@@ -185,6 +191,41 @@ def index_score(cache: Cache, q_idx: torch.Tensor, q_pos: torch.Tensor,
         ctypes.byref(cache.c), _ptr(_bits16(q_idx)), _ptr(_i32t(q_pos)), _ptr(_i32t(q_seq)), nq,
         _ptr(_i32t(cand)), n if cand is not None else 0, block, _ptr(out), int(out.stride(0)),
         _stream()))
+    return out
+
+
+def prefill_score(cache: Cache, seq: int, q_idx: torch.Tensor, q_pos: torch.Tensor,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense scores of a chunk of queries on one sequence (MFMA): [nq][t_cap]."""
+    nq = int(q_pos.shape[0])
+    if out is None:
+        out = torch.empty((nq, cache.t_cap), dtype=torch.float32, device=q_pos.device)
+    _check("csa2_prefill_score", lib().csa2_prefill_score(
+        ctypes.byref(cache.c), int(seq), _ptr(_bits16(q_idx)), _ptr(_i32t(q_pos)), nq, _ptr(out),
+        int(out.stride(0)), _stream()))
+    return out
+
+
+def prefill_topk_workspace(nq: int, t_cap: int, k: int) -> int:
+    n = _sz()
+    _check("csa2_prefill_topk_workspace",
+           lib().csa2_prefill_topk_workspace(int(nq), int(t_cap), int(k), ctypes.byref(n)))
+    return n.value
+
+
+def prefill_topk(cache: Cache, seq: int, q_idx: torch.Tensor, q_pos: torch.Tensor, k: int,
+                 out: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-k positions of every query of a prefill chunk on one sequence: [nq][k]."""
+    nq = int(q_pos.shape[0])
+    if out is None:
+        out = torch.empty((nq, k), dtype=torch.int32, device=q_pos.device)
+    need = prefill_topk_workspace(nq, cache.t_cap, k)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q_pos.device)
+    _check("csa2_prefill_topk", lib().csa2_prefill_topk(
+        ctypes.byref(cache.c), int(seq), _ptr(_bits16(q_idx)), _ptr(_i32t(q_pos)), nq, int(k),
+        _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out
 
 

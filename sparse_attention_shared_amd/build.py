@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libcsa2.so")
 
-SOURCES = ["k_fp4.hip", "k_score.hip", "k_topk.hip", "k_attn.hip", "csa2_api.cpp"]
+SOURCES = ["k_fp4.hip", "k_score.hip", "k_topk.hip", "k_prefill.hip", "k_attn.hip", "csa2_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -37,9 +37,16 @@ def _torch_lib_dir() -> str:
     return os.path.join(list(spec.submodule_search_locations)[0], "lib")
 
 
+# Per-file code generation options: these kernels keep their MFMA accumulators
+# in ordinary VGPRs, so reading a result costs no v_accvgpr_read.
+FILE_FLAGS = {"k_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + CFLAGS + FILE_FLAGS.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src),
+                                                         "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -186,6 +186,39 @@ csa2_status csa2_index_score(const csa2_cache* cache, const uint16_t* q_idx, con
     return from_hip(launch_score_dense(cv, q_idx, q_pos, q_seq, nq, block, scores, ld_scores, s));
 }
 
+csa2_status csa2_prefill_score(const csa2_cache* cache, int32_t seq, const uint16_t* q_idx,
+                               const int32_t* q_pos, int32_t nq, float* scores, int64_t ld_scores,
+                               void* stream) {
+    CacheView cv;
+    if (csa2_status st = check_cache(cache, false, true, &cv)) return st;
+    if (nq < 0 || seq < 0 || seq >= cv.n_seq || ld_scores < cv.t_cap) return CSA2_ERR_SHAPE;
+    if (nq > 65535 * 64) return CSA2_ERR_SHAPE;
+    if (nq > 0 && (!q_idx || !q_pos || !scores || !aligned16(q_idx))) return CSA2_ERR_INVALID_ARG;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_score_mq(cv, seq, q_idx, q_pos, nq, scores, ld_scores, (hipStream_t)stream));
+}
+
+csa2_status csa2_prefill_topk_workspace(int32_t nq, int64_t t_cap, int32_t k, size_t* bytes) {
+    if (!bytes) return CSA2_ERR_INVALID_ARG;
+    if (nq < 0 || t_cap < 1 || t_cap > kPfMaxT || k < 1 || k > kPfMaxK) return CSA2_ERR_SHAPE;
+    *bytes = prefill_topk_ws_bytes(nq, t_cap);
+    return CSA2_OK;
+}
+
+csa2_status csa2_prefill_topk(const csa2_cache* cache, int32_t seq, const uint16_t* q_idx,
+                              const int32_t* q_pos, int32_t nq, int32_t k, int32_t* sel, void* ws,
+                              size_t ws_bytes, void* stream) {
+    CacheView cv;
+    if (csa2_status st = check_cache(cache, false, true, &cv)) return st;
+    if (nq < 0 || seq < 0 || seq >= cv.n_seq || k < 1 || k > kPfMaxK || cv.t_cap > kPfMaxT)
+        return CSA2_ERR_SHAPE;
+    if (nq == 0) return CSA2_OK;
+    if (!q_idx || !q_pos || !sel || !ws || !aligned16(q_idx)) return CSA2_ERR_INVALID_ARG;
+    if (ws_bytes < prefill_topk_ws_bytes(nq, cv.t_cap)) return CSA2_ERR_WORKSPACE;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_prefill_topk(cv, seq, q_idx, q_pos, nq, k, sel, ws, (hipStream_t)stream));
+}
+
 csa2_status csa2_topk_workspace(int32_t nq, int64_t n, int32_t k, int32_t k2, size_t* bytes) {
     if (!bytes) return CSA2_ERR_INVALID_ARG;
     if (nq < 0 || n < 0 || k <= 0 || k2 < 0) return CSA2_ERR_SHAPE;

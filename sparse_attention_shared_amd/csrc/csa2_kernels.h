@@ -38,6 +38,22 @@ hipError_t launch_score_cand(const CacheView& c, const uint16_t* q_idx, const in
                              const int32_t* q_seq, int32_t nq, const int32_t* cand, int64_t n_cand,
                              float* scores, int64_t ld, hipStream_t s);
 
+// Dense scores of many queries on one sequence (prefill chunk), on MFMA.
+hipError_t launch_score_mq(const CacheView& c, int32_t seq, const uint16_t* q_idx,
+                           const int32_t* q_pos, int32_t nq, float* scores, int64_t ld,
+                           hipStream_t s);
+
+// Fused indexer top-k of a prefill chunk on one sequence (MFMA scores, never
+// written out).  Limits: k <= kPfMaxK, t_cap <= kPfMaxT.  The workspace needs
+// no initial contents.
+constexpr int kPfCap = 4096;
+constexpr int32_t kPfMaxK = 2048;
+constexpr int64_t kPfMaxT = int64_t(1) << 18;
+size_t prefill_topk_ws_bytes(int32_t nq, int64_t t_cap);
+hipError_t launch_prefill_topk(const CacheView& c, int32_t seq, const uint16_t* q_idx,
+                               const int32_t* q_pos, int32_t nq, int32_t k, int32_t* sel, void* ws,
+                               hipStream_t s);
+
 // Candidate scores + top-k among them in one launch (n_cand <= 16384); `ctr`
 // is nq counters that must be zero and are left zero.
 hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
@@ -53,6 +69,9 @@ hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, c
 hipError_t launch_expand_blocks(const int32_t* blocks, int32_t nq, int32_t nb, int32_t block,
                                 const int32_t* q_pos, int32_t* tokens, hipStream_t s);
 
+// From this many queries on, attention runs one workgroup per query (no
+// workspace); below it, each query is split over several workgroups.
+constexpr int32_t kManyQueries = 256;
 size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window);
 hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
                               const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,

@@ -81,23 +81,26 @@ __device__ __forceinline__ void wave_find_bucket(const int* hist, int nb, int re
     }
 }
 
-// Exact (tau, need) of the kk-th key among the selectable keys keys[0..m) in
-// LDS.  The top `known` bits (0 or 12) are shared by every key that can reach
-// the kk-th place (the caller already resolved them); the remaining bits are
+// Exact (tau, need) of the kk-th key among the selectable keys K(0..m).  The
+// top `known` bits (0 or 12) are shared by every key that can reach the kk-th
+// place (the caller already resolved them, `prefix` holds them); K is called
+// once per slot and digit pass, so it may recompute keys.  The remaining bits are
 // resolved in digits of 12, 12 and 8 bits, highest first, stopping as soon as
 // a whole bucket is taken.  hist needs kHistWords ints, res 4 ints of LDS.
 // NT threads; every thread returns the same result.
-template <int NT>
-__device__ void lds_kth(const uint32_t* keys, int m, int kk, int known, int* hist, int* res,
-                        uint32_t& tau, int& need) {
+template <int NT, class KeyFn>
+__device__ void kth_fn(KeyFn K, int64_t m, int kk, int known, uint32_t prefix, int* hist, int* res,
+                       uint32_t& tau, int& need) {
     const int tid = threadIdx.x;
     tau = 0u;
     need = 0;
     if (m <= 0 || kk <= 0) return;
-    uint32_t prefix = 0u, mask = 0u;
+    uint32_t mask = 0u;
     if (known > 0) {
         mask = 0xFFFFFFFFu << (32 - known);
-        prefix = keys[0] & mask;
+        prefix &= mask;
+    } else {
+        prefix = 0u;
     }
     int rem = kk;
     for (int hi_bit = 32 - known; hi_bit > 0;) {
@@ -107,10 +110,10 @@ __device__ void lds_kth(const uint32_t* keys, int m, int kk, int known, int* his
         const uint32_t dm = (uint32_t)nb - 1u;
         for (int i = tid; i < hidx(nb); i += NT) hist[i] = 0;
         __syncthreads();
-        for (int i0 = tid; i0 < m; i0 += 4 * NT) {
+        for (int64_t i0 = tid; i0 < m; i0 += 4 * NT) {
             uint32_t kv[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) kv[u] = (i0 + u * NT < m) ? keys[i0 + u * NT] : 0u;
+            for (int u = 0; u < 4; ++u) kv[u] = (i0 + u * NT < m) ? K(i0 + u * NT) : 0u;
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 if (kv[u] && (kv[u] & mask) == prefix)
@@ -140,6 +143,14 @@ __device__ void lds_kth(const uint32_t* keys, int m, int kk, int known, int* his
     }
     tau = prefix;
     need = rem;
+}
+
+// kth_fn over keys held in LDS.
+template <int NT>
+__device__ void lds_kth(const uint32_t* keys, int m, int kk, int known, int* hist, int* res,
+                        uint32_t& tau, int& need) {
+    kth_fn<NT>([&](int64_t i) { return keys[i]; }, m, kk, known, m > 0 ? keys[0] : 0u, hist, res,
+               tau, need);
 }
 
 // Ordered compaction of slots [0, n) with keys K(i): writes the chosen slots

@@ -377,13 +377,289 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     if (tid == 0) ctr[qi] = 0u;  // ready for the next call
 }
 
+// ---------------------------------------------------------------------------
+// Many queries (a prefill chunk): one workgroup of 4 waves per query, no
+// workspace.  Each wave walks its share of the entries in tiles of 32 with an
+// online softmax (running max, sum and unnormalised O per head, kept in
+// registers) and loads the next tile's rows while the current one computes;
+// the 4 waves are combined at the end.  FP4 rows are dequantised with their
+// E8M0 scale by v_cvt_scalef32_pk_bf16_fp4 (exact: an E2M1 value times a power
+// of two fits bf16), so both products take plain bf16 operands.
+//
+// Entry slots of a tile: lane row n16 loads entries 2 n16 and 2 n16 + 1 of the
+// tile (MFMA tiles 0 and 1), so a lane holds two neighbouring slots of every V
+// dim and writes V^T with one dword per dim.  Lane group g loads dims
+// 32 g .. 32 g + 31 of K and of V (one scale block each).  The K fragment of
+// k-step kb is dims 32 g + 8 kb .. + 8 (the Q fragment uses the same map).
+constexpr int kLW = 4;                       // waves per workgroup
+constexpr int kVtRow = 16;                   // dwords per V^T row (32 slots)
+constexpr int kVtWave = kHeadDim * kVtRow + 4 * kVtRow;  // + a 16-dword skew per 32 rows
+
+__device__ __forceinline__ int vt_addr(int d) { return d * kVtRow + (d >> 5) * kVtRow; }
+
+struct LoopLds {
+    union {
+        uint32_t vt[kLW][kVtWave];
+        float obuf[kLW][kHeads][kHeadDim + 4];
+    } u;
+    float alpha[kLW][kHeads];
+    float m[kLW][kHeads];
+    float l[kLW][kHeads];
+};
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t w, float sc, int sel) {
+    bf16x2_t r;
+    switch (sel) {
+        case 0: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0); break;
+        case 1: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1); break;
+        case 2: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2); break;
+        default: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3); break;
+    }
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 32 FP4 codes (16 bytes) of one scale block -> 16 dwords of bf16 pairs.
+__device__ __forceinline__ void dq_block(uint4 c, float sc, uint32_t (&o)[16]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[4 * i + 0] = cvt_fp4x2(w[i], sc, 0);
+        o[4 * i + 1] = cvt_fp4x2(w[i], sc, 1);
+        o[4 * i + 2] = cvt_fp4x2(w[i], sc, 2);
+        o[4 * i + 3] = cvt_fp4x2(w[i], sc, 3);
+    }
+}
+
+struct RowRaw {  // the FP4 data one lane loads for one entry
+    uint4 k, v;
+    uint32_t sk, sv;  // scale bytes of the lane's K and V blocks
+};
+
+// grid nq, kLW * 64 threads.
+__global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint16_t* __restrict__ q,
+                                                        const int32_t* __restrict__ q_pos,
+                                                        const int32_t* __restrict__ q_seq,
+                                                        const int32_t* __restrict__ sel, int32_t k,
+                                                        LocalView loc, float sm_scale,
+                                                        uint16_t* __restrict__ out) {
+    __shared__ LoopLds sh;
+    const int qi = blockIdx.x, tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int n16 = lane & 15, g = lane >> 4;
+    uint32_t* vt = sh.u.vt[wave];
+
+    const int32_t seq = q_seq ? q_seq[qi] : qi;
+    int64_t t = q_pos[qi];
+    if (seq < 0 || seq >= c.n_seq) t = -1;
+    if (t >= c.t_cap) t = c.t_cap - 1;
+    int64_t w0 = t - loc.window + 1;
+    if (w0 < loc.lo) w0 = loc.lo;
+    if (w0 < 0) w0 = 0;
+    const int64_t nw = (loc.window > 0 && t >= w0) ? t - w0 + 1 : 0;
+    const int64_t n_ent = t >= 0 ? (int64_t)k + nw : 0;
+    const int n_tiles = (int)((n_ent + 31) / 32);
+
+    // Q^T as the B operand of S: head n16, dims 32 g + 8 kb .. + 8 at step kb
+    bf16x8_t qf[4];
+    {
+        const uint4* qr = reinterpret_cast<const uint4*>(q + ((int64_t)qi * kHeads + n16) * kHeadDim + 32 * g);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const uint4 v = qr[kb];
+            qf[kb] = as_bf16x8(v.x, v.y, v.z, v.w);
+        }
+    }
+    const float zs = sm_scale * kLog2e;
+    const float NEG = -__builtin_inff();
+
+    // kind of entry e: 0 none, 1 global FP4, 2 global bf16, 3 local bf16; row index
+    auto locate = [&](int64_t e, int& kind, int64_t& row) {
+        kind = 0;
+        row = 0;
+        if (e < k) {
+            const int64_t j = sel[(int64_t)qi * k + e];
+            if (j >= 0 && j <= t) {
+                kind = c.fp4 ? 1 : 2;
+                row = (int64_t)seq * c.t_cap + j;
+            }
+        } else if (e - k < nw) {
+            kind = 3;
+            row = (int64_t)seq * loc.cap + (w0 + (e - k)) % loc.cap;
+        }
+    };
+    auto load_fp4 = [&](int64_t row, RowRaw& r) {
+        const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row * kRowCodes;
+        r.k = *reinterpret_cast<const uint4*>(cr + 16 * g);
+        r.v = *reinterpret_cast<const uint4*>(cr + 64 + 16 * g);
+        const uint2 sc = *reinterpret_cast<const uint2*>(c.scales + row * kRowScales);
+        r.sk = (sc.x >> (8 * g)) & 0xFFu;
+        r.sv = (sc.y >> (8 * g)) & 0xFFu;
+    };
+
+    float m_run = NEG, l_part = 0.f;
+    f32x4_t o[8];
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8) o[t8] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    // tiles of this wave: wave, wave + kLW, ...; the FP4 rows of the next tile
+    // are loaded as soon as the current ones are decoded
+    int kind[2];
+    int64_t row[2];
+    RowRaw raw[2];
+    int tile = wave;
+    if (tile < n_tiles) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            locate((int64_t)tile * 32 + 2 * n16 + u, kind[u], row[u]);
+            if (kind[u] == 1) load_fp4(row[u], raw[u]);
+        }
+    }
+    for (; tile < n_tiles; tile += kLW) {
+        // ---- rows -> bf16 K fragments; V dims 32 g .. + 32 go to V^T at once
+        bf16x8_t kf[2][4];
+        const uint64_t vm0 = __ballot(kind[0] != 0) & 0xFFFFull;  // bit n16: slot row valid
+        const uint64_t vm1 = __ballot(kind[1] != 0) & 0xFFFFull;
+        uint32_t vd0[16];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            uint32_t kd[16], vd[16];
+            if (kind[u] == 1) {
+                dq_block(raw[u].k, e8m0_value(raw[u].sk), kd);
+                dq_block(raw[u].v, e8m0_value(raw[u].sv), vd);
+            } else if (kind[u] >= 2) {
+                const uint16_t* kr = kind[u] == 2 ? static_cast<const uint16_t*>(c.data) + row[u] * kRowBf16
+                                                  : loc.k + row[u] * kHeadDim;
+                const uint16_t* vr = kind[u] == 2 ? kr + kHeadDim : loc.v + row[u] * kHeadDim;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 a = *reinterpret_cast<const uint4*>(kr + 32 * g + 8 * i);
+                    const uint4 b = *reinterpret_cast<const uint4*>(vr + 32 * g + 8 * i);
+                    kd[4 * i] = a.x; kd[4 * i + 1] = a.y; kd[4 * i + 2] = a.z; kd[4 * i + 3] = a.w;
+                    vd[4 * i] = b.x; vd[4 * i + 1] = b.y; vd[4 * i + 2] = b.z; vd[4 * i + 3] = b.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) kd[i] = vd[i] = 0u;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                kf[u][kb] = as_bf16x8(kd[4 * kb], kd[4 * kb + 1], kd[4 * kb + 2], kd[4 * kb + 3]);
+            if (u == 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) vd0[i] = vd[i];
+            } else {
+                // V^T: dims d, d + 1 of slots 2 n16, 2 n16 + 1 -> two dwords
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int d = 32 * g + 2 * i;
+                    vt[vt_addr(d) + n16] = __builtin_amdgcn_perm(vd[i], vd0[i], 0x05040100u);
+                    vt[vt_addr(d + 1) + n16] = __builtin_amdgcn_perm(vd[i], vd0[i], 0x07060302u);
+                }
+            }
+        }
+        const int next = tile + kLW;
+        if (next < n_tiles) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                locate((int64_t)next * 32 + 2 * n16 + u, kind[u], row[u]);
+                if (kind[u] == 1) load_fp4(row[u], raw[u]);
+            }
+        }
+        // ---- S^T = K Q^T: lane holds head n16, rows 4 g + r of tile u = slot 8 g + 2 r + u
+        float s[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][kb], qf[kb], z, 0, 0, 0);
+            const uint64_t vm = u ? vm1 : vm0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[u][r] = ((vm >> (4 * g + r)) & 1) ? z[r] * zs : NEG;
+        }
+        float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_new == m_run) ? 1.f : exp2f(m_run - m_new);  // m_run = -inf: 0
+        float p[2][4];
+        float ps = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[u][r] = (s[u][r] == NEG) ? 0.f : exp2f(s[u][r] - m_new);
+                ps += p[u][r];
+            }
+        l_part = fmaf(l_part, alpha, ps);
+        m_run = m_new;
+        // ---- rescale O (heads 4 g + r of this lane) when a running max moved
+        if (__ballot(alpha != 1.f)) {
+            if (g == 0) sh.alpha[wave][n16] = alpha;
+            const float4 a4 = *reinterpret_cast<const float4*>(&sh.alpha[wave][4 * g]);
+#pragma unroll
+            for (int t8 = 0; t8 < 8; ++t8) {
+                o[t8][0] *= a4.x;
+                o[t8][1] *= a4.y;
+                o[t8][2] *= a4.z;
+                o[t8][3] *= a4.w;
+            }
+        }
+        // ---- O += P V: A = P (head n16, slots 8 g + j, j = 2 r + u), B = V (slots, dim n16)
+        const bf16x8_t pf = as_bf16x8(__builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][0], (__bf16)p[1][0]}),
+                                      __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][1], (__bf16)p[1][1]}),
+                                      __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][2], (__bf16)p[1][2]}),
+                                      __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][3], (__bf16)p[1][3]}));
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) {
+            const uint4 vv = *reinterpret_cast<const uint4*>(&vt[vt_addr(16 * t8 + n16) + 4 * g]);
+            o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, as_bf16x8(vv.x, vv.y, vv.z, vv.w), o[t8], 0, 0, 0);
+        }
+    }
+    // ---- combine the waves
+    l_part += __shfl_xor(l_part, 16, 64);
+    l_part += __shfl_xor(l_part, 32, 64);
+    if (g == 0) {
+        sh.m[wave][n16] = m_run;
+        sh.l[wave][n16] = l_part;
+    }
+    __syncthreads();  // every wave is done with its V^T tile
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sh.u.obuf[wave][4 * g + r][16 * t8 + n16] = o[t8][r];
+    __syncthreads();
+    const int h = tid >> 4, d0 = (tid & 15) * 8;  // 256 threads: head h, 8 dims
+    float M = NEG;
+#pragma unroll
+    for (int w = 0; w < kLW; ++w) M = fmaxf(M, sh.m[w][h]);
+    float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (M != NEG) {
+#pragma unroll
+        for (int w = 0; w < kLW; ++w) {
+            const float mw = sh.m[w][h];
+            const float f = (mw == NEG) ? 0.f : exp2f(mw - M);
+            L = fmaf(sh.l[w][h], f, L);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(sh.u.obuf[w][h][d0 + i], f, acc[i]);
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t* orow = out + ((int64_t)qi * kHeads + h) * kHeadDim + d0;
+    *reinterpret_cast<uint4*>(orow) =
+        make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                   pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
+}
+
 static int32_t attn_chunks(int32_t k, int32_t window) {
     return (k + window + kWgEntries - 1) / kWgEntries;
 }
 
 size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window) {
     const int64_t nc = attn_chunks(k, window);
-    if (nc <= 1) return 0;
+    if (nc <= 1 || nq >= kManyQueries) return 0;
     return (size_t)nq * nc * kHeads * (kHeadDim + 2) * sizeof(float) + (size_t)nq * sizeof(uint32_t);
 }
 
@@ -392,6 +668,11 @@ hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32
                               const LocalView& loc, float sm_scale, uint16_t* out, void* ws,
                               hipStream_t s) {
     if (nq == 0) return hipSuccess;
+    if (nq >= kManyQueries) {  // enough queries to fill the GPU one workgroup each
+        hipLaunchKernelGGL(k_attn_loop, dim3((uint32_t)nq), dim3(kLW * 64), 0, s, c, q, q_pos, q_seq,
+                           sel, k, loc, sm_scale, out);
+        return hipGetLastError();
+    }
     int32_t nc = attn_chunks(k, loc.window);
     if (nc < 1) nc = 1;
     float* ws_o = static_cast<float*>(ws);

@@ -1,0 +1,628 @@
+// k_prefill.hip -- indexer top-k of a prefill chunk: many queries on one
+// sequence, each at its own position, select their k best positions by
+// q_I . k_I over the causal range ("CED: Continuing Context with a Causal
+// Encoder and Decoder", section "Why Prefill Recomputes a Recent Segment",
+// Fig. 6: the recent positions pass through the decoder again and each one
+// selects as a decode query does, section "Selecting Positions and Reading
+// Values with Attention", Fig. 4).
+//
+// The score matrix (queries x positions x 64 dims) is a dense contraction; it
+// runs on v_mfma_f32_16x16x32_bf16 and is never written out.  Four launches:
+//   1. cmax:   scores on MFMA; per query, the maximum key of every 16-position
+//              chunk (1/16 of the scores) goes to the workspace.
+//   2. thresh: per query, thr = the k-th largest chunk maximum.  Each of the k
+//              chunks at or above thr holds a position scoring >= thr, so at
+//              least k positions pass thr and every top-k position does.
+//   3. filter: the same MFMA scores again (same instructions, so bit-identical);
+//              positions with key >= thr are appended, with their keys, to the
+//              query's candidate list (about 1.1 k of them for i.i.d. scores).
+//   4. select: per query, candidates are put in position order through an
+//              LDS bitmap, then the exact (score desc, position asc) top-k is
+//              taken and written ascending.  A query whose list overflowed
+//              (ties, short rows) is resolved exactly by recomputing its scores.
+#include "csa2_dev.h"
+#include "csa2_kernels.h"
+#include "csa2_select.h"
+
+namespace csa2 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 pf_bf16x8;
+typedef __attribute__((ext_vector_type(4))) float pf_f32x4;
+
+constexpr int kPfQB = 8;        // 16-query blocks per wave
+constexpr int kPfQ = 16 * kPfQB; // queries per workgroup tile (every wave takes all of them)
+constexpr int kPfSpan = 2048;   // positions per chunk-maximum workgroup (8 steps of 4 waves x 64)
+constexpr int kPfFiltSpan = 1024;  // positions per filter workgroup
+constexpr int kPfChunk = 16;    // positions per chunk maximum
+constexpr int kPfLB = 24;       // LDS candidate slots per query in the filter (about 18 expected)
+constexpr int kPfSelNT = 512;
+
+__device__ __forceinline__ int64_t pf_clamp_pos(int64_t p, int64_t t_cap) {
+    return p < 0 ? -1 : (p >= t_cap ? t_cap - 1 : p);
+}
+
+// Query fragments of the tile's kPfQ queries (B operand): lane column n16 of
+// block i is query q0 + 16 i + n16, dims 32 kb + 8 g .. + 8.
+__device__ __forceinline__ void pf_load_q(const uint16_t* __restrict__ q_idx, int32_t nq,
+                                          int64_t q0, int n16, int g, pf_bf16x8 (&a)[kPfQB][2]) {
+#pragma unroll
+    for (int i = 0; i < kPfQB; ++i) {
+        const int64_t qq = q0 + 16 * i + n16;
+        // a query past nq repeats the last one; its scores are never used
+        const uint4* row = reinterpret_cast<const uint4*>(q_idx + (qq < nq ? qq : nq - 1) * kIdxDim + 8 * g);
+        a[i][0] = __builtin_bit_cast(pf_bf16x8, row[0]);
+        a[i][1] = __builtin_bit_cast(pf_bf16x8, row[4]);
+    }
+}
+
+// Key fragments of positions t0 .. t0 + 63 (A operand): lane row n16 of block
+// j is position t0 + 16 j + n16.  Rows past t_cap repeat the last row: every
+// query masks those positions, so no branch guards the loads.
+__device__ __forceinline__ void pf_load_k(const uint16_t* __restrict__ kseq, int32_t t_cap,
+                                          int32_t t0, int n16, int g, pf_bf16x8 (&b)[4][2]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int32_t tt = min(t0 + 16 * j + n16, t_cap - 1);
+        const uint4* row = reinterpret_cast<const uint4*>(kseq + (int64_t)tt * kIdxDim + 8 * g);
+        b[j][0] = __builtin_bit_cast(pf_bf16x8, row[0]);
+        b[j][1] = __builtin_bit_cast(pf_bf16x8, row[4]);
+    }
+}
+
+// Scores of position block j against query block i: lane holds query
+// q0 + 16 i + n16 at positions t0 + 16 j + 4 g + r, r = 0..3.  The cmax and
+// filter kernels both call this, so their scores agree bit for bit.
+__device__ __forceinline__ pf_f32x4 pf_tile(const pf_bf16x8 (&kf)[2], const pf_bf16x8 (&qf)[2]) {
+    pf_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1], qf[1], c, 0, 0, 0);
+    return c;
+}
+
+// Clamped position of the lane's query of each block (-1 past nq), and the
+// largest and smallest of them over the tile (wave-uniform).  The loads are
+// unconditional (index clamped to nq - 1), so all of them are in flight at once.
+__device__ __forceinline__ void pf_tile_pos(const int32_t* __restrict__ q_pos, int32_t nq,
+                                            int64_t t_cap, int64_t q0, int n16,
+                                            int32_t (&pos)[kPfQB], int32_t& tmax, int32_t& tmin) {
+    int32_t raw[kPfQB];
+#pragma unroll
+    for (int i = 0; i < kPfQB; ++i) {
+        const int64_t qq = q0 + 16 * i + n16;
+        raw[i] = q_pos[qq < nq ? qq : nq - 1];
+    }
+    tmax = -1;
+    tmin = INT32_MAX;
+#pragma unroll
+    for (int i = 0; i < kPfQB; ++i) {
+        const int64_t qq = q0 + 16 * i + n16;
+        pos[i] = qq < nq ? (int32_t)pf_clamp_pos(raw[i], t_cap) : -1;
+        tmax = max(tmax, pos[i]);
+        tmin = min(tmin, pos[i]);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        tmax = max(tmax, __shfl_xor(tmax, o, 64));
+        tmin = min(tmin, __shfl_xor(tmin, o, 64));
+    }
+    tmax = __builtin_amdgcn_readfirstlane(tmax);  // wave-uniform: scalar registers
+    tmin = __builtin_amdgcn_readfirstlane(tmin);
+}
+
+// Runs f(kf, t0) over this wave's steps t0 = t_first + 256 s (s < SPAN /
+// 256, t0 < t_cap, t0 <= tmax).  The next step's key fragments are loaded
+// while the current step computes; the load is issued on every step (rows are
+// clamped, so it stays in bounds), which keeps the number of loads in flight
+// the same on every path and the compiler's wait before the MFMAs covers only
+// the fragments of the current step.  One copy of the body keeps the kernel
+// small enough for the instruction cache.
+template <int SPAN, class StepFn>
+__device__ __forceinline__ void pf_sweep(const uint16_t* __restrict__ kseq, int32_t t_cap,
+                                         int32_t t_first, int32_t tmax, int n16, int g, StepFn f) {
+    auto valid = [&](int32_t t, int s) { return s < SPAN / 256 && t < t_cap && t <= tmax; };
+    if (!valid(t_first, 0)) return;
+    pf_bf16x8 kn[4][2];
+    pf_load_k(kseq, t_cap, t_first, n16, g, kn);
+    for (int32_t t0 = t_first, s = 0; valid(t0, s); t0 += 256, ++s) {
+        pf_bf16x8 kf[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            kf[j][0] = kn[j][0];
+            kf[j][1] = kn[j][1];
+        }
+        pf_load_k(kseq, t_cap, t0 + 256, n16, g, kn);
+        f(kf, t0);
+    }
+}
+
+// ---- 1. chunk maxima -------------------------------------------------------
+// A chunk is the 16 positions one lane holds for one query in a 64-position
+// step: t0 + 16 j + 4 g + r (j, r = 0..3), chunk index t0 / 16 + g, so the
+// maximum needs no cross-lane traffic.  Chunk c holds a position <= t exactly
+// when c < pf_nchunks(t).
+// grid (ceil(nq / kPfQ), ceil(t_cap / kPfSpan)), 256 threads.  cmax: [nq][ldc] keys.
+template <bool MASK>
+__device__ __forceinline__ void pf_cmax_step(const pf_bf16x8 (&kf)[4][2],
+                                             const pf_bf16x8 (&qf)[kPfQB][2], int32_t t0, int g,
+                                             const int32_t (&pos)[kPfQB], float (&m)[kPfQB]) {
+    const float NEG = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        pf_f32x4 c[kPfQB];
+#pragma unroll
+        for (int i = 0; i < kPfQB; ++i) c[i] = pf_tile(kf[j], qf[i]);
+        const int32_t tt = t0 + 16 * j + 4 * g;
+#pragma unroll
+        for (int i = 0; i < kPfQB; ++i) {
+            if (MASK) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (tt + r > pos[i]) c[i][r] = NEG;
+            }
+            m[i] = fmaxf(m[i], fmaxf(fmaxf(c[i][0], c[i][1]), fmaxf(c[i][2], c[i][3])));
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_pf_cmax(const uint16_t* __restrict__ kseq, int32_t t_cap,
+                                                 const uint16_t* __restrict__ q_idx,
+                                                 const int32_t* __restrict__ q_pos, int32_t nq,
+                                                 uint32_t* __restrict__ cmax, int64_t ldc) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n16 = lane & 15, g = lane >> 4;
+    const int64_t q0 = (int64_t)blockIdx.x * kPfQ;
+    const int32_t span0 = (int32_t)blockIdx.y * kPfSpan;
+    int32_t tmax, tmin, pos[kPfQB];
+    pf_tile_pos(q_pos, nq, t_cap, q0, n16, pos, tmax, tmin);
+    if (span0 > tmax) return;
+    pf_bf16x8 qf[kPfQB][2];
+    pf_load_q(q_idx, nq, q0, n16, g, qf);
+    const float NEG = -__builtin_inff();
+    pf_sweep<kPfSpan>(kseq, t_cap, span0 + wave * 64, tmax, n16, g,
+             [&](const pf_bf16x8 (&kf)[4][2], int32_t t0) {
+                 float m[kPfQB];
+#pragma unroll
+                 for (int i = 0; i < kPfQB; ++i) m[i] = NEG;
+                 if (t0 + 63 <= tmin)  // no query of the tile masks these positions
+                     pf_cmax_step<false>(kf, qf, t0, g, pos, m);
+                 else
+                     pf_cmax_step<true>(kf, qf, t0, g, pos, m);
+                 const int64_t c0 = t0 / kPfChunk + g;
+#pragma unroll
+                 for (int i = 0; i < kPfQB; ++i) {
+                     const int64_t qq = q0 + 16 * i + n16;
+                     if (qq < nq) cmax[qq * ldc + c0] = score_key(m[i]);
+                 }
+             });
+}
+
+// Chunks holding at least one position <= t.
+__device__ __forceinline__ int64_t pf_nchunks(int64_t t) {
+    if (t < 0) return 0;
+    const int64_t g = (t & 63) >> 2;
+    return 4 * (t >> 6) + (g < 3 ? g : 3) + 1;
+}
+
+// ---- 2. thresholds -----------------------------------------------------------
+// key -> the float with that key (keys below that of -inf give a NaN, which
+// lets every score through the float pre-filter of the filter kernel).
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+struct PfThrLds {
+    int hist[kHistWords];
+    int res[4];
+};
+
+// grid nq, 256 threads, dynamic LDS ldc keys.
+__global__ __launch_bounds__(256) void k_pf_thresh(const uint32_t* __restrict__ cmax, int64_t ldc,
+                                                   const int32_t* __restrict__ q_pos,
+                                                   int64_t t_cap, int32_t k,
+                                                   float* __restrict__ thr_f,
+                                                   uint32_t* __restrict__ thr_k,
+                                                   uint32_t* __restrict__ cnt) {
+    extern __shared__ uint32_t pf_keys[];
+    __shared__ PfThrLds sh;
+    const int q = blockIdx.x, tid = threadIdx.x;
+    const int64_t t = pf_clamp_pos(q_pos[q], t_cap);
+    const int64_t nc = pf_nchunks(t);
+    uint32_t thr = 1u;  // fewer chunks than k: every valid position is a candidate
+    if (nc >= k) {
+        // ldc is a multiple of 4 and the row is 16-byte aligned: stage whole
+        // uint4s (keys past nc are never read), eight loads in flight per thread
+        const uint4* src = reinterpret_cast<const uint4*>(cmax + (int64_t)q * ldc);
+        uint4* dst = reinterpret_cast<uint4*>(pf_keys);
+        const int nv = (int)((nc + 3) / 4);
+        for (int i0 = tid; i0 < nv; i0 += 8 * 256) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = (i0 + u * 256 < nv) ? src[i0 + u * 256] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u * 256 < nv) dst[i0 + u * 256] = v[u];
+        }
+        __syncthreads();
+        uint32_t tau;
+        int need;
+        lds_kth<256>(pf_keys, (int)nc, k, 0, sh.hist, sh.res, tau, need);
+        thr = need > 0 ? tau : tau + 1u;
+        if (thr < 1u) thr = 1u;
+    }
+    if (tid == 0) {
+        thr_k[q] = thr;
+        thr_f[q] = key_float(thr);
+        cnt[q] = 0u;
+    }
+}
+
+// ---- 3. filter ---------------------------------------------------------------
+// Pre-filter granularity: a lane's four scores of one tile (one query, four
+// consecutive positions) are queued together when any of them passes, so one
+// wave-wide compaction serves four compares.
+constexpr int kPfQueue = 576;  // per-wave queue entries: one j-block (8 x 64) past the drain mark
+
+struct PfFiltLds {
+    uint2 buf[kPfQ][kPfLB];          // per-query candidates of this workgroup
+    uint4 qscore[4][kPfQueue];       // per-wave queue: the four scores of an entry
+    uint32_t qtag[4][kPfQueue];      // and (first position << 7 | query in tile)
+    int n[kPfQ];
+    int base[kPfQ];
+    int32_t pos[kPfQ];
+    uint32_t thr[kPfQ];
+};
+
+// Exact test of the wave's queued scores (causal mask, key >= thr); the ones
+// that pass go to their query's list.
+__device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int qn, int64_t q0,
+                                         uint32_t* __restrict__ cnt, uint2* __restrict__ cand,
+                                         int32_t cap) {
+    for (int e = lane; e < qn; e += 64) {
+        const uint4 sc = sh.qscore[wave][e];
+        const uint32_t tag = sh.qtag[wave][e];
+        const int ql = (int)(tag & 127u);
+        const int32_t t0 = (int32_t)(tag >> 7);
+        const int32_t lim = sh.pos[ql];
+        const uint32_t thr = sh.thr[ql];
+        const uint32_t v[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t key = score_key(__uint_as_float(v[r]));
+            const int32_t tt = t0 + r;
+            if (tt <= lim && key >= thr) {
+                const int slot = atomicAdd(&sh.n[ql], 1);
+                if (slot < kPfLB) {
+                    sh.buf[ql][slot] = make_uint2((uint32_t)tt, key);
+                } else {  // this workgroup's list of the query is full: straight to its global list
+                    const uint32_t gs = atomicAdd(&cnt[q0 + ql], 1u);
+                    if (gs < (uint32_t)cap) cand[(q0 + ql) * cap + gs] = make_uint2((uint32_t)tt, key);
+                }
+            }
+        }
+    }
+}
+
+// grid (ceil(nq / kPfQ), ceil(t_cap / kPfFiltSpan)), 256 threads.  cand: [nq][cap]
+// (position, key); cnt: [nq].
+__global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ kseq, int32_t t_cap,
+                                                   const uint16_t* __restrict__ q_idx,
+                                                   const int32_t* __restrict__ q_pos, int32_t nq,
+                                                   const float* __restrict__ thr_f,
+                                                   const uint32_t* __restrict__ thr_k,
+                                                   uint32_t* __restrict__ cnt,
+                                                   uint2* __restrict__ cand, int32_t cap) {
+    __shared__ PfFiltLds sh;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, g = lane >> 4;
+    const int64_t q0 = (int64_t)blockIdx.x * kPfQ;
+    const int32_t span0 = (int32_t)blockIdx.y * kPfFiltSpan;
+    int32_t tmax, tmin, pos[kPfQB];
+    pf_tile_pos(q_pos, nq, t_cap, q0, n16, pos, tmax, tmin);
+    if (span0 > tmax) return;  // uniform over the workgroup
+    if (tid < kPfQ) {
+        const int64_t qq = q0 + tid;
+        sh.pos[tid] = qq < nq ? (int32_t)pf_clamp_pos(q_pos[qq], t_cap) : -1;
+        sh.thr[tid] = qq < nq ? thr_k[qq] : 0xFFFFFFFFu;
+        sh.n[tid] = 0;
+    }
+    float th[kPfQB];
+#pragma unroll
+    for (int i = 0; i < kPfQB; ++i) {
+        const int64_t qq = q0 + 16 * i + n16;
+        const float tv = thr_f[qq < nq ? qq : nq - 1];
+        th[i] = qq < nq ? tv : __builtin_inff();
+    }
+    pf_bf16x8 qf[kPfQB][2];
+    pf_load_q(q_idx, nq, q0, n16, g, qf);
+    __syncthreads();
+    int qn = 0;  // entries in this wave's queue (wave-uniform)
+    pf_sweep<kPfFiltSpan>(kseq, t_cap, span0 + wave * 64, tmax, n16, g,
+             [&](const pf_bf16x8 (&kf)[4][2], int32_t t0) {
+#pragma unroll
+                 for (int j = 0; j < 4; ++j) {
+                     pf_f32x4 c[kPfQB];
+#pragma unroll
+                     for (int i = 0; i < kPfQB; ++i) c[i] = pf_tile(kf[j], qf[i]);
+                     const uint32_t tag = (((uint32_t)t0 + 16u * j + 4u * g) << 7) | (uint32_t)n16;
+#pragma unroll
+                     for (int i = 0; i < kPfQB; ++i) {
+                         // float pre-filter: passes every key >= thr (and NaN)
+                         const bool h = !(c[i][0] < th[i]) || !(c[i][1] < th[i]) ||
+                                        !(c[i][2] < th[i]) || !(c[i][3] < th[i]);
+                         const uint64_t mask = __ballot(h);
+                         if (mask) {
+                             if (h) {
+                                 const int off = qn + lanes_below(mask);
+                                 sh.qscore[wave][off] =
+                                     make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
+                                                __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
+                                 sh.qtag[wave][off] = tag + 16u * i;
+                             }
+                             qn += __popcll(mask);
+                         }
+                     }
+                     if (qn > kPfQueue - kPfQB * 64) {  // room for the next j-block's entries
+                         pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
+                         qn = 0;
+                     }
+                 }
+             });
+    pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
+    __syncthreads();
+    if (tid < kPfQ) {
+        const int m = min(sh.n[tid], kPfLB);
+        sh.base[tid] = m > 0 ? (int)atomicAdd(&cnt[q0 + tid], (uint32_t)m) : 0;
+    }
+    __syncthreads();
+    for (int e = tid; e < kPfQ * kPfLB; e += 256) {
+        const int ql = e / kPfLB, j = e % kPfLB;
+        if (j < min(sh.n[ql], kPfLB) && sh.base[ql] + j < cap)
+            cand[(q0 + ql) * cap + sh.base[ql] + j] = sh.buf[ql][j];
+    }
+}
+
+// ---- 4. select ---------------------------------------------------------------
+struct PfSelLds {
+    int hist[kHistWords];
+    uint32_t skey[kPfCap];
+    int32_t spos[kPfCap];
+    int tmp[kPfSelNT / 64 + 1];
+    int wtmp[2 * kPfSelNT / 64];
+    int res[4];
+};
+
+// Exact top-k of one query by recomputing its scores (VALU dot products): the
+// path of a query whose candidate list overflowed.
+__device__ void pf_select_recompute(const uint16_t* __restrict__ kseq, const uint16_t* __restrict__ qr,
+                                    int64_t t, int32_t k, int32_t* __restrict__ dst, PfSelLds& sh) {
+    float qf[kIdxDim];
+#pragma unroll
+    for (int d = 0; d < kIdxDim; d += 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qr + d);
+        qf[d + 0] = bf16_lo(v.x); qf[d + 1] = bf16_hi(v.x);
+        qf[d + 2] = bf16_lo(v.y); qf[d + 3] = bf16_hi(v.y);
+        qf[d + 4] = bf16_lo(v.z); qf[d + 5] = bf16_hi(v.z);
+        qf[d + 6] = bf16_lo(v.w); qf[d + 7] = bf16_hi(v.w);
+    }
+    auto K = [&](int64_t i) -> uint32_t {
+        if (i > t) return 0u;
+        const uint4* row = reinterpret_cast<const uint4*>(kseq + i * kIdxDim);
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const uint4 v = row[w];
+            s = fmaf(qf[8 * w + 0], bf16_lo(v.x), s); s = fmaf(qf[8 * w + 1], bf16_hi(v.x), s);
+            s = fmaf(qf[8 * w + 2], bf16_lo(v.y), s); s = fmaf(qf[8 * w + 3], bf16_hi(v.y), s);
+            s = fmaf(qf[8 * w + 4], bf16_lo(v.z), s); s = fmaf(qf[8 * w + 5], bf16_hi(v.z), s);
+            s = fmaf(qf[8 * w + 6], bf16_lo(v.w), s); s = fmaf(qf[8 * w + 7], bf16_hi(v.w), s);
+        }
+        return score_key(s);
+    };
+    uint32_t tau;
+    int need;
+    kth_fn<kPfSelNT>(K, t + 1, k, 0, 0u, sh.hist, sh.res, tau, need);
+    ordered_write<kPfSelNT>(K, t + 1, tau, need, nullptr, k, dst, sh.wtmp);
+}
+
+// grid nq, 512 threads, dynamic LDS: bitmap [nw] words then [nw] u16 prefixes,
+// nw = ceil(t_cap / 32).
+__global__ __launch_bounds__(kPfSelNT) void k_pf_select(const uint16_t* __restrict__ kseq,
+                                                        int64_t t_cap,
+                                                        const uint16_t* __restrict__ q_idx,
+                                                        const int32_t* __restrict__ q_pos,
+                                                        int32_t k, const uint32_t* __restrict__ cnt,
+                                                        const uint2* __restrict__ cand, int32_t cap,
+                                                        int32_t* __restrict__ sel) {
+    extern __shared__ uint32_t pf_bits[];
+    __shared__ PfSelLds sh;
+    const int q = blockIdx.x, tid = threadIdx.x;
+    int32_t* dst = sel + (int64_t)q * k;
+    const int64_t t = pf_clamp_pos(q_pos[q], t_cap);
+    if (t < 0) {
+        for (int i = tid; i < k; i += kPfSelNT) dst[i] = -1;
+        return;
+    }
+    const uint32_t n = cnt[q];
+    if (n > (uint32_t)cap) {
+        pf_select_recompute(kseq, q_idx + (int64_t)q * kIdxDim, t, k, dst, sh);
+        return;
+    }
+    const int nw = (int)(t / 32 + 1);
+    uint16_t* wpre = reinterpret_cast<uint16_t*>(pf_bits + ((t_cap + 31) / 32));
+    for (int w = tid; w < nw; w += kPfSelNT) pf_bits[w] = 0u;
+    __syncthreads();
+    constexpr int PER = kPfCap / kPfSelNT;
+    uint2 cv[PER];
+    const uint2* src = cand + (int64_t)q * cap;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int i = tid + u * kPfSelNT;
+        cv[u] = i < (int)n ? src[i] : make_uint2(0xFFFFFFFFu, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+        if (cv[u].x != 0xFFFFFFFFu) atomicOr(&pf_bits[cv[u].x >> 5], 1u << (cv[u].x & 31));
+    __syncthreads();
+    // set bits before each word: contiguous words per thread, one block scan
+    const int wpt = (nw + kPfSelNT - 1) / kPfSelNT;
+    const int w0 = min(nw, tid * wpt), w1 = min(nw, w0 + wpt);
+    int mine = 0;
+    for (int w = w0; w < w1; ++w) mine += __popc(pf_bits[w]);
+    int total;
+    int run = block_excl_scan<kPfSelNT>(mine, sh.tmp, &total);
+    for (int w = w0; w < w1; ++w) {
+        wpre[w] = (uint16_t)run;
+        run += __popc(pf_bits[w]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        if (cv[u].x != 0xFFFFFFFFu) {
+            const uint32_t p = cv[u].x, w = p >> 5;
+            const int rank = wpre[w] + __popc(pf_bits[w] & ((1u << (p & 31)) - 1u));
+            sh.skey[rank] = cv[u].y;
+            sh.spos[rank] = (int32_t)p;
+        }
+    }
+    __syncthreads();
+    uint32_t tau;
+    int need;
+    lds_kth<kPfSelNT>(sh.skey, (int)n, k, 0, sh.hist, sh.res, tau, need);
+    ordered_write<kPfSelNT>([&](int64_t i) { return sh.skey[i]; }, (int64_t)n, tau, need, sh.spos, k,
+                            dst, sh.wtmp);
+}
+
+// Multi-query scores of a prefill chunk on one sequence: S = Q_I K_I^T, a
+// dense contraction (queries x positions x 64), on v_mfma_f32_16x16x32_bf16.
+// Both operands come straight from global memory in MFMA layout: lane l holds
+// 8 consecutive dims of query row l%16 (A) or of key l%16 (B), so every load
+// is 16 contiguous bytes.  Workgroup tile: 64 queries x 256 positions; wave w
+// takes positions [64w, 64w + 64).  Positions after a query are -inf.
+__global__ __launch_bounds__(256) void k_score_mq(const uint16_t* __restrict__ kseq, int64_t t_cap,
+                                                  const uint16_t* __restrict__ q_idx,
+                                                  const int32_t* __restrict__ q_pos, int32_t nq,
+                                                  float* __restrict__ scores, int64_t ld) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n16 = lane & 15, g = lane >> 4;
+    const int64_t q0 = (int64_t)blockIdx.y * 64;
+    const int64_t t0 = (int64_t)blockIdx.x * 256 + wave * 64;
+    if (t0 >= t_cap) return;
+    // the largest position any query of the tile may read
+    int64_t tmax = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t qq = q0 + 16 * i + n16;
+        const int64_t p = qq < nq ? q_pos[qq] : -1;
+        tmax = p > tmax ? p : tmax;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        const int64_t other = __shfl_xor(tmax, o, 64);
+        tmax = other > tmax ? other : tmax;
+    }
+    const float NEG = -__builtin_inff();
+    if (t0 > tmax) {  // every position of this wave is after every query: masked
+        for (int i = 0; i < 64; ++i) {
+            const int64_t qq = q0 + i;
+            if (qq < nq && t0 + lane < t_cap) scores[qq * ld + t0 + lane] = NEG;
+        }
+        return;
+    }
+    pf_bf16x8 a[4][2], b[4][2];
+    int32_t pos[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t qq = q0 + 16 * i + n16;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (qq < nq) v = *reinterpret_cast<const uint4*>(q_idx + qq * kIdxDim + 32 * kb + 8 * g);
+            a[i][kb] = __builtin_bit_cast(pf_bf16x8, v);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t qr = q0 + 16 * i + 4 * g + r;
+            pos[i][r] = qr < nq ? q_pos[qr] : -1;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t tt = t0 + 16 * j + n16;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (tt < t_cap) v = *reinterpret_cast<const uint4*>(kseq + tt * kIdxDim + 32 * kb + 8 * g);
+            b[j][kb] = __builtin_bit_cast(pf_bf16x8, v);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pf_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][0], b[j][0], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][1], b[j][1], c, 0, 0, 0);
+            // lane holds position t0 + 16j + n16 for queries q0 + 16i + 4g + r
+            const int64_t tt = t0 + 16 * j + n16;
+            if (tt < t_cap) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t qr = q0 + 16 * i + 4 * g + r;
+                    if (qr < nq) scores[qr * ld + tt] = (tt <= pos[i][r]) ? c[r] : NEG;
+                }
+            }
+        }
+}
+
+hipError_t launch_score_mq(const CacheView& c, int32_t seq, const uint16_t* q_idx,
+                           const int32_t* q_pos, int32_t nq, float* scores, int64_t ld,
+                           hipStream_t s) {
+    if (nq == 0) return hipSuccess;
+    const uint16_t* kseq = c.k_idx + (int64_t)seq * c.t_cap * kIdxDim;
+    dim3 grid((uint32_t)((c.t_cap + 255) / 256), (uint32_t)((nq + 63) / 64));
+    hipLaunchKernelGGL(k_score_mq, grid, dim3(256), 0, s, kseq, c.t_cap, q_idx, q_pos, nq, scores,
+                       ld);
+    return hipGetLastError();
+}
+
+size_t prefill_topk_ws_bytes(int32_t nq, int64_t t_cap) {
+    const int64_t ldc = ((t_cap + kPfChunk - 1) / kPfChunk + 3) / 4 * 4;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    return al((size_t)nq * ldc * 4) + 3 * al((size_t)nq * 4) + al((size_t)nq * kPfCap * 8);
+}
+
+hipError_t launch_prefill_topk(const CacheView& c, int32_t seq, const uint16_t* q_idx,
+                               const int32_t* q_pos, int32_t nq, int32_t k, int32_t* sel, void* ws,
+                               hipStream_t s) {
+    if (nq == 0) return hipSuccess;
+    const int64_t ldc = ((c.t_cap + kPfChunk - 1) / kPfChunk + 3) / 4 * 4;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    char* p = static_cast<char*>(ws);
+    uint32_t* cmax = reinterpret_cast<uint32_t*>(p);
+    p += al((size_t)nq * ldc * 4);
+    float* thr_f = reinterpret_cast<float*>(p);
+    p += al((size_t)nq * 4);
+    uint32_t* thr_k = reinterpret_cast<uint32_t*>(p);
+    p += al((size_t)nq * 4);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(p);
+    p += al((size_t)nq * 4);
+    uint2* cand = reinterpret_cast<uint2*>(p);
+    const uint16_t* kseq = c.k_idx + (int64_t)seq * c.t_cap * kIdxDim;
+    const dim3 grid((uint32_t)((nq + kPfQ - 1) / kPfQ), (uint32_t)((c.t_cap + kPfSpan - 1) / kPfSpan));
+    hipLaunchKernelGGL(k_pf_cmax, grid, dim3(256), 0, s, kseq, (int32_t)c.t_cap, q_idx, q_pos, nq, cmax,
+                       ldc);
+    hipLaunchKernelGGL(k_pf_thresh, dim3(nq), dim3(256), (size_t)ldc * 4, s, cmax, ldc, q_pos,
+                       c.t_cap, k, thr_f, thr_k, cnt);
+    const dim3 fgrid(grid.x, (uint32_t)((c.t_cap + kPfFiltSpan - 1) / kPfFiltSpan));
+    hipLaunchKernelGGL(k_pf_filter, fgrid, dim3(256), 0, s, kseq, (int32_t)c.t_cap, q_idx, q_pos, nq, thr_f,
+                       thr_k, cnt, cand, kPfCap);
+    const size_t nw = (size_t)((c.t_cap + 31) / 32);
+    hipLaunchKernelGGL(k_pf_select, dim3(nq), dim3(kPfSelNT), nw * 4 + nw * 2, s, kseq, c.t_cap,
+                       q_idx, q_pos, k, cnt, cand, kPfCap, sel);
+    return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -130,3 +130,28 @@ def test_valid_arguments_without_a_device_report_no_device():
     n = _lib._sz()
     assert L.csa2_stack_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
     assert L.csa2_stack_run(ctypes.byref(d), FAKE, n.value, None) == NO_DEVICE
+
+
+def test_prefill_validation():
+    L = csa2.lib()
+    c = _cache(t_cap=1000)
+    bp = ctypes.byref
+    # prefill scores: sequence in range, row stride >= t_cap, non-null operands
+    assert L.csa2_prefill_score(bp(c), 2, FAKE, FAKE, 4, FAKE, 1000, None) == SHAPE
+    assert L.csa2_prefill_score(bp(c), 0, FAKE, FAKE, 4, FAKE, 999, None) == SHAPE
+    assert L.csa2_prefill_score(bp(c), 0, None, FAKE, 4, FAKE, 1000, None) == INVALID
+    assert L.csa2_prefill_score(bp(c), 0, FAKE_ODD, FAKE, 4, FAKE, 1000, None) == INVALID
+    # fused prefill top-k: 1 <= k <= 2048, t_cap <= 2^18, workspace large enough
+    n = _lib._sz()
+    assert L.csa2_prefill_topk_workspace(4, 1000, 0, bp(n)) == SHAPE
+    assert L.csa2_prefill_topk_workspace(4, 1000, 4096, bp(n)) == SHAPE
+    assert L.csa2_prefill_topk_workspace(4, (1 << 18) + 1, 64, bp(n)) == SHAPE
+    assert L.csa2_prefill_topk_workspace(4, 1000, 64, bp(n)) == OK and n.value > 0
+    assert L.csa2_prefill_topk(bp(c), 0, FAKE, FAKE, 4, 64, FAKE, FAKE, n.value - 1, None) == WORKSPACE
+    assert L.csa2_prefill_topk(bp(c), 0, FAKE, FAKE, 4, 3000, FAKE, FAKE, n.value, None) == SHAPE
+    assert L.csa2_prefill_topk(bp(c), 5, FAKE, FAKE, 4, 64, FAKE, FAKE, n.value, None) == SHAPE
+    big = _cache(t_cap=(1 << 18) + 64)
+    assert L.csa2_prefill_topk(bp(big), 0, FAKE, FAKE, 4, 64, FAKE, FAKE, 1 << 30, None) == SHAPE
+    assert L.csa2_prefill_topk(bp(c), 0, None, FAKE, 4, 64, FAKE, FAKE, n.value, None) == INVALID
+    # nothing to do is not an error
+    assert L.csa2_prefill_topk(bp(c), 0, None, None, 0, 64, None, None, 0, None) == OK

@@ -168,6 +168,29 @@ def test_sparse_attn_on_oracle_selection(kv, window, lo, cap):
     log("attn max abs err", err)
 
 
+@pytest.mark.parametrize("kv,window,lo,cap", [("fp4", 40, 0, 64), ("bf16", 40, 0, 64),
+                                              ("fp4", 0, 0, 64), ("fp4", 64, 4090, 64)])
+def test_sparse_attn_many_queries(kv, window, lo, cap):
+    """300 queries: one workgroup per query (the prefill layout); k = 96 puts
+    the selection/window boundary inside a 32-entry tile."""
+    rng = np.random.default_rng(77)
+    nq = 300
+    q_pos = [int(v) for v in rng.integers(0, 5003, nq)]
+    q_pos[:4] = [5002, 0, 31, 4100]
+    q_seq = [int(v) for v in rng.integers(0, 3, nq)]
+    sp = _ragged_spec(kv=kv, window=window, lo=lo, local_cap=cap, q_pos=q_pos, q_seq=q_seq, seed=31)
+    x = synth.make_inputs(sp)
+    d = DevInputs(x)
+    c = oracle.Cache(x.kv, x.k_idx, fp4=(kv == "fp4"))
+    _, sel, _ = oracle.layer(c, x.q_pos, x.q_seq, oracle.FULL, x.q[0], x.q_idx[0], x.local_k[0],
+                             x.local_v[0], window, lo, sp.k)
+    sel[1::7, ::5] = -1  # empty slots are skipped
+    ref = oracle.attend(c, x.q_pos, x.q_seq, x.q[0], sel, x.local_k[0], x.local_v[0], window, lo)
+    out = host(csa2.sparse_attn(d.cache, d.q[0], d.q_pos, d.q_seq, dev32(sel), d.local[0]))
+    err = attn_check(out, ref, "attn x%d %s W=%d lo=%d" % (nq, kv, window, lo))
+    log("many-query attn max abs err", err)
+
+
 # ---------------------------------------------------------------- stack
 
 def check_stack(sp, x, d, outs, sels, pool, sample=None):

@@ -1,0 +1,142 @@
+"""GPU parity of the prefill-chunk indexer (MFMA scores and the fused top-k
+that never writes the score rows) against the oracle: ragged query tiles, rows
+shorter than k, rows whose candidate list overflows (the exact recompute
+path), exact ties, and the 4096-query workload at full size on sampled
+queries."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sparse_attention_shared_amd as csa2
+from gpu_util import DevInputs, attn_check, boundary_check, dev16, dev32, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa2.device_check()
+    yield
+    torch.cuda.synchronize()
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def _cache(k_idx_bits, n_seq=1):
+    """A bf16 cache whose values are never read: only k_idx matters here."""
+    t_cap = k_idx_bits.shape[1]
+    data = torch.zeros((n_seq, t_cap, 256), dtype=torch.bfloat16, device="cuda")
+    k = dev16(k_idx_bits)
+    return csa2.Cache(data, k), k
+
+
+def _normal(seed, shape):
+    rng = np.random.default_rng(seed)
+    return synth.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+def _positions(t_cap, n, seed, extra):
+    rng = np.random.default_rng(seed)
+    p = np.concatenate([np.asarray(extra, np.int64), rng.integers(0, t_cap, n - len(extra))])
+    return p.astype(np.int32)
+
+
+def _check_rows(gsel, q_idx, k_idx, q_pos, t_cap, k, what):
+    for i, p in enumerate(q_pos):
+        t = min(int(p), t_cap - 1)
+        if p < 0:
+            assert (gsel[i] == -1).all(), "%s row %d: negative position must select nothing" % (what, i)
+            continue
+        s = oracle.scores(q_idx[i], k_idx[:t + 1])
+        boundary_check(gsel[i], np.arange(t + 1, dtype=np.int32), s, k, "%s q%d t=%d" % (what, i, t))
+
+
+def test_prefill_score_matches_oracle():
+    t_cap, nq = 3000, 70  # ragged position and query tiles
+    k_idx = _normal(11, (1, t_cap, 64))
+    q_idx = _normal(12, (nq, 64))
+    q_pos = _positions(t_cap, nq, 13, [-1, 0, 1, 63, 64, 2999, 4000])
+    cache, _ = _cache(k_idx)
+    g = host(csa2.prefill_score(cache, 0, dev16(q_idx), dev32(q_pos)))
+    q64 = (q_idx.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    k64 = (k_idx[0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for i, p in enumerate(q_pos):
+        t = min(int(p), t_cap - 1)
+        row = g[i]
+        assert np.all(np.isneginf(row[t + 1:])), "row %d: positions after the query must be -inf" % i
+        if t < 0:
+            continue
+        ref = oracle.scores(q_idx[i], k_idx[0, :t + 1]).astype(np.float64)
+        # fp32 accumulation of 64 exact bf16 products: |err| <= 64 u sum |q_d k_d|, u = 2^-24
+        bound = 64 * 2.0 ** -24 * np.abs(k64[:t + 1] * q64[i]).sum(axis=1) + 2.0 ** -24 * np.abs(ref)
+        err = np.abs(row[:t + 1].astype(np.float64) - ref)
+        assert np.all(err <= bound), "row %d: max err %.3g" % (i, err.max())
+
+
+@pytest.mark.parametrize("t_cap,nq,k,seed", [
+    (5000, 130, 256, 21),     # threshold path, short rows, rows shorter than k
+    (20000, 70, 2048, 22),    # rows of 4097..20000 positions overflow: exact recompute path
+    (131072, 64, 2048, 23),   # the workload's row length, one query tile
+])
+def test_prefill_topk_matches_oracle(t_cap, nq, k, seed):
+    k_idx = _normal(seed, (1, t_cap, 64))
+    q_idx = _normal(seed + 100, (nq, 64))
+    extra = [-1, 0, 1, k - 2, k - 1, k, 4095, 4096, t_cap - 1, t_cap + 5]
+    q_pos = _positions(t_cap, nq, seed + 200, [e for e in extra if e < t_cap + 10])
+    cache, _ = _cache(k_idx)
+    log("prefill topk t_cap", t_cap, "nq", nq, "k", k)
+    g = host(csa2.prefill_topk(cache, 0, dev16(q_idx), dev32(q_pos), k))
+    _check_rows(g, q_idx, k_idx[0], q_pos, t_cap, k, "prefill topk")
+
+
+def test_prefill_topk_exact_ties():
+    """Many positions share a key row, so scores tie exactly (on both sides):
+    the lower positions of a tied group must be taken first."""
+    t_cap, nq, k = 40000, 64, 512
+    distinct = _normal(31, (40, 64))
+    rng = np.random.default_rng(32)
+    k_idx = distinct[rng.integers(0, 40, t_cap)][None]
+    q_idx = _normal(33, (nq, 64))
+    q_pos = _positions(t_cap, nq, 34, [t_cap - 1, 9000, 600])
+    cache, _ = _cache(k_idx)
+    g = host(csa2.prefill_topk(cache, 0, dev16(q_idx), dev32(q_pos), k))
+    for i, p in enumerate(q_pos):
+        t = int(p)
+        s = oracle.scores(q_idx[i], k_idx[0, :t + 1])
+        ref = oracle.topk(s, k)
+        chosen = [int(v) for v in g[i] if v >= 0]
+        assert chosen == sorted(chosen) and len(chosen) == min(k, t + 1)
+        # tied groups are whole rows of equal scores on both sides: the
+        # selection must be exactly the oracle's
+        assert chosen == [int(v) for v in ref if v >= 0], "row %d differs from the oracle" % i
+
+
+def test_prefill_workload_full_size_sampled():
+    """The 4096-query prefill chunk: fused top-k then attention, as timed."""
+    sp = synth.config(5)
+    log("workload 5", sp.name)
+    x = synth.make_inputs(sp)
+    d = DevInputs(x)
+    nq = sp.nq
+    sel = csa2.prefill_topk(d.cache, 0, d.q_idx[0], d.q_pos, sp.k)
+    out = csa2.sparse_attn(d.cache, d.q[0], d.q_pos, d.q_seq, sel, d.local[0])
+    torch.cuda.synchronize()
+    gsel = host(sel)
+    gout = host(out)
+    sample = np.unique(np.concatenate([[0, 1, 63, 64, nq - 1],
+                                       np.random.default_rng(5).choice(nq, 27)]))
+    for i in sample:
+        t = sp.q_pos[i]
+        s = oracle.scores(x.q_idx[0, i], x.k_idx[0, :t + 1])
+        boundary_check(gsel[i], np.arange(t + 1, dtype=np.int32), s, sp.k, "prefill q%d" % i)
+    c = oracle.Cache(x.kv, x.k_idx, fp4=True)
+    ref = oracle.attend(c, x.q_pos[sample], x.q_seq[sample], x.q[0, sample], gsel[sample],
+                        x.local_k[0], x.local_v[0], sp.window, sp.lo)
+    err = attn_check(gout[sample], ref, "prefill attention")
+    log("prefill sampled max abs err", err)
