@@ -402,7 +402,6 @@ struct LoopLds {
         uint32_t vt[kLW][kVtWave];
         float obuf[kLW][kHeads][kHeadDim + 4];
     } u;
-    float alpha[kLW][kHeads];
     float m[kLW][kHeads];
     float l[kLW][kHeads];
 };
@@ -474,12 +473,15 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
     const float zs = sm_scale * kLog2e;
     const float NEG = -__builtin_inff();
 
-    // kind of entry e: 0 none, 1 global FP4, 2 global bf16, 3 local bf16; row index
-    auto locate = [&](int64_t e, int& kind, int64_t& row) {
+    // Entry e of the query: a selected position (e < k) or a window position.
+    // sel_of(e) reads the selection slot (-1 past the selection); locate()
+    // turns it into a kind (0 none, 1 global FP4, 2 global bf16, 3 local
+    // bf16) and a row index.
+    auto sel_of = [&](int64_t e) -> int64_t { return e < k ? (int64_t)sel[(int64_t)qi * k + e] : -1; };
+    auto locate = [&](int64_t e, int64_t j, int& kind, int64_t& row) {
         kind = 0;
         row = 0;
         if (e < k) {
-            const int64_t j = sel[(int64_t)qi * k + e];
             if (j >= 0 && j <= t) {
                 kind = c.fp4 ? 1 : 2;
                 row = (int64_t)seq * c.t_cap + j;
@@ -503,111 +505,55 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
 #pragma unroll
     for (int t8 = 0; t8 < 8; ++t8) o[t8] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    // tiles of this wave: wave, wave + kLW, ...; the FP4 rows of the next tile
-    // are loaded as soon as the current ones are decoded
-    int kind[2];
-    int64_t row[2];
-    RowRaw raw[2];
-    int tile = wave;
-    if (tile < n_tiles) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            locate((int64_t)tile * 32 + 2 * n16 + u, kind[u], row[u]);
-            if (kind[u] == 1) load_fp4(row[u], raw[u]);
-        }
-    }
-    for (; tile < n_tiles; tile += kLW) {
-        // ---- rows -> bf16 K fragments; V dims 32 g .. + 32 go to V^T at once
-        bf16x8_t kf[2][4];
-        const uint64_t vm0 = __ballot(kind[0] != 0) & 0xFFFFull;  // bit n16: slot row valid
-        const uint64_t vm1 = __ballot(kind[1] != 0) & 0xFFFFull;
-        uint32_t vd0[16];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            uint32_t kd[16], vd[16];
-            if (kind[u] == 1) {
-                dq_block(raw[u].k, e8m0_value(raw[u].sk), kd);
-                dq_block(raw[u].v, e8m0_value(raw[u].sv), vd);
-            } else if (kind[u] >= 2) {
-                const uint16_t* kr = kind[u] == 2 ? static_cast<const uint16_t*>(c.data) + row[u] * kRowBf16
-                                                  : loc.k + row[u] * kHeadDim;
-                const uint16_t* vr = kind[u] == 2 ? kr + kHeadDim : loc.v + row[u] * kHeadDim;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint4 a = *reinterpret_cast<const uint4*>(kr + 32 * g + 8 * i);
-                    const uint4 b = *reinterpret_cast<const uint4*>(vr + 32 * g + 8 * i);
-                    kd[4 * i] = a.x; kd[4 * i + 1] = a.y; kd[4 * i + 2] = a.z; kd[4 * i + 3] = a.w;
-                    vd[4 * i] = b.x; vd[4 * i + 1] = b.y; vd[4 * i + 2] = b.z; vd[4 * i + 3] = b.w;
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) kd[i] = vd[i] = 0u;
-            }
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                kf[u][kb] = as_bf16x8(kd[4 * kb], kd[4 * kb + 1], kd[4 * kb + 2], kd[4 * kb + 3]);
-            if (u == 0) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) vd0[i] = vd[i];
-            } else {
-                // V^T: dims d, d + 1 of slots 2 n16, 2 n16 + 1 -> two dwords
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int d = 32 * g + 2 * i;
-                    vt[vt_addr(d) + n16] = __builtin_amdgcn_perm(vd[i], vd0[i], 0x05040100u);
-                    vt[vt_addr(d + 1) + n16] = __builtin_amdgcn_perm(vd[i], vd0[i], 0x07060302u);
-                }
-            }
-        }
-        const int next = tile + kLW;
-        if (next < n_tiles) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                locate((int64_t)next * 32 + 2 * n16 + u, kind[u], row[u]);
-                if (kind[u] == 1) load_fp4(row[u], raw[u]);
-            }
-        }
-        // ---- S^T = K Q^T: lane holds head n16, rows 4 g + r of tile u = slot 8 g + 2 r + u
-        float s[2][4];
+    // One tile once its K fragments are in kf and its V^T is in LDS: S^T = K
+    // Q^T (lane: head n16, rows 4 g + r of MFMA tile u = slot 8 g + 2 r + u),
+    // the online softmax, and O^T += V^T P^T (lane: head n16, dims
+    // 16 t8 + 4 g + r, so the rescale by alpha is lane-local).
+    auto consume = [&](const bf16x8_t (&kf)[2][4], uint64_t vm0, uint64_t vm1) {
+        float sv[2][4];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][kb], qf[kb], z, 0, 0, 0);
-            const uint64_t vm = u ? vm1 : vm0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s[u][r] = ((vm >> (4 * g + r)) & 1) ? z[r] * zs : NEG;
+            for (int r = 0; r < 4; ++r) sv[u][r] = z[r] * zs;
         }
-        float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        if ((vm0 & vm1) != 0xFFFFull) {  // some slot of the tile is empty: -inf
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (!((vm0 >> (4 * g + r)) & 1)) sv[0][r] = NEG;
+                if (!((vm1 >> (4 * g + r)) & 1)) sv[1][r] = NEG;
+            }
+        }
+        float mt = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                         fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_new == m_run) ? 1.f : exp2f(m_run - m_new);  // m_run = -inf: 0
+        const float m_use = m_new == NEG ? 0.f : m_new;  // no valid slot yet: every p is 0
+        // v_exp_f32: 2^-inf = 0; results below 2^-126 flush to 0
+        const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_use);
         float p[2][4];
         float ps = 0.f;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[u][r] = (s[u][r] == NEG) ? 0.f : exp2f(s[u][r] - m_new);
+                p[u][r] = __builtin_amdgcn_exp2f(sv[u][r] - m_use);
                 ps += p[u][r];
             }
         l_part = fmaf(l_part, alpha, ps);
         m_run = m_new;
-        // ---- rescale O (heads 4 g + r of this lane) when a running max moved
         if (__ballot(alpha != 1.f)) {
-            if (g == 0) sh.alpha[wave][n16] = alpha;
-            const float4 a4 = *reinterpret_cast<const float4*>(&sh.alpha[wave][4 * g]);
 #pragma unroll
             for (int t8 = 0; t8 < 8; ++t8) {
-                o[t8][0] *= a4.x;
-                o[t8][1] *= a4.y;
-                o[t8][2] *= a4.z;
-                o[t8][3] *= a4.w;
+                o[t8][0] *= alpha;
+                o[t8][1] *= alpha;
+                o[t8][2] *= alpha;
+                o[t8][3] *= alpha;
             }
         }
-        // ---- O += P V: A = P (head n16, slots 8 g + j, j = 2 r + u), B = V (slots, dim n16)
         const bf16x8_t pf = as_bf16x8(__builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][0], (__bf16)p[1][0]}),
                                       __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][1], (__bf16)p[1][1]}),
                                       __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][2], (__bf16)p[1][2]}),
@@ -615,8 +561,155 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) {
             const uint4 vv = *reinterpret_cast<const uint4*>(&vt[vt_addr(16 * t8 + n16) + 4 * g]);
-            o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, as_bf16x8(vv.x, vv.y, vv.z, vv.w), o[t8], 0, 0, 0);
+            o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv.x, vv.y, vv.z, vv.w), pf, o[t8], 0, 0, 0);
         }
+    };
+
+    // ---- tiles inside the selection of an FP4 cache: every slot is a global
+    // FP4 row or empty.  While tile i computes, the rows of tile i + 1 and the
+    // selection slots of tile i + 2 are in flight.  An empty slot loads zero
+    // codes, so its V is zero.
+    const int n_fast = (c.fp4 && t >= 0) ? k / 32 : 0;
+    const uint8_t* codes = static_cast<const uint8_t*>(c.data) + (int64_t)max(seq, 0) * c.t_cap * kRowCodes;
+    const uint8_t* scl = c.scales ? c.scales + (int64_t)max(seq, 0) * c.t_cap * kRowScales : nullptr;
+    auto fetch = [&](int64_t j, RowRaw& r) {
+        if (j >= 0 && j <= t) {
+            r.k = *reinterpret_cast<const uint4*>(codes + j * kRowCodes + 16 * g);
+            r.v = *reinterpret_cast<const uint4*>(codes + j * kRowCodes + 64 + 16 * g);
+            const uint2 sc = *reinterpret_cast<const uint2*>(scl + j * kRowScales);
+            r.sk = (sc.x >> (8 * g)) & 0xFFu;
+            r.sv = (sc.y >> (8 * g)) & 0xFFu;
+        } else {
+            r.k = r.v = make_uint4(0, 0, 0, 0);
+            r.sk = r.sv = 127u;
+        }
+    };
+    {
+        RowRaw raw[2];
+        int64_t jc[2] = {-1, -1}, jn[2] = {-1, -1};
+        int tile = wave;
+        if (tile < n_fast) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                jc[u] = sel_of((int64_t)tile * 32 + 2 * n16 + u);
+                fetch(jc[u], raw[u]);
+            }
+            if (tile + kLW < n_fast) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) jn[u] = sel_of((int64_t)(tile + kLW) * 32 + 2 * n16 + u);
+            }
+        }
+        for (; tile < n_fast; tile += kLW) {
+            const uint64_t vm0 = __ballot(jc[0] >= 0 && jc[0] <= t) & 0xFFFFull;
+            const uint64_t vm1 = __ballot(jc[1] >= 0 && jc[1] <= t) & 0xFFFFull;
+            bf16x8_t kf[2][4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float sc = e8m0_value(raw[u].sk);
+                const uint32_t w[4] = {raw[u].k.x, raw[u].k.y, raw[u].k.z, raw[u].k.w};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    kf[u][kb] = as_bf16x8(cvt_fp4x2(w[kb], sc, 0), cvt_fp4x2(w[kb], sc, 1),
+                                          cvt_fp4x2(w[kb], sc, 2), cvt_fp4x2(w[kb], sc, 3));
+            }
+            {
+                const float s0 = e8m0_value(raw[0].sv), s1 = e8m0_value(raw[1].sv);
+                const uint32_t w0v[4] = {raw[0].v.x, raw[0].v.y, raw[0].v.z, raw[0].v.w};
+                const uint32_t w1v[4] = {raw[1].v.x, raw[1].v.y, raw[1].v.z, raw[1].v.w};
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t va = cvt_fp4x2(w0v[i >> 2], s0, i & 3);
+                    const uint32_t vb = cvt_fp4x2(w1v[i >> 2], s1, i & 3);
+                    const int d = 32 * g + 2 * i;
+                    vt[vt_addr(d) + n16] = __builtin_amdgcn_perm(vb, va, 0x05040100u);
+                    vt[vt_addr(d + 1) + n16] = __builtin_amdgcn_perm(vb, va, 0x07060302u);
+                }
+            }
+            const int next = tile + kLW;
+            if (next < n_fast) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    jc[u] = jn[u];
+                    fetch(jc[u], raw[u]);
+                }
+                if (next + kLW < n_fast) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) jn[u] = sel_of((int64_t)(next + kLW) * 32 + 2 * n16 + u);
+                }
+            }
+            consume(kf, vm0, vm1);
+        }
+    }
+
+    // ---- the other tiles (window rows, a bf16 cache, a tile across the end of
+    // the selection): rows loaded when the tile starts
+    for (int tile = n_fast + wave; tile < n_tiles; tile += kLW) {
+        int kind[2];
+        int64_t row[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t e = (int64_t)tile * 32 + 2 * n16 + u;
+            locate(e, sel_of(e), kind[u], row[u]);
+        }
+        const uint64_t vm0 = __ballot(kind[0] != 0) & 0xFFFFull;
+        const uint64_t vm1 = __ballot(kind[1] != 0) & 0xFFFFull;
+        bf16x8_t kf[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (kind[u] == 1) {
+                RowRaw r;
+                load_fp4(row[u], r);
+                const float sc = e8m0_value(r.sk);
+                const uint32_t w[4] = {r.k.x, r.k.y, r.k.z, r.k.w};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    kf[u][kb] = as_bf16x8(cvt_fp4x2(w[kb], sc, 0), cvt_fp4x2(w[kb], sc, 1),
+                                          cvt_fp4x2(w[kb], sc, 2), cvt_fp4x2(w[kb], sc, 3));
+            } else if (kind[u] >= 2) {
+                const uint16_t* kr = kind[u] == 2 ? static_cast<const uint16_t*>(c.data) + row[u] * kRowBf16
+                                                  : loc.k + row[u] * kHeadDim;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const uint4 av = *reinterpret_cast<const uint4*>(kr + 32 * g + 8 * kb);
+                    kf[u][kb] = as_bf16x8(av.x, av.y, av.z, av.w);
+                }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) kf[u][kb] = as_bf16x8(0u, 0u, 0u, 0u);
+            }
+        }
+        // V^T eight dims at a time
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            uint32_t vv[2][4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (kind[u] == 1) {
+                    const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row[u] * kRowCodes;
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(cr + 64 + 16 * g + 4 * i4);
+                    const float sc = e8m0_value(c.scales[row[u] * kRowScales + 4 + g]);
+                    vv[u][0] = cvt_fp4x2(w, sc, 0);
+                    vv[u][1] = cvt_fp4x2(w, sc, 1);
+                    vv[u][2] = cvt_fp4x2(w, sc, 2);
+                    vv[u][3] = cvt_fp4x2(w, sc, 3);
+                } else if (kind[u] >= 2) {
+                    const uint16_t* vr = kind[u] == 2
+                                             ? static_cast<const uint16_t*>(c.data) + row[u] * kRowBf16 + kHeadDim
+                                             : loc.v + row[u] * kHeadDim;
+                    const uint4 bq = *reinterpret_cast<const uint4*>(vr + 32 * g + 8 * i4);
+                    vv[u][0] = bq.x; vv[u][1] = bq.y; vv[u][2] = bq.z; vv[u][3] = bq.w;
+                } else {
+                    vv[u][0] = vv[u][1] = vv[u][2] = vv[u][3] = 0u;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d = 32 * g + 8 * i4 + 2 * i;
+                vt[vt_addr(d) + n16] = __builtin_amdgcn_perm(vv[1][i], vv[0][i], 0x05040100u);
+                vt[vt_addr(d + 1) + n16] = __builtin_amdgcn_perm(vv[1][i], vv[0][i], 0x07060302u);
+            }
+        }
+        consume(kf, vm0, vm1);
     }
     // ---- combine the waves
     l_part += __shfl_xor(l_part, 16, 64);
@@ -628,8 +721,8 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
     __syncthreads();  // every wave is done with its V^T tile
 #pragma unroll
     for (int t8 = 0; t8 < 8; ++t8)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sh.u.obuf[wave][4 * g + r][16 * t8 + n16] = o[t8][r];
+        *reinterpret_cast<float4*>(&sh.u.obuf[wave][n16][16 * t8 + 4 * g]) =
+            make_float4(o[t8][0], o[t8][1], o[t8][2], o[t8][3]);
     __syncthreads();
     const int h = tid >> 4, d0 = (tid & 15) * 8;  // 256 threads: head h, 8 dims
     float M = NEG;
