@@ -12,6 +12,11 @@ scoring, top-k, gather + FP4 dequant, attention), launched through the C ABI
 timed steps rotate over several copies of the cache so that consecutive steps
 do not find it in the 256 MB Infinity Cache.
 
+With --workload prefill it times the prefill chunk instead: 4096 queries at
+positions 126976..131071 of one 131072-token sequence, each selecting its
+top-2048 positions (csa2_prefill_topk) and attending to them plus its window
+(csa2_sparse_attn), reported as query positions per second.
+
 Prints one JSON line (see the repository's design doc for the fields).
 """
 from __future__ import annotations
@@ -90,6 +95,138 @@ def cpu_baseline(budget_s=12.0):
                       "(T=131072, FP4, pool 8192, k=2048, W=128) in %.1f s, one thread" % (n, el)}
 
 
+PREFILL_METRIC = "CSA2 prefill-chunk query positions/s at 128k ctx, FP4 shared KV"
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def cpu_baseline_prefill(x, sp, budget_s=12.0):
+    """The oracle (plain C, one thread) on a bounded sample of the prefill
+    chunk: single queries (scores, top-k, attention) until the budget."""
+    import numpy as np
+    import oracle
+    c = oracle.Cache(x.kv, x.k_idx, fp4=True)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        i = (n * 997) % sp.nq
+        t = int(sp.q_pos[i])
+        s = oracle.scores(x.q_idx[0, i], x.k_idx[0, :t + 1])
+        sel = oracle.topk(s, sp.k)
+        oracle.attend(c, x.q_pos[i:i + 1], x.q_seq[i:i + 1], x.q[0, i:i + 1], sel[None],
+                      x.local_k[0], x.local_v[0], sp.window, sp.lo)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 512:
+            break
+    return {"value": n / el, "unit": "query positions/s", "cores": 1, "kind": "oracle",
+            "sample": "%d queries of the prefill chunk (scores over ~129k positions, top-2048, "
+                      "attention) in %.1f s, one thread" % (n, el)}
+
+
+def bench_prefill(args):
+    """One step = the whole 4096-query prefill chunk: fused indexer top-k then
+    attention, both through the C ABI, inputs resident in HBM."""
+    import numpy as np
+    import torch
+    import synth
+    import sparse_attention_shared_amd as csa2
+
+    sp = synth.config(5)
+    print("generating inputs ...", file=sys.stderr, flush=True)
+    x = synth.make_inputs(sp)
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    codes, scales = csa2.pack_fp4(d16(x.kv))
+    cache = csa2.Cache(codes, d16(x.k_idx), scales)
+    nq = sp.nq
+    q_pos = torch.from_numpy(x.q_pos).cuda()
+    q_seq = torch.from_numpy(x.q_seq).cuda()
+    q = d16(x.q[0])
+    q_idx = d16(x.q_idx[0])
+    local = csa2.Local(d16(x.local_k[0]), d16(x.local_v[0]), sp.window)
+    sel = torch.empty((nq, sp.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((nq, 16, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(csa2.prefill_topk_workspace(nq, sp.t_cap, sp.k), dtype=torch.uint8,
+                     device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record()
+        csa2.prefill_topk(cache, 0, q_idx, q_pos, sp.k, out=sel, ws=ws)
+        if e:
+            e[1].record()
+        csa2.sparse_attn(cache, q, q_pos, q_seq, sel, local, out=out)
+        if e:
+            e[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        step(ev[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+    topk_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev)
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev)
+    # algorithmic work: the causal indexer product once, and QK + PV over the
+    # selection and window for 16 heads
+    pos = np.asarray(sp.q_pos, dtype=np.int64)
+    idx_flop = float(2 * 64 * (pos + 1).sum())
+    ent = sp.k + np.minimum(pos + 1, sp.window)
+    attn_flop = float((2 * 2 * 16 * 128 * ent).sum())
+    parts = {
+        "csa2_prefill_topk": {"ms": topk_ms, "tflops": idx_flop / (topk_ms * 1e-3) / 1e12,
+                              "algorithmic_flop": idx_flop},
+        "csa2_sparse_attn": {"ms": attn_ms, "tflops": attn_flop / (attn_ms * 1e-3) / 1e12,
+                             "algorithmic_flop": attn_flop},
+    }
+    dom = max(parts, key=lambda n: parts[n]["ms"])
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": nq / (ms * 1e-3),
+        "unit": "query positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "CSA2 prefill chunk: 4096 queries at positions 126976..131071 of one "
+                        "131072-token sequence, FP4 (E2M1 + E8M0/32) shared KV, indexer dim 64, "
+                        "top-k 2048, SWA 128, 16 q heads / 1 KV head, head_dim 128",
+            "queries": nq, "context": sp.t_cap, "k": sp.k, "window": sp.window,
+        },
+        "parts": parts,
+        "wall_s_timed_region": wall,
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": parts[dom]["tflops"],
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": parts[dom]["tflops"] / PEAK_BF16_TFLOPS,
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("timing the oracle on the host ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_prefill(x, sp)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +235,7 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["repeat", "page"], default="repeat")
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -113,6 +251,9 @@ def main():
 
     torch.cuda.set_device(0)
     csa2.device_check()
+    if args.workload == "prefill":
+        bench_prefill(args)
+        return
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 18  # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")

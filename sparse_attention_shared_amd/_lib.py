@@ -266,12 +266,12 @@ def sparse_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, q_seq: Optio
     if out is None:
         out = torch.empty((nq, HEADS, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
     need = sparse_attn_workspace(nq, k, local.c.window)
-    if ws is None:
-        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    if ws is None and need > 0:
+        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)
     _check("csa2_sparse_attn", lib().csa2_sparse_attn(
         ctypes.byref(cache.c), _ptr(_bits16(q)), _ptr(_i32t(q_pos)), _ptr(_i32t(q_seq)), nq,
         _ptr(_i32t(sel)), k, ctypes.byref(local.c), float(sm_scale), _ptr(out), _ptr(ws),
-        ws.numel(), _stream()))
+        ws.numel() if ws is not None else 0, _stream()))
     return out
 
 
