@@ -8,10 +8,10 @@
 // All 16 heads read the same K/V row (one KV head), so per entry block the
 // work is two small dense products: S = K Q^T (16 entries x 16 heads, K = 128
 // dims) and O += P V (16 heads x 16 dims, K = 32 entries).  Both run on
-// v_mfma_f32_16x16x32_bf16.  FP4 codes become bf16 of the unscaled E2M1 value
-// (exact); each MFMA k-step covers exactly one 32-element scale block, so the
-// power-of-two scales are applied exactly in fp32: on S per (entry, block),
-// and on P per (entry, V block) before P feeds the second product.
+// v_mfma_f32_16x16x32_bf16.  FP4 rows are dequantised with their E8M0 scale by
+// v_cvt_scalef32_pk_bf16_fp4: an E2M1 value times a power of two is exact in
+// bf16 (every scale a 32-channel block can carry keeps the result in range),
+// so both products take plain bf16 operands.
 //
 // Work split: a wave takes 32 entries, a workgroup 8 waves (256 entries).  A
 // query with more entries is cut into chunks, one workgroup each; every chunk
@@ -30,33 +30,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlk = 32;                  // entries per wave
 constexpr int kWgEntries = kWaves * kBlk;  // entries per workgroup
-constexpr int kVtStride = kBlk + 4;       // padded row of the V^T tile (bf16), 8-byte aligned
 constexpr float kLog2e = 1.4426950408889634f;
-
-// 8 FP4 codes (one dword, element i in nibble i) -> 8 bf16 of the unscaled
-// E2M1 value, packed two per dword (element 2i in the low half of out[i/2]...).
-// bf16 of the magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}: high bytes
-// 00 3F 3F 3F 40 40 40 40, low bytes 00 00 80 C0 00 40 80 C0; the sign bit of
-// the code becomes bit 7 of the high byte.  v_perm_b32 does the table lookups.
-__device__ __forceinline__ void fp4x8_bf16(uint32_t w, uint32_t* out) {
-    constexpr uint32_t HI_03 = 0x3F3F3F00u, HI_47 = 0x40404040u;
-    constexpr uint32_t LO_03 = 0xC0800000u, LO_47 = 0xC0804000u;
-    const uint32_t ev = w & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6
-    const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
-    const uint32_t me = ev & 0x07070707u, mo = od & 0x07070707u;
-    const uint32_t he = __builtin_amdgcn_perm(HI_47, HI_03, me) | ((ev & 0x08080808u) << 4);
-    const uint32_t le = __builtin_amdgcn_perm(LO_47, LO_03, me);
-    const uint32_t ho = __builtin_amdgcn_perm(HI_47, HI_03, mo) | ((od & 0x08080808u) << 4);
-    const uint32_t lo = __builtin_amdgcn_perm(LO_47, LO_03, mo);
-    const uint32_t x01 = __builtin_amdgcn_perm(he, le, 0x05010400u);  // e0 | e2 << 16
-    const uint32_t x23 = __builtin_amdgcn_perm(he, le, 0x07030602u);  // e4 | e6 << 16
-    const uint32_t y01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u);  // e1 | e3 << 16
-    const uint32_t y23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);  // e5 | e7 << 16
-    out[0] = __builtin_amdgcn_perm(y01, x01, 0x05040100u);            // e0 | e1 << 16
-    out[1] = __builtin_amdgcn_perm(y01, x01, 0x07060302u);            // e2 | e3 << 16
-    out[2] = __builtin_amdgcn_perm(y23, x23, 0x05040100u);            // e4 | e5 << 16
-    out[3] = __builtin_amdgcn_perm(y23, x23, 0x07060302u);            // e6 | e7 << 16
-}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
@@ -73,16 +47,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)f_to_bf16(a) | ((uint32_t)f_to_bf16(b) << 16);
 }
 
-struct WaveTile {
-    uint16_t vt[kHeadDim][kVtStride];  // V^T of the wave's 32 entries (bf16 bits)
-    float sk[kBlk][4];                 // K scale of each 32-dim block
-    float sv[kBlk][4];                 // V scale of each 32-dim block
-    int valid[kBlk];
+// ---- shared by both attention kernels --------------------------------------
+// V^T tile of one wave: 128 dim rows of 32 entry slots (bf16), 16 dwords per
+// row, rows skewed by 16 dwords every 32 rows so that the four lane groups of
+// a transposing store land in different banks.
+constexpr int kVtRow = 16;
+constexpr int kVtWave = kHeadDim * kVtRow + 4 * kVtRow;
+
+__device__ __forceinline__ int vt_addr(int d) { return d * kVtRow + (d >> 5) * kVtRow; }
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t w, float sc, int sel) {
+    bf16x2_t r;
+    switch (sel) {
+        case 0: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0); break;
+        case 1: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1); break;
+        case 2: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2); break;
+        default: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3); break;
+    }
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 32 FP4 codes (16 bytes) of one scale block -> 16 dwords of bf16 pairs.
+__device__ __forceinline__ void dq_block(uint4 c, float sc, uint32_t (&o)[16]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[4 * i + 0] = cvt_fp4x2(w[i], sc, 0);
+        o[4 * i + 1] = cvt_fp4x2(w[i], sc, 1);
+        o[4 * i + 2] = cvt_fp4x2(w[i], sc, 2);
+        o[4 * i + 3] = cvt_fp4x2(w[i], sc, 3);
+    }
+}
+
+struct RowRaw {  // the FP4 data one lane loads for one entry
+    uint4 k, v;
+    uint32_t sk, sv;  // scale bytes of the lane's K and V blocks
 };
 
 struct AttnLds {
     union {
-        WaveTile w[kWaves];
+        uint32_t vt[kWaves][kVtWave];
         float obuf[kWaves][kHeads][kHeadDim + 4];  // after the V^T tiles are consumed
     } u;
     float m[kWaves][kHeads];
@@ -90,7 +96,9 @@ struct AttnLds {
     int last;
 };
 
-// grid: (n_chunk, nq), kThreads threads.
+// grid: (n_chunk, nq), kThreads threads.  Wave w of chunk c takes entries
+// 256 c + 32 w .. + 32: lane row n16 loads entries 2 n16 and 2 n16 + 1 (MFMA
+// tiles 0 and 1), lane group g dims 32 g .. + 32 of K and of V.
 __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint16_t* __restrict__ q,
                                                          const int32_t* __restrict__ q_pos,
                                                          const int32_t* __restrict__ q_seq,
@@ -105,7 +113,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     const int qi = blockIdx.y, chunk = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n16 = lane & 15, g = lane >> 4;
-    WaveTile& W = sh.u.w[wave];
+    uint32_t* vt = sh.u.vt[wave];
+    const float NEG = -__builtin_inff();
 
     const int32_t seq = q_seq ? q_seq[qi] : qi;
     int64_t t = q_pos[qi];
@@ -116,152 +125,126 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     if (w0 < 0) w0 = 0;
     const int64_t nw = (loc.window > 0 && t >= w0) ? t - w0 + 1 : 0;
 
-    // Q^T as the B operand of S: head n16, dims 32 kb + 8 g .. +8 at step kb
-    bf16x8_t qf[4];
-    {
-        const uint4* qr = reinterpret_cast<const uint4*>(q + ((int64_t)qi * kHeads + n16) * kHeadDim);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const uint4 v = qr[4 * kb + g];
-            qf[kb] = as_bf16x8(v.x, v.y, v.z, v.w);
-        }
-    }
-
-    // ---- gather: this lane loads entry (tile tau, row n16) of the wave.  The
-    // selection slots of both tiles are read first, then every row load of
-    // both tiles is issued, then the rows are decoded.
-    bf16x8_t kf[2][4];
-    const int64_t e_base = (int64_t)chunk * kWgEntries + wave * kBlk;
+    // ---- slots first, then every row load of both tiles, then the decode
     int kind[2];     // 0 none, 1 global FP4, 2 global bf16, 3 local bf16
     int64_t row[2];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-        const int64_t ge = e_base + tau * 16 + n16;
-        kind[tau] = 0;
-        row[tau] = 0;
-        if (ge < k) {
-            const int64_t j = sel[(int64_t)qi * k + ge];
+    for (int u = 0; u < 2; ++u) {
+        const int64_t e = (int64_t)chunk * kWgEntries + wave * kBlk + 2 * n16 + u;
+        kind[u] = 0;
+        row[u] = 0;
+        if (e < k) {
+            const int64_t j = sel[(int64_t)qi * k + e];
             if (j >= 0 && j <= t) {
-                kind[tau] = c.fp4 ? 1 : 2;
-                row[tau] = (int64_t)seq * c.t_cap + j;
+                kind[u] = c.fp4 ? 1 : 2;
+                row[u] = (int64_t)seq * c.t_cap + j;
             }
-        } else if (ge - k < nw) {
-            kind[tau] = 3;
-            row[tau] = (int64_t)seq * loc.cap + (w0 + (ge - k)) % loc.cap;
+        } else if (e - k < nw) {
+            kind[u] = 3;
+            row[u] = (int64_t)seq * loc.cap + (w0 + (e - k)) % loc.cap;
         }
     }
-    uint32_t rk[2][16], rv[2][16];
-    uint2 rsc[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-        rsc[tau] = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);  // scale 1 for bf16 rows
-        if (kind[tau] == 1) {
-            const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row[tau] * kRowCodes;
-            const uint32_t* kw = reinterpret_cast<const uint32_t*>(cr);
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) rk[tau][kb] = kw[4 * kb + g];  // dims 32kb + 8g .. +8
-            const uint4 vv = *reinterpret_cast<const uint4*>(cr + 64 + 16 * g);  // dims 32g .. +32
-            rv[tau][0] = vv.x; rv[tau][1] = vv.y; rv[tau][2] = vv.z; rv[tau][3] = vv.w;
-            rsc[tau] = *reinterpret_cast<const uint2*>(c.scales + row[tau] * kRowScales);
-        } else if (kind[tau] >= 2) {
-            const uint16_t* kr = kind[tau] == 2
-                                     ? static_cast<const uint16_t*>(c.data) + row[tau] * kRowBf16
-                                     : loc.k + row[tau] * kHeadDim;
-            const uint16_t* vr = kind[tau] == 2 ? kr + kHeadDim : loc.v + row[tau] * kHeadDim;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const uint4 v = *reinterpret_cast<const uint4*>(kr + 32 * kb + 8 * g);
-                rk[tau][4 * kb] = v.x; rk[tau][4 * kb + 1] = v.y;
-                rk[tau][4 * kb + 2] = v.z; rk[tau][4 * kb + 3] = v.w;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 v = *reinterpret_cast<const uint4*>(vr + 32 * g + 8 * i);
-                rv[tau][4 * i] = v.x; rv[tau][4 * i + 1] = v.y;
-                rv[tau][4 * i + 2] = v.z; rv[tau][4 * i + 3] = v.w;
-            }
-        }
-    }
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-        const int eslot = tau * 16 + n16;
-        uint32_t vb[16];
-        if (kind[tau] == 1) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                uint32_t o[4];
-                fp4x8_bf16(rk[tau][kb], o);
-                kf[tau][kb] = as_bf16x8(o[0], o[1], o[2], o[3]);
-            }
-            fp4x8_bf16(rv[tau][0], vb + 0);
-            fp4x8_bf16(rv[tau][1], vb + 4);
-            fp4x8_bf16(rv[tau][2], vb + 8);
-            fp4x8_bf16(rv[tau][3], vb + 12);
-        } else if (kind[tau] >= 2) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                kf[tau][kb] = as_bf16x8(rk[tau][4 * kb], rk[tau][4 * kb + 1], rk[tau][4 * kb + 2],
-                                        rk[tau][4 * kb + 3]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) vb[i] = rv[tau][i];
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) kf[tau][kb] = as_bf16x8(0u, 0u, 0u, 0u);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) vb[i] = 0u;
-        }
-        // V^T tile: dims 32 g + j of entry eslot
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            W.vt[32 * g + 2 * i][eslot] = (uint16_t)(vb[i] & 0xFFFFu);
-            W.vt[32 * g + 2 * i + 1][eslot] = (uint16_t)(vb[i] >> 16);
-        }
-        if (g == 0) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                W.sk[eslot][b] = e8m0_value((rsc[tau].x >> (8 * b)) & 0xFFu);
-                W.sv[eslot][b] = e8m0_value((rsc[tau].y >> (8 * b)) & 0xFFu);
-            }
-            W.valid[eslot] = kind[tau] != 0;
-        }
-    }
-    __syncthreads();
-
-    // ---- S^T = K Q^T: lane holds head n16, entries 4g + r of each tile
-    const float zs = sm_scale * kLog2e;
-    float s[2][4];
-    bool ok[2][4];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    // Q^T as the B operand of S: head n16, dims 32 g + 8 kb .. + 8 at step kb
+    bf16x8_t qf[4];
+    {
+        const uint4* qr = reinterpret_cast<const uint4*>(q + ((int64_t)qi * kHeads + n16) * kHeadDim + 32 * g);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tau][kb], qf[kb], z, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = fmaf(z[r], W.sk[tau * 16 + 4 * g + r][kb], acc[r]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            ok[tau][r] = W.valid[tau * 16 + 4 * g + r] != 0;
-            s[tau][r] = ok[tau][r] ? acc[r] * zs : -__builtin_inff();
+            const uint4 v = qr[kb];
+            qf[kb] = as_bf16x8(v.x, v.y, v.z, v.w);
         }
     }
-    float m = -__builtin_inff();
+    uint4 rk[2][4], rv[2][4];  // K and V dims 32 g .. + 32: FP4 uses [0], bf16 all four
+    uint32_t rsk[2], rsv[2];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
+    for (int u = 0; u < 2; ++u) {
+        rsk[u] = rsv[u] = 127u;
+        if (kind[u] == 1) {
+            const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row[u] * kRowCodes;
+            rk[u][0] = *reinterpret_cast<const uint4*>(cr + 16 * g);
+            rv[u][0] = *reinterpret_cast<const uint4*>(cr + 64 + 16 * g);
+            const uint2 sc = *reinterpret_cast<const uint2*>(c.scales + row[u] * kRowScales);
+            rsk[u] = (sc.x >> (8 * g)) & 0xFFu;
+            rsv[u] = (sc.y >> (8 * g)) & 0xFFu;
+        } else if (kind[u] >= 2) {
+            const uint16_t* kr = kind[u] == 2 ? static_cast<const uint16_t*>(c.data) + row[u] * kRowBf16
+                                              : loc.k + row[u] * kHeadDim;
+            const uint16_t* vr = kind[u] == 2 ? kr + kHeadDim : loc.v + row[u] * kHeadDim;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) m = fmaxf(m, s[tau][r]);
+            for (int i = 0; i < 4; ++i) {
+                rk[u][i] = *reinterpret_cast<const uint4*>(kr + 32 * g + 8 * i);
+                rv[u][i] = *reinterpret_cast<const uint4*>(vr + 32 * g + 8 * i);
+            }
+        } else {
+            rk[u][0] = rv[u][0] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int i = 1; i < 4; ++i) rk[u][i] = rv[u][i] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    // ---- decode: K fragments (FP4 scaled exactly by v_cvt_scalef32_pk_bf16_fp4),
+    // V dims d, d + 1 of slots 2 n16, 2 n16 + 1 -> two dwords of V^T
+    bf16x8_t kf[2][4];
+    uint32_t vd[2][16];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (kind[u] == 1) {
+            const float sk = e8m0_value(rsk[u]), sv = e8m0_value(rsv[u]);
+            const uint32_t wk[4] = {rk[u][0].x, rk[u][0].y, rk[u][0].z, rk[u][0].w};
+            const uint32_t wv[4] = {rv[u][0].x, rv[u][0].y, rv[u][0].z, rv[u][0].w};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                kf[u][kb] = as_bf16x8(cvt_fp4x2(wk[kb], sk, 0), cvt_fp4x2(wk[kb], sk, 1),
+                                      cvt_fp4x2(wk[kb], sk, 2), cvt_fp4x2(wk[kb], sk, 3));
+                vd[u][4 * kb + 0] = cvt_fp4x2(wv[kb], sv, 0);
+                vd[u][4 * kb + 1] = cvt_fp4x2(wv[kb], sv, 1);
+                vd[u][4 * kb + 2] = cvt_fp4x2(wv[kb], sv, 2);
+                vd[u][4 * kb + 3] = cvt_fp4x2(wv[kb], sv, 3);
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                kf[u][kb] = as_bf16x8(rk[u][kb].x, rk[u][kb].y, rk[u][kb].z, rk[u][kb].w);
+                vd[u][4 * kb + 0] = rv[u][kb].x;
+                vd[u][4 * kb + 1] = rv[u][kb].y;
+                vd[u][4 * kb + 2] = rv[u][kb].z;
+                vd[u][4 * kb + 3] = rv[u][kb].w;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int d = 32 * g + 2 * i;
+        vt[vt_addr(d) + n16] = __builtin_amdgcn_perm(vd[1][i], vd[0][i], 0x05040100u);
+        vt[vt_addr(d + 1) + n16] = __builtin_amdgcn_perm(vd[1][i], vd[0][i], 0x07060302u);
+    }
+    const uint64_t vm0 = __ballot(kind[0] != 0) & 0xFFFFull;  // bit n16: slot row valid
+    const uint64_t vm1 = __ballot(kind[1] != 0) & 0xFFFFull;
+
+    // ---- S^T = K Q^T: lane holds head n16, rows 4 g + r of tile u = slot 8 g + 2 r + u
+    const float zs = sm_scale * kLog2e;
+    float s[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][kb], qf[kb], z, 0, 0, 0);
+        const uint64_t vm = u ? vm1 : vm0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[u][r] = ((vm >> (4 * g + r)) & 1) ? z[r] * zs : NEG;
+    }
+    float m = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
+    const float m_use = m == NEG ? 0.f : m;  // an empty wave: every p is 0
     float p[2][4];
     float lsum = 0.f;
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            p[tau][r] = (ok[tau][r] && m != -__builtin_inff()) ? exp2f(s[tau][r] - m) : 0.f;
-            lsum += p[tau][r];
+            p[u][r] = __builtin_amdgcn_exp2f(s[u][r] - m_use);  // 2^-inf = 0
+            lsum += p[u][r];
         }
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
@@ -269,36 +252,24 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
         sh.m[wave][n16] = m;
         sh.l[wave][n16] = lsum;
     }
-
-    // ---- O = P V: A = P (head n16, entry slots 8g + j), one variant per V block
-    bf16x8_t pf[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        float v[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            v[r] = p[0][r] * W.sv[4 * g + r][b];
-            v[4 + r] = p[1][r] * W.sv[16 + 4 * g + r][b];
-        }
-        pf[b] = as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-    }
+    // ---- O^T = V^T P^T: A = V^T (dim n16, slots 8 g + j), B = P^T (slots, head n16);
+    // lane holds head n16, dims 16 t8 + 4 g + r
+    const bf16x8_t pf = as_bf16x8(__builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][0], (__bf16)p[1][0]}),
+                                  __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][1], (__bf16)p[1][1]}),
+                                  __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][2], (__bf16)p[1][2]}),
+                                  __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][3], (__bf16)p[1][3]}));
     f32x4_t o[8];
 #pragma unroll
     for (int t8 = 0; t8 < 8; ++t8) {
-        const uint16_t* vr = &W.vt[16 * t8 + n16][0];
-        const uint2 a = *reinterpret_cast<const uint2*>(vr + 4 * g);
-        const uint2 b2 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
-        const bf16x8_t vf = as_bf16x8(a.x, a.y, b2.x, b2.y);
-        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[t8 >> 1], vf, z, 0, 0, 0);
+        const uint4 vv = *reinterpret_cast<const uint4*>(&vt[vt_addr(16 * t8 + n16) + 4 * g]);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv.x, vv.y, vv.z, vv.w), pf, z, 0, 0, 0);
     }
     __syncthreads();  // every wave is done with its V^T tile
-    // O tile: lane holds dim 16 t8 + n16, heads 4 g + r
 #pragma unroll
     for (int t8 = 0; t8 < 8; ++t8)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sh.u.obuf[wave][4 * g + r][16 * t8 + n16] = o[t8][r];
+        *reinterpret_cast<float4*>(&sh.u.obuf[wave][n16][16 * t8 + 4 * g]) =
+            make_float4(o[t8][0], o[t8][1], o[t8][2], o[t8][3]);
     __syncthreads();
 
     // ---- combine the waves: thread -> head h, 4 dims
@@ -392,10 +363,6 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
 // 32 g .. 32 g + 31 of K and of V (one scale block each).  The K fragment of
 // k-step kb is dims 32 g + 8 kb .. + 8 (the Q fragment uses the same map).
 constexpr int kLW = 4;                       // waves per workgroup
-constexpr int kVtRow = 16;                   // dwords per V^T row (32 slots)
-constexpr int kVtWave = kHeadDim * kVtRow + 4 * kVtRow;  // + a 16-dword skew per 32 rows
-
-__device__ __forceinline__ int vt_addr(int d) { return d * kVtRow + (d >> 5) * kVtRow; }
 
 struct LoopLds {
     union {
@@ -404,36 +371,6 @@ struct LoopLds {
     } u;
     float m[kLW][kHeads];
     float l[kLW][kHeads];
-};
-
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-
-__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t w, float sc, int sel) {
-    bf16x2_t r;
-    switch (sel) {
-        case 0: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0); break;
-        case 1: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1); break;
-        case 2: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2); break;
-        default: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3); break;
-    }
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-// 32 FP4 codes (16 bytes) of one scale block -> 16 dwords of bf16 pairs.
-__device__ __forceinline__ void dq_block(uint4 c, float sc, uint32_t (&o)[16]) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        o[4 * i + 0] = cvt_fp4x2(w[i], sc, 0);
-        o[4 * i + 1] = cvt_fp4x2(w[i], sc, 1);
-        o[4 * i + 2] = cvt_fp4x2(w[i], sc, 2);
-        o[4 * i + 3] = cvt_fp4x2(w[i], sc, 3);
-    }
-}
-
-struct RowRaw {  // the FP4 data one lane loads for one entry
-    uint4 k, v;
-    uint32_t sk, sv;  // scale bytes of the lane's K and V blocks
 };
 
 // grid nq, kLW * 64 threads.
