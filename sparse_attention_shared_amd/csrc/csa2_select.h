@@ -33,10 +33,11 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Padded histogram index: one spare word every 64 bins, so that 64 lanes
-// reading 64 consecutive bins each hit 64 different LDS banks.
-__device__ __forceinline__ int hidx(int b) { return b + (b >> 6); }
-constexpr int kHistWords = 4096 + 64;  // LDS ints a 12-bit digit needs
+// Padded histogram index: four spare words every 64 bins, so that 64 lanes
+// adding to 64 consecutive bins hit 64 different LDS banks, and every run of
+// 64 bins starts 16-byte aligned (the bucket search reads them as int4).
+__device__ __forceinline__ int hidx(int b) { return b + 4 * (b >> 6); }
+constexpr int kHistWords = 4096 + 256;  // LDS ints a 12-bit digit needs
 
 // Bucket search by one wave over nb bins (descending): finds the bin where the
 // running count from the top first reaches rem.  Phase A: lane l sums bins
@@ -47,12 +48,20 @@ constexpr int kHistWords = 4096 + 64;  // LDS ints a 12-bit digit needs
 __device__ __forceinline__ void wave_find_bucket(const int* hist, int nb, int rem, int* res) {
     const int lane = threadIdx.x & 63;
     const int per = nb >> 6;  // 64 bins per lane for 12-bit digits, 4 for 8-bit
-    const int top = nb - 1 - per * lane;
+    // lane l sums bins [nb - per (l + 1), nb - per l): contiguous, 16-byte aligned
+    const int4* blk = reinterpret_cast<const int4*>(hist + hidx(nb - per * (lane + 1)));
     int sa = 0;
-    for (int j = 0; j < per; j += 4) {
-        const int v0 = hist[hidx(top - j)], v1 = hist[hidx(top - j - 1)];
-        const int v2 = hist[hidx(top - j - 2)], v3 = hist[hidx(top - j - 3)];
-        sa += v0 + v1 + v2 + v3;
+    if (per == 64) {
+        int4 v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = blk[j];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sa += v[j].x + v[j].y + v[j].z + v[j].w;
+    } else {
+        for (int j = 0; j < per / 4; ++j) {
+            const int4 v = blk[j];
+            sa += v.x + v.y + v.z + v.w;
+        }
     }
     const int incl = wave_scan_dpp(sa);
     const int total = __builtin_amdgcn_readlane(incl, 63);
@@ -228,24 +237,24 @@ __device__ int ordered_write(KeyFn K, int64_t n, uint32_t tau, int need, const i
 }
 
 // LDS of reg_select.
-template <int NT, int CAP>
+template <int NT>
 struct RegSelShared {
-    int hist[kHistWords];
-    alignas(16) uint32_t cand[CAP + 4];
+    alignas(16) int hist[kHistWords];
     int tmp[NT / 64 + 1];
     int res[4];
-    int ncand;
 };
 
 // Top-kk of one row of n <= NT * PER slots by one workgroup, keys in
 // registers: thread t owns slots [t*PER, t*PER + PER); slot i is written as
 // ids[i] when IDS (ids non-null, 16-byte aligned rows), else as i.  A 12-bit histogram
-// finds the boundary bucket; the keys of that bucket (at most CAP) are
-// resolved exactly in LDS; one block scan of packed (greater, equal) counts
-// then places every chosen slot, ascending.  Writes dst[0..kk), -1 padded.
-template <int NT, int PER, int CAP, bool IDS>
+// finds the boundary bucket; further 12- and 8-bit histograms of the register
+// keys inside it resolve the exact (tau, need), stopping as soon as a whole
+// sub-bucket completes the selection; one block scan of packed (greater,
+// equal) counts then places every chosen slot, ascending.  Writes dst[0..kk),
+// -1 padded.
+template <int NT, int PER, bool IDS>
 __device__ void reg_select(const float* s, const int32_t* ids, int n, int kk, int32_t* dst,
-                           RegSelShared<NT, CAP>& sh) {
+                           RegSelShared<NT>& sh) {
     static_assert(PER % 4 == 0, "PER must be a multiple of 4");
     const int tid = threadIdx.x;
     const int s0 = tid * PER;
@@ -275,7 +284,6 @@ __device__ void reg_select(const float* s, const int32_t* ids, int n, int kk, in
         }
     }
     for (int i = tid; i < kHistWords; i += NT) sh.hist[i] = 0;
-    if (tid == 0) sh.ncand = 0;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < PER; ++j)
@@ -289,69 +297,33 @@ __device__ void reg_select(const float* s, const int32_t* ids, int n, int kk, in
     uint32_t tau = 0u;
     int need = 0;
     if (total_valid > kk && cnt != rem) {
-        // keys of the boundary bucket -> LDS (one LDS atomic per wave)
-        const int lane = tid & 63;
-        int mine = 0;
+        // resolve the boundary bucket on the register keys: 12 more bits, then
+        // the last 8 unless a whole sub-bucket completes the selection
+        uint32_t prefix = b1 << 20, mask = 0xFFF00000u;
+        int r = rem;
+        bool done = false;
+        for (int shift = 8; shift >= 0 && !done; shift -= 8) {
+            const int bits = shift ? 12 : 8;
+            const uint32_t dm = (1u << bits) - 1u;
+            for (int i = tid; i < kHistWords; i += NT) sh.hist[i] = 0;
+            __syncthreads();
 #pragma unroll
-        for (int j = 0; j < PER; ++j) mine += key[j] && (key[j] >> 20) == b1;
-        const int incl = wave_scan_dpp(mine);
-        int base = 0;
-        if (lane == 63 && incl) base = atomicAdd(&sh.ncand, incl);  // one LDS atomic per wave
-        int pos = __builtin_amdgcn_readlane(base, 63) + incl - mine;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            if (key[j] && (key[j] >> 20) == b1) {
-                if (pos < CAP) sh.cand[pos] = key[j];
-                ++pos;
-            }
+            for (int j = 0; j < PER; ++j)
+                if (key[j] && (key[j] & mask) == prefix)
+                    atomicAdd(&sh.hist[hidx((int)((key[j] >> shift) & dm))], 1);
+            __syncthreads();
+            if (tid < 64) wave_find_bucket(sh.hist, 1 << bits, r, sh.res);
+            __syncthreads();
+            prefix |= (uint32_t)sh.res[0] << shift;
+            mask |= dm << shift;
+            r -= sh.res[1];
+            done = sh.res[2] == r;  // the whole sub-bucket is taken
+            __syncthreads();
         }
-        __syncthreads();
-        const int m = sh.ncand;
-        if (m <= NT && m + 4 <= CAP + 4) {
-            // small bucket: the rem-th largest key by counting, one candidate per thread
-            if (tid < 4) sh.cand[m + tid] = 0u;  // pad to whole uint4 reads (key 0 counts for nothing)
-            __syncthreads();
-            const uint32_t mine = tid < m ? sh.cand[tid] : 0u;
-            int gt = 0, ge = 0;
-            const uint4* c4 = reinterpret_cast<const uint4*>(sh.cand);
-#pragma unroll 4
-            for (int j = 0; j < (m + 3) / 4; ++j) {
-                const uint4 o = c4[j];
-                gt += (o.x > mine) + (o.y > mine) + (o.z > mine) + (o.w > mine);
-                ge += (o.x >= mine) + (o.y >= mine) + (o.z >= mine) + (o.w >= mine);
-            }
-            if (tid == 0) sh.res[0] = 0;
-            __syncthreads();
-            if (tid < m && gt < rem && ge >= rem) {
-                sh.res[0] = (int)mine;  // every thread holding this key writes the same
-                sh.res[1] = rem - gt;
-            }
-            __syncthreads();
-            tau = (uint32_t)sh.res[0];
-            need = sh.res[1];
-        } else if (m <= CAP) {
-            lds_kth<NT>(sh.cand, m, rem, 12, sh.hist, sh.res, tau, need);
+        if (done) {
+            tau = prefix - 1u;  // every key >= prefix (the remaining bits are free)
+            need = 0;
         } else {
-            // the bucket does not fit: refine over the register keys, 12 then 8 bits
-            uint32_t prefix = b1 << 20, mask = 0xFFF00000u;
-            int r = rem;
-            for (int shift = 8; shift >= 0; shift -= 8) {
-                const int bits = shift ? 12 : 8;
-                const uint32_t dm = (1u << bits) - 1u;
-                for (int i = tid; i < kHistWords; i += NT) sh.hist[i] = 0;
-                __syncthreads();
-#pragma unroll
-                for (int j = 0; j < PER; ++j)
-                    if (key[j] && (key[j] & mask) == prefix)
-                        atomicAdd(&sh.hist[hidx((int)((key[j] >> shift) & dm))], 1);
-                __syncthreads();
-                if (tid < 64) wave_find_bucket(sh.hist, 1 << bits, r, sh.res);
-                __syncthreads();
-                prefix |= (uint32_t)sh.res[0] << shift;
-                mask |= dm << shift;
-                r -= sh.res[1];
-                __syncthreads();
-            }
             tau = prefix;
             need = r;
         }

@@ -212,7 +212,7 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 }
 
 struct PfThrLds {
-    int hist[kHistWords];
+    alignas(16) int hist[kHistWords];
     int res[4];
 };
 
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ 
 
 // ---- 4. select ---------------------------------------------------------------
 struct PfSelLds {
-    int hist[kHistWords];
+    alignas(16) int hist[kHistWords];
     uint32_t skey[kPfCap];
     int32_t spos[kPfCap];
     int tmp[kPfSelNT / 64 + 1];

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
                                                          int64_t n_cand, float* __restrict__ scores,
                                                          uint32_t* __restrict__ ctr, int32_t k,
                                                          int32_t* __restrict__ sel) {
-    __shared__ RegSelShared<kSelNT, 4096> sh;
+    __shared__ RegSelShared<kSelNT> sh;
     __shared__ int last;
     const int qi = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
     if (!last) return;
     if (threadIdx.x == 0) __threadfence();  // acquire for the whole workgroup
     __syncthreads();
-    reg_select<kSelNT, kSelMaxCand / kSelNT, 4096, true>(srow, crow, (int)n_cand, k,
+    reg_select<kSelNT, kSelMaxCand / kSelNT, true>(srow, crow, (int)n_cand, k,
                                                    sel + (int64_t)qi * k, sh);
     if (threadIdx.x == 0) ctr[qi] = 0u;
 }

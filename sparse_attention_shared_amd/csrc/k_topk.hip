@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kSmallNT) void k_topk_small(const float* __restrict
                                                          const int32_t* __restrict__ ids,
                                                          int32_t k, int32_t* __restrict__ out,
                                                          int32_t k2, int32_t* __restrict__ out2) {
-    __shared__ RegSelShared<kSmallNT, 8192> sh;
+    __shared__ RegSelShared<kSmallNT> sh;
     const int64_t row = blockIdx.x;
     const float* s = scores + row * ld;
     const int32_t* irow = IDS ? ids + row * n : nullptr;
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kSmallNT) void k_topk_small(const float* __restrict
         if (t) __syncthreads();
         const int32_t kk = t ? k2 : k;
         int32_t* dst = t ? out2 + row * k2 : out + row * k;
-        reg_select<kSmallNT, PER, 8192, IDS>(s, irow, (int)n, kk, dst, sh);
+        reg_select<kSmallNT, PER, IDS>(s, irow, (int)n, kk, dst, sh);
     }
 }
 
@@ -89,7 +89,7 @@ __device__ __forceinline__ int64_t chunk_begin(int c) { return (int64_t)c * kChu
 __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__ scores, int64_t n,
                                                        int64_t ld, const int32_t* __restrict__ ids,
                                                        int32_t k, int32_t k2, LongWs ws) {
-    __shared__ int hist[kHistWords];
+    __shared__ alignas(16) int hist[kHistWords];
     __shared__ int res[4];
     __shared__ int last;
     const int c = blockIdx.x, nc = gridDim.x;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
                                                        int32_t k, int32_t k2, LongWs ws) {
     __shared__ uint32_t ckeys[kCandCap];
     __shared__ int32_t cslot[kCandCap];
-    __shared__ int hist[kHistWords];
+    __shared__ alignas(16) int hist[kHistWords];
     __shared__ int tmp[kLongNT / 64 + 1];
     __shared__ int res[4];
     __shared__ int cnt_gt[kMaxTargets], cnt_cand[kMaxTargets], cbase[kMaxTargets];
