@@ -87,9 +87,9 @@ struct RowRaw {  // the FP4 data one lane loads for one entry
 };
 
 struct AttnLds {
-    union {
+    struct {  // not aliased: a wave stores its O as soon as its own products are done
         uint32_t vt[kWaves][kVtWave];
-        float obuf[kWaves][kHeads][kHeadDim + 4];  // after the V^T tiles are consumed
+        float obuf[kWaves][kHeads][kHeadDim + 4];
     } u;
     float m[kWaves][kHeads];
     float l[kWaves][kHeads];
@@ -265,27 +265,35 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv.x, vv.y, vv.z, vv.w), pf, z, 0, 0, 0);
     }
-    __syncthreads();  // every wave is done with its V^T tile
 #pragma unroll
     for (int t8 = 0; t8 < 8; ++t8)
         *reinterpret_cast<float4*>(&sh.u.obuf[wave][n16][16 * t8 + 4 * g]) =
             make_float4(o[t8][0], o[t8][1], o[t8][2], o[t8][3]);
     __syncthreads();
 
-    // ---- combine the waves: thread -> head h, 4 dims
+    // ---- combine the waves: thread -> head h, 4 dims (2^-inf = 0 drops an empty wave)
     const int h = tid >> 5, d0 = (tid & 31) * 4;
+    float mw[kWaves], lw[kWaves];
+    float4 ow[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        mw[w] = sh.m[w][h];
+        lw[w] = sh.l[w][h];
+        ow[w] = *reinterpret_cast<const float4*>(&sh.u.obuf[w][h][d0]);
+    }
     float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.m[w][h]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
     float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (M != -__builtin_inff()) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float mw = sh.m[w][h];
-            const float f = (mw == -__builtin_inff()) ? 0.f : exp2f(mw - M);
-            L = fmaf(sh.l[w][h], f, L);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = fmaf(sh.u.obuf[w][h][d0 + i], f, acc[i]);
+            const float f = __builtin_amdgcn_exp2f(mw[w] - M);
+            L = fmaf(lw[w], f, L);
+            acc[0] = fmaf(ow[w].x, f, acc[0]);
+            acc[1] = fmaf(ow[w].y, f, acc[1]);
+            acc[2] = fmaf(ow[w].z, f, acc[2]);
+            acc[3] = fmaf(ow[w].w, f, acc[3]);
         }
     }
     uint16_t* orow = out + ((int64_t)qi * kHeads + h) * kHeadDim + d0;
@@ -328,12 +336,12 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
 #pragma unroll
         for (int u = 0; u < 16; ++u) Mn = fmaxf(Mn, ml[u].x);
         if (Mn == -__builtin_inff()) continue;
-        const float rs = (Mq == -__builtin_inff()) ? 0.f : exp2f(Mq - Mn);
+        const float rs = __builtin_amdgcn_exp2f(Mq - Mn);  // Mq = -inf: 0
         Lq *= rs;
         aq[0] *= rs; aq[1] *= rs; aq[2] *= rs; aq[3] *= rs;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const float f = (ml[u].x == -__builtin_inff()) ? 0.f : exp2f(ml[u].x - Mn);
+            const float f = __builtin_amdgcn_exp2f(ml[u].x - Mn);  // an empty chunk: 0
             Lq = fmaf(ml[u].y, f, Lq);
             aq[0] = fmaf(ov[u].x, f, aq[0]);
             aq[1] = fmaf(ov[u].y, f, aq[1]);
