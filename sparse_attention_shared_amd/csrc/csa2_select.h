@@ -23,6 +23,31 @@ __device__ __forceinline__ uint32_t load_key(const float* s, const int32_t* ids,
     return k == kNegInfKey ? 0u : k;
 }
 
+// Keys of slots first + j * STRIDE (j < PER) of a row of n >= 1 slots; slots
+// past n give key 0.  Every load is issued before any is used (indices are
+// clamped, so no branch guards them).
+template <int PER, int STRIDE>
+__device__ __forceinline__ void load_keys(const float* s, const int32_t* ids, int64_t n,
+                                          int64_t first, uint32_t (&kr)[PER]) {
+    float v[PER];
+    int32_t w[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[j] = s[min(first + (int64_t)j * STRIDE, n - 1)];
+    if (ids) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) w[j] = ids[min(first + (int64_t)j * STRIDE, n - 1)];
+    } else {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) w[j] = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t k = score_key(v[j]);
+        const bool ok = first + (int64_t)j * STRIDE < n && w[j] >= 0 && k != kNegInfKey;
+        kr[j] = ok ? k : 0u;
+    }
+}
+
 __device__ __forceinline__ int wave_sum_dpp(int x) {
     return __builtin_amdgcn_readlane(wave_scan_dpp(x), 63);
 }

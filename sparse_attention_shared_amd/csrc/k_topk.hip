@@ -103,11 +103,7 @@ __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__
     constexpr int kPer = kChunk / kLongNT;
     const int64_t b0 = chunk_begin(c);
     uint32_t kr[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int64_t i = b0 + tid + (int64_t)j * kLongNT;
-        kr[j] = i < n ? load_key(s, irow, i) : 0u;
-    }
+    load_keys<kPer, kLongNT>(s, irow, n, b0 + tid, kr);
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
         if (kr[j]) atomicAdd(&hist[hidx((int)(kr[j] >> 20))], 1);
@@ -177,8 +173,8 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
     const int32_t* irow = ids ? ids + row * n : nullptr;
     RowState* st = ws.st + row;
     const int nt = k2 > 0 ? 2 : 1;
-    uint32_t bucket[kMaxTargets];
-    int rem[kMaxTargets];
+    uint32_t bucket[kMaxTargets] = {0u, 0u};
+    int rem[kMaxTargets] = {0, 0};
     for (int t = 0; t < nt; ++t) {
         bucket[t] = st->bucket[t];
         rem[t] = st->rem[t];
@@ -192,50 +188,61 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
     constexpr int kPer = kChunk / kLongNT;
     const int64_t b0 = chunk_begin(c);
     uint32_t kr[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int64_t i = b0 + tid + (int64_t)j * kLongNT;
-        kr[j] = i < n ? load_key(s, irow, i) : 0u;
-    }
+    load_keys<kPer, kLongNT>(s, irow, n, b0 + tid, kr);
+    // per target: keys above the boundary bucket and keys inside it
     int gt[kMaxTargets] = {0, 0}, nca[kMaxTargets] = {0, 0};
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const uint32_t key = kr[j];
-        if (!key) continue;
-        const uint32_t d = key >> 20;
-        for (int t = 0; t < nt; ++t) {
-            if (rem[t] < 0 || d > bucket[t]) gt[t] += 1;
-            else if (d == bucket[t]) nca[t] += 1;
+    for (int t = 0; t < kMaxTargets; ++t) {
+        const bool all = rem[t] < 0;
+        const uint32_t bk = bucket[t];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const uint32_t d = kr[j] >> 20;
+            gt[t] += kr[j] && (all || d > bk);
+            nca[t] += kr[j] && !all && d == bk;
         }
     }
-    for (int t = 0; t < nt; ++t) {
-        if (nca[t]) atomicAdd(&cnt_cand[t], nca[t]);
+    // wave totals, one LDS atomic per wave: the wave's base in the chunk's
+    // range of the candidate list, and the chunk's count of keys above it
+    const int lane = tid & 63;
+    int wbase[kMaxTargets] = {0, 0};
+#pragma unroll
+    for (int t = 0; t < kMaxTargets; ++t) {
+        if (t >= nt) break;
+        const int wn = wave_sum_dpp(nca[t]), wg = wave_sum_dpp(gt[t]);
+        int b = 0;
+        if (lane == 0) {
+            if (wn) b = atomicAdd(&cnt_cand[t], wn);
+            if (wg) atomicAdd(&cnt_gt[t], wg);
+        }
+        wbase[t] = __builtin_amdgcn_readfirstlane(b);
     }
     __syncthreads();
     if (tid < nt) {
         // one device atomic per chunk reserves its range of the candidate list
         cbase[tid] = (int)atomicAdd(&st->ncand[tid], (uint32_t)cnt_cand[tid]);
-        cnt_cand[tid] = 0;
     }
     __syncthreads();
+    // candidates go to their place by ballots: no atomics per key
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const uint32_t key = kr[j];
-        if (!key) continue;
-        const uint32_t d = key >> 20;
-        for (int t = 0; t < nt; ++t) {
-            if (rem[t] >= 0 && d == bucket[t]) {
-                const int pos = cbase[t] + atomicAdd(&cnt_cand[t], 1);
+    for (int t = 0; t < kMaxTargets; ++t) {
+        if (t >= nt || rem[t] < 0) continue;
+        Cand* cb = ws.cand + ((int64_t)row * kMaxTargets + t) * kCandCap;
+        int pos0 = cbase[t] + wbase[t];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const bool is = kr[j] && (kr[j] >> 20) == bucket[t];
+            const uint64_t m = __ballot(is);
+            if (is) {
+                const int pos = pos0 + lanes_below(m);
                 if (pos < kCandCap) {
-                    Cand* cb = ws.cand + ((int64_t)row * kMaxTargets + t) * kCandCap;
-                    cb[pos].key = key;
+                    cb[pos].key = kr[j];
                     cb[pos].slot = (int32_t)(tid + (int64_t)j * kLongNT + b0);
                 }
             }
+            pos0 += __popcll(m);
         }
     }
-    for (int t = 0; t < nt; ++t) atomicAdd(&cnt_gt[t], gt[t]);
-    __syncthreads();
     if (tid < nt) ws.rec[((int64_t)row * kMaxTargets + tid) * nc + c].gt = cnt_gt[tid];
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
     if (tid == 0) {
@@ -246,11 +253,32 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
     if (!last) return;
     if (tid == 0) __threadfence();  // acquire for the whole workgroup
     __syncthreads();
-    // ---- last workgroup of the row: exact (tau, need) and chunk offsets
-    for (int t = 0; t < nt; ++t) {
+    // ---- last workgroup of the row: exact (tau, need) and chunk offsets.
+    // Every load it needs is issued first: both targets' candidate lists
+    // (whole buffers: slots past the count are read but not used) and the
+    // per-chunk counts of keys above the bucket.
+    static_assert(kCandCap == 8 * kLongNT, "eight candidates per thread");
+    const int cper = (nc + kLongNT - 1) / kLongNT;  // nc <= 2048 chunks: at most 4
+    const int cc0 = min(nc, tid * cper), cc1 = min(nc, cc0 + cper);
+    Cand cpre[kMaxTargets][8];
+    int gpre[kMaxTargets][4];
+    uint32_t mpre[kMaxTargets];
+#pragma unroll
+    for (int t = 0; t < kMaxTargets; ++t) {
+        mpre[t] = t < nt ? __hip_atomic_load(&st->ncand[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        const Cand* cb = ws.cand + ((int64_t)row * kMaxTargets + t) * kCandCap;
+        const ChunkRec* rec = ws.rec + ((int64_t)row * kMaxTargets + t) * nc;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cpre[t][u] = t < nt ? cb[tid + u * kLongNT] : Cand{0u, 0};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) gpre[t][u] = (t < nt && cc0 + u < cc1) ? rec[cc0 + u].gt : 0;
+    }
+#pragma unroll
+    for (int t = 0; t < kMaxTargets; ++t) {
+        if (t >= nt) break;
         const int kk = t ? k2 : k;
         ChunkRec* rec = ws.rec + ((int64_t)row * kMaxTargets + t) * nc;
-        const uint32_t m = __hip_atomic_load(&st->ncand[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t m = mpre[t];
         uint32_t tau;
         int need;
         bool exact = true;
@@ -258,21 +286,12 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
             tau = 0u;  // all selectable keys
             need = 0;
         } else if (m <= (uint32_t)kCandCap) {
-            const Cand* cb = ws.cand + ((int64_t)row * kMaxTargets + t) * kCandCap;
-            for (int i0 = tid; i0 < (int)m; i0 += 8 * kLongNT) {
-                Cand cv[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int i = i0 + u * kLongNT;
-                    if (i < (int)m) cv[u] = cb[i];
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int i = i0 + u * kLongNT;
-                    if (i < (int)m) {
-                        ckeys[i] = cv[u].key;
-                        cslot[i] = cv[u].slot;
-                    }
+            for (int u = 0; u < 8; ++u) {
+                const int i = tid + u * kLongNT;
+                if (i < (int)m) {
+                    ckeys[i] = cpre[t][u].key;
+                    cslot[i] = cpre[t][u].slot;
                 }
             }
             __syncthreads();
@@ -328,10 +347,26 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
         __syncthreads();
         if (rem[t] >= 0) {
             if (exact) {
-                for (int i = tid; i < (int)m; i += kLongNT) {
-                    const int ch = cslot[i] / kChunk;
-                    if (ckeys[i] > tau) atomicAdd(&cgt[ch], 1);
-                    else if (ckeys[i] == tau && need > 0) atomicAdd(&ceq[ch], 1);
+                // a chunk's candidates are contiguous in the list, so a wave's
+                // 64 usually share one chunk: then one atomic per wave
+                const int lane = tid & 63;
+                for (int i0 = tid - lane; i0 < (int)m; i0 += kLongNT) {
+                    const int i = i0 + lane;
+                    const bool in = i < (int)m;
+                    const int ch = in ? cslot[i] / kChunk : -1;
+                    const int g1 = in && ckeys[i] > tau;
+                    const int e1 = in && ckeys[i] == tau && need > 0;
+                    const int ch0 = __builtin_amdgcn_readfirstlane(ch);
+                    if (__ballot(in && ch != ch0) == 0) {
+                        const int sg = wave_sum_dpp(g1), se = wave_sum_dpp(e1);
+                        if (lane == 0) {
+                            if (sg) atomicAdd(&cgt[ch0], sg);
+                            if (se) atomicAdd(&ceq[ch0], se);
+                        }
+                    } else if (in) {
+                        if (g1) atomicAdd(&cgt[ch], 1);
+                        else if (e1) atomicAdd(&ceq[ch], 1);
+                    }
                 }
             } else {
                 for (int64_t i = tid; i < n; i += kLongNT) {
@@ -345,11 +380,10 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
         __syncthreads();
         {
             // chunk offsets: each thread owns a run of consecutive chunks
-            const int per = (nc + kLongNT - 1) / kLongNT;
-            const int c0 = min(nc, tid * per), c1 = min(nc, c0 + per);
-            int gtv[4], eqsum = 0;  // nc <= 2048 chunks: per <= 4
+            const int c0 = cc0, c1 = cc1;
+            int gtv[4], eqsum = 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) gtv[u] = (c0 + u < c1) ? rec[c0 + u].gt : 0;
+            for (int u = 0; u < 4; ++u) gtv[u] = gpre[t][u];
             for (int ch = c0; ch < c1; ++ch) eqsum += ceq[ch];
             int tot;
             int eqb = block_excl_scan<kLongNT>(eqsum, tmp, &tot);
