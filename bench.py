@@ -7,10 +7,12 @@ top-2048, then [Reindex, Reuse, Reuse, Reuse] repeats; every layer attends to
 its 2048 selected entries plus a 128-position local window.
 
 One step = one decode token for every sequence through all 20 layers (index
-scoring, top-k, gather + FP4 dequant, attention), launched through the C ABI
-(csa2_stack_run).  Inputs are resident in HBM before the timed region; the
-timed steps rotate over several copies of the cache so that consecutive steps
-do not find it in the 256 MB Infinity Cache.
+scoring, top-k, gather + FP4 dequant, attention) through the C ABI: by default
+every kernel launched from the host (csa2_stack_run); --graph replays a stack
+recorded once per cache copy (csa2_stack_plan_create) as a HIP graph.  Inputs
+are resident in HBM before the timed region; the timed steps rotate over
+several copies of the cache so that consecutive steps do not find it in the
+256 MB Infinity Cache.
 
 With --workload prefill it times the prefill chunk instead: 4096 queries at
 positions 126976..131071 of one 131072-token sequence, each selecting its
@@ -236,6 +238,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["repeat", "page"], default="repeat")
     ap.add_argument("--workload", choices=["decode", "prefill"], default="decode")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay a recorded stack (HIP graph) per step instead of host launches")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -299,32 +303,65 @@ def main():
                                       sp.pool, 1, 128 ** -0.5, None, None))
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
 
-    n_ev = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_ev)]
-    for a, b in ev:  # create the underlying HIP events
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
+    if not args.graph:
+        n_ev = args.steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_ev)]
+        for a, b in ev:  # create the underlying HIP events
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
 
-    def step(i, events=None):
-        csa2.stack_run(caches[i % len(caches)], sp.schedule, q_pos, q, q_idx, local, sp.k,
-                       sp.pool, want_sel=False, ws=ws, out=out, scan_events=events)
+        def step(i, events=None):
+            csa2.stack_run(caches[i % len(caches)], sp.schedule, q_pos, q, q_idx, local, sp.k,
+                           sp.pool, want_sel=False, ws=ws, out=out, scan_events=events)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        step(i, ev[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t_start.elapsed_time(t_end) / args.steps
-    scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t_start.record()
+        for i in range(args.steps):
+            step(i, ev[i])
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms = t_start.elapsed_time(t_end) / args.steps
+        scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    else:
+        # one recorded stack (HIP graph) per cache copy
+        plans = [csa2.StackPlan(c, sp.schedule, q_pos, q, q_idx, local, sp.k, sp.pool, out=out)
+                 for c in caches]
+        for i in range(args.warmup):
+            plans[i % len(plans)].launch()
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t_start.record()
+        for i in range(args.steps):
+            plans[i % len(plans)].launch()
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms = t_start.elapsed_time(t_end) / args.steps
+        for pl in plans:
+            pl.close()
+        # events recorded inside a graph do not bracket its kernels, so the
+        # scan is timed on host-launched steps of the same stack
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(40)]
+        for a, b in ev:  # create the underlying HIP events
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for i, e in enumerate(ev):
+            csa2.stack_run(caches[i % len(caches)], sp.schedule, q_pos, q, q_idx, local, sp.k,
+                           sp.pool, want_sel=False, ws=ws, out=out, scan_events=e)
+        torch.cuda.synchronize()
+        scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
 
     step_bytes = algorithmic_bytes(sp.schedule, B, T, sp.k, sp.pool, sp.window)
     scan_bytes = B * T * 128
@@ -351,6 +388,8 @@ def main():
             "schedule": "".join("FIU"[m] for m in sp.schedule),
             "k": sp.k, "pool": sp.pool, "window": sp.window,
             "cache_copies_rotated": args.copies,
+            "launch": "recorded stack replayed as a HIP graph (csa2_stack_plan_launch)"
+                      if args.graph else "host launches (csa2_stack_run)",
         },
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,

@@ -252,6 +252,23 @@ csa2_status csa2_stack_workspace(const csa2_stack_desc *desc, size_t *bytes);
  * pool > 0 and pool % block == 0. */
 csa2_status csa2_stack_run(const csa2_stack_desc *desc, void *ws, size_t ws_bytes, void *stream);
 
+/* A stack plan records what csa2_stack_run would enqueue, once, into a HIP
+ * graph; each launch replays it on `stream`.  Every pointer of `desc` and `ws`
+ * is fixed at creation: the caller keeps those buffers alive for the plan's
+ * life and may change their contents between launches (new queries, new
+ * cache rows).  The workspace follows the csa2_stack_workspace rules (zero
+ * before the first launch, left zero by each); launches of plans sharing a
+ * workspace must not overlap.  With scan_events set, the event records are
+ * part of the graph.  Creation validates like csa2_stack_run and returns its
+ * codes (CSA2_ERR_HIP if the runtime cannot record or instantiate the graph);
+ * the plan object and its graph are the only memory the library allocates,
+ * released by csa2_stack_plan_destroy. */
+typedef struct csa2_stack_plan csa2_stack_plan;
+csa2_status csa2_stack_plan_create(const csa2_stack_desc *desc, void *ws, size_t ws_bytes,
+                                   csa2_stack_plan **plan);
+csa2_status csa2_stack_plan_launch(const csa2_stack_plan *plan, void *stream);
+csa2_status csa2_stack_plan_destroy(csa2_stack_plan *plan);
+
 #ifdef __cplusplus
 }
 #endif

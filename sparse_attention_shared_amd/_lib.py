@@ -76,10 +76,15 @@ def lib() -> ctypes.CDLL:
         L.csa2_sparse_attn_workspace.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_sz)]
         L.csa2_stack_workspace.argtypes = [ctypes.POINTER(csa2_stack_desc), ctypes.POINTER(_sz)]
         L.csa2_stack_run.argtypes = [ctypes.POINTER(csa2_stack_desc), _P, _sz, _P]
+        L.csa2_stack_plan_create.argtypes = [ctypes.POINTER(csa2_stack_desc), _P, _sz,
+                                             ctypes.POINTER(_P)]
+        L.csa2_stack_plan_launch.argtypes = [_P, _P]
+        L.csa2_stack_plan_destroy.argtypes = [_P]
         for f in ("csa2_pack_fp4", "csa2_unpack_fp4", "csa2_index_score", "csa2_prefill_score",
                   "csa2_prefill_topk", "csa2_prefill_topk_workspace", "csa2_topk",
                   "csa2_topk_workspace", "csa2_expand_blocks", "csa2_sparse_attn",
-                  "csa2_sparse_attn_workspace", "csa2_stack_workspace", "csa2_stack_run"):
+                  "csa2_sparse_attn_workspace", "csa2_stack_workspace", "csa2_stack_run",
+                  "csa2_stack_plan_create", "csa2_stack_plan_launch", "csa2_stack_plan_destroy"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -335,3 +340,51 @@ def stack_run(cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
     _check("csa2_stack_run", lib().csa2_stack_run(ctypes.byref(args.desc), _ptr(ws), ws.numel(),
                                                   _stream()))
     return out, sel, pool_out
+
+
+class StackPlan:
+    """A decoder stack recorded once into a HIP graph (csa2_stack_plan_*).
+
+    The output, selection, pool and workspace buffers are allocated here and
+    fixed for the plan's life; :meth:`launch` replays the whole stack on the
+    current stream (inputs may be updated in place between launches).
+    """
+
+    def __init__(self, cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
+                 q: Sequence[torch.Tensor], q_idx: Sequence[Optional[torch.Tensor]],
+                 local: Sequence[Local], k: int, pool: int = 0, block: int = 1,
+                 sm_scale: float = HEAD_DIM ** -0.5, want_sel: bool = False,
+                 out: Optional[Sequence[torch.Tensor]] = None, scan_events=None):
+        S = int(q_pos.shape[0])
+        dev = q_pos.device
+        self.out = out if out is not None else [
+            torch.empty((S, HEADS, HEAD_DIM), dtype=torch.bfloat16, device=dev) for _ in modes]
+        self.sel = ([torch.empty((S, k), dtype=torch.int32, device=dev) for _ in modes]
+                    if want_sel else None)
+        self.pool = torch.empty((S, pool), dtype=torch.int32, device=dev) if pool > 0 else None
+        ev = None
+        if scan_events is not None:
+            ev = tuple(ctypes.c_void_p(e.cuda_event) for e in scan_events)
+        self.args = _StackArgs(cache, modes, q_pos, q, q_idx, local, self.out, k, pool, block,
+                               sm_scale, self.sel, self.pool, ev)
+        need = stack_workspace(self.args)
+        self.ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize(dev)  # the zero fill lands before the plan is recorded
+        self._plan = _P()
+        _check("csa2_stack_plan_create", lib().csa2_stack_plan_create(
+            ctypes.byref(self.args.desc), _ptr(self.ws), self.ws.numel(), ctypes.byref(self._plan)))
+
+    def launch(self):
+        _check("csa2_stack_plan_launch", lib().csa2_stack_plan_launch(self._plan, _stream()))
+        return self.out, self.sel, self.pool
+
+    def close(self):
+        if getattr(self, "_plan", None) is not None and self._plan.value:
+            lib().csa2_stack_plan_destroy(self._plan)
+            self._plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <new>
 #include <vector>
 
 #include "csa2.h"
@@ -310,14 +311,11 @@ csa2_status csa2_stack_workspace(const csa2_stack_desc* d, size_t* bytes) {
     return CSA2_OK;
 }
 
-csa2_status csa2_stack_run(const csa2_stack_desc* d, void* ws, size_t ws_bytes, void* stream) {
-    CacheView cv;
-    int32_t mw;
-    if (csa2_status st = check_stack(d, &cv, &mw)) return st;
-    const StackWs W = stack_ws_layout(cv.n_seq, cv.t_cap, d->k, d->pool, d->block, mw);
-    if (!ws || ws_bytes < W.total) return CSA2_ERR_WORKSPACE;
-    if (csa2_status st = device_ok()) return st;
-    hipStream_t s = (hipStream_t)stream;
+}  // extern "C"
+
+// Enqueue every layer of a validated stack on s.
+static csa2_status enqueue_stack(const csa2_stack_desc* d, const CacheView& cv, const StackWs& W,
+                                 void* ws, hipStream_t s) {
     char* base = static_cast<char*>(ws);
     float* scores = reinterpret_cast<float*>(base + W.scores);
     float* bscores = reinterpret_cast<float*>(base + W.bscores);
@@ -380,6 +378,84 @@ csa2_status csa2_stack_run(const csa2_stack_desc* d, void* ws, size_t ws_bytes, 
         if (e != hipSuccess) return CSA2_ERR_HIP;
     }
     return CSA2_OK;
+}
+
+extern "C" {
+
+csa2_status csa2_stack_run(const csa2_stack_desc* d, void* ws, size_t ws_bytes, void* stream) {
+    CacheView cv;
+    int32_t mw;
+    if (csa2_status st = check_stack(d, &cv, &mw)) return st;
+    const StackWs W = stack_ws_layout(cv.n_seq, cv.t_cap, d->k, d->pool, d->block, mw);
+    if (!ws || ws_bytes < W.total) return CSA2_ERR_WORKSPACE;
+    if (csa2_status st = device_ok()) return st;
+    return enqueue_stack(d, cv, W, ws, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// A recorded stack: the graph captured from one enqueue_stack and its
+// executable instance.
+struct csa2_stack_plan {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+csa2_status csa2_stack_plan_create(const csa2_stack_desc* d, void* ws, size_t ws_bytes,
+                                   csa2_stack_plan** plan) {
+    if (!plan) return CSA2_ERR_INVALID_ARG;
+    *plan = nullptr;
+    CacheView cv;
+    int32_t mw;
+    if (csa2_status st = check_stack(d, &cv, &mw)) return st;
+    const StackWs W = stack_ws_layout(cv.n_seq, cv.t_cap, d->k, d->pool, d->block, mw);
+    if (!ws || ws_bytes < W.total) return CSA2_ERR_WORKSPACE;
+    if (csa2_status st = device_ok()) return st;
+    hipStream_t cs = nullptr;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return CSA2_ERR_HIP;
+    hipGraph_t graph = nullptr;
+    csa2_status st = CSA2_OK;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        st = CSA2_ERR_HIP;
+    } else {
+        st = enqueue_stack(d, cv, W, ws, cs);
+        // the capture must be ended whatever happened inside it
+        if (hipStreamEndCapture(cs, &graph) != hipSuccess && st == CSA2_OK) st = CSA2_ERR_HIP;
+    }
+    hipStreamDestroy(cs);
+    if (st == CSA2_OK && !graph) st = CSA2_ERR_HIP;
+    hipGraphExec_t exec = nullptr;
+    if (st == CSA2_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess)
+        st = CSA2_ERR_HIP;
+    csa2_stack_plan* p = nullptr;
+    if (st == CSA2_OK) {
+        p = new (std::nothrow) csa2_stack_plan;
+        if (!p) st = CSA2_ERR_HIP;
+    }
+    if (st != CSA2_OK) {
+        if (exec) hipGraphExecDestroy(exec);
+        if (graph) hipGraphDestroy(graph);
+        return st;
+    }
+    p->graph = graph;
+    p->exec = exec;
+    *plan = p;
+    return CSA2_OK;
+}
+
+csa2_status csa2_stack_plan_launch(const csa2_stack_plan* plan, void* stream) {
+    if (!plan || !plan->exec) return CSA2_ERR_INVALID_ARG;
+    return from_hip(hipGraphLaunch(plan->exec, (hipStream_t)stream));
+}
+
+csa2_status csa2_stack_plan_destroy(csa2_stack_plan* plan) {
+    if (!plan) return CSA2_OK;
+    hipError_t e1 = plan->exec ? hipGraphExecDestroy(plan->exec) : hipSuccess;
+    hipError_t e2 = plan->graph ? hipGraphDestroy(plan->graph) : hipSuccess;
+    delete plan;
+    return (e1 == hipSuccess && e2 == hipSuccess) ? CSA2_OK : CSA2_ERR_HIP;
 }
 
 }  // extern "C"

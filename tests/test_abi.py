@@ -155,3 +155,26 @@ def test_prefill_validation():
     assert L.csa2_prefill_topk(bp(c), 0, None, FAKE, 4, 64, FAKE, FAKE, n.value, None) == INVALID
     # nothing to do is not an error
     assert L.csa2_prefill_topk(bp(c), 0, None, None, 0, 64, None, None, 0, None) == OK
+
+
+def test_stack_plan_validation():
+    L = csa2.lib()
+    plan = _lib._P()
+    d, keep = _desc([2, 0])  # Reuse first
+    assert L.csa2_stack_plan_create(ctypes.byref(d), FAKE, 1 << 30, ctypes.byref(plan)) == SCHEDULE
+    assert plan.value is None
+    d, keep = _desc([0, 1, 2, 2])
+    assert L.csa2_stack_plan_create(ctypes.byref(d), FAKE, 1 << 30, None) == INVALID
+    assert L.csa2_stack_plan_create(ctypes.byref(d), FAKE, 1, ctypes.byref(plan)) == WORKSPACE
+    assert L.csa2_stack_plan_launch(None, None) == INVALID
+    assert L.csa2_stack_plan_destroy(None) == OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
+def test_stack_plan_without_a_device_reports_no_device():
+    L = csa2.lib()
+    d, keep = _desc([0, 1, 2, 2])
+    n = _lib._sz()
+    assert L.csa2_stack_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
+    plan = _lib._P()
+    assert L.csa2_stack_plan_create(ctypes.byref(d), FAKE, n.value, ctypes.byref(plan)) == NO_DEVICE
