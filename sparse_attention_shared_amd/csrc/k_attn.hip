@@ -271,42 +271,58 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
             make_float4(o[t8][0], o[t8][1], o[t8][2], o[t8][3]);
     __syncthreads();
 
-    // ---- combine the waves: thread -> head h, 4 dims (2^-inf = 0 drops an empty wave)
-    const int h = tid >> 5, d0 = (tid & 31) * 4;
+    // ---- combine the waves: thread -> head h, kDpt dims (2^-inf = 0 drops an empty wave)
+    constexpr int kDpt = kHeads * kHeadDim / kThreads;
+    static_assert(kDpt % 4 == 0, "whole float4s per thread");
+    const int h = tid / (kHeadDim / kDpt), d0 = (tid % (kHeadDim / kDpt)) * kDpt;
     float mw[kWaves], lw[kWaves];
-    float4 ow[kWaves];
+    float4 ow[kWaves][kDpt / 4];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
         mw[w] = sh.m[w][h];
         lw[w] = sh.l[w][h];
-        ow[w] = *reinterpret_cast<const float4*>(&sh.u.obuf[w][h][d0]);
+#pragma unroll
+        for (int v = 0; v < kDpt / 4; ++v)
+            ow[w][v] = *reinterpret_cast<const float4*>(&sh.u.obuf[w][h][d0 + 4 * v]);
     }
     float M = -__builtin_inff();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
-    float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f, acc[kDpt];
+#pragma unroll
+    for (int i = 0; i < kDpt; ++i) acc[i] = 0.f;
     if (M != -__builtin_inff()) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float f = __builtin_amdgcn_exp2f(mw[w] - M);
             L = fmaf(lw[w], f, L);
-            acc[0] = fmaf(ow[w].x, f, acc[0]);
-            acc[1] = fmaf(ow[w].y, f, acc[1]);
-            acc[2] = fmaf(ow[w].z, f, acc[2]);
-            acc[3] = fmaf(ow[w].w, f, acc[3]);
+#pragma unroll
+            for (int v = 0; v < kDpt / 4; ++v) {
+                acc[4 * v + 0] = fmaf(ow[w][v].x, f, acc[4 * v + 0]);
+                acc[4 * v + 1] = fmaf(ow[w][v].y, f, acc[4 * v + 1]);
+                acc[4 * v + 2] = fmaf(ow[w][v].z, f, acc[4 * v + 2]);
+                acc[4 * v + 3] = fmaf(ow[w][v].w, f, acc[4 * v + 3]);
+            }
         }
     }
     uint16_t* orow = out + ((int64_t)qi * kHeads + h) * kHeadDim + d0;
+    auto store_out = [&](const float* a, float inv) {
+#pragma unroll
+        for (int v = 0; v < kDpt / 4; ++v)
+            *reinterpret_cast<uint2*>(orow + 4 * v) =
+                make_uint2(pack_bf16x2(a[4 * v] * inv, a[4 * v + 1] * inv),
+                           pack_bf16x2(a[4 * v + 2] * inv, a[4 * v + 3] * inv));
+    };
     if (n_chunk == 1) {  // the whole query in one workgroup
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        *reinterpret_cast<uint2*>(orow) =
-            make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+        store_out(acc, L > 0.f ? 1.f / L : 0.f);
         return;
     }
     const int64_t part0 = (int64_t)qi * n_chunk;
-    *reinterpret_cast<float4*>(ws_o + ((part0 + chunk) * kHeads + h) * kHeadDim + d0) =
-        make_float4(acc[0], acc[1], acc[2], acc[3]);
-    if ((tid & 31) == 0)
+#pragma unroll
+    for (int v = 0; v < kDpt / 4; ++v)
+        *reinterpret_cast<float4*>(ws_o + ((part0 + chunk) * kHeads + h) * kHeadDim + d0 + 4 * v) =
+            make_float4(acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]);
+    if (d0 == 0)
         *reinterpret_cast<float2*>(ws_ml + ((part0 + chunk) * kHeads + h) * 2) = make_float2(M, L);
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
     if (tid == 0) {
@@ -318,41 +334,47 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     if (tid == 0) __threadfence();  // acquire for the whole workgroup
     __syncthreads();
     // ---- the last chunk of the query merges all chunks in order
-    float Mq = -__builtin_inff(), Lq = 0.f, aq[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < n_chunk; j0 += 16) {
-        // all loads of up to 16 chunks are issued before any is used
-        float2 ml[16];
-        float4 ov[16];
+    float Mq = -__builtin_inff(), Lq = 0.f, aq[kDpt];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+    for (int i = 0; i < kDpt; ++i) aq[i] = 0.f;
+    constexpr int kMB = 64 / kDpt;  // chunks per batch: every load of a batch in flight at once
+    for (int j0 = 0; j0 < n_chunk; j0 += kMB) {
+        float2 ml[kMB];
+        float4 ov[kMB][kDpt / 4];
+#pragma unroll
+        for (int u = 0; u < kMB; ++u) {
             const int64_t pj = part0 + j0 + u;
             const bool in = j0 + u < n_chunk;
             ml[u] = in ? *reinterpret_cast<const float2*>(ws_ml + (pj * kHeads + h) * 2)
                        : make_float2(-__builtin_inff(), 0.f);
-            ov[u] = in ? *reinterpret_cast<const float4*>(ws_o + (pj * kHeads + h) * kHeadDim + d0)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int v = 0; v < kDpt / 4; ++v)
+                ov[u][v] = in ? *reinterpret_cast<const float4*>(ws_o + (pj * kHeads + h) * kHeadDim + d0 + 4 * v)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         float Mn = Mq;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) Mn = fmaxf(Mn, ml[u].x);
+        for (int u = 0; u < kMB; ++u) Mn = fmaxf(Mn, ml[u].x);
         if (Mn == -__builtin_inff()) continue;
         const float rs = __builtin_amdgcn_exp2f(Mq - Mn);  // Mq = -inf: 0
         Lq *= rs;
-        aq[0] *= rs; aq[1] *= rs; aq[2] *= rs; aq[3] *= rs;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int i = 0; i < kDpt; ++i) aq[i] *= rs;
+#pragma unroll
+        for (int u = 0; u < kMB; ++u) {
             const float f = __builtin_amdgcn_exp2f(ml[u].x - Mn);  // an empty chunk: 0
             Lq = fmaf(ml[u].y, f, Lq);
-            aq[0] = fmaf(ov[u].x, f, aq[0]);
-            aq[1] = fmaf(ov[u].y, f, aq[1]);
-            aq[2] = fmaf(ov[u].z, f, aq[2]);
-            aq[3] = fmaf(ov[u].w, f, aq[3]);
+#pragma unroll
+            for (int v = 0; v < kDpt / 4; ++v) {
+                aq[4 * v + 0] = fmaf(ov[u][v].x, f, aq[4 * v + 0]);
+                aq[4 * v + 1] = fmaf(ov[u][v].y, f, aq[4 * v + 1]);
+                aq[4 * v + 2] = fmaf(ov[u][v].z, f, aq[4 * v + 2]);
+                aq[4 * v + 3] = fmaf(ov[u][v].w, f, aq[4 * v + 3]);
+            }
         }
         Mq = Mn;
     }
-    const float inv = Lq > 0.f ? 1.f / Lq : 0.f;
-    *reinterpret_cast<uint2*>(orow) =
-        make_uint2(pack_bf16x2(aq[0] * inv, aq[1] * inv), pack_bf16x2(aq[2] * inv, aq[3] * inv));
+    store_out(aq, Lq > 0.f ? 1.f / Lq : 0.f);
     if (tid == 0) ctr[qi] = 0u;  // ready for the next call
 }
 
