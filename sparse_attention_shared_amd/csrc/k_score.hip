@@ -142,11 +142,11 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__
 // Candidate scoring fused with the selection among the candidates, for the
 // Reindex layers (rescore the Full layer's pool with the layer's own indexer
 // query and keep the top k, "What Full, Reindex, and Reuse Share", Fig. 5).
-// grid: (ceil(n_cand / 256), nq).  Every workgroup scores 256 candidates into
+// grid: (ceil(n_cand / kSelNT), nq).  Every workgroup scores kSelNT candidates into
 // `scores`; the last one of a query to finish (per-query counter `ctr`, reset
 // on exit) selects the top k of all n_cand <= kSelMaxCand candidates in LDS.
 constexpr int kSelMaxCand = 16384;
-constexpr int kSelNT = 512;
+constexpr int kSelNT = 1024;
 
 __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restrict__ k_idx,
                                                          int32_t n_seq, int64_t t_cap,
