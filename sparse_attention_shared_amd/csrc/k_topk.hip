@@ -30,7 +30,7 @@ namespace csa2 {
 
 constexpr int kSmallNT = 1024;
 constexpr int kSmallMax = 32768;  // slots kept in LDS by the one-workgroup path
-constexpr int kLongNT = 512;
+constexpr int kLongNT = 1024;
 constexpr int kChunk = 8192;      // slots per workgroup on the long path
 constexpr int kCandCap = 4096;    // candidates per row and target
 constexpr int kMaxTargets = 2;
@@ -257,10 +257,11 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
     // Every load it needs is issued first: both targets' candidate lists
     // (whole buffers: slots past the count are read but not used) and the
     // per-chunk counts of keys above the bucket.
-    static_assert(kCandCap == 8 * kLongNT, "eight candidates per thread");
+    constexpr int kCpt = kCandCap / kLongNT;  // candidates per thread
+    static_assert(kCandCap == kCpt * kLongNT, "whole candidates per thread");
     const int cper = (nc + kLongNT - 1) / kLongNT;  // nc <= 2048 chunks: at most 4
     const int cc0 = min(nc, tid * cper), cc1 = min(nc, cc0 + cper);
-    Cand cpre[kMaxTargets][8];
+    Cand cpre[kMaxTargets][kCpt];
     int gpre[kMaxTargets][4];
     uint32_t mpre[kMaxTargets];
 #pragma unroll
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
         const Cand* cb = ws.cand + ((int64_t)row * kMaxTargets + t) * kCandCap;
         const ChunkRec* rec = ws.rec + ((int64_t)row * kMaxTargets + t) * nc;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) cpre[t][u] = t < nt ? cb[tid + u * kLongNT] : Cand{0u, 0};
+        for (int u = 0; u < kCpt; ++u) cpre[t][u] = t < nt ? cb[tid + u * kLongNT] : Cand{0u, 0};
 #pragma unroll
         for (int u = 0; u < 4; ++u) gpre[t][u] = (t < nt && cc0 + u < cc1) ? rec[cc0 + u].gt : 0;
     }
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
             need = 0;
         } else if (m <= (uint32_t)kCandCap) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < kCpt; ++u) {
                 const int i = tid + u * kLongNT;
                 if (i < (int)m) {
                     ckeys[i] = cpre[t][u].key;
