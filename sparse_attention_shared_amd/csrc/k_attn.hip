@@ -13,11 +13,15 @@
 // bf16 (every scale a 32-channel block can carry keeps the result in range),
 // so both products take plain bf16 operands.
 //
-// Work split: a wave takes 32 entries, a workgroup 8 waves (256 entries).  A
-// query with more entries is cut into chunks, one workgroup each; every chunk
-// writes its partial (max, sum, unnormalised O per head) to the workspace and
-// the last chunk to finish (a per-query counter) combines all of them in chunk
-// order, so results do not depend on scheduling.
+// Work split (few queries): a workgroup of 8 waves takes 256 entries.  Each
+// wave loads, dequantises and scores 32 of them (S and its V^T tile); the
+// softmax uses the workgroup's maximum per head, and P^T goes through LDS so
+// that each wave forms O for 16 of the 128 dims over all 256 entries -- no
+// wave ever holds a full 16 x 128 O that would have to be summed across waves.
+// A query with more entries is cut into chunks, one workgroup each; every
+// chunk writes its partial (max, sum, unnormalised O per head) to the
+// workspace and the last chunk to finish (a per-query counter) combines all
+// of them in chunk order, so results do not depend on scheduling.
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
 
@@ -87,10 +91,8 @@ struct RowRaw {  // the FP4 data one lane loads for one entry
 };
 
 struct AttnLds {
-    struct {  // not aliased: a wave stores its O as soon as its own products are done
-        uint32_t vt[kWaves][kVtWave];
-        float obuf[kWaves][kHeads][kHeadDim + 4];
-    } u;
+    uint32_t vt[kWaves][kVtWave];  // V^T of each wave's 32 entries
+    uint4 p[kWaves][64];           // P^T fragments (bf16) of each wave's 32 entries
     float m[kWaves][kHeads];
     float l[kWaves][kHeads];
     int last;
@@ -98,7 +100,8 @@ struct AttnLds {
 
 // grid: (n_chunk, nq), kThreads threads.  Wave w of chunk c takes entries
 // 256 c + 32 w .. + 32: lane row n16 loads entries 2 n16 and 2 n16 + 1 (MFMA
-// tiles 0 and 1), lane group g dims 32 g .. + 32 of K and of V.
+// tiles 0 and 1), lane group g dims 32 g .. + 32 of K and of V.  After the
+// second barrier wave w forms dims 16 w .. + 16 of O for the whole chunk.
 __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint16_t* __restrict__ q,
                                                          const int32_t* __restrict__ q_pos,
                                                          const int32_t* __restrict__ q_seq,
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     const int qi = blockIdx.y, chunk = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n16 = lane & 15, g = lane >> 4;
-    uint32_t* vt = sh.u.vt[wave];
+    uint32_t* vt = sh.vt[wave];
     const float NEG = -__builtin_inff();
 
     const int32_t seq = q_seq ? q_seq[qi] : qi;
@@ -232,11 +235,18 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[u][r] = ((vm >> (4 * g + r)) & 1) ? z[r] * zs : NEG;
     }
+    // ---- softmax over the workgroup's 256 entries: wave maxima -> LDS, then
+    // every wave takes the workgroup maximum per head
     float m = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
-    const float m_use = m == NEG ? 0.f : m;  // an empty wave: every p is 0
+    if (g == 0) sh.m[wave][n16] = m;
+    __syncthreads();  // every wave's maxima and V^T tile are in LDS
+    float M = NEG;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.m[w][n16]);
+    const float m_use = M == NEG ? 0.f : M;  // no valid entry: every p is 0
     float p[2][4];
     float lsum = 0.f;
 #pragma unroll
@@ -248,92 +258,52 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
         }
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
-    if (g == 0) {
-        sh.m[wave][n16] = m;
-        sh.l[wave][n16] = lsum;
-    }
-    // ---- O^T = V^T P^T: A = V^T (dim n16, slots 8 g + j), B = P^T (slots, head n16);
-    // lane holds head n16, dims 16 t8 + 4 g + r
-    const bf16x8_t pf = as_bf16x8(__builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][0], (__bf16)p[1][0]}),
+    if (g == 0) sh.l[wave][n16] = lsum;
+    // P^T as the B operand of O^T (slots 8 g + j, head n16): the lane's own
+    // slots, so the fragment is built in registers and shared through LDS
+    sh.p[wave][lane] = make_uint4(__builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][0], (__bf16)p[1][0]}),
                                   __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][1], (__bf16)p[1][1]}),
                                   __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][2], (__bf16)p[1][2]}),
                                   __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][3], (__bf16)p[1][3]}));
-    f32x4_t o[8];
-#pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8) {
-        const uint4 vv = *reinterpret_cast<const uint4*>(&vt[vt_addr(16 * t8 + n16) + 4 * g]);
-        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv.x, vv.y, vv.z, vv.w), pf, z, 0, 0, 0);
-    }
-#pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8)
-        *reinterpret_cast<float4*>(&sh.u.obuf[wave][n16][16 * t8 + 4 * g]) =
-            make_float4(o[t8][0], o[t8][1], o[t8][2], o[t8][3]);
     __syncthreads();
 
-    // ---- combine the waves: thread -> head h, kDpt dims (2^-inf = 0 drops an empty wave)
-    constexpr int kDpt = kHeads * kHeadDim / kThreads;
-    static_assert(kDpt % 4 == 0, "whole float4s per thread");
-    const int h = tid / (kHeadDim / kDpt), d0 = (tid % (kHeadDim / kDpt)) * kDpt;
-    float mw[kWaves], lw[kWaves];
-    float4 ow[kWaves][kDpt / 4];
+    // ---- O^T for dims 16 wave .. + 16 over all 256 entries: A = V^T (dim
+    // 16 wave + n16, slots 8 g + j of wave block b), B = P^T of block b; the
+    // lane ends with head n16, dims 16 wave + 4 g + r
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        mw[w] = sh.m[w][h];
-        lw[w] = sh.l[w][h];
-#pragma unroll
-        for (int v = 0; v < kDpt / 4; ++v)
-            ow[w][v] = *reinterpret_cast<const float4*>(&sh.u.obuf[w][h][d0 + 4 * v]);
+    for (int b = 0; b < kWaves; ++b) {
+        const uint4 vv = *reinterpret_cast<const uint4*>(&sh.vt[b][vt_addr(16 * wave + n16) + 4 * g]);
+        const uint4 pb = sh.p[b][lane];
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv.x, vv.y, vv.z, vv.w),
+                                                    as_bf16x8(pb.x, pb.y, pb.z, pb.w), o, 0, 0, 0);
     }
-    float M = -__builtin_inff();
+    float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
-    float L = 0.f, acc[kDpt];
-#pragma unroll
-    for (int i = 0; i < kDpt; ++i) acc[i] = 0.f;
-    if (M != -__builtin_inff()) {
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = __builtin_amdgcn_exp2f(mw[w] - M);
-            L = fmaf(lw[w], f, L);
-#pragma unroll
-            for (int v = 0; v < kDpt / 4; ++v) {
-                acc[4 * v + 0] = fmaf(ow[w][v].x, f, acc[4 * v + 0]);
-                acc[4 * v + 1] = fmaf(ow[w][v].y, f, acc[4 * v + 1]);
-                acc[4 * v + 2] = fmaf(ow[w][v].z, f, acc[4 * v + 2]);
-                acc[4 * v + 3] = fmaf(ow[w][v].w, f, acc[4 * v + 3]);
-            }
-        }
-    }
-    uint16_t* orow = out + ((int64_t)qi * kHeads + h) * kHeadDim + d0;
-    auto store_out = [&](const float* a, float inv) {
-#pragma unroll
-        for (int v = 0; v < kDpt / 4; ++v)
-            *reinterpret_cast<uint2*>(orow + 4 * v) =
-                make_uint2(pack_bf16x2(a[4 * v] * inv, a[4 * v + 1] * inv),
-                           pack_bf16x2(a[4 * v + 2] * inv, a[4 * v + 3] * inv));
-    };
+    for (int w = 0; w < kWaves; ++w) L += sh.l[w][n16];
+    const int dq = 16 * wave + 4 * g;
     if (n_chunk == 1) {  // the whole query in one workgroup
-        store_out(acc, L > 0.f ? 1.f / L : 0.f);
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        *reinterpret_cast<uint2*>(out + ((int64_t)qi * kHeads + n16) * kHeadDim + dq) =
+            make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
         return;
     }
     const int64_t part0 = (int64_t)qi * n_chunk;
-#pragma unroll
-    for (int v = 0; v < kDpt / 4; ++v)
-        *reinterpret_cast<float4*>(ws_o + ((part0 + chunk) * kHeads + h) * kHeadDim + d0 + 4 * v) =
-            make_float4(acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]);
-    if (d0 == 0)
-        *reinterpret_cast<float2*>(ws_ml + ((part0 + chunk) * kHeads + h) * 2) = make_float2(M, L);
+    *reinterpret_cast<float4*>(ws_o + ((part0 + chunk) * kHeads + n16) * kHeadDim + dq) =
+        make_float4(o[0], o[1], o[2], o[3]);
+    if (wave == 0 && g == 0)
+        *reinterpret_cast<float2*>(ws_ml + ((part0 + chunk) * kHeads + n16) * 2) = make_float2(M, L);
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (tid == 0) {
-        __threadfence();
-        sh.last = atomicAdd(&ctr[qi], 1u) == (uint32_t)(n_chunk - 1);
-    }
+    if (tid == 0)  // release this chunk's partial; the last chunk also acquires all others
+        sh.last = __hip_atomic_fetch_add(&ctr[qi], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (uint32_t)(n_chunk - 1);
     __syncthreads();
     if (!sh.last) return;
-    if (tid == 0) __threadfence();  // acquire for the whole workgroup
-    __syncthreads();
-    // ---- the last chunk of the query merges all chunks in order
+    // ---- the last chunk of the query merges all chunks in order: thread ->
+    // head h, kDpt dims
+    constexpr int kDpt = kHeads * kHeadDim / kThreads;
+    static_assert(kDpt % 4 == 0, "whole float4s per thread");
+    const int h = tid / (kHeadDim / kDpt), d0 = (tid % (kHeadDim / kDpt)) * kDpt;
     float Mq = -__builtin_inff(), Lq = 0.f, aq[kDpt];
 #pragma unroll
     for (int i = 0; i < kDpt; ++i) aq[i] = 0.f;
@@ -374,7 +344,12 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
         }
         Mq = Mn;
     }
-    store_out(aq, Lq > 0.f ? 1.f / Lq : 0.f);
+    const float inv = Lq > 0.f ? 1.f / Lq : 0.f;
+    uint16_t* orow = out + ((int64_t)qi * kHeads + h) * kHeadDim + d0;
+#pragma unroll
+    for (int v = 0; v < kDpt / 4; ++v)
+        *reinterpret_cast<uint2*>(orow + 4 * v) = make_uint2(pack_bf16x2(aq[4 * v] * inv, aq[4 * v + 1] * inv),
+                                                             pack_bf16x2(aq[4 * v + 2] * inv, aq[4 * v + 3] * inv));
     if (tid == 0) ctr[qi] = 0u;  // ready for the next call
 }
 
