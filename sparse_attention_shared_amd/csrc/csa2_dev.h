@@ -98,6 +98,16 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
     return r;
 }
 
+// Last-arrival counter of a group of n workgroups, called by thread 0 after a
+// barrier that follows the workgroup's stores.  The agent-scope acquire-release
+// add publishes those stores (one L2 write-back on the way in) and, for the
+// arrival that returns true, makes every other member's visible (one L2
+// invalidate on the way out); a barrier after the call extends that to the
+// whole workgroup.  The counter is reset by the last arrival's owner.
+__device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t n) {
+    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+}
+
 // XCD-aware remap of a flat workgroup id: the hardware deals consecutive ids
 // round-robin over the 8 XCDs; this makes each XCD own a contiguous range of
 // logical ids, so neighbouring tiles share an L2.  `n` is the grid size.

@@ -294,10 +294,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     if (wave == 0 && g == 0)
         *reinterpret_cast<float2*>(ws_ml + ((part0 + chunk) * kHeads + n16) * 2) = make_float2(M, L);
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (tid == 0)  // release this chunk's partial; the last chunk also acquires all others
-        sh.last = __hip_atomic_fetch_add(&ctr[qi], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-                  (uint32_t)(n_chunk - 1);
-    __syncthreads();
+    if (tid == 0) sh.last = arrive_last(&ctr[qi], (uint32_t)n_chunk);
+    __syncthreads();  // thread 0's acquire covers the workgroup
     if (!sh.last) return;
     // ---- the last chunk of the query merges all chunks in order: thread ->
     // head h, kDpt dims

@@ -193,14 +193,9 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
         if (c < n_cand) srow[c] = my;
     }
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (threadIdx.x == 0) {
-        __threadfence();
-        last = atomicAdd(&ctr[qi], 1u) == gridDim.x - 1;
-    }
-    __syncthreads();
+    if (threadIdx.x == 0) last = arrive_last(&ctr[qi], gridDim.x);
+    __syncthreads();  // thread 0's acquire covers the workgroup
     if (!last) return;
-    if (threadIdx.x == 0) __threadfence();  // acquire for the whole workgroup
-    __syncthreads();
     reg_select<kSelNT, kSelMaxCand / kSelNT, true>(srow, crow, (int)n_cand, k,
                                                    sel + (int64_t)qi * k, sh);
     if (threadIdx.x == 0) ctr[qi] = 0u;

@@ -113,14 +113,9 @@ __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__
         if (v) atomicAdd(&st->hist[i], (uint32_t)v);
     }
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (tid == 0) {
-        __threadfence();
-        last = atomicAdd(&st->ctr_hist, 1u) == (uint32_t)(nc - 1);
-    }
-    __syncthreads();
+    if (tid == 0) last = arrive_last(&st->ctr_hist, (uint32_t)nc);
+    __syncthreads();  // thread 0's acquire covers the workgroup
     if (!last) return;
-    if (tid == 0) __threadfence();  // acquire for the whole workgroup
-    __syncthreads();
     // the last workgroup of the row: boundary bucket of each target
     {
         constexpr int kB = kHistBins / kLongNT;
@@ -245,14 +240,9 @@ __global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__
     }
     if (tid < nt) ws.rec[((int64_t)row * kMaxTargets + tid) * nc + c].gt = cnt_gt[tid];
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (tid == 0) {
-        __threadfence();
-        last = atomicAdd(&st->ctr_cand, 1u) == (uint32_t)(nc - 1);
-    }
-    __syncthreads();
+    if (tid == 0) last = arrive_last(&st->ctr_cand, (uint32_t)nc);
+    __syncthreads();  // thread 0's acquire covers the workgroup
     if (!last) return;
-    if (tid == 0) __threadfence();  // acquire for the whole workgroup
-    __syncthreads();
     // ---- last workgroup of the row: exact (tau, need) and chunk offsets.
     // Every load it needs is issued first: both targets' candidate lists
     // (whole buffers: slots past the count are read but not used) and the
