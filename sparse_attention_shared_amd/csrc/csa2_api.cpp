@@ -112,7 +112,7 @@ StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, i
     w.pscores = take((size_t)n_seq * (pool > 0 ? pool : 1) * sizeof(float));
     w.pool = take((size_t)n_seq * (pool > 0 ? pool : 1) * sizeof(int32_t));
     w.sel0 = take((size_t)n_seq * k * sizeof(int32_t));
-    w.ctr = take((size_t)n_seq * sizeof(uint32_t));
+    w.ctr = take((size_t)n_seq * kCtrStride * sizeof(uint32_t));
     size_t tk = topk_ws_bytes(n_seq, t_cap, k, pool);
     if (block > 1) tk = std::max(tk, topk_ws_bytes(n_seq, nb, nbsel, 0));
     if (pool > 0) tk = std::max(tk, topk_ws_bytes(n_seq, pool, k, 0));

@@ -55,7 +55,7 @@ hipError_t launch_prefill_topk(const CacheView& c, int32_t seq, const uint16_t* 
                                hipStream_t s);
 
 // Candidate scores + top-k among them in one launch (n_cand <= 16384); `ctr`
-// is nq counters that must be zero and are left zero.
+// holds nq counters kCtrStride words apart that must be zero and are left zero.
 hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
                                const int32_t* q_seq, int32_t nq, const int32_t* cand,
                                int64_t n_cand, float* scores, uint32_t* ctr, int32_t k,
@@ -72,6 +72,10 @@ hipError_t launch_expand_blocks(const int32_t* blocks, int32_t nq, int32_t nb, i
 // From this many queries on, attention runs one workgroup per query (no
 // workspace); below it, each query is split over several workgroups.
 constexpr int32_t kManyQueries = 256;
+
+// Per-query arrival counters sit 256 bytes apart, so the workgroups of
+// different queries never contend for one cache line.
+constexpr int64_t kCtrStride = 64;
 size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window);
 hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
                               const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,

@@ -13,15 +13,18 @@
 // bf16 (every scale a 32-channel block can carry keeps the result in range),
 // so both products take plain bf16 operands.
 //
-// Work split (few queries): a workgroup of 8 waves takes 256 entries.  Each
-// wave loads, dequantises and scores 32 of them (S and its V^T tile); the
-// softmax uses the workgroup's maximum per head, and P^T goes through LDS so
-// that each wave forms O for 16 of the 128 dims over all 256 entries -- no
-// wave ever holds a full 16 x 128 O that would have to be summed across waves.
-// A query with more entries is cut into chunks, one workgroup each; every
-// chunk writes its partial (max, sum, unnormalised O per head) to the
-// workspace and the last chunk to finish (a per-query counter) combines all
-// of them in chunk order, so results do not depend on scheduling.
+// Work split (few queries): a query's selected entries are cut into chunks of
+// 256 and its window entries spread evenly over the same chunks (at most 32
+// each), one workgroup per chunk: 8 waves on 32 selected entries each plus a
+// ninth on the chunk's window entries.  Each wave loads, dequantises and
+// scores its entries (S and its V^T tile); the softmax uses the workgroup's
+// maximum per head, and P^T goes through LDS so that each of the 8 selection
+// waves forms O for 16 of the 128 dims over all of the chunk's entries -- no
+// wave ever holds a full 16 x 128 O that would have to be summed across
+// waves.  Every chunk writes its partial (max, sum, unnormalised O per head)
+// to the workspace and the last chunk to finish (a per-query counter)
+// combines all of them in chunk order, so results do not depend on
+// scheduling.
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
 
@@ -30,10 +33,11 @@ namespace csa2 {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
-constexpr int kWaves = 8;
+constexpr int kSelWaves = 8;                  // waves on selected entries
+constexpr int kWaves = kSelWaves + 1;         // + one wave on the chunk's window entries
 constexpr int kThreads = kWaves * 64;
-constexpr int kBlk = 32;                  // entries per wave
-constexpr int kWgEntries = kWaves * kBlk;  // entries per workgroup
+constexpr int kBlk = 32;                      // entries per wave
+constexpr int kWgEntries = kSelWaves * kBlk;  // selected entries per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -98,10 +102,12 @@ struct AttnLds {
     int last;
 };
 
-// grid: (n_chunk, nq), kThreads threads.  Wave w of chunk c takes entries
-// 256 c + 32 w .. + 32: lane row n16 loads entries 2 n16 and 2 n16 + 1 (MFMA
-// tiles 0 and 1), lane group g dims 32 g .. + 32 of K and of V.  After the
-// second barrier wave w forms dims 16 w .. + 16 of O for the whole chunk.
+// grid: (n_chunk, nq), kThreads threads, n_chunk >= ceil(window / 32).  Wave
+// w < 8 of chunk c takes selected entries 256 c + 32 w .. + 32, wave 8 window
+// entries wpc c .. + wpc (wpc = ceil(window / n_chunk) <= 32): lane row n16
+// loads entries 2 n16 and 2 n16 + 1 of the wave's block (MFMA tiles 0 and 1),
+// lane group g dims 32 g .. + 32 of K and of V.  After the second barrier
+// wave w < 8 forms dims 16 w .. + 16 of O for the whole chunk.
 __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint16_t* __restrict__ q,
                                                          const int32_t* __restrict__ q_pos,
                                                          const int32_t* __restrict__ q_seq,
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     __shared__ AttnLds sh;
 
     const int qi = blockIdx.y, chunk = blockIdx.x;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n16 = lane & 15, g = lane >> 4;
     uint32_t* vt = sh.vt[wave];
     const float NEG = -__builtin_inff();
@@ -133,18 +139,25 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     int64_t row[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int64_t e = (int64_t)chunk * kWgEntries + wave * kBlk + 2 * n16 + u;
         kind[u] = 0;
         row[u] = 0;
-        if (e < k) {
-            const int64_t j = sel[(int64_t)qi * k + e];
-            if (j >= 0 && j <= t) {
-                kind[u] = c.fp4 ? 1 : 2;
-                row[u] = (int64_t)seq * c.t_cap + j;
+        if (wave < kSelWaves) {
+            const int64_t e = (int64_t)chunk * kWgEntries + wave * kBlk + 2 * n16 + u;
+            if (e < k) {
+                const int64_t j = sel[(int64_t)qi * k + e];
+                if (j >= 0 && j <= t) {
+                    kind[u] = c.fp4 ? 1 : 2;
+                    row[u] = (int64_t)seq * c.t_cap + j;
+                }
             }
-        } else if (e - k < nw) {
-            kind[u] = 3;
-            row[u] = (int64_t)seq * loc.cap + (w0 + (e - k)) % loc.cap;
+        } else {
+            const int wpc = (loc.window + n_chunk - 1) / n_chunk;
+            const int sl = 2 * n16 + u;
+            const int64_t ew = (int64_t)chunk * wpc + sl;
+            if (sl < wpc && ew < nw) {
+                kind[u] = 3;
+                row[u] = (int64_t)seq * loc.cap + (w0 + ew) % loc.cap;
+            }
         }
     }
     // Q^T as the B operand of S: head n16, dims 32 g + 8 kb .. + 8 at step kb
@@ -270,36 +283,40 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     // ---- O^T for dims 16 wave .. + 16 over all 256 entries: A = V^T (dim
     // 16 wave + n16, slots 8 g + j of wave block b), B = P^T of block b; the
     // lane ends with head n16, dims 16 wave + 4 g + r
-    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int b = 0; b < kWaves; ++b) {
-        const uint4 vv = *reinterpret_cast<const uint4*>(&sh.vt[b][vt_addr(16 * wave + n16) + 4 * g]);
-        const uint4 pb = sh.p[b][lane];
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv.x, vv.y, vv.z, vv.w),
-                                                    as_bf16x8(pb.x, pb.y, pb.z, pb.w), o, 0, 0, 0);
-    }
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) L += sh.l[w][n16];
-    const int dq = 16 * wave + 4 * g;
-    if (n_chunk == 1) {  // the whole query in one workgroup
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        *reinterpret_cast<uint2*>(out + ((int64_t)qi * kHeads + n16) * kHeadDim + dq) =
-            make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
-        return;
-    }
     const int64_t part0 = (int64_t)qi * n_chunk;
-    *reinterpret_cast<float4*>(ws_o + ((part0 + chunk) * kHeads + n16) * kHeadDim + dq) =
-        make_float4(o[0], o[1], o[2], o[3]);
-    if (wave == 0 && g == 0)
-        *reinterpret_cast<float2*>(ws_ml + ((part0 + chunk) * kHeads + n16) * 2) = make_float2(M, L);
+    if (wave < kSelWaves) {  // the window wave has no dims of O
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < kWaves; ++b) {
+            const uint4 vv = *reinterpret_cast<const uint4*>(&sh.vt[b][vt_addr(16 * wave + n16) + 4 * g]);
+            const uint4 pb = sh.p[b][lane];
+            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv.x, vv.y, vv.z, vv.w),
+                                                        as_bf16x8(pb.x, pb.y, pb.z, pb.w), o, 0, 0, 0);
+        }
+        const int dq = 16 * wave + 4 * g;
+        if (n_chunk == 1) {  // the whole query in one workgroup
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            *reinterpret_cast<uint2*>(out + ((int64_t)qi * kHeads + n16) * kHeadDim + dq) =
+                make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+        } else {
+            *reinterpret_cast<float4*>(ws_o + ((part0 + chunk) * kHeads + n16) * kHeadDim + dq) =
+                make_float4(o[0], o[1], o[2], o[3]);
+            if (wave == 0 && g == 0)
+                *reinterpret_cast<float2*>(ws_ml + ((part0 + chunk) * kHeads + n16) * 2) = make_float2(M, L);
+        }
+    }
+    if (n_chunk == 1) return;
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (tid == 0) sh.last = arrive_last(&ctr[qi], (uint32_t)n_chunk);
+    if (tid == 0) sh.last = arrive_last(&ctr[qi * kCtrStride], (uint32_t)n_chunk);
     __syncthreads();  // thread 0's acquire covers the workgroup
-    if (!sh.last) return;
-    // ---- the last chunk of the query merges all chunks in order: thread ->
-    // head h, kDpt dims
-    constexpr int kDpt = kHeads * kHeadDim / kThreads;
+    if (!sh.last || wave >= kSelWaves) return;
+    // ---- the last chunk of the query merges all chunks in order: thread of
+    // the 8 selection waves -> head h, kDpt dims
+    constexpr int kMergeThreads = kSelWaves * 64;
+    constexpr int kDpt = kHeads * kHeadDim / kMergeThreads;
     static_assert(kDpt % 4 == 0, "whole float4s per thread");
     const int h = tid / (kHeadDim / kDpt), d0 = (tid % (kHeadDim / kDpt)) * kDpt;
     float Mq = -__builtin_inff(), Lq = 0.f, aq[kDpt];
@@ -348,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     for (int v = 0; v < kDpt / 4; ++v)
         *reinterpret_cast<uint2*>(orow + 4 * v) = make_uint2(pack_bf16x2(aq[4 * v] * inv, aq[4 * v + 1] * inv),
                                                              pack_bf16x2(aq[4 * v + 2] * inv, aq[4 * v + 3] * inv));
-    if (tid == 0) ctr[qi] = 0u;  // ready for the next call
+    if (tid == 0) ctr[qi * kCtrStride] = 0u;  // ready for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -686,14 +703,16 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                    pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
 }
 
+// Chunks of a query: 256 selected entries each, and enough of them that the
+// window spreads at most 32 entries over each.
 static int32_t attn_chunks(int32_t k, int32_t window) {
-    return (k + window + kWgEntries - 1) / kWgEntries;
+    return std::max(std::max((k + kWgEntries - 1) / kWgEntries, (window + kBlk - 1) / kBlk), 1);
 }
 
 size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window) {
     const int64_t nc = attn_chunks(k, window);
     if (nc <= 1 || nq >= kManyQueries) return 0;
-    return (size_t)nq * nc * kHeads * (kHeadDim + 2) * sizeof(float) + (size_t)nq * sizeof(uint32_t);
+    return (size_t)nq * nc * kHeads * (kHeadDim + 2) * sizeof(float) + (size_t)nq * kCtrStride * sizeof(uint32_t);
 }
 
 hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32_t* q_pos,

@@ -193,12 +193,12 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
         if (c < n_cand) srow[c] = my;
     }
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (threadIdx.x == 0) last = arrive_last(&ctr[qi], gridDim.x);
+    if (threadIdx.x == 0) last = arrive_last(&ctr[qi * kCtrStride], gridDim.x);
     __syncthreads();  // thread 0's acquire covers the workgroup
     if (!last) return;
     reg_select<kSelNT, kSelMaxCand / kSelNT, true>(srow, crow, (int)n_cand, k,
                                                    sel + (int64_t)qi * k, sh);
-    if (threadIdx.x == 0) ctr[qi] = 0u;
+    if (threadIdx.x == 0) ctr[qi * kCtrStride] = 0u;
 }
 
 hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,

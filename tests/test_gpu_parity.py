@@ -153,7 +153,8 @@ def test_topk_through_ascending_ids_with_empty_slots():
 # ------------------------------------------------------------ attention
 
 @pytest.mark.parametrize("kv,window,lo,cap", [("fp4", 40, 0, 64), ("bf16", 40, 0, 64),
-                                              ("fp4", 0, 0, 64), ("fp4", 64, 4090, 64)])
+                                              ("fp4", 0, 0, 64), ("fp4", 64, 4090, 64),
+                                              ("fp4", 200, 0, 256)])  # window over 7 chunks
 def test_sparse_attn_on_oracle_selection(kv, window, lo, cap):
     sp = _ragged_spec(kv=kv, window=window, lo=lo, local_cap=cap)
     x = synth.make_inputs(sp)
