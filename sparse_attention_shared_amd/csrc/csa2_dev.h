@@ -98,6 +98,15 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
     return r;
 }
 
+// Workgroup barrier that orders LDS only: unlike __syncthreads it does not
+// wait for the caller's global loads, so loads issued before it stay in
+// flight.  For barriers that publish LDS data alone.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Last-arrival counter of a group of n workgroups, called by thread 0 after a
 // barrier that follows the workgroup's stores.  The agent-scope acquire-release
 // add publishes those stores (one L2 write-back on the way in) and, for the

@@ -379,6 +379,129 @@ __device__ void reg_select(const float* s, const int32_t* ids, int n, int kk, in
     for (int i = chosen + tid; i < kk; i += NT) dst[i] = -1;
 }
 
+// LDS of wave_select.
+template <int NT>
+struct WaveSelShared {
+    alignas(16) int hist[kHistWords];
+    int wcnt[2 * (NT / 64)];
+    int res[4];
+};
+
+// Top-kk of one row of n <= NT * PER scores by one workgroup, keys in
+// registers, slot i written as ids[i].  Wave w owns slots [64 PER w,
+// 64 PER (w + 1)); lane l holds slots 64 PER w + 64 j + l, so every wave has
+// keys when n is near NT * PER and a wave's slots ascend in (j, l).  Scores of
+// slots that can never be chosen must be -inf (key 0).
+//  1. loads: scores, then ids (only the write needs them: the barriers below
+//     order LDS alone, so the id loads stay in flight until then);
+//  2. a 12-bit histogram of the top digit finds the boundary bucket, and
+//     12- then 8-bit histograms of the register keys inside it resolve the
+//     exact (tau, need), stopping as soon as a whole sub-bucket completes the
+//     selection;
+//  3. per-wave counts and ballots place every chosen slot, ascending.
+// Writes dst[0..kk), -1 padded.
+template <int NT, int PER>
+__device__ void wave_select(const float* s, const int32_t* ids, int n, int kk, int32_t* dst,
+                            WaveSelShared<NT>& sh) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int s0 = w * 64 * PER + lane;
+    float v[PER];
+    int32_t id[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[j] = s[min(s0 + 64 * j, n - 1)];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) id[j] = ids[min(s0 + 64 * j, n - 1)];
+    for (int i = tid; i < kHistWords; i += NT) sh.hist[i] = 0;
+    uint32_t key[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t k = score_key(v[j]);
+        key[j] = (s0 + 64 * j < n && k != kNegInfKey) ? k : 0u;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (key[j]) atomicAdd(&sh.hist[hidx((int)(key[j] >> 20))], 1);
+    lds_barrier();
+    if (w == 0) wave_find_bucket(sh.hist, kHistBins, kk, sh.res);
+    lds_barrier();
+    const int total_valid = sh.res[3];
+    const uint32_t b1 = (uint32_t)sh.res[0];
+    const int rem = kk - sh.res[1], cnt = sh.res[2];
+    uint32_t tau = 0u;  // total_valid <= kk: every valid key (key > 0)
+    int need = 0;
+    if (total_valid > kk && cnt == rem) {
+        tau = (b1 << 20) - 1u;  // the whole boundary bucket is taken
+    } else if (total_valid > kk) {
+        // 12 more bits, then the last 8 unless a whole sub-bucket completes
+        // the selection
+        uint32_t prefix = b1 << 20, mask = 0xFFF00000u;
+        int r = rem;
+        bool done = false;
+        for (int shift = 8; shift >= 0 && !done; shift -= 8) {
+            const int bits = shift ? 12 : 8;
+            const uint32_t dm = (1u << bits) - 1u;
+            for (int i = tid; i < kHistWords; i += NT) sh.hist[i] = 0;
+            lds_barrier();
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+                if (key[j] && (key[j] & mask) == prefix)
+                    atomicAdd(&sh.hist[hidx((int)((key[j] >> shift) & dm))], 1);
+            lds_barrier();
+            if (w == 0) wave_find_bucket(sh.hist, 1 << bits, r, sh.res);
+            lds_barrier();
+            prefix |= (uint32_t)sh.res[0] << shift;
+            mask |= dm << shift;
+            r -= sh.res[1];
+            done = sh.res[2] == r;  // the whole sub-bucket is taken
+            lds_barrier();
+        }
+        if (done) {
+            tau = prefix - 1u;  // every key >= prefix (the remaining bits are free)
+        } else {
+            tau = prefix;
+            need = r;
+        }
+    }
+    // ordered write: per-wave (greater, equal) counts, then ballots per j
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        gt += key[j] > tau;
+        eq += (need > 0) & (key[j] == tau);
+    }
+    gt = wave_sum_dpp(gt);
+    eq = wave_sum_dpp(eq);
+    if (lane == 0) {
+        sh.wcnt[w] = gt;
+        sh.wcnt[NW + w] = eq;
+    }
+    lds_barrier();
+    int eqb = 0, selb = 0, total = 0, eqrun = 0;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+        const int g = sh.wcnt[u], e = sh.wcnt[NW + u];
+        const int take = g + min(max(need - eqrun, 0), e);
+        if (u < w) selb += take;
+        if (u == w) eqb = eqrun;
+        total += take;
+        eqrun += e;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const bool eqf = need > 0 && key[j] == tau;
+        const uint64_t em = __ballot(eqf);
+        const bool take = key[j] > tau || (eqf && eqb + lanes_below(em) < need);
+        const uint64_t sm = __ballot(take);
+        const int pos = selb + lanes_below(sm);
+        if (take && pos < kk) dst[pos] = id[j];
+        eqb += __popcll(em);
+        selb += __popcll(sm);
+    }
+    for (int i = min(total, kk) + tid; i < kk; i += NT) dst[i] = -1;
+}
+
 // Stage the keys of slots [0, n) of a row into LDS; global loads are issued
 // eight per thread before any of them is used.
 template <int NT>

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
                                                          int64_t n_cand, float* __restrict__ scores,
                                                          uint32_t* __restrict__ ctr, int32_t k,
                                                          int32_t* __restrict__ sel) {
-    __shared__ RegSelShared<kSelNT> sh;
+    __shared__ WaveSelShared<kSelNT> sh;
     __shared__ int last;
     const int qi = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -196,8 +196,10 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
     if (threadIdx.x == 0) last = arrive_last(&ctr[qi * kCtrStride], gridDim.x);
     __syncthreads();  // thread 0's acquire covers the workgroup
     if (!last) return;
-    reg_select<kSelNT, kSelMaxCand / kSelNT, true>(srow, crow, (int)n_cand, k,
-                                                   sel + (int64_t)qi * k, sh);
+    if (n_cand <= kSelNT * 8)  // every wave holds keys
+        wave_select<kSelNT, 8>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
+    else
+        wave_select<kSelNT, kSelMaxCand / kSelNT>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
     if (threadIdx.x == 0) ctr[qi * kCtrStride] = 0u;
 }
 

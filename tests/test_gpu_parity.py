@@ -288,6 +288,32 @@ def test_page_schedule_small():
     check_stack(sp, x, d, outs, sels, pool)
 
 
+@pytest.mark.parametrize("distinct", [20, 40, 120])
+def test_reindex_exact_ties(distinct):
+    """Key rows drawn from `distinct` rows, so pool scores tie exactly in
+    groups of ~20000/distinct: the Reindex selection must be the oracle's,
+    lower positions first inside the boundary group.  Small boundary buckets
+    are ranked directly, large ones (20 rows: ~1000 ties) go through the radix
+    refinement."""
+    sp = synth.Spec("reindex-ties", n_seq=2, t_cap=20000, q_pos=[19999, 15000], q_seq=[0, 1],
+                    kv_format="fp4", k=2048, window=16, pool=8192,
+                    schedule=[synth.FULL, synth.REINDEX], local_cap=16, seed=61)
+    x = synth.make_inputs(sp)
+    rng = np.random.default_rng(62 + distinct)
+    rows = x.k_idx[0, :distinct].copy()
+    for b in range(sp.n_seq):
+        x.k_idx[b] = rows[rng.integers(0, distinct, sp.t_cap)]
+    d = DevInputs(x)
+    outs, sels, pool = run_stack(sp, x, d)
+    gpool, g = host(pool), host(sels[1])
+    for b in range(sp.n_seq):
+        gp = gpool[b]
+        assert np.all(gp >= 0)
+        ps = oracle.scores(x.q_idx[1, b], x.k_idx[b, gp])
+        ref = oracle.topk(ps, sp.k, gp)
+        assert np.array_equal(g[b], ref), "b%d: Reindex selection differs from the oracle" % b
+
+
 # ------------------------------------------------------ named workloads
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4])
