@@ -57,8 +57,15 @@ def algorithmic_bytes(schedule, B, T, k, P, W):
     return total * B
 
 
-def src_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def scan_src_hash():
+    """Fingerprint of the scan kernel's source: its part of k_score.hip (the
+    kernel and its helpers) and the shared device header."""
+    src = open(SCAN_KERNEL_SRC).read()
+    a = src.index("constexpr int kScoreTile")
+    b = src.index("// grid: (ceil(n_cand / 256), nq)")
+    h = hashlib.sha256(src[a:b].encode())
+    h.update(open(os.path.join(os.path.dirname(SCAN_KERNEL_SRC), "csa2_dev.h"), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(launch_units):
@@ -68,7 +75,7 @@ def traffic_from_profile(launch_units):
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kernel_src_sha256_16") != src_hash(SCAN_KERNEL_SRC):
+    if d.get("kernel_src_sha256_16") != scan_src_hash():
         return None
     return d.get("hbm_bytes_per_launch")
 

@@ -240,8 +240,11 @@ typedef struct {
     int32_t *const *sel_out;           /* NULL, or [l] -> int32 [n_seq][k] (entries may be NULL) */
     int32_t *pool_out;                 /* NULL, or int32 [n_seq][pool] */
     void *scan_events[2];              /* optional timing hook: two hipEvent_t the caller
-                                          created, recorded on `stream` right before and
-                                          after layer 0's indexer scan kernel; NULL skips */
+                                          created (with timing).  csa2_stack_run stores the
+                                          start and end of layer 0's indexer scan kernel in
+                                          them (the kernel's own times); a plan records them
+                                          on the stream right before and after that kernel.
+                                          NULL skips */
 } csa2_stack_desc;
 
 /* Workspace of csa2_stack_run; like the top-k workspace it must be

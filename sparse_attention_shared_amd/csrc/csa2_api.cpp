@@ -344,27 +344,36 @@ static csa2_status enqueue_stack(const csa2_stack_desc* d, const CacheView& cv, 
         hipError_t e = hipSuccess;
         if (m == CSA2_MODE_FULL || m == CSA2_MODE_REINDEX) {
             int32_t* dst = sel_l ? sel_l : selbuf;
+            // layer 0 is Full: on a stream being recorded into a graph the
+            // events bracket the scan; otherwise they take the kernel's own
+            // start and end times
             const bool timed = l == 0 && d->scan_events[0] && d->scan_events[1];
-            if (timed) e = hipEventRecord((hipEvent_t)d->scan_events[0], s);
+            hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+            if (timed) e = hipStreamIsCapturing(s, &cap);
+            const bool own = timed && e == hipSuccess && cap == hipStreamCaptureStatusNone;
+            hipEvent_t ev0 = own ? (hipEvent_t)d->scan_events[0] : nullptr;
+            hipEvent_t ev1 = own ? (hipEvent_t)d->scan_events[1] : nullptr;
+            const bool around = timed && !own;
+            if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[0], s);
             if (e != hipSuccess) return CSA2_ERR_HIP;
             if (m == CSA2_MODE_FULL && B == 1) {
-                e = launch_score_dense(cv, d->q_idx[l], d->q_pos, q_seq, S, 1, scores, cv.t_cap, s);
-                if (timed && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
+                e = launch_score_dense(cv, d->q_idx[l], d->q_pos, q_seq, S, 1, scores, cv.t_cap, s, ev0,
+                                       ev1);
+                if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
                 if (e == hipSuccess)
                     e = launch_topk(scores, S, cv.t_cap, cv.t_cap, nullptr, k, dst, P, P ? pool : nullptr,
                                     tkws, s);
             } else if (m == CSA2_MODE_FULL) {
                 const int64_t nb = (cv.t_cap + B - 1) / B;
                 const int32_t nbsel = P / B;
-                e = launch_score_dense(cv, d->q_idx[l], d->q_pos, q_seq, S, B, bscores, nb, s);
-                if (timed && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
+                e = launch_score_dense(cv, d->q_idx[l], d->q_pos, q_seq, S, B, bscores, nb, s, ev0, ev1);
+                if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
                 if (e == hipSuccess)
                     e = launch_topk(bscores, S, nb, nb, nullptr, nbsel, blocks, 0, nullptr, tkws, s);
                 if (e == hipSuccess) e = launch_expand_blocks(blocks, S, nbsel, B, d->q_pos, pool, s);
                 if (e == hipSuccess) e = rescore_pool(l, dst);
             } else {
                 e = rescore_pool(l, dst);
-                if (timed && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
             }
             cur = dst;
         } else if (sel_l) {

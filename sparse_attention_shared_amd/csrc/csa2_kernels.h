@@ -30,9 +30,11 @@ hipError_t launch_unpack_fp4(const uint8_t* codes, const uint8_t* scales, int64_
                              hipStream_t s);
 
 // Dense indexer scores: scores[i][b], b < ceil(t_cap / block), block in {1, 64}.
+// With ev0/ev1 set, the kernel's own start and end times are recorded in them.
 hipError_t launch_score_dense(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
                               const int32_t* q_seq, int32_t nq, int32_t block, float* scores,
-                              int64_t ld, hipStream_t s);
+                              int64_t ld, hipStream_t s, hipEvent_t ev0 = nullptr,
+                              hipEvent_t ev1 = nullptr);
 // Candidate scores: scores[i][j] = score of position cand[i][j].
 hipError_t launch_score_cand(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
                              const int32_t* q_seq, int32_t nq, const int32_t* cand, int64_t n_cand,

@@ -9,6 +9,8 @@
 // lanes share one key: each lane loads 16 contiguous bytes, so every load
 // instruction of a wave reads 1 KB of consecutive memory (8 keys), and the
 // eight partial dots are summed with three lane exchanges.
+#include <hip/hip_ext.h>
+
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
 #include "csa2_select.h"
@@ -217,15 +219,15 @@ hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const 
 
 hipError_t launch_score_dense(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
                               const int32_t* q_seq, int32_t nq, int32_t block, float* scores,
-                              int64_t ld, hipStream_t s) {
+                              int64_t ld, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (nq == 0 || c.t_cap == 0) return hipSuccess;
     dim3 grid((uint32_t)((c.t_cap + kScoreTile - 1) / kScoreTile), (uint32_t)nq);
     if (block == 1)
-        hipLaunchKernelGGL(k_score_dense<1>, grid, dim3(256), 0, s, c.k_idx, c.n_seq, c.t_cap,
-                           q_idx, q_pos, q_seq, scores, ld);
+        hipExtLaunchKernelGGL(k_score_dense<1>, grid, dim3(256), 0, s, ev0, ev1, 0, c.k_idx, c.n_seq,
+                              c.t_cap, q_idx, q_pos, q_seq, scores, ld);
     else
-        hipLaunchKernelGGL(k_score_dense<64>, grid, dim3(256), 0, s, c.k_idx, c.n_seq, c.t_cap,
-                           q_idx, q_pos, q_seq, scores, ld);
+        hipExtLaunchKernelGGL(k_score_dense<64>, grid, dim3(256), 0, s, ev0, ev1, 0, c.k_idx, c.n_seq,
+                              c.t_cap, q_idx, q_pos, q_seq, scores, ld);
     return hipGetLastError();
 }
 
