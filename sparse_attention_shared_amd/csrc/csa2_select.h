@@ -188,17 +188,15 @@ __device__ void lds_kth(const uint32_t* keys, int m, int kk, int known, int* his
 }
 
 // Ordered compaction of slots [0, n) with keys K(i): writes the chosen slots
-// (through ids when given) ascending at dst[off0 + ...], counting the keys
-// equal to tau from eq0 (the equal keys of earlier slots outside this range).
-// Wave w owns a contiguous range of slots; within it, lanes take consecutive
-// slots and ballots give every chosen slot its place.  Slot i is written as
-// ids[i], or slot0 + i without ids.  Returns the number of slots this range
-// chose.  wtmp needs 2 * NT/64 ints of LDS.  When pad is set, dst[total .. kk)
-// is filled with -1.
-template <int NT, class KeyFn>
-__device__ int ordered_write(KeyFn K, int64_t n, uint32_t tau, int need, const int32_t* ids,
-                             int32_t kk, int32_t* dst, int* wtmp, int off0 = 0, int eq0 = 0,
-                             bool pad = true, int64_t slot0 = 0) {
+// ascending as V(i) at dst[off0 + ...], counting the keys equal to tau from
+// eq0 (the equal keys of earlier slots outside this range).  Wave w owns a
+// contiguous range of slots; within it, lanes take consecutive slots and
+// ballots give every chosen slot its place.  Returns the number of slots this
+// range chose.  wtmp needs 2 * NT/64 ints of LDS.  When pad is set,
+// dst[total .. kk) is filled with -1.
+template <int NT, class KeyFn, class ValFn>
+__device__ int ordered_write_v(KeyFn K, ValFn V, int64_t n, uint32_t tau, int need, int32_t kk,
+                               int32_t* dst, int* wtmp, int off0 = 0, int eq0 = 0, bool pad = true) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t per = ((n + NW - 1) / NW + 63) / 64 * 64;
@@ -250,7 +248,7 @@ __device__ int ordered_write(KeyFn K, int64_t n, uint32_t tau, int need, const i
             const bool take = in && (kv[u] > tau || (eqf && er < need));
             const uint64_t sm = __ballot(take);
             const int pos = selb + lanes_below(sm);
-            if (take && pos < kk) dst[pos] = ids ? ids[i] : (int32_t)(slot0 + i);
+            if (take && pos < kk) dst[pos] = V(i);
             eqb += __popcll(em);
             selb += __popcll(sm);
         }
@@ -259,6 +257,16 @@ __device__ int ordered_write(KeyFn K, int64_t n, uint32_t tau, int need, const i
         for (int i = off0 + total + tid; i < kk; i += NT) dst[i] = -1;
     __syncthreads();
     return total;
+}
+
+// ordered_write_v writing slot i as ids[i], or slot0 + i without ids.
+template <int NT, class KeyFn>
+__device__ int ordered_write(KeyFn K, int64_t n, uint32_t tau, int need, const int32_t* ids,
+                             int32_t kk, int32_t* dst, int* wtmp, int off0 = 0, int eq0 = 0,
+                             bool pad = true, int64_t slot0 = 0) {
+    return ordered_write_v<NT>(
+        K, [&](int64_t i) { return ids ? ids[i] : (int32_t)(slot0 + i); }, n, tau, need, kk, dst,
+        wtmp, off0, eq0, pad);
 }
 
 // LDS of reg_select.

@@ -12,14 +12,14 @@
 // that stops as soon as a whole bucket is taken.
 //
 // Short rows (<= 32768 slots): one 1024-thread workgroup per row, keys in LDS.
-// Long rows: three multi-workgroup kernels per row set --
+// Long rows: two multi-workgroup kernels per row set --
 //   hist:  12-bit histogram of the top digit (LDS, then device atomics); the
 //          last workgroup of a row picks the boundary bucket of each target;
-//   cand:  every chunk counts its keys above the bucket and appends the keys of
-//          the bucket to a small candidate list; the last workgroup resolves
-//          (tau, need) exactly on the candidates and turns per-chunk counts
-//          into output offsets;
-//   write: each chunk writes its chosen slots at its offset, in order.
+//   keep:  every chunk compacts, in slot order, the keys any target can still
+//          take (those at or above the lowest boundary bucket) into its own
+//          region; the last workgroup of the row stages the row's kept keys
+//          (about k plus one bucket) in LDS, resolves (tau, need) of each
+//          target exactly on them and writes both selections in order.
 // The workspace's counters and histogram reset themselves, so it must be
 // zero-filled before its first use and is left zero-filled by every call.
 #include "csa2_dev.h"
@@ -32,8 +32,9 @@ constexpr int kSmallNT = 1024;
 constexpr int kSmallMax = 32768;  // slots kept in LDS by the one-workgroup path
 constexpr int kLongNT = 1024;
 constexpr int kChunk = 8192;      // slots per workgroup on the long path
-constexpr int kCandCap = 4096;    // candidates per row and target
 constexpr int kMaxTargets = 2;
+constexpr int kStage = 12288;     // kept keys of a row the last workgroup holds in registers
+constexpr int kMaxChunks = 2048;  // rows of up to 2^24 slots
 
 // ---------------------------------------------------------------- short rows
 template <bool IDS, int PER>
@@ -59,28 +60,20 @@ __global__ __launch_bounds__(kSmallNT) void k_topk_small(const float* __restrict
 // Per-row workspace of the long path.
 struct RowState {
     uint32_t hist[kHistBins];
-    uint32_t ctr_hist, ctr_cand;
+    uint32_t ctr_hist, ctr_keep;
     uint32_t bucket[kMaxTargets];  // top digit of the boundary bucket
-    int32_t rem[kMaxTargets];      // rank still needed inside that bucket
-    uint32_t ncand[kMaxTargets];
-    uint32_t tau[kMaxTargets];
-    int32_t need[kMaxTargets];
-    int32_t total[kMaxTargets];
+    int32_t rem[kMaxTargets];      // rank still needed inside that bucket (-1: take all)
     int32_t pad[2];
 };
 struct Cand {
     uint32_t key;
-    int32_t slot;
-};
-// chunk records: [row][target][chunk] {above-bucket count, output offset, tau-equal keys before}
-struct ChunkRec {
-    int32_t gt, off, eq_before, pad;
+    int32_t val;  // the slot's output value (its id, or the slot)
 };
 
 struct LongWs {
-    RowState* st;   // [nq]
-    Cand* cand;     // [nq][targets][kCandCap]
-    ChunkRec* rec;  // [nq][targets][n_chunk]
+    RowState* st;    // [nq]
+    Cand* keep;      // [nq][n_chunk][kChunk]: each chunk's kept keys, slot order
+    int32_t* nkeep;  // [nq][n_chunk]
 };
 
 __device__ __forceinline__ int64_t chunk_begin(int c) { return (int64_t)c * kChunk; }
@@ -150,291 +143,220 @@ __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__
     if (tid == 0) st->ctr_hist = 0u;
 }
 
+struct KeepLds {
+    union {
+        struct {  // a chunk: keys and output values of its slots
+            uint32_t key[kChunk];
+            int32_t val[kChunk];
+        } c;
+    } u;
+    alignas(16) int hist[kHistWords];
+    int koff[kMaxChunks + 1];
+    int tmp[kLongNT / 64 + 1];
+    int wtmp[2 * kLongNT / 64];
+    int res[4];
+    int last;
+};
+
 // grid (n_chunk, nq)
-__global__ __launch_bounds__(kLongNT) void k_topk_cand(const float* __restrict__ scores, int64_t n,
+__global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__ scores, int64_t n,
                                                        int64_t ld, const int32_t* __restrict__ ids,
-                                                       int32_t k, int32_t k2, LongWs ws) {
-    __shared__ uint32_t ckeys[kCandCap];
-    __shared__ int32_t cslot[kCandCap];
-    __shared__ alignas(16) int hist[kHistWords];
-    __shared__ int tmp[kLongNT / 64 + 1];
-    __shared__ int res[4];
-    __shared__ int cnt_gt[kMaxTargets], cnt_cand[kMaxTargets], cbase[kMaxTargets];
-    __shared__ int last;
+                                                       int32_t k, int32_t* __restrict__ out,
+                                                       int32_t k2, int32_t* __restrict__ out2,
+                                                       LongWs ws) {
+    __shared__ KeepLds sh;
     const int c = blockIdx.x, nc = gridDim.x;
     const int64_t row = blockIdx.y;
     const int tid = threadIdx.x;
     const float* s = scores + row * ld;
     const int32_t* irow = ids ? ids + row * n : nullptr;
     RowState* st = ws.st + row;
-    const int nt = k2 > 0 ? 2 : 1;
+    const int nt = out2 ? 2 : 1;
     uint32_t bucket[kMaxTargets] = {0u, 0u};
     int rem[kMaxTargets] = {0, 0};
+    uint32_t low = 0xFFFFFFFFu;  // the lowest key any target can take
     for (int t = 0; t < nt; ++t) {
         bucket[t] = st->bucket[t];
         rem[t] = st->rem[t];
+        low = min(low, rem[t] < 0 ? 1u : bucket[t] << 20);
     }
-    if (tid < kMaxTargets) {
-        cnt_gt[tid] = 0;
-        cnt_cand[tid] = 0;
-    }
-    __syncthreads();
-    // this chunk's keys stay in registers for the two passes below
-    constexpr int kPer = kChunk / kLongNT;
+    // ---- the chunk: stage keys and output values (loads all issued first)
     const int64_t b0 = chunk_begin(c);
-    uint32_t kr[kPer];
-    load_keys<kPer, kLongNT>(s, irow, n, b0 + tid, kr);
-    // per target: keys above the boundary bucket and keys inside it
-    int gt[kMaxTargets] = {0, 0}, nca[kMaxTargets] = {0, 0};
+    const int len = (int)min((int64_t)kChunk, n - b0);
+    {
+        constexpr int kPer = kChunk / kLongNT;
+        float v[kPer];
+        int32_t id[kPer];
 #pragma unroll
-    for (int t = 0; t < kMaxTargets; ++t) {
-        const bool all = rem[t] < 0;
-        const uint32_t bk = bucket[t];
+        for (int u = 0; u < kPer; ++u) v[u] = s[b0 + min(tid + u * kLongNT, len - 1)];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const uint32_t d = kr[j] >> 20;
-            gt[t] += kr[j] && (all || d > bk);
-            nca[t] += kr[j] && !all && d == bk;
+        for (int u = 0; u < kPer; ++u) id[u] = irow ? irow[b0 + min(tid + u * kLongNT, len - 1)] : 0;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = tid + u * kLongNT;
+            const uint32_t key = score_key(v[u]);
+            sh.u.c.key[i] = (i < len && id[u] >= 0 && key != kNegInfKey) ? key : 0u;
+            sh.u.c.val[i] = irow ? id[u] : (int32_t)(b0 + i);
         }
-    }
-    // wave totals, one LDS atomic per wave: the wave's base in the chunk's
-    // range of the candidate list, and the chunk's count of keys above it
-    const int lane = tid & 63;
-    int wbase[kMaxTargets] = {0, 0};
-#pragma unroll
-    for (int t = 0; t < kMaxTargets; ++t) {
-        if (t >= nt) break;
-        const int wn = wave_sum_dpp(nca[t]), wg = wave_sum_dpp(gt[t]);
-        int b = 0;
-        if (lane == 0) {
-            if (wn) b = atomicAdd(&cnt_cand[t], wn);
-            if (wg) atomicAdd(&cnt_gt[t], wg);
-        }
-        wbase[t] = __builtin_amdgcn_readfirstlane(b);
     }
     __syncthreads();
-    if (tid < nt) {
-        // one device atomic per chunk reserves its range of the candidate list
-        cbase[tid] = (int)atomicAdd(&st->ncand[tid], (uint32_t)cnt_cand[tid]);
+    // thread t owns slots 8 t .. 8 t + 7: kept ones go to the chunk's region in order
+    uint32_t kk8[8];
+    {
+        const uint4 a = *reinterpret_cast<const uint4*>(&sh.u.c.key[8 * tid]);
+        const uint4 b = *reinterpret_cast<const uint4*>(&sh.u.c.key[8 * tid + 4]);
+        kk8[0] = a.x; kk8[1] = a.y; kk8[2] = a.z; kk8[3] = a.w;
+        kk8[4] = b.x; kk8[5] = b.y; kk8[6] = b.z; kk8[7] = b.w;
     }
-    __syncthreads();
-    // candidates go to their place by ballots: no atomics per key
+    int mine = 0;
 #pragma unroll
-    for (int t = 0; t < kMaxTargets; ++t) {
-        if (t >= nt || rem[t] < 0) continue;
-        Cand* cb = ws.cand + ((int64_t)row * kMaxTargets + t) * kCandCap;
-        int pos0 = cbase[t] + wbase[t];
+    for (int u = 0; u < 8; ++u) mine += kk8[u] >= low;  // key 0 (past len too) is below low
+    int tot;
+    int pos = block_excl_scan<kLongNT>(mine, sh.tmp, &tot);
+    Cand* reg = ws.keep + ((int64_t)row * nc + c) * kChunk;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const bool is = kr[j] && (kr[j] >> 20) == bucket[t];
-            const uint64_t m = __ballot(is);
-            if (is) {
-                const int pos = pos0 + lanes_below(m);
-                if (pos < kCandCap) {
-                    cb[pos].key = kr[j];
-                    cb[pos].slot = (int32_t)(tid + (int64_t)j * kLongNT + b0);
-                }
-            }
-            pos0 += __popcll(m);
-        }
-    }
-    if (tid < nt) ws.rec[((int64_t)row * kMaxTargets + tid) * nc + c].gt = cnt_gt[tid];
+    for (int u = 0; u < 8; ++u)
+        if (kk8[u] >= low) reg[pos++] = Cand{kk8[u], sh.u.c.val[8 * tid + u]};
+    if (tid == 0) ws.nkeep[row * nc + c] = tot;
     __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (tid == 0) last = arrive_last(&st->ctr_cand, (uint32_t)nc);
+    if (tid == 0) sh.last = arrive_last(&st->ctr_keep, (uint32_t)nc);
     __syncthreads();  // thread 0's acquire covers the workgroup
-    if (!last) return;
-    // ---- last workgroup of the row: exact (tau, need) and chunk offsets.
-    // Every load it needs is issued first: both targets' candidate lists
-    // (whole buffers: slots past the count are read but not used) and the
-    // per-chunk counts of keys above the bucket.
-    constexpr int kCpt = kCandCap / kLongNT;  // candidates per thread
-    static_assert(kCandCap == kCpt * kLongNT, "whole candidates per thread");
-    const int cper = (nc + kLongNT - 1) / kLongNT;  // nc <= 2048 chunks: at most 4
-    const int cc0 = min(nc, tid * cper), cc1 = min(nc, cc0 + cper);
-    Cand cpre[kMaxTargets][kCpt];
-    int gpre[kMaxTargets][4];
-    uint32_t mpre[kMaxTargets];
-#pragma unroll
-    for (int t = 0; t < kMaxTargets; ++t) {
-        mpre[t] = t < nt ? __hip_atomic_load(&st->ncand[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-        const Cand* cb = ws.cand + ((int64_t)row * kMaxTargets + t) * kCandCap;
-        const ChunkRec* rec = ws.rec + ((int64_t)row * kMaxTargets + t) * nc;
-#pragma unroll
-        for (int u = 0; u < kCpt; ++u) cpre[t][u] = t < nt ? cb[tid + u * kLongNT] : Cand{0u, 0};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) gpre[t][u] = (t < nt && cc0 + u < cc1) ? rec[cc0 + u].gt : 0;
+    if (!sh.last) return;
+
+    // ---- the last workgroup of the row: chunk offsets of the kept keys
+    {
+        const int c0 = 2 * tid;  // nc <= 2048: two chunks per thread
+        const int a = c0 < nc ? ws.nkeep[row * nc + c0] : 0;
+        const int b = c0 + 1 < nc ? ws.nkeep[row * nc + c0 + 1] : 0;
+        int all;
+        const int pre = block_excl_scan<kLongNT>(a + b, sh.tmp, &all);
+        if (c0 < nc) sh.koff[c0] = pre;
+        if (c0 + 1 < nc) sh.koff[c0 + 1] = pre + a;
+        if (tid == 0) sh.koff[nc] = all;
     }
-#pragma unroll
-    for (int t = 0; t < kMaxTargets; ++t) {
-        if (t >= nt) break;
-        const int kk = t ? k2 : k;
-        ChunkRec* rec = ws.rec + ((int64_t)row * kMaxTargets + t) * nc;
-        const uint32_t m = mpre[t];
-        uint32_t tau;
-        int need;
-        bool exact = true;
-        if (rem[t] < 0) {
-            tau = 0u;  // all selectable keys
-            need = 0;
-        } else if (m <= (uint32_t)kCandCap) {
-#pragma unroll
-            for (int u = 0; u < kCpt; ++u) {
-                const int i = tid + u * kLongNT;
-                if (i < (int)m) {
-                    ckeys[i] = cpre[t][u].key;
-                    cslot[i] = cpre[t][u].slot;
-                }
-            }
-            __syncthreads();
-            lds_kth<kLongNT>(ckeys, (int)m, rem[t], 12, hist, res, tau, need);
-        } else {
-            exact = false;  // bucket too large for LDS: resolve below over the row
-            tau = 0u;
-            need = 0;
+    __syncthreads();
+    const int m = sh.koff[nc];
+    const Cand* kb = ws.keep + (int64_t)row * nc * kChunk;
+    // kept key i of the row: chunk = the last one whose offset is <= i
+    auto at = [&](int64_t i) -> const Cand* {
+        int lo = 0, hi = nc - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sh.koff[mid] <= i) lo = mid;
+            else hi = mid - 1;
         }
-        if (!exact) {
-            // Radix over the whole row (rare): prefix = bucket, three more digits.
-            uint32_t prefix = bucket[t] << 20, mask = 0xFFF00000u;
-            int r = rem[t];
-            for (int shift = 8; shift >= 0; shift -= 8) {
-                const int bits = shift == 8 ? 12 : 8;
-                const int nb = 1 << bits;
-                const uint32_t bm = (uint32_t)nb - 1u;
-                for (int i = tid; i < nb; i += kLongNT) hist[i] = 0;
-                __syncthreads();
-                for (int64_t i = tid; i < n; i += kLongNT) {
-                    const uint32_t key = load_key(s, irow, i);
-                    if (key && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & bm], 1);
-                }
-                __syncthreads();
-                if (tid == 0) {
-                    int acc = 0;
-                    for (int b = nb - 1; b >= 0; --b) {
-                        if (acc + hist[b] >= r) {
-                            res[0] = b;
-                            res[1] = acc;
-                            break;
-                        }
-                        acc += hist[b];
-                    }
-                }
-                __syncthreads();
-                prefix |= (uint32_t)res[0] << shift;
-                mask |= bm << shift;
-                r -= res[1];
-                __syncthreads();
-            }
-            tau = prefix;
-            need = r;
-        }
-        // per-chunk counts of keys > tau inside the bucket and of keys == tau
-        // (reuse hist as two int arrays of nc entries)
-        int* cgt = hist;
-        int* ceq = hist + 2048;
-        for (int i = tid; i < nc; i += kLongNT) {
-            cgt[i] = 0;
-            ceq[i] = 0;
-        }
-        __syncthreads();
-        if (rem[t] >= 0) {
-            if (exact) {
-                // a chunk's candidates are contiguous in the list, so a wave's
-                // 64 usually share one chunk: then one atomic per wave
-                const int lane = tid & 63;
-                for (int i0 = tid - lane; i0 < (int)m; i0 += kLongNT) {
-                    const int i = i0 + lane;
-                    const bool in = i < (int)m;
-                    const int ch = in ? cslot[i] / kChunk : -1;
-                    const int g1 = in && ckeys[i] > tau;
-                    const int e1 = in && ckeys[i] == tau && need > 0;
-                    const int ch0 = __builtin_amdgcn_readfirstlane(ch);
-                    if (__ballot(in && ch != ch0) == 0) {
-                        const int sg = wave_sum_dpp(g1), se = wave_sum_dpp(e1);
-                        if (lane == 0) {
-                            if (sg) atomicAdd(&cgt[ch0], sg);
-                            if (se) atomicAdd(&ceq[ch0], se);
-                        }
-                    } else if (in) {
-                        if (g1) atomicAdd(&cgt[ch], 1);
-                        else if (e1) atomicAdd(&ceq[ch], 1);
-                    }
-                }
-            } else {
-                for (int64_t i = tid; i < n; i += kLongNT) {
-                    const uint32_t key = load_key(s, irow, i);
-                    if ((key >> 20) != bucket[t]) continue;
-                    if (key > tau) atomicAdd(&cgt[i / kChunk], 1);
-                    else if (key == tau && need > 0) atomicAdd(&ceq[i / kChunk], 1);
-                }
-            }
-        }
-        __syncthreads();
+        return kb + (int64_t)lo * kChunk + (i - sh.koff[lo]);
+    };
+    if (m <= kStage) {
+        // thread t holds kept keys [E t, E t + E) of the row in registers
+        // (the row order is chunk-major, each chunk in slot order)
+        constexpr int kE = kStage / kLongNT;
+        static_assert(kStage == kE * kLongNT, "whole entries per thread");
+        const int E = (m + kLongNT - 1) / kLongNT;
+        const int i0 = min(tid * E, m);
+        int ch = 0;  // the chunk holding entry i0: the last one whose offset is <= i0
         {
-            // chunk offsets: each thread owns a run of consecutive chunks
-            const int c0 = cc0, c1 = cc1;
-            int gtv[4], eqsum = 0;
+            int lo = 0, hi = nc - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sh.koff[mid] <= i0) lo = mid;
+                else hi = mid - 1;
+            }
+            ch = lo;
+        }
+        int64_t addr[kE];
+        int off = i0 - sh.koff[ch];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) gtv[u] = gpre[t][u];
-            for (int ch = c0; ch < c1; ++ch) eqsum += ceq[ch];
-            int tot;
-            int eqb = block_excl_scan<kLongNT>(eqsum, tmp, &tot);
-            int selsum = 0, e2 = eqb;
-            for (int ch = c0; ch < c1; ++ch) {
-                selsum += gtv[ch - c0] + cgt[ch] + min(max(need - e2, 0), ceq[ch]);
-                e2 += ceq[ch];
+        for (int u = 0; u < kE; ++u) {
+            const bool in = u < E && i0 + u < m;
+            while (in && ch < nc - 1 && i0 + u >= sh.koff[ch + 1]) {  // past this chunk's keys
+                ++ch;
+                off = i0 + u - sh.koff[ch];
+            }
+            addr[u] = in ? (int64_t)ch * kChunk + off : 0;
+            off += in;
+        }
+        Cand e[kE];
+#pragma unroll
+        for (int u = 0; u < kE; ++u) e[u] = kb[addr[u]];  // every load issued before any use
+        uint32_t key[kE];
+#pragma unroll
+        for (int u = 0; u < kE; ++u) key[u] = (u < E && i0 + u < m) ? e[u].key : 0u;
+        for (int t = 0; t < nt; ++t) {
+            const int32_t kk = t ? k2 : k;
+            int32_t* dst = t ? out2 + row * k2 : out + row * k;
+            uint32_t tau = 0u;  // rem < 0: every selectable key
+            int need = 0;
+            if (rem[t] >= 0) {
+                // the top 12 bits are the bucket's: 12 more, then the last 8
+                // unless a whole sub-bucket completes the selection
+                uint32_t prefix = bucket[t] << 20, mask = 0xFFF00000u;
+                int r = rem[t];
+                bool done = false;
+                for (int shift = 8; shift >= 0 && !done; shift -= 8) {
+                    const int bits = shift ? 12 : 8;
+                    const uint32_t dm = (1u << bits) - 1u;
+                    for (int i = tid; i < kHistWords; i += kLongNT) sh.hist[i] = 0;
+                    __syncthreads();
+#pragma unroll
+                    for (int u = 0; u < kE; ++u)
+                        if (key[u] && (key[u] & mask) == prefix)
+                            atomicAdd(&sh.hist[hidx((int)((key[u] >> shift) & dm))], 1);
+                    __syncthreads();
+                    if (tid < 64) wave_find_bucket(sh.hist, 1 << bits, r, sh.res);
+                    __syncthreads();
+                    prefix |= (uint32_t)sh.res[0] << shift;
+                    mask |= dm << shift;
+                    r -= sh.res[1];
+                    done = sh.res[2] == r;  // the whole sub-bucket is taken
+                    __syncthreads();
+                }
+                if (done) {
+                    tau = prefix - 1u;  // every key >= prefix
+                } else {
+                    tau = prefix;
+                    need = r;
+                }
+            }
+            // ordered write: one scan of packed (greater, equal) counts
+            // (m <= kStage < 2^16, so the halves never carry)
+            int packed = 0;
+#pragma unroll
+            for (int u = 0; u < kE; ++u) {
+                packed += key[u] > tau;
+                packed += ((need > 0) & (key[u] == tau)) << 16;
             }
             int total;
-            int off = block_excl_scan<kLongNT>(selsum, tmp, &total);
-            for (int ch = c0; ch < c1; ++ch) {
-                rec[ch].off = off;
-                rec[ch].eq_before = eqb;
-                off += gtv[ch - c0] + cgt[ch] + min(max(need - eqb, 0), ceq[ch]);
-                eqb += ceq[ch];
+            const int before = block_excl_scan<kLongNT>(packed, sh.tmp, &total);
+            int eq = (int)((uint32_t)before >> 16);
+            int pos = (int)((uint32_t)before & 0xFFFFu) + min(need, eq);
+#pragma unroll
+            for (int u = 0; u < kE; ++u) {
+                bool take = key[u] > tau;
+                if (need > 0 && key[u] == tau) {
+                    take = eq < need;
+                    ++eq;
+                }
+                if (take && pos < kk) dst[pos++] = e[u].val;
             }
-            if (tid == 0) {
-                st->tau[t] = tau;
-                st->need[t] = need;
-                st->total[t] = total;
-                st->ncand[t] = 0u;
-            }
+            const int chosen = (int)((uint32_t)total & 0xFFFFu) + min(need, (int)((uint32_t)total >> 16));
+            for (int i = min(chosen, kk) + tid; i < kk; i += kLongNT) dst[i] = -1;
+            __syncthreads();
         }
-        __syncthreads();
+    } else {
+        // a row with many keys tied around the boundary: read them in place
+        auto K = [&](int64_t i) { return at(i)->key; };
+        auto V = [&](int64_t i) { return at(i)->val; };
+        for (int t = 0; t < nt; ++t) {
+            const int32_t kk = t ? k2 : k;
+            int32_t* dst = t ? out2 + row * k2 : out + row * k;
+            uint32_t tau = 0u;
+            int need = 0;
+            if (rem[t] >= 0) kth_fn<kLongNT>(K, m, rem[t], 12, bucket[t] << 20, sh.hist, sh.res, tau, need);
+            ordered_write_v<kLongNT>(K, V, m, tau, need, kk, dst, sh.wtmp);
+        }
     }
-    if (tid == 0) st->ctr_cand = 0u;
-}
-
-// grid (n_chunk, nq)
-__global__ __launch_bounds__(kLongNT) void k_topk_write(const float* __restrict__ scores, int64_t n,
-                                                        int64_t ld, const int32_t* __restrict__ ids,
-                                                        int32_t k, int32_t* __restrict__ out,
-                                                        int32_t k2, int32_t* __restrict__ out2,
-                                                        LongWs ws) {
-    __shared__ uint32_t keys[kChunk];
-    __shared__ int wtmp[2 * kLongNT / 64];
-    const int c = blockIdx.x, nc = gridDim.x;
-    const int64_t row = blockIdx.y;
-    const int tid = threadIdx.x;
-    const float* s = scores + row * ld;
-    const int32_t* irow = ids ? ids + row * n : nullptr;
-    const RowState* st = ws.st + row;
-    const int64_t b0 = chunk_begin(c), b1 = min(n, b0 + kChunk);
-    const int64_t len = b1 - b0;
-    stage_keys<kLongNT>(s + b0, irow ? irow + b0 : nullptr, len, keys);
-    __syncthreads();
-    const int nt = out2 ? 2 : 1;
-    for (int t = 0; t < nt; ++t) {
-        const int32_t kk = t ? k2 : k;
-        int32_t* dst = (t ? out2 + row * k2 : out + row * k);
-        const ChunkRec r = ws.rec[((int64_t)row * kMaxTargets + t) * nc + c];
-        const uint32_t tau = st->tau[t];
-        const int need = st->need[t];
-        const int32_t* ich = irow ? irow + b0 : nullptr;
-        ordered_write<kLongNT>([&](int64_t i) { return keys[i]; }, len, tau, need, ich, kk, dst,
-                               wtmp, r.off, r.eq_before, false, b0);
-        if (c == nc - 1)
-            for (int i = st->total[t] + tid; i < kk; i += kLongNT) dst[i] = -1;
-        __syncthreads();
-    }
+    if (tid == 0) st->ctr_keep = 0u;
 }
 
 static int32_t long_chunks(int64_t n) { return (int32_t)((n + kChunk - 1) / kChunk); }
@@ -442,8 +364,7 @@ static int32_t long_chunks(int64_t n) { return (int32_t)((n + kChunk - 1) / kChu
 size_t topk_ws_bytes(int32_t nq, int64_t n, int32_t, int32_t) {
     if (n <= kSmallMax) return 0;
     const size_t nc = (size_t)long_chunks(n);
-    return (size_t)nq * (sizeof(RowState) + kMaxTargets * kCandCap * sizeof(Cand) +
-                         kMaxTargets * nc * sizeof(ChunkRec)) + 256;
+    return (size_t)nq * (sizeof(RowState) + nc * kChunk * sizeof(Cand) + nc * sizeof(int32_t)) + 256;
 }
 
 hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, const int32_t* ids,
@@ -461,17 +382,17 @@ hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, c
         return hipGetLastError();
     }
     const int32_t nc = long_chunks(n);
+    if (nc > kMaxChunks) return hipErrorInvalidValue;
     char* base = static_cast<char*>(ws);
     LongWs w;
     w.st = reinterpret_cast<RowState*>(base);
-    w.cand = reinterpret_cast<Cand*>(base + (size_t)nq * sizeof(RowState));
-    w.rec = reinterpret_cast<ChunkRec*>(reinterpret_cast<char*>(w.cand) +
-                                        (size_t)nq * kMaxTargets * kCandCap * sizeof(Cand));
+    w.keep = reinterpret_cast<Cand*>(base + (size_t)nq * sizeof(RowState));
+    w.nkeep = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(w.keep) +
+                                         (size_t)nq * nc * kChunk * sizeof(Cand));
     const int32_t kk2 = out2 ? k2 : 0;
     dim3 grid((uint32_t)nc, (uint32_t)nq);
     hipLaunchKernelGGL(k_topk_hist, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, kk2, w);
-    hipLaunchKernelGGL(k_topk_cand, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, kk2, w);
-    hipLaunchKernelGGL(k_topk_write, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
+    hipLaunchKernelGGL(k_topk_keep, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
                        out2, w);
     return hipGetLastError();
 }

@@ -136,18 +136,22 @@ def test_topk_bit_exact_on_identical_scores(n, k, k2):
     del ids
 
 
-def test_topk_through_ascending_ids_with_empty_slots():
+@pytest.mark.parametrize("n,k,k2", [(9000, 300, 0), (50000, 500, 3000)])  # one workgroup; long path
+def test_topk_through_ascending_ids_with_empty_slots(n, k, k2):
     rng = np.random.default_rng(7)
-    nq, n, k = 4, 9000, 300
-    ids = np.sort(rng.choice(100000, size=(nq, n), replace=True), axis=1).astype(np.int32)
+    nq = 4
+    ids = np.sort(rng.choice(10 * n, size=(nq, n), replace=True), axis=1).astype(np.int32)
     ids = np.maximum.accumulate(ids, axis=1)
     ids[:, 1:][ids[:, 1:] == ids[:, :-1]] = -1  # duplicates become empty slots
     ids[rng.random((nq, n)) < 0.05] = -1
     s = (rng.integers(-10, 11, size=(nq, n))).astype(np.float32)
-    g, _ = csa2.topk(torch.from_numpy(s).cuda(), k, ids=dev32(ids))
+    s[1] = rng.standard_normal(n).astype(np.float32) * 8  # few ties
+    g, g2 = csa2.topk(torch.from_numpy(s).cuda(), k, ids=dev32(ids), k2=k2)
     g = host(g)
     for i in range(nq):
         assert np.array_equal(g[i], oracle.topk(s[i], k, ids[i])), i
+        if k2:
+            assert np.array_equal(host(g2)[i], oracle.topk(s[i], k2, ids[i])), i
 
 
 # ------------------------------------------------------------ attention
