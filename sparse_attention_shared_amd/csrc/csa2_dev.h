@@ -98,6 +98,39 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
     return r;
 }
 
+// Two exclusive scans over a whole workgroup at once (same rules as
+// block_excl_scan; `tmp` needs 2 (NT/64 + 1) ints of LDS).
+template <int NT>
+__device__ __forceinline__ void block_excl_scan2(int a, int b, int* tmp, int (&before)[2],
+                                                 int (&total)[2]) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+    if (lane == 63) {
+        tmp[w] = ia;
+        tmp[NW + 1 + w] = ib;
+    }
+    __syncthreads();
+    if (w == 0) {
+        const int xa = lane < NW ? tmp[lane] : 0, xb = lane < NW ? tmp[NW + 1 + lane] : 0;
+        const int ya = wave_incl_scan(xa), yb = wave_incl_scan(xb);
+        if (lane < NW) {
+            tmp[lane] = ya - xa;
+            tmp[NW + 1 + lane] = yb - xb;
+        }
+        if (lane == NW - 1) {
+            tmp[NW] = ya;
+            tmp[2 * NW + 1] = yb;
+        }
+    }
+    __syncthreads();
+    before[0] = tmp[w] + ia - a;
+    before[1] = tmp[NW + 1 + w] + ib - b;
+    total[0] = tmp[NW];
+    total[1] = tmp[2 * NW + 1];
+    __syncthreads();
+}
+
 // Workgroup barrier that orders LDS only: unlike __syncthreads it does not
 // wait for the caller's global loads, so loads issued before it stay in
 // flight.  For barriers that publish LDS data alone.

@@ -153,8 +153,10 @@ struct KeepLds {
     alignas(16) int hist[kHistWords];
     int koff[kMaxChunks + 1];
     int tmp[kLongNT / 64 + 1];
+    int tmp2[2 * (kLongNT / 64 + 1)];
     int wtmp[2 * kLongNT / 64];
     int res[4];
+    int res2[kMaxTargets][4];
     int last;
 };
 
@@ -282,66 +284,84 @@ __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__
         uint32_t key[kE];
 #pragma unroll
         for (int u = 0; u < kE; ++u) key[u] = (u < E && i0 + u < m) ? e[u].key : 0u;
+        // (tau, need) of both targets at once: the top 12 bits are the
+        // bucket's; two more 10-bit digits, each target stopping as soon as a
+        // whole sub-bucket completes its selection
+        uint32_t tau[kMaxTargets] = {0u, 0u};  // rem < 0: every selectable key
+        int need[kMaxTargets] = {0, 0};
+        {
+            uint32_t prefix[kMaxTargets], mask[kMaxTargets];
+            int r[kMaxTargets];
+            bool done[kMaxTargets];
+#pragma unroll
+            for (int t = 0; t < kMaxTargets; ++t) {
+                done[t] = t >= nt || rem[t] < 0;
+                prefix[t] = bucket[t] << 20;
+                mask[t] = 0xFFF00000u;
+                r[t] = rem[t];
+            }
+            constexpr int kBits = 10;
+            constexpr uint32_t kDm = (1u << kBits) - 1u;
+            constexpr int kW = (1 << kBits) + (1 << kBits) / 16;  // hidx(1 << kBits)
+            for (int shift = 20 - kBits; shift >= 0 && !(done[0] && done[1]); shift -= kBits) {
+                for (int i = tid; i < kMaxTargets * kW; i += kLongNT) sh.hist[i] = 0;
+                __syncthreads();
+#pragma unroll
+                for (int u = 0; u < kE; ++u)
+#pragma unroll
+                    for (int t = 0; t < kMaxTargets; ++t)
+                        if (!done[t] && key[u] && (key[u] & mask[t]) == prefix[t])
+                            atomicAdd(&sh.hist[t * kW + hidx((int)((key[u] >> shift) & kDm))], 1);
+                __syncthreads();
+                const int w = tid >> 6;
+                if (w < kMaxTargets && !done[w]) wave_find_bucket(sh.hist + w * kW, 1 << kBits, r[w], sh.res2[w]);
+                __syncthreads();
+#pragma unroll
+                for (int t = 0; t < kMaxTargets; ++t) {
+                    if (done[t]) continue;
+                    prefix[t] |= (uint32_t)sh.res2[t][0] << shift;
+                    mask[t] |= kDm << shift;
+                    r[t] -= sh.res2[t][1];
+                    if (sh.res2[t][2] == r[t]) {  // the whole sub-bucket is taken
+                        done[t] = true;
+                        tau[t] = prefix[t] - 1u;  // every key >= prefix
+                    } else if (shift == 0) {
+                        tau[t] = prefix[t];
+                        need[t] = r[t];
+                    }
+                }
+            }
+        }
+        // ordered writes: one scan of packed (greater, equal) counts per
+        // target (m <= kStage < 2^16, so the halves never carry)
+        int packed[kMaxTargets] = {0, 0};
+#pragma unroll
+        for (int u = 0; u < kE; ++u)
+#pragma unroll
+            for (int t = 0; t < kMaxTargets; ++t) {
+                packed[t] += key[u] > tau[t];
+                packed[t] += ((need[t] > 0) & (key[u] == tau[t])) << 16;
+            }
+        int total[kMaxTargets];
+        int before[kMaxTargets];
+        block_excl_scan2<kLongNT>(packed[0], packed[1], sh.tmp2, before, total);
         for (int t = 0; t < nt; ++t) {
             const int32_t kk = t ? k2 : k;
             int32_t* dst = t ? out2 + row * k2 : out + row * k;
-            uint32_t tau = 0u;  // rem < 0: every selectable key
-            int need = 0;
-            if (rem[t] >= 0) {
-                // the top 12 bits are the bucket's: 12 more, then the last 8
-                // unless a whole sub-bucket completes the selection
-                uint32_t prefix = bucket[t] << 20, mask = 0xFFF00000u;
-                int r = rem[t];
-                bool done = false;
-                for (int shift = 8; shift >= 0 && !done; shift -= 8) {
-                    const int bits = shift ? 12 : 8;
-                    const uint32_t dm = (1u << bits) - 1u;
-                    for (int i = tid; i < kHistWords; i += kLongNT) sh.hist[i] = 0;
-                    __syncthreads();
-#pragma unroll
-                    for (int u = 0; u < kE; ++u)
-                        if (key[u] && (key[u] & mask) == prefix)
-                            atomicAdd(&sh.hist[hidx((int)((key[u] >> shift) & dm))], 1);
-                    __syncthreads();
-                    if (tid < 64) wave_find_bucket(sh.hist, 1 << bits, r, sh.res);
-                    __syncthreads();
-                    prefix |= (uint32_t)sh.res[0] << shift;
-                    mask |= dm << shift;
-                    r -= sh.res[1];
-                    done = sh.res[2] == r;  // the whole sub-bucket is taken
-                    __syncthreads();
-                }
-                if (done) {
-                    tau = prefix - 1u;  // every key >= prefix
-                } else {
-                    tau = prefix;
-                    need = r;
-                }
-            }
-            // ordered write: one scan of packed (greater, equal) counts
-            // (m <= kStage < 2^16, so the halves never carry)
-            int packed = 0;
+            int eq = (int)((uint32_t)before[t] >> 16);
+            int pos = (int)((uint32_t)before[t] & 0xFFFFu) + min(need[t], eq);
 #pragma unroll
             for (int u = 0; u < kE; ++u) {
-                packed += key[u] > tau;
-                packed += ((need > 0) & (key[u] == tau)) << 16;
-            }
-            int total;
-            const int before = block_excl_scan<kLongNT>(packed, sh.tmp, &total);
-            int eq = (int)((uint32_t)before >> 16);
-            int pos = (int)((uint32_t)before & 0xFFFFu) + min(need, eq);
-#pragma unroll
-            for (int u = 0; u < kE; ++u) {
-                bool take = key[u] > tau;
-                if (need > 0 && key[u] == tau) {
-                    take = eq < need;
+                bool take = key[u] > tau[t];
+                if (need[t] > 0 && key[u] == tau[t]) {
+                    take = eq < need[t];
                     ++eq;
                 }
                 if (take && pos < kk) dst[pos++] = e[u].val;
             }
-            const int chosen = (int)((uint32_t)total & 0xFFFFu) + min(need, (int)((uint32_t)total >> 16));
+            const int chosen = (int)((uint32_t)total[t] & 0xFFFFu) +
+                               min(need[t], (int)((uint32_t)total[t] >> 16));
             for (int i = min(chosen, kk) + tid; i < kk; i += kLongNT) dst[i] = -1;
-            __syncthreads();
         }
     } else {
         // a row with many keys tied around the boundary: read them in place
