@@ -8,18 +8,20 @@
 //
 // The score matrix (queries x positions x 64 dims) is a dense contraction; it
 // runs on v_mfma_f32_16x16x32_bf16 and is never written out.  Four launches:
-//   1. cmax:   scores on MFMA; per query, the maximum key of every 16-position
-//              chunk (1/16 of the scores) goes to the workspace.
-//   2. thresh: per query, thr = the k-th largest chunk maximum.  Each of the k
-//              chunks at or above thr holds a position scoring >= thr, so at
-//              least k positions pass thr and every top-k position does.
-//   3. filter: the same MFMA scores again (same instructions, so bit-identical);
-//              positions with key >= thr are appended, with their keys, to the
-//              query's candidate list (about 1.1 k of them for i.i.d. scores).
+//   1. cmax:   scores on MFMA over a sample -- every eighth 64-position step;
+//              per query, the maximum key of every 16-position chunk of the
+//              sample goes to the workspace.
+//   2. thresh: per query, thr = the m-th largest sampled chunk maximum, m =
+//              1.3 k / 8: about 1.3 k scores of the whole row reach it.
+//   3. filter: all the scores on MFMA; positions with key >= thr are
+//              appended, with their keys, to the query's candidate list.
 //   4. select: per query, candidates are put in position order through an
 //              LDS bitmap, then the exact (score desc, position asc) top-k is
-//              taken and written ascending.  A query whose list overflowed
-//              (ties, short rows) is resolved exactly by recomputing its scores.
+//              taken and written ascending.  The list certifies itself: when
+//              it holds at least k positions, the k-th best score is >= thr,
+//              so every top-k position is on it.  A query with fewer (an
+//              unlucky sample) or with more than the list holds (ties) is
+//              resolved exactly by recomputing its scores.
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
 #include "csa2_select.h"
@@ -31,10 +33,11 @@ typedef __attribute__((ext_vector_type(4))) float pf_f32x4;
 
 constexpr int kPfQB = 8;        // 16-query blocks per wave
 constexpr int kPfQ = 16 * kPfQB; // queries per workgroup tile (every wave takes all of them)
-constexpr int kPfSpan = 2048;   // positions per chunk-maximum workgroup (8 steps of 4 waves x 64)
-constexpr int kPfFiltSpan = 1024;  // positions per filter workgroup
+constexpr int kPfCStride = 512; // positions between sampled 64-position steps
+constexpr int kPfCSteps = 4;    // sampled steps per chunk-maximum workgroup
+constexpr int kPfFiltSpan = 512;   // positions per filter workgroup (about 11 candidates per query)
 constexpr int kPfChunk = 16;    // positions per chunk maximum
-constexpr int kPfLB = 24;       // LDS candidate slots per query in the filter (about 18 expected)
+constexpr int kPfLB = 24;       // LDS candidate slots per query in the filter
 constexpr int kPfSelNT = 512;
 
 __device__ __forceinline__ int64_t pf_clamp_pos(int64_t p, int64_t t_cap) {
@@ -135,12 +138,11 @@ __device__ __forceinline__ void pf_sweep(const uint16_t* __restrict__ kseq, int3
     }
 }
 
-// ---- 1. chunk maxima -------------------------------------------------------
+// ---- 1. sampled chunk maxima -------------------------------------------
 // A chunk is the 16 positions one lane holds for one query in a 64-position
-// step: t0 + 16 j + 4 g + r (j, r = 0..3), chunk index t0 / 16 + g, so the
-// maximum needs no cross-lane traffic.  Chunk c holds a position <= t exactly
-// when c < pf_nchunks(t).
-// grid (ceil(nq / kPfQ), ceil(t_cap / kPfSpan)), 256 threads.  cmax: [nq][ldc] keys.
+// step: t0 + 16 j + 4 g + r (j, r = 0..3), so its maximum needs no
+// cross-lane traffic.  Sampled chunk c holds a position <= t exactly when
+// c < pf_nchunks(t).
 template <bool MASK>
 __device__ __forceinline__ void pf_cmax_step(const pf_bf16x8 (&kf)[4][2],
                                              const pf_bf16x8 (&qf)[kPfQB][2], int32_t t0, int g,
@@ -164,44 +166,129 @@ __device__ __forceinline__ void pf_cmax_step(const pf_bf16x8 (&kf)[4][2],
     }
 }
 
+// The cmax workgroup's four waves take different query tiles (4 x 128
+// queries) over the same sampled positions, so each 64-position key tile is
+// loaded from global memory once and read by all four waves from LDS.  Rows are
+// padded to 144 bytes: the 16 lanes of a lane group read 16 rows at one
+// column, and the padding puts them in 16 different bank groups.
+constexpr int kPfWQ = 4 * kPfQ;      // queries per cmax workgroup
+constexpr int kPfTileRow = 36;       // LDS words per key row (128 B + 16 B)
+constexpr int kPfTileWords = 64 * kPfTileRow;
+
+// The two 16-byte pieces thread tid (of 256) loads of the key tile at t0:
+// rows tid / 8 and 32 + tid / 8, dims 8 (tid % 8) .. + 8.  Rows past t_cap
+// repeat the last row (masked by every query).
+__device__ __forceinline__ void pf_tile_load(const uint16_t* __restrict__ kseq, int32_t t_cap,
+                                             int32_t t0, int tid, uint4& r0, uint4& r1) {
+    const int32_t ta = min(t0 + (tid >> 3), t_cap - 1), tb = min(t0 + 32 + (tid >> 3), t_cap - 1);
+    r0 = *reinterpret_cast<const uint4*>(kseq + (int64_t)ta * kIdxDim + 8 * (tid & 7));
+    r1 = *reinterpret_cast<const uint4*>(kseq + (int64_t)tb * kIdxDim + 8 * (tid & 7));
+}
+
+__device__ __forceinline__ void pf_tile_store(uint32_t* buf, int tid, const uint4& r0, const uint4& r1) {
+    *reinterpret_cast<uint4*>(buf + (tid >> 3) * kPfTileRow + 4 * (tid & 7)) = r0;
+    *reinterpret_cast<uint4*>(buf + (32 + (tid >> 3)) * kPfTileRow + 4 * (tid & 7)) = r1;
+}
+
+// Key fragments of the tile's position blocks (the layout pf_load_k gives).
+__device__ __forceinline__ void pf_tile_frag(const uint32_t* buf, int n16, int g, pf_bf16x8 (&kf)[4][2]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t* row = buf + (16 * j + n16) * kPfTileRow;
+        kf[j][0] = __builtin_bit_cast(pf_bf16x8, *reinterpret_cast<const uint4*>(row + 4 * g));
+        kf[j][1] = __builtin_bit_cast(pf_bf16x8, *reinterpret_cast<const uint4*>(row + 16 + 4 * g));
+    }
+}
+
+// grid (ceil(nq / kPfWQ), ceil(t_cap / (kPfCStride kPfCSteps))), 256 threads.
+// Sampled step i starts at position kPfCStride i; its chunk g (of 4) is
+// written to cmax[q][4 i + g] (ldc words per query).
 __global__ __launch_bounds__(256) void k_pf_cmax(const uint16_t* __restrict__ kseq, int32_t t_cap,
                                                  const uint16_t* __restrict__ q_idx,
                                                  const int32_t* __restrict__ q_pos, int32_t nq,
                                                  uint32_t* __restrict__ cmax, int64_t ldc) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ uint32_t tile[2][kPfTileWords];
+    __shared__ int32_t wmax[4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g = lane >> 4;
-    const int64_t q0 = (int64_t)blockIdx.x * kPfQ;
-    const int32_t span0 = (int32_t)blockIdx.y * kPfSpan;
+    const int64_t q0 = (int64_t)blockIdx.x * kPfWQ + wave * kPfQ;  // this wave's queries
+    const int32_t span0 = (int32_t)blockIdx.y * (kPfCStride * kPfCSteps);
     int32_t tmax, tmin, pos[kPfQB];
-    pf_tile_pos(q_pos, nq, t_cap, q0, n16, pos, tmax, tmin);
-    if (span0 > tmax) return;
+    pf_tile_pos(q_pos, nq, t_cap, min(q0, (int64_t)nq - 1), n16, pos, tmax, tmin);
+    if (q0 >= nq) tmax = -1;  // a wave past the last query computes nothing
+    if (lane == 0) wmax[wave] = tmax;
+    __syncthreads();
+    const int32_t T = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    if (span0 > T) return;  // uniform over the workgroup
+    const int nsteps = min(kPfCSteps, (min(T, t_cap - 1) - span0) / kPfCStride + 1);
     pf_bf16x8 qf[kPfQB][2];
-    pf_load_q(q_idx, nq, q0, n16, g, qf);
+    pf_load_q(q_idx, nq, q0 < nq ? q0 : 0, n16, g, qf);
     const float NEG = -__builtin_inff();
-    pf_sweep<kPfSpan>(kseq, t_cap, span0 + wave * 64, tmax, n16, g,
-             [&](const pf_bf16x8 (&kf)[4][2], int32_t t0) {
-                 float m[kPfQB];
+    auto step = [&](const uint32_t* buf, int32_t t0) {
+        if (t0 > tmax) return;  // wave-uniform
+        pf_bf16x8 kf[4][2];
+        pf_tile_frag(buf, n16, g, kf);
+        float m[kPfQB];
 #pragma unroll
-                 for (int i = 0; i < kPfQB; ++i) m[i] = NEG;
-                 if (t0 + 63 <= tmin)  // no query of the tile masks these positions
-                     pf_cmax_step<false>(kf, qf, t0, g, pos, m);
-                 else
-                     pf_cmax_step<true>(kf, qf, t0, g, pos, m);
-                 const int64_t c0 = t0 / kPfChunk + g;
+        for (int i = 0; i < kPfQB; ++i) m[i] = NEG;
+        if (t0 + 63 <= tmin)  // no query of the wave masks these positions
+            pf_cmax_step<false>(kf, qf, t0, g, pos, m);
+        else
+            pf_cmax_step<true>(kf, qf, t0, g, pos, m);
+        const int64_t c0 = 4 * (t0 / kPfCStride) + g;
 #pragma unroll
-                 for (int i = 0; i < kPfQB; ++i) {
-                     const int64_t qq = q0 + 16 * i + n16;
-                     if (qq < nq) cmax[qq * ldc + c0] = score_key(m[i]);
-                 }
-             });
+        for (int i = 0; i < kPfQB; ++i) {
+            const int64_t qq = q0 + 16 * i + n16;
+            if (qq < nq) cmax[qq * ldc + c0] = score_key(m[i]);
+        }
+    };
+    // tile s is read from LDS while tiles s + 1 and s + 2 wait in registers.
+    // After a step its successor goes to the other buffer (whose readers
+    // finished with it before the previous barrier) and the freed registers
+    // request the tile three steps ahead.  Step 0 is peeled: it is where the
+    // query fragments are first used, so inside the loop the only loads in
+    // flight are tiles and the compiler's waits count only those.
+    constexpr int D = kPfCStride;
+    uint4 a0, a1, b0, b1, c0, c1;
+    pf_tile_load(kseq, t_cap, span0, tid, a0, a1);
+    pf_tile_load(kseq, t_cap, span0 + D, tid, b0, b1);
+    pf_tile_load(kseq, t_cap, span0 + 2 * D, tid, c0, c1);
+    pf_tile_store(tile[0], tid, a0, a1);
+    lds_barrier();
+    step(tile[0], span0);
+    pf_tile_store(tile[1], tid, b0, b1);                    // tile 1
+    pf_tile_load(kseq, t_cap, span0 + 3 * D, tid, b0, b1);  // tile 3
+    lds_barrier();
+    for (int s = 1; s < nsteps; s += 2) {  // tile[1] holds tile s, c tile s + 1, b tile s + 2
+        const int32_t t0 = span0 + D * s;
+        step(tile[1], t0);
+        pf_tile_store(tile[0], tid, c0, c1);                  // tile s + 1
+        pf_tile_load(kseq, t_cap, t0 + 3 * D, tid, c0, c1);  // tile s + 3
+        lds_barrier();
+        if (s + 1 >= nsteps) break;
+        step(tile[0], t0 + D);
+        pf_tile_store(tile[1], tid, b0, b1);                  // tile s + 2
+        pf_tile_load(kseq, t_cap, t0 + 4 * D, tid, b0, b1);  // tile s + 4
+        lds_barrier();
+    }
 }
 
-// Chunks holding at least one position <= t.
+// Sampled chunks holding at least one position <= t: step i (positions
+// kPfCStride i ..) has chunk g's first position at kPfCStride i + 4 g.
 __device__ __forceinline__ int64_t pf_nchunks(int64_t t) {
     if (t < 0) return 0;
-    const int64_t g = (t & 63) >> 2;
-    return 4 * (t >> 6) + (g < 3 ? g : 3) + 1;
+    const int64_t g = (t % kPfCStride) >> 2;
+    return 4 * (t / kPfCStride) + (g < 3 ? g : 3) + 1;
+}
+
+// Sampled chunk maxima whose m-th largest is the threshold: about 1.3 k
+// scores of the row reach it (the sample is 1/8 of the positions and a
+// chunk's maximum stands for one score), so a list shorter than k -- which
+// sends the query to the exact recompute -- is a rare event for scores
+// without structure.
+__device__ __forceinline__ int32_t pf_sample_rank(int32_t k) {
+    return (13 * k + 79) / 80;
 }
 
 // ---- 2. thresholds -----------------------------------------------------------
@@ -228,8 +315,9 @@ __global__ __launch_bounds__(256) void k_pf_thresh(const uint32_t* __restrict__ 
     const int q = blockIdx.x, tid = threadIdx.x;
     const int64_t t = pf_clamp_pos(q_pos[q], t_cap);
     const int64_t nc = pf_nchunks(t);
-    uint32_t thr = 1u;  // fewer chunks than k: every valid position is a candidate
-    if (nc >= k) {
+    const int32_t m = pf_sample_rank(k);
+    uint32_t thr = 1u;  // fewer sampled chunks than m: every valid position is a candidate
+    if (nc >= m) {
         // ldc is a multiple of 4 and the row is 16-byte aligned: stage whole
         // uint4s (keys past nc are never read), eight loads in flight per thread
         const uint4* src = reinterpret_cast<const uint4*>(cmax + (int64_t)q * ldc);
@@ -247,7 +335,7 @@ __global__ __launch_bounds__(256) void k_pf_thresh(const uint32_t* __restrict__ 
         __syncthreads();
         uint32_t tau;
         int need;
-        lds_kth<256>(pf_keys, (int)nc, k, 0, sh.hist, sh.res, tau, need);
+        lds_kth<256>(pf_keys, (int)nc, m, 0, sh.hist, sh.res, tau, need);
         thr = need > 0 ? tau : tau + 1u;
         if (thr < 1u) thr = 1u;
     }
@@ -347,22 +435,32 @@ __global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ 
 #pragma unroll
                      for (int i = 0; i < kPfQB; ++i) c[i] = pf_tile(kf[j], qf[i]);
                      const uint32_t tag = (((uint32_t)t0 + 16u * j + 4u * g) << 7) | (uint32_t)n16;
+                     // float pre-filter (passes every key >= thr, and NaN): one
+                     // bit per query block, then one wave scan places the
+                     // lane's passing tiles in the queue
+                     uint32_t bits = 0u;
 #pragma unroll
                      for (int i = 0; i < kPfQB; ++i) {
-                         // float pre-filter: passes every key >= thr (and NaN)
                          const bool h = !(c[i][0] < th[i]) || !(c[i][1] < th[i]) ||
                                         !(c[i][2] < th[i]) || !(c[i][3] < th[i]);
-                         const uint64_t mask = __ballot(h);
-                         if (mask) {
-                             if (h) {
-                                 const int off = qn + lanes_below(mask);
+                         bits |= (uint32_t)h << i;
+                     }
+                     const int mine = __popc(bits);
+                     const int incl = wave_scan_dpp(mine);
+                     const int tot = __builtin_amdgcn_readlane(incl, 63);
+                     if (tot) {  // wave-uniform
+                         int off = qn + incl - mine;
+#pragma unroll
+                         for (int i = 0; i < kPfQB; ++i) {
+                             if ((bits >> i) & 1u) {
                                  sh.qscore[wave][off] =
                                      make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
                                                 __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
                                  sh.qtag[wave][off] = tag + 16u * i;
+                                 ++off;
                              }
-                             qn += __popcll(mask);
                          }
+                         qn += tot;
                      }
                      if (qn > kPfQueue - kPfQB * 64) {  // room for the next j-block's entries
                          pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
@@ -446,7 +544,8 @@ __global__ __launch_bounds__(kPfSelNT) void k_pf_select(const uint16_t* __restri
         return;
     }
     const uint32_t n = cnt[q];
-    if (n > (uint32_t)cap) {
+    // too many candidates for the list, or too few to certify the selection
+    if (n > (uint32_t)cap || ((int64_t)n < k && (int64_t)n < t + 1)) {
         pf_select_recompute(kseq, q_idx + (int64_t)q * kIdxDim, t, k, dst, sh);
         return;
     }
@@ -589,7 +688,7 @@ hipError_t launch_score_mq(const CacheView& c, int32_t seq, const uint16_t* q_id
 }
 
 size_t prefill_topk_ws_bytes(int32_t nq, int64_t t_cap) {
-    const int64_t ldc = ((t_cap + kPfChunk - 1) / kPfChunk + 3) / 4 * 4;
+    const int64_t ldc = 4 * ((t_cap + kPfCStride - 1) / kPfCStride);
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     return al((size_t)nq * ldc * 4) + 3 * al((size_t)nq * 4) + al((size_t)nq * kPfCap * 8);
 }
@@ -598,7 +697,7 @@ hipError_t launch_prefill_topk(const CacheView& c, int32_t seq, const uint16_t* 
                                const int32_t* q_pos, int32_t nq, int32_t k, int32_t* sel, void* ws,
                                hipStream_t s) {
     if (nq == 0) return hipSuccess;
-    const int64_t ldc = ((c.t_cap + kPfChunk - 1) / kPfChunk + 3) / 4 * 4;
+    const int64_t ldc = 4 * ((c.t_cap + kPfCStride - 1) / kPfCStride);
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     char* p = static_cast<char*>(ws);
     uint32_t* cmax = reinterpret_cast<uint32_t*>(p);
@@ -611,12 +710,13 @@ hipError_t launch_prefill_topk(const CacheView& c, int32_t seq, const uint16_t* 
     p += al((size_t)nq * 4);
     uint2* cand = reinterpret_cast<uint2*>(p);
     const uint16_t* kseq = c.k_idx + (int64_t)seq * c.t_cap * kIdxDim;
-    const dim3 grid((uint32_t)((nq + kPfQ - 1) / kPfQ), (uint32_t)((c.t_cap + kPfSpan - 1) / kPfSpan));
+    const dim3 grid((uint32_t)((nq + kPfWQ - 1) / kPfWQ),
+                    (uint32_t)((c.t_cap + kPfCStride * kPfCSteps - 1) / (kPfCStride * kPfCSteps)));
     hipLaunchKernelGGL(k_pf_cmax, grid, dim3(256), 0, s, kseq, (int32_t)c.t_cap, q_idx, q_pos, nq, cmax,
                        ldc);
     hipLaunchKernelGGL(k_pf_thresh, dim3(nq), dim3(256), (size_t)ldc * 4, s, cmax, ldc, q_pos,
                        c.t_cap, k, thr_f, thr_k, cnt);
-    const dim3 fgrid(grid.x, (uint32_t)((c.t_cap + kPfFiltSpan - 1) / kPfFiltSpan));
+    const dim3 fgrid((uint32_t)((nq + kPfQ - 1) / kPfQ), (uint32_t)((c.t_cap + kPfFiltSpan - 1) / kPfFiltSpan));
     hipLaunchKernelGGL(k_pf_filter, fgrid, dim3(256), 0, s, kseq, (int32_t)c.t_cap, q_idx, q_pos, nq, thr_f,
                        thr_k, cnt, cand, kPfCap);
     const size_t nw = (size_t)((c.t_cap + 31) / 32);
