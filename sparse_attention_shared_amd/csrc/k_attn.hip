@@ -56,13 +56,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // ---- shared by both attention kernels --------------------------------------
-// V^T tile of one wave: 128 dim rows of 32 entry slots (bf16), 16 dwords per
-// row, rows skewed by 16 dwords every 32 rows so that the four lane groups of
-// a transposing store land in different banks.
-constexpr int kVtRow = 16;
-constexpr int kVtWave = kHeadDim * kVtRow + 4 * kVtRow;
+// V^T tile of one wave: 128 dim rows of 32 entry slots (bf16 pairs, 16
+// dwords) on a 20-dword pitch, rows skewed by 16 dwords every 32 rows.  The
+// pitch puts the 16 rows a lane group reads (one 16-byte read each) on 16
+// disjoint groups of 4 banks; the skew puts the four lane groups of a
+// transposing store (rows 32 g + ..) on disjoint banks.
+constexpr int kVtRow = 20;
+constexpr int kVtWave = kHeadDim * kVtRow + 4 * 16;
 
-__device__ __forceinline__ int vt_addr(int d) { return d * kVtRow + (d >> 5) * kVtRow; }
+__device__ __forceinline__ int vt_addr(int d) { return d * kVtRow + (d >> 5) * 16; }
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
@@ -434,7 +436,7 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
     // sel_of(e) reads the selection slot (-1 past the selection); locate()
     // turns it into a kind (0 none, 1 global FP4, 2 global bf16, 3 local
     // bf16) and a row index.
-    auto sel_of = [&](int64_t e) -> int64_t { return e < k ? (int64_t)sel[(int64_t)qi * k + e] : -1; };
+    auto sel_of = [&](int64_t e) -> int32_t { return e < k ? sel[(int64_t)qi * k + e] : -1; };
     auto locate = [&](int64_t e, int64_t j, int& kind, int64_t& row) {
         kind = 0;
         row = 0;
@@ -465,16 +467,20 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
     // One tile once its K fragments are in kf and its V^T is in LDS: S^T = K
     // Q^T (lane: head n16, rows 4 g + r of MFMA tile u = slot 8 g + 2 r + u),
     // the online softmax, and O^T += V^T P^T (lane: head n16, dims
-    // 16 t8 + 4 g + r, so the rescale by alpha is lane-local).
+    // 16 t8 + 4 g + r, so the rescale by alpha is lane-local).  The reference
+    // maximum m_run (scaled, log2 units) moves only when a head's tile
+    // maximum passes it by more than 8, so most tiles skip the rescale and
+    // p = 2^(s zs - m_run) stays below 2^8 (exact up to bf16/fp32 rounding:
+    // the softmax does not depend on the reference).
     auto consume = [&](const bf16x8_t (&kf)[2][4], uint64_t vm0, uint64_t vm1) {
-        float sv[2][4];
+        float sv[2][4];  // raw scores
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][kb], qf[kb], z, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sv[u][r] = z[r] * zs;
+            for (int r = 0; r < 4; ++r) sv[u][r] = z[r];
         }
         if ((vm0 & vm1) != 0xFFFFull) {  // some slot of the tile is empty: -inf
 #pragma unroll
@@ -487,22 +493,13 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                          fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = m_new == NEG ? 0.f : m_new;  // no valid slot yet: every p is 0
-        // v_exp_f32: 2^-inf = 0; results below 2^-126 flush to 0
-        const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_use);
-        float p[2][4];
-        float ps = 0.f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[u][r] = __builtin_amdgcn_exp2f(sv[u][r] - m_use);
-                ps += p[u][r];
-            }
-        l_part = fmaf(l_part, alpha, ps);
-        m_run = m_new;
-        if (__ballot(alpha != 1.f)) {
+        const float ms = mt * zs;            // zs > 0: the scaled tile maximum
+        const bool bump = ms > m_run + 8.f;  // m_run = -inf: any valid slot
+        if (__ballot(bump)) {
+            // v_exp_f32: 2^-inf = 0 (the first valid tile of a head)
+            const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - ms) : 1.f;
+            if (bump) m_run = ms;
+            l_part *= alpha;
 #pragma unroll
             for (int t8 = 0; t8 < 8; ++t8) {
                 o[t8][0] *= alpha;
@@ -511,6 +508,17 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                 o[t8][3] *= alpha;
             }
         }
+        const float nm = m_run == NEG ? 0.f : -m_run;  // no valid slot yet: every p is 0
+        float p[2][4];
+        float ps = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[u][r] = __builtin_amdgcn_exp2f(fmaf(sv[u][r], zs, nm));  // 2^-inf = 0
+                ps += p[u][r];
+            }
+        l_part += ps;
         const bf16x8_t pf = as_bf16x8(__builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][0], (__bf16)p[1][0]}),
                                       __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][1], (__bf16)p[1][1]}),
                                       __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][2], (__bf16)p[1][2]}),
@@ -529,21 +537,21 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
     const int n_fast = (c.fp4 && t >= 0) ? k / 32 : 0;
     const uint8_t* codes = static_cast<const uint8_t*>(c.data) + (int64_t)max(seq, 0) * c.t_cap * kRowCodes;
     const uint8_t* scl = c.scales ? c.scales + (int64_t)max(seq, 0) * c.t_cap * kRowScales : nullptr;
-    auto fetch = [&](int64_t j, RowRaw& r) {
-        if (j >= 0 && j <= t) {
-            r.k = *reinterpret_cast<const uint4*>(codes + j * kRowCodes + 16 * g);
-            r.v = *reinterpret_cast<const uint4*>(codes + j * kRowCodes + 64 + 16 * g);
-            const uint2 sc = *reinterpret_cast<const uint2*>(scl + j * kRowScales);
-            r.sk = (sc.x >> (8 * g)) & 0xFFu;
-            r.sv = (sc.y >> (8 * g)) & 0xFFu;
-        } else {
-            r.k = r.v = make_uint4(0, 0, 0, 0);
-            r.sk = r.sv = 127u;
-        }
+    // An empty slot reads row 0 (no branch around the loads) with scale 1:
+    // its codes are finite and its p is 0, so it adds nothing.
+    const int32_t t32 = (int32_t)t;  // positions fit 32 bits (t_cap <= 2^31)
+    auto fetch = [&](int32_t j, RowRaw& r) {
+        const bool ok = j >= 0 && j <= t32;
+        const int64_t jj = ok ? j : 0;
+        r.k = *reinterpret_cast<const uint4*>(codes + jj * kRowCodes + 16 * g);
+        r.v = *reinterpret_cast<const uint4*>(codes + jj * kRowCodes + 64 + 16 * g);
+        const uint2 sc = *reinterpret_cast<const uint2*>(scl + jj * kRowScales);
+        r.sk = ok ? (sc.x >> (8 * g)) & 0xFFu : 127u;
+        r.sv = ok ? (sc.y >> (8 * g)) & 0xFFu : 127u;
     };
     {
         RowRaw raw[2];
-        int64_t jc[2] = {-1, -1}, jn[2] = {-1, -1};
+        int32_t jc[2] = {-1, -1}, jn[2] = {-1, -1};
         int tile = wave;
         if (tile < n_fast) {
 #pragma unroll
@@ -557,8 +565,8 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
             }
         }
         for (; tile < n_fast; tile += kLW) {
-            const uint64_t vm0 = __ballot(jc[0] >= 0 && jc[0] <= t) & 0xFFFFull;
-            const uint64_t vm1 = __ballot(jc[1] >= 0 && jc[1] <= t) & 0xFFFFull;
+            const uint64_t vm0 = __ballot(jc[0] >= 0 && jc[0] <= t32) & 0xFFFFull;
+            const uint64_t vm1 = __ballot(jc[1] >= 0 && jc[1] <= t32) & 0xFFFFull;
             bf16x8_t kf[2][4];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {

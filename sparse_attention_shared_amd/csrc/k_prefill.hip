@@ -586,12 +586,39 @@ __global__ __launch_bounds__(kPfSelNT) void k_pf_select(const uint16_t* __restri
             sh.spos[rank] = (int32_t)p;
         }
     }
+    // every candidate is at or above the threshold, so their keys share
+    // their top bits; the radix works on the bits below that common prefix
+    // (shifted up; the set low bit keeps every key nonzero and the order
+    // unchanged), so its first digit spreads over the whole histogram
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+        if (cv[u].x != 0xFFFFFFFFu) {
+            kmin = min(kmin, cv[u].y);
+            kmax = max(kmax, cv[u].y);
+        }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    }
+    if ((tid & 63) == 0) {
+        sh.wtmp[tid >> 6] = (int)kmin;
+        sh.wtmp[kPfSelNT / 64 + (tid >> 6)] = (int)kmax;
+    }
     __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kPfSelNT / 64; ++w) {
+        kmin = min(kmin, (uint32_t)sh.wtmp[w]);
+        kmax = max(kmax, (uint32_t)sh.wtmp[kPfSelNT / 64 + w]);
+    }
+    __syncthreads();  // wtmp is reused by the ordered write
+    const int sp = kmin <= kmax ? min(31, __clz((int)(kmin ^ kmax))) : 0;
+    auto K = [&](int64_t i) { return (sh.skey[i] << sp) | 1u; };
     uint32_t tau;
     int need;
-    lds_kth<kPfSelNT>(sh.skey, (int)n, k, 0, sh.hist, sh.res, tau, need);
-    ordered_write<kPfSelNT>([&](int64_t i) { return sh.skey[i]; }, (int64_t)n, tau, need, sh.spos, k,
-                            dst, sh.wtmp);
+    kth_fn<kPfSelNT>(K, (int64_t)n, k, 0, 0u, sh.hist, sh.res, tau, need);
+    ordered_write<kPfSelNT>(K, (int64_t)n, tau, need, sh.spos, k, dst, sh.wtmp);
 }
 
 // Multi-query scores of a prefill chunk on one sequence: S = Q_I K_I^T, a
