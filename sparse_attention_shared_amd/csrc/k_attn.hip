@@ -386,9 +386,37 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
 // k-step kb is dims 32 g + 8 kb .. + 8 (the Q fragment uses the same map).
 constexpr int kLW = 4;                       // waves per workgroup
 
+// V of one wave's 32 entries, row-major (entry, 128 bf16 dims) on a 72-dword
+// (288-byte) pitch.  The PV product reads it transposed with
+// ds_read_b64_tr_b16: within a 16-lane group, lane i receives element i % 4
+// of the 8-byte blocks addressed by lanes 4 k + i / 4 (k = 0..3), so lane
+// (n16, g) addressing row 8 g + 4 h + n16 / 4 at dims 16 t8 + 4 (n16 % 4)
+// receives dim 16 t8 + n16 of rows 8 g + 4 h .. + 3: the V^T operand of
+// the MFMA.  The pitch puts the four rows a group reads on disjoint banks.
+constexpr int kVrRow = 72;
+constexpr int kVrWave = 32 * kVrRow;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void vr_store_row(uint32_t* vr, int slot, int g, const uint32_t (&d)[16]) {
+    uint32_t* row = vr + slot * kVrRow + 16 * g;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<uint4*>(row + 4 * c) = make_uint4(d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]);
+}
+
+// The V^T operand of dims 16 t8 .. + 16 (A of O^T += V^T P^T).
+__device__ __forceinline__ bf16x8_t vr_frag(const uint32_t* vr, int t8, int n16, int g) {
+    const uint32_t* p0 = vr + (8 * g + (n16 >> 2)) * kVrRow + 8 * t8 + 2 * (n16 & 3);
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+    const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+    const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * kVrRow));
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    return as_bf16x8(ua.x, ua.y, ub.x, ub.y);
+}
+
 struct LoopLds {
     union {
-        uint32_t vt[kLW][kVtWave];
+        uint32_t vr[kLW][kVrWave];
         float obuf[kLW][kHeads][kHeadDim + 4];
     } u;
     float m[kLW][kHeads];
@@ -406,7 +434,7 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
     const int qi = blockIdx.x, tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n16 = lane & 15, g = lane >> 4;
-    uint32_t* vt = sh.u.vt[wave];
+    uint32_t* vr = sh.u.vr[wave];
 
     const int32_t seq = q_seq ? q_seq[qi] : qi;
     int64_t t = q_pos[qi];
@@ -524,10 +552,8 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                                       __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][2], (__bf16)p[1][2]}),
                                       __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][3], (__bf16)p[1][3]}));
 #pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) {
-            const uint4 vv = *reinterpret_cast<const uint4*>(&vt[vt_addr(16 * t8 + n16) + 4 * g]);
-            o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv.x, vv.y, vv.z, vv.w), pf, o[t8], 0, 0, 0);
-        }
+        for (int t8 = 0; t8 < 8; ++t8)
+            o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr_frag(vr, t8, n16, g), pf, o[t8], 0, 0, 0);
     };
 
     // ---- tiles inside the selection of an FP4 cache: every slot is a global
@@ -577,18 +603,14 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                     kf[u][kb] = as_bf16x8(cvt_fp4x2(w[kb], sc, 0), cvt_fp4x2(w[kb], sc, 1),
                                           cvt_fp4x2(w[kb], sc, 2), cvt_fp4x2(w[kb], sc, 3));
             }
-            {
-                const float s0 = e8m0_value(raw[0].sv), s1 = e8m0_value(raw[1].sv);
-                const uint32_t w0v[4] = {raw[0].v.x, raw[0].v.y, raw[0].v.z, raw[0].v.w};
-                const uint32_t w1v[4] = {raw[1].v.x, raw[1].v.y, raw[1].v.z, raw[1].v.w};
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const uint32_t va = cvt_fp4x2(w0v[i >> 2], s0, i & 3);
-                    const uint32_t vb = cvt_fp4x2(w1v[i >> 2], s1, i & 3);
-                    const int d = 32 * g + 2 * i;
-                    vt[vt_addr(d) + n16] = __builtin_amdgcn_perm(vb, va, 0x05040100u);
-                    vt[vt_addr(d + 1) + n16] = __builtin_amdgcn_perm(vb, va, 0x07060302u);
-                }
+            for (int u = 0; u < 2; ++u) {  // V rows of slots 2 n16 + u, dims 32 g .. + 32
+                const float sv = e8m0_value(raw[u].sv);
+                const uint32_t wv[4] = {raw[u].v.x, raw[u].v.y, raw[u].v.z, raw[u].v.w};
+                uint32_t d[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) d[i] = cvt_fp4x2(wv[i >> 2], sv, i & 3);
+                vr_store_row(vr, 2 * n16 + u, g, d);
             }
             const int next = tile + kLW;
             if (next < n_fast) {
@@ -643,7 +665,8 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                 for (int kb = 0; kb < 4; ++kb) kf[u][kb] = as_bf16x8(0u, 0u, 0u, 0u);
             }
         }
-        // V^T eight dims at a time
+        // V rows eight dims at a time
+        uint32_t vd[2][16];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             uint32_t vv[2][4];
@@ -668,12 +691,12 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d = 32 * g + 8 * i4 + 2 * i;
-                vt[vt_addr(d) + n16] = __builtin_amdgcn_perm(vv[1][i], vv[0][i], 0x05040100u);
-                vt[vt_addr(d + 1) + n16] = __builtin_amdgcn_perm(vv[1][i], vv[0][i], 0x07060302u);
-            }
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vd[u][4 * i4 + i] = vv[u][i];
         }
+        vr_store_row(vr, 2 * n16, g, vd[0]);
+        vr_store_row(vr, 2 * n16 + 1, g, vd[1]);
         consume(kf, vm0, vm1);
     }
     // ---- combine the waves
