@@ -252,8 +252,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     }
     // ---- softmax over the workgroup's 256 entries: wave maxima -> LDS, then
     // every wave takes the workgroup maximum per head
-    float m = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    // chained from -inf (canonical), so it compiles to v_max3_f32 only
+    float m = fmaxf(fmaxf(NEG, s[0][0]), s[0][1]);
+    m = fmaxf(fmaxf(m, s[0][2]), s[0][3]);
+    m = fmaxf(fmaxf(m, s[1][0]), s[1][1]);
+    m = fmaxf(fmaxf(m, s[1][2]), s[1][3]);
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
     if (g == 0) sh.m[wave][n16] = m;
@@ -517,8 +520,10 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                 if (!((vm1 >> (4 * g + r)) & 1)) sv[1][r] = NEG;
             }
         }
-        float mt = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                         fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+        float mt = fmaxf(fmaxf(NEG, sv[0][0]), sv[0][1]);  // v_max3_f32 chain
+        mt = fmaxf(fmaxf(mt, sv[0][2]), sv[0][3]);
+        mt = fmaxf(fmaxf(mt, sv[1][0]), sv[1][1]);
+        mt = fmaxf(fmaxf(mt, sv[1][2]), sv[1][3]);
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float ms = mt * zs;            // zs > 0: the scaled tile maximum

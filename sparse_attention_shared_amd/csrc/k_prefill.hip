@@ -35,7 +35,8 @@ constexpr int kPfQB = 8;        // 16-query blocks per wave
 constexpr int kPfQ = 16 * kPfQB; // queries per workgroup tile (every wave takes all of them)
 constexpr int kPfCStride = 512; // positions between sampled 64-position steps
 constexpr int kPfCSteps = 4;    // sampled steps per chunk-maximum workgroup
-constexpr int kPfFiltSpan = 512;   // positions per filter workgroup (about 11 candidates per query)
+constexpr int kPfFiltSpan = 4096;  // positions per filter workgroup
+constexpr int kPfFiltSeg = 512;    // positions per LDS list flush (about 11 candidates per query)
 constexpr int kPfChunk = 16;    // positions per chunk maximum
 constexpr int kPfLB = 24;       // LDS candidate slots per query in the filter
 constexpr int kPfSelNT = 512;
@@ -161,7 +162,10 @@ __device__ __forceinline__ void pf_cmax_step(const pf_bf16x8 (&kf)[4][2],
                 for (int r = 0; r < 4; ++r)
                     if (tt + r > pos[i]) c[i][r] = NEG;
             }
-            m[i] = fmaxf(m[i], fmaxf(fmaxf(c[i][0], c[i][1]), fmaxf(c[i][2], c[i][3])));
+            // chained from the running maximum (already canonical): two
+            // v_max3_f32, no quieting of the MFMA results
+            m[i] = fmaxf(fmaxf(m[i], c[i][0]), c[i][1]);
+            m[i] = fmaxf(fmaxf(m[i], c[i][2]), c[i][3]);
         }
     }
 }
@@ -426,59 +430,67 @@ __global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ 
     pf_bf16x8 qf[kPfQB][2];
     pf_load_q(q_idx, nq, q0, n16, g, qf);
     __syncthreads();
-    int qn = 0;  // entries in this wave's queue (wave-uniform)
-    pf_sweep<kPfFiltSpan>(kseq, t_cap, span0 + wave * 64, tmax, n16, g,
-             [&](const pf_bf16x8 (&kf)[4][2], int32_t t0) {
+    // the span in segments of kPfFiltSeg positions; after each one the
+    // per-query LDS lists go to the global lists, so their capacity covers a
+    // segment while the workgroup's set-up covers the whole span
+    for (int32_t seg0 = span0; seg0 < span0 + kPfFiltSpan && seg0 <= tmax; seg0 += kPfFiltSeg) {
+        int qn = 0;  // entries in this wave's queue (wave-uniform)
+        pf_sweep<kPfFiltSeg>(kseq, t_cap, seg0 + wave * 64, tmax, n16, g,
+                 [&](const pf_bf16x8 (&kf)[4][2], int32_t t0) {
 #pragma unroll
-                 for (int j = 0; j < 4; ++j) {
-                     pf_f32x4 c[kPfQB];
+                     for (int j = 0; j < 4; ++j) {
+                         pf_f32x4 c[kPfQB];
 #pragma unroll
-                     for (int i = 0; i < kPfQB; ++i) c[i] = pf_tile(kf[j], qf[i]);
-                     const uint32_t tag = (((uint32_t)t0 + 16u * j + 4u * g) << 7) | (uint32_t)n16;
-                     // float pre-filter (passes every key >= thr, and NaN): one
-                     // bit per query block, then one wave scan places the
-                     // lane's passing tiles in the queue
-                     uint32_t bits = 0u;
-#pragma unroll
-                     for (int i = 0; i < kPfQB; ++i) {
-                         const bool h = !(c[i][0] < th[i]) || !(c[i][1] < th[i]) ||
-                                        !(c[i][2] < th[i]) || !(c[i][3] < th[i]);
-                         bits |= (uint32_t)h << i;
-                     }
-                     const int mine = __popc(bits);
-                     const int incl = wave_scan_dpp(mine);
-                     const int tot = __builtin_amdgcn_readlane(incl, 63);
-                     if (tot) {  // wave-uniform
-                         int off = qn + incl - mine;
+                         for (int i = 0; i < kPfQB; ++i) c[i] = pf_tile(kf[j], qf[i]);
+                         const uint32_t tag = (((uint32_t)t0 + 16u * j + 4u * g) << 7) | (uint32_t)n16;
+                         // float pre-filter (passes every key >= thr, and NaN):
+                         // one bit per query block, then one wave scan places
+                         // the lane's passing tiles in the queue
+                         uint32_t bits = 0u;
 #pragma unroll
                          for (int i = 0; i < kPfQB; ++i) {
-                             if ((bits >> i) & 1u) {
-                                 sh.qscore[wave][off] =
-                                     make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
-                                                __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
-                                 sh.qtag[wave][off] = tag + 16u * i;
-                                 ++off;
-                             }
+                             const bool h = !(c[i][0] < th[i]) || !(c[i][1] < th[i]) ||
+                                            !(c[i][2] < th[i]) || !(c[i][3] < th[i]);
+                             bits |= (uint32_t)h << i;
                          }
-                         qn += tot;
+                         const int mine = __popc(bits);
+                         const int incl = wave_scan_dpp(mine);
+                         const int tot = __builtin_amdgcn_readlane(incl, 63);
+                         if (tot) {  // wave-uniform
+                             int off = qn + incl - mine;
+#pragma unroll
+                             for (int i = 0; i < kPfQB; ++i) {
+                                 if ((bits >> i) & 1u) {
+                                     sh.qscore[wave][off] =
+                                         make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
+                                                    __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
+                                     sh.qtag[wave][off] = tag + 16u * i;
+                                     ++off;
+                                 }
+                             }
+                             qn += tot;
+                         }
+                         if (qn > kPfQueue - kPfQB * 64) {  // room for the next j-block's entries
+                             pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
+                             qn = 0;
+                         }
                      }
-                     if (qn > kPfQueue - kPfQB * 64) {  // room for the next j-block's entries
-                         pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
-                         qn = 0;
-                     }
-                 }
-             });
-    pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
-    __syncthreads();
-    if (tid < kPfQ) {
-        const int m = min(sh.n[tid], kPfLB);
-        sh.base[tid] = m > 0 ? (int)atomicAdd(&cnt[q0 + tid], (uint32_t)m) : 0;
-    }
-    __syncthreads();
-    for (int e = tid; e < kPfQ * kPfLB; e += 256) {
-        const int ql = e / kPfLB, j = e % kPfLB;
-        if (j < min(sh.n[ql], kPfLB) && sh.base[ql] + j < cap)
-            cand[(q0 + ql) * cap + sh.base[ql] + j] = sh.buf[ql][j];
+                 });
+        pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
+        __syncthreads();
+        if (tid < kPfQ) {
+            const int m = min(sh.n[tid], kPfLB);
+            sh.base[tid] = m > 0 ? (int)atomicAdd(&cnt[q0 + tid], (uint32_t)m) : 0;
+        }
+        __syncthreads();
+        for (int e = tid; e < kPfQ * kPfLB; e += 256) {
+            const int ql = e / kPfLB, j = e % kPfLB;
+            if (j < min(sh.n[ql], kPfLB) && sh.base[ql] + j < cap)
+                cand[(q0 + ql) * cap + sh.base[ql] + j] = sh.buf[ql][j];
+        }
+        __syncthreads();
+        if (tid < kPfQ) sh.n[tid] = 0;
+        __syncthreads();
     }
 }
 
