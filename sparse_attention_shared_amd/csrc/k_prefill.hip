@@ -449,9 +449,10 @@ __global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ 
                          uint32_t bits = 0u;
 #pragma unroll
                          for (int i = 0; i < kPfQB; ++i) {
-                             const bool h = !(c[i][0] < th[i]) || !(c[i][1] < th[i]) ||
-                                            !(c[i][2] < th[i]) || !(c[i][3] < th[i]);
-                             bits |= (uint32_t)h << i;
+                             // bitwise, not ||: no short-circuit branches
+                             const uint32_t h = (uint32_t)!(c[i][0] < th[i]) | (uint32_t)!(c[i][1] < th[i]) |
+                                                (uint32_t)!(c[i][2] < th[i]) | (uint32_t)!(c[i][3] < th[i]);
+                             bits |= h << i;
                          }
                          const int mine = __popc(bits);
                          const int incl = wave_scan_dpp(mine);
