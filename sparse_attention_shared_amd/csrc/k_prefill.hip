@@ -430,68 +430,85 @@ __global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ 
     pf_bf16x8 qf[kPfQB][2];
     pf_load_q(q_idx, nq, q0, n16, g, qf);
     __syncthreads();
-    // the span in segments of kPfFiltSeg positions; after each one the
-    // per-query LDS lists go to the global lists, so their capacity covers a
-    // segment while the workgroup's set-up covers the whole span
-    for (int32_t seg0 = span0; seg0 < span0 + kPfFiltSpan && seg0 <= tmax; seg0 += kPfFiltSeg) {
-        int qn = 0;  // entries in this wave's queue (wave-uniform)
-        pf_sweep<kPfFiltSeg>(kseq, t_cap, seg0 + wave * 64, tmax, n16, g,
-                 [&](const pf_bf16x8 (&kf)[4][2], int32_t t0) {
+    // One pass over the span, the next step's key fragments in flight while
+    // a step computes.  Every kPfFiltSeg positions (two steps of the four
+    // waves) the per-query LDS lists go to the global lists, so their
+    // capacity covers a segment while the workgroup's set-up covers the whole
+    // span.  Every wave runs the same number of steps (the barriers of the
+    // flush), computing only the steps that hold a position <= tmax.
+    constexpr int kSegSteps = kPfFiltSeg / 256;
+    const int nsteps = min(kPfFiltSpan / 256, (min(tmax, t_cap - 1) - span0) / 256 + 1);
+    int qn = 0;  // entries in this wave's queue (wave-uniform)
+    pf_bf16x8 kn[4][2];
+    pf_load_k(kseq, t_cap, span0 + wave * 64, n16, g, kn);
+    for (int s = 0; s < nsteps; ++s) {
+        const int32_t t0 = span0 + wave * 64 + 256 * s;
+        pf_bf16x8 kf[4][2];
 #pragma unroll
-                     for (int j = 0; j < 4; ++j) {
-                         pf_f32x4 c[kPfQB];
-#pragma unroll
-                         for (int i = 0; i < kPfQB; ++i) c[i] = pf_tile(kf[j], qf[i]);
-                         const uint32_t tag = (((uint32_t)t0 + 16u * j + 4u * g) << 7) | (uint32_t)n16;
-                         // float pre-filter (passes every key >= thr, and NaN):
-                         // one bit per query block, then one wave scan places
-                         // the lane's passing tiles in the queue
-                         uint32_t bits = 0u;
-#pragma unroll
-                         for (int i = 0; i < kPfQB; ++i) {
-                             // bitwise, not ||: no short-circuit branches
-                             const uint32_t h = (uint32_t)!(c[i][0] < th[i]) | (uint32_t)!(c[i][1] < th[i]) |
-                                                (uint32_t)!(c[i][2] < th[i]) | (uint32_t)!(c[i][3] < th[i]);
-                             bits |= h << i;
-                         }
-                         const int mine = __popc(bits);
-                         const int incl = wave_scan_dpp(mine);
-                         const int tot = __builtin_amdgcn_readlane(incl, 63);
-                         if (tot) {  // wave-uniform
-                             int off = qn + incl - mine;
-#pragma unroll
-                             for (int i = 0; i < kPfQB; ++i) {
-                                 if ((bits >> i) & 1u) {
-                                     sh.qscore[wave][off] =
-                                         make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
-                                                    __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
-                                     sh.qtag[wave][off] = tag + 16u * i;
-                                     ++off;
-                                 }
-                             }
-                             qn += tot;
-                         }
-                         if (qn > kPfQueue - kPfQB * 64) {  // room for the next j-block's entries
-                             pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
-                             qn = 0;
-                         }
-                     }
-                 });
-        pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
-        __syncthreads();
-        if (tid < kPfQ) {
-            const int m = min(sh.n[tid], kPfLB);
-            sh.base[tid] = m > 0 ? (int)atomicAdd(&cnt[q0 + tid], (uint32_t)m) : 0;
+        for (int j = 0; j < 4; ++j) {
+            kf[j][0] = kn[j][0];
+            kf[j][1] = kn[j][1];
         }
-        __syncthreads();
-        for (int e = tid; e < kPfQ * kPfLB; e += 256) {
-            const int ql = e / kPfLB, j = e % kPfLB;
-            if (j < min(sh.n[ql], kPfLB) && sh.base[ql] + j < cap)
-                cand[(q0 + ql) * cap + sh.base[ql] + j] = sh.buf[ql][j];
+        pf_load_k(kseq, t_cap, t0 + 256, n16, g, kn);  // rows clamped: always in bounds
+        if (t0 <= tmax && t0 < t_cap) {                 // wave-uniform
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pf_f32x4 c[kPfQB];
+#pragma unroll
+                for (int i = 0; i < kPfQB; ++i) c[i] = pf_tile(kf[j], qf[i]);
+                const uint32_t tag = (((uint32_t)t0 + 16u * j + 4u * g) << 7) | (uint32_t)n16;
+                // float pre-filter (passes every key >= thr, and NaN): one bit
+                // per query block, then one wave scan places the lane's
+                // passing tiles in the queue
+                uint32_t bits = 0u;
+#pragma unroll
+                for (int i = 0; i < kPfQB; ++i) {
+                    // bitwise, not ||: no short-circuit branches
+                    const uint32_t h = (uint32_t)!(c[i][0] < th[i]) | (uint32_t)!(c[i][1] < th[i]) |
+                                       (uint32_t)!(c[i][2] < th[i]) | (uint32_t)!(c[i][3] < th[i]);
+                    bits |= h << i;
+                }
+                const int mine = __popc(bits);
+                const int incl = wave_scan_dpp(mine);
+                const int tot = __builtin_amdgcn_readlane(incl, 63);
+                if (tot) {  // wave-uniform
+                    int off = qn + incl - mine;
+#pragma unroll
+                    for (int i = 0; i < kPfQB; ++i) {
+                        if ((bits >> i) & 1u) {
+                            sh.qscore[wave][off] =
+                                make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
+                                           __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
+                            sh.qtag[wave][off] = tag + 16u * i;
+                            ++off;
+                        }
+                    }
+                    qn += tot;
+                }
+                if (qn > kPfQueue - kPfQB * 64) {  // room for the next j-block's entries
+                    pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
+                    qn = 0;
+                }
+            }
         }
-        __syncthreads();
-        if (tid < kPfQ) sh.n[tid] = 0;
-        __syncthreads();
+        if (s % kSegSteps == kSegSteps - 1 || s == nsteps - 1) {  // uniform: flush the lists
+            pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
+            qn = 0;
+            __syncthreads();
+            if (tid < kPfQ) {
+                const int m = min(sh.n[tid], kPfLB);
+                sh.base[tid] = m > 0 ? (int)atomicAdd(&cnt[q0 + tid], (uint32_t)m) : 0;
+            }
+            __syncthreads();
+            for (int e = tid; e < kPfQ * kPfLB; e += 256) {
+                const int ql = e / kPfLB, j = e % kPfLB;
+                if (j < min(sh.n[ql], kPfLB) && sh.base[ql] + j < cap)
+                    cand[(q0 + ql) * cap + sh.base[ql] + j] = sh.buf[ql][j];
+            }
+            __syncthreads();
+            if (tid < kPfQ) sh.n[tid] = 0;
+            __syncthreads();
+        }
     }
 }
 
