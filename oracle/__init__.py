@@ -60,6 +60,8 @@ def lib():
                                  i32, i32, i32, dbl, P]
         L.orc_stack.argtypes = [i32, P, i32, P, i32, i64, P, P, P, P, P, P, P, P,
                                 i32, i32, i32, i32, i32, i32, dbl, P, P, P]
+        L.orc_append.argtypes = [i32, i64, P, P, P, P, P, i32, i32, P, P, P, P]
+        L.orc_append.restype = None
         _lib = L
     return _lib
 
@@ -210,3 +212,30 @@ def stack(cache: Cache, modes, q_pos, q, q_idx, lk, lv, window, lo, k, pool, blo
     if rc:
         raise ValueError("orc_stack rc=%d" % rc)
     return out, sel, pool_out
+
+
+def append(kv, k_idx, lk, lv, pos, kv_new, kidx_new=None, k_new=None, v_new=None):
+    """Decode append on copies of the bf16 arrays: kv [S][T][256], k_idx
+    [S][T][64], lk / lv [L][S][cap][128] (may be None), rows kv_new [S][256],
+    kidx_new [S][64] (may be None), k_new / v_new [L][S][128].  Returns the
+    updated (kv, k_idx, lk, lv)."""
+    kv = _c(kv, np.uint16).copy()
+    k_idx = _c(k_idx, np.uint16).copy()
+    pos = _c(pos, np.int32)
+    S, T = kv.shape[0], kv.shape[1]
+    assert pos.size == S
+    if lk is not None:
+        lk = _c(lk, np.uint16).copy()
+        lv = _c(lv, np.uint16).copy()
+        L, cap = lk.shape[0], lk.shape[2]
+        k_new = _c(k_new, np.uint16)
+        v_new = _c(v_new, np.uint16)
+        assert k_new.shape == (L, S, 128) and v_new.shape == (L, S, 128)
+    else:
+        L, cap = 0, 1
+    kv_new = _c(kv_new, np.uint16)
+    kidx_new = None if kidx_new is None else _c(kidx_new, np.uint16)
+    lib().orc_append(S, T, _p(pos), _p(kv_new), _p(kidx_new), _p(kv), _p(k_idx), L, cap,
+                     _p(k_new) if L else None, _p(v_new) if L else None,
+                     _p(lk) if L else None, _p(lv) if L else None)
+    return kv, k_idx, lk, lv

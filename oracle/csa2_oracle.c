@@ -366,6 +366,39 @@ static int layer_one(const orc_cache *c, int mode, int32_t seq, int32_t t,
     return attend_one(c, seq, t, q, sel_io, k, lk, lv, cap, W, lo, scale, out);
 }
 
+/* -------------------------------------------------------- decode append */
+
+/* Decode append [CED, section "Why Prefill Recomputes a Recent Segment":
+ * once a token is chosen, its global KV is appended and every layer updates
+ * its local state].  For each sequence b with 0 <= pos[b] < t_cap: row pos[b]
+ * of kv [n_seq][t_cap][256] takes kv_new[b], row pos[b] of k_idx
+ * [n_seq][t_cap][64] takes kidx_new[b] (when kidx_new is given), and for each
+ * of the L layers slot pos[b] % cap of lk, lv [L][n_seq][cap][128] takes
+ * k_new, v_new [L][n_seq][128].  Other sequences are left alone.  The rows
+ * are bf16; an FP4 cache is the packing of the updated kv. */
+void orc_append(int32_t n_seq, int64_t t_cap, const int32_t *pos,
+                const uint16_t *kv_new, const uint16_t *kidx_new, uint16_t *kv, uint16_t *k_idx,
+                int32_t L, int32_t cap, const uint16_t *k_new, const uint16_t *v_new,
+                uint16_t *lk, uint16_t *lv)
+{
+    for (int32_t b = 0; b < n_seq; ++b) {
+        int64_t p = pos[b];
+        if (p < 0 || p >= t_cap) continue;
+        memcpy(kv + ((int64_t)b * t_cap + p) * 2 * ORC_D, kv_new + (int64_t)b * 2 * ORC_D,
+               sizeof(uint16_t) * 2 * ORC_D);
+        if (kidx_new)
+            memcpy(k_idx + ((int64_t)b * t_cap + p) * ORC_DI, kidx_new + (int64_t)b * ORC_DI,
+                   sizeof(uint16_t) * ORC_DI);
+        for (int32_t l = 0; l < L; ++l) {
+            int64_t slot = ((int64_t)l * n_seq + b) * cap + p % cap;
+            memcpy(lk + slot * ORC_D, k_new + ((int64_t)l * n_seq + b) * ORC_D,
+                   sizeof(uint16_t) * ORC_D);
+            memcpy(lv + slot * ORC_D, v_new + ((int64_t)l * n_seq + b) * ORC_D,
+                   sizeof(uint16_t) * ORC_D);
+        }
+    }
+}
+
 /* ------------------------------------------------------------ public API */
 
 /* One layer for nq queries.  q [nq][16][128], q_idx [nq][64];
