@@ -6,8 +6,10 @@ context 131072 tokens per sequence, 16 query heads over one KV head
 top-2048, then [Reindex, Reuse, Reuse, Reuse] repeats; every layer attends to
 its 2048 selected entries plus a 128-position local window.
 
-One step = one decode token for every sequence through all 20 layers (index
-scoring, top-k, gather + FP4 dequant, attention) through the C ABI: by default
+One step = one decode token for every sequence: the append of its position
+(global K | V row packed to FP4, indexer key, and the 20 layers' local ring
+slots; --no-append leaves it out), then all 20 layers (index scoring, top-k,
+gather + FP4 dequant, attention) through the C ABI: by default
 every kernel launched from the host (csa2_stack_run); --graph replays a stack
 recorded once per cache copy (csa2_stack_plan_create) as a HIP graph.  Inputs
 are resident in HBM before the timed region; the timed steps rotate over
@@ -38,15 +40,17 @@ PEAK_HBM_GBPS = 8000.0
 SCAN_KERNEL_SRC = os.path.join(ROOT, "sparse_attention_shared_amd", "csrc", "k_score.hip")
 
 
-def algorithmic_bytes(schedule, B, T, k, P, W):
-    """Bytes the method must move per step (selected rows, the scans the
-    indexer needs, window, queries, outputs and index lists); the dense
-    attention it avoids is not counted."""
+def algorithmic_bytes(schedule, B, T, k, P, W, append=True):
+    """Bytes the method must move per step (the append, selected rows, the
+    scans the indexer needs, window, queries, outputs and index lists); the
+    dense attention it avoids is not counted."""
     row = 136            # FP4 K+V codes (128 B) + E8M0 scales (8 B)
     kidx = 128           # bf16 indexer key
     win = W * 2 * 128 * 2
     qio = 16 * 128 * 2 * 2  # main Q in + output
     total = 0
+    if append:           # read bf16 K|V, key, local K/V; write FP4 row, key, ring slots
+        total += 512 + kidx + row + kidx + len(schedule) * 2 * (2 * 128 * 2)
     for m in schedule:
         b = k * row + win + qio + k * 4          # gather, window, q/out, read sel
         if m == 0:
@@ -101,7 +105,8 @@ def cpu_baseline(budget_s=12.0):
             break
     return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": "%d single-sequence 20-layer decode steps of the same workload "
-                      "(T=131072, FP4, pool 8192, k=2048, W=128) in %.1f s, one thread" % (n, el)}
+                      "(T=131072, FP4, pool 8192, k=2048, W=128) in %.1f s, one thread; the "
+                      "append's few-KB row writes are not in the sample" % (n, el)}
 
 
 PREFILL_METRIC = "CSA2 prefill-chunk query positions/s at 128k ctx, FP4 shared KV"
@@ -247,6 +252,8 @@ def main():
     ap.add_argument("--workload", choices=["decode", "prefill"], default="decode")
     ap.add_argument("--graph", action="store_true",
                     help="replay a recorded stack (HIP graph) per step instead of host launches")
+    ap.add_argument("--no-append", action="store_true",
+                    help="leave the decode append of the new position out of the step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -301,9 +308,18 @@ def main():
     local = [csa2.Local(d16(x.local_k[l]), d16(x.local_v[l]), sp.window) for l in range(L)]
     out = [torch.empty((B, 16, 128), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
     ws = torch.empty(1, dtype=torch.uint8, device="cuda")
+    # the appended rows are the ones the inputs already hold at q_pos, so every
+    # step rewrites the same values and the cache stays what the oracle sees
+    app = None
+    if not args.no_append:
+        bi = np.arange(B)
+        t = x.q_pos.astype(np.int64)
+        app = (d16(x.kv[bi, t]), d16(x.k_idx[bi, t]),
+               [d16(x.local_k[l][bi, t % sp.local_cap]) for l in range(L)],
+               [d16(x.local_v[l][bi, t % sp.local_cap]) for l in range(L)])
     # size the workspace once
     _, _, _ = csa2.stack_run(caches[0], sp.schedule, q_pos, q, q_idx, local, sp.k, sp.pool,
-                             want_sel=False, out=out)
+                             want_sel=False, out=out, append=app)
     torch.cuda.synchronize()
     from sparse_attention_shared_amd._lib import _StackArgs, stack_workspace
     need = stack_workspace(_StackArgs(caches[0], sp.schedule, q_pos, q, q_idx, local, out, sp.k,
@@ -321,7 +337,8 @@ def main():
 
         def step(i, events=None):
             csa2.stack_run(caches[i % len(caches)], sp.schedule, q_pos, q, q_idx, local, sp.k,
-                           sp.pool, want_sel=False, ws=ws, out=out, scan_events=events)
+                           sp.pool, want_sel=False, ws=ws, out=out, scan_events=events,
+                           append=app)
 
         for i in range(args.warmup):
             step(i)
@@ -339,8 +356,8 @@ def main():
         scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
     else:
         # one recorded stack (HIP graph) per cache copy
-        plans = [csa2.StackPlan(c, sp.schedule, q_pos, q, q_idx, local, sp.k, sp.pool, out=out)
-                 for c in caches]
+        plans = [csa2.StackPlan(c, sp.schedule, q_pos, q, q_idx, local, sp.k, sp.pool, out=out,
+                                append=app) for c in caches]
         for i in range(args.warmup):
             plans[i % len(plans)].launch()
         torch.cuda.synchronize()
@@ -366,11 +383,12 @@ def main():
         torch.cuda.synchronize()
         for i, e in enumerate(ev):
             csa2.stack_run(caches[i % len(caches)], sp.schedule, q_pos, q, q_idx, local, sp.k,
-                           sp.pool, want_sel=False, ws=ws, out=out, scan_events=e)
+                           sp.pool, want_sel=False, ws=ws, out=out, scan_events=e, append=app)
         torch.cuda.synchronize()
         scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
 
-    step_bytes = algorithmic_bytes(sp.schedule, B, T, sp.k, sp.pool, sp.window)
+    step_bytes = algorithmic_bytes(sp.schedule, B, T, sp.k, sp.pool, sp.window,
+                                   append=app is not None)
     scan_bytes = B * T * 128
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     result = {
@@ -387,7 +405,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "20-layer CSA2 decode stack over one shared FP4 (E2M1 + E8M0/32) global "
+            "workload": ("decode append + " if app is not None else "") +
+                        "20-layer CSA2 decode stack over one shared FP4 (E2M1 + E8M0/32) global "
                         "KV cache: batch 4, context 131072, 16 q heads / 1 KV head, head_dim "
                         "128, indexer dim 64, Full pool 8192 then [Reindex, Reuse x3]*, "
                         "top-k 2048, SWA 128",
@@ -395,6 +414,7 @@ def main():
             "schedule": "".join("FIU"[m] for m in sp.schedule),
             "k": sp.k, "pool": sp.pool, "window": sp.window,
             "cache_copies_rotated": args.copies,
+            "append": app is not None,
             "launch": "recorded stack replayed as a HIP graph (csa2_stack_plan_launch)"
                       if args.graph else "host launches (csa2_stack_run)",
         },

@@ -121,6 +121,29 @@ csa2_status csa2_pack_fp4(const uint16_t *x, int64_t rows, int32_t dim, uint8_t 
 csa2_status csa2_unpack_fp4(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                             int32_t dim, float *out, void *stream);
 
+/* --------------------------------------------------------------- append */
+
+/* Decode append ("CED", section "Why Prefill Recomputes a Recent Segment":
+ * once a token is chosen, the global KV of its position is appended and every
+ * decoder layer updates its local state).  For every sequence b with
+ * 0 <= pos[b] < t_cap, row pos[b] of the global cache receives kv[b] (K | V,
+ * bf16 [n_seq][256]; FP4-packed exactly as csa2_pack_fp4 does, or copied for
+ * a BF16 cache) and, when kidx is not NULL, its indexer key kidx[b] (bf16
+ * [n_seq][64]).  Then, for each of the n_local layers l, slot pos[b] %
+ * local[l].cap of that layer's ring receives k_new[l][b] and v_new[l][b]
+ * (bf16 [n_seq][128] each).  Sequences with pos[b] outside [0, t_cap) are
+ * skipped.  The call WRITES through cache->data, cache->scales,
+ * cache->k_idx and local[l].k / .v (the const of those structs is for the
+ * read-only calls).  kv may be NULL to update the local rings only.
+ *   pos: int32 [cache->n_seq]; local, k_new, v_new: host arrays [n_local]
+ *   (n_local may be 0 and then they may be NULL); every row pointer and ring
+ *   16-byte aligned, every local[l].cap > 0.  Rows written here are read by
+ *   later calls on the same stream. */
+csa2_status csa2_append(const csa2_cache *cache, const int32_t *pos, const uint16_t *kv,
+                        const uint16_t *kidx, int32_t n_local, const csa2_local *local,
+                        const uint16_t *const *k_new, const uint16_t *const *v_new,
+                        void *stream);
+
 /* -------------------------------------------------------------- indexer */
 
 /* Indexer scores (Fig. 4: indexer Q of the layer against indexer K of the
@@ -247,6 +270,18 @@ typedef struct {
                                           them (the kernel's own times); a plan records them
                                           on the stream right before and after that kernel.
                                           NULL skips */
+    /* Decode append (optional; see csa2_append).  When append_kv is not NULL
+     * the stack first writes position q_pos[b] of every sequence: the global
+     * row append_kv (bf16 [n_seq][256]), the indexer key append_kidx (bf16
+     * [n_seq][64], may be NULL) and, when append_k and append_v are not NULL,
+     * layer l's local ring slot from append_k[l] / append_v[l] (bf16
+     * [n_seq][128]; a NULL pair skips that layer).  Layer 0's scan then sees
+     * the new position.  In a plan the append is recorded with the layers, so
+     * a launch appends whatever the buffers hold at that time. */
+    const uint16_t *append_kv;
+    const uint16_t *append_kidx;
+    const uint16_t *const *append_k;   /* host [n_layers], or NULL */
+    const uint16_t *const *append_v;   /* host [n_layers], or NULL */
 } csa2_stack_desc;
 
 /* Workspace of csa2_stack_run; like the top-k workspace it must be

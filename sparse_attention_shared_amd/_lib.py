@@ -38,7 +38,9 @@ class csa2_stack_desc(ctypes.Structure):
                 ("pool", _i32), ("block", _i32), ("sm_scale", _f32),
                 ("q", ctypes.POINTER(_P)), ("q_idx", ctypes.POINTER(_P)),
                 ("local", ctypes.POINTER(csa2_local)), ("out", ctypes.POINTER(_P)),
-                ("sel_out", ctypes.POINTER(_P)), ("pool_out", _P), ("scan_events", _P * 2)]
+                ("sel_out", ctypes.POINTER(_P)), ("pool_out", _P), ("scan_events", _P * 2),
+                ("append_kv", _P), ("append_kidx", _P), ("append_k", ctypes.POINTER(_P)),
+                ("append_v", ctypes.POINTER(_P))]
 
 
 class Csa2Error(RuntimeError):
@@ -61,6 +63,9 @@ def lib() -> ctypes.CDLL:
         L.csa2_device_check.restype = ctypes.c_int
         L.csa2_pack_fp4.argtypes = [_P, _i64, _i32, _P, _P, _P]
         L.csa2_unpack_fp4.argtypes = [_P, _P, _i64, _i32, _P, _P]
+        L.csa2_append.argtypes = [ctypes.POINTER(csa2_cache), _P, _P, _P, _i32,
+                                  ctypes.POINTER(csa2_local), ctypes.POINTER(_P),
+                                  ctypes.POINTER(_P), _P]
         L.csa2_index_score.argtypes = [ctypes.POINTER(csa2_cache), _P, _P, _P, _i32, _P, _i64,
                                        _i32, _P, _i64, _P]
         L.csa2_prefill_score.argtypes = [ctypes.POINTER(csa2_cache), _i32, _P, _P, _i32, _P, _i64,
@@ -80,7 +85,7 @@ def lib() -> ctypes.CDLL:
                                              ctypes.POINTER(_P)]
         L.csa2_stack_plan_launch.argtypes = [_P, _P]
         L.csa2_stack_plan_destroy.argtypes = [_P]
-        for f in ("csa2_pack_fp4", "csa2_unpack_fp4", "csa2_index_score", "csa2_prefill_score",
+        for f in ("csa2_pack_fp4", "csa2_unpack_fp4", "csa2_append", "csa2_index_score", "csa2_prefill_score",
                   "csa2_prefill_topk", "csa2_prefill_topk_workspace", "csa2_topk",
                   "csa2_topk_workspace", "csa2_expand_blocks", "csa2_sparse_attn",
                   "csa2_sparse_attn_workspace", "csa2_stack_workspace", "csa2_stack_run",
@@ -180,6 +185,25 @@ def unpack_fp4(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
     _check("csa2_unpack_fp4", lib().csa2_unpack_fp4(_ptr(codes), _ptr(scales), rows, dim,
                                                     _ptr(out), _stream()))
     return out
+
+
+def append(cache: Cache, pos: torch.Tensor, kv: Optional[torch.Tensor] = None,
+           kidx: Optional[torch.Tensor] = None, local: Sequence[Local] = (),
+           k_new: Sequence[torch.Tensor] = (), v_new: Sequence[torch.Tensor] = ()) -> None:
+    """Decode append (csa2_append): row pos[b] of the global cache takes kv[b]
+    (bf16 [n_seq][256], FP4-packed for an FP4 cache) and k_idx takes kidx[b]
+    (bf16 [n_seq][64]); ring slot pos[b] % cap of local[l] takes k_new[l][b] and
+    v_new[l][b] (bf16 [n_seq][128]).  Sequences with pos outside [0, t_cap) are
+    skipped."""
+    n = len(local)
+    if len(k_new) != n or len(v_new) != n:
+        raise ValueError("local, k_new and v_new must have the same length")
+    locs = (csa2_local * n)(*[l.c for l in local]) if n else None
+    kn = (_P * n)(*[_bits16(t).data_ptr() for t in k_new]) if n else None
+    vn = (_P * n)(*[_bits16(t).data_ptr() for t in v_new]) if n else None
+    _check("csa2_append", lib().csa2_append(
+        ctypes.byref(cache.c), _ptr(_i32t(pos)), _ptr(_bits16(kv)) if kv is not None else None,
+        _ptr(_bits16(kidx)) if kidx is not None else None, n, locs, kn, vn, _stream()))
 
 
 def index_score(cache: Cache, q_idx: torch.Tensor, q_pos: torch.Tensor,
@@ -287,9 +311,10 @@ class _StackArgs:
                  q: Sequence[torch.Tensor], q_idx: Sequence[Optional[torch.Tensor]],
                  local: Sequence[Local], out: Sequence[torch.Tensor], k: int, pool: int,
                  block: int, sm_scale: float, sel_out: Optional[Sequence[torch.Tensor]],
-                 pool_out: Optional[torch.Tensor], scan_events=None):
+                 pool_out: Optional[torch.Tensor], scan_events=None, append=None):
         L = len(modes)
-        self.refs = (cache, q_pos, list(q), list(q_idx), list(local), list(out), sel_out, pool_out)
+        self.refs = (cache, q_pos, list(q), list(q_idx), list(local), list(out), sel_out, pool_out,
+                     append)
         self.modes = (_i32 * L)(*modes)
         self.q = (_P * L)(*[t.data_ptr() for t in q])
         self.q_idx = (_P * L)(*[(t.data_ptr() if t is not None else None) for t in q_idx])
@@ -302,6 +327,19 @@ class _StackArgs:
             self.sel if self.sel is not None else None,
             _ptr(pool_out) if pool_out is not None else None,
             (_P * 2)(*(scan_events or (None, None))))
+        if append is not None:
+            kv, kidx, kn, vn = append
+            self.desc.append_kv = _ptr(_bits16(kv)).value
+            self.desc.append_kidx = _ptr(_bits16(kidx)).value if kidx is not None else None
+            if kn is not None:
+                if len(kn) != L or len(vn) != L:
+                    raise ValueError("append rows: one (k, v) pair per layer")
+                self.app_k = (_P * L)(*[(_bits16(t).data_ptr() if t is not None else None)
+                                        for t in kn])
+                self.app_v = (_P * L)(*[(_bits16(t).data_ptr() if t is not None else None)
+                                        for t in vn])
+                self.desc.append_k = self.app_k
+                self.desc.append_v = self.app_v
 
 
 def stack_workspace(args: _StackArgs) -> int:
@@ -316,12 +354,15 @@ def stack_run(cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
               local: Sequence[Local], k: int, pool: int = 0, block: int = 1,
               sm_scale: float = HEAD_DIM ** -0.5, want_sel: bool = True,
               ws: Optional[torch.Tensor] = None, out: Optional[Sequence[torch.Tensor]] = None,
-              scan_events=None):
+              scan_events=None, append=None):
     """Run a decoder stack (one decode query per sequence).
 
     Returns (out list of bf16 [n_seq][16][128], sel list or None, pool or None).
     ``scan_events``: optional pair of ``torch.cuda.Event(enable_timing=True)``
-    recorded around layer 0's indexer scan.
+    recorded around layer 0's indexer scan.  ``append``: optional
+    ``(kv, kidx, k_new, v_new)`` written at q_pos before layer 0 (the decode
+    append of csa2_append; kidx may be None, k_new / v_new None or one bf16
+    [n_seq][128] tensor (or None) per layer).
     """
     S = int(q_pos.shape[0])
     dev = q_pos.device
@@ -333,7 +374,7 @@ def stack_run(cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
     if scan_events is not None:
         ev = tuple(ctypes.c_void_p(e.cuda_event) for e in scan_events)
     args = _StackArgs(cache, modes, q_pos, q, q_idx, local, out, k, pool, block, sm_scale, sel,
-                      pool_out, ev)
+                      pool_out, ev, append)
     need = stack_workspace(args)
     if ws is None or ws.numel() < need:
         ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
@@ -354,7 +395,7 @@ class StackPlan:
                  q: Sequence[torch.Tensor], q_idx: Sequence[Optional[torch.Tensor]],
                  local: Sequence[Local], k: int, pool: int = 0, block: int = 1,
                  sm_scale: float = HEAD_DIM ** -0.5, want_sel: bool = False,
-                 out: Optional[Sequence[torch.Tensor]] = None, scan_events=None):
+                 out: Optional[Sequence[torch.Tensor]] = None, scan_events=None, append=None):
         S = int(q_pos.shape[0])
         dev = q_pos.device
         self.out = out if out is not None else [
@@ -366,7 +407,7 @@ class StackPlan:
         if scan_events is not None:
             ev = tuple(ctypes.c_void_p(e.cuda_event) for e in scan_events)
         self.args = _StackArgs(cache, modes, q_pos, q, q_idx, local, self.out, k, pool, block,
-                               sm_scale, self.sel, self.pool, ev)
+                               sm_scale, self.sel, self.pool, ev, append)
         need = stack_workspace(self.args)
         self.ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize(dev)  # the zero fill lands before the plan is recorded

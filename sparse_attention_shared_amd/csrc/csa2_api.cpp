@@ -88,6 +88,58 @@ csa2_status check_local(const csa2_local* l, LocalView* v) {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Validate one layer's local append: its ring and both new rows.
+csa2_status check_append_local(const csa2_local& l, const uint16_t* kn, const uint16_t* vn) {
+    if (l.cap <= 0) return CSA2_ERR_SHAPE;
+    if (!l.k || !l.v || !kn || !vn) return CSA2_ERR_INVALID_ARG;
+    if (!aligned16(l.k) || !aligned16(l.v) || !aligned16(kn) || !aligned16(vn))
+        return CSA2_ERR_INVALID_ARG;
+    return CSA2_OK;
+}
+
+// Enqueue the append of validated arguments: the global row with the first
+// (up to kMaxAppendLayers) local layers, then further launches for the rest.
+// Layers whose new rows are both NULL are skipped.
+hipError_t enqueue_append(const CacheView& cv, const int32_t* pos, const uint16_t* kv,
+                          const uint16_t* kidx, int32_t n_local, const csa2_local* local,
+                          const uint16_t* const* kn, const uint16_t* const* vn, hipStream_t s) {
+    AppendArgs a{};
+    a.pos = pos;
+    a.t_cap = cv.t_cap;
+    a.fp4 = cv.fp4;
+    a.kv = kv;
+    a.kidx = kidx;
+    void* data = const_cast<void*>(cv.data);
+    if (cv.fp4) {
+        a.codes = static_cast<uint8_t*>(data);
+        a.scales = const_cast<uint8_t*>(cv.scales);
+    } else {
+        a.bf16 = static_cast<uint16_t*>(data);
+    }
+    a.k_idx = const_cast<uint16_t*>(cv.k_idx);
+    bool first = true;
+    int32_t l = 0;
+    do {
+        a.n_local = 0;
+        for (; l < n_local && a.n_local < kMaxAppendLayers; ++l) {
+            if (!kn[l] && !vn[l]) continue;
+            AppendLocal& d = a.local[a.n_local++];
+            d.k = const_cast<uint16_t*>(local[l].k);
+            d.v = const_cast<uint16_t*>(local[l].v);
+            d.k_new = kn[l];
+            d.v_new = vn[l];
+            d.cap = local[l].cap;
+        }
+        if (first || a.n_local > 0) {
+            if (hipError_t e = launch_append(a, cv.n_seq, s)) return e;
+        }
+        first = false;
+        a.kv = nullptr;  // later launches update local rings only
+        a.kidx = nullptr;
+    } while (l < n_local);
+    return hipSuccess;
+}
+
 // Workspace of one stack run: scores, block scores / block ids, pool scores,
 // pool, the current selection, per-sequence counters, top-k and attention
 // scratch.  Counters reset themselves: the workspace must start zero-filled.
@@ -161,6 +213,23 @@ csa2_status csa2_unpack_fp4(const uint8_t* codes, const uint8_t* scales, int64_t
         return CSA2_ERR_INVALID_ARG;
     if (csa2_status st = device_ok()) return st;
     return from_hip(launch_unpack_fp4(codes, scales, rows * (dim / 32), out, (hipStream_t)stream));
+}
+
+csa2_status csa2_append(const csa2_cache* cache, const int32_t* pos, const uint16_t* kv,
+                        const uint16_t* kidx, int32_t n_local, const csa2_local* local,
+                        const uint16_t* const* k_new, const uint16_t* const* v_new,
+                        void* stream) {
+    CacheView cv;
+    if (csa2_status st = check_cache(cache, kv != nullptr, kidx != nullptr, &cv)) return st;
+    if (n_local < 0) return CSA2_ERR_SHAPE;
+    if (!pos) return CSA2_ERR_INVALID_ARG;
+    if ((kv && !aligned16(kv)) || (kidx && !aligned16(kidx))) return CSA2_ERR_INVALID_ARG;
+    if (n_local > 0 && (!local || !k_new || !v_new)) return CSA2_ERR_INVALID_ARG;
+    for (int32_t l = 0; l < n_local; ++l)
+        if (csa2_status st = check_append_local(local[l], k_new[l], v_new[l])) return st;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(enqueue_append(cv, pos, kv, kidx, n_local, local, k_new, v_new,
+                                   (hipStream_t)stream));
 }
 
 csa2_status csa2_index_score(const csa2_cache* cache, const uint16_t* q_idx, const int32_t* q_pos,
@@ -298,6 +367,19 @@ static csa2_status check_stack(const csa2_stack_desc* d, CacheView* cv, int32_t*
         if (csa2_status st = check_local(&d->local[l], &lv)) return st;
         mw = std::max(mw, lv.window);
     }
+    if (d->append_kidx && !d->append_kv) return CSA2_ERR_INVALID_ARG;
+    if ((d->append_k != nullptr) != (d->append_v != nullptr)) return CSA2_ERR_INVALID_ARG;
+    if (d->append_k && !d->append_kv) return CSA2_ERR_INVALID_ARG;
+    if (d->append_kv) {
+        if (!aligned16(d->append_kv) || (d->append_kidx && !aligned16(d->append_kidx)))
+            return CSA2_ERR_INVALID_ARG;
+        if (d->append_k)
+            for (int32_t l = 0; l < d->n_layers; ++l) {
+                if (!d->append_k[l] && !d->append_v[l]) continue;
+                if (csa2_status st = check_append_local(d->local[l], d->append_k[l], d->append_v[l]))
+                    return st;
+            }
+    }
     *max_window = mw;
     return CSA2_OK;
 }
@@ -337,6 +419,12 @@ static csa2_status enqueue_stack(const csa2_stack_desc* d, const CacheView& cv, 
         if (e == hipSuccess) e = launch_topk(pscores, S, P, P, pool, k, dst, 0, nullptr, tkws, s);
         return e;
     };
+    if (d->append_kv) {
+        const int32_t nl = d->append_k ? d->n_layers : 0;
+        if (enqueue_append(cv, d->q_pos, d->append_kv, d->append_kidx, nl, d->local, d->append_k,
+                           d->append_v, s) != hipSuccess)
+            return CSA2_ERR_HIP;
+    }
     const int32_t* cur = nullptr;
     for (int32_t l = 0; l < d->n_layers; ++l) {
         const int32_t m = d->modes[l];

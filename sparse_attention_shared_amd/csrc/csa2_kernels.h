@@ -30,6 +30,31 @@ hipError_t launch_unpack_fp4(const uint8_t* codes, const uint8_t* scales, int64_
                              hipStream_t s);
 
 // Dense indexer scores: scores[i][b], b < ceil(t_cap / block), block in {1, 64}.
+// Decode append: the new position's global row (FP4-packed or copied),
+// indexer key and every listed layer's local K/V ring slot, per sequence.
+constexpr int kMaxAppendLayers = 32;  // layers per launch (kernel argument size)
+struct AppendLocal {
+    uint16_t* k;
+    uint16_t* v;
+    const uint16_t* k_new;  // bf16 [n_seq][128]
+    const uint16_t* v_new;
+    int32_t cap;
+};
+struct AppendArgs {
+    const int32_t* pos;  // [n_seq]; rows outside [0, t_cap) are skipped
+    int64_t t_cap;
+    int32_t fp4;
+    const uint16_t* kv;    // bf16 [n_seq][256]
+    const uint16_t* kidx;  // bf16 [n_seq][64] or null
+    uint8_t* codes;        // FP4 cache
+    uint8_t* scales;
+    uint16_t* bf16;        // bf16 cache
+    uint16_t* k_idx;
+    int32_t n_local;
+    AppendLocal local[kMaxAppendLayers];
+};
+hipError_t launch_append(const AppendArgs& a, int32_t n_seq, hipStream_t s);
+
 // With ev0/ev1 set, the kernel's own start and end times are recorded in them.
 hipError_t launch_score_dense(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
                               const int32_t* q_seq, int32_t nq, int32_t block, float* scores,

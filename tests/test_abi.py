@@ -181,3 +181,56 @@ def test_stack_plan_without_a_device_reports_no_device():
     assert L.csa2_stack_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
     plan = _lib._P()
     assert L.csa2_stack_plan_create(ctypes.byref(d), FAKE, n.value, ctypes.byref(plan)) == NO_DEVICE
+
+
+def test_append_validation():
+    L = csa2.lib()
+    bp = ctypes.byref
+    c = _cache()
+    loc = (_lib.csa2_local * 2)(_lib.csa2_local(FAKE, FAKE, 16, 8, 0),
+                                _lib.csa2_local(FAKE, FAKE, 0, 0, 0))
+    rows = (ctypes.c_void_p * 2)(0x10000, 0x10000)
+    odd = (ctypes.c_void_p * 2)(0x10000, 0x10004)
+    nul = (ctypes.c_void_p * 2)(0x10000, None)
+    assert L.csa2_append(bp(c), None, FAKE, FAKE, 0, None, None, None, None) == INVALID
+    assert L.csa2_append(bp(c), FAKE, FAKE_ODD, FAKE, 0, None, None, None, None) == INVALID
+    assert L.csa2_append(bp(c), FAKE, FAKE, FAKE_ODD, 0, None, None, None, None) == INVALID
+    assert L.csa2_append(bp(c), FAKE, FAKE, FAKE, -1, None, None, None, None) == SHAPE
+    assert L.csa2_append(bp(c), FAKE, FAKE, FAKE, 1, None, rows, rows, None) == INVALID
+    assert L.csa2_append(bp(c), FAKE, FAKE, FAKE, 2, loc, rows, rows, None) == SHAPE  # cap 0
+    loc2 = (_lib.csa2_local * 2)(_lib.csa2_local(FAKE, FAKE, 16, 8, 0),
+                                 _lib.csa2_local(FAKE, FAKE, 16, 8, 0))
+    assert L.csa2_append(bp(c), FAKE, FAKE, FAKE, 2, loc2, rows, odd, None) == INVALID
+    assert L.csa2_append(bp(c), FAKE, FAKE, FAKE, 2, loc2, nul, rows, None) == INVALID
+    loc2[1].v = FAKE_ODD
+    assert L.csa2_append(bp(c), FAKE, FAKE, FAKE, 2, loc2, rows, rows, None) == INVALID
+    # a cache whose rows the append needs
+    nodata = _cache(data=None)
+    assert L.csa2_append(bp(nodata), FAKE, FAKE, None, 0, None, None, None, None) == INVALID
+    noidx = _cache(k_idx=None)
+    assert L.csa2_append(bp(noidx), FAKE, FAKE, FAKE, 0, None, None, None, None) == INVALID
+    # the stack's append fields
+    d, keep = _desc([0, 2])
+    n = _lib._sz()
+    d.append_kidx = 0x10000  # an indexer row without the KV row
+    assert L.csa2_stack_workspace(bp(d), bp(n)) == INVALID
+    d.append_kv = 0x10004
+    assert L.csa2_stack_workspace(bp(d), bp(n)) == INVALID
+    d.append_kv = 0x10000
+    assert L.csa2_stack_workspace(bp(d), bp(n)) == OK
+    d.append_k = rows  # k rows without v rows
+    assert L.csa2_stack_workspace(bp(d), bp(n)) == INVALID
+    d.append_v = odd
+    assert L.csa2_stack_workspace(bp(d), bp(n)) == INVALID
+    d.append_v = rows
+    assert L.csa2_stack_workspace(bp(d), bp(n)) == OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
+def test_append_without_a_device_reports_no_device():
+    L = csa2.lib()
+    c = _cache()
+    loc = (_lib.csa2_local * 1)(_lib.csa2_local(FAKE, FAKE, 16, 8, 0))
+    rows = (ctypes.c_void_p * 1)(0x10000)
+    assert L.csa2_append(ctypes.byref(c), FAKE, FAKE, FAKE, 1, loc, rows, rows, None) == NO_DEVICE
+    assert L.csa2_append(ctypes.byref(c), FAKE, None, None, 0, None, None, None, None) == NO_DEVICE
