@@ -61,6 +61,8 @@ def lib():
         L.orc_stack.argtypes = [i32, P, i32, P, i32, i64, P, P, P, P, P, P, P, P,
                                 i32, i32, i32, i32, i32, i32, dbl, P, P, P]
         L.orc_append.argtypes = [i32, i64, P, P, P, P, P, i32, i32, P, P, P, P]
+        L.orc_replay.argtypes = [i32, P, i32, i32, i32, P, i32, i64, P, P, P, P, P, P, P, P,
+                                 i32, i32, i32, i32, i32, i32, P, P, dbl, P, P, P]
         L.orc_append.restype = None
         _lib = L
     return _lib
@@ -239,3 +241,32 @@ def append(kv, k_idx, lk, lv, pos, kv_new, kidx_new=None, k_new=None, v_new=None
                      _p(k_new) if L else None, _p(v_new) if L else None,
                      _p(lk) if L else None, _p(lv) if L else None)
     return kv, k_idx, lk, lv
+
+
+def replay(cache: Cache, modes, seq, pos, q, q_idx, lk, lv, window, lo, k, pool, k_new, v_new,
+           block=1, scale=128 ** -0.5):
+    """Bounded replay of positions pos (one sequence) through a decoder stack.
+    q [L][n][16][128], q_idx [L][n][64], lk / lv [L][n_seq][cap][128] (copied,
+    then updated as the replay writes the segment's rows k_new / v_new
+    [L][n][128]).  Returns (out [L][n][16][128], sel [L][n][k], pool [n][pool],
+    lk, lv)."""
+    modes = _c(modes, np.int32)
+    pos = _c(pos, np.int32)
+    L, n = modes.size, pos.size
+    q = _c(q, np.uint16)
+    q_idx = _c(q_idx, np.uint16)
+    lk = _c(lk, np.uint16).copy()
+    lv = _c(lv, np.uint16).copy()
+    k_new = _c(k_new, np.uint16)
+    v_new = _c(v_new, np.uint16)
+    assert k_new.shape == (L, n, 128) and v_new.shape == (L, n, 128)
+    sel = np.full((L, n, k), -1, np.int32)
+    pool_out = np.full((n, max(pool, 0)), -1, np.int32)
+    out = np.empty((L, n, 16, 128), np.float64)
+    rc = lib().orc_replay(L, _p(modes), lk.shape[1], seq, n, _p(pos), *cache.args(),
+                          _p(cache.k_idx), _p(q), _p(q_idx), _p(lk), _p(lv), lk.shape[-2],
+                          window, lo, k, pool, block, _p(k_new), _p(v_new), scale, _p(sel),
+                          _p(pool_out), _p(out))
+    if rc:
+        raise ValueError("orc_replay rc=%d" % rc)
+    return out, sel, pool_out, lk, lv

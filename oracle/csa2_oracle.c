@@ -477,3 +477,54 @@ int orc_stack(int32_t n_layers, const int32_t *modes, int32_t n_seq, const int32
     free(sel);
     return rc;
 }
+
+/* Bounded replay of a prompt's recent segment [CED, section "Why Prefill
+ * Recomputes a Recent Segment", Fig. 6]: positions pos[0..n) of sequence seq
+ * pass through every decoder layer again so that each layer rebuilds its
+ * local state; window references before lo (normally the segment's first
+ * position) are cut off, the approximation that section describes.  For each
+ * layer l in order: the segment's local rows k_new / v_new [L][n][128] enter
+ * the layer's ring (slot p % cap; n <= cap, so no two rows share a slot),
+ * then every query of the segment runs the layer's mode (Fig. 5) exactly as
+ * orc_layer does.  lk, lv [L][n_seq][cap][128] are updated in place.
+ * q [L][n][16][128], q_idx [L][n][64], sel_out [L][n][k], pool_out [n][pool],
+ * out [L][n][16][128]. */
+int orc_replay(int32_t n_layers, const int32_t *modes, int32_t n_seq, int32_t seq, int32_t n,
+               const int32_t *pos, int32_t fp4, int64_t t_cap, const uint16_t *kv,
+               const uint8_t *codes, const uint8_t *scales, const uint16_t *k_idx,
+               const uint16_t *q, const uint16_t *q_idx, uint16_t *lk, uint16_t *lv,
+               int32_t cap, int32_t W, int32_t lo, int32_t k, int32_t pool, int32_t block,
+               const uint16_t *k_new, const uint16_t *v_new, double scale,
+               int32_t *sel_out, int32_t *pool_out, double *out)
+{
+    if (n < 0 || n > cap || seq < 0 || seq >= n_seq) return 8;
+    int32_t *q_seq = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1) * k);
+    int rc = 0;
+    int have_pool = 0;
+    for (int32_t i = 0; i < n; ++i) q_seq[i] = seq;
+    for (int64_t i = 0; i < (int64_t)n * k; ++i) sel[i] = -1;
+    for (int32_t l = 0; l < n_layers && !rc; ++l) {
+        int32_t m = modes[l];
+        if (m == ORC_REUSE && l == 0) { rc = 7; break; }
+        if (m == ORC_REINDEX && !have_pool) { rc = 7; break; }
+        uint16_t *rk = lk + (int64_t)l * n_seq * cap * ORC_D;
+        uint16_t *rv = lv + (int64_t)l * n_seq * cap * ORC_D;
+        for (int32_t i = 0; i < n; ++i) {
+            if (pos[i] < 0 || pos[i] >= t_cap) { rc = 4; break; }
+            int64_t slot = (int64_t)seq * cap + pos[i] % cap;
+            memcpy(rk + slot * ORC_D, k_new + ((int64_t)l * n + i) * ORC_D, sizeof(uint16_t) * ORC_D);
+            memcpy(rv + slot * ORC_D, v_new + ((int64_t)l * n + i) * ORC_D, sizeof(uint16_t) * ORC_D);
+        }
+        if (rc) break;
+        int64_t qo = (int64_t)l * n;
+        rc = orc_layer(n, pos, q_seq, m, fp4, t_cap, kv, codes, scales, k_idx,
+                       q + qo * ORC_H * ORC_D, q_idx + qo * ORC_DI, rk, rv, cap, W, lo,
+                       k, pool, block, pool_out, sel, scale, out + qo * ORC_H * ORC_D);
+        if (m == ORC_FULL && pool > 0) have_pool = 1;
+        memcpy(sel_out + qo * k, sel, sizeof(int32_t) * (size_t)n * k);
+    }
+    free(q_seq);
+    free(sel);
+    return rc;
+}
