@@ -309,6 +309,57 @@ csa2_status csa2_stack_plan_create(const csa2_stack_desc *desc, void *ws, size_t
 csa2_status csa2_stack_plan_launch(const csa2_stack_plan *plan, void *stream);
 csa2_status csa2_stack_plan_destroy(csa2_stack_plan *plan);
 
+/* ------------------------------------------------------- bounded replay */
+
+/* Bounded replay of a prompt's recent segment ("CED", section "Why Prefill
+ * Recomputes a Recent Segment", Fig. 6): once the global KV of the whole
+ * prompt is in the cache, only the last positions pass through the decoder
+ * again, so that every layer rebuilds its local state; window references
+ * before the segment are cut off (set each layer's local.lo to the segment's
+ * first position for the section's approximation; a smaller lo lets the
+ * window read older ring slots).
+ * The n queries at q_pos (device int32 [n], each in [0, t_cap); normally
+ * consecutive) all belong to sequence `seq`.  Layer by layer, in the
+ * schedule's order: when local_k and local_v are set, the segment's local
+ * rows local_k[l] / local_v[l] (bf16 [n][128]; a NULL pair skips the layer)
+ * enter slot q_pos[i] % cap of the layer's ring (n <= cap, so no two rows
+ * share a slot); then every query runs the layer's mode exactly as a decode
+ * query at its position would (Full: its own top-k over [0, t] and, with
+ * pool > 0, its pool; Reindex: top-k of its pool; Reuse: the previous
+ * layer's picks) and attends with the layer's q and window.  All ring rows
+ * are written before layer 0 runs (each layer reads only its own ring).
+ *   q [l] -> bf16 [n][16][128]; q_idx [l] -> bf16 [n][64] (unused on Reuse);
+ *   out [l] -> bf16 [n][16][128]; sel_out NULL or [l] -> int32 [n][k];
+ *   pool_out NULL or int32 [n][pool].  1 <= n <= 65535.
+ * Workspace rules as csa2_stack_workspace (zero-filled before first use, left
+ * zero; calls sharing one must not overlap).  A Full layer with block 1, no
+ * pool, k <= 2048 and t_cap <= 2^18 uses the fused top-k of
+ * csa2_prefill_topk; otherwise the segment's score rows are materialised
+ * (n * t_cap floats of workspace). */
+typedef struct {
+    int32_t n_layers;
+    const int32_t *modes;              /* host [n_layers], csa2_mode */
+    const csa2_cache *cache;           /* host pointer */
+    int32_t seq;                       /* the sequence replayed */
+    int32_t n;                         /* queries in the segment */
+    const int32_t *q_pos;              /* device int32 [n] */
+    int32_t k;
+    int32_t pool;
+    int32_t block;                     /* 1, or 64 (blockwise Full) */
+    float sm_scale;
+    const uint16_t *const *q;          /* host [n_layers] of device pointers */
+    const uint16_t *const *q_idx;
+    const csa2_local *local;           /* host [n_layers] */
+    const uint16_t *const *local_k;    /* host [n_layers], or NULL */
+    const uint16_t *const *local_v;    /* host [n_layers], or NULL */
+    uint16_t *const *out;
+    int32_t *const *sel_out;
+    int32_t *pool_out;
+} csa2_replay_desc;
+
+csa2_status csa2_replay_workspace(const csa2_replay_desc *desc, size_t *bytes);
+csa2_status csa2_replay_run(const csa2_replay_desc *desc, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

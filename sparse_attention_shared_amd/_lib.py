@@ -43,6 +43,16 @@ class csa2_stack_desc(ctypes.Structure):
                 ("append_v", ctypes.POINTER(_P))]
 
 
+class csa2_replay_desc(ctypes.Structure):
+    _fields_ = [("n_layers", _i32), ("modes", ctypes.POINTER(_i32)),
+                ("cache", ctypes.POINTER(csa2_cache)), ("seq", _i32), ("n", _i32),
+                ("q_pos", _P), ("k", _i32), ("pool", _i32), ("block", _i32), ("sm_scale", _f32),
+                ("q", ctypes.POINTER(_P)), ("q_idx", ctypes.POINTER(_P)),
+                ("local", ctypes.POINTER(csa2_local)), ("local_k", ctypes.POINTER(_P)),
+                ("local_v", ctypes.POINTER(_P)), ("out", ctypes.POINTER(_P)),
+                ("sel_out", ctypes.POINTER(_P)), ("pool_out", _P)]
+
+
 class Csa2Error(RuntimeError):
     pass
 
@@ -85,11 +95,14 @@ def lib() -> ctypes.CDLL:
                                              ctypes.POINTER(_P)]
         L.csa2_stack_plan_launch.argtypes = [_P, _P]
         L.csa2_stack_plan_destroy.argtypes = [_P]
+        L.csa2_replay_workspace.argtypes = [ctypes.POINTER(csa2_replay_desc), ctypes.POINTER(_sz)]
+        L.csa2_replay_run.argtypes = [ctypes.POINTER(csa2_replay_desc), _P, _sz, _P]
         for f in ("csa2_pack_fp4", "csa2_unpack_fp4", "csa2_append", "csa2_index_score", "csa2_prefill_score",
                   "csa2_prefill_topk", "csa2_prefill_topk_workspace", "csa2_topk",
                   "csa2_topk_workspace", "csa2_expand_blocks", "csa2_sparse_attn",
                   "csa2_sparse_attn_workspace", "csa2_stack_workspace", "csa2_stack_run",
-                  "csa2_stack_plan_create", "csa2_stack_plan_launch", "csa2_stack_plan_destroy"):
+                  "csa2_stack_plan_create", "csa2_stack_plan_launch", "csa2_stack_plan_destroy",
+                  "csa2_replay_workspace", "csa2_replay_run"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -429,3 +442,70 @@ class StackPlan:
             self.close()
         except Exception:
             pass
+
+
+class _ReplayArgs:
+    """Keeps the ctypes arrays of one replay descriptor alive."""
+
+    def __init__(self, cache: Cache, modes: Sequence[int], seq: int, q_pos: torch.Tensor,
+                 q: Sequence[torch.Tensor], q_idx: Sequence[Optional[torch.Tensor]],
+                 local: Sequence[Local], out: Sequence[torch.Tensor], k: int, pool: int,
+                 block: int, sm_scale: float, local_k=None, local_v=None, sel_out=None,
+                 pool_out: Optional[torch.Tensor] = None):
+        L = len(modes)
+        self.refs = (cache, q_pos, list(q), list(q_idx), list(local), list(out), sel_out,
+                     pool_out, local_k, local_v)
+        self.modes = (_i32 * L)(*modes)
+        self.q = (_P * L)(*[_bits16(t).data_ptr() for t in q])
+        self.q_idx = (_P * L)(*[(_bits16(t).data_ptr() if t is not None else None)
+                                for t in q_idx])
+        self.local = (csa2_local * L)(*[l.c for l in local])
+        self.out = (_P * L)(*[t.data_ptr() for t in out])
+        self.sel = (_P * L)(*[t.data_ptr() for t in sel_out]) if sel_out is not None else None
+        rows = local_k is not None
+        if rows and (len(local_k) != L or len(local_v) != L):
+            raise ValueError("local rows: one (k, v) pair per layer")
+        self.lk = (_P * L)(*[(_bits16(t).data_ptr() if t is not None else None)
+                             for t in local_k]) if rows else None
+        self.lv = (_P * L)(*[(_bits16(t).data_ptr() if t is not None else None)
+                             for t in local_v]) if rows else None
+        self.desc = csa2_replay_desc(
+            L, self.modes, ctypes.pointer(cache.c), int(seq), int(q_pos.shape[0]),
+            _ptr(_i32t(q_pos)), k, pool, block, float(sm_scale), self.q, self.q_idx, self.local,
+            self.lk, self.lv, self.out, self.sel,
+            _ptr(pool_out) if pool_out is not None else None)
+
+
+def replay_workspace(args: _ReplayArgs) -> int:
+    n = _sz()
+    _check("csa2_replay_workspace", lib().csa2_replay_workspace(ctypes.byref(args.desc),
+                                                                ctypes.byref(n)))
+    return n.value
+
+
+def replay_run(cache: Cache, modes: Sequence[int], seq: int, q_pos: torch.Tensor,
+               q: Sequence[torch.Tensor], q_idx: Sequence[Optional[torch.Tensor]],
+               local: Sequence[Local], k: int, pool: int = 0, block: int = 1,
+               sm_scale: float = HEAD_DIM ** -0.5, local_k=None, local_v=None,
+               want_sel: bool = True, ws: Optional[torch.Tensor] = None,
+               out: Optional[Sequence[torch.Tensor]] = None):
+    """Bounded replay (csa2_replay_run): the queries at q_pos (int32 [n], all
+    on sequence ``seq``) through every layer; ``local_k`` / ``local_v``: None,
+    or per layer a bf16 [n][128] tensor (or None) of the segment's local rows,
+    written into the layer's ring first.  Set each Local's ``lo`` to the
+    segment's first position for the window cut-off.  Returns (out list of
+    bf16 [n][16][128], sel list or None, pool or None)."""
+    n = int(q_pos.shape[0])
+    dev = q_pos.device
+    if out is None:
+        out = [torch.empty((n, HEADS, HEAD_DIM), dtype=torch.bfloat16, device=dev) for _ in modes]
+    sel = [torch.empty((n, k), dtype=torch.int32, device=dev) for _ in modes] if want_sel else None
+    pool_out = torch.empty((n, pool), dtype=torch.int32, device=dev) if pool > 0 else None
+    args = _ReplayArgs(cache, modes, seq, q_pos, q, q_idx, local, out, k, pool, block, sm_scale,
+                       local_k, local_v, sel, pool_out)
+    need = replay_workspace(args)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("csa2_replay_run", lib().csa2_replay_run(ctypes.byref(args.desc), _ptr(ws), ws.numel(),
+                                                    _stream()))
+    return out, sel, pool_out

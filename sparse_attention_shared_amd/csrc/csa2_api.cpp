@@ -100,11 +100,17 @@ csa2_status check_append_local(const csa2_local& l, const uint16_t* kn, const ui
 // Enqueue the append of validated arguments: the global row with the first
 // (up to kMaxAppendLayers) local layers, then further launches for the rest.
 // Layers whose new rows are both NULL are skipped.
-hipError_t enqueue_append(const CacheView& cv, const int32_t* pos, const uint16_t* kv,
-                          const uint16_t* kidx, int32_t n_local, const csa2_local* local,
-                          const uint16_t* const* kn, const uint16_t* const* vn, hipStream_t s) {
+// rows = n_seq with seq = -1 (decode: row b is sequence b's new position), or
+// the rows of one sequence's replayed segment (seq >= 0); q_seq_out, when set,
+// receives each row's sequence.
+hipError_t enqueue_append(const CacheView& cv, int32_t rows, int32_t seq, const int32_t* pos,
+                          const uint16_t* kv, const uint16_t* kidx, int32_t n_local,
+                          const csa2_local* local, const uint16_t* const* kn,
+                          const uint16_t* const* vn, int32_t* q_seq_out, hipStream_t s) {
     AppendArgs a{};
     a.pos = pos;
+    a.seq = seq;
+    a.q_seq_out = q_seq_out;
     a.t_cap = cv.t_cap;
     a.fp4 = cv.fp4;
     a.kv = kv;
@@ -131,11 +137,12 @@ hipError_t enqueue_append(const CacheView& cv, const int32_t* pos, const uint16_
             d.cap = local[l].cap;
         }
         if (first || a.n_local > 0) {
-            if (hipError_t e = launch_append(a, cv.n_seq, s)) return e;
+            if (hipError_t e = launch_append(a, rows, s)) return e;
         }
         first = false;
         a.kv = nullptr;  // later launches update local rings only
         a.kidx = nullptr;
+        a.q_seq_out = nullptr;
     } while (l < n_local);
     return hipSuccess;
 }
@@ -144,11 +151,19 @@ hipError_t enqueue_append(const CacheView& cv, const int32_t* pos, const uint16_
 // pool, the current selection, per-sequence counters, top-k and attention
 // scratch.  Counters reset themselves: the workspace must start zero-filled.
 struct StackWs {
-    size_t scores, bscores, blocks, pscores, pool, sel0, ctr, topk, attn, total;
+    size_t scores, bscores, blocks, pscores, pool, sel0, ctr, topk, attn, qseq, pf, total;
 };
 
+// Whether a Full layer of a one-sequence segment takes the fused prefill top-k
+// (scores never written out) instead of dense score rows + top-k.
+bool replay_fused_full(int64_t t_cap, int32_t k, int32_t pool, int32_t block) {
+    return block == 1 && pool == 0 && k <= kPfMaxK && t_cap <= kPfMaxT;
+}
+
+// n_seq = queries (one per sequence for decode, the segment's rows for a
+// replay); replay adds the per-query sequence ids and the fused top-k scratch.
 StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, int32_t block,
-                        int32_t max_window) {
+                        int32_t max_window, bool replay = false) {
     StackWs w{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -158,7 +173,8 @@ StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, i
     };
     const int64_t nb = block > 1 ? (t_cap + block - 1) / block : 0;
     const int32_t nbsel = block > 1 ? pool / block : 0;
-    w.scores = take((size_t)n_seq * t_cap * sizeof(float));
+    const bool fused = replay && replay_fused_full(t_cap, k, pool, block);
+    w.scores = take(fused ? 1 : (size_t)n_seq * t_cap * sizeof(float));
     w.bscores = take((size_t)n_seq * (nb > 0 ? nb : 1) * sizeof(float));
     w.blocks = take((size_t)n_seq * (nbsel > 0 ? nbsel : 1) * sizeof(int32_t));
     w.pscores = take((size_t)n_seq * (pool > 0 ? pool : 1) * sizeof(float));
@@ -170,6 +186,10 @@ StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, i
     if (pool > 0) tk = std::max(tk, topk_ws_bytes(n_seq, pool, k, 0));
     w.topk = take(tk > 0 ? tk : 1);
     w.attn = take(attn_ws_bytes(n_seq, k, max_window));
+    if (replay) {
+        w.qseq = take((size_t)n_seq * sizeof(int32_t));
+        if (fused) w.pf = take(prefill_topk_ws_bytes(n_seq, t_cap));
+    }
     w.total = off;
     return w;
 }
@@ -228,8 +248,8 @@ csa2_status csa2_append(const csa2_cache* cache, const int32_t* pos, const uint1
     for (int32_t l = 0; l < n_local; ++l)
         if (csa2_status st = check_append_local(local[l], k_new[l], v_new[l])) return st;
     if (csa2_status st = device_ok()) return st;
-    return from_hip(enqueue_append(cv, pos, kv, kidx, n_local, local, k_new, v_new,
-                                   (hipStream_t)stream));
+    return from_hip(enqueue_append(cv, cv.n_seq, -1, pos, kv, kidx, n_local, local, k_new, v_new,
+                                   nullptr, (hipStream_t)stream));
 }
 
 csa2_status csa2_index_score(const csa2_cache* cache, const uint16_t* q_idx, const int32_t* q_pos,
@@ -343,45 +363,136 @@ csa2_status csa2_sparse_attn(const csa2_cache* cache, const uint16_t* q, const i
                                        (hipStream_t)stream));
 }
 
+// What one stack run needs, from a decode descriptor (one query per
+// sequence) or a replay descriptor (a segment of one sequence).
+struct StackJob {
+    int32_t n_layers;
+    const int32_t* modes;
+    int32_t nq;   // queries
+    int32_t seq;  // -1: query b is on sequence b; else every query is on `seq`
+    const int32_t* q_pos;
+    int32_t k, pool, block;
+    float sm_scale;
+    const uint16_t* const* q;
+    const uint16_t* const* q_idx;
+    const csa2_local* local;
+    uint16_t* const* out;
+    int32_t* const* sel_out;
+    int32_t* pool_out;
+    void* const* scan_events;  // [2] or null (decode only)
+    const uint16_t* app_kv;
+    const uint16_t* app_kidx;
+    const uint16_t* const* app_k;
+    const uint16_t* const* app_v;
+};
+
+// Checks shared by both descriptors: schedule, per-layer operands, local
+// rings and the rows to write into them.
+static csa2_status check_job(const StackJob& j, int32_t* max_window) {
+    if (j.n_layers <= 0) return CSA2_ERR_SHAPE;
+    if (j.k <= 0 || j.pool < 0 || j.block <= 0) return CSA2_ERR_SHAPE;
+    if (j.block != 1 && j.block != 64) return CSA2_ERR_SHAPE;
+    if (j.pool > 0 && j.pool < j.k) return CSA2_ERR_SHAPE;
+    if (j.block > 1 && (j.pool <= 0 || j.pool % j.block)) return CSA2_ERR_SHAPE;
+    if (j.modes[0] != CSA2_MODE_FULL) return CSA2_ERR_SCHEDULE;
+    int32_t mw = 0;
+    for (int32_t l = 0; l < j.n_layers; ++l) {
+        const int32_t m = j.modes[l];
+        if (m != CSA2_MODE_FULL && m != CSA2_MODE_REINDEX && m != CSA2_MODE_REUSE)
+            return CSA2_ERR_SCHEDULE;
+        if (m == CSA2_MODE_REINDEX && j.pool <= 0) return CSA2_ERR_SCHEDULE;
+        if (!j.q[l] || !j.out[l] || !aligned16(j.q[l])) return CSA2_ERR_INVALID_ARG;
+        if (m != CSA2_MODE_REUSE && (!j.q_idx || !j.q_idx[l] || !aligned16(j.q_idx[l])))
+            return CSA2_ERR_INVALID_ARG;
+        LocalView lv;
+        if (csa2_status st = check_local(&j.local[l], &lv)) return st;
+        mw = std::max(mw, lv.window);
+    }
+    if ((j.app_k != nullptr) != (j.app_v != nullptr)) return CSA2_ERR_INVALID_ARG;
+    if (j.app_k)
+        for (int32_t l = 0; l < j.n_layers; ++l) {
+            if (!j.app_k[l] && !j.app_v[l]) continue;
+            if (csa2_status st = check_append_local(j.local[l], j.app_k[l], j.app_v[l])) return st;
+            // a segment's rows must land in distinct slots
+            if (j.seq >= 0 && j.nq > j.local[l].cap) return CSA2_ERR_SHAPE;
+        }
+    *max_window = mw;
+    return CSA2_OK;
+}
+
+static StackJob decode_job(const csa2_stack_desc* d) {
+    StackJob j{};
+    j.n_layers = d->n_layers;
+    j.modes = d->modes;
+    j.nq = d->cache->n_seq;
+    j.seq = -1;
+    j.q_pos = d->q_pos;
+    j.k = d->k;
+    j.pool = d->pool;
+    j.block = d->block;
+    j.sm_scale = d->sm_scale;
+    j.q = d->q;
+    j.q_idx = d->q_idx;
+    j.local = d->local;
+    j.out = d->out;
+    j.sel_out = d->sel_out;
+    j.pool_out = d->pool_out;
+    j.scan_events = d->scan_events;
+    j.app_kv = d->append_kv;
+    j.app_kidx = d->append_kidx;
+    j.app_k = d->append_k;
+    j.app_v = d->append_v;
+    return j;
+}
+
 static csa2_status check_stack(const csa2_stack_desc* d, CacheView* cv, int32_t* max_window) {
     if (!d || !d->modes || !d->cache || !d->q_pos || !d->q || !d->local || !d->out)
         return CSA2_ERR_INVALID_ARG;
     if (d->n_layers <= 0) return CSA2_ERR_SHAPE;
     if (csa2_status st = check_cache(d->cache, true, true, cv)) return st;
     if (cv->n_seq > 65535) return CSA2_ERR_SHAPE;
-    if (d->k <= 0 || d->pool < 0 || d->block <= 0) return CSA2_ERR_SHAPE;
-    if (d->block != 1 && d->block != 64) return CSA2_ERR_SHAPE;
-    if (d->pool > 0 && d->pool < d->k) return CSA2_ERR_SHAPE;
-    if (d->block > 1 && (d->pool <= 0 || d->pool % d->block)) return CSA2_ERR_SHAPE;
-    if (d->modes[0] != CSA2_MODE_FULL) return CSA2_ERR_SCHEDULE;
-    int32_t mw = 0;
-    for (int32_t l = 0; l < d->n_layers; ++l) {
-        const int32_t m = d->modes[l];
-        if (m != CSA2_MODE_FULL && m != CSA2_MODE_REINDEX && m != CSA2_MODE_REUSE)
-            return CSA2_ERR_SCHEDULE;
-        if (m == CSA2_MODE_REINDEX && d->pool <= 0) return CSA2_ERR_SCHEDULE;
-        if (!d->q[l] || !d->out[l] || !aligned16(d->q[l])) return CSA2_ERR_INVALID_ARG;
-        if (m != CSA2_MODE_REUSE && (!d->q_idx || !d->q_idx[l] || !aligned16(d->q_idx[l])))
-            return CSA2_ERR_INVALID_ARG;
-        LocalView lv;
-        if (csa2_status st = check_local(&d->local[l], &lv)) return st;
-        mw = std::max(mw, lv.window);
-    }
     if (d->append_kidx && !d->append_kv) return CSA2_ERR_INVALID_ARG;
-    if ((d->append_k != nullptr) != (d->append_v != nullptr)) return CSA2_ERR_INVALID_ARG;
     if (d->append_k && !d->append_kv) return CSA2_ERR_INVALID_ARG;
-    if (d->append_kv) {
-        if (!aligned16(d->append_kv) || (d->append_kidx && !aligned16(d->append_kidx)))
-            return CSA2_ERR_INVALID_ARG;
-        if (d->append_k)
-            for (int32_t l = 0; l < d->n_layers; ++l) {
-                if (!d->append_k[l] && !d->append_v[l]) continue;
-                if (csa2_status st = check_append_local(d->local[l], d->append_k[l], d->append_v[l]))
-                    return st;
-            }
-    }
-    *max_window = mw;
-    return CSA2_OK;
+    if (d->append_kv &&
+        (!aligned16(d->append_kv) || (d->append_kidx && !aligned16(d->append_kidx))))
+        return CSA2_ERR_INVALID_ARG;
+    return check_job(decode_job(d), max_window);
+}
+
+static StackJob replay_job(const csa2_replay_desc* d) {
+    StackJob j{};
+    j.n_layers = d->n_layers;
+    j.modes = d->modes;
+    j.nq = d->n;
+    j.seq = d->seq;
+    j.q_pos = d->q_pos;
+    j.k = d->k;
+    j.pool = d->pool;
+    j.block = d->block;
+    j.sm_scale = d->sm_scale;
+    j.q = d->q;
+    j.q_idx = d->q_idx;
+    j.local = d->local;
+    j.out = d->out;
+    j.sel_out = d->sel_out;
+    j.pool_out = d->pool_out;
+    j.app_k = d->local_k;
+    j.app_v = d->local_v;
+    return j;
+}
+
+static csa2_status check_replay(const csa2_replay_desc* d, CacheView* cv, int32_t* max_window) {
+    if (!d || !d->modes || !d->cache || !d->q_pos || !d->q || !d->local || !d->out)
+        return CSA2_ERR_INVALID_ARG;
+    if (d->n_layers <= 0) return CSA2_ERR_SHAPE;
+    if (csa2_status st = check_cache(d->cache, true, true, cv)) return st;
+    if (d->seq < 0 || d->seq >= cv->n_seq) return CSA2_ERR_SHAPE;
+    if (d->n <= 0 || d->n > 65535) return CSA2_ERR_SHAPE;
+    return check_job(replay_job(d), max_window);
+}
+
+static StackWs job_ws_layout(const StackJob& j, const CacheView& cv, int32_t mw) {
+    return stack_ws_layout(j.nq, cv.t_cap, j.k, j.pool, j.block, mw, j.seq >= 0);
 }
 
 csa2_status csa2_stack_workspace(const csa2_stack_desc* d, size_t* bytes) {
@@ -389,76 +500,93 @@ csa2_status csa2_stack_workspace(const csa2_stack_desc* d, size_t* bytes) {
     CacheView cv;
     int32_t mw;
     if (csa2_status st = check_stack(d, &cv, &mw)) return st;
-    *bytes = stack_ws_layout(cv.n_seq, cv.t_cap, d->k, d->pool, d->block, mw).total;
+    *bytes = job_ws_layout(decode_job(d), cv, mw).total;
+    return CSA2_OK;
+}
+
+csa2_status csa2_replay_workspace(const csa2_replay_desc* d, size_t* bytes) {
+    if (!bytes) return CSA2_ERR_INVALID_ARG;
+    CacheView cv;
+    int32_t mw;
+    if (csa2_status st = check_replay(d, &cv, &mw)) return st;
+    *bytes = job_ws_layout(replay_job(d), cv, mw).total;
     return CSA2_OK;
 }
 
 }  // extern "C"
 
 // Enqueue every layer of a validated stack on s.
-static csa2_status enqueue_stack(const csa2_stack_desc* d, const CacheView& cv, const StackWs& W,
+static csa2_status enqueue_stack(const StackJob& j, const CacheView& cv, const StackWs& W,
                                  void* ws, hipStream_t s) {
     char* base = static_cast<char*>(ws);
     float* scores = reinterpret_cast<float*>(base + W.scores);
     float* bscores = reinterpret_cast<float*>(base + W.bscores);
     int32_t* blocks = reinterpret_cast<int32_t*>(base + W.blocks);
     float* pscores = reinterpret_cast<float*>(base + W.pscores);
-    int32_t* pool = d->pool_out ? d->pool_out : reinterpret_cast<int32_t*>(base + W.pool);
+    int32_t* pool = j.pool_out ? j.pool_out : reinterpret_cast<int32_t*>(base + W.pool);
     int32_t* selbuf = reinterpret_cast<int32_t*>(base + W.sel0);
     uint32_t* ctr = reinterpret_cast<uint32_t*>(base + W.ctr);
     void* tkws = base + W.topk;
     void* atws = base + W.attn;
-    const int32_t* q_seq = nullptr;  // query b reads sequence b
-    const int32_t S = cv.n_seq, k = d->k, P = d->pool, B = d->block;
+    const bool replay = j.seq >= 0;
+    // decode: query b reads sequence b; replay: the ids the append step writes
+    int32_t* q_seq = replay ? reinterpret_cast<int32_t*>(base + W.qseq) : nullptr;
+    const int32_t S = j.nq, k = j.k, P = j.pool, B = j.block;
+    const bool fused_full = replay && replay_fused_full(cv.t_cap, k, P, B);
     // score the pool with layer l's indexer query and keep the top k
     auto rescore_pool = [&](int32_t l, int32_t* dst) -> hipError_t {
         if (P <= kFusedSelectMax)
-            return launch_score_select(cv, d->q_idx[l], d->q_pos, q_seq, S, pool, P, pscores, ctr,
+            return launch_score_select(cv, j.q_idx[l], j.q_pos, q_seq, S, pool, P, pscores, ctr,
                                        k, dst, s);
-        hipError_t e = launch_score_cand(cv, d->q_idx[l], d->q_pos, q_seq, S, pool, P, pscores, P, s);
+        hipError_t e = launch_score_cand(cv, j.q_idx[l], j.q_pos, q_seq, S, pool, P, pscores, P, s);
         if (e == hipSuccess) e = launch_topk(pscores, S, P, P, pool, k, dst, 0, nullptr, tkws, s);
         return e;
     };
-    if (d->append_kv) {
-        const int32_t nl = d->append_k ? d->n_layers : 0;
-        if (enqueue_append(cv, d->q_pos, d->append_kv, d->append_kidx, nl, d->local, d->append_k,
-                           d->append_v, s) != hipSuccess)
+    // decode append of the new positions, or the segment's ring rows (the
+    // replay always launches it: it also writes the sequence ids)
+    if (j.app_kv || replay) {
+        const int32_t nl = j.app_k ? j.n_layers : 0;
+        if (enqueue_append(cv, S, j.seq, j.q_pos, j.app_kv, j.app_kidx, nl, j.local, j.app_k,
+                           j.app_v, q_seq, s) != hipSuccess)
             return CSA2_ERR_HIP;
     }
     const int32_t* cur = nullptr;
-    for (int32_t l = 0; l < d->n_layers; ++l) {
-        const int32_t m = d->modes[l];
-        int32_t* sel_l = (d->sel_out && d->sel_out[l]) ? d->sel_out[l] : nullptr;
+    for (int32_t l = 0; l < j.n_layers; ++l) {
+        const int32_t m = j.modes[l];
+        int32_t* sel_l = (j.sel_out && j.sel_out[l]) ? j.sel_out[l] : nullptr;
         hipError_t e = hipSuccess;
         if (m == CSA2_MODE_FULL || m == CSA2_MODE_REINDEX) {
             int32_t* dst = sel_l ? sel_l : selbuf;
             // layer 0 is Full: on a stream being recorded into a graph the
             // events bracket the scan; otherwise they take the kernel's own
             // start and end times
-            const bool timed = l == 0 && d->scan_events[0] && d->scan_events[1];
+            const bool timed = l == 0 && j.scan_events && j.scan_events[0] && j.scan_events[1];
             hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
             if (timed) e = hipStreamIsCapturing(s, &cap);
             const bool own = timed && e == hipSuccess && cap == hipStreamCaptureStatusNone;
-            hipEvent_t ev0 = own ? (hipEvent_t)d->scan_events[0] : nullptr;
-            hipEvent_t ev1 = own ? (hipEvent_t)d->scan_events[1] : nullptr;
+            hipEvent_t ev0 = own ? (hipEvent_t)j.scan_events[0] : nullptr;
+            hipEvent_t ev1 = own ? (hipEvent_t)j.scan_events[1] : nullptr;
             const bool around = timed && !own;
-            if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[0], s);
+            if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)j.scan_events[0], s);
             if (e != hipSuccess) return CSA2_ERR_HIP;
-            if (m == CSA2_MODE_FULL && B == 1) {
-                e = launch_score_dense(cv, d->q_idx[l], d->q_pos, q_seq, S, 1, scores, cv.t_cap, s, ev0,
-                                       ev1);
-                if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
+            if (m == CSA2_MODE_FULL && fused_full) {
+                e = launch_prefill_topk(cv, j.seq, j.q_idx[l], j.q_pos, S, k, dst, base + W.pf, s);
+            } else if (m == CSA2_MODE_FULL && B == 1) {
+                e = replay ? launch_score_mq(cv, j.seq, j.q_idx[l], j.q_pos, S, scores, cv.t_cap, s)
+                           : launch_score_dense(cv, j.q_idx[l], j.q_pos, q_seq, S, 1, scores,
+                                                cv.t_cap, s, ev0, ev1);
+                if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)j.scan_events[1], s);
                 if (e == hipSuccess)
                     e = launch_topk(scores, S, cv.t_cap, cv.t_cap, nullptr, k, dst, P, P ? pool : nullptr,
                                     tkws, s);
             } else if (m == CSA2_MODE_FULL) {
                 const int64_t nb = (cv.t_cap + B - 1) / B;
                 const int32_t nbsel = P / B;
-                e = launch_score_dense(cv, d->q_idx[l], d->q_pos, q_seq, S, B, bscores, nb, s, ev0, ev1);
-                if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)d->scan_events[1], s);
+                e = launch_score_dense(cv, j.q_idx[l], j.q_pos, q_seq, S, B, bscores, nb, s, ev0, ev1);
+                if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)j.scan_events[1], s);
                 if (e == hipSuccess)
                     e = launch_topk(bscores, S, nb, nb, nullptr, nbsel, blocks, 0, nullptr, tkws, s);
-                if (e == hipSuccess) e = launch_expand_blocks(blocks, S, nbsel, B, d->q_pos, pool, s);
+                if (e == hipSuccess) e = launch_expand_blocks(blocks, S, nbsel, B, j.q_pos, pool, s);
                 if (e == hipSuccess) e = rescore_pool(l, dst);
             } else {
                 e = rescore_pool(l, dst);
@@ -469,8 +597,8 @@ static csa2_status enqueue_stack(const csa2_stack_desc* d, const CacheView& cv, 
         }
         if (e != hipSuccess) return CSA2_ERR_HIP;
         LocalView lv;
-        check_local(&d->local[l], &lv);
-        e = launch_sparse_attn(cv, d->q[l], d->q_pos, q_seq, S, cur, k, lv, d->sm_scale, d->out[l],
+        check_local(&j.local[l], &lv);
+        e = launch_sparse_attn(cv, j.q[l], j.q_pos, q_seq, S, cur, k, lv, j.sm_scale, j.out[l],
                                atws, s);
         if (e != hipSuccess) return CSA2_ERR_HIP;
     }
@@ -483,10 +611,22 @@ csa2_status csa2_stack_run(const csa2_stack_desc* d, void* ws, size_t ws_bytes, 
     CacheView cv;
     int32_t mw;
     if (csa2_status st = check_stack(d, &cv, &mw)) return st;
-    const StackWs W = stack_ws_layout(cv.n_seq, cv.t_cap, d->k, d->pool, d->block, mw);
+    const StackJob j = decode_job(d);
+    const StackWs W = job_ws_layout(j, cv, mw);
     if (!ws || ws_bytes < W.total) return CSA2_ERR_WORKSPACE;
     if (csa2_status st = device_ok()) return st;
-    return enqueue_stack(d, cv, W, ws, (hipStream_t)stream);
+    return enqueue_stack(j, cv, W, ws, (hipStream_t)stream);
+}
+
+csa2_status csa2_replay_run(const csa2_replay_desc* d, void* ws, size_t ws_bytes, void* stream) {
+    CacheView cv;
+    int32_t mw;
+    if (csa2_status st = check_replay(d, &cv, &mw)) return st;
+    const StackJob j = replay_job(d);
+    const StackWs W = job_ws_layout(j, cv, mw);
+    if (!ws || ws_bytes < W.total) return CSA2_ERR_WORKSPACE;
+    if (csa2_status st = device_ok()) return st;
+    return enqueue_stack(j, cv, W, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"
@@ -507,7 +647,8 @@ csa2_status csa2_stack_plan_create(const csa2_stack_desc* d, void* ws, size_t ws
     CacheView cv;
     int32_t mw;
     if (csa2_status st = check_stack(d, &cv, &mw)) return st;
-    const StackWs W = stack_ws_layout(cv.n_seq, cv.t_cap, d->k, d->pool, d->block, mw);
+    const StackJob j = decode_job(d);
+    const StackWs W = job_ws_layout(j, cv, mw);
     if (!ws || ws_bytes < W.total) return CSA2_ERR_WORKSPACE;
     if (csa2_status st = device_ok()) return st;
     hipStream_t cs = nullptr;
@@ -517,7 +658,7 @@ csa2_status csa2_stack_plan_create(const csa2_stack_desc* d, void* ws, size_t ws
     if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
         st = CSA2_ERR_HIP;
     } else {
-        st = enqueue_stack(d, cv, W, ws, cs);
+        st = enqueue_stack(j, cv, W, ws, cs);
         // the capture must be ended whatever happened inside it
         if (hipStreamEndCapture(cs, &graph) != hipSuccess && st == CSA2_OK) st = CSA2_ERR_HIP;
     }

@@ -36,16 +36,18 @@ constexpr int kMaxAppendLayers = 32;  // layers per launch (kernel argument size
 struct AppendLocal {
     uint16_t* k;
     uint16_t* v;
-    const uint16_t* k_new;  // bf16 [n_seq][128]
+    const uint16_t* k_new;  // bf16 [n rows][128]
     const uint16_t* v_new;
     int32_t cap;
 };
 struct AppendArgs {
-    const int32_t* pos;  // [n_seq]; rows outside [0, t_cap) are skipped
+    const int32_t* pos;  // [n rows]; rows outside [0, t_cap) are skipped
+    int32_t seq;         // -1: row b belongs to sequence b; else every row to `seq`
+    int32_t* q_seq_out;  // null, or [n rows]: receives each row's sequence
     int64_t t_cap;
     int32_t fp4;
-    const uint16_t* kv;    // bf16 [n_seq][256]
-    const uint16_t* kidx;  // bf16 [n_seq][64] or null
+    const uint16_t* kv;    // bf16 [n rows][256] or null
+    const uint16_t* kidx;  // bf16 [n rows][64] or null
     uint8_t* codes;        // FP4 cache
     uint8_t* scales;
     uint16_t* bf16;        // bf16 cache
@@ -53,7 +55,7 @@ struct AppendArgs {
     int32_t n_local;
     AppendLocal local[kMaxAppendLayers];
 };
-hipError_t launch_append(const AppendArgs& a, int32_t n_seq, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, int32_t n_rows, hipStream_t s);
 
 // With ev0/ev1 set, the kernel's own start and end times are recorded in them.
 hipError_t launch_score_dense(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,

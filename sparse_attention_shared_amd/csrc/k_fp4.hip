@@ -97,11 +97,13 @@ __global__ __launch_bounds__(256) void k_pack_fp4(const uint16_t* __restrict__ x
 
 // ---- decode append ("CED", section "Why Prefill Recomputes a Recent
 // Segment": after a token is chosen, every layer updates its local state and
-// the global KV of the new position is appended).  Grid (n_seq, 1 + layer
-// groups): workgroup (b, 0) packs (or copies) sequence b's global K | V row,
-// one element per thread, and copies its indexer key; in workgroup (b, g > 0)
-// each wave copies one 256-byte local row (K or V of one layer), 4 bytes per
-// lane, so the ring descriptor is wave-uniform.  Every thread issues the position load and its source load
+// the global KV of the new position is appended); also the ring rows of a
+// replayed segment ("Why Prefill Recomputes a Recent Segment"), where every
+// row belongs to one sequence.  Grid (rows, 1 + layer groups): workgroup
+// (b, 0) packs (or copies) row b's global K | V, one element per thread, and
+// copies its indexer key; in workgroup (b, g > 0) each wave copies one
+// 256-byte local row (K or V of one layer), 4 bytes per lane, so the ring
+// descriptor is wave-uniform.  Every thread issues the position load and its source load
 // before it waits for either (`hold`), so a launch costs about two memory
 // round trips.
 constexpr int kAppendLayersPerWg = 2;
@@ -116,7 +118,9 @@ __device__ __forceinline__ void hold(T& x) {
 
 __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     const int b = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+    const int64_t sb = a.seq >= 0 ? a.seq : b;  // the row's sequence
     if (g == 0) {
+        if (a.q_seq_out && tid == 0) a.q_seq_out[b] = (int32_t)sb;
         // one element of the K | V row per thread: the 32 lanes of a block
         // reduce its largest magnitude and OR their nibbles into code words,
         // so the pack costs a few dozen instructions of latency
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
         hold(ki);
         hold(p);
         if (p < 0 || p >= a.t_cap) return;
-        const int64_t row = (int64_t)b * a.t_cap + p;
+        const int64_t row = sb * a.t_cap + p;
         if (a.kidx && tid < 8) reinterpret_cast<uint4*>(a.k_idx + row * 64)[tid] = ki;
         if (!a.kv) return;
         if (!a.fp4) {
@@ -164,14 +168,14 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     hold(v);
     hold(p);
     if (p < 0 || p >= a.t_cap) return;
-    const int64_t slot = (int64_t)b * cap + p % cap;
+    const int64_t slot = sb * cap + p % cap;
     dst[slot * 64 + lane] = v;
 }
 
-hipError_t launch_append(const AppendArgs& a, int32_t n_seq, hipStream_t s) {
-    if (n_seq == 0) return hipSuccess;
+hipError_t launch_append(const AppendArgs& a, int32_t n_rows, hipStream_t s) {
+    if (n_rows == 0) return hipSuccess;
     const uint32_t groups = (uint32_t)((a.n_local + kAppendLayersPerWg - 1) / kAppendLayersPerWg);
-    hipLaunchKernelGGL(k_append, dim3((uint32_t)n_seq, 1 + groups), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_append, dim3((uint32_t)n_rows, 1 + groups), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

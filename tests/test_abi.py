@@ -234,3 +234,60 @@ def test_append_without_a_device_reports_no_device():
     rows = (ctypes.c_void_p * 1)(0x10000)
     assert L.csa2_append(ctypes.byref(c), FAKE, FAKE, FAKE, 1, loc, rows, rows, None) == NO_DEVICE
     assert L.csa2_append(ctypes.byref(c), FAKE, None, None, 0, None, None, None, None) == NO_DEVICE
+
+
+def _replay(modes=(0, 2), seq=0, n=8, k=16, pool=0, cap=128, rows=True):
+    keep = {}
+    Lr = len(modes)
+    keep["cache"] = _cache()
+    keep["modes"] = (ctypes.c_int32 * Lr)(*modes)
+    ptrs = (ctypes.c_void_p * Lr)(*([0x10000] * Lr))
+    keep["ptrs"] = ptrs
+    keep["loc"] = (_lib.csa2_local * Lr)(*[_lib.csa2_local(FAKE, FAKE, cap, 32, 0)] * Lr)
+    lr = ptrs if rows else None
+    d = _lib.csa2_replay_desc(Lr, keep["modes"], ctypes.pointer(keep["cache"]), seq, n, FAKE, k,
+                              pool, 1, 0.1, ptrs, ptrs, keep["loc"], lr, lr, ptrs, None, None)
+    return d, keep
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(seq=2), SHAPE),               # sequence out of range (n_seq = 2)
+    (dict(seq=-1), SHAPE),
+    (dict(n=0), SHAPE),
+    (dict(n=200, cap=128), SHAPE),      # segment rows would share ring slots
+    (dict(n=200, cap=128, rows=False), OK),  # no rows written: any n
+    (dict(modes=(2, 0)), SCHEDULE),     # Reuse first
+    (dict(modes=(0, 1)), SCHEDULE),     # Reindex without a pool
+    (dict(), OK),
+])
+def test_replay_validation(kw, want):
+    L = csa2.lib()
+    d, keep = _replay(**kw)
+    n = _lib._sz()
+    assert L.csa2_replay_workspace(ctypes.byref(d), ctypes.byref(n)) == want
+    if want != OK:
+        assert L.csa2_replay_run(ctypes.byref(d), FAKE, 1 << 30, None) == want
+    else:
+        assert n.value > 0
+        assert L.csa2_replay_run(ctypes.byref(d), FAKE, n.value - 1, None) == WORKSPACE
+
+
+def test_replay_null_operands():
+    L = csa2.lib()
+    d, keep = _replay()
+    d.q_pos = None
+    n = _lib._sz()
+    assert L.csa2_replay_workspace(ctypes.byref(d), ctypes.byref(n)) == INVALID
+    d, keep = _replay()
+    odd = (ctypes.c_void_p * 2)(0x10000, 0x10004)
+    d.local_v = odd
+    assert L.csa2_replay_workspace(ctypes.byref(d), ctypes.byref(n)) == INVALID
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a GPU")
+def test_replay_without_a_device_reports_no_device():
+    L = csa2.lib()
+    d, keep = _replay()
+    n = _lib._sz()
+    assert L.csa2_replay_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert L.csa2_replay_run(ctypes.byref(d), FAKE, n.value, None) == NO_DEVICE
