@@ -19,7 +19,9 @@ several copies of the cache so that consecutive steps do not find it in the
 With --workload prefill it times the prefill chunk instead: 4096 queries at
 positions 126976..131071 of one 131072-token sequence, each selecting its
 top-2048 positions (csa2_prefill_topk) and attending to them plus its window
-(csa2_sparse_attn), reported as query positions per second.
+(csa2_sparse_attn), reported as query positions per second.  With --workload
+replay it times the bounded replay of the last 128 positions of one
+131072-token sequence through the same 20-layer stack (csa2_replay_run).
 
 Prints one JSON line (see the repository's design doc for the fields).
 """
@@ -137,6 +139,126 @@ def cpu_baseline_prefill(x, sp, budget_s=12.0):
                       "attention) in %.1f s, one thread" % (n, el)}
 
 
+REPLAY_METRIC = "CSA2 bounded-replay query positions/s (last 128 positions, 20 layers) at 128k ctx"
+
+
+def replay_spec():
+    """The 20-layer workload's stack on one 131072-token sequence, replaying
+    its last 128 positions with every window cut off at the segment."""
+    import synth
+    base = synth.config(3)
+    n, T = 128, base.t_cap
+    return synth.Spec("replay", n_seq=1, t_cap=T, q_pos=list(range(T - n, T)), q_seq=[0] * n,
+                      kv_format="fp4", k=base.k, window=base.window, pool=base.pool,
+                      schedule=base.schedule, local_cap=128, lo=T - n, seed=1007)
+
+
+def cpu_baseline_replay(x, sp, k_new, v_new, budget_s=12.0):
+    """The oracle on a bounded sample of the replay: sub-segments of 4
+    positions through all 20 layers until the budget."""
+    import oracle
+    c = oracle.Cache(x.kv, x.k_idx, fp4=True)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        i = (n * 4) % sp.nq
+        sl = slice(i, i + 4)
+        oracle.replay(c, sp.schedule, 0, x.q_pos[sl], x.q[:, sl], x.q_idx[:, sl], x.local_k,
+                      x.local_v, sp.window, sp.lo, sp.k, sp.pool, k_new[:, sl], v_new[:, sl])
+        n += 4
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 128:
+            break
+    return {"value": n / el, "unit": "query positions/s", "cores": 1, "kind": "oracle",
+            "sample": "%d segment positions (groups of 4) through the 20 layers in %.1f s, one "
+                      "thread" % (n, el)}
+
+
+def bench_replay(args):
+    """One step = csa2_replay_run of the last 128 positions of a 131072-token
+    sequence through the 20-layer stack (ring rows, Full / Reindex / Reuse
+    selections, attention), inputs resident in HBM."""
+    import ctypes
+    import numpy as np
+    import torch
+    import synth
+    import sparse_attention_shared_amd as csa2
+    from sparse_attention_shared_amd import _lib
+
+    sp = replay_spec()
+    L, n = sp.n_layers, sp.nq
+    print("generating inputs ...", file=sys.stderr, flush=True)
+    x = synth.make_inputs(sp)
+    rng = np.random.default_rng(7)
+    k_new = synth.f32_to_bf16_bits(rng.standard_normal((L, n, 128)).astype(np.float32))
+    v_new = synth.f32_to_bf16_bits(rng.standard_normal((L, n, 128)).astype(np.float32))
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    codes, scales = csa2.pack_fp4(d16(x.kv))
+    cache = csa2.Cache(codes, d16(x.k_idx), scales)
+    q_pos = torch.from_numpy(x.q_pos).cuda()
+    q = [d16(x.q[l]) for l in range(L)]
+    q_idx = [d16(x.q_idx[l]) if sp.schedule[l] != synth.REUSE else None for l in range(L)]
+    local = [csa2.Local(d16(x.local_k[l]), d16(x.local_v[l]), sp.window, sp.lo) for l in range(L)]
+    lk = [d16(k_new[l]) for l in range(L)]
+    lv = [d16(v_new[l]) for l in range(L)]
+    out = [torch.empty((n, 16, 128), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    args_c = _lib._ReplayArgs(cache, sp.schedule, 0, q_pos, q, q_idx, local, out, sp.k, sp.pool,
+                              1, 128 ** -0.5, lk, lv)
+    ws = torch.zeros(_lib.replay_workspace(args_c), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    L_ = csa2.lib()
+
+    def step():
+        st = L_.csa2_replay_run(ctypes.byref(args_c.desc), _lib._ptr(ws), ws.numel(),
+                                _lib._stream())
+        if st:
+            raise RuntimeError("csa2_replay_run status %d" % st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+    result = {
+        "metric": REPLAY_METRIC,
+        "value": n / (ms * 1e-3),
+        "unit": "query positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "bounded replay: the last 128 positions of one 131072-token sequence "
+                        "through the 20-layer CSA2 stack (Full pool 8192 then [Reindex, Reuse "
+                        "x3]*, top-k 2048, SWA 128 cut off at the segment), FP4 (E2M1 + E8M0/32) "
+                        "shared KV, 16 q heads / 1 KV head, head_dim 128, indexer dim 64",
+            "queries": n, "context": sp.t_cap, "layers": L, "k": sp.k, "pool": sp.pool,
+            "window": sp.window,
+        },
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("timing the oracle on the host ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_replay(x, sp, k_new, v_new)
+    print(json.dumps(result), flush=True)
+
+
 def bench_prefill(args):
     """One step = the whole 4096-query prefill chunk: fused indexer top-k then
     attention, both through the C ABI, inputs resident in HBM."""
@@ -249,7 +371,7 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["repeat", "page"], default="repeat")
-    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode")
+    ap.add_argument("--workload", choices=["decode", "prefill", "replay"], default="decode")
     ap.add_argument("--graph", action="store_true",
                     help="replay a recorded stack (HIP graph) per step instead of host launches")
     ap.add_argument("--no-append", action="store_true",
@@ -271,6 +393,9 @@ def main():
     csa2.device_check()
     if args.workload == "prefill":
         bench_prefill(args)
+        return
+    if args.workload == "replay":
+        bench_replay(args)
         return
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 18  # float32 elements

@@ -225,7 +225,7 @@ csa2_status csa2_expand_blocks(const int32_t *blocks, int32_t nq, int32_t nb, in
  * (fp32 accumulation, rounded to nearest even).  A query with no entry at
  * all gets zeros.  q_seq may be NULL (query i reads sequence i).  nq <= 65535.
  * ws: at least csa2_sparse_attn_workspace bytes: 0 when one workgroup covers
- * a query (k <= 256 and window <= 32, or nq >= 256, where each query gets one
+ * a query (k <= 256 and window <= 32, or nq >= 64, where each query gets one
  * workgroup of its own); otherwise it holds per-chunk partials and per-query
  * counters that reset themselves, so it must be zero-filled before its first
  * use and calls sharing it must not overlap. */

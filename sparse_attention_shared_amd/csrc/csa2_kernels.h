@@ -99,8 +99,12 @@ hipError_t launch_expand_blocks(const int32_t* blocks, int32_t nq, int32_t nb, i
                                 const int32_t* q_pos, int32_t* tokens, hipStream_t s);
 
 // From this many queries on, attention runs one workgroup per query (no
-// workspace); below it, each query is split over several workgroups.
-constexpr int32_t kManyQueries = 256;
+// workspace); below it, each query is split over several workgroups.  The
+// split kernel holds ~105 KB of LDS (one workgroup per CU) and takes ~9
+// workgroups per query, so from ~64 queries on it needs three or more waves
+// of workgroups and the one-per-query loop is faster (measured: 128 queries
+// with k = 2048, W = 128 take 64 us split, 39 us in the loop).
+constexpr int32_t kManyQueries = 64;
 
 // Per-query arrival counters sit 256 bytes apart, so the workgroups of
 // different queries never contend for one cache line.

@@ -89,6 +89,10 @@ def test_score_topk_attn_validation():
     assert L.csa2_sparse_attn_workspace(2, 8, 32, ctypes.byref(n)) == OK and n.value == 0
     assert L.csa2_sparse_attn_workspace(2, 8, 128, ctypes.byref(n)) == OK and n.value > 0
     assert L.csa2_sparse_attn_workspace(2, 2048, 128, ctypes.byref(n)) == OK and n.value > 0
+    # from 64 queries on every query has a workgroup of its own
+    m = _lib._sz()
+    assert L.csa2_sparse_attn_workspace(63, 2048, 128, ctypes.byref(m)) == OK and m.value > 0
+    assert L.csa2_sparse_attn_workspace(64, 2048, 128, ctypes.byref(m)) == OK and m.value == 0
     assert L.csa2_sparse_attn(bp(c), FAKE, FAKE, None, 2, FAKE, 2048, bp(loc), 0.1, FAKE, FAKE,
                               n.value - 1, None) == WORKSPACE
 

@@ -173,13 +173,15 @@ def test_sparse_attn_on_oracle_selection(kv, window, lo, cap):
     log("attn max abs err", err)
 
 
-@pytest.mark.parametrize("kv,window,lo,cap", [("fp4", 40, 0, 64), ("bf16", 40, 0, 64),
-                                              ("fp4", 0, 0, 64), ("fp4", 64, 4090, 64)])
-def test_sparse_attn_many_queries(kv, window, lo, cap):
-    """300 queries: one workgroup per query (the prefill layout); k = 96 puts
-    the selection/window boundary inside a 32-entry tile."""
+@pytest.mark.parametrize("kv,window,lo,cap,nq", [
+    ("fp4", 40, 0, 64, 300), ("bf16", 40, 0, 64, 300), ("fp4", 0, 0, 64, 300),
+    ("fp4", 64, 4090, 64, 300),
+    ("fp4", 40, 0, 64, 64), ("fp4", 40, 0, 64, 63)])  # both sides of the layout switch
+def test_sparse_attn_many_queries(kv, window, lo, cap, nq):
+    """From 64 queries on, one workgroup per query (the prefill layout), below
+    it split workgroups; k = 96 puts the selection/window boundary inside a
+    32-entry tile."""
     rng = np.random.default_rng(77)
-    nq = 300
     q_pos = [int(v) for v in rng.integers(0, 5003, nq)]
     q_pos[:4] = [5002, 0, 31, 4100]
     q_seq = [int(v) for v in rng.integers(0, 3, nq)]
