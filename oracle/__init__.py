@@ -46,6 +46,10 @@ def lib():
         i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         L.orc_fp4_pack.argtypes = [P, i64, i32, P, P]
         L.orc_fp4_unpack.argtypes = [P, P, i64, i32, P]
+        L.orc_fp4e_pack.argtypes = [P, i64, i32, P, P]
+        L.orc_fp4e_unpack.argtypes = [P, P, i64, i32, P]
+        L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_value.restype = dbl
         L.orc_scores.argtypes = [P, P, i64, P]
         L.orc_scores.restype = None
         L.orc_block_scores.argtypes = [P, i64, i32, P]
@@ -101,6 +105,36 @@ def fp4_unpack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return out
 
 
+def fp4e_pack(x_bf16: np.ndarray):
+    """FP4 with one E4M3 scale per 16: [..., dim] bf16 bits -> (codes
+    [..., dim/2] u8, scales [..., dim/16] u8)."""
+    x = _c(x_bf16, np.uint16)
+    dim = x.shape[-1]
+    rows = x.size // dim
+    codes = np.empty(x.shape[:-1] + (dim // 2,), np.uint8)
+    scales = np.empty(x.shape[:-1] + (dim // 16,), np.uint8)
+    rc = lib().orc_fp4e_pack(_p(x), rows, dim, _p(codes), _p(scales))
+    if rc:
+        raise ValueError("orc_fp4e_pack rc=%d" % rc)
+    return codes, scales
+
+
+def fp4e_unpack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    s = _c(scales, np.uint8)
+    dim = c.shape[-1] * 2
+    rows = c.size // c.shape[-1]
+    out = np.empty(c.shape[:-1] + (dim,), np.float64)
+    rc = lib().orc_fp4e_unpack(_p(c), _p(s), rows, dim, _p(out))
+    if rc:
+        raise ValueError("orc_fp4e_unpack rc=%d" % rc)
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(int(code))
+
+
 def scores(q_idx: np.ndarray, k_idx: np.ndarray) -> np.ndarray:
     q = _c(q_idx, np.uint16)
     k = _c(k_idx, np.uint16)
@@ -137,22 +171,30 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.n
 class Cache:
     """The global cache of every sequence as the oracle reads it.
 
-    For FP4 the oracle quantises the bf16 rows with its own packer.
+    For FP4 the oracle quantises the bf16 rows with its own packer: one E8M0
+    scale per 32 (``scale="e8m0"``) or one E4M3 scale per 16 (``"e4m3"``).
     """
 
-    def __init__(self, kv_bf16: np.ndarray, k_idx: np.ndarray, fp4: bool):
+    def __init__(self, kv_bf16: np.ndarray, k_idx: np.ndarray, fp4: bool, scale: str = "e8m0"):
         self.t_cap = kv_bf16.shape[1]
         self.fp4 = bool(fp4)
+        self.fmt = 0
         self.k_idx = _c(k_idx, np.uint16)
         if self.fp4:
             self.kv = None
-            self.codes, self.scales = fp4_pack(kv_bf16)
+            if scale == "e4m3":
+                self.fmt = 2
+                self.codes, self.scales = fp4e_pack(kv_bf16)
+            else:
+                assert scale == "e8m0", scale
+                self.fmt = 1
+                self.codes, self.scales = fp4_pack(kv_bf16)
         else:
             self.kv = _c(kv_bf16, np.uint16)
             self.codes = self.scales = None
 
     def args(self):
-        return (int(self.fp4), self.t_cap, _p(self.kv), _p(self.codes), _p(self.scales))
+        return (self.fmt, self.t_cap, _p(self.kv), _p(self.codes), _p(self.scales))
 
 
 def layer(cache: Cache, q_pos, q_seq, mode, q, q_idx, lk, lv, window, lo, k,

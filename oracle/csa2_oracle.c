@@ -134,6 +134,106 @@ int orc_fp4_unpack(const uint8_t *codes, const uint8_t *scales, int64_t rows, in
     return 0;
 }
 
+/* ------------------------------------------------- FP4 with E4M3 / 16 */
+
+/* The pages' own form of the FP4 cache [KVC, summary and closing paragraph]:
+ * E2M1 elements with one E4M3 scale per 16 channels.  E4M3 is the 8-bit
+ * float with 1 sign bit, 4 exponent bits (bias 7) and 3 mantissa bits, no
+ * infinities, and S.1111.111 as NaN; exponent field 0 holds subnormals
+ * m/8 * 2^-6.  Readings (the pages fix neither): the scale of a block is the
+ * finite non-negative E4M3 value nearest to amax / 6 (so the block's largest
+ * magnitude lands on E2M1's largest, 6), ties to the even code; each element
+ * becomes the E2M1 magnitude c whose value c * s is nearest to |x| (ties to
+ * the even code, beyond 6 s the nearest is 6 s); the sign bit is kept; a
+ * block whose scale is 0 has every magnitude code 0. */
+double orc_e4m3_value(uint8_t b)
+{
+    int e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);
+    return (b & 0x80) ? -v : v;
+}
+
+/* Scale code of a block: scan the non-negative finite codes 0x00..0x7E and
+ * keep the one with the least |6 v - amax| (exact in double: v has 4
+ * significant bits, amax 8), ties to the even code. */
+static uint8_t e4m3_block_scale(double amax)
+{
+    int best = 0;
+    double bd = fabs(amax);
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs(6.0 * orc_e4m3_value((uint8_t)c) - amax);
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return (uint8_t)best;
+}
+
+/* E2M1 magnitude code of |x| = a under scale s > 0: the c with the least
+ * |e2m1(c) s - a| (exact products), ties to the even code. */
+static int e2m1_nearest_scaled(double a, double s)
+{
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        double d = fabs(e2m1_mag[c] * s - a);
+        double bd = fabs(e2m1_mag[best] * s - a);
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1))
+            best = c;
+    }
+    return best;
+}
+
+/* x: [rows][dim] bf16, dim % 16 == 0.  codes: [rows][dim/2] (low nibble =
+ * even channel); scales: E4M3 bytes [rows][dim/16]. */
+int orc_fp4e_pack(const uint16_t *x, int64_t rows, int32_t dim, uint8_t *codes, uint8_t *scales)
+{
+    if (dim <= 0 || dim % 16 != 0 || rows < 0)
+        return 1;
+    int64_t nblk = rows * (dim / 16);
+    for (int64_t b = 0; b < nblk; ++b) {
+        const uint16_t *xb = x + b * 16;
+        double amax = 0.0;
+        for (int i = 0; i < 16; ++i) {
+            double a = fabs(bf16_val(xb[i]));
+            if (a > amax) amax = a;
+        }
+        uint8_t sc = e4m3_block_scale(amax);
+        double s = orc_e4m3_value(sc);
+        scales[b] = sc;
+        uint8_t *cb = codes + b * 8;
+        memset(cb, 0, 8);
+        for (int i = 0; i < 16; ++i) {
+            double v = bf16_val(xb[i]);
+            int mag = s > 0.0 ? e2m1_nearest_scaled(fabs(v), s) : 0;
+            int code = (signbit(v) ? 8 : 0) | mag;
+            cb[i / 2] |= (uint8_t)(code << (4 * (i & 1)));
+        }
+    }
+    return 0;
+}
+
+static double fp4e_value(uint8_t code, uint8_t scale)
+{
+    double m = e2m1_mag[code & 7] * orc_e4m3_value(scale);
+    return (code & 8) ? -m : m;
+}
+
+int orc_fp4e_unpack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int32_t dim, double *out)
+{
+    if (dim <= 0 || dim % 16 != 0 || rows < 0)
+        return 1;
+    int64_t n = rows * dim;
+    for (int64_t i = 0; i < n; ++i) {
+        uint8_t byte = codes[i / 2];
+        uint8_t code = (i & 1) ? (byte >> 4) : (byte & 15);
+        out[i] = fp4e_value(code, scales[i / 16]);
+    }
+    return 0;
+}
+
 /* ---------------------------------------------------------------- scores */
 
 /* s[j] = fl32(sum_d q[d] * k[j][d]) for j < n  [CED, Fig. 4: indexer Q from
@@ -240,11 +340,11 @@ void orc_attention(const uint16_t *q, const double *K, const double *V, int64_t 
 /* ------------------------------------------------------- one query, layer */
 
 typedef struct {
-    int32_t fp4;             /* 1: FP4 codes + scales, 0: bf16 rows */
+    int32_t fp4;             /* 0: bf16 rows; 1: FP4 + E8M0 per 32; 2: FP4 + E4M3 per 16 */
     int64_t t_cap;           /* rows per sequence */
     const uint16_t *kv;      /* bf16 [n_seq][t_cap][256]: K | V */
     const uint8_t *codes;    /* FP4 [n_seq][t_cap][128] */
-    const uint8_t *scales;   /* E8M0 [n_seq][t_cap][8] */
+    const uint8_t *scales;   /* E8M0 [n_seq][t_cap][8], or E4M3 [n_seq][t_cap][16] */
     const uint16_t *k_idx;   /* bf16 [n_seq][t_cap][64] */
 } orc_cache;
 
@@ -252,7 +352,12 @@ typedef struct {
 static void cache_row(const orc_cache *c, int32_t seq, int64_t j, double *K, double *V)
 {
     int64_t r = (int64_t)seq * c->t_cap + j;
-    if (c->fp4) {
+    if (c->fp4 == 2) {
+        double row[ORC_ROW];
+        orc_fp4e_unpack(c->codes + r * (ORC_ROW / 2), c->scales + r * (ORC_ROW / 16), 1, ORC_ROW, row);
+        memcpy(K, row, sizeof(double) * ORC_D);
+        memcpy(V, row + ORC_D, sizeof(double) * ORC_D);
+    } else if (c->fp4) {
         double row[ORC_ROW];
         orc_fp4_unpack(c->codes + r * (ORC_ROW / 2), c->scales + r * (ORC_ROW / 32), 1, ORC_ROW, row);
         memcpy(K, row, sizeof(double) * ORC_D);
