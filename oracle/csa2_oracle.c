@@ -156,10 +156,15 @@ double orc_e4m3_value(uint8_t b)
 }
 
 /* Scale code of a block: scan the non-negative finite codes 0x00..0x7E and
- * keep the one with the least |6 v - amax| (exact in double: v has 4
- * significant bits, amax 8), ties to the even code. */
+ * keep the one with the least |6 v - amax|, ties to the even code.  Above
+ * 6 * 448 the nearest finite value is 448 itself (taken directly: there the
+ * double differences would absorb amax's size and compare equal).  Below it
+ * every difference that decides the choice is between numbers of similar
+ * size, so it is exact. */
 static uint8_t e4m3_block_scale(double amax)
 {
+    if (amax >= 6.0 * 448.0)
+        return 0x7E;
     int best = 0;
     double bd = fabs(amax);
     for (int c = 1; c <= 0x7E; ++c) {

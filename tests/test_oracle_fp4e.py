@@ -49,6 +49,7 @@ def test_scale_is_amax_over_6_rounded_like_torch():
     assert _scale_of_block(6.375) == 0x38
     # beyond 6 * 448 the scale saturates at 448; below 6 * 2^-10 it is 0
     assert _scale_of_block(3000.0) == 0x7E
+    assert _scale_of_block(1e30) == 0x7E and _scale_of_block(3.0e38) == 0x7E
     assert _scale_of_block(6 * 2.0 ** -11) == 0
 
 
