@@ -178,9 +178,13 @@ static uint8_t e4m3_block_scale(double amax)
 }
 
 /* E2M1 magnitude code of |x| = a under scale s > 0: the c with the least
- * |e2m1(c) s - a| (exact products), ties to the even code. */
+ * |e2m1(c) s - a| (exact products), ties to the even code.  From 6 s on the
+ * nearest is 6 s (code 7), taken directly since a saturated block's
+ * elements can dwarf the grid and absorb the differences. */
 static int e2m1_nearest_scaled(double a, double s)
 {
+    if (a >= 6.0 * s)
+        return 7;
     int best = 0;
     for (int c = 1; c < 8; ++c) {
         double d = fabs(e2m1_mag[c] * s - a);

@@ -50,6 +50,11 @@ def test_scale_is_amax_over_6_rounded_like_torch():
     # beyond 6 * 448 the scale saturates at 448; below 6 * 2^-10 it is 0
     assert _scale_of_block(3000.0) == 0x7E
     assert _scale_of_block(1e30) == 0x7E and _scale_of_block(3.0e38) == 0x7E
+    # and the elements of such a block saturate at 6 * 448
+    blk = np.zeros((1, 16), np.uint16)
+    blk[0, :3] = bf16([1e30, -5000.0, 1000.0])
+    c, sc = oracle.fp4e_pack(blk)
+    assert np.array_equal(oracle.fp4e_unpack(c, sc)[0, :3], [2688.0, -2688.0, 896.0])
     assert _scale_of_block(6 * 2.0 ** -11) == 0
 
 
