@@ -65,7 +65,7 @@ typedef enum {
 
 typedef enum { CSA2_MODE_FULL = 0, CSA2_MODE_REINDEX = 1, CSA2_MODE_REUSE = 2 } csa2_mode;
 
-typedef enum { CSA2_KV_BF16 = 0, CSA2_KV_FP4 = 1 } csa2_kv_format;
+typedef enum { CSA2_KV_BF16 = 0, CSA2_KV_FP4 = 1, CSA2_KV_FP4_E4M3 = 2 } csa2_kv_format;
 
 /* The global cache shared by all decoder layers (Fig. 3).
  *   BF16: data = uint16 [n_seq][t_cap][256]; channels 0..127 are K, 128..255 V.
@@ -74,6 +74,11 @@ typedef enum { CSA2_KV_BF16 = 0, CSA2_KV_FP4 = 1 } csa2_kv_format;
  *         scales = uint8 E8M0 [n_seq][t_cap][8]: bytes 0..3 scale the four
  *         32-channel blocks of K, bytes 4..7 those of V.
  *         This is exactly what csa2_pack_fp4 writes for rows of 256 (K | V).
+ *   FP4_E4M3: the pages' own form ("DeepSeek-V4.1 Flash ...", summary: E2M1
+ *         with an E4M3 scale per 16 channels): codes as for FP4; scales =
+ *         uint8 E4M3 [n_seq][t_cap][16]: bytes 0..7 scale the eight
+ *         16-channel blocks of K, bytes 8..15 those of V (144 B per token).
+ *         This is exactly what csa2_pack_fp4_e4m3 writes for rows of 256.
  *   k_idx = indexer keys, bf16 [n_seq][t_cap][64].
  * data, scales and k_idx must be 16-byte aligned; t_cap <= 2^24. */
 typedef struct {
@@ -121,14 +126,31 @@ csa2_status csa2_pack_fp4(const uint16_t *x, int64_t rows, int32_t dim, uint8_t 
 csa2_status csa2_unpack_fp4(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                             int32_t dim, float *out, void *stream);
 
+/* Quantise rows of bf16 to FP4 with one E4M3 scale per 16 elements (the
+ * pages' own form).  x: bf16 [rows][dim], dim % 16 == 0; codes [rows][dim/2]
+ * (low nibble = even channel); scales: E4M3 bytes [rows][dim/16].  For each
+ * block with largest magnitude a, the scale s is the E4M3 value (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits) nearest to a / 6, ties to the
+ * even code, saturating at 448 (0x7E); each element x becomes the E2M1
+ * magnitude c for which c * s is nearest to |x| (ties to the even code,
+ * beyond 6 s: 6), keeping the sign bit; when s is 0 every magnitude is 0.
+ * x 16-byte aligned, codes 8-byte aligned. */
+csa2_status csa2_pack_fp4_e4m3(const uint16_t *x, int64_t rows, int32_t dim, uint8_t *codes,
+                               uint8_t *scales, void *stream);
+
+/* Exact dequantisation of that form: out[i] = (-1)^s * e2m1(c) * e4m3(scale)
+ * as fp32.  out 16-byte aligned, codes 8-byte aligned. */
+csa2_status csa2_unpack_fp4_e4m3(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                                 int32_t dim, float *out, void *stream);
+
 /* --------------------------------------------------------------- append */
 
 /* Decode append ("CED", section "Why Prefill Recomputes a Recent Segment":
  * once a token is chosen, the global KV of its position is appended and every
  * decoder layer updates its local state).  For every sequence b with
  * 0 <= pos[b] < t_cap, row pos[b] of the global cache receives kv[b] (K | V,
- * bf16 [n_seq][256]; FP4-packed exactly as csa2_pack_fp4 does, or copied for
- * a BF16 cache) and, when kidx is not NULL, its indexer key kidx[b] (bf16
+ * bf16 [n_seq][256]; FP4-packed exactly as csa2_pack_fp4 or
+ * csa2_pack_fp4_e4m3 does for the cache's format, or copied for a BF16 cache) and, when kidx is not NULL, its indexer key kidx[b] (bf16
  * [n_seq][64]).  Then, for each of the n_local layers l, slot pos[b] %
  * local[l].cap of that layer's ring receives k_new[l][b] and v_new[l][b]
  * (bf16 [n_seq][128] each).  Sequences with pos[b] outside [0, t_cap) are

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libcsa2.so")
 
 FULL, REINDEX, REUSE = 0, 1, 2
-KV_BF16, KV_FP4 = 0, 1
+KV_BF16, KV_FP4, KV_FP4_E4M3 = 0, 1, 2
 HEADS, HEAD_DIM, INDEX_DIM = 16, 128, 64
 
 _P = ctypes.c_void_p
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_device_check.restype = ctypes.c_int
         L.csa2_pack_fp4.argtypes = [_P, _i64, _i32, _P, _P, _P]
         L.csa2_unpack_fp4.argtypes = [_P, _P, _i64, _i32, _P, _P]
+        L.csa2_pack_fp4_e4m3.argtypes = [_P, _i64, _i32, _P, _P, _P]
+        L.csa2_unpack_fp4_e4m3.argtypes = [_P, _P, _i64, _i32, _P, _P]
         L.csa2_append.argtypes = [ctypes.POINTER(csa2_cache), _P, _P, _P, _i32,
                                   ctypes.POINTER(csa2_local), ctypes.POINTER(_P),
                                   ctypes.POINTER(_P), _P]
@@ -97,7 +99,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_stack_plan_destroy.argtypes = [_P]
         L.csa2_replay_workspace.argtypes = [ctypes.POINTER(csa2_replay_desc), ctypes.POINTER(_sz)]
         L.csa2_replay_run.argtypes = [ctypes.POINTER(csa2_replay_desc), _P, _sz, _P]
-        for f in ("csa2_pack_fp4", "csa2_unpack_fp4", "csa2_append", "csa2_index_score", "csa2_prefill_score",
+        for f in ("csa2_pack_fp4", "csa2_unpack_fp4", "csa2_pack_fp4_e4m3", "csa2_unpack_fp4_e4m3",
+                  "csa2_append", "csa2_index_score", "csa2_prefill_score",
                   "csa2_prefill_topk", "csa2_prefill_topk_workspace", "csa2_topk",
                   "csa2_topk_workspace", "csa2_expand_blocks", "csa2_sparse_attn",
                   "csa2_sparse_attn_workspace", "csa2_stack_workspace", "csa2_stack_run",
@@ -152,7 +155,9 @@ class Cache:
 
     BF16: ``data`` bf16 [n_seq][t_cap][256] (K | V).  FP4: ``data`` uint8 codes
     [n_seq][t_cap][128] and ``scales`` uint8 [n_seq][t_cap][8] as written by
-    :func:`pack_fp4` on rows of 256.  ``k_idx`` bf16 [n_seq][t_cap][64].
+    :func:`pack_fp4` on rows of 256 (one E8M0 scale per 32), or
+    [n_seq][t_cap][16] as written by :func:`pack_fp4_e4m3` (one E4M3 scale per
+    16).  ``k_idx`` bf16 [n_seq][t_cap][64].
     """
 
     def __init__(self, data: torch.Tensor, k_idx: torch.Tensor,
@@ -160,13 +165,17 @@ class Cache:
         self.fp4 = scales is not None
         self.data, self.scales, self.k_idx = data, scales, _bits16(k_idx)
         self.n_seq, self.t_cap = int(k_idx.shape[0]), int(k_idx.shape[1])
+        fmt = KV_BF16
         if self.fp4:
             assert data.dtype == torch.uint8 and tuple(data.shape) == (self.n_seq, self.t_cap, 128)
-            assert scales.dtype == torch.uint8 and tuple(scales.shape) == (self.n_seq, self.t_cap, 8)
+            assert scales.dtype == torch.uint8 and scales.dim() == 3
+            assert tuple(scales.shape[:2]) == (self.n_seq, self.t_cap) and scales.shape[2] in (8, 16)
+            fmt = KV_FP4 if scales.shape[2] == 8 else KV_FP4_E4M3
         else:
             _bits16(data)
             assert tuple(data.shape) == (self.n_seq, self.t_cap, 256)
-        self.c = csa2_cache(KV_FP4 if self.fp4 else KV_BF16, self.n_seq, self.t_cap,
+        self.format = fmt
+        self.c = csa2_cache(fmt, self.n_seq, self.t_cap,
                             _ptr(data), _ptr(scales) if self.fp4 else None, _ptr(self.k_idx))
 
 
@@ -189,6 +198,27 @@ def pack_fp4(x: torch.Tensor):
     _check("csa2_pack_fp4", lib().csa2_pack_fp4(_ptr(x), rows, dim, _ptr(codes), _ptr(scales),
                                                 _stream()))
     return codes, scales
+
+
+def pack_fp4_e4m3(x: torch.Tensor):
+    """bf16 [..., dim] -> (codes uint8 [..., dim/2], E4M3 scales uint8 [..., dim/16])."""
+    x = _bits16(x)
+    dim = int(x.shape[-1])
+    rows = x.numel() // dim if dim else 0
+    codes = torch.empty(tuple(x.shape[:-1]) + (dim // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(tuple(x.shape[:-1]) + (dim // 16,), dtype=torch.uint8, device=x.device)
+    _check("csa2_pack_fp4_e4m3", lib().csa2_pack_fp4_e4m3(_ptr(x), rows, dim, _ptr(codes),
+                                                          _ptr(scales), _stream()))
+    return codes, scales
+
+
+def unpack_fp4_e4m3(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    dim = int(codes.shape[-1]) * 2
+    rows = codes.numel() // (dim // 2) if dim else 0
+    out = torch.empty(tuple(codes.shape[:-1]) + (dim,), dtype=torch.float32, device=codes.device)
+    _check("csa2_unpack_fp4_e4m3", lib().csa2_unpack_fp4_e4m3(_ptr(codes), _ptr(scales), rows, dim,
+                                                              _ptr(out), _stream()))
+    return out
 
 
 def unpack_fp4(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:

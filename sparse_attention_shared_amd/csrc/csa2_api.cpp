@@ -55,15 +55,16 @@ csa2_status from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR
 
 csa2_status check_cache(const csa2_cache* c, bool need_kv, bool need_idx, CacheView* v) {
     if (!c) return CSA2_ERR_INVALID_ARG;
-    if (c->format != CSA2_KV_BF16 && c->format != CSA2_KV_FP4) return CSA2_ERR_INVALID_ARG;
+    if (c->format != CSA2_KV_BF16 && c->format != CSA2_KV_FP4 && c->format != CSA2_KV_FP4_E4M3)
+        return CSA2_ERR_INVALID_ARG;
     if (c->n_seq <= 0 || c->t_cap <= 0 || c->t_cap > ((int64_t)1 << 24)) return CSA2_ERR_SHAPE;
     if (need_kv) {
         if (!c->data || !aligned16(c->data)) return CSA2_ERR_INVALID_ARG;
-        if (c->format == CSA2_KV_FP4 && (!c->scales || !aligned16(c->scales)))
+        if (c->format != CSA2_KV_BF16 && (!c->scales || !aligned16(c->scales)))
             return CSA2_ERR_INVALID_ARG;
     }
     if (need_idx && (!c->k_idx || !aligned16(c->k_idx))) return CSA2_ERR_INVALID_ARG;
-    v->fp4 = c->format == CSA2_KV_FP4;
+    v->fp4 = c->format == CSA2_KV_FP4 ? 1 : c->format == CSA2_KV_FP4_E4M3 ? 2 : 0;
     v->n_seq = c->n_seq;
     v->t_cap = c->t_cap;
     v->data = c->data;
@@ -224,6 +225,26 @@ csa2_status csa2_pack_fp4(const uint16_t* x, int64_t rows, int32_t dim, uint8_t*
         return CSA2_ERR_INVALID_ARG;
     if (csa2_status st = device_ok()) return st;
     return from_hip(launch_pack_fp4(x, rows * (dim / 32), codes, scales, (hipStream_t)stream));
+}
+
+csa2_status csa2_pack_fp4_e4m3(const uint16_t* x, int64_t rows, int32_t dim, uint8_t* codes,
+                               uint8_t* scales, void* stream) {
+    if (rows < 0 || dim <= 0 || dim % 16) return CSA2_ERR_SHAPE;
+    if (rows > 0 && (!x || !codes || !scales || !aligned16(x) ||
+                     (reinterpret_cast<uintptr_t>(codes) & 7u) != 0))
+        return CSA2_ERR_INVALID_ARG;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_pack_fp4e(x, rows * (dim / 16), codes, scales, (hipStream_t)stream));
+}
+
+csa2_status csa2_unpack_fp4_e4m3(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                 int32_t dim, float* out, void* stream) {
+    if (rows < 0 || dim <= 0 || dim % 16) return CSA2_ERR_SHAPE;
+    if (rows > 0 && (!codes || !scales || !out || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0 ||
+                     !aligned16(out)))
+        return CSA2_ERR_INVALID_ARG;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_unpack_fp4e(codes, scales, rows * (dim / 16), out, (hipStream_t)stream));
 }
 
 csa2_status csa2_unpack_fp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t dim,

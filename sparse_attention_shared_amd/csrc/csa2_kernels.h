@@ -10,11 +10,11 @@
 namespace csa2 {
 
 struct CacheView {
-    int32_t fp4;            // 1: FP4 codes + scales, 0: bf16 rows
+    int32_t fp4;            // 0: bf16 rows; 1: FP4 + E8M0 per 32; 2: FP4 + E4M3 per 16
     int32_t n_seq;
     int64_t t_cap;
     const void* data;       // bf16 [n_seq][t_cap][256] or codes [n_seq][t_cap][128]
-    const uint8_t* scales;  // [n_seq][t_cap][8]
+    const uint8_t* scales;  // [n_seq][t_cap][8] (E8M0) or [n_seq][t_cap][16] (E4M3)
     const uint16_t* k_idx;  // [n_seq][t_cap][64]
 };
 
@@ -28,6 +28,11 @@ hipError_t launch_pack_fp4(const uint16_t* x, int64_t nblk, uint8_t* codes, uint
                            hipStream_t s);
 hipError_t launch_unpack_fp4(const uint8_t* codes, const uint8_t* scales, int64_t nblk, float* out,
                              hipStream_t s);
+// FP4 with one E4M3 scale per 16 elements: nblk blocks of 16.
+hipError_t launch_pack_fp4e(const uint16_t* x, int64_t nblk, uint8_t* codes, uint8_t* scales,
+                            hipStream_t s);
+hipError_t launch_unpack_fp4e(const uint8_t* codes, const uint8_t* scales, int64_t nblk, float* out,
+                              hipStream_t s);
 
 // Dense indexer scores: scores[i][b], b < ceil(t_cap / block), block in {1, 64}.
 // Decode append: the new position's global row (FP4-packed or copied),
@@ -45,7 +50,7 @@ struct AppendArgs {
     int32_t seq;         // -1: row b belongs to sequence b; else every row to `seq`
     int32_t* q_seq_out;  // null, or [n rows]: receives each row's sequence
     int64_t t_cap;
-    int32_t fp4;
+    int32_t fp4;           // the cache's format code (CacheView::fp4)
     const uint16_t* kv;    // bf16 [n rows][256] or null
     const uint16_t* kidx;  // bf16 [n rows][64] or null
     uint8_t* codes;        // FP4 cache

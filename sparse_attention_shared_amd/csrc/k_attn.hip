@@ -51,6 +51,62 @@ __device__ __forceinline__ float e8m0_value(uint32_t byte) {
     return __uint_as_float(byte ? (byte << 23) : 0x00400000u);
 }
 
+// A decode scale split for the hardware conversion, which applies only the
+// power-of-two part of its fp32 scale (it is built for E8M0 blocks): codes
+// are converted with p2 and the rest of the scale, mult, is applied after.
+struct DqScale {
+    float p2, mult;
+};
+
+// An E4M3 byte (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+// exponent field 0: m/8 * 2^-6) as p2 * mult: 2^(e-7) * (1 + m/8), or
+// 2^-9 * m for the subnormals.  Scales are never negative or NaN (the packer
+// writes 0x00..0x7E).
+__device__ __forceinline__ DqScale e4m3_split(uint32_t byte) {
+    const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
+    DqScale d;
+    d.p2 = __uint_as_float(e ? (e + 120u) << 23 : (118u << 23));  // 2^(e-7), or 2^-9
+    d.mult = e ? 1.f + 0.125f * (float)m : (float)m;
+    return d;
+}
+
+// An E4M3 byte as fp32 (exact).
+__device__ __forceinline__ float e4m3_value(uint32_t byte) {
+    const DqScale d = e4m3_split(byte);
+    return d.p2 * d.mult;
+}
+
+// Scale formats of an FP4 cache (template parameter SF): 0 = one E8M0 byte
+// per 32 channels (8 bytes a row), 1 = one E4M3 byte per 16 channels (16
+// bytes a row).  Lane group g decodes dims 32 g .. + 32 of K and of V, i.e.
+// one E8M0 block or two E4M3 blocks; row_scales gives the lane's scale bits
+// (one byte, or two bytes: dims 32 g .. + 16 in the low one) and dw_scale the
+// multiplier of code dword kb (dims 32 g + 8 kb .. + 8).
+template <int SF>
+__device__ __forceinline__ constexpr int row_scale_bytes() { return SF ? 16 : 8; }
+
+template <int SF>
+__device__ __forceinline__ constexpr uint32_t unit_scale_bits() { return SF ? 0x3838u : 127u; }
+
+template <int SF>
+__device__ __forceinline__ void row_scales(const uint8_t* sp, int g, uint32_t& sk, uint32_t& sv) {
+    if (SF == 0) {
+        const uint2 sc = *reinterpret_cast<const uint2*>(sp);
+        sk = (sc.x >> (8 * g)) & 0xFFu;
+        sv = (sc.y >> (8 * g)) & 0xFFu;
+    } else {
+        const uint4 sc = *reinterpret_cast<const uint4*>(sp);
+        sk = ((g < 2 ? sc.x : sc.y) >> (16 * (g & 1))) & 0xFFFFu;
+        sv = ((g < 2 ? sc.z : sc.w) >> (16 * (g & 1))) & 0xFFFFu;
+    }
+}
+
+template <int SF>
+__device__ __forceinline__ DqScale dw_scale(uint32_t bits, int kb) {
+    if (SF == 0) return DqScale{e8m0_value(bits), 1.f};
+    return e4m3_split(kb < 2 ? (bits & 0xFFu) : (bits >> 8));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)f_to_bf16(a) | ((uint32_t)f_to_bf16(b) << 16);
 }
@@ -79,16 +135,23 @@ __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t w, float sc, int sel) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// 32 FP4 codes (16 bytes) of one scale block -> 16 dwords of bf16 pairs.
-__device__ __forceinline__ void dq_block(uint4 c, float sc, uint32_t (&o)[16]) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        o[4 * i + 0] = cvt_fp4x2(w[i], sc, 0);
-        o[4 * i + 1] = cvt_fp4x2(w[i], sc, 1);
-        o[4 * i + 2] = cvt_fp4x2(w[i], sc, 2);
-        o[4 * i + 3] = cvt_fp4x2(w[i], sc, 3);
+// Codes sel (byte) of w times a split scale -> a bf16 pair.  E8M0 (SF 0):
+// the conversion alone.  E4M3 (SF 1): converted to fp32 with p2, times mult
+// (exact: an E2M1 value times an E4M3 scale has at most 6 significant
+// bits), and the high halves kept (exact values need no rounding).
+template <int SF>
+__device__ __forceinline__ uint32_t dq_pair(uint32_t w, DqScale d, int sel) {
+    if (SF == 0) return cvt_fp4x2(w, d.p2, sel);
+    typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+    f32x2_t r;
+    switch (sel) {
+        case 0: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, d.p2, 0); break;
+        case 1: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, d.p2, 1); break;
+        case 2: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, d.p2, 2); break;
+        default: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, d.p2, 3); break;
     }
+    return __builtin_amdgcn_perm(__float_as_uint(r.y * d.mult), __float_as_uint(r.x * d.mult),
+                                 0x07060302u);
 }
 
 struct RowRaw {  // the FP4 data one lane loads for one entry
@@ -110,6 +173,7 @@ struct AttnLds {
 // loads entries 2 n16 and 2 n16 + 1 of the wave's block (MFMA tiles 0 and 1),
 // lane group g dims 32 g .. + 32 of K and of V.  After the second barrier
 // wave w < 8 forms dims 16 w .. + 16 of O for the whole chunk.
+template <int SF>
 __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint16_t* __restrict__ q,
                                                          const int32_t* __restrict__ q_pos,
                                                          const int32_t* __restrict__ q_seq,
@@ -176,14 +240,12 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     uint32_t rsk[2], rsv[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        rsk[u] = rsv[u] = 127u;
+        rsk[u] = rsv[u] = unit_scale_bits<SF>();
         if (kind[u] == 1) {
             const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row[u] * kRowCodes;
             rk[u][0] = *reinterpret_cast<const uint4*>(cr + 16 * g);
             rv[u][0] = *reinterpret_cast<const uint4*>(cr + 64 + 16 * g);
-            const uint2 sc = *reinterpret_cast<const uint2*>(c.scales + row[u] * kRowScales);
-            rsk[u] = (sc.x >> (8 * g)) & 0xFFu;
-            rsv[u] = (sc.y >> (8 * g)) & 0xFFu;
+            row_scales<SF>(c.scales + row[u] * row_scale_bytes<SF>(), g, rsk[u], rsv[u]);
         } else if (kind[u] >= 2) {
             const uint16_t* kr = kind[u] == 2 ? static_cast<const uint16_t*>(c.data) + row[u] * kRowBf16
                                               : loc.k + row[u] * kHeadDim;
@@ -206,17 +268,17 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         if (kind[u] == 1) {
-            const float sk = e8m0_value(rsk[u]), sv = e8m0_value(rsv[u]);
             const uint32_t wk[4] = {rk[u][0].x, rk[u][0].y, rk[u][0].z, rk[u][0].w};
             const uint32_t wv[4] = {rv[u][0].x, rv[u][0].y, rv[u][0].z, rv[u][0].w};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                kf[u][kb] = as_bf16x8(cvt_fp4x2(wk[kb], sk, 0), cvt_fp4x2(wk[kb], sk, 1),
-                                      cvt_fp4x2(wk[kb], sk, 2), cvt_fp4x2(wk[kb], sk, 3));
-                vd[u][4 * kb + 0] = cvt_fp4x2(wv[kb], sv, 0);
-                vd[u][4 * kb + 1] = cvt_fp4x2(wv[kb], sv, 1);
-                vd[u][4 * kb + 2] = cvt_fp4x2(wv[kb], sv, 2);
-                vd[u][4 * kb + 3] = cvt_fp4x2(wv[kb], sv, 3);
+                const DqScale sk = dw_scale<SF>(rsk[u], kb), sv = dw_scale<SF>(rsv[u], kb);
+                kf[u][kb] = as_bf16x8(dq_pair<SF>(wk[kb], sk, 0), dq_pair<SF>(wk[kb], sk, 1),
+                                      dq_pair<SF>(wk[kb], sk, 2), dq_pair<SF>(wk[kb], sk, 3));
+                vd[u][4 * kb + 0] = dq_pair<SF>(wv[kb], sv, 0);
+                vd[u][4 * kb + 1] = dq_pair<SF>(wv[kb], sv, 1);
+                vd[u][4 * kb + 2] = dq_pair<SF>(wv[kb], sv, 2);
+                vd[u][4 * kb + 3] = dq_pair<SF>(wv[kb], sv, 3);
             }
         } else {
 #pragma unroll
@@ -427,6 +489,7 @@ struct LoopLds {
 };
 
 // grid nq, kLW * 64 threads.
+template <int SF>
 __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint16_t* __restrict__ q,
                                                         const int32_t* __restrict__ q_pos,
                                                         const int32_t* __restrict__ q_seq,
@@ -485,9 +548,7 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
         const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row * kRowCodes;
         r.k = *reinterpret_cast<const uint4*>(cr + 16 * g);
         r.v = *reinterpret_cast<const uint4*>(cr + 64 + 16 * g);
-        const uint2 sc = *reinterpret_cast<const uint2*>(c.scales + row * kRowScales);
-        r.sk = (sc.x >> (8 * g)) & 0xFFu;
-        r.sv = (sc.y >> (8 * g)) & 0xFFu;
+        row_scales<SF>(c.scales + row * row_scale_bytes<SF>(), g, r.sk, r.sv);
     };
 
     float m_run = NEG, l_part = 0.f;
@@ -567,7 +628,8 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
     // codes, so its V is zero.
     const int n_fast = (c.fp4 && t >= 0) ? k / 32 : 0;
     const uint8_t* codes = static_cast<const uint8_t*>(c.data) + (int64_t)max(seq, 0) * c.t_cap * kRowCodes;
-    const uint8_t* scl = c.scales ? c.scales + (int64_t)max(seq, 0) * c.t_cap * kRowScales : nullptr;
+    const uint8_t* scl =
+        c.scales ? c.scales + (int64_t)max(seq, 0) * c.t_cap * row_scale_bytes<SF>() : nullptr;
     // An empty slot reads row 0 (no branch around the loads) with scale 1:
     // its codes are finite and its p is 0, so it adds nothing.
     const int32_t t32 = (int32_t)t;  // positions fit 32 bits (t_cap <= 2^31)
@@ -576,9 +638,10 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
         const int64_t jj = ok ? j : 0;
         r.k = *reinterpret_cast<const uint4*>(codes + jj * kRowCodes + 16 * g);
         r.v = *reinterpret_cast<const uint4*>(codes + jj * kRowCodes + 64 + 16 * g);
-        const uint2 sc = *reinterpret_cast<const uint2*>(scl + jj * kRowScales);
-        r.sk = ok ? (sc.x >> (8 * g)) & 0xFFu : 127u;
-        r.sv = ok ? (sc.y >> (8 * g)) & 0xFFu : 127u;
+        uint32_t sk, sv;
+        row_scales<SF>(scl + jj * row_scale_bytes<SF>(), g, sk, sv);
+        r.sk = ok ? sk : unit_scale_bits<SF>();
+        r.sv = ok ? sv : unit_scale_bits<SF>();
     };
     {
         RowRaw raw[2];
@@ -601,20 +664,21 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
             bf16x8_t kf[2][4];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const float sc = e8m0_value(raw[u].sk);
                 const uint32_t w[4] = {raw[u].k.x, raw[u].k.y, raw[u].k.z, raw[u].k.w};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-                    kf[u][kb] = as_bf16x8(cvt_fp4x2(w[kb], sc, 0), cvt_fp4x2(w[kb], sc, 1),
-                                          cvt_fp4x2(w[kb], sc, 2), cvt_fp4x2(w[kb], sc, 3));
+                for (int kb = 0; kb < 4; ++kb) {
+                    const DqScale sc = dw_scale<SF>(raw[u].sk, kb);
+                    kf[u][kb] = as_bf16x8(dq_pair<SF>(w[kb], sc, 0), dq_pair<SF>(w[kb], sc, 1),
+                                          dq_pair<SF>(w[kb], sc, 2), dq_pair<SF>(w[kb], sc, 3));
+                }
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {  // V rows of slots 2 n16 + u, dims 32 g .. + 32
-                const float sv = e8m0_value(raw[u].sv);
                 const uint32_t wv[4] = {raw[u].v.x, raw[u].v.y, raw[u].v.z, raw[u].v.w};
                 uint32_t d[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) d[i] = cvt_fp4x2(wv[i >> 2], sv, i & 3);
+                for (int i = 0; i < 16; ++i)
+                    d[i] = dq_pair<SF>(wv[i >> 2], dw_scale<SF>(raw[u].sv, i >> 2), i & 3);
                 vr_store_row(vr, 2 * n16 + u, g, d);
             }
             const int next = tile + kLW;
@@ -651,12 +715,13 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
             if (kind[u] == 1) {
                 RowRaw r;
                 load_fp4(row[u], r);
-                const float sc = e8m0_value(r.sk);
                 const uint32_t w[4] = {r.k.x, r.k.y, r.k.z, r.k.w};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-                    kf[u][kb] = as_bf16x8(cvt_fp4x2(w[kb], sc, 0), cvt_fp4x2(w[kb], sc, 1),
-                                          cvt_fp4x2(w[kb], sc, 2), cvt_fp4x2(w[kb], sc, 3));
+                for (int kb = 0; kb < 4; ++kb) {
+                    const DqScale sc = dw_scale<SF>(r.sk, kb);
+                    kf[u][kb] = as_bf16x8(dq_pair<SF>(w[kb], sc, 0), dq_pair<SF>(w[kb], sc, 1),
+                                          dq_pair<SF>(w[kb], sc, 2), dq_pair<SF>(w[kb], sc, 3));
+                }
             } else if (kind[u] >= 2) {
                 const uint16_t* kr = kind[u] == 2 ? static_cast<const uint16_t*>(c.data) + row[u] * kRowBf16
                                                   : loc.k + row[u] * kHeadDim;
@@ -680,11 +745,14 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                 if (kind[u] == 1) {
                     const uint8_t* cr = static_cast<const uint8_t*>(c.data) + row[u] * kRowCodes;
                     const uint32_t w = *reinterpret_cast<const uint32_t*>(cr + 64 + 16 * g + 4 * i4);
-                    const float sc = e8m0_value(c.scales[row[u] * kRowScales + 4 + g]);
-                    vv[u][0] = cvt_fp4x2(w, sc, 0);
-                    vv[u][1] = cvt_fp4x2(w, sc, 1);
-                    vv[u][2] = cvt_fp4x2(w, sc, 2);
-                    vv[u][3] = cvt_fp4x2(w, sc, 3);
+                    // V scale of dims 32 g + 8 i4 .. + 8
+                    const DqScale sc =
+                        SF ? e4m3_split(c.scales[row[u] * 16 + 8 + 2 * g + (i4 >> 1)])
+                           : DqScale{e8m0_value(c.scales[row[u] * kRowScales + 4 + g]), 1.f};
+                    vv[u][0] = dq_pair<SF>(w, sc, 0);
+                    vv[u][1] = dq_pair<SF>(w, sc, 1);
+                    vv[u][2] = dq_pair<SF>(w, sc, 2);
+                    vv[u][3] = dq_pair<SF>(w, sc, 3);
                 } else if (kind[u] >= 2) {
                     const uint16_t* vr = kind[u] == 2
                                              ? static_cast<const uint16_t*>(c.data) + row[u] * kRowBf16 + kHeadDim
@@ -757,8 +825,12 @@ hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32
                               hipStream_t s) {
     if (nq == 0) return hipSuccess;
     if (nq >= kManyQueries) {  // enough queries to fill the GPU one workgroup each
-        hipLaunchKernelGGL(k_attn_loop, dim3((uint32_t)nq), dim3(kLW * 64), 0, s, c, q, q_pos, q_seq,
-                           sel, k, loc, sm_scale, out);
+        if (c.fp4 == 2)
+            hipLaunchKernelGGL(k_attn_loop<1>, dim3((uint32_t)nq), dim3(kLW * 64), 0, s, c, q, q_pos,
+                               q_seq, sel, k, loc, sm_scale, out);
+        else
+            hipLaunchKernelGGL(k_attn_loop<0>, dim3((uint32_t)nq), dim3(kLW * 64), 0, s, c, q, q_pos,
+                               q_seq, sel, k, loc, sm_scale, out);
         return hipGetLastError();
     }
     int32_t nc = attn_chunks(k, loc.window);
@@ -766,8 +838,12 @@ hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32
     float* ws_o = static_cast<float*>(ws);
     float* ws_ml = nc > 1 ? ws_o + (size_t)nq * nc * kHeads * kHeadDim : nullptr;
     uint32_t* ctr = nc > 1 ? reinterpret_cast<uint32_t*>(ws_ml + (size_t)nq * nc * kHeads * 2) : nullptr;
-    hipLaunchKernelGGL(k_attn_chunk, dim3((uint32_t)nc, (uint32_t)nq), dim3(kThreads), 0, s, c, q,
-                       q_pos, q_seq, sel, k, loc, sm_scale, nc, ws_o, ws_ml, ctr, out);
+    if (c.fp4 == 2)
+        hipLaunchKernelGGL(k_attn_chunk<1>, dim3((uint32_t)nc, (uint32_t)nq), dim3(kThreads), 0, s, c,
+                           q, q_pos, q_seq, sel, k, loc, sm_scale, nc, ws_o, ws_ml, ctr, out);
+    else
+        hipLaunchKernelGGL(k_attn_chunk<0>, dim3((uint32_t)nc, (uint32_t)nq), dim3(kThreads), 0, s, c,
+                           q, q_pos, q_seq, sel, k, loc, sm_scale, nc, ws_o, ws_ml, ctr, out);
     return hipGetLastError();
 }
 

@@ -95,6 +95,105 @@ __global__ __launch_bounds__(256) void k_pack_fp4(const uint16_t* __restrict__ x
     scales[b] = sc;
 }
 
+// ---- FP4 with one E4M3 scale per 16 channels (the pages' own cache form,
+// "DeepSeek-V4.1 Flash Pushes KV Cache Compression for Agent Workloads").
+// Scale: the E4M3 value (1 sign, 4 exponent bits with bias 7, 3 mantissa
+// bits) nearest to amax / 6, ties to the even code, saturating at 448.
+// amax / 6 is formed as a correctly rounded fp32 quotient: an exact tie of
+// the E4M3 rounding needs amax = 6 h with h of 5 significant bits, and then
+// the quotient is exact; otherwise amax / 6 lies at least 2^-11 (relative)
+// from every E4M3 rounding boundary, far beyond fp32's rounding, so rounding
+// the quotient decides as rounding the exact value would.
+__device__ __forceinline__ uint32_t e4m3_code_of(float x) {  // x >= 0, finite
+    const uint32_t b = __float_as_uint(x);
+    if (x < 0.015625f) {  // below 2^-6: multiples of 2^-9, round to nearest even
+        const float m = __builtin_rintf(x * 512.0f);  // exact scaling
+        return (uint32_t)m;                           // 8 gives 0x08 = 2^-6
+    }
+    // keep 3 mantissa bits, round to nearest even, rebias 127 -> 7
+    const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+    const uint32_t code = (r >> 20) - (120u << 3);
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+    const uint32_t e = (code >> 3) & 15u, m = code & 7u;
+    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+
+// Scale code of a 16-element block from the bf16 magnitude bits of its amax.
+__device__ __forceinline__ uint32_t e4m3_block_scale(uint32_t amax_bits) {
+    const float a = __uint_as_float(amax_bits << 16);
+    return e4m3_code_of(__fdiv_rn(a, 6.0f));
+}
+
+// E2M1 magnitude code of bf16 magnitude bits `a` under scale s: the nearest
+// grid value c * s, ties to the even code.  The decision points are 0.25,
+// 0.75, 1.25, 1.75, 2.5, 3.5 and 5 times s; each product has at most 7
+// significant bits, so the fp32 comparisons are exact.  s = 0 gives 0.
+__device__ __forceinline__ uint32_t e2m1_code_scaled(uint32_t a, float s) {
+    if (s == 0.f) return 0u;
+    const float y = __uint_as_float(a << 16);
+    return (uint32_t)(y > 0.25f * s) + (uint32_t)(y >= 0.75f * s) + (uint32_t)(y > 1.25f * s) +
+           (uint32_t)(y >= 1.75f * s) + (uint32_t)(y > 2.5f * s) + (uint32_t)(y >= 3.5f * s) +
+           (uint32_t)(y > 5.f * s);
+}
+
+// One thread per 16-element block: 32 B of bf16 in, 8 B of codes + 1 scale out.
+__global__ __launch_bounds__(256) void k_pack_fp4e(const uint16_t* __restrict__ x, int64_t nblk,
+                                                   uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblk) return;
+    const uint4* src = reinterpret_cast<const uint4*>(x + b * 16);
+    const uint4 v0 = src[0], v1 = src[1];
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        amax = max(amax, w[i] & 0x7FFFu);
+        amax = max(amax, (w[i] >> 16) & 0x7FFFu);
+    }
+    const uint32_t sc = e4m3_block_scale(amax);
+    const float s = e4m3_to_f32(sc);
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
+        const uint32_t c0 = e2m1_code_scaled(lo & 0x7FFFu, s) | ((lo >> 15) << 3);
+        const uint32_t c1 = e2m1_code_scaled(hi & 0x7FFFu, s) | ((hi >> 15) << 3);
+        out[i >> 2] |= (c0 | (c1 << 4)) << (8 * (i & 3));
+    }
+    reinterpret_cast<uint2*>(codes)[b] = make_uint2(out[0], out[1]);
+    scales[b] = (uint8_t)sc;
+}
+
+// Exact: an E2M1 value (2 significant bits) times an E4M3 scale (4) is an
+// fp32 product without rounding.
+__global__ __launch_bounds__(256) void k_unpack_fp4e(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales,
+                                                     int64_t nblk, float* __restrict__ out) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblk) return;
+    const uint2 c = reinterpret_cast<const uint2*>(codes)[b];
+    const float s = e4m3_to_f32(scales[b]);
+    const uint32_t w[2] = {c.x, c.y};
+    const float mag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+    float4* dst = reinterpret_cast<float4*>(out) + b * 4;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t q = (w[i] >> (4 * j)) & 15u;
+            const float m = mag[q & 7u] * s;
+            v[j] = (q & 8u) ? -m : m;
+        }
+        dst[2 * i] = make_float4(v[0], v[1], v[2], v[3]);
+        dst[2 * i + 1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
 // ---- decode append ("CED", section "Why Prefill Recomputes a Recent
 // Segment": after a token is chosen, every layer updates its local state and
 // the global KV of the new position is appended); also the ring rows of a
@@ -141,17 +240,28 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
             return;
         }
         const uint32_t mag = x & 0x7FFFu;
-        uint32_t amax = mag;
+        uint32_t code;
+        if (a.fp4 == 2) {  // E4M3 per 16: 16-lane blocks
+            uint32_t amax = mag;
 #pragma unroll
-        for (int m = 1; m < 32; m <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, m, 32));
-        int E = -127;
-        if (amax) E = min(max(floor_log2_bf16(amax) - 2, -127), 127);
-        // channel 8m + c of the block sits in nibble c of code word m
-        uint32_t word = (e2m1_mag_code(mag, E) | ((x >> 15) << 3)) << (4 * (tid & 7));
+            for (int m = 1; m < 16; m <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, m, 16));
+            const uint32_t sc = e4m3_block_scale(amax);
+            code = e2m1_code_scaled(mag, e4m3_to_f32(sc));
+            if ((tid & 15) == 0) a.scales[row * 16 + (tid >> 4)] = (uint8_t)sc;
+        } else {  // E8M0 per 32
+            uint32_t amax = mag;
+#pragma unroll
+            for (int m = 1; m < 32; m <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, m, 32));
+            int E = -127;
+            if (amax) E = min(max(floor_log2_bf16(amax) - 2, -127), 127);
+            code = e2m1_mag_code(mag, E);
+            if ((tid & 31) == 0) a.scales[row * 8 + (tid >> 5)] = (uint8_t)(E + 127);
+        }
+        // channel 8m + c of the row sits in nibble c of code word m
+        uint32_t word = (code | ((x >> 15) << 3)) << (4 * (tid & 7));
 #pragma unroll
         for (int m = 1; m < 8; m <<= 1) word |= (uint32_t)__shfl_xor((int)word, m, 32);
         if ((tid & 7) == 0) reinterpret_cast<uint32_t*>(a.codes + row * 128)[tid >> 3] = word;
-        if ((tid & 31) == 0) a.scales[row * 8 + (tid >> 5)] = (uint8_t)(E + 127);
         return;
     }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -203,6 +313,23 @@ hipError_t launch_pack_fp4(const uint16_t* x, int64_t nblk, uint8_t* codes, uint
     if (nblk == 0) return hipSuccess;
     const int64_t grid = (nblk + 255) / 256;
     hipLaunchKernelGGL(k_pack_fp4, dim3((uint32_t)grid), dim3(256), 0, s, x, nblk, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_fp4e(const uint16_t* x, int64_t nblk, uint8_t* codes, uint8_t* scales,
+                            hipStream_t s) {
+    if (nblk == 0) return hipSuccess;
+    const int64_t grid = (nblk + 255) / 256;
+    hipLaunchKernelGGL(k_pack_fp4e, dim3((uint32_t)grid), dim3(256), 0, s, x, nblk, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_fp4e(const uint8_t* codes, const uint8_t* scales, int64_t nblk, float* out,
+                              hipStream_t s) {
+    if (nblk == 0) return hipSuccess;
+    const int64_t grid = (nblk + 255) / 256;
+    hipLaunchKernelGGL(k_unpack_fp4e, dim3((uint32_t)grid), dim3(256), 0, s, codes, scales, nblk,
+                       out);
     return hipGetLastError();
 }
 

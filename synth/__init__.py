@@ -89,7 +89,7 @@ class Spec:
     t_cap: int                 # global KV rows allocated per sequence
     q_pos: List[int]
     q_seq: List[int]
-    kv_format: str             # "fp4" or "bf16"
+    kv_format: str             # "fp4" (E8M0 per 32), "fp4e" (E4M3 per 16) or "bf16"
     k: int                     # selected global entries per query
     window: int                # SWA window W
     pool: int = 0              # Full-layer candidate pool size in tokens (0 = none)

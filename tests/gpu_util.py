@@ -48,8 +48,9 @@ class DevInputs:
         self.x = x
         self.kv = dev16(x.kv)
         self.k_idx = dev16(x.k_idx)
-        if sp.kv_format == "fp4":
-            self.codes, self.scales = csa2.pack_fp4(self.kv)
+        if sp.kv_format in ("fp4", "fp4e"):
+            pack = csa2.pack_fp4 if sp.kv_format == "fp4" else csa2.pack_fp4_e4m3
+            self.codes, self.scales = pack(self.kv)
             self.cache = csa2.Cache(self.codes, self.k_idx, self.scales)
         else:
             self.codes = self.scales = None
@@ -60,6 +61,12 @@ class DevInputs:
         self.q_idx = [dev16(x.q_idx[l]) for l in range(sp.n_layers)]
         self.local = [csa2.Local(dev16(x.local_k[l]), dev16(x.local_v[l]), sp.window, sp.lo)
                       for l in range(sp.n_layers)]
+
+
+def oracle_cache(sp, kv, k_idx):
+    """The oracle's view of a cache of the spec's format."""
+    return oracle.Cache(kv, k_idx, fp4=sp.kv_format != "bf16",
+                        scale="e4m3" if sp.kv_format == "fp4e" else "e8m0")
 
 
 def boundary_check(gpu_ids, ids, scores, k, what=""):

@@ -41,8 +41,8 @@ def _new_rows(S, L, seed, varied=True):
 
 
 def _check_cache(sp, d, kv, k_idx, what):
-    if sp.kv_format == "fp4":
-        oc, os_ = oracle.fp4_pack(kv)
+    if sp.kv_format in ("fp4", "fp4e"):
+        oc, os_ = (oracle.fp4_pack if sp.kv_format == "fp4" else oracle.fp4e_pack)(kv)
         assert np.array_equal(host(d.codes), oc), what + ": FP4 codes"
         assert np.array_equal(host(d.scales), os_), what + ": FP4 scales"
     else:

@@ -8,7 +8,8 @@ import torch
 import oracle
 import synth
 import sparse_attention_shared_amd as csa2
-from gpu_util import (DevInputs, attn_check, bf16_to_f64, boundary_check, dev16, dev32, host)
+from gpu_util import (DevInputs, attn_check, bf16_to_f64, boundary_check, dev16, dev32, host,
+                      oracle_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -202,7 +203,7 @@ def test_sparse_attn_many_queries(kv, window, lo, cap, nq):
 
 def check_stack(sp, x, d, outs, sels, pool, sample=None):
     """Layer-by-layer cascade: each oracle step runs on the GPU's upstream picks."""
-    c = oracle.Cache(x.kv, x.k_idx, fp4=(sp.kv_format == "fp4"))
+    c = oracle_cache(sp, x.kv, x.k_idx)
     sels = [host(s) for s in sels]
     outs = [host(o) for o in outs]
     pool = host(pool) if pool is not None else None

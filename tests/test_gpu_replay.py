@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 import sparse_attention_shared_amd as csa2
-from gpu_util import DevInputs, attn_check, boundary_check, dev16, host
+from gpu_util import DevInputs, attn_check, boundary_check, dev16, host, oracle_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -65,7 +65,7 @@ def _rings_after(sp, x, seq, k_new, v_new):
 
 
 def check_replay(sp, x, seq, outs, sels, pool, lk, lv, sample):
-    c = oracle.Cache(x.kv, x.k_idx, fp4=(sp.kv_format == "fp4"))
+    c = oracle_cache(sp, x.kv, x.k_idx)
     sels = [host(s) for s in sels]
     outs = [host(o) for o in outs]
     pool = host(pool) if pool is not None else None
