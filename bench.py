@@ -42,11 +42,11 @@ PEAK_HBM_GBPS = 8000.0
 SCAN_KERNEL_SRC = os.path.join(ROOT, "sparse_attention_shared_amd", "csrc", "k_score.hip")
 
 
-def algorithmic_bytes(schedule, B, T, k, P, W, append=True):
+def algorithmic_bytes(schedule, B, T, k, P, W, append=True, row=136):
     """Bytes the method must move per step (the append, selected rows, the
     scans the indexer needs, window, queries, outputs and index lists); the
-    dense attention it avoids is not counted."""
-    row = 136            # FP4 K+V codes (128 B) + E8M0 scales (8 B)
+    dense attention it avoids is not counted.  row: bytes of one global K+V
+    entry (136 with E8M0 per 32, 144 with E4M3 per 16)."""
     kidx = 128           # bf16 indexer key
     win = W * 2 * 128 * 2
     qio = 16 * 128 * 2 * 2  # main Q in + output
@@ -371,6 +371,9 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", choices=["repeat", "page"], default="repeat")
+    ap.add_argument("--kv", choices=["fp4", "fp4e"], default="fp4",
+                    help="fp4: one E8M0 scale per 32 channels; fp4e: one E4M3 scale per 16")
+    ap.add_argument("--topk", type=int, default=0, help="selected entries per layer (default 2048)")
     ap.add_argument("--workload", choices=["decode", "prefill", "replay"], default="decode")
     ap.add_argument("--graph", action="store_true",
                     help="replay a recorded stack (HIP graph) per step instead of host launches")
@@ -409,6 +412,9 @@ def main():
     sp = synth.config(3)
     if args.schedule == "page":
         sp = synth.Spec(**{**sp.__dict__, "schedule": synth.page_schedule_20()})
+    if args.topk:
+        sp = synth.Spec(**{**sp.__dict__, "k": args.topk})
+    sp = synth.Spec(**{**sp.__dict__, "kv_format": args.kv})
     B, T, L = sp.n_seq, sp.t_cap, sp.n_layers
     print("generating inputs ...", file=sys.stderr, flush=True)
     x = synth.make_inputs(sp)
@@ -418,7 +424,7 @@ def main():
 
     kv = d16(x.kv)
     k_idx0 = d16(x.k_idx)
-    codes0, scales0 = csa2.pack_fp4(kv)
+    codes0, scales0 = (csa2.pack_fp4 if args.kv == "fp4" else csa2.pack_fp4_e4m3)(kv)
     del kv
     caches = []
     for i in range(args.copies):
@@ -513,7 +519,7 @@ def main():
         scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
 
     step_bytes = algorithmic_bytes(sp.schedule, B, T, sp.k, sp.pool, sp.window,
-                                   append=app is not None)
+                                   append=app is not None, row=136 if args.kv == "fp4" else 144)
     scan_bytes = B * T * 128
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     result = {
@@ -531,10 +537,14 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": ("decode append + " if app is not None else "") +
-                        "20-layer CSA2 decode stack over one shared FP4 (E2M1 + E8M0/32) global "
+                        "20-layer CSA2 decode stack over one shared FP4 (E2M1 + %s) global "
                         "KV cache: batch 4, context 131072, 16 q heads / 1 KV head, head_dim "
-                        "128, indexer dim 64, Full pool 8192 then [Reindex, Reuse x3]*, "
-                        "top-k 2048, SWA 128",
+                        "128, indexer dim 64, Full pool 8192 then %s, "
+                        "top-k %d, SWA 128" % ("E8M0/32" if args.kv == "fp4" else "E4M3/16",
+                                               "[Reindex, Reuse x3]*" if args.schedule == "repeat"
+                                               else "the pages' 1 Full / 4 Reindex / 15 Reuse",
+                                               sp.k),
+            "kv_scales": "E8M0/32" if args.kv == "fp4" else "E4M3/16",
             "batch": B, "context": T, "layers": L,
             "schedule": "".join("FIU"[m] for m in sp.schedule),
             "k": sp.k, "pool": sp.pool, "window": sp.window,
