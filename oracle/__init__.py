@@ -58,14 +58,15 @@ def lib():
         L.orc_topk.restype = i32
         L.orc_attention.argtypes = [P, P, P, i64, dbl, P]
         L.orc_attention.restype = None
-        L.orc_layer.argtypes = [i32, P, P, i32, i32, i64, P, P, P, P, P, P, P, P,
+        L.orc_layer.argtypes = [i32, P, P, i32, i32, i64, i32, P, P, P, P, P, P, P, P,
                                 i32, i32, i32, i32, i32, i32, P, P, dbl, P]
-        L.orc_attend.argtypes = [i32, P, P, i32, i64, P, P, P, P, P, i32, P, P,
+        L.orc_attend.argtypes = [i32, P, P, i32, i64, i32, P, P, P, P, P, i32, P, P,
                                  i32, i32, i32, dbl, P]
-        L.orc_stack.argtypes = [i32, P, i32, P, i32, i64, P, P, P, P, P, P, P, P,
+        L.orc_stack.argtypes = [i32, P, i32, P, i32, i64, i32, P, P, P, P, P, P, P, P,
                                 i32, i32, i32, i32, i32, i32, dbl, P, P, P]
+        L.orc_compress.argtypes = [P, i64, i32, i32, P]
         L.orc_append.argtypes = [i32, i64, P, P, P, P, P, i32, i32, P, P, P, P]
-        L.orc_replay.argtypes = [i32, P, i32, i32, i32, P, i32, i64, P, P, P, P, P, P, P, P,
+        L.orc_replay.argtypes = [i32, P, i32, i32, i32, P, i32, i64, i32, P, P, P, P, P, P, P, P,
                                  i32, i32, i32, i32, i32, i32, P, P, dbl, P, P, P]
         L.orc_append.restype = None
         _lib = L
@@ -175,8 +176,10 @@ class Cache:
     scale per 32 (``scale="e8m0"``) or one E4M3 scale per 16 (``"e4m3"``).
     """
 
-    def __init__(self, kv_bf16: np.ndarray, k_idx: np.ndarray, fp4: bool, scale: str = "e8m0"):
+    def __init__(self, kv_bf16: np.ndarray, k_idx: np.ndarray, fp4: bool, scale: str = "e8m0",
+                 m: int = 1):
         self.t_cap = kv_bf16.shape[1]
+        self.m = int(m)  # positions per entry: rows are entries of m positions
         self.fp4 = bool(fp4)
         self.fmt = 0
         self.k_idx = _c(k_idx, np.uint16)
@@ -194,7 +197,7 @@ class Cache:
             self.codes = self.scales = None
 
     def args(self):
-        return (self.fmt, self.t_cap, _p(self.kv), _p(self.codes), _p(self.scales))
+        return (self.fmt, self.t_cap, self.m, _p(self.kv), _p(self.codes), _p(self.scales))
 
 
 def layer(cache: Cache, q_pos, q_seq, mode, q, q_idx, lk, lv, window, lo, k,
@@ -312,3 +315,21 @@ def replay(cache: Cache, modes, seq, pos, q, q_idx, lk, lv, window, lo, k, pool,
     if rc:
         raise ValueError("orc_replay rc=%d" % rc)
     return out, sel, pool_out, lk, lv
+
+
+def compress(x_bf16: np.ndarray, m: int) -> np.ndarray:
+    """Sequence compression: bf16 [..., groups * m, dim] -> [..., groups, dim],
+    each entry the mean of its m positions rounded to bf16 (rows beyond the
+    last complete group are dropped)."""
+    x = _c(x_bf16, np.uint16)
+    dim = x.shape[-1]
+    n = x.shape[-2]
+    groups = n // m
+    lead = x.shape[:-2]
+    x = np.ascontiguousarray(x[..., :groups * m, :])
+    out = np.empty(lead + (groups, dim), np.uint16)
+    total = int(np.prod(lead, dtype=np.int64)) * groups
+    rc = lib().orc_compress(_p(x), total, m, dim, _p(out))
+    if rc:
+        raise ValueError("orc_compress rc=%d" % rc)
+    return out

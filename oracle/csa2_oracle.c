@@ -243,6 +243,49 @@ int orc_fp4e_unpack(const uint8_t *codes, const uint8_t *scales, int64_t rows, i
     return 0;
 }
 
+/* ---------------------------------------------- sequence compression m */
+
+/* Nearest bf16 to a double, ties to even (one rounding; bf16 has fp32's
+ * exponent range and 8 significant bits). */
+static uint16_t bf16_rne(double v)
+{
+    double a = fabs(v);
+    double r;
+    if (a == 0.0) {
+        r = 0.0;
+    } else if (a < ldexp(1.0, -126)) {   /* subnormal: multiples of 2^-133 */
+        r = ldexp(nearbyint(ldexp(a, 133)), -133);
+    } else {
+        int e;
+        frexp(a, &e);                     /* a in [2^(e-1), 2^e) */
+        r = ldexp(nearbyint(ldexp(a, 8 - e)), e - 8);
+    }
+    float f = (float)r;                   /* exact: r has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t h = (uint16_t)(u >> 16);
+    return signbit(v) ? (uint16_t)(h | 0x8000u) : h;
+}
+
+/* Sequence compression [CED, "What Does the Sequence Compression Rate
+ * Reduce?": with rate m, the information of m positions is combined into one
+ * entry].  The combine rule is not given; the reading taken here is the
+ * element-wise mean of the group's bf16 rows, rounded once to bf16.
+ * x: bf16 [groups][m][dim] -> out bf16 [groups][dim]. */
+int orc_compress(const uint16_t *x, int64_t groups, int32_t m, int32_t dim, uint16_t *out)
+{
+    if (m < 1 || dim <= 0 || groups < 0)
+        return 1;
+    for (int64_t g = 0; g < groups; ++g)
+        for (int32_t d = 0; d < dim; ++d) {
+            double s = 0.0;
+            for (int32_t i = 0; i < m; ++i)
+                s += bf16_val(x[(g * m + i) * dim + d]);
+            out[g * dim + d] = bf16_rne(s / m);
+        }
+    return 0;
+}
+
 /* ---------------------------------------------------------------- scores */
 
 /* s[j] = fl32(sum_d q[d] * k[j][d]) for j < n  [CED, Fig. 4: indexer Q from
@@ -350,14 +393,24 @@ void orc_attention(const uint16_t *q, const double *K, const double *V, int64_t 
 
 typedef struct {
     int32_t fp4;             /* 0: bf16 rows; 1: FP4 + E8M0 per 32; 2: FP4 + E4M3 per 16 */
-    int64_t t_cap;           /* rows per sequence */
+    int64_t t_cap;           /* rows (entries) per sequence */
+    int32_t m;               /* positions per entry (sequence compression rate) */
     const uint16_t *kv;      /* bf16 [n_seq][t_cap][256]: K | V */
     const uint8_t *codes;    /* FP4 [n_seq][t_cap][128] */
     const uint8_t *scales;   /* E8M0 [n_seq][t_cap][8], or E4M3 [n_seq][t_cap][16] */
     const uint16_t *k_idx;   /* bf16 [n_seq][t_cap][64] */
 } orc_cache;
 
-/* Global K and V of token j of sequence seq, as doubles. */
+/* The last entry a query at position t may read: with m positions per entry
+ * only complete groups are visible, entry j holding positions m j .. m j +
+ * m - 1 [CED, "What Does the Sequence Compression Rate Reduce?"; Fig. 2's
+ * causal rule applied to the group's last position].  -1 when none is. */
+static int64_t last_entry(const orc_cache *c, int64_t t)
+{
+    return (t + 1) / c->m - 1;
+}
+
+/* Global K and V of entry j of sequence seq, as doubles. */
 static void cache_row(const orc_cache *c, int32_t seq, int64_t j, double *K, double *V)
 {
     int64_t r = (int64_t)seq * c->t_cap + j;
@@ -399,7 +452,7 @@ static int attend_one(const orc_cache *c, int32_t seq, int32_t t, const uint16_t
     for (int32_t i = 0; i < k; ++i) {
         int32_t j = sel[i];
         if (j < 0) continue;
-        if (j > t || j >= c->t_cap) { rc = 3; goto done; } /* causal triangle, Fig. 2 */
+        if (j > last_entry(c, t) || j >= c->t_cap) { rc = 3; goto done; } /* causal, Fig. 2 */
         cache_row(c, seq, j, K + n * ORC_D, V + n * ORC_D);
         ++n;
     }
@@ -435,10 +488,11 @@ static int layer_one(const orc_cache *c, int mode, int32_t seq, int32_t t,
                      int32_t k, int32_t pool, int32_t block, int32_t *pool_io, int32_t *sel_io,
                      double scale, double *out)
 {
-    if (t < 0 || t >= c->t_cap) return 4;
+    if (t < 0 || t >= c->t_cap * c->m) return 4;
     const uint16_t *kseq = c->k_idx + (int64_t)seq * c->t_cap * ORC_DI;
+    const int64_t tg = last_entry(c, t);  /* entries 0..tg are causal */
     if (mode == ORC_FULL) {
-        int64_t n = (int64_t)t + 1;
+        int64_t n = tg + 1;
         float *s = (float *)malloc(sizeof(float) * (size_t)n);
         orc_scores(q_idx, kseq, n, s);
         if (block <= 1) {
@@ -455,7 +509,7 @@ static int layer_one(const orc_cache *c, int mode, int32_t seq, int32_t t,
             for (int32_t i = 0; i < nbsel; ++i)
                 for (int32_t r = 0; r < block; ++r) {
                     int64_t j = (int64_t)blocks[i] * block + r;
-                    int32_t id = (blocks[i] >= 0 && j <= t) ? (int32_t)j : -1;
+                    int32_t id = (blocks[i] >= 0 && j <= tg) ? (int32_t)j : -1;
                     pool_io[i * block + r] = id;
                     ps[i * block + r] = id >= 0 ? s[id] : -INFINITY;
                 }
@@ -520,14 +574,14 @@ void orc_append(int32_t n_seq, int64_t t_cap, const int32_t *pos,
  * pool_io [nq][pool], sel_io [nq][k] (inputs for Reindex / Reuse, outputs
  * otherwise); out [nq][16][128]. */
 int orc_layer(int32_t nq, const int32_t *q_pos, const int32_t *q_seq, int32_t mode,
-              int32_t fp4, int64_t t_cap, const uint16_t *kv, const uint8_t *codes,
+              int32_t fp4, int64_t t_cap, int32_t m, const uint16_t *kv, const uint8_t *codes,
               const uint8_t *scales, const uint16_t *k_idx,
               const uint16_t *q, const uint16_t *q_idx,
               const uint16_t *lk, const uint16_t *lv, int32_t cap, int32_t W, int32_t lo,
               int32_t k, int32_t pool, int32_t block, int32_t *pool_io, int32_t *sel_io,
               double scale, double *out)
 {
-    orc_cache c = {fp4, t_cap, kv, codes, scales, k_idx};
+    orc_cache c = {fp4, t_cap, m > 1 ? m : 1, kv, codes, scales, k_idx};
     if (mode == ORC_REINDEX && pool <= 0) return 6;
     if (mode == ORC_FULL && block > 1 && (pool <= 0 || pool % block)) return 6;
     for (int32_t i = 0; i < nq; ++i) {
@@ -543,12 +597,12 @@ int orc_layer(int32_t nq, const int32_t *q_pos, const int32_t *q_seq, int32_t mo
 /* Attention only, on a given selection (used to re-run attention on another
  * implementation's indices). */
 int orc_attend(int32_t nq, const int32_t *q_pos, const int32_t *q_seq,
-               int32_t fp4, int64_t t_cap, const uint16_t *kv, const uint8_t *codes,
+               int32_t fp4, int64_t t_cap, int32_t m, const uint16_t *kv, const uint8_t *codes,
                const uint8_t *scales, const uint16_t *q, const int32_t *sel, int32_t k,
                const uint16_t *lk, const uint16_t *lv, int32_t cap, int32_t W, int32_t lo,
                double scale, double *out)
 {
-    orc_cache c = {fp4, t_cap, kv, codes, scales, NULL};
+    orc_cache c = {fp4, t_cap, m > 1 ? m : 1, kv, codes, scales, NULL};
     for (int32_t i = 0; i < nq; ++i) {
         int rc = attend_one(&c, q_seq[i], q_pos[i], q + (int64_t)i * ORC_H * ORC_D,
                             sel + (int64_t)i * k, k, lk, lv, cap, W, lo, scale,
@@ -563,7 +617,7 @@ int orc_attend(int32_t nq, const int32_t *q_pos, const int32_t *q_seq,
  * q [L][n_seq][16][128], q_idx [L][n_seq][64], lk/lv [L][n_seq][cap][128],
  * sel_out [L][n_seq][k], pool_out [n_seq][pool], out [L][n_seq][16][128]. */
 int orc_stack(int32_t n_layers, const int32_t *modes, int32_t n_seq, const int32_t *q_pos,
-              int32_t fp4, int64_t t_cap, const uint16_t *kv, const uint8_t *codes,
+              int32_t fp4, int64_t t_cap, int32_t mrate, const uint16_t *kv, const uint8_t *codes,
               const uint8_t *scales, const uint16_t *k_idx,
               const uint16_t *q, const uint16_t *q_idx, const uint16_t *lk, const uint16_t *lv,
               int32_t cap, int32_t W, int32_t lo, int32_t k, int32_t pool, int32_t block,
@@ -580,7 +634,7 @@ int orc_stack(int32_t n_layers, const int32_t *modes, int32_t n_seq, const int32
         if (m == ORC_REUSE && l == 0) { rc = 7; break; }
         if (m == ORC_REINDEX && !have_pool) { rc = 7; break; }
         int64_t qo = (int64_t)l * n_seq;
-        rc = orc_layer(n_seq, q_pos, q_seq, m, fp4, t_cap, kv, codes, scales, k_idx,
+        rc = orc_layer(n_seq, q_pos, q_seq, m, fp4, t_cap, mrate, kv, codes, scales, k_idx,
                        q + qo * ORC_H * ORC_D, q_idx + qo * ORC_DI,
                        lk + qo * cap * ORC_D, lv + qo * cap * ORC_D, cap, W, lo,
                        k, pool, block, pool_out, sel, scale, out + qo * ORC_H * ORC_D);
@@ -604,7 +658,7 @@ int orc_stack(int32_t n_layers, const int32_t *modes, int32_t n_seq, const int32
  * q [L][n][16][128], q_idx [L][n][64], sel_out [L][n][k], pool_out [n][pool],
  * out [L][n][16][128]. */
 int orc_replay(int32_t n_layers, const int32_t *modes, int32_t n_seq, int32_t seq, int32_t n,
-               const int32_t *pos, int32_t fp4, int64_t t_cap, const uint16_t *kv,
+               const int32_t *pos, int32_t fp4, int64_t t_cap, int32_t mrate, const uint16_t *kv,
                const uint8_t *codes, const uint8_t *scales, const uint16_t *k_idx,
                const uint16_t *q, const uint16_t *q_idx, uint16_t *lk, uint16_t *lv,
                int32_t cap, int32_t W, int32_t lo, int32_t k, int32_t pool, int32_t block,
@@ -625,14 +679,14 @@ int orc_replay(int32_t n_layers, const int32_t *modes, int32_t n_seq, int32_t se
         uint16_t *rk = lk + (int64_t)l * n_seq * cap * ORC_D;
         uint16_t *rv = lv + (int64_t)l * n_seq * cap * ORC_D;
         for (int32_t i = 0; i < n; ++i) {
-            if (pos[i] < 0 || pos[i] >= t_cap) { rc = 4; break; }
+            if (pos[i] < 0 || pos[i] >= t_cap * (mrate > 1 ? mrate : 1)) { rc = 4; break; }
             int64_t slot = (int64_t)seq * cap + pos[i] % cap;
             memcpy(rk + slot * ORC_D, k_new + ((int64_t)l * n + i) * ORC_D, sizeof(uint16_t) * ORC_D);
             memcpy(rv + slot * ORC_D, v_new + ((int64_t)l * n + i) * ORC_D, sizeof(uint16_t) * ORC_D);
         }
         if (rc) break;
         int64_t qo = (int64_t)l * n;
-        rc = orc_layer(n, pos, q_seq, m, fp4, t_cap, kv, codes, scales, k_idx,
+        rc = orc_layer(n, pos, q_seq, m, fp4, t_cap, mrate, kv, codes, scales, k_idx,
                        q + qo * ORC_H * ORC_D, q_idx + qo * ORC_DI, rk, rv, cap, W, lo,
                        k, pool, block, pool_out, sel, scale, out + qo * ORC_H * ORC_D);
         if (m == ORC_FULL && pool > 0) have_pool = 1;
