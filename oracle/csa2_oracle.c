@@ -278,8 +278,10 @@ int orc_compress(const uint16_t *x, int64_t groups, int32_t m, int32_t dim, uint
         return 1;
     for (int64_t g = 0; g < groups; ++g)
         for (int32_t d = 0; d < dim; ++d) {
-            double s = 0.0;
-            for (int32_t i = 0; i < m; ++i)
+            /* the sum starts from the first element, so the mean of
+               negative zeros keeps its sign (IEEE: -0 + -0 = -0) */
+            double s = bf16_val(x[(g * m) * dim + d]);
+            for (int32_t i = 1; i < m; ++i)
                 s += bf16_val(x[(g * m + i) * dim + d]);
             out[g * dim + d] = bf16_rne(s / m);
         }

@@ -38,6 +38,9 @@ def test_mean_ties_and_exact_cases():
     # equal rows and opposite rows
     x = bf16([[[3.5, -2.0]], [[3.5, 2.0]]]).reshape(1, 2, 2)
     assert np.array_equal(f64(oracle.compress(x, 2))[0, 0], [3.5, 0.0])
+    # signed zeros follow IEEE addition: -0 and -0 give -0, -0 and +0 give +0
+    z = np.array([[[0x8000, 0x8000]], [[0x8000, 0x0000]]], np.uint16).reshape(1, 2, 2)
+    assert oracle.compress(z, 2)[0, 0].tolist() == [0x8000, 0x0000]
     # m = 1 is the identity; a trailing incomplete group is dropped
     y = bf16(np.arange(24, dtype=np.float32).reshape(1, 3, 8))
     assert np.array_equal(oracle.compress(y, 1), y)
