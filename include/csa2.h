@@ -80,14 +80,22 @@ typedef enum { CSA2_KV_BF16 = 0, CSA2_KV_FP4 = 1, CSA2_KV_FP4_E4M3 = 2 } csa2_kv
  *         16-channel blocks of K, bytes 8..15 those of V (144 B per token).
  *         This is exactly what csa2_pack_fp4_e4m3 writes for rows of 256.
  *   k_idx = indexer keys, bf16 [n_seq][t_cap][64].
- * data, scales and k_idx must be 16-byte aligned; t_cap <= 2^24. */
+ * data, scales and k_idx must be 16-byte aligned; t_cap <= 2^24.
+ * m: positions per global entry ("CED", section "What Does the Sequence
+ * Compression Rate Reduce?"): 0 or 1 — one entry per position (the
+ * decoder's cache); 2 — entry j combines positions 2j and 2j + 1 (the
+ * encoder's rate; see csa2_compress), and a query at position t reads only
+ * entries whose whole group is at or before t, i.e. j <= (t + 1) / 2 - 1.
+ * q_pos arguments stay token positions (the window reads positions).  The
+ * prefill calls and the replay take m <= 1 only (CSA2_ERR_UNSUPPORTED). */
 typedef struct {
     int32_t format;           /* csa2_kv_format */
     int32_t n_seq;
-    int64_t t_cap;            /* rows per sequence */
+    int64_t t_cap;            /* rows (entries) per sequence */
     const void *data;
     const uint8_t *scales;    /* FP4 only; NULL for BF16 */
     const uint16_t *k_idx;
+    int32_t m;                /* positions per entry: 0 or 1, or 2 */
 } csa2_cache;
 
 /* A layer's local (sliding-window) KV, a ring of `cap` slots per sequence:
@@ -143,6 +151,19 @@ csa2_status csa2_pack_fp4_e4m3(const uint16_t *x, int64_t rows, int32_t dim, uin
 csa2_status csa2_unpack_fp4_e4m3(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                                  int32_t dim, float *out, void *stream);
 
+/* ------------------------------------------------- sequence compression */
+
+/* Sequence compression ("CED", section "What Does the Sequence Compression
+ * Rate Reduce?": with rate m the information of m positions is combined into
+ * one entry).  The pages do not give the combine rule; this library's
+ * reading is the element-wise mean of the group's rows, rounded once to bf16
+ * (nearest, ties to even).  x: bf16 [groups][m][dim] (m consecutive
+ * positions per group); out: bf16 [groups][dim]; m in {1, 2}; dim % 8 == 0;
+ * x and out 16-byte aligned.  Apply it to the K | V rows and to the indexer
+ * keys, then pack the entries as usual. */
+csa2_status csa2_compress(const uint16_t *x, int64_t groups, int32_t m, int32_t dim,
+                          uint16_t *out, void *stream);
+
 /* --------------------------------------------------------------- append */
 
 /* Decode append ("CED", section "Why Prefill Recomputes a Recent Segment":
@@ -151,10 +172,13 @@ csa2_status csa2_unpack_fp4_e4m3(const uint8_t *codes, const uint8_t *scales, in
  * 0 <= pos[b] < t_cap, row pos[b] of the global cache receives kv[b] (K | V,
  * bf16 [n_seq][256]; FP4-packed exactly as csa2_pack_fp4 or
  * csa2_pack_fp4_e4m3 does for the cache's format, or copied for a BF16 cache) and, when kidx is not NULL, its indexer key kidx[b] (bf16
- * [n_seq][64]).  Then, for each of the n_local layers l, slot pos[b] %
+ * [n_seq][64]); with m = 2 the global row is the new entry's (already
+ * combined) row and is written to entry (pos[b] + 1) / 2 - 1 only when
+ * pos[b] completes its group (pos[b] odd).  Then, for each of the n_local
+ * layers l, slot pos[b] %
  * local[l].cap of that layer's ring receives k_new[l][b] and v_new[l][b]
- * (bf16 [n_seq][128] each).  Sequences with pos[b] outside [0, t_cap) are
- * skipped.  The call WRITES through cache->data, cache->scales,
+ * (bf16 [n_seq][128] each).  Sequences with pos[b] outside [0, m t_cap)
+ * are skipped.  The call WRITES through cache->data, cache->scales,
  * cache->k_idx and local[l].k / .v (the const of those structs is for the
  * read-only calls).  kv may be NULL to update the local rings only.
  *   pos: int32 [cache->n_seq]; local, k_new, v_new: host arrays [n_local]

@@ -11,6 +11,6 @@ from __future__ import annotations
 from ._lib import (  # noqa: F401
     FULL, REINDEX, REUSE, KV_BF16, KV_FP4, KV_FP4_E4M3, HEADS, HEAD_DIM, INDEX_DIM,
     Cache, Local, Csa2Error, lib, lib_path, version, device_check,
-    pack_fp4, unpack_fp4, pack_fp4_e4m3, unpack_fp4_e4m3, append, index_score, prefill_score, prefill_topk, prefill_topk_workspace, topk, expand_blocks, sparse_attn,
+    pack_fp4, unpack_fp4, pack_fp4_e4m3, unpack_fp4_e4m3, compress, append, index_score, prefill_score, prefill_topk, prefill_topk_workspace, topk, expand_blocks, sparse_attn,
     sparse_attn_workspace, stack_run, stack_workspace, StackPlan, replay_run, replay_workspace,
 )

@@ -25,7 +25,7 @@ _i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c
 
 class csa2_cache(ctypes.Structure):
     _fields_ = [("format", _i32), ("n_seq", _i32), ("t_cap", _i64), ("data", _P),
-                ("scales", _P), ("k_idx", _P)]
+                ("scales", _P), ("k_idx", _P), ("m", _i32)]
 
 
 class csa2_local(ctypes.Structure):
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_pack_fp4.argtypes = [_P, _i64, _i32, _P, _P, _P]
         L.csa2_unpack_fp4.argtypes = [_P, _P, _i64, _i32, _P, _P]
         L.csa2_pack_fp4_e4m3.argtypes = [_P, _i64, _i32, _P, _P, _P]
+        L.csa2_compress.argtypes = [_P, _i64, _i32, _i32, _P, _P]
         L.csa2_unpack_fp4_e4m3.argtypes = [_P, _P, _i64, _i32, _P, _P]
         L.csa2_append.argtypes = [ctypes.POINTER(csa2_cache), _P, _P, _P, _i32,
                                   ctypes.POINTER(csa2_local), ctypes.POINTER(_P),
@@ -100,7 +101,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_replay_workspace.argtypes = [ctypes.POINTER(csa2_replay_desc), ctypes.POINTER(_sz)]
         L.csa2_replay_run.argtypes = [ctypes.POINTER(csa2_replay_desc), _P, _sz, _P]
         for f in ("csa2_pack_fp4", "csa2_unpack_fp4", "csa2_pack_fp4_e4m3", "csa2_unpack_fp4_e4m3",
-                  "csa2_append", "csa2_index_score", "csa2_prefill_score",
+                  "csa2_append", "csa2_compress", "csa2_index_score", "csa2_prefill_score",
                   "csa2_prefill_topk", "csa2_prefill_topk_workspace", "csa2_topk",
                   "csa2_topk_workspace", "csa2_expand_blocks", "csa2_sparse_attn",
                   "csa2_sparse_attn_workspace", "csa2_stack_workspace", "csa2_stack_run",
@@ -161,7 +162,7 @@ class Cache:
     """
 
     def __init__(self, data: torch.Tensor, k_idx: torch.Tensor,
-                 scales: Optional[torch.Tensor] = None):
+                 scales: Optional[torch.Tensor] = None, m: int = 1):
         self.fp4 = scales is not None
         self.data, self.scales, self.k_idx = data, scales, _bits16(k_idx)
         self.n_seq, self.t_cap = int(k_idx.shape[0]), int(k_idx.shape[1])
@@ -175,8 +176,10 @@ class Cache:
             _bits16(data)
             assert tuple(data.shape) == (self.n_seq, self.t_cap, 256)
         self.format = fmt
+        self.m = int(m)  # positions per entry (rows are entries)
         self.c = csa2_cache(fmt, self.n_seq, self.t_cap,
-                            _ptr(data), _ptr(scales) if self.fp4 else None, _ptr(self.k_idx))
+                            _ptr(data), _ptr(scales) if self.fp4 else None, _ptr(self.k_idx),
+                            self.m)
 
 
 class Local:
@@ -198,6 +201,22 @@ def pack_fp4(x: torch.Tensor):
     _check("csa2_pack_fp4", lib().csa2_pack_fp4(_ptr(x), rows, dim, _ptr(codes), _ptr(scales),
                                                 _stream()))
     return codes, scales
+
+
+def compress(x: torch.Tensor, m: int) -> torch.Tensor:
+    """Sequence compression (csa2_compress): bf16 [..., groups * m, dim] ->
+    [..., groups, dim], each entry the mean of its m positions (bf16)."""
+    x = _bits16(x)
+    if not x.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    dim, n = int(x.shape[-1]), int(x.shape[-2])
+    if n % m:
+        raise ValueError("positions must fill whole groups")
+    lead = tuple(x.shape[:-2])
+    groups = (x.numel() // (n * dim)) * (n // m) if dim and n else 0
+    out = torch.empty(lead + (n // m, dim), dtype=x.dtype, device=x.device)
+    _check("csa2_compress", lib().csa2_compress(_ptr(x), groups, m, dim, _ptr(out), _stream()))
+    return out
 
 
 def pack_fp4_e4m3(x: torch.Tensor):

@@ -58,6 +58,7 @@ csa2_status check_cache(const csa2_cache* c, bool need_kv, bool need_idx, CacheV
     if (c->format != CSA2_KV_BF16 && c->format != CSA2_KV_FP4 && c->format != CSA2_KV_FP4_E4M3)
         return CSA2_ERR_INVALID_ARG;
     if (c->n_seq <= 0 || c->t_cap <= 0 || c->t_cap > ((int64_t)1 << 24)) return CSA2_ERR_SHAPE;
+    if (c->m < 0 || c->m > 2) return CSA2_ERR_SHAPE;
     if (need_kv) {
         if (!c->data || !aligned16(c->data)) return CSA2_ERR_INVALID_ARG;
         if (c->format != CSA2_KV_BF16 && (!c->scales || !aligned16(c->scales)))
@@ -65,6 +66,7 @@ csa2_status check_cache(const csa2_cache* c, bool need_kv, bool need_idx, CacheV
     }
     if (need_idx && (!c->k_idx || !aligned16(c->k_idx))) return CSA2_ERR_INVALID_ARG;
     v->fp4 = c->format == CSA2_KV_FP4 ? 1 : c->format == CSA2_KV_FP4_E4M3 ? 2 : 0;
+    v->msh = c->m == 2 ? 1 : 0;
     v->n_seq = c->n_seq;
     v->t_cap = c->t_cap;
     v->data = c->data;
@@ -113,6 +115,7 @@ hipError_t enqueue_append(const CacheView& cv, int32_t rows, int32_t seq, const 
     a.seq = seq;
     a.q_seq_out = q_seq_out;
     a.t_cap = cv.t_cap;
+    a.msh = cv.msh;
     a.fp4 = cv.fp4;
     a.kv = kv;
     a.kidx = kidx;
@@ -256,6 +259,14 @@ csa2_status csa2_unpack_fp4(const uint8_t* codes, const uint8_t* scales, int64_t
     return from_hip(launch_unpack_fp4(codes, scales, rows * (dim / 32), out, (hipStream_t)stream));
 }
 
+csa2_status csa2_compress(const uint16_t* x, int64_t groups, int32_t m, int32_t dim,
+                          uint16_t* out, void* stream) {
+    if (groups < 0 || dim <= 0 || dim % 8 || (m != 1 && m != 2)) return CSA2_ERR_SHAPE;
+    if (groups > 0 && (!x || !out || !aligned16(x) || !aligned16(out))) return CSA2_ERR_INVALID_ARG;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_compress(x, groups, m, dim, out, (hipStream_t)stream));
+}
+
 csa2_status csa2_append(const csa2_cache* cache, const int32_t* pos, const uint16_t* kv,
                         const uint16_t* kidx, int32_t n_local, const csa2_local* local,
                         const uint16_t* const* k_new, const uint16_t* const* v_new,
@@ -302,6 +313,7 @@ csa2_status csa2_prefill_score(const csa2_cache* cache, int32_t seq, const uint1
                                void* stream) {
     CacheView cv;
     if (csa2_status st = check_cache(cache, false, true, &cv)) return st;
+    if (cv.msh) return CSA2_ERR_UNSUPPORTED;  // prefill kernels read one position per entry
     if (nq < 0 || seq < 0 || seq >= cv.n_seq || ld_scores < cv.t_cap) return CSA2_ERR_SHAPE;
     if (nq > 65535 * 64) return CSA2_ERR_SHAPE;
     if (nq > 0 && (!q_idx || !q_pos || !scores || !aligned16(q_idx))) return CSA2_ERR_INVALID_ARG;
@@ -321,6 +333,7 @@ csa2_status csa2_prefill_topk(const csa2_cache* cache, int32_t seq, const uint16
                               size_t ws_bytes, void* stream) {
     CacheView cv;
     if (csa2_status st = check_cache(cache, false, true, &cv)) return st;
+    if (cv.msh) return CSA2_ERR_UNSUPPORTED;
     if (nq < 0 || seq < 0 || seq >= cv.n_seq || k < 1 || k > kPfMaxK || cv.t_cap > kPfMaxT)
         return CSA2_ERR_SHAPE;
     if (nq == 0) return CSA2_OK;
@@ -507,6 +520,7 @@ static csa2_status check_replay(const csa2_replay_desc* d, CacheView* cv, int32_
         return CSA2_ERR_INVALID_ARG;
     if (d->n_layers <= 0) return CSA2_ERR_SHAPE;
     if (csa2_status st = check_cache(d->cache, true, true, cv)) return st;
+    if (cv->msh) return CSA2_ERR_UNSUPPORTED;
     if (d->seq < 0 || d->seq >= cv->n_seq) return CSA2_ERR_SHAPE;
     if (d->n <= 0 || d->n > 65535) return CSA2_ERR_SHAPE;
     return check_job(replay_job(d), max_window);
@@ -607,7 +621,8 @@ static csa2_status enqueue_stack(const StackJob& j, const CacheView& cv, const S
                 if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)j.scan_events[1], s);
                 if (e == hipSuccess)
                     e = launch_topk(bscores, S, nb, nb, nullptr, nbsel, blocks, 0, nullptr, tkws, s);
-                if (e == hipSuccess) e = launch_expand_blocks(blocks, S, nbsel, B, j.q_pos, pool, s);
+                if (e == hipSuccess)
+                    e = launch_expand_blocks(blocks, S, nbsel, B, j.q_pos, pool, s, cv.msh);
                 if (e == hipSuccess) e = rescore_pool(l, dst);
             } else {
                 e = rescore_pool(l, dst);

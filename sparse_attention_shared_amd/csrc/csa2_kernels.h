@@ -12,7 +12,8 @@ namespace csa2 {
 struct CacheView {
     int32_t fp4;            // 0: bf16 rows; 1: FP4 + E8M0 per 32; 2: FP4 + E4M3 per 16
     int32_t n_seq;
-    int64_t t_cap;
+    int64_t t_cap;          // entries per sequence
+    int32_t msh;            // log2 of positions per entry (0, or 1 for m = 2)
     const void* data;       // bf16 [n_seq][t_cap][256] or codes [n_seq][t_cap][128]
     const uint8_t* scales;  // [n_seq][t_cap][8] (E8M0) or [n_seq][t_cap][16] (E4M3)
     const uint16_t* k_idx;  // [n_seq][t_cap][64]
@@ -34,6 +35,10 @@ hipError_t launch_pack_fp4e(const uint16_t* x, int64_t nblk, uint8_t* codes, uin
 hipError_t launch_unpack_fp4e(const uint8_t* codes, const uint8_t* scales, int64_t nblk, float* out,
                               hipStream_t s);
 
+// Sequence compression: out[g] = bf16 mean of x[g][0..m), m in {1, 2}; dim % 8 == 0.
+hipError_t launch_compress(const uint16_t* x, int64_t groups, int32_t m, int32_t dim, uint16_t* out,
+                           hipStream_t s);
+
 // Dense indexer scores: scores[i][b], b < ceil(t_cap / block), block in {1, 64}.
 // Decode append: the new position's global row (FP4-packed or copied),
 // indexer key and every listed layer's local K/V ring slot, per sequence.
@@ -46,10 +51,12 @@ struct AppendLocal {
     int32_t cap;
 };
 struct AppendArgs {
-    const int32_t* pos;  // [n rows]; rows outside [0, t_cap) are skipped
+    const int32_t* pos;  // [n rows] positions; rows outside [0, t_cap << msh) are skipped
     int32_t seq;         // -1: row b belongs to sequence b; else every row to `seq`
     int32_t* q_seq_out;  // null, or [n rows]: receives each row's sequence
-    int64_t t_cap;
+    int64_t t_cap;         // entries per sequence
+    int32_t msh;           // log2 of positions per entry: the global row of a
+                           // position completing its group goes to that entry
     int32_t fp4;           // the cache's format code (CacheView::fp4)
     const uint16_t* kv;    // bf16 [n rows][256] or null
     const uint16_t* kidx;  // bf16 [n rows][64] or null
@@ -100,8 +107,11 @@ size_t topk_ws_bytes(int32_t nq, int64_t n, int32_t k, int32_t k2);
 hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, const int32_t* ids,
                        int32_t k, int32_t* out, int32_t k2, int32_t* out2, void* ws, hipStream_t s);
 
+// msh: the positions are those of entries of 2^msh positions (q_pos stays a
+// token position).
 hipError_t launch_expand_blocks(const int32_t* blocks, int32_t nq, int32_t nb, int32_t block,
-                                const int32_t* q_pos, int32_t* tokens, hipStream_t s);
+                                const int32_t* q_pos, int32_t* tokens, hipStream_t s,
+                                int32_t msh = 0);
 
 // From this many queries on, attention runs one workgroup per query (no
 // workspace); below it, each query is split over several workgroups.  The

@@ -192,9 +192,12 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
     const float NEG = -__builtin_inff();
 
     const int32_t seq = q_seq ? q_seq[qi] : qi;
-    int64_t t = q_pos[qi];
+    int64_t t = q_pos[qi];  // the query's position (window)
     if (seq < 0 || seq >= c.n_seq) t = -1;
-    if (t >= c.t_cap) t = c.t_cap - 1;
+    if (t >= (c.t_cap << c.msh)) t = (c.t_cap << c.msh) - 1;
+    // the last global entry it may read: entries of 2^msh positions count
+    // once their whole group is at or before t
+    const int64_t tg = ((t + 1) >> c.msh) - 1;
     int64_t w0 = t - loc.window + 1;
     if (w0 < loc.lo) w0 = loc.lo;
     if (w0 < 0) w0 = 0;
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
             const int64_t e = (int64_t)chunk * kWgEntries + wave * kBlk + 2 * n16 + u;
             if (e < k) {
                 const int64_t j = sel[(int64_t)qi * k + e];
-                if (j >= 0 && j <= t) {
+                if (j >= 0 && j <= tg) {
                     kind[u] = c.fp4 ? 1 : 2;
                     row[u] = (int64_t)seq * c.t_cap + j;
                 }
@@ -503,9 +506,12 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
     uint32_t* vr = sh.u.vr[wave];
 
     const int32_t seq = q_seq ? q_seq[qi] : qi;
-    int64_t t = q_pos[qi];
+    int64_t t = q_pos[qi];  // the query's position (window)
     if (seq < 0 || seq >= c.n_seq) t = -1;
-    if (t >= c.t_cap) t = c.t_cap - 1;
+    if (t >= (c.t_cap << c.msh)) t = (c.t_cap << c.msh) - 1;
+    // the last global entry it may read: entries of 2^msh positions count
+    // once their whole group is at or before t
+    const int64_t tg = ((t + 1) >> c.msh) - 1;
     int64_t w0 = t - loc.window + 1;
     if (w0 < loc.lo) w0 = loc.lo;
     if (w0 < 0) w0 = 0;
@@ -535,7 +541,7 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
         kind = 0;
         row = 0;
         if (e < k) {
-            if (j >= 0 && j <= t) {
+            if (j >= 0 && j <= tg) {
                 kind = c.fp4 ? 1 : 2;
                 row = (int64_t)seq * c.t_cap + j;
             }
@@ -632,7 +638,7 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
         c.scales ? c.scales + (int64_t)max(seq, 0) * c.t_cap * row_scale_bytes<SF>() : nullptr;
     // An empty slot reads row 0 (no branch around the loads) with scale 1:
     // its codes are finite and its p is 0, so it adds nothing.
-    const int32_t t32 = (int32_t)t;  // positions fit 32 bits (t_cap <= 2^31)
+    const int32_t t32 = (int32_t)tg;  // entries fit 32 bits (t_cap <= 2^24)
     auto fetch = [&](int32_t j, RowRaw& r) {
         const bool ok = j >= 0 && j <= t32;
         const int64_t jj = ok ? j : 0;

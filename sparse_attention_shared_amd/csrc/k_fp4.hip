@@ -226,13 +226,15 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
         int32_t p = a.pos[b];
         uint32_t x = 0;
         uint4 ki = make_uint4(0u, 0u, 0u, 0u);
+        // entries of 2^msh positions: only a position completing its group
+        // writes the group's entry
         if (a.kv) x = a.kv[(int64_t)b * 256 + tid];
         if (a.kidx && tid < 8) ki = reinterpret_cast<const uint4*>(a.kidx + (int64_t)b * 64)[tid];
         hold(x);
         hold(ki);
         hold(p);
-        if (p < 0 || p >= a.t_cap) return;
-        const int64_t row = sb * a.t_cap + p;
+        if (p < 0 || p >= (a.t_cap << a.msh) || ((p + 1) & ((1 << a.msh) - 1)) != 0) return;
+        const int64_t row = sb * a.t_cap + ((p + 1) >> a.msh) - 1;
         if (a.kidx && tid < 8) reinterpret_cast<uint4*>(a.k_idx + row * 64)[tid] = ki;
         if (!a.kv) return;
         if (!a.fp4) {
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     uint32_t v = src[lane];
     hold(v);
     hold(p);
-    if (p < 0 || p >= a.t_cap) return;
+    if (p < 0 || p >= (a.t_cap << a.msh)) return;
     const int64_t slot = sb * cap + p % cap;
     dst[slot * 64 + lane] = v;
 }
@@ -286,6 +288,46 @@ hipError_t launch_append(const AppendArgs& a, int32_t n_rows, hipStream_t s) {
     if (n_rows == 0) return hipSuccess;
     const uint32_t groups = (uint32_t)((a.n_local + kAppendLayersPerWg - 1) / kAppendLayersPerWg);
     hipLaunchKernelGGL(k_append, dim3((uint32_t)n_rows, 1 + groups), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---- sequence compression ("CED", section "What Does the Sequence
+// Compression Rate Reduce?": with rate m the information of m positions is
+// combined into one entry; the combine rule is not given, the element-wise
+// mean is the reading taken).  One thread per 8 channels of a group.  For
+// m = 2: a + b in fp32 is exact unless the exponents differ by more than 15,
+// and then the sum lies within 2^-16 (relative) of a value bf16 represents,
+// far from any bf16 rounding tie, so halving and rounding to bf16 once gives
+// the correctly rounded mean.
+__global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ x, int64_t n8,
+                                                  int32_t m, int32_t dim, uint16_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8-channel piece of the output
+    if (i >= n8) return;
+    const int64_t per = dim / 8;
+    const int64_t g = i / per, c = i % per;
+    const uint4* src = reinterpret_cast<const uint4*>(x + g * m * dim) + c;
+    uint4 a = src[0];
+    if (m == 2) {
+        const uint4 b = src[per];
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+        uint32_t r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float lo = (__uint_as_float(aw[j] << 16) + __uint_as_float(bw[j] << 16)) * 0.5f;
+            const float hi = (__uint_as_float(aw[j] & 0xFFFF0000u) + __uint_as_float(bw[j] & 0xFFFF0000u)) * 0.5f;
+            r[j] = (uint32_t)f_to_bf16(lo) | ((uint32_t)f_to_bf16(hi) << 16);
+        }
+        a = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+    reinterpret_cast<uint4*>(out + g * dim)[c] = a;
+}
+
+hipError_t launch_compress(const uint16_t* x, int64_t groups, int32_t m, int32_t dim, uint16_t* out,
+                           hipStream_t s) {
+    const int64_t n8 = groups * (dim / 8);
+    if (n8 == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_compress, dim3((uint32_t)((n8 + 255) / 256)), dim3(256), 0, s, x, n8, m, dim,
+                       out);
     return hipGetLastError();
 }
 

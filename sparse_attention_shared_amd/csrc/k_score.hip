@@ -43,7 +43,7 @@ __device__ __forceinline__ void load_q8(const uint16_t* q, float* qf) {
 // [16 sub, 16 sub + 16) of key base + 8 r + grp in round r.
 template <int BLOCK>
 __global__ __launch_bounds__(256) void k_score_dense(const uint16_t* __restrict__ k_idx,
-                                                     int32_t n_seq, int64_t t_cap,
+                                                     int32_t n_seq, int64_t t_cap, int32_t msh,
                                                      const uint16_t* __restrict__ q_idx,
                                                      const int32_t* __restrict__ q_pos,
                                                      const int32_t* __restrict__ q_seq,
@@ -54,7 +54,9 @@ __global__ __launch_bounds__(256) void k_score_dense(const uint16_t* __restrict_
     const int64_t base = (int64_t)blockIdx.x * kScoreTile + wave * 64;
     float* srow = scores + (int64_t)qi * ld;
     const int32_t seq = q_seq ? q_seq[qi] : qi;
-    int64_t t = q_pos[qi];
+    // the last entry the query may read: entries of 2^msh positions count
+    // once their whole group is at or before the query's position
+    int64_t t = (((int64_t)q_pos[qi] + 1) >> msh) - 1;
     if (seq < 0 || seq >= n_seq) t = -1;  // a bad sequence id reads nothing
     if (t >= t_cap) t = t_cap - 1;
     if (base >= t_cap) return;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(256) void k_score_dense(const uint16_t* __restrict_
 // grid: (ceil(n_cand / 256), nq).  Same lane layout; key c of the tile is
 // position cand[qi][c].
 __global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__ k_idx,
-                                                    int32_t n_seq, int64_t t_cap,
+                                                    int32_t n_seq, int64_t t_cap, int32_t msh,
                                                     const uint16_t* __restrict__ q_idx,
                                                     const int32_t* __restrict__ q_pos,
                                                     const int32_t* __restrict__ q_seq,
@@ -116,7 +118,9 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__
     float* srow = scores + (int64_t)qi * ld;
     const int32_t* crow = cand + (int64_t)qi * n_cand;
     const int32_t seq = q_seq ? q_seq[qi] : qi;
-    int64_t t = q_pos[qi];
+    // the last entry the query may read: entries of 2^msh positions count
+    // once their whole group is at or before the query's position
+    int64_t t = (((int64_t)q_pos[qi] + 1) >> msh) - 1;
     if (seq < 0 || seq >= n_seq) t = -1;
     if (t >= t_cap) t = t_cap - 1;
     float qf[8];
@@ -151,7 +155,7 @@ constexpr int kSelMaxCand = 16384;
 constexpr int kSelNT = 1024;
 
 __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restrict__ k_idx,
-                                                         int32_t n_seq, int64_t t_cap,
+                                                         int32_t n_seq, int64_t t_cap, int32_t msh,
                                                          const uint16_t* __restrict__ q_idx,
                                                          const int32_t* __restrict__ q_pos,
                                                          const int32_t* __restrict__ q_seq,
@@ -168,7 +172,9 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
     float* srow = scores + (int64_t)qi * n_cand;
     const int32_t* crow = cand + (int64_t)qi * n_cand;
     const int32_t seq = q_seq ? q_seq[qi] : qi;
-    int64_t t = q_pos[qi];
+    // the last entry the query may read: entries of 2^msh positions count
+    // once their whole group is at or before the query's position
+    int64_t t = (((int64_t)q_pos[qi] + 1) >> msh) - 1;
     if (seq < 0 || seq >= n_seq) t = -1;
     if (t >= t_cap) t = t_cap - 1;
     if (base < n_cand) {
@@ -212,8 +218,8 @@ hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const 
     if (nq == 0 || n_cand == 0) return hipSuccess;
     if (n_cand > kSelMaxCand) return hipErrorInvalidValue;
     dim3 grid((uint32_t)((n_cand + kSelNT - 1) / kSelNT), (uint32_t)nq);
-    hipLaunchKernelGGL(k_score_select, grid, dim3(kSelNT), 0, s, c.k_idx, c.n_seq, c.t_cap, q_idx,
-                       q_pos, q_seq, cand, n_cand, scores, ctr, k, sel);
+    hipLaunchKernelGGL(k_score_select, grid, dim3(kSelNT), 0, s, c.k_idx, c.n_seq, c.t_cap, c.msh,
+                       q_idx, q_pos, q_seq, cand, n_cand, scores, ctr, k, sel);
     return hipGetLastError();
 }
 
@@ -224,10 +230,10 @@ hipError_t launch_score_dense(const CacheView& c, const uint16_t* q_idx, const i
     dim3 grid((uint32_t)((c.t_cap + kScoreTile - 1) / kScoreTile), (uint32_t)nq);
     if (block == 1)
         hipExtLaunchKernelGGL(k_score_dense<1>, grid, dim3(256), 0, s, ev0, ev1, 0, c.k_idx, c.n_seq,
-                              c.t_cap, q_idx, q_pos, q_seq, scores, ld);
+                              c.t_cap, c.msh, q_idx, q_pos, q_seq, scores, ld);
     else
         hipExtLaunchKernelGGL(k_score_dense<64>, grid, dim3(256), 0, s, ev0, ev1, 0, c.k_idx, c.n_seq,
-                              c.t_cap, q_idx, q_pos, q_seq, scores, ld);
+                              c.t_cap, c.msh, q_idx, q_pos, q_seq, scores, ld);
     return hipGetLastError();
 }
 
@@ -236,7 +242,7 @@ hipError_t launch_score_cand(const CacheView& c, const uint16_t* q_idx, const in
                              float* scores, int64_t ld, hipStream_t s) {
     if (nq == 0 || n_cand == 0) return hipSuccess;
     dim3 grid((uint32_t)((n_cand + kScoreTile - 1) / kScoreTile), (uint32_t)nq);
-    hipLaunchKernelGGL(k_score_cand, grid, dim3(256), 0, s, c.k_idx, c.n_seq, c.t_cap, q_idx,
+    hipLaunchKernelGGL(k_score_cand, grid, dim3(256), 0, s, c.k_idx, c.n_seq, c.t_cap, c.msh, q_idx,
                        q_pos, q_seq, cand, n_cand, scores, ld);
     return hipGetLastError();
 }

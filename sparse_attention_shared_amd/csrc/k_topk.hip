@@ -418,25 +418,27 @@ hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, c
 }
 
 // tokens[i][c*block + r] = blocks[i][c]*block + r when the block is chosen and
-// the position is <= q_pos[i], else -1.
+// the entry is readable by query i (entries of 2^msh positions: the whole
+// group at or before q_pos[i]), else -1.
 __global__ __launch_bounds__(256) void k_expand_blocks(const int32_t* __restrict__ blocks, int32_t nb,
                                                        int32_t block, const int32_t* __restrict__ q_pos,
-                                                       int32_t* __restrict__ tokens) {
+                                                       int32_t msh, int32_t* __restrict__ tokens) {
     const int32_t qi = blockIdx.y;
     const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t n = (int64_t)nb * block;
     if (j >= n) return;
     const int32_t b = blocks[(int64_t)qi * nb + j / block];
     const int64_t pos = (int64_t)b * block + j % block;
-    tokens[(int64_t)qi * n + j] = (b >= 0 && pos <= q_pos[qi]) ? (int32_t)pos : -1;
+    const int64_t last = (((int64_t)q_pos[qi] + 1) >> msh) - 1;
+    tokens[(int64_t)qi * n + j] = (b >= 0 && pos <= last) ? (int32_t)pos : -1;
 }
 
 hipError_t launch_expand_blocks(const int32_t* blocks, int32_t nq, int32_t nb, int32_t block,
-                                const int32_t* q_pos, int32_t* tokens, hipStream_t s) {
+                                const int32_t* q_pos, int32_t* tokens, hipStream_t s, int32_t msh) {
     const int64_t n = (int64_t)nb * block;
     if (nq == 0 || n == 0) return hipSuccess;
     hipLaunchKernelGGL(k_expand_blocks, dim3((uint32_t)((n + 255) / 256), (uint32_t)nq), dim3(256),
-                       0, s, blocks, nb, block, q_pos, tokens);
+                       0, s, blocks, nb, block, q_pos, msh, tokens);
     return hipGetLastError();
 }
 

@@ -63,10 +63,10 @@ class DevInputs:
                       for l in range(sp.n_layers)]
 
 
-def oracle_cache(sp, kv, k_idx):
-    """The oracle's view of a cache of the spec's format."""
+def oracle_cache(sp, kv, k_idx, m=1):
+    """The oracle's view of a cache of the spec's format (m positions per entry)."""
     return oracle.Cache(kv, k_idx, fp4=sp.kv_format != "bf16",
-                        scale="e4m3" if sp.kv_format == "fp4e" else "e8m0")
+                        scale="e4m3" if sp.kv_format == "fp4e" else "e8m0", m=m)
 
 
 def boundary_check(gpu_ids, ids, scores, k, what=""):

@@ -295,3 +295,24 @@ def test_replay_without_a_device_reports_no_device():
     n = _lib._sz()
     assert L.csa2_replay_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
     assert L.csa2_replay_run(ctypes.byref(d), FAKE, n.value, None) == NO_DEVICE
+
+
+def test_compression_rate_validation():
+    L = csa2.lib()
+    bp = ctypes.byref
+    c = _cache()
+    c.m = 3
+    n = _lib._sz()
+    assert L.csa2_index_score(bp(c), FAKE, FAKE, None, 2, None, 0, 1, FAKE, 100, None) == SHAPE
+    c.m = 2  # the prefill kernels read one position per entry
+    assert L.csa2_prefill_score(bp(c), 0, FAKE, FAKE, 4, FAKE, 100, None) == UNSUPPORTED
+    assert L.csa2_prefill_topk(bp(c), 0, FAKE, FAKE, 4, 64, FAKE, FAKE, 1 << 30, None) == UNSUPPORTED
+    d, keep = _replay()
+    keep["cache"].m = 2
+    assert L.csa2_replay_workspace(bp(d), bp(n)) == UNSUPPORTED
+    # csa2_compress: m in {1, 2}, dim % 8 == 0, aligned operands
+    assert L.csa2_compress(FAKE, 4, 3, 256, FAKE, None) == SHAPE
+    assert L.csa2_compress(FAKE, 4, 2, 250, FAKE, None) == SHAPE
+    assert L.csa2_compress(FAKE, -1, 2, 256, FAKE, None) == SHAPE
+    assert L.csa2_compress(None, 4, 2, 256, FAKE, None) == INVALID
+    assert L.csa2_compress(FAKE_ODD, 4, 2, 256, FAKE, None) == INVALID

@@ -201,9 +201,11 @@ def test_sparse_attn_many_queries(kv, window, lo, cap, nq):
 
 # ---------------------------------------------------------------- stack
 
-def check_stack(sp, x, d, outs, sels, pool, sample=None):
-    """Layer-by-layer cascade: each oracle step runs on the GPU's upstream picks."""
-    c = oracle_cache(sp, x.kv, x.k_idx)
+def check_stack(sp, x, d, outs, sels, pool, sample=None, rate=1):
+    """Layer-by-layer cascade: each oracle step runs on the GPU's upstream picks.
+    With rate > 1, x.kv / x.k_idx hold entries of `rate` positions and a
+    query at t reads entries 0 .. (t + 1) / rate - 1."""
+    c = oracle_cache(sp, x.kv, x.k_idx, rate)
     sels = [host(s) for s in sels]
     outs = [host(o) for o in outs]
     pool = host(pool) if pool is not None else None
@@ -211,7 +213,7 @@ def check_stack(sp, x, d, outs, sels, pool, sample=None):
     worst = 0.0
     for l, m in enumerate(sp.schedule):
         for b in seqs:
-            t = sp.q_pos[b]
+            t = (sp.q_pos[b] + 1) // rate - 1  # the last readable entry
             g = sels[l][b]
             assert np.all(g <= t), "causal"
             if m == synth.REUSE:
