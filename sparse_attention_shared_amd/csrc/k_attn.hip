@@ -46,9 +46,10 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// 2^(byte - 127) as fp32 (exact; byte 0 gives the subnormal 2^-127).
+// 2^(byte - 127) as fp32 (exact; byte 0 gives the subnormal 2^-127, kept
+// since fp32 denormals are not flushed).
 __device__ __forceinline__ float e8m0_value(uint32_t byte) {
-    return __uint_as_float(byte ? (byte << 23) : 0x00400000u);
+    return __builtin_amdgcn_ldexpf(1.0f, (int)byte - 127);
 }
 
 // A decode scale split for the hardware conversion, which applies only the
@@ -639,60 +640,66 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
     // An empty slot reads row 0 (no branch around the loads) with scale 1:
     // its codes are finite and its p is 0, so it adds nothing.
     const int32_t t32 = (int32_t)tg;  // entries fit 32 bits (t_cap <= 2^24)
+    // Row offsets stay 32-bit (entries < 2^24, so entry * 128 < 2^31) over a
+    // uniform base, which the loads take as scalar base + vector offset.
     auto fetch = [&](int32_t j, RowRaw& r) {
         const bool ok = j >= 0 && j <= t32;
-        const int64_t jj = ok ? j : 0;
-        r.k = *reinterpret_cast<const uint4*>(codes + jj * kRowCodes + 16 * g);
-        r.v = *reinterpret_cast<const uint4*>(codes + jj * kRowCodes + 64 + 16 * g);
+        const uint32_t jj = ok ? (uint32_t)j : 0u;
+        const uint32_t off = jj * (uint32_t)kRowCodes + 16u * (uint32_t)g;
+        r.k = *reinterpret_cast<const uint4*>(codes + off);
+        r.v = *reinterpret_cast<const uint4*>(codes + off + 64u);
         uint32_t sk, sv;
-        row_scales<SF>(scl + jj * row_scale_bytes<SF>(), g, sk, sv);
+        row_scales<SF>(scl + jj * (uint32_t)row_scale_bytes<SF>(), g, sk, sv);
         r.sk = ok ? sk : unit_scale_bits<SF>();
         r.sv = ok ? sv : unit_scale_bits<SF>();
     };
     {
-        RowRaw raw[2];
+        // two row buffers, used alternately (the loop is unrolled by two), so
+        // the rows in flight never have to be copied into the decode registers
+        RowRaw ra[2], rb[2];
         int32_t jc[2] = {-1, -1}, jn[2] = {-1, -1};
         int tile = wave;
         if (tile < n_fast) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 jc[u] = sel_of((int64_t)tile * 32 + 2 * n16 + u);
-                fetch(jc[u], raw[u]);
+                fetch(jc[u], ra[u]);
             }
             if (tile + kLW < n_fast) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) jn[u] = sel_of((int64_t)(tile + kLW) * 32 + 2 * n16 + u);
             }
         }
-        for (; tile < n_fast; tile += kLW) {
+        // one tile from cur; the next tile's rows go to nxt
+        auto step = [&](const RowRaw (&cur)[2], RowRaw (&nxt)[2], int tl) {
             const uint64_t vm0 = __ballot(jc[0] >= 0 && jc[0] <= t32) & 0xFFFFull;
             const uint64_t vm1 = __ballot(jc[1] >= 0 && jc[1] <= t32) & 0xFFFFull;
             bf16x8_t kf[2][4];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const uint32_t w[4] = {raw[u].k.x, raw[u].k.y, raw[u].k.z, raw[u].k.w};
+                const uint32_t w[4] = {cur[u].k.x, cur[u].k.y, cur[u].k.z, cur[u].k.w};
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const DqScale sc = dw_scale<SF>(raw[u].sk, kb);
+                    const DqScale sc = dw_scale<SF>(cur[u].sk, kb);
                     kf[u][kb] = as_bf16x8(dq_pair<SF>(w[kb], sc, 0), dq_pair<SF>(w[kb], sc, 1),
                                           dq_pair<SF>(w[kb], sc, 2), dq_pair<SF>(w[kb], sc, 3));
                 }
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {  // V rows of slots 2 n16 + u, dims 32 g .. + 32
-                const uint32_t wv[4] = {raw[u].v.x, raw[u].v.y, raw[u].v.z, raw[u].v.w};
+                const uint32_t wv[4] = {cur[u].v.x, cur[u].v.y, cur[u].v.z, cur[u].v.w};
                 uint32_t d[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    d[i] = dq_pair<SF>(wv[i >> 2], dw_scale<SF>(raw[u].sv, i >> 2), i & 3);
+                    d[i] = dq_pair<SF>(wv[i >> 2], dw_scale<SF>(cur[u].sv, i >> 2), i & 3);
                 vr_store_row(vr, 2 * n16 + u, g, d);
             }
-            const int next = tile + kLW;
+            const int next = tl + kLW;
             if (next < n_fast) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     jc[u] = jn[u];
-                    fetch(jc[u], raw[u]);
+                    fetch(jc[u], nxt[u]);
                 }
                 if (next + kLW < n_fast) {
 #pragma unroll
@@ -700,6 +707,11 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                 }
             }
             consume(kf, vm0, vm1);
+        };
+        for (; tile < n_fast; tile += 2 * kLW) {
+            step(ra, rb, tile);
+            if (tile + kLW >= n_fast) break;
+            step(rb, ra, tile + kLW);
         }
     }
 
