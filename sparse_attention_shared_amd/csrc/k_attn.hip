@@ -455,19 +455,23 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
 // k-step kb is dims 32 g + 8 kb .. + 8 (the Q fragment uses the same map).
 constexpr int kLW = 4;                       // waves per workgroup
 
-// V of one wave's 32 entries, row-major (entry, 128 bf16 dims) on a 72-dword
-// (288-byte) pitch.  The PV product reads it transposed with
+// V of one wave's 32 entries, row-major (128 bf16 dims a row) on a 72-dword
+// (288-byte) pitch, slot s in row 16 (s % 2) + s / 2, so the 8 lanes of one
+// 16-byte store (slots 2 n16 + u) write consecutive rows: 8 rows apart in
+// banks instead of 16.  The PV product reads it transposed with
 // ds_read_b64_tr_b16: within a 16-lane group, lane i receives element i % 4
 // of the 8-byte blocks addressed by lanes 4 k + i / 4 (k = 0..3), so lane
-// (n16, g) addressing row 8 g + 4 h + n16 / 4 at dims 16 t8 + 4 (n16 % 4)
-// receives dim 16 t8 + n16 of rows 8 g + 4 h .. + 3: the V^T operand of
-// the MFMA.  The pitch puts the four rows a group reads on disjoint banks.
+// (n16, g) addressing row 16 h + 4 g + n16 / 4 at dims 16 t8 + 4 (n16 % 4)
+// receives dim 16 t8 + n16 of slots 8 g + 2 k + h (k = 0..3): the V^T
+// operand of the MFMA, whose contraction index then runs over slots 8 g + 0,
+// 2, 4, 6, 1, 3, 5, 7 (the P^T operand follows the same order).  The pitch
+// puts the four rows a group reads on disjoint banks.
 constexpr int kVrRow = 72;
 constexpr int kVrWave = 32 * kVrRow;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void vr_store_row(uint32_t* vr, int slot, int g, const uint32_t (&d)[16]) {
-    uint32_t* row = vr + slot * kVrRow + 16 * g;
+    uint32_t* row = vr + (16 * (slot & 1) + (slot >> 1)) * kVrRow + 16 * g;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
         *reinterpret_cast<uint4*>(row + 4 * c) = make_uint4(d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]);
@@ -475,10 +479,10 @@ __device__ __forceinline__ void vr_store_row(uint32_t* vr, int slot, int g, cons
 
 // The V^T operand of dims 16 t8 .. + 16 (A of O^T += V^T P^T).
 __device__ __forceinline__ bf16x8_t vr_frag(const uint32_t* vr, int t8, int n16, int g) {
-    const uint32_t* p0 = vr + (8 * g + (n16 >> 2)) * kVrRow + 8 * t8 + 2 * (n16 & 3);
+    const uint32_t* p0 = vr + (4 * g + (n16 >> 2)) * kVrRow + 8 * t8 + 2 * (n16 & 3);
     typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
     const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-    const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * kVrRow));
+    const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 16 * kVrRow));
     const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
     return as_bf16x8(ua.x, ua.y, ub.x, ub.y);
 }
@@ -620,10 +624,12 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                 ps += p[u][r];
             }
         l_part += ps;
-        const bf16x8_t pf = as_bf16x8(__builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][0], (__bf16)p[1][0]}),
-                                      __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][1], (__bf16)p[1][1]}),
-                                      __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][2], (__bf16)p[1][2]}),
-                                      __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][3], (__bf16)p[1][3]}));
+        // P^T in the contraction order of vr_frag: slots 8 g + 0, 2, 4, 6 (MFMA
+        // tile 0, rows 4 g .. + 3), then 8 g + 1, 3, 5, 7 (tile 1)
+        const bf16x8_t pf = as_bf16x8(__builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][0], (__bf16)p[0][1]}),
+                                      __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[0][2], (__bf16)p[0][3]}),
+                                      __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[1][0], (__bf16)p[1][1]}),
+                                      __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)p[1][2], (__bf16)p[1][3]}));
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8)
             o[t8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr_frag(vr, t8, n16, g), pf, o[t8], 0, 0, 0);
