@@ -457,16 +457,18 @@ __global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ 
 #pragma unroll
                 for (int i = 0; i < kPfQB; ++i) c[i] = pf_tile(kf[j], qf[i]);
                 const uint32_t tag = (((uint32_t)t0 + 16u * j + 4u * g) << 7) | (uint32_t)n16;
-                // float pre-filter (passes every key >= thr, and NaN): one bit
+                // float pre-filter (passes every finite key >= thr: the largest
+                // of the four scores against the threshold's float): one bit
                 // per query block, then one wave scan places the lane's
                 // passing tiles in the queue
                 uint32_t bits = 0u;
 #pragma unroll
                 for (int i = 0; i < kPfQB; ++i) {
-                    // bitwise, not ||: no short-circuit branches
-                    const uint32_t h = (uint32_t)!(c[i][0] < th[i]) | (uint32_t)!(c[i][1] < th[i]) |
-                                       (uint32_t)!(c[i][2] < th[i]) | (uint32_t)!(c[i][3] < th[i]);
-                    bits |= h << i;
+                    // max3 chains from a canonical value (no canonicalising
+                    // of the MFMA results)
+                    float mx = fmaxf(fmaxf(-__builtin_inff(), c[i][0]), c[i][1]);
+                    mx = fmaxf(fmaxf(mx, c[i][2]), c[i][3]);
+                    bits |= (uint32_t)(mx >= th[i]) << i;
                 }
                 const int mine = __popc(bits);
                 const int incl = wave_scan_dpp(mine);
