@@ -379,18 +379,25 @@ __device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int 
         const int32_t lim = sh.pos[ql];
         const uint32_t thr = sh.thr[ql];
         const uint32_t v[4] = {sc.x, sc.y, sc.z, sc.w};
+        uint32_t key[4], okm = 0u;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const uint32_t key = score_key(__uint_as_float(v[r]));
+            key[r] = score_key(__uint_as_float(v[r]));
+            okm |= (uint32_t)(t0 + r <= lim && key[r] >= thr) << r;
+        }
+        if (okm == 0u) continue;
+        // one list reservation for all of the entry's passing positions
+        const int slot0 = atomicAdd(&sh.n[ql], __popc(okm));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (!((okm >> r) & 1u)) continue;
+            const int slot = slot0 + __popc(okm & ((1u << r) - 1u));
             const int32_t tt = t0 + r;
-            if (tt <= lim && key >= thr) {
-                const int slot = atomicAdd(&sh.n[ql], 1);
-                if (slot < kPfLB) {
-                    sh.buf[ql][slot] = make_uint2((uint32_t)tt, key);
-                } else {  // this workgroup's list of the query is full: straight to its global list
-                    const uint32_t gs = atomicAdd(&cnt[q0 + ql], 1u);
-                    if (gs < (uint32_t)cap) cand[(q0 + ql) * cap + gs] = make_uint2((uint32_t)tt, key);
-                }
+            if (slot < kPfLB) {
+                sh.buf[ql][slot] = make_uint2((uint32_t)tt, key[r]);
+            } else {  // this workgroup's list of the query is full: straight to its global list
+                const uint32_t gs = atomicAdd(&cnt[q0 + ql], 1u);
+                if (gs < (uint32_t)cap) cand[(q0 + ql) * cap + gs] = make_uint2((uint32_t)tt, key[r]);
             }
         }
     }
