@@ -407,8 +407,9 @@ struct WaveSelShared {
 //     exact (tau, need), stopping as soon as a whole sub-bucket completes the
 //     selection;
 //  3. per-wave counts and ballots place every chosen slot, ascending.
-// Writes dst[0..kk), -1 padded.
-template <int NT, int PER>
+// Writes dst[0..kk), -1 padded.  COH: the scores were handed over with
+// agent-coherent stores (read with load_coherent).
+template <int NT, int PER, bool COH = false>
 __device__ void wave_select(const float* s, const int32_t* ids, int n, int kk, int32_t* dst,
                             WaveSelShared<NT>& sh) {
     constexpr int NW = NT / 64;
@@ -417,7 +418,8 @@ __device__ void wave_select(const float* s, const int32_t* ids, int n, int kk, i
     float v[PER];
     int32_t id[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) v[j] = s[min(s0 + 64 * j, n - 1)];
+    for (int j = 0; j < PER; ++j)
+        v[j] = COH ? load_coherent(&s[min(s0 + 64 * j, n - 1)]) : s[min(s0 + 64 * j, n - 1)];
 #pragma unroll
     for (int j = 0; j < PER; ++j) id[j] = ids[min(s0 + 64 * j, n - 1)];
     for (int i = tid; i < kHistWords; i += NT) sh.hist[i] = 0;

@@ -153,6 +153,8 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__
 // on exit) selects the top k of all n_cand <= kSelMaxCand candidates in LDS.
 constexpr int kSelMaxCand = 16384;
 constexpr int kSelNT = 1024;
+constexpr int kSelR = 2;                        // keys per lane group (8 lanes a key)
+constexpr int kSelKeys = (kSelNT / 64) * 8 * kSelR;  // keys scored per workgroup
 
 __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restrict__ k_idx,
                                                          int32_t n_seq, int64_t t_cap, int32_t msh,
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
     const int qi = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane & 7, grp = lane >> 3;
-    const int64_t base = (int64_t)blockIdx.x * (kSelNT / 4) * 4 + wave * 64;
+    const int64_t base = (int64_t)blockIdx.x * kSelKeys + wave * 8 * kSelR;
     float* srow = scores + (int64_t)qi * n_cand;
     const int32_t* crow = cand + (int64_t)qi * n_cand;
     const int32_t seq = q_seq ? q_seq[qi] : qi;
@@ -182,10 +184,10 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
         load_q8(q_idx + (int64_t)qi * kIdxDim + sub * 8, qf);
         const uint4* kb =
             reinterpret_cast<const uint4*>(k_idx) + (int64_t)(seq < 0 ? 0 : seq) * t_cap * 8;
-        uint4 kv[8];
-        bool ok[8];
+        uint4 kv[kSelR];
+        bool ok[kSelR];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
+        for (int r = 0; r < kSelR; ++r) {
             const int64_t c = base + r * 8 + grp;
             const int64_t tok = (c < n_cand) ? crow[c] : -1;
             ok[r] = tok >= 0 && tok <= t;
@@ -193,21 +195,22 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
         }
         float my = -__builtin_inff();
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
+        for (int r = 0; r < kSelR; ++r) {
             const float sc = ok[r] ? sum8(dot8(qf, kv[r])) : -__builtin_inff();
             if (sub == r) my = sc;
         }
         const int64_t c = base + sub * 8 + grp;
-        if (c < n_cand) srow[c] = my;
+        if (sub < kSelR && c < n_cand) store_coherent(&srow[c], my);
     }
-    __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (threadIdx.x == 0) last = arrive_last(&ctr[qi * kCtrStride], gridDim.x);
-    __syncthreads();  // thread 0's acquire covers the workgroup
+    hand_off_wait();  // this thread's score stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) last = arrive_last_coherent(&ctr[qi * kCtrStride], gridDim.x);
+    __syncthreads();
     if (!last) return;
     if (n_cand <= kSelNT * 8)  // every wave holds keys
-        wave_select<kSelNT, 8>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
+        wave_select<kSelNT, 8, true>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
     else
-        wave_select<kSelNT, kSelMaxCand / kSelNT>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
+        wave_select<kSelNT, kSelMaxCand / kSelNT, true>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
     if (threadIdx.x == 0) ctr[qi * kCtrStride] = 0u;
 }
 
@@ -217,7 +220,7 @@ hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const 
                                int32_t* sel, hipStream_t s) {
     if (nq == 0 || n_cand == 0) return hipSuccess;
     if (n_cand > kSelMaxCand) return hipErrorInvalidValue;
-    dim3 grid((uint32_t)((n_cand + kSelNT - 1) / kSelNT), (uint32_t)nq);
+    dim3 grid((uint32_t)((n_cand + kSelKeys - 1) / kSelKeys), (uint32_t)nq);
     hipLaunchKernelGGL(k_score_select, grid, dim3(kSelNT), 0, s, c.k_idx, c.n_seq, c.t_cap, c.msh,
                        q_idx, q_pos, q_seq, cand, n_cand, scores, ctr, k, sel);
     return hipGetLastError();
