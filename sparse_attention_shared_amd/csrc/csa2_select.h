@@ -410,7 +410,7 @@ struct WaveSelShared {
 // Writes dst[0..kk), -1 padded.  COH: the scores were handed over with
 // agent-coherent stores (read with load_coherent).
 template <int NT, int PER, bool COH = false>
-__device__ void wave_select(const float* s, const int32_t* ids, int n, int kk, int32_t* dst,
+__device__ __forceinline__ void wave_select(const float* s, const int32_t* ids, int n, int kk, int32_t* dst,
                             WaveSelShared<NT>& sh) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;

@@ -148,14 +148,21 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__
 // Candidate scoring fused with the selection among the candidates, for the
 // Reindex layers (rescore the Full layer's pool with the layer's own indexer
 // query and keep the top k, "What Full, Reindex, and Reuse Share", Fig. 5).
-// grid: (ceil(n_cand / kSelNT), nq).  Every workgroup scores kSelNT candidates into
-// `scores`; the last one of a query to finish (per-query counter `ctr`, reset
-// on exit) selects the top k of all n_cand <= kSelMaxCand candidates in LDS.
+// grid: (ceil(n_cand / sel_keys<R>()), nq).  Every workgroup scores
+// sel_keys<R>() candidates into `scores` (handed over with agent-coherent
+// stores); the last one of a query to finish (per-query counter `ctr`, reset on
+// exit) selects the top k of all n_cand <= kSelMaxCand candidates.
 constexpr int kSelMaxCand = 16384;
 constexpr int kSelNT = 1024;
-constexpr int kSelR = 2;                        // keys per lane group (8 lanes a key)
-constexpr int kSelKeys = (kSelNT / 64) * 8 * kSelR;  // keys scored per workgroup
 
+// A workgroup scores (kSelNT / 64) * 8 * R candidates (R per lane group of 8
+// lanes, one 128-byte key each): R = 8 when the queries alone give enough
+// workgroups to fill the GPU, R = 2 for a handful of queries (decode), where
+// spreading the gather over 4x the workgroups shortens it.
+template <int R>
+constexpr int sel_keys() { return (kSelNT / 64) * 8 * R; }
+
+template <int R>
 __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restrict__ k_idx,
                                                          int32_t n_seq, int64_t t_cap, int32_t msh,
                                                          const uint16_t* __restrict__ q_idx,
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
     const int qi = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane & 7, grp = lane >> 3;
-    const int64_t base = (int64_t)blockIdx.x * kSelKeys + wave * 8 * kSelR;
+    const int64_t base = (int64_t)blockIdx.x * sel_keys<R>() + wave * 8 * R;
     float* srow = scores + (int64_t)qi * n_cand;
     const int32_t* crow = cand + (int64_t)qi * n_cand;
     const int32_t seq = q_seq ? q_seq[qi] : qi;
@@ -184,10 +191,10 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
         load_q8(q_idx + (int64_t)qi * kIdxDim + sub * 8, qf);
         const uint4* kb =
             reinterpret_cast<const uint4*>(k_idx) + (int64_t)(seq < 0 ? 0 : seq) * t_cap * 8;
-        uint4 kv[kSelR];
-        bool ok[kSelR];
+        uint4 kv[R];
+        bool ok[R];
 #pragma unroll
-        for (int r = 0; r < kSelR; ++r) {
+        for (int r = 0; r < R; ++r) {
             const int64_t c = base + r * 8 + grp;
             const int64_t tok = (c < n_cand) ? crow[c] : -1;
             ok[r] = tok >= 0 && tok <= t;
@@ -195,12 +202,12 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
         }
         float my = -__builtin_inff();
 #pragma unroll
-        for (int r = 0; r < kSelR; ++r) {
+        for (int r = 0; r < R; ++r) {
             const float sc = ok[r] ? sum8(dot8(qf, kv[r])) : -__builtin_inff();
             if (sub == r) my = sc;
         }
         const int64_t c = base + sub * 8 + grp;
-        if (sub < kSelR && c < n_cand) store_coherent(&srow[c], my);
+        if (sub < R && c < n_cand) store_coherent(&srow[c], my);
     }
     hand_off_wait();  // this thread's score stores are complete
     __syncthreads();
@@ -220,9 +227,17 @@ hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const 
                                int32_t* sel, hipStream_t s) {
     if (nq == 0 || n_cand == 0) return hipSuccess;
     if (n_cand > kSelMaxCand) return hipErrorInvalidValue;
-    dim3 grid((uint32_t)((n_cand + kSelKeys - 1) / kSelKeys), (uint32_t)nq);
-    hipLaunchKernelGGL(k_score_select, grid, dim3(kSelNT), 0, s, c.k_idx, c.n_seq, c.t_cap, c.msh,
-                       q_idx, q_pos, q_seq, cand, n_cand, scores, ctr, k, sel);
+    const int64_t wide = (n_cand + sel_keys<8>() - 1) / sel_keys<8>();
+    if (wide * nq >= 256) {  // the queries fill the GPU
+        hipLaunchKernelGGL(k_score_select<8>, dim3((uint32_t)wide, (uint32_t)nq), dim3(kSelNT), 0, s,
+                           c.k_idx, c.n_seq, c.t_cap, c.msh, q_idx, q_pos, q_seq, cand, n_cand,
+                           scores, ctr, k, sel);
+    } else {
+        const int64_t nb = (n_cand + sel_keys<2>() - 1) / sel_keys<2>();
+        hipLaunchKernelGGL(k_score_select<2>, dim3((uint32_t)nb, (uint32_t)nq), dim3(kSelNT), 0, s,
+                           c.k_idx, c.n_seq, c.t_cap, c.msh, q_idx, q_pos, q_seq, cand, n_cand,
+                           scores, ctr, k, sel);
+    }
     return hipGetLastError();
 }
 
