@@ -158,11 +158,13 @@ __device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t n) {
 // side.  Each cache line of the handed-over data is written by one workgroup.
 // Over 16-64 workgroups per group the arrival costs far less than the
 // acquire-release one (0.3 vs 1.8 us at 32).
-__device__ __forceinline__ void store_coherent(float* p, float v) {
+template <typename T>
+__device__ __forceinline__ void store_coherent(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float load_coherent(const float* p) {
+template <typename T>
+__device__ __forceinline__ T load_coherent(const T* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -105,9 +105,12 @@ __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__
         const int v = hist[hidx(i)];
         if (v) atomicAdd(&st->hist[i], (uint32_t)v);
     }
-    __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (tid == 0) last = arrive_last(&st->ctr_hist, (uint32_t)nc);
-    __syncthreads();  // thread 0's acquire covers the workgroup
+    // the row histogram is built and read by device atomics alone, so the
+    // arrival needs no release or acquire: only this thread's adds complete
+    hand_off_wait();
+    __syncthreads();
+    if (tid == 0) last = arrive_last_coherent(&st->ctr_hist, (uint32_t)nc);
+    __syncthreads();
     if (!last) return;
     // the last workgroup of the row: boundary bucket of each target
     {
@@ -160,7 +163,14 @@ struct KeepLds {
     int last;
 };
 
-// grid (n_chunk, nq)
+// grid (n_chunk, nq).  COH: the kept keys and counts reach the row's last
+// workgroup through agent-coherent accesses and a relaxed arrival (no L2
+// write-back or invalidate); else through plain stores and an acquire-release
+// arrival.  The first pays when many rows fill the GPU (a prefill chunk or a
+// replayed segment: 1.063 -> 0.999 ms for 128 rows of 131072 over 20 layers),
+// the second for a handful of rows (decode), whose last workgroups read their
+// kept keys faster with plain loads after the invalidate.
+template <bool COH>
 __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__ scores, int64_t n,
                                                        int64_t ld, const int32_t* __restrict__ ids,
                                                        int32_t k, int32_t* __restrict__ out,
@@ -215,21 +225,32 @@ __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__
     for (int u = 0; u < 8; ++u) mine += kk8[u] >= low;  // key 0 (past len too) is below low
     int tot;
     int pos = block_excl_scan<kLongNT>(mine, sh.tmp, &tot);
-    Cand* reg = ws.keep + ((int64_t)row * nc + c) * kChunk;
+    // kept keys (a key and its value as one 8-byte word) and counts
+    uint64_t* reg = reinterpret_cast<uint64_t*>(ws.keep + ((int64_t)row * nc + c) * kChunk);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-        if (kk8[u] >= low) reg[pos++] = Cand{kk8[u], sh.u.c.val[8 * tid + u]};
-    if (tid == 0) ws.nkeep[row * nc + c] = tot;
-    __syncthreads();  // the workgroup's stores are ordered before thread 0's release
-    if (tid == 0) sh.last = arrive_last(&st->ctr_keep, (uint32_t)nc);
-    __syncthreads();  // thread 0's acquire covers the workgroup
+        if (kk8[u] >= low) {
+            const uint64_t w = (uint64_t)kk8[u] | ((uint64_t)(uint32_t)sh.u.c.val[8 * tid + u] << 32);
+            if (COH) store_coherent(reg + pos++, w);
+            else reg[pos++] = w;
+        }
+    if (tid == 0) {
+        if (COH) store_coherent(ws.nkeep + row * nc + c, tot);
+        else ws.nkeep[row * nc + c] = tot;
+    }
+    if (COH) hand_off_wait();
+    __syncthreads();
+    if (tid == 0)
+        sh.last = COH ? arrive_last_coherent(&st->ctr_keep, (uint32_t)nc) : arrive_last(&st->ctr_keep, (uint32_t)nc);
+    __syncthreads();
     if (!sh.last) return;
 
     // ---- the last workgroup of the row: chunk offsets of the kept keys
     {
         const int c0 = 2 * tid;  // nc <= 2048: two chunks per thread
-        const int a = c0 < nc ? ws.nkeep[row * nc + c0] : 0;
-        const int b = c0 + 1 < nc ? ws.nkeep[row * nc + c0 + 1] : 0;
+        const int32_t* nk = ws.nkeep + row * nc;
+        const int a = c0 < nc ? (COH ? load_coherent(nk + c0) : nk[c0]) : 0;
+        const int b = c0 + 1 < nc ? (COH ? load_coherent(nk + c0 + 1) : nk[c0 + 1]) : 0;
         int all;
         const int pre = block_excl_scan<kLongNT>(a + b, sh.tmp, &all);
         if (c0 < nc) sh.koff[c0] = pre;
@@ -240,14 +261,16 @@ __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__
     const int m = sh.koff[nc];
     const Cand* kb = ws.keep + (int64_t)row * nc * kChunk;
     // kept key i of the row: chunk = the last one whose offset is <= i
-    auto at = [&](int64_t i) -> const Cand* {
+    auto at = [&](int64_t i) -> Cand {
         int lo = 0, hi = nc - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (sh.koff[mid] <= i) lo = mid;
             else hi = mid - 1;
         }
-        return kb + (int64_t)lo * kChunk + (i - sh.koff[lo]);
+        const uint64_t* p = reinterpret_cast<const uint64_t*>(kb + (int64_t)lo * kChunk + (i - sh.koff[lo]));
+        const uint64_t w = COH ? load_coherent(p) : *p;
+        return Cand{(uint32_t)w, (int32_t)(uint32_t)(w >> 32)};
     };
     if (m <= kStage) {
         // thread t holds kept keys [E t, E t + E) of the row in registers
@@ -280,7 +303,11 @@ __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__
         }
         Cand e[kE];
 #pragma unroll
-        for (int u = 0; u < kE; ++u) e[u] = kb[addr[u]];  // every load issued before any use
+        for (int u = 0; u < kE; ++u) {  // every load issued before any use
+            const uint64_t* p = reinterpret_cast<const uint64_t*>(kb + addr[u]);
+            const uint64_t w = COH ? load_coherent(p) : *p;
+            e[u] = Cand{(uint32_t)w, (int32_t)(uint32_t)(w >> 32)};
+        }
         uint32_t key[kE];
 #pragma unroll
         for (int u = 0; u < kE; ++u) key[u] = (u < E && i0 + u < m) ? e[u].key : 0u;
@@ -365,8 +392,8 @@ __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__
         }
     } else {
         // a row with many keys tied around the boundary: read them in place
-        auto K = [&](int64_t i) { return at(i)->key; };
-        auto V = [&](int64_t i) { return at(i)->val; };
+        auto K = [&](int64_t i) { return at(i).key; };
+        auto V = [&](int64_t i) { return at(i).val; };
         for (int t = 0; t < nt; ++t) {
             const int32_t kk = t ? k2 : k;
             int32_t* dst = t ? out2 + row * k2 : out + row * k;
@@ -412,8 +439,12 @@ hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, c
     const int32_t kk2 = out2 ? k2 : 0;
     dim3 grid((uint32_t)nc, (uint32_t)nq);
     hipLaunchKernelGGL(k_topk_hist, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, kk2, w);
-    hipLaunchKernelGGL(k_topk_keep, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
-                       out2, w);
+    if ((int64_t)nc * nq >= 256)  // the rows fill the GPU
+        hipLaunchKernelGGL(k_topk_keep<true>, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
+                           out2, w);
+    else
+        hipLaunchKernelGGL(k_topk_keep<false>, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
+                           out2, w);
     return hipGetLastError();
 }
 
