@@ -163,21 +163,24 @@ struct KeepLds {
     int last;
 };
 
-// grid (n_chunk, nq).  COH: the kept keys and counts reach the row's last
-// workgroup through agent-coherent accesses and a relaxed arrival (no L2
-// write-back or invalidate); else through plain stores and an acquire-release
-// arrival.  The first pays when many rows fill the GPU (a prefill chunk or a
-// replayed segment: 1.063 -> 0.999 ms for 128 rows of 131072 over 20 layers),
-// the second for a handful of rows (decode), whose last workgroups read their
-// kept keys faster with plain loads after the invalidate.
-template <bool COH>
+// MODE 0, grid (n_chunk, nq): every workgroup compacts its chunk and the last
+// one of a row to finish (acquire-release arrival) resolves the row.  For a
+// handful of rows (decode).
+// MODE 1, grid (n_chunk, nq): the chunks alone; MODE 2, grid (1, nq), launched
+// after it: one workgroup per row resolves it.  For many rows (a replayed
+// segment, a prefill chunk): with the rows' resolution left to whichever
+// workgroup arrives last, an XCD that falls behind receives the late arrivals
+// and with them the 13 us resolutions, so it falls further behind (128 rows of
+// 131072: one XCD still starting chunk workgroups at 150 us while the other
+// seven were done by 60 us); a launch of its own deals them out evenly.
+template <int MODE>
 __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__ scores, int64_t n,
                                                        int64_t ld, const int32_t* __restrict__ ids,
                                                        int32_t k, int32_t* __restrict__ out,
                                                        int32_t k2, int32_t* __restrict__ out2,
                                                        LongWs ws) {
     __shared__ KeepLds sh;
-    const int c = blockIdx.x, nc = gridDim.x;
+    const int c = blockIdx.x, nc = (int)((n + kChunk - 1) / kChunk);
     const int64_t row = blockIdx.y;
     const int tid = threadIdx.x;
     const float* s = scores + row * ld;
@@ -192,65 +195,60 @@ __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__
         rem[t] = st->rem[t];
         low = min(low, rem[t] < 0 ? 1u : bucket[t] << 20);
     }
-    // ---- the chunk: stage keys and output values (loads all issued first)
-    const int64_t b0 = chunk_begin(c);
-    const int len = (int)min((int64_t)kChunk, n - b0);
-    {
-        constexpr int kPer = kChunk / kLongNT;
-        float v[kPer];
-        int32_t id[kPer];
+    if (MODE != 2) {
+        // ---- the chunk: stage keys and output values (loads all issued first)
+        const int64_t b0 = chunk_begin(c);
+        const int len = (int)min((int64_t)kChunk, n - b0);
+        {
+            constexpr int kPer = kChunk / kLongNT;
+            float v[kPer];
+            int32_t id[kPer];
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) v[u] = s[b0 + min(tid + u * kLongNT, len - 1)];
+            for (int u = 0; u < kPer; ++u) v[u] = s[b0 + min(tid + u * kLongNT, len - 1)];
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) id[u] = irow ? irow[b0 + min(tid + u * kLongNT, len - 1)] : 0;
+            for (int u = 0; u < kPer; ++u) id[u] = irow ? irow[b0 + min(tid + u * kLongNT, len - 1)] : 0;
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int i = tid + u * kLongNT;
-            const uint32_t key = score_key(v[u]);
-            sh.u.c.key[i] = (i < len && id[u] >= 0 && key != kNegInfKey) ? key : 0u;
-            sh.u.c.val[i] = irow ? id[u] : (int32_t)(b0 + i);
+            for (int u = 0; u < kPer; ++u) {
+                const int i = tid + u * kLongNT;
+                const uint32_t key = score_key(v[u]);
+                sh.u.c.key[i] = (i < len && id[u] >= 0 && key != kNegInfKey) ? key : 0u;
+                sh.u.c.val[i] = irow ? id[u] : (int32_t)(b0 + i);
+            }
         }
-    }
-    __syncthreads();
-    // thread t owns slots 8 t .. 8 t + 7: kept ones go to the chunk's region in order
-    uint32_t kk8[8];
-    {
-        const uint4 a = *reinterpret_cast<const uint4*>(&sh.u.c.key[8 * tid]);
-        const uint4 b = *reinterpret_cast<const uint4*>(&sh.u.c.key[8 * tid + 4]);
-        kk8[0] = a.x; kk8[1] = a.y; kk8[2] = a.z; kk8[3] = a.w;
-        kk8[4] = b.x; kk8[5] = b.y; kk8[6] = b.z; kk8[7] = b.w;
-    }
-    int mine = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) mine += kk8[u] >= low;  // key 0 (past len too) is below low
-    int tot;
-    int pos = block_excl_scan<kLongNT>(mine, sh.tmp, &tot);
-    // kept keys (a key and its value as one 8-byte word) and counts
-    uint64_t* reg = reinterpret_cast<uint64_t*>(ws.keep + ((int64_t)row * nc + c) * kChunk);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-        if (kk8[u] >= low) {
-            const uint64_t w = (uint64_t)kk8[u] | ((uint64_t)(uint32_t)sh.u.c.val[8 * tid + u] << 32);
-            if (COH) store_coherent(reg + pos++, w);
-            else reg[pos++] = w;
+        __syncthreads();
+        // thread t owns slots 8 t .. 8 t + 7: kept ones go to the chunk's region in order
+        uint32_t kk8[8];
+        {
+            const uint4 a = *reinterpret_cast<const uint4*>(&sh.u.c.key[8 * tid]);
+            const uint4 b = *reinterpret_cast<const uint4*>(&sh.u.c.key[8 * tid + 4]);
+            kk8[0] = a.x; kk8[1] = a.y; kk8[2] = a.z; kk8[3] = a.w;
+            kk8[4] = b.x; kk8[5] = b.y; kk8[6] = b.z; kk8[7] = b.w;
         }
-    if (tid == 0) {
-        if (COH) store_coherent(ws.nkeep + row * nc + c, tot);
-        else ws.nkeep[row * nc + c] = tot;
+        int mine = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mine += kk8[u] >= low;  // key 0 (past len too) is below low
+        int tot;
+        int pos = block_excl_scan<kLongNT>(mine, sh.tmp, &tot);
+        // kept keys (a key and its value as one 8-byte word) and counts
+        uint64_t* reg = reinterpret_cast<uint64_t*>(ws.keep + ((int64_t)row * nc + c) * kChunk);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (kk8[u] >= low)
+                reg[pos++] = (uint64_t)kk8[u] | ((uint64_t)(uint32_t)sh.u.c.val[8 * tid + u] << 32);
+        if (tid == 0) ws.nkeep[row * nc + c] = tot;
+        if (MODE == 1) return;
+        __syncthreads();  // the workgroup's stores are ordered before thread 0's release
+        if (tid == 0) sh.last = arrive_last(&st->ctr_keep, (uint32_t)nc);
+        __syncthreads();  // thread 0's acquire covers the workgroup
+        if (!sh.last) return;
     }
-    if (COH) hand_off_wait();
-    __syncthreads();
-    if (tid == 0)
-        sh.last = COH ? arrive_last_coherent(&st->ctr_keep, (uint32_t)nc) : arrive_last(&st->ctr_keep, (uint32_t)nc);
-    __syncthreads();
-    if (!sh.last) return;
 
     // ---- the last workgroup of the row: chunk offsets of the kept keys
     {
         const int c0 = 2 * tid;  // nc <= 2048: two chunks per thread
         const int32_t* nk = ws.nkeep + row * nc;
-        const int a = c0 < nc ? (COH ? load_coherent(nk + c0) : nk[c0]) : 0;
-        const int b = c0 + 1 < nc ? (COH ? load_coherent(nk + c0 + 1) : nk[c0 + 1]) : 0;
+        const int a = c0 < nc ? nk[c0] : 0;
+        const int b = c0 + 1 < nc ? nk[c0 + 1] : 0;
         int all;
         const int pre = block_excl_scan<kLongNT>(a + b, sh.tmp, &all);
         if (c0 < nc) sh.koff[c0] = pre;
@@ -268,8 +266,7 @@ __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__
             if (sh.koff[mid] <= i) lo = mid;
             else hi = mid - 1;
         }
-        const uint64_t* p = reinterpret_cast<const uint64_t*>(kb + (int64_t)lo * kChunk + (i - sh.koff[lo]));
-        const uint64_t w = COH ? load_coherent(p) : *p;
+        const uint64_t w = *reinterpret_cast<const uint64_t*>(kb + (int64_t)lo * kChunk + (i - sh.koff[lo]));
         return Cand{(uint32_t)w, (int32_t)(uint32_t)(w >> 32)};
     };
     if (m <= kStage) {
@@ -304,8 +301,7 @@ __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__
         Cand e[kE];
 #pragma unroll
         for (int u = 0; u < kE; ++u) {  // every load issued before any use
-            const uint64_t* p = reinterpret_cast<const uint64_t*>(kb + addr[u]);
-            const uint64_t w = COH ? load_coherent(p) : *p;
+            const uint64_t w = *reinterpret_cast<const uint64_t*>(kb + addr[u]);
             e[u] = Cand{(uint32_t)w, (int32_t)(uint32_t)(w >> 32)};
         }
         uint32_t key[kE];
@@ -439,12 +435,15 @@ hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, c
     const int32_t kk2 = out2 ? k2 : 0;
     dim3 grid((uint32_t)nc, (uint32_t)nq);
     hipLaunchKernelGGL(k_topk_hist, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, kk2, w);
-    if ((int64_t)nc * nq >= 256)  // the rows fill the GPU
-        hipLaunchKernelGGL(k_topk_keep<true>, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
+    if ((int64_t)nc * nq >= 256) {  // the rows fill the GPU
+        hipLaunchKernelGGL(k_topk_keep<1>, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
                            out2, w);
-    else
-        hipLaunchKernelGGL(k_topk_keep<false>, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
+        hipLaunchKernelGGL(k_topk_keep<2>, dim3(1u, (uint32_t)nq), dim3(kLongNT), 0, s, scores, n, ld, ids, k,
+                           out, kk2, out2, w);
+    } else {
+        hipLaunchKernelGGL(k_topk_keep<0>, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
                            out2, w);
+    }
     return hipGetLastError();
 }
 
