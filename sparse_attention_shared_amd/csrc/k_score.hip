@@ -148,10 +148,15 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__
 // Candidate scoring fused with the selection among the candidates, for the
 // Reindex layers (rescore the Full layer's pool with the layer's own indexer
 // query and keep the top k, "What Full, Reindex, and Reuse Share", Fig. 5).
-// grid: (ceil(n_cand / sel_keys<R>()), nq).  Every workgroup scores
+// MODE 0, grid (ceil(n_cand / sel_keys<R>()), nq): every workgroup scores
 // sel_keys<R>() candidates into `scores` (handed over with agent-coherent
 // stores); the last one of a query to finish (per-query counter `ctr`, reset on
-// exit) selects the top k of all n_cand <= kSelMaxCand candidates.
+// exit) selects the top k of all n_cand <= kSelMaxCand candidates.  For a
+// handful of queries (decode).
+// MODE 1, same grid: the scores alone (plain stores); MODE 2, grid (1, nq),
+// launched after it: one workgroup per query selects.  For many queries, where
+// leaving the selections to the last arrivals would pile them onto whichever
+// XCD falls behind (as in the long-row top-k).
 constexpr int kSelMaxCand = 16384;
 constexpr int kSelNT = 1024;
 
@@ -162,7 +167,7 @@ constexpr int kSelNT = 1024;
 template <int R>
 constexpr int sel_keys() { return (kSelNT / 64) * 8 * R; }
 
-template <int R>
+template <int R, int MODE>
 __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restrict__ k_idx,
                                                          int32_t n_seq, int64_t t_cap, int32_t msh,
                                                          const uint16_t* __restrict__ q_idx,
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
     int64_t t = (((int64_t)q_pos[qi] + 1) >> msh) - 1;
     if (seq < 0 || seq >= n_seq) t = -1;
     if (t >= t_cap) t = t_cap - 1;
-    if (base < n_cand) {
+    if (MODE != 2 && base < n_cand) {
         float qf[8];
         load_q8(q_idx + (int64_t)qi * kIdxDim + sub * 8, qf);
         const uint4* kb =
@@ -207,18 +212,24 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
             if (sub == r) my = sc;
         }
         const int64_t c = base + sub * 8 + grp;
-        if (sub < R && c < n_cand) store_coherent(&srow[c], my);
+        if (sub < R && c < n_cand) {
+            if (MODE == 0) store_coherent(&srow[c], my);
+            else srow[c] = my;
+        }
     }
-    hand_off_wait();  // this thread's score stores are complete
-    __syncthreads();
-    if (threadIdx.x == 0) last = arrive_last_coherent(&ctr[qi * kCtrStride], gridDim.x);
-    __syncthreads();
-    if (!last) return;
+    if (MODE == 1) return;
+    if (MODE == 0) {
+        hand_off_wait();  // this thread's score stores are complete
+        __syncthreads();
+        if (threadIdx.x == 0) last = arrive_last_coherent(&ctr[qi * kCtrStride], gridDim.x);
+        __syncthreads();
+        if (!last) return;
+    }
     if (n_cand <= kSelNT * 8)  // every wave holds keys
-        wave_select<kSelNT, 8, true>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
+        wave_select<kSelNT, 8, MODE == 0>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
     else
-        wave_select<kSelNT, kSelMaxCand / kSelNT, true>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
-    if (threadIdx.x == 0) ctr[qi * kCtrStride] = 0u;
+        wave_select<kSelNT, kSelMaxCand / kSelNT, MODE == 0>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
+    if (MODE == 0 && threadIdx.x == 0) ctr[qi * kCtrStride] = 0u;
 }
 
 hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
@@ -229,12 +240,15 @@ hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const 
     if (n_cand > kSelMaxCand) return hipErrorInvalidValue;
     const int64_t wide = (n_cand + sel_keys<8>() - 1) / sel_keys<8>();
     if (wide * nq >= 256) {  // the queries fill the GPU
-        hipLaunchKernelGGL(k_score_select<8>, dim3((uint32_t)wide, (uint32_t)nq), dim3(kSelNT), 0, s,
+        hipLaunchKernelGGL((k_score_select<8, 1>), dim3((uint32_t)wide, (uint32_t)nq), dim3(kSelNT), 0, s,
+                           c.k_idx, c.n_seq, c.t_cap, c.msh, q_idx, q_pos, q_seq, cand, n_cand,
+                           scores, ctr, k, sel);
+        hipLaunchKernelGGL((k_score_select<8, 2>), dim3(1u, (uint32_t)nq), dim3(kSelNT), 0, s,
                            c.k_idx, c.n_seq, c.t_cap, c.msh, q_idx, q_pos, q_seq, cand, n_cand,
                            scores, ctr, k, sel);
     } else {
         const int64_t nb = (n_cand + sel_keys<2>() - 1) / sel_keys<2>();
-        hipLaunchKernelGGL(k_score_select<2>, dim3((uint32_t)nb, (uint32_t)nq), dim3(kSelNT), 0, s,
+        hipLaunchKernelGGL((k_score_select<2, 0>), dim3((uint32_t)nb, (uint32_t)nq), dim3(kSelNT), 0, s,
                            c.k_idx, c.n_seq, c.t_cap, c.msh, q_idx, q_pos, q_seq, cand, n_cand,
                            scores, ctr, k, sel);
     }
