@@ -453,7 +453,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_chunk(CacheView c, const uint
 // dim and writes V^T with one dword per dim.  Lane group g loads dims
 // 32 g .. 32 g + 31 of K and of V (one scale block each).  The K fragment of
 // k-step kb is dims 32 g + 8 kb .. + 8 (the Q fragment uses the same map).
-constexpr int kLW = 4;                       // waves per workgroup
+constexpr int kLW = 4;                       // waves per workgroup (many queries)
+constexpr int kLWFew = 8;                    // fewer queries than CUs: 8 waves share a query
 
 // V of one wave's 32 entries, row-major (128 bf16 dims a row) on a 72-dword
 // (288-byte) pitch, slot s in row 16 (s % 2) + s / 2, so the 8 lanes of one
@@ -487,24 +488,26 @@ __device__ __forceinline__ bf16x8_t vr_frag(const uint32_t* vr, int t8, int n16,
     return as_bf16x8(ua.x, ua.y, ub.x, ub.y);
 }
 
+template <int LW>
 struct LoopLds {
     union {
-        uint32_t vr[kLW][kVrWave];
-        float obuf[kLW][kHeads][kHeadDim + 4];
+        uint32_t vr[LW][kVrWave];
+        float obuf[LW][kHeads][kHeadDim + 4];
     } u;
-    float m[kLW][kHeads];
-    float l[kLW][kHeads];
+    float m[LW][kHeads];
+    float l[LW][kHeads];
 };
 
-// grid nq, kLW * 64 threads.
-template <int SF>
-__global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint16_t* __restrict__ q,
+// grid nq, LW * 64 threads (LW = 4, or 8 when the queries are fewer than
+// the CUs, so that each CU runs two waves per SIMD instead of one).
+template <int SF, int LW>
+__global__ __launch_bounds__(LW * 64) void k_attn_loop(CacheView c, const uint16_t* __restrict__ q,
                                                         const int32_t* __restrict__ q_pos,
                                                         const int32_t* __restrict__ q_seq,
                                                         const int32_t* __restrict__ sel, int32_t k,
                                                         LocalView loc, float sm_scale,
                                                         uint16_t* __restrict__ out) {
-    __shared__ LoopLds sh;
+    __shared__ LoopLds<LW> sh;
     const int qi = blockIdx.x, tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n16 = lane & 15, g = lane >> 4;
@@ -671,9 +674,9 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                 jc[u] = sel_of((int64_t)tile * 32 + 2 * n16 + u);
                 fetch(jc[u], ra[u]);
             }
-            if (tile + kLW < n_fast) {
+            if (tile + LW < n_fast) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) jn[u] = sel_of((int64_t)(tile + kLW) * 32 + 2 * n16 + u);
+                for (int u = 0; u < 2; ++u) jn[u] = sel_of((int64_t)(tile + LW) * 32 + 2 * n16 + u);
             }
         }
         // one tile from cur; the next tile's rows go to nxt
@@ -700,30 +703,30 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
                     d[i] = dq_pair<SF>(wv[i >> 2], dw_scale<SF>(cur[u].sv, i >> 2), i & 3);
                 vr_store_row(vr, 2 * n16 + u, g, d);
             }
-            const int next = tl + kLW;
+            const int next = tl + LW;
             if (next < n_fast) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     jc[u] = jn[u];
                     fetch(jc[u], nxt[u]);
                 }
-                if (next + kLW < n_fast) {
+                if (next + LW < n_fast) {
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) jn[u] = sel_of((int64_t)(next + kLW) * 32 + 2 * n16 + u);
+                    for (int u = 0; u < 2; ++u) jn[u] = sel_of((int64_t)(next + LW) * 32 + 2 * n16 + u);
                 }
             }
             consume(kf, vm0, vm1);
         };
-        for (; tile < n_fast; tile += 2 * kLW) {
+        for (; tile < n_fast; tile += 2 * LW) {
             step(ra, rb, tile);
-            if (tile + kLW >= n_fast) break;
-            step(rb, ra, tile + kLW);
+            if (tile + LW >= n_fast) break;
+            step(rb, ra, tile + LW);
         }
     }
 
     // ---- the other tiles (window rows, a bf16 cache, a tile across the end of
     // the selection): rows loaded when the tile starts
-    for (int tile = n_fast + wave; tile < n_tiles; tile += kLW) {
+    for (int tile = n_fast + wave; tile < n_tiles; tile += LW) {
         int kind[2];
         int64_t row[2];
 #pragma unroll
@@ -809,26 +812,31 @@ __global__ __launch_bounds__(kLW * 64) void k_attn_loop(CacheView c, const uint1
         *reinterpret_cast<float4*>(&sh.u.obuf[wave][n16][16 * t8 + 4 * g]) =
             make_float4(o[t8][0], o[t8][1], o[t8][2], o[t8][3]);
     __syncthreads();
-    const int h = tid >> 4, d0 = (tid & 15) * 8;  // 256 threads: head h, 8 dims
+    constexpr int tph = LW * 64 / kHeads;  // threads per head
+    constexpr int dpt = kHeadDim / tph;    // dims per thread: 8 (LW 4) or 4 (LW 8)
+    const int h = tid / tph, d0 = (tid % tph) * dpt;
     float M = NEG;
 #pragma unroll
-    for (int w = 0; w < kLW; ++w) M = fmaxf(M, sh.m[w][h]);
-    float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < LW; ++w) M = fmaxf(M, sh.m[w][h]);
+    float L = 0.f, acc[dpt];
+#pragma unroll
+    for (int i = 0; i < dpt; ++i) acc[i] = 0.f;
     if (M != NEG) {
 #pragma unroll
-        for (int w = 0; w < kLW; ++w) {
+        for (int w = 0; w < LW; ++w) {
             const float mw = sh.m[w][h];
             const float f = (mw == NEG) ? 0.f : exp2f(mw - M);
             L = fmaf(sh.l[w][h], f, L);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(sh.u.obuf[w][h][d0 + i], f, acc[i]);
+            for (int i = 0; i < dpt; ++i) acc[i] = fmaf(sh.u.obuf[w][h][d0 + i], f, acc[i]);
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint16_t* orow = out + ((int64_t)qi * kHeads + h) * kHeadDim + d0;
-    *reinterpret_cast<uint4*>(orow) =
-        make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                   pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
+#pragma unroll
+    for (int i = 0; i < dpt; i += 4)
+        *reinterpret_cast<uint2*>(orow + i) =
+            make_uint2(pack_bf16x2(acc[i] * inv, acc[i + 1] * inv), pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv));
 }
 
 // Chunks of a query: 256 selected entries each, and enough of them that the
@@ -849,11 +857,18 @@ hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32
                               hipStream_t s) {
     if (nq == 0) return hipSuccess;
     if (nq >= kManyQueries) {  // enough queries to fill the GPU one workgroup each
-        if (c.fp4 == 2)
-            hipLaunchKernelGGL(k_attn_loop<1>, dim3((uint32_t)nq), dim3(kLW * 64), 0, s, c, q, q_pos,
+        const bool few = nq < 256;  // fewer queries than CUs
+        if (c.fp4 == 2 && few)
+            hipLaunchKernelGGL((k_attn_loop<1, kLWFew>), dim3((uint32_t)nq), dim3(kLWFew * 64), 0, s, c, q,
+                               q_pos, q_seq, sel, k, loc, sm_scale, out);
+        else if (c.fp4 == 2)
+            hipLaunchKernelGGL((k_attn_loop<1, kLW>), dim3((uint32_t)nq), dim3(kLW * 64), 0, s, c, q, q_pos,
                                q_seq, sel, k, loc, sm_scale, out);
+        else if (few)
+            hipLaunchKernelGGL((k_attn_loop<0, kLWFew>), dim3((uint32_t)nq), dim3(kLWFew * 64), 0, s, c, q,
+                               q_pos, q_seq, sel, k, loc, sm_scale, out);
         else
-            hipLaunchKernelGGL(k_attn_loop<0>, dim3((uint32_t)nq), dim3(kLW * 64), 0, s, c, q, q_pos,
+            hipLaunchKernelGGL((k_attn_loop<0, kLW>), dim3((uint32_t)nq), dim3(kLW * 64), 0, s, c, q, q_pos,
                                q_seq, sel, k, loc, sm_scale, out);
         return hipGetLastError();
     }
