@@ -78,41 +78,48 @@ struct LongWs {
 
 __device__ __forceinline__ int64_t chunk_begin(int c) { return (int64_t)c * kChunk; }
 
-// grid (n_chunk, nq)
+// MODE 0, grid (n_chunk, nq): every workgroup adds its chunk to the row
+// histogram and the last one of a row finds the boundary buckets; MODE 1, the
+// chunks alone, then MODE 2, grid (1, nq): one workgroup per row finds them
+// (many rows: see k_topk_keep).
+template <int MODE>
 __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__ scores, int64_t n,
                                                        int64_t ld, const int32_t* __restrict__ ids,
                                                        int32_t k, int32_t k2, LongWs ws) {
     __shared__ alignas(16) int hist[kHistWords];
     __shared__ int res[4];
     __shared__ int last;
-    const int c = blockIdx.x, nc = gridDim.x;
+    const int c = blockIdx.x, nc = (int)((n + kChunk - 1) / kChunk);
     const int64_t row = blockIdx.y;
     const int tid = threadIdx.x;
     const float* s = scores + row * ld;
     const int32_t* irow = ids ? ids + row * n : nullptr;
     RowState* st = ws.st + row;
-    for (int i = tid; i < kHistWords; i += kLongNT) hist[i] = 0;
-    __syncthreads();
-    constexpr int kPer = kChunk / kLongNT;
-    const int64_t b0 = chunk_begin(c);
-    uint32_t kr[kPer];
-    load_keys<kPer, kLongNT>(s, irow, n, b0 + tid, kr);
+    if (MODE != 2) {
+        for (int i = tid; i < kHistWords; i += kLongNT) hist[i] = 0;
+        __syncthreads();
+        constexpr int kPer = kChunk / kLongNT;
+        const int64_t b0 = chunk_begin(c);
+        uint32_t kr[kPer];
+        load_keys<kPer, kLongNT>(s, irow, n, b0 + tid, kr);
 #pragma unroll
-    for (int j = 0; j < kPer; ++j)
-        if (kr[j]) atomicAdd(&hist[hidx((int)(kr[j] >> 20))], 1);
-    __syncthreads();
-    for (int i = tid; i < kHistBins; i += kLongNT) {
-        const int v = hist[hidx(i)];
-        if (v) atomicAdd(&st->hist[i], (uint32_t)v);
+        for (int j = 0; j < kPer; ++j)
+            if (kr[j]) atomicAdd(&hist[hidx((int)(kr[j] >> 20))], 1);
+        __syncthreads();
+        for (int i = tid; i < kHistBins; i += kLongNT) {
+            const int v = hist[hidx(i)];
+            if (v) atomicAdd(&st->hist[i], (uint32_t)v);
+        }
+        if (MODE == 1) return;
+        // the row histogram is built and read by device atomics alone, so the
+        // arrival needs no release or acquire: only this thread's adds complete
+        hand_off_wait();
+        __syncthreads();
+        if (tid == 0) last = arrive_last_coherent(&st->ctr_hist, (uint32_t)nc);
+        __syncthreads();
+        if (!last) return;
     }
-    // the row histogram is built and read by device atomics alone, so the
-    // arrival needs no release or acquire: only this thread's adds complete
-    hand_off_wait();
-    __syncthreads();
-    if (tid == 0) last = arrive_last_coherent(&st->ctr_hist, (uint32_t)nc);
-    __syncthreads();
-    if (!last) return;
-    // the last workgroup of the row: boundary bucket of each target
+    // the row's resolving workgroup: boundary bucket of each target
     {
         constexpr int kB = kHistBins / kLongNT;
         uint32_t hv[kB];
@@ -434,13 +441,16 @@ hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, c
                                          (size_t)nq * nc * kChunk * sizeof(Cand));
     const int32_t kk2 = out2 ? k2 : 0;
     dim3 grid((uint32_t)nc, (uint32_t)nq);
-    hipLaunchKernelGGL(k_topk_hist, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, kk2, w);
     if ((int64_t)nc * nq >= 256) {  // the rows fill the GPU
+        hipLaunchKernelGGL(k_topk_hist<1>, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, kk2, w);
+        hipLaunchKernelGGL(k_topk_hist<2>, dim3(1u, (uint32_t)nq), dim3(kLongNT), 0, s, scores, n, ld, ids, k,
+                           kk2, w);
         hipLaunchKernelGGL(k_topk_keep<1>, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
                            out2, w);
         hipLaunchKernelGGL(k_topk_keep<2>, dim3(1u, (uint32_t)nq), dim3(kLongNT), 0, s, scores, n, ld, ids, k,
                            out, kk2, out2, w);
     } else {
+        hipLaunchKernelGGL(k_topk_hist<0>, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, kk2, w);
         hipLaunchKernelGGL(k_topk_keep<0>, grid, dim3(kLongNT), 0, s, scores, n, ld, ids, k, out, kk2,
                            out2, w);
     }
