@@ -13,13 +13,16 @@
 //
 // Short rows (<= 32768 slots): one 1024-thread workgroup per row, keys in LDS.
 // Long rows: two multi-workgroup kernels per row set --
-//   hist:  12-bit histogram of the top digit (LDS, then device atomics); the
-//          last workgroup of a row picks the boundary bucket of each target;
+//   hist:  12-bit histogram of the top digit (LDS, then device atomics); one
+//          workgroup per row picks the boundary bucket of each target;
 //   keep:  every chunk compacts, in slot order, the keys any target can still
 //          take (those at or above the lowest boundary bucket) into its own
-//          region; the last workgroup of the row stages the row's kept keys
-//          (about k plus one bucket) in LDS, resolves (tau, need) of each
-//          target exactly on them and writes both selections in order.
+//          region; one workgroup per row holds the row's kept keys (about k
+//          plus one bucket) in registers, resolves (tau, need) of each target
+//          exactly on them and writes both selections in order.
+// For a handful of rows the per-row step is done by the row's last chunk
+// workgroup to arrive; for rows enough to fill the GPU each kernel is two
+// launches, chunks then one workgroup per row.
 // The workspace's counters and histogram reset themselves, so it must be
 // zero-filled before its first use and is left zero-filled by every call.
 #include "csa2_dev.h"
