@@ -181,7 +181,7 @@ StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, i
     w.scores = take(fused ? 1 : (size_t)n_seq * t_cap * sizeof(float));
     w.bscores = take((size_t)n_seq * (nb > 0 ? nb : 1) * sizeof(float));
     w.blocks = take((size_t)n_seq * (nbsel > 0 ? nbsel : 1) * sizeof(int32_t));
-    w.pscores = take((size_t)n_seq * (pool > 0 ? pool : 1) * sizeof(float));
+    w.pscores = take((size_t)n_seq * score_select_ld(pool > 0 ? pool : 1) * sizeof(float));
     w.pool = take((size_t)n_seq * (pool > 0 ? pool : 1) * sizeof(int32_t));
     w.sel0 = take((size_t)n_seq * k * sizeof(int32_t));
     w.ctr = take((size_t)n_seq * kCtrStride * sizeof(uint32_t));

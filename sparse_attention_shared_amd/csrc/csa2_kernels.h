@@ -95,8 +95,11 @@ hipError_t launch_prefill_topk(const CacheView& c, int32_t seq, const uint16_t* 
                                const int32_t* q_pos, int32_t nq, int32_t k, int32_t* sel, void* ws,
                                hipStream_t s);
 
-// Candidate scores + top-k among them in one launch (n_cand <= 16384); `ctr`
-// holds nq counters kCtrStride words apart that must be zero and are left zero.
+// Candidate scores + top-k among them (n_cand <= 16384); `scores` holds nq
+// rows of score_select_ld(n_cand) floats (whole 128-byte lines per row, so no
+// line is written by two workgroups); `ctr` holds nq counters kCtrStride words
+// apart that must be zero and are left zero.
+__host__ __device__ inline int64_t score_select_ld(int64_t n_cand) { return (n_cand + 31) / 32 * 32; }
 hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
                                const int32_t* q_seq, int32_t nq, const int32_t* cand,
                                int64_t n_cand, float* scores, uint32_t* ctr, int32_t k,

@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane & 7, grp = lane >> 3;
     const int64_t base = (int64_t)blockIdx.x * sel_keys<R>() + wave * 8 * R;
-    float* srow = scores + (int64_t)qi * n_cand;
+    float* srow = scores + (int64_t)qi * score_select_ld(n_cand);
     const int32_t* crow = cand + (int64_t)qi * n_cand;
     const int32_t seq = q_seq ? q_seq[qi] : qi;
     // the last entry the query may read: entries of 2^msh positions count

@@ -276,6 +276,24 @@ def test_stack_small_ragged_and_deterministic():
     assert torch.equal(pool, pool2)
 
 
+def test_stack_pool_not_a_multiple_of_32():
+    """A pool of 1000: the Reindex scores of consecutive queries do not start on
+    cache-line boundaries unless the score rows are padded (the scoring
+    workgroups hand their scores over line by line)."""
+    sp = synth.Spec("stack-pool1000", n_seq=3, t_cap=3001, q_pos=[3000, 2222, 1500],
+                    q_seq=[0, 1, 2], kv_format="fp4", k=64, window=32, pool=1000,
+                    schedule=synth.repeating_schedule(6), local_cap=48, seed=37)
+    x = synth.make_inputs(sp)
+    d = DevInputs(x)
+    outs, sels, pool = run_stack(sp, x, d)
+    err = check_stack(sp, x, d, outs, sels, pool)
+    log("stack pool 1000 max abs err", err)
+    outs2, sels2, _ = run_stack(sp, x, d)
+    for l in range(sp.n_layers):
+        assert torch.equal(outs[l].view(torch.int16), outs2[l].view(torch.int16))
+        assert torch.equal(sels[l], sels2[l])
+
+
 def test_stack_blockwise_small():
     sp = synth.Spec("blockwise-small", n_seq=2, t_cap=20000, q_pos=[19999, 12345], q_seq=[0, 1],
                     kv_format="fp4", k=128, window=16, pool=32 * 64, block=64,

@@ -101,6 +101,7 @@ def check_replay(sp, x, seq, outs, sels, pool, lk, lv, sample):
     (101, "repeat", 256),   # split attention, materialised Full rows (pool)
     (300, "repeat", 256),   # one workgroup per query
     (77, "full", 0),        # fused Full top-k, every layer Full
+    (300, "repeat", 1000),  # scoring and selecting launches; score rows padded to whole lines
 ])
 def test_replay_small_segments(n, schedule, pool):
     sched = (synth.repeating_schedule(7) if schedule == "repeat"
