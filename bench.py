@@ -9,25 +9,31 @@ its 2048 selected entries plus a 128-position local window.
 One step = one decode token for every sequence: the append of its position
 (global K | V row packed to FP4, indexer key, and the 20 layers' local ring
 slots; --no-append leaves it out), then all 20 layers (index scoring, top-k,
-gather + FP4 dequant, attention) through the C ABI: by default
-every kernel launched from the host (csa2_stack_run); --graph replays a stack
-recorded once per cache copy (csa2_stack_plan_create) as a HIP graph.  Inputs
-are resident in HBM before the timed region; the timed steps rotate over
-several copies of the cache so that consecutive steps do not find it in the
-256 MB Infinity Cache.
+gather + FP4 dequant, attention) through the C ABI: by default every kernel
+launched from the host (csa2_stack_run); --graph replays a stack recorded once
+per cache copy (csa2_stack_plan_create) as a HIP graph.  Inputs are resident
+in HBM before the timed region; the timed steps rotate over several copies of
+the cache so that consecutive steps do not find it in the 256 MB Infinity
+Cache.
 
-With --workload prefill it times the prefill chunk instead: 4096 queries at
+The default line also measures the other named workloads as extra keys
+(--no-extra leaves them out): one Full layer at batch 1 over 2048 bf16
+entries, one Full layer at batch 8 over 32768 FP4 entries, the blockwise
+Full layer over 2^20 entries, and the 4096-query prefill chunk.
+
+With --workload prefill it times the prefill chunk alone: 4096 queries at
 positions 126976..131071 of one 131072-token sequence, each selecting its
 top-2048 positions (csa2_prefill_topk) and attending to them plus its window
 (csa2_sparse_attn), reported as query positions per second.  With --workload
 replay it times the bounded replay of the last 128 positions of one
 131072-token sequence through the same 20-layer stack (csa2_replay_run).
 
-Prints one JSON line (see the repository's design doc for the fields).
+Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import hashlib
 import json
 import os
@@ -39,14 +45,19 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CSA2 decode tokens/s + achieved HBM GB/s (% peak) at 128k ctx, FP4 shared KV"
 PEAK_HBM_GBPS = 8000.0
-SCAN_KERNEL_SRC = os.path.join(ROOT, "sparse_attention_shared_amd", "csrc", "k_score.hip")
+PEAK_BF16_TFLOPS = 2500.0
+CSRC = os.path.join(ROOT, "sparse_attention_shared_amd", "csrc")
 
 
-def algorithmic_bytes(schedule, B, T, k, P, W, append=True, row=136):
+# ----------------------------------------------------------------- accounting
+
+def algorithmic_bytes(schedule, B, T, k, P, W, append=True, row=136, block=1):
     """Bytes the method must move per step (the append, selected rows, the
     scans the indexer needs, window, queries, outputs and index lists); the
-    dense attention it avoids is not counted.  row: bytes of one global K+V
-    entry (136 with E8M0 per 32, 144 with E4M3 per 16)."""
+    dense attention it avoids and intermediates such as score rows are not
+    counted.  row: bytes of one global K+V entry (136 with E8M0 per 32, 144
+    with E4M3 per 16, 512 in bf16).  block > 1: the Full layer scores
+    64-token blocks, then regathers the pool's keys (P of them) tokenwise."""
     kidx = 128           # bf16 indexer key
     win = W * 2 * 128 * 2
     qio = 16 * 128 * 2 * 2  # main Q in + output
@@ -54,241 +65,367 @@ def algorithmic_bytes(schedule, B, T, k, P, W, append=True, row=136):
     if append:           # read bf16 K|V, key, local K/V; write FP4 row, key, ring slots
         total += 512 + kidx + row + kidx + len(schedule) * 2 * (2 * 128 * 2)
     for m in schedule:
-        b = k * row + win + qio + k * 4          # gather, window, q/out, read sel
+        b = attn_bytes_per_query(k, W, row)
         if m == 0:
             b += T * kidx + 64 * 2 + (P + k) * 4  # full scan, q_I, write pool + sel
+            if block > 1:
+                nb = (T + block - 1) // block
+                b += 2 * nb * 4 + P * kidx + P * 4  # block scores out + in, pool keys, read pool
         elif m == 1:
             b += P * kidx + 64 * 2 + (P + k) * 4  # pool rescore, q_I, read pool, write sel
         total += b
     return total * B
 
 
-def scan_src_hash():
-    """Fingerprint of the scan kernel's source: its part of k_score.hip (the
-    kernel and its helpers) and the shared device header."""
-    src = open(SCAN_KERNEL_SRC).read()
-    a = src.index("constexpr int kScoreTile")
-    b = src.index("// grid: (ceil(n_cand / 256), nq)")
-    h = hashlib.sha256(src[a:b].encode())
-    h.update(open(os.path.join(os.path.dirname(SCAN_KERNEL_SRC), "csa2_dev.h"), "rb").read())
+def attn_bytes_per_query(k, W, row=136):
+    """Algorithmic bytes of one query's attention: the k gathered global
+    entries, the window's bf16 local K and V, main Q in and output out, and
+    the selection list read."""
+    return k * row + W * 2 * 128 * 2 + 16 * 128 * 2 * 2 + k * 4
+
+
+def src_hash(names):
+    """Fingerprint of kernel sources (the files the kernel is built from)."""
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(CSRC, n), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(launch_units):
-    """HBM bytes per launch of the scan kernel from the committed counter
-    summary, or None when the kernel source changed since it was taken."""
-    p = os.path.join(ROOT, "profiles", "k_score_dense_b4_t131072_counters.json")
+ATTN_SRC = ("k_attn.hip", "csa2_dev.h", "csa2_kernels.h")
+
+
+def traffic_from_profile(name, srcs):
+    """HBM bytes per launch of a kernel from a committed counter summary
+    (profiles/<name>.json), or None when it is missing or the kernel's sources
+    changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", name + ".json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kernel_src_sha256_16") != scan_src_hash():
+    if d.get("kernel_src_sha256_16") != src_hash(srcs):
         return None
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle (plain C, one thread) on a bounded sample of the same
-    workload: whole 20-layer stacks of single sequences until the budget."""
+def pct(xs, q):
     import numpy as np
-    import oracle
-    import synth
-    sp = synth.config(3)
-    sp1 = synth.Spec(**{**sp.__dict__, "n_seq": 1, "q_pos": [sp.q_pos[0]], "q_seq": [0]})
-    x = synth.make_inputs(sp1)
-    c = oracle.Cache(x.kv, x.k_idx, fp4=True)
-    n = 0
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def oracle_threads():
+    # the box grants one GPU's share of its CPUs (16)
+    return max(1, min(16, host_cores()))
+
+
+# ------------------------------------------------------------- CPU baseline
+
+def _rate(fn, units_per_call, budget_s, threads, max_calls):
+    """Calls fn(i) (each a plain C oracle call that releases the GIL) on
+    `threads` threads until the budget; returns (units/s, calls, seconds)."""
     t0 = time.perf_counter()
-    while True:
-        oracle.stack(c, sp1.schedule, x.q_pos, x.q, x.q_idx, x.local_k, x.local_v, sp1.window, 0,
-                     sp1.k, sp1.pool)
-        n += 1
+    n = 0
+    if threads == 1:
+        while True:
+            fn(n)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or n >= max_calls:
+                break
+        return n * units_per_call / el, n, el
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        pending = set()
+        i = 0
+        while True:
+            while len(pending) < 2 * threads and i < max_calls and time.perf_counter() - t0 < budget_s:
+                pending.add(ex.submit(fn, i))
+                i += 1
+            if not pending:
+                break
+            done, pending = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+            for f in done:
+                f.result()
+                n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 64:
-            break
-    return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d single-sequence 20-layer decode steps of the same workload "
-                      "(T=131072, FP4, pool 8192, k=2048, W=128) in %.1f s, one thread; the "
-                      "append's few-KB row writes are not in the sample" % (n, el)}
+    return n * units_per_call / el, n, el
 
 
-PREFILL_METRIC = "CSA2 prefill-chunk query positions/s at 128k ctx, FP4 shared KV"
-PEAK_BF16_TFLOPS = 2500.0
-
-
-def cpu_baseline_prefill(x, sp, budget_s=12.0):
-    """The oracle (plain C, one thread) on a bounded sample of the prefill
-    chunk: single queries (scores, top-k, attention) until the budget."""
+def cpu_baseline_stack(sp, x, budget_s=6.0, what="decode steps", unit="tokens/s"):
+    """The oracle (plain C, unchanged) on whole single-sequence stacks of the
+    same workload (sequence 0 of the inputs x): one thread, then one thread
+    per host core given to this process (independent steps in parallel)."""
     import numpy as np
     import oracle
+    c = oracle.Cache(x.kv[:1], x.k_idx[:1], fp4=sp.kv_format != "bf16",
+                     scale="e4m3" if sp.kv_format == "fp4e" else "e8m0")
+    q_pos = np.ascontiguousarray(x.q_pos[:1])
+    q, q_idx = np.ascontiguousarray(x.q[:, :1]), np.ascontiguousarray(x.q_idx[:, :1])
+    lk, lv = np.ascontiguousarray(x.local_k[:, :1]), np.ascontiguousarray(x.local_v[:, :1])
+
+    def one(_):
+        oracle.stack(c, sp.schedule, q_pos, q, q_idx, lk, lv, sp.window, sp.lo, sp.k, sp.pool,
+                     sp.block)
+
+    v1, n1, e1 = _rate(one, 1, budget_s / 2, 1, 64)
+    nt = oracle_threads()
+    vn, nn, en = _rate(one, 1, budget_s / 2, nt, 4096)
+    return {"value": vn, "unit": unit, "cores": nt, "host_cores": host_cores(),
+            "value_1thread": v1, "kind": "oracle",
+            "sample": "single-sequence %s of the same workload (%s): %d on one thread in "
+                      "%.1f s, %d on %d threads in %.1f s; the oracle code is unchanged, the "
+                      "threads run independent steps (ctypes releases the GIL); the append's "
+                      "few-KB row writes are not in the sample" % (what, sp.name, n1, e1, nn,
+                                                                   nt, en)}
+
+
+def cpu_baseline_prefill(x, sp, budget_s=6.0):
+    """The oracle on single queries of the prefill chunk (scores over ~129k
+    positions, top-2048, attention): one thread, then one per core."""
+    import oracle
     c = oracle.Cache(x.kv, x.k_idx, fp4=True)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def one(n):
         i = (n * 997) % sp.nq
         t = int(sp.q_pos[i])
         s = oracle.scores(x.q_idx[0, i], x.k_idx[0, :t + 1])
         sel = oracle.topk(s, sp.k)
         oracle.attend(c, x.q_pos[i:i + 1], x.q_seq[i:i + 1], x.q[0, i:i + 1], sel[None],
                       x.local_k[0], x.local_v[0], sp.window, sp.lo)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 512:
-            break
-    return {"value": n / el, "unit": "query positions/s", "cores": 1, "kind": "oracle",
-            "sample": "%d queries of the prefill chunk (scores over ~129k positions, top-2048, "
-                      "attention) in %.1f s, one thread" % (n, el)}
+
+    v1, n1, e1 = _rate(one, 1, budget_s / 2, 1, 512)
+    nt = oracle_threads()
+    vn, nn, en = _rate(one, 1, budget_s / 2, nt, 4096)
+    return {"value": vn, "unit": "query positions/s", "cores": nt, "host_cores": host_cores(),
+            "value_1thread": v1, "kind": "oracle",
+            "sample": "queries of the prefill chunk: %d on one thread in %.1f s, %d on %d "
+                      "threads in %.1f s" % (n1, e1, nn, nt, en)}
 
 
-REPLAY_METRIC = "CSA2 bounded-replay query positions/s (last 128 positions, 20 layers) at 128k ctx"
+# ------------------------------------------------------------------ devices
 
-
-def replay_spec():
-    """The 20-layer workload's stack on one 131072-token sequence, replaying
-    its last 128 positions with every window cut off at the segment."""
-    import synth
-    base = synth.config(3)
-    n, T = 128, base.t_cap
-    return synth.Spec("replay", n_seq=1, t_cap=T, q_pos=list(range(T - n, T)), q_seq=[0] * n,
-                      kv_format="fp4", k=base.k, window=base.window, pool=base.pool,
-                      schedule=base.schedule, local_cap=128, lo=T - n, seed=1007)
-
-
-def cpu_baseline_replay(x, sp, k_new, v_new, budget_s=12.0):
-    """The oracle on a bounded sample of the replay: sub-segments of 4
-    positions through all 20 layers until the budget."""
-    import oracle
-    c = oracle.Cache(x.kv, x.k_idx, fp4=True)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        i = (n * 4) % sp.nq
-        sl = slice(i, i + 4)
-        oracle.replay(c, sp.schedule, 0, x.q_pos[sl], x.q[:, sl], x.q_idx[:, sl], x.local_k,
-                      x.local_v, sp.window, sp.lo, sp.k, sp.pool, k_new[:, sl], v_new[:, sl])
-        n += 4
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 128:
-            break
-    return {"value": n / el, "unit": "query positions/s", "cores": 1, "kind": "oracle",
-            "sample": "%d segment positions (groups of 4) through the 20 layers in %.1f s, one "
-                      "thread" % (n, el)}
-
-
-def bench_replay(args):
-    """One step = csa2_replay_run of the last 128 positions of a 131072-token
-    sequence through the 20-layer stack (ring rows, Full / Reindex / Reuse
-    selections, attention), inputs resident in HBM."""
-    import ctypes
+def _d16(a):
     import numpy as np
     import torch
-    import synth
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+class Timer:
+    """HIP events around each timed step (per-step times) and around the whole
+    timed region (the mean), on the current stream."""
+
+    def __init__(self, steps):
+        import torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+        self.t0 = torch.cuda.Event(enable_timing=True)
+        self.t1 = torch.cuda.Event(enable_timing=True)
+
+    def run(self, step, steps):
+        import torch
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        self.t0.record()
+        for i in range(steps):
+            self.ev[i][0].record()
+            step(i)
+            self.ev[i][1].record()
+        self.t1.record()
+        torch.cuda.synchronize()
+        self.wall = time.perf_counter() - wall0
+        self.ms = self.t0.elapsed_time(self.t1) / steps
+        self.per = [a.elapsed_time(b) for a, b in self.ev[:steps]]
+        return self.ms
+
+    def stats(self):
+        return {"ms_per_step": self.ms, "ms_median": pct(self.per, 50), "ms_p10": pct(self.per, 10),
+                "ms_p90": pct(self.per, 90)}
+
+
+def _events(n):
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in ev:  # create the underlying HIP events
+        e.record()
+    torch.cuda.synchronize()
+    return ev
+
+
+class DecodeSetup:
+    """Device inputs of a decode workload: `copies` copies of the cache (rotated
+    across steps), per-layer queries and rings, optional append rows."""
+
+    def __init__(self, sp, copies, append, kv_fmt="fp4"):
+        import numpy as np
+        import torch
+        import synth
+        import sparse_attention_shared_amd as csa2
+        self.sp = sp
+        B, L = sp.n_seq, sp.n_layers
+        x = synth.make_inputs(sp)
+        self.x = x
+        kv = _d16(x.kv)
+        k_idx0 = _d16(x.k_idx)
+        if sp.kv_format == "bf16":
+            data0, scales0 = kv, None
+        else:
+            data0, scales0 = (csa2.pack_fp4 if sp.kv_format == "fp4" else csa2.pack_fp4_e4m3)(kv)
+            del kv
+        self.caches = []
+        for i in range(copies):
+            if i == 0:
+                d, s, ki = data0, scales0, k_idx0
+            else:
+                d, s, ki = data0.clone(), (scales0.clone() if scales0 is not None else None), \
+                    k_idx0.clone()
+            self.caches.append(csa2.Cache(d, ki, s))
+        self.q_pos = torch.from_numpy(x.q_pos).cuda()
+        self.q = [_d16(x.q[l]) for l in range(L)]
+        self.q_idx = [_d16(x.q_idx[l]) if sp.schedule[l] != synth.REUSE else None for l in range(L)]
+        self.local = [csa2.Local(_d16(x.local_k[l]), _d16(x.local_v[l]), sp.window) for l in range(L)]
+        self.out = [torch.empty((B, 16, 128), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+        # the appended rows are the ones the inputs already hold at q_pos, so
+        # every step rewrites the same values and the cache stays what the
+        # oracle sees
+        self.app = None
+        if append:
+            bi = np.arange(B)
+            t = x.q_pos.astype(np.int64)
+            self.app = (_d16(x.kv[bi, t]), _d16(x.k_idx[bi, t]),
+                        [_d16(x.local_k[l][bi, t % sp.local_cap]) for l in range(L)],
+                        [_d16(x.local_v[l][bi, t % sp.local_cap]) for l in range(L)])
+        from sparse_attention_shared_amd._lib import _StackArgs, stack_workspace
+        need = stack_workspace(_StackArgs(self.caches[0], sp.schedule, self.q_pos, self.q,
+                                          self.q_idx, self.local, self.out, sp.k, sp.pool,
+                                          sp.block, 128 ** -0.5, None, None))
+        self.ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self, i, scan_ev=None, attn_ev=None):
+        import sparse_attention_shared_amd as csa2
+        sp = self.sp
+        csa2.stack_run(self.caches[i % len(self.caches)], sp.schedule, self.q_pos, self.q,
+                       self.q_idx, self.local, sp.k, sp.pool, sp.block, want_sel=False,
+                       ws=self.ws, out=self.out, scan_events=scan_ev, attn_events=attn_ev,
+                       append=self.app)
+
+
+def time_decode(setup, steps, warmup, kernel_events=True, graph=False):
+    """Times `steps` decode steps after `warmup`; returns (Timer, attention
+    launch durations in ms, scan durations in ms)."""
+    import torch
     import sparse_attention_shared_amd as csa2
-    from sparse_attention_shared_amd import _lib
-
-    sp = replay_spec()
-    L, n = sp.n_layers, sp.nq
-    print("generating inputs ...", file=sys.stderr, flush=True)
-    x = synth.make_inputs(sp)
-    rng = np.random.default_rng(7)
-    k_new = synth.f32_to_bf16_bits(rng.standard_normal((L, n, 128)).astype(np.float32))
-    v_new = synth.f32_to_bf16_bits(rng.standard_normal((L, n, 128)).astype(np.float32))
-
-    def d16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-
-    codes, scales = csa2.pack_fp4(d16(x.kv))
-    cache = csa2.Cache(codes, d16(x.k_idx), scales)
-    q_pos = torch.from_numpy(x.q_pos).cuda()
-    q = [d16(x.q[l]) for l in range(L)]
-    q_idx = [d16(x.q_idx[l]) if sp.schedule[l] != synth.REUSE else None for l in range(L)]
-    local = [csa2.Local(d16(x.local_k[l]), d16(x.local_v[l]), sp.window, sp.lo) for l in range(L)]
-    lk = [d16(k_new[l]) for l in range(L)]
-    lv = [d16(v_new[l]) for l in range(L)]
-    out = [torch.empty((n, 16, 128), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
-    args_c = _lib._ReplayArgs(cache, sp.schedule, 0, q_pos, q, q_idx, local, out, sp.k, sp.pool,
-                              1, 128 ** -0.5, lk, lv)
-    ws = torch.zeros(_lib.replay_workspace(args_c), dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-    L_ = csa2.lib()
-
-    def step():
-        st = L_.csa2_replay_run(ctypes.byref(args_c.desc), _lib._ptr(ws), ws.numel(),
-                                _lib._stream())
-        if st:
-            raise RuntimeError("csa2_replay_run status %d" % st)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record()
-    for _ in range(args.steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1) / args.steps
-    result = {
-        "metric": REPLAY_METRIC,
-        "value": n / (ms * 1e-3),
-        "unit": "query positions/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": "bounded replay: the last 128 positions of one 131072-token sequence "
-                        "through the 20-layer CSA2 stack (Full pool 8192 then [Reindex, Reuse "
-                        "x3]*, top-k 2048, SWA 128 cut off at the segment), FP4 (E2M1 + E8M0/32) "
-                        "shared KV, 16 q heads / 1 KV head, head_dim 128, indexer dim 64",
-            "queries": n, "context": sp.t_cap, "layers": L, "k": sp.k, "pool": sp.pool,
-            "window": sp.window,
-        },
-        "wall_s_timed_region": wall,
-    }
-    if not args.no_cpu_baseline:
-        print("timing the oracle on the host ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline_replay(x, sp, k_new, v_new)
-    print(json.dumps(result), flush=True)
+    sp = setup.sp
+    L = sp.n_layers
+    tm = Timer(steps)
+    attn_ms, scan_ms = [], []
+    if not graph:
+        # each step times the scan and ONE layer's attention launch (layer
+        # i % L at step i): bracketing a launch with events costs the host
+        # ~20 us, and every launch of a step bracketed leaves the GPU waiting
+        # for the host (measured 0.68 vs 0.30 ms per step)
+        def one_layer(i):
+            e = [None] * (2 * L)
+            e[2 * (i % L)], e[2 * (i % L) + 1] = _events(2)
+            return e
+        aev = [one_layer(i) for i in range(steps)] if kernel_events else None
+        sev = [_events(2) for _ in range(steps)] if kernel_events else None
+        for i in range(warmup):
+            setup.step(i)
+        torch.cuda.synchronize()
+        tm.run(lambda i: setup.step(i, sev[i] if sev else None, aev[i] if aev else None), steps)
+        if kernel_events:
+            for i in range(steps):
+                l = i % L
+                attn_ms.append(aev[i][2 * l].elapsed_time(aev[i][2 * l + 1]))
+                scan_ms.append(sev[i][0].elapsed_time(sev[i][1]))
+    else:
+        plans = [csa2.StackPlan(c, sp.schedule, setup.q_pos, setup.q, setup.q_idx, setup.local,
+                                sp.k, sp.pool, sp.block, out=setup.out, append=setup.app)
+                 for c in setup.caches]
+        for i in range(warmup):
+            plans[i % len(plans)].launch()
+        tm.run(lambda i: plans[i % len(plans)].launch(), steps)
+        for pl in plans:
+            pl.close()
+        if kernel_events:
+            # events inside a graph do not bracket its kernels: the kernels
+            # are timed on host-launched steps of the same stack afterwards
+            n = min(steps, 40)
+            aev = [_events(2 * L) for _ in range(n)]
+            sev = [_events(2) for _ in range(n)]
+            for i in range(n):
+                setup.step(i, sev[i], aev[i])
+            torch.cuda.synchronize()
+            for i in range(n):
+                attn_ms += [aev[i][2 * l].elapsed_time(aev[i][2 * l + 1]) for l in range(L)]
+                scan_ms.append(sev[i][0].elapsed_time(sev[i][1]))
+    return tm, attn_ms, scan_ms
 
 
-def bench_prefill(args):
-    """One step = the whole 4096-query prefill chunk: fused indexer top-k then
-    attention, both through the C ABI, inputs resident in HBM."""
+def decode_record(setup, tm, attn_ms, scan_ms, row):
+    """Throughput, step bandwidth and per-kernel rooflines of a decode run."""
+    sp = setup.sp
+    B, T = sp.n_seq, sp.t_cap
+    step_bytes = algorithmic_bytes(sp.schedule, B, T, sp.k, sp.pool, sp.window,
+                                   append=setup.app is not None, row=row, block=sp.block)
+    rec = dict(tm.stats())
+    rec["value"] = B / (tm.ms * 1e-3)
+    rec["step_algorithmic_bytes"] = step_bytes
+    rec["hbm_gbps"] = step_bytes / (tm.ms * 1e-3) / 1e9
+    rec["hbm_frac_of_peak"] = rec["hbm_gbps"] / PEAK_HBM_GBPS
+    kern = {}
+    if attn_ms:
+        a_ms = sum(attn_ms) / len(attn_ms)
+        a_bytes = B * attn_bytes_per_query(sp.k, sp.window, row)
+        kern["attention"] = {
+            "launches_per_step": sp.n_layers, "launch_ms_mean": a_ms,
+            "launch_ms_median": pct(attn_ms, 50), "algorithmic_bytes_per_launch": a_bytes,
+            "achieved_gbps": a_bytes / (a_ms * 1e-3) / 1e9,
+            "ms_per_step": a_ms * sp.n_layers}
+    if scan_ms:
+        s_ms = sum(scan_ms) / len(scan_ms)
+        s_bytes = B * T * 128
+        kern["scan"] = {"launches_per_step": 1, "launch_ms_mean": s_ms,
+                        "algorithmic_bytes_per_launch": s_bytes,
+                        "achieved_gbps": s_bytes / (s_ms * 1e-3) / 1e9, "ms_per_step": s_ms}
+    rec["kernels"] = kern
+    return rec
+
+
+# ----------------------------------------------------------------- workloads
+
+def bench_prefill_run(steps, warmup):
+    """The 4096-query prefill chunk: fused indexer top-k then attention, both
+    through the C ABI, inputs resident in HBM.  Returns (record, x, sp)."""
     import numpy as np
     import torch
     import synth
     import sparse_attention_shared_amd as csa2
 
     sp = synth.config(5)
-    print("generating inputs ...", file=sys.stderr, flush=True)
     x = synth.make_inputs(sp)
-
-    def d16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-
-    codes, scales = csa2.pack_fp4(d16(x.kv))
-    cache = csa2.Cache(codes, d16(x.k_idx), scales)
+    codes, scales = csa2.pack_fp4(_d16(x.kv))
+    cache = csa2.Cache(codes, _d16(x.k_idx), scales)
     nq = sp.nq
     q_pos = torch.from_numpy(x.q_pos).cuda()
     q_seq = torch.from_numpy(x.q_seq).cuda()
-    q = d16(x.q[0])
-    q_idx = d16(x.q_idx[0])
-    local = csa2.Local(d16(x.local_k[0]), d16(x.local_v[0]), sp.window)
+    q = _d16(x.q[0])
+    q_idx = _d16(x.q_idx[0])
+    local = csa2.Local(_d16(x.local_k[0]), _d16(x.local_v[0]), sp.window)
     sel = torch.empty((nq, sp.k), dtype=torch.int32, device="cuda")
     out = torch.empty((nq, 16, 128), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(csa2.prefill_topk_workspace(nq, sp.t_cap, sp.k), dtype=torch.uint8,
                      device="cuda")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [_events(3) for _ in range(steps)]
 
-    def step(e=None):
+    def step(i, e=None):
         if e:
             e[0].record()
         csa2.prefill_topk(cache, 0, q_idx, q_pos, sp.k, out=sel, ws=ws)
@@ -298,19 +435,10 @@ def bench_prefill(args):
         if e:
             e[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record()
-    for i in range(args.steps):
-        step(ev[i])
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1) / args.steps
+    for i in range(warmup):
+        step(i)
+    tm = Timer(steps)
+    tm.run(lambda i: step(i, ev[i]), steps)
     topk_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev)
     attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev)
     # algorithmic work: the causal indexer product once, and QK + PV over the
@@ -326,37 +454,137 @@ def bench_prefill(args):
                              "algorithmic_flop": attn_flop},
     }
     dom = max(parts, key=lambda n: parts[n]["ms"])
+    rec = dict(tm.stats())
+    rec.update({
+        "value": nq / (tm.ms * 1e-3), "unit": "query positions/s",
+        "tflops": (idx_flop + attn_flop) / (tm.ms * 1e-3) / 1e12,
+        "mfma_frac_of_peak": (idx_flop + attn_flop) / (tm.ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "parts": parts,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": parts[dom]["tflops"],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": parts[dom]["tflops"] / PEAK_BF16_TFLOPS, "traffic": None},
+        "wall_s_timed_region": tm.wall,
+    })
+    return rec, x, sp
+
+
+def extra_decode(cid, steps, warmup, oracle_budget):
+    """One of the single-layer decode workloads (1, 2, 4) as an extra key."""
+    import torch
+    import synth
+    sp = synth.config(cid)
+    row = {"bf16": 512, "fp4": 136, "fp4e": 144}[sp.kv_format]
+    st = DecodeSetup(sp, copies=2 if cid == 4 else 4, append=False)
+    tm, attn_ms, scan_ms = time_decode(st, steps, warmup)
+    rec = decode_record(st, tm, attn_ms, scan_ms, row)
+    rec["unit"] = "tokens/s"
+    rec["workload"] = sp.name
+    rec["append"] = False
+    if oracle_budget > 0:
+        rec["cpu_baseline"] = cpu_baseline_stack(sp, st.x, oracle_budget, "one-layer decode steps")
+    del st
+    torch.cuda.empty_cache()
+    return rec
+
+
+def bench_replay(args):
+    """One step = csa2_replay_run of the last 128 positions of a 131072-token
+    sequence through the 20-layer stack (ring rows, Full / Reindex / Reuse
+    selections, attention), inputs resident in HBM."""
+    import ctypes
+    import numpy as np
+    import torch
+    import oracle
+    import synth
+    import sparse_attention_shared_amd as csa2
+    from sparse_attention_shared_amd import _lib
+
+    base = synth.config(3)
+    n, T = 128, base.t_cap
+    sp = synth.Spec("replay", n_seq=1, t_cap=T, q_pos=list(range(T - n, T)), q_seq=[0] * n,
+                    kv_format="fp4", k=base.k, window=base.window, pool=base.pool,
+                    schedule=base.schedule, local_cap=128, lo=T - n, seed=1007)
+    L = sp.n_layers
+    print("generating inputs ...", file=sys.stderr, flush=True)
+    x = synth.make_inputs(sp)
+    rng = np.random.default_rng(7)
+    k_new = synth.f32_to_bf16_bits(rng.standard_normal((L, n, 128)).astype(np.float32))
+    v_new = synth.f32_to_bf16_bits(rng.standard_normal((L, n, 128)).astype(np.float32))
+    codes, scales = csa2.pack_fp4(_d16(x.kv))
+    cache = csa2.Cache(codes, _d16(x.k_idx), scales)
+    q_pos = torch.from_numpy(x.q_pos).cuda()
+    q = [_d16(x.q[l]) for l in range(L)]
+    q_idx = [_d16(x.q_idx[l]) if sp.schedule[l] != synth.REUSE else None for l in range(L)]
+    local = [csa2.Local(_d16(x.local_k[l]), _d16(x.local_v[l]), sp.window, sp.lo) for l in range(L)]
+    lk = [_d16(k_new[l]) for l in range(L)]
+    lv = [_d16(v_new[l]) for l in range(L)]
+    out = [torch.empty((n, 16, 128), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    args_c = _lib._ReplayArgs(cache, sp.schedule, 0, q_pos, q, q_idx, local, out, sp.k, sp.pool,
+                              1, 128 ** -0.5, lk, lv)
+    ws = torch.zeros(_lib.replay_workspace(args_c), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    L_ = csa2.lib()
+
+    def step(i):
+        st = L_.csa2_replay_run(ctypes.byref(args_c.desc), _lib._ptr(ws), ws.numel(),
+                                _lib._stream())
+        if st:
+            raise RuntimeError("csa2_replay_run status %d" % st)
+
+    for i in range(args.warmup):
+        step(i)
+    tm = Timer(args.steps)
+    tm.run(step, args.steps)
     result = {
-        "metric": PREFILL_METRIC,
-        "value": nq / (ms * 1e-3),
-        "unit": "query positions/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
+        "metric": "CSA2 bounded-replay query positions/s (last 128 positions, 20 layers) "
+                  "at 128k ctx",
+        "value": n / (tm.ms * 1e-3), "unit": "query positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": "bounded replay: the last 128 positions of one 131072-token sequence "
+                        "through the 20-layer CSA2 stack (Full pool 8192 then [Reindex, Reuse "
+                        "x3]*, top-k 2048, SWA 128 cut off at the segment), FP4 (E2M1 + E8M0/32) "
+                        "shared KV, 16 q heads / 1 KV head, head_dim 128, indexer dim 64",
+            "queries": n, "context": sp.t_cap, "layers": L, "k": sp.k, "pool": sp.pool,
+            "window": sp.window},
+        "wall_s_timed_region": tm.wall,
+    }
+    result.update(tm.stats())
+    if not args.no_cpu_baseline:
+        print("timing the oracle on the host ...", file=sys.stderr, flush=True)
+        c = oracle.Cache(x.kv, x.k_idx, fp4=True)
+
+        def one(i):
+            j = (i * 4) % n
+            sl = slice(j, j + 4)
+            oracle.replay(c, sp.schedule, 0, x.q_pos[sl], x.q[:, sl], x.q_idx[:, sl], x.local_k,
+                          x.local_v, sp.window, sp.lo, sp.k, sp.pool, k_new[:, sl], v_new[:, sl])
+
+        v1, n1, e1 = _rate(one, 4, 6.0, 1, 32)
+        nt = oracle_threads()
+        vn, nn, en = _rate(one, 4, 6.0, nt, 4096)
+        result["cpu_baseline"] = {
+            "value": vn, "unit": "query positions/s", "cores": nt, "host_cores": host_cores(),
+            "value_1thread": v1, "kind": "oracle",
+            "sample": "4-position sub-segments through the 20 layers: %d on one thread in %.1f "
+                      "s, %d on %d threads in %.1f s" % (n1, e1, nn, nt, en)}
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(args):
+    rec, x, sp = bench_prefill_run(args.steps, args.warmup)
+    result = {
+        "metric": "CSA2 prefill-chunk query positions/s at 128k ctx, FP4 shared KV",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {
             "workload": "CSA2 prefill chunk: 4096 queries at positions 126976..131071 of one "
                         "131072-token sequence, FP4 (E2M1 + E8M0/32) shared KV, indexer dim 64, "
                         "top-k 2048, SWA 128, 16 q heads / 1 KV head, head_dim 128",
-            "queries": nq, "context": sp.t_cap, "k": sp.k, "window": sp.window,
-        },
-        "parts": parts,
-        "wall_s_timed_region": wall,
-        "roofline": {
-            "kernel": dom,
-            "bound": "mfma",
-            "achieved": parts[dom]["tflops"],
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": parts[dom]["tflops"] / PEAK_BF16_TFLOPS,
-            "traffic": None,
-        },
+            "queries": sp.nq, "context": sp.t_cap, "k": sp.k, "window": sp.window},
     }
+    result.update(rec)
     if not args.no_cpu_baseline:
         print("timing the oracle on the host ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline_prefill(x, sp)
@@ -370,6 +598,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="leave the other named workloads out of the default line")
     ap.add_argument("--schedule", choices=["repeat", "page"], default="repeat")
     ap.add_argument("--kv", choices=["fp4", "fp4e"], default="fp4",
                     help="fp4: one E8M0 scale per 32 channels; fp4e: one E4M3 scale per 16")
@@ -379,6 +609,8 @@ def main():
                     help="replay a recorded stack (HIP graph) per step instead of host launches")
     ap.add_argument("--no-append", action="store_true",
                     help="leave the decode append of the new position out of the step")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="do not time the scan and attention kernels inside the timed steps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -387,7 +619,6 @@ def main():
               "(a sharding plan is described in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import synth
     import sparse_attention_shared_amd as csa2
@@ -415,128 +646,48 @@ def main():
     if args.topk:
         sp = synth.Spec(**{**sp.__dict__, "k": args.topk})
     sp = synth.Spec(**{**sp.__dict__, "kv_format": args.kv})
-    B, T, L = sp.n_seq, sp.t_cap, sp.n_layers
+    row = 136 if args.kv == "fp4" else 144
     print("generating inputs ...", file=sys.stderr, flush=True)
-    x = synth.make_inputs(sp)
-
-    def d16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-
-    kv = d16(x.kv)
-    k_idx0 = d16(x.k_idx)
-    codes0, scales0 = (csa2.pack_fp4 if args.kv == "fp4" else csa2.pack_fp4_e4m3)(kv)
-    del kv
-    caches = []
-    for i in range(args.copies):
-        if i == 0:
-            codes, scales, k_idx = codes0, scales0, k_idx0
-        else:
-            codes, scales, k_idx = codes0.clone(), scales0.clone(), k_idx0.clone()
-        caches.append(csa2.Cache(codes, k_idx, scales))
-    q_pos = torch.from_numpy(x.q_pos).cuda()
-    q = [d16(x.q[l]) for l in range(L)]
-    q_idx = [d16(x.q_idx[l]) if sp.schedule[l] != synth.REUSE else None for l in range(L)]
-    local = [csa2.Local(d16(x.local_k[l]), d16(x.local_v[l]), sp.window) for l in range(L)]
-    out = [torch.empty((B, 16, 128), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
-    ws = torch.empty(1, dtype=torch.uint8, device="cuda")
-    # the appended rows are the ones the inputs already hold at q_pos, so every
-    # step rewrites the same values and the cache stays what the oracle sees
-    app = None
-    if not args.no_append:
-        bi = np.arange(B)
-        t = x.q_pos.astype(np.int64)
-        app = (d16(x.kv[bi, t]), d16(x.k_idx[bi, t]),
-               [d16(x.local_k[l][bi, t % sp.local_cap]) for l in range(L)],
-               [d16(x.local_v[l][bi, t % sp.local_cap]) for l in range(L)])
-    # size the workspace once
-    _, _, _ = csa2.stack_run(caches[0], sp.schedule, q_pos, q, q_idx, local, sp.k, sp.pool,
-                             want_sel=False, out=out, append=app)
-    torch.cuda.synchronize()
-    from sparse_attention_shared_amd._lib import _StackArgs, stack_workspace
-    need = stack_workspace(_StackArgs(caches[0], sp.schedule, q_pos, q, q_idx, local, out, sp.k,
-                                      sp.pool, 1, 128 ** -0.5, None, None))
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-
-    if not args.graph:
-        n_ev = args.steps
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n_ev)]
-        for a, b in ev:  # create the underlying HIP events
-            a.record()
-            b.record()
-        torch.cuda.synchronize()
-
-        def step(i, events=None):
-            csa2.stack_run(caches[i % len(caches)], sp.schedule, q_pos, q, q_idx, local, sp.k,
-                           sp.pool, want_sel=False, ws=ws, out=out, scan_events=events,
-                           append=app)
-
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        wall0 = time.perf_counter()
-        t_start.record()
-        for i in range(args.steps):
-            step(i, ev[i])
-        t_end.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        ms = t_start.elapsed_time(t_end) / args.steps
-        scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-    else:
-        # one recorded stack (HIP graph) per cache copy
-        plans = [csa2.StackPlan(c, sp.schedule, q_pos, q, q_idx, local, sp.k, sp.pool, out=out,
-                                append=app) for c in caches]
-        for i in range(args.warmup):
-            plans[i % len(plans)].launch()
-        torch.cuda.synchronize()
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        wall0 = time.perf_counter()
-        t_start.record()
-        for i in range(args.steps):
-            plans[i % len(plans)].launch()
-        t_end.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        ms = t_start.elapsed_time(t_end) / args.steps
-        for pl in plans:
-            pl.close()
-        # events recorded inside a graph do not bracket its kernels, so the
-        # scan is timed on host-launched steps of the same stack
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(40)]
-        for a, b in ev:  # create the underlying HIP events
-            a.record()
-            b.record()
-        torch.cuda.synchronize()
-        for i, e in enumerate(ev):
-            csa2.stack_run(caches[i % len(caches)], sp.schedule, q_pos, q, q_idx, local, sp.k,
-                           sp.pool, want_sel=False, ws=ws, out=out, scan_events=e, append=app)
-        torch.cuda.synchronize()
-        scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-
-    step_bytes = algorithmic_bytes(sp.schedule, B, T, sp.k, sp.pool, sp.window,
-                                   append=app is not None, row=136 if args.kv == "fp4" else 144)
-    scan_bytes = B * T * 128
-    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    st = DecodeSetup(sp, args.copies, not args.no_append)
+    tm, attn_ms, scan_ms = time_decode(st, args.steps, args.warmup,
+                                       kernel_events=not args.no_kernel_events, graph=args.graph)
+    rec = decode_record(st, tm, attn_ms, scan_ms, row)
+    B = sp.n_seq
+    kern = rec.pop("kernels")
+    roofline = None
+    if kern:
+        # the dominant kernel: the most time per step
+        name = max(kern, key=lambda n: kern[n]["ms_per_step"])
+        kk = kern[name]
+        roofline = {
+            "kernel": {"attention": "k_attn_chunk (decode attention, one launch per layer)",
+                       "scan": "k_score_dense<1> (layer-0 Full indexer scan)"}[name],
+            "bound": "hbm", "achieved": kk["achieved_gbps"], "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": kk["achieved_gbps"] / PEAK_HBM_GBPS,
+            "traffic": (traffic_from_profile("k_attn_chunk_b4_t131072_fp4_counters", ATTN_SRC)
+                        if name == "attention" and args.kv == "fp4" and not args.topk else None),
+            "launch_ms": kk["launch_ms_mean"],
+            "algorithmic_bytes_per_launch": kk["algorithmic_bytes_per_launch"],
+            "share_of_step": kk["ms_per_step"] / rec["ms_per_step"],
+        }
     result = {
         "metric": METRIC,
-        "value": B / (ms * 1e-3),
+        "value": rec["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": rec["ms_per_step"],
+        "ms_median": rec["ms_median"], "ms_p10": rec["ms_p10"], "ms_p90": rec["ms_p90"],
+        "hbm_gbps": rec["hbm_gbps"],
+        "hbm_pct_of_peak": 100.0 * rec["hbm_frac_of_peak"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": ("decode append + " if app is not None else "") +
+            "workload": ("decode append + " if st.app is not None else "") +
                         "20-layer CSA2 decode stack over one shared FP4 (E2M1 + %s) global "
                         "KV cache: batch 4, context 131072, 16 q heads / 1 KV head, head_dim "
                         "128, indexer dim 64, Full pool 8192 then %s, "
@@ -545,33 +696,42 @@ def main():
                                                else "the pages' 1 Full / 4 Reindex / 15 Reuse",
                                                sp.k),
             "kv_scales": "E8M0/32" if args.kv == "fp4" else "E4M3/16",
-            "batch": B, "context": T, "layers": L,
+            "batch": B, "context": sp.t_cap, "layers": sp.n_layers,
             "schedule": "".join("FIU"[m] for m in sp.schedule),
             "k": sp.k, "pool": sp.pool, "window": sp.window,
             "cache_copies_rotated": args.copies,
-            "append": app is not None,
+            "append": st.app is not None,
             "launch": "recorded stack replayed as a HIP graph (csa2_stack_plan_launch)"
                       if args.graph else "host launches (csa2_stack_run)",
         },
-        "step_algorithmic_bytes": step_bytes,
-        "step_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
-        "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "wall_s_timed_region": wall,
-        "roofline": {
-            "kernel": "k_score_dense<1> (layer-0 Full indexer scan)",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBPS,
-            "traffic": traffic_from_profile(B * T),
-            "launch_ms": scan_ms,
-            "algorithmic_bytes_per_launch": scan_bytes,
-        },
+        "dtype_note": "FP4 storage (E2M1 codes + block scales), dequantised exactly to bf16 "
+                      "MFMA operands, fp32 accumulation, bf16 output",
+        "step_algorithmic_bytes": rec["step_algorithmic_bytes"],
+        "roofline": roofline,
+        "kernels": kern,
+        "wall_s_timed_region": tm.wall,
     }
+    x3 = st.x
+    del st
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        extra = {}
+        for cid, key in ((1, "config1_single_layer_b1_t2048_bf16"),
+                         (2, "config2_single_layer_b8_t32768_fp4"),
+                         (4, "config4_blockwise_b1_t1048576_fp4")):
+            print("extra workload %d ..." % cid, file=sys.stderr, flush=True)
+            extra[key] = extra_decode(cid, args.steps, args.warmup,
+                                      0 if args.no_cpu_baseline else 3.0)
+        print("extra workload 5 ...", file=sys.stderr, flush=True)
+        prec, px, psp = bench_prefill_run(args.steps, args.warmup)
+        if not args.no_cpu_baseline:
+            prec["cpu_baseline"] = cpu_baseline_prefill(px, psp, 4.0)
+        prec["workload"] = psp.name
+        extra["config5_prefill_q4096_t131072_fp4"] = prec
+        result["extra_workloads"] = extra
     if not args.no_cpu_baseline:
         print("timing the oracle on the host ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline()
+        result["cpu_baseline"] = cpu_baseline_stack(sp, x3, 10.0)
     print(json.dumps(result), flush=True)
 
 

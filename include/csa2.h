@@ -247,9 +247,12 @@ csa2_status csa2_prefill_topk(const csa2_cache *cache, int32_t seq, const uint16
  * padded with -1 when fewer than k can be chosen.  When out2 != NULL the
  * first k2 >= k under the same order are also written to out2 [nq][k2]
  * (the Full layer's candidate pool, Fig. 5).  n <= 2^24.  ws: at least the
- * size returned by csa2_topk_workspace (may be 0); it holds counters that
- * reset themselves, so it must be zero-filled before its first use, every
- * call leaves it zero-filled, and calls sharing a workspace must not overlap. */
+ * size returned by csa2_topk_workspace (may be 0).  Rows longer than 32768
+ * slots keep per-row counters in fixed records at the start of ws (max(nq, 64)
+ * of them, addressed by row index only) that every call leaves zero, so a
+ * workspace zero-filled once serves any later calls with nq <= 64 (any n, k,
+ * k2), or with the same nq; zero-fill it again before a call with a
+ * different nq above 64.  Calls sharing a workspace must not overlap. */
 csa2_status csa2_topk(const float *scores, int32_t nq, int64_t n, int64_t ld, const int32_t *ids,
                       int32_t k, int32_t *out, int32_t k2, int32_t *out2, void *ws,
                       size_t ws_bytes, void *stream);
@@ -272,9 +275,11 @@ csa2_status csa2_expand_blocks(const int32_t *blocks, int32_t nq, int32_t nb, in
  * all gets zeros.  q_seq may be NULL (query i reads sequence i).  nq <= 65535.
  * ws: at least csa2_sparse_attn_workspace bytes: 0 when one workgroup covers
  * a query (k <= 256 and window <= 32, or nq >= 64, where each query gets one
- * workgroup of its own); otherwise it holds per-chunk partials and per-query
- * counters that reset themselves, so it must be zero-filled before its first
- * use and calls sharing it must not overlap. */
+ * workgroup of its own); otherwise a fixed 16 KiB block of per-query counters
+ * (at the start, addressed by query index only, left zero by every call)
+ * followed by per-chunk partials.  It must be zero-filled before its first
+ * use; after that it serves calls of any shape.  Calls sharing it must not
+ * overlap. */
 csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, const int32_t *q_pos,
                              const int32_t *q_seq, int32_t nq, const int32_t *sel, int32_t k,
                              const csa2_local *local, float sm_scale, uint16_t *out, void *ws,
@@ -328,10 +333,17 @@ typedef struct {
     const uint16_t *append_kidx;
     const uint16_t *const *append_k;   /* host [n_layers], or NULL */
     const uint16_t *const *append_v;   /* host [n_layers], or NULL */
+    void *const *attn_events;          /* optional timing hook: NULL, or a host array of
+                                          2 * n_layers hipEvent_t the caller created (with
+                                          timing); csa2_stack_run stores the start and end of
+                                          layer l's attention kernel (its own times) in
+                                          entries 2l and 2l + 1.  Ignored by a plan */
 } csa2_stack_desc;
 
-/* Workspace of csa2_stack_run; like the top-k workspace it must be
- * zero-filled before its first use and is left zero-filled by every run. */
+/* Workspace of csa2_stack_run.  Its counters sit at the start at offsets
+ * that depend only on n_seq (and on nothing up to 64 sequences) and every run
+ * leaves them zero: zero-fill the workspace before its first use, and again
+ * only before reusing it for a stack with a different n_seq above 64. */
 csa2_status csa2_stack_workspace(const csa2_stack_desc *desc, size_t *bytes);
 /* Run every layer in order on `stream`.  Validates the schedule: layer 0 must
  * be Full and Reindex needs pool > 0; k <= pool when pool > 0; with block > 1,
@@ -377,8 +389,9 @@ csa2_status csa2_stack_plan_destroy(csa2_stack_plan *plan);
  *   q [l] -> bf16 [n][16][128]; q_idx [l] -> bf16 [n][64] (unused on Reuse);
  *   out [l] -> bf16 [n][16][128]; sel_out NULL or [l] -> int32 [n][k];
  *   pool_out NULL or int32 [n][pool].  1 <= n <= 65535.
- * Workspace rules as csa2_stack_workspace (zero-filled before first use, left
- * zero; calls sharing one must not overlap).  A Full layer with block 1, no
+ * Workspace rules as csa2_stack_workspace, with n in place of n_seq
+ * (zero-filled before first use; again before a different n above 64; calls
+ * sharing one must not overlap).  A Full layer with block 1, no
  * pool, k <= 2048 and t_cap <= 2^18 uses the fused top-k of
  * csa2_prefill_topk; otherwise the segment's score rows are materialised
  * (n * t_cap floats of workspace). */

@@ -40,7 +40,7 @@ class csa2_stack_desc(ctypes.Structure):
                 ("local", ctypes.POINTER(csa2_local)), ("out", ctypes.POINTER(_P)),
                 ("sel_out", ctypes.POINTER(_P)), ("pool_out", _P), ("scan_events", _P * 2),
                 ("append_kv", _P), ("append_kidx", _P), ("append_k", ctypes.POINTER(_P)),
-                ("append_v", ctypes.POINTER(_P))]
+                ("append_v", ctypes.POINTER(_P)), ("attn_events", ctypes.POINTER(_P))]
 
 
 class csa2_replay_desc(ctypes.Structure):
@@ -320,17 +320,26 @@ def prefill_topk(cache: Cache, seq: int, q_idx: torch.Tensor, q_pos: torch.Tenso
     return out
 
 
-def topk(scores: torch.Tensor, k: int, ids: Optional[torch.Tensor] = None, k2: int = 0):
-    """Returns (out [nq][k], out2 [nq][k2] or None); positions ascending, -1 padded."""
+def topk_workspace(nq: int, n: int, k: int, k2: int = 0) -> int:
+    ws_n = _sz()
+    _check("csa2_topk_workspace", lib().csa2_topk_workspace(nq, n, k, k2, ctypes.byref(ws_n)))
+    return ws_n.value
+
+
+def topk(scores: torch.Tensor, k: int, ids: Optional[torch.Tensor] = None, k2: int = 0,
+         ws: Optional[torch.Tensor] = None):
+    """Returns (out [nq][k], out2 [nq][k2] or None); positions ascending, -1 padded.
+    ``ws``: an optional workspace (zero-filled before its first use; see
+    csa2_topk for when it may be reused)."""
     nq, n = int(scores.shape[0]), int(scores.shape[1])
     out = torch.empty((nq, k), dtype=torch.int32, device=scores.device)
     out2 = torch.empty((nq, k2), dtype=torch.int32, device=scores.device) if k2 else None
-    ws_n = _sz()
-    _check("csa2_topk_workspace", lib().csa2_topk_workspace(nq, n, k, k2, ctypes.byref(ws_n)))
-    ws = torch.zeros(max(ws_n.value, 1), dtype=torch.uint8, device=scores.device)
+    need = topk_workspace(nq, n, k, k2)
+    if ws is None:
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=scores.device)
     _check("csa2_topk", lib().csa2_topk(_ptr(scores), nq, n, int(scores.stride(0)),
                                         _ptr(_i32t(ids)), k, _ptr(out), k2, _ptr(out2), _ptr(ws),
-                                        ws_n.value, _stream()))
+                                        ws.numel(), _stream()))
     return out, out2
 
 
@@ -373,7 +382,8 @@ class _StackArgs:
                  q: Sequence[torch.Tensor], q_idx: Sequence[Optional[torch.Tensor]],
                  local: Sequence[Local], out: Sequence[torch.Tensor], k: int, pool: int,
                  block: int, sm_scale: float, sel_out: Optional[Sequence[torch.Tensor]],
-                 pool_out: Optional[torch.Tensor], scan_events=None, append=None):
+                 pool_out: Optional[torch.Tensor], scan_events=None, append=None,
+                 attn_events=None):
         L = len(modes)
         self.refs = (cache, q_pos, list(q), list(q_idx), list(local), list(out), sel_out, pool_out,
                      append)
@@ -402,6 +412,12 @@ class _StackArgs:
                                         for t in vn])
                 self.desc.append_k = self.app_k
                 self.desc.append_v = self.app_v
+        if attn_events is not None:
+            if len(attn_events) != 2 * L:
+                raise ValueError("attn_events: two events per layer")
+            self.attn_ev = (_P * (2 * L))(*[(e.value if isinstance(e, ctypes.c_void_p) else e)
+                                            if e is not None else None for e in attn_events])
+            self.desc.attn_events = self.attn_ev
 
 
 def stack_workspace(args: _StackArgs) -> int:
@@ -416,12 +432,14 @@ def stack_run(cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
               local: Sequence[Local], k: int, pool: int = 0, block: int = 1,
               sm_scale: float = HEAD_DIM ** -0.5, want_sel: bool = True,
               ws: Optional[torch.Tensor] = None, out: Optional[Sequence[torch.Tensor]] = None,
-              scan_events=None, append=None):
+              scan_events=None, append=None, attn_events=None):
     """Run a decoder stack (one decode query per sequence).
 
     Returns (out list of bf16 [n_seq][16][128], sel list or None, pool or None).
     ``scan_events``: optional pair of ``torch.cuda.Event(enable_timing=True)``
-    recorded around layer 0's indexer scan.  ``append``: optional
+    recorded around layer 0's indexer scan; ``attn_events``: optional list of
+    2 * n_layers such events (or None to skip a layer), receiving the start
+    and end of each layer's attention kernel.  ``append``: optional
     ``(kv, kidx, k_new, v_new)`` written at q_pos before layer 0 (the decode
     append of csa2_append; kidx may be None, k_new / v_new None or one bf16
     [n_seq][128] tensor (or None) per layer).
@@ -435,8 +453,11 @@ def stack_run(cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
     ev = None
     if scan_events is not None:
         ev = tuple(ctypes.c_void_p(e.cuda_event) for e in scan_events)
+    aev = None
+    if attn_events is not None:
+        aev = [ctypes.c_void_p(e.cuda_event) if e is not None else None for e in attn_events]
     args = _StackArgs(cache, modes, q_pos, q, q_idx, local, out, k, pool, block, sm_scale, sel,
-                      pool_out, ev, append)
+                      pool_out, ev, append, aev)
     need = stack_workspace(args)
     if ws is None or ws.numel() < need:
         ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)

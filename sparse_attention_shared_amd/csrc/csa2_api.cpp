@@ -151,11 +151,15 @@ hipError_t enqueue_append(const CacheView& cv, int32_t rows, int32_t seq, const 
     return hipSuccess;
 }
 
-// Workspace of one stack run: scores, block scores / block ids, pool scores,
-// pool, the current selection, per-sequence counters, top-k and attention
-// scratch.  Counters reset themselves: the workspace must start zero-filled.
+// Workspace of one stack run.  The regions holding self-resetting counters
+// come first, at offsets that depend on the number of queries alone (and not
+// at all up to 64 queries): the attention counters, the Reindex select
+// counters and the top-k row records; then the scratch regions (scores,
+// block scores / block ids, pool scores, pool, the current selection,
+// attention partials, replay sequence ids and fused top-k scratch), which no
+// call needs cleared.
 struct StackWs {
-    size_t scores, bscores, blocks, pscores, pool, sel0, ctr, topk, attn, qseq, pf, total;
+    size_t actr, ctr, topk, scores, bscores, blocks, pscores, pool, sel0, attn, qseq, pf, total;
 };
 
 // Whether a Full layer of a one-sequence segment takes the fused prefill top-k
@@ -178,18 +182,19 @@ StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, i
     const int64_t nb = block > 1 ? (t_cap + block - 1) / block : 0;
     const int32_t nbsel = block > 1 ? pool / block : 0;
     const bool fused = replay && replay_fused_full(t_cap, k, pool, block);
+    w.actr = take(kAttnCtrBytes);
+    w.ctr = take((size_t)std::max(n_seq, kManyQueries) * kCtrStride * sizeof(uint32_t));
+    size_t tk = topk_ws_bytes(n_seq, t_cap, k, pool);
+    if (block > 1) tk = std::max(tk, topk_ws_bytes(n_seq, nb, nbsel, 0));
+    if (pool > 0) tk = std::max(tk, topk_ws_bytes(n_seq, pool, k, 0));
+    w.topk = take(tk > 0 ? tk : 1);
     w.scores = take(fused ? 1 : (size_t)n_seq * t_cap * sizeof(float));
     w.bscores = take((size_t)n_seq * (nb > 0 ? nb : 1) * sizeof(float));
     w.blocks = take((size_t)n_seq * (nbsel > 0 ? nbsel : 1) * sizeof(int32_t));
     w.pscores = take((size_t)n_seq * score_select_ld(pool > 0 ? pool : 1) * sizeof(float));
     w.pool = take((size_t)n_seq * (pool > 0 ? pool : 1) * sizeof(int32_t));
     w.sel0 = take((size_t)n_seq * k * sizeof(int32_t));
-    w.ctr = take((size_t)n_seq * kCtrStride * sizeof(uint32_t));
-    size_t tk = topk_ws_bytes(n_seq, t_cap, k, pool);
-    if (block > 1) tk = std::max(tk, topk_ws_bytes(n_seq, nb, nbsel, 0));
-    if (pool > 0) tk = std::max(tk, topk_ws_bytes(n_seq, pool, k, 0));
-    w.topk = take(tk > 0 ? tk : 1);
-    w.attn = take(attn_ws_bytes(n_seq, k, max_window));
+    w.attn = take(std::max<size_t>(attn_part_bytes(n_seq, k, max_window), 1));
     if (replay) {
         w.qseq = take((size_t)n_seq * sizeof(int32_t));
         if (fused) w.pf = take(prefill_topk_ws_bytes(n_seq, t_cap));
@@ -197,7 +202,6 @@ StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, i
     w.total = off;
     return w;
 }
-
 }  // namespace
 
 extern "C" {
@@ -414,6 +418,7 @@ struct StackJob {
     int32_t* const* sel_out;
     int32_t* pool_out;
     void* const* scan_events;  // [2] or null (decode only)
+    void* const* attn_events;  // [2 n_layers] or null (decode only)
     const uint16_t* app_kv;
     const uint16_t* app_kidx;
     const uint16_t* const* app_k;
@@ -472,6 +477,7 @@ static StackJob decode_job(const csa2_stack_desc* d) {
     j.sel_out = d->sel_out;
     j.pool_out = d->pool_out;
     j.scan_events = d->scan_events;
+    j.attn_events = d->attn_events;
     j.app_kv = d->append_kv;
     j.app_kidx = d->append_kidx;
     j.app_k = d->append_k;
@@ -562,7 +568,8 @@ static csa2_status enqueue_stack(const StackJob& j, const CacheView& cv, const S
     int32_t* selbuf = reinterpret_cast<int32_t*>(base + W.sel0);
     uint32_t* ctr = reinterpret_cast<uint32_t*>(base + W.ctr);
     void* tkws = base + W.topk;
-    void* atws = base + W.attn;
+    uint32_t* actr = reinterpret_cast<uint32_t*>(base + W.actr);
+    float* apart = reinterpret_cast<float*>(base + W.attn);
     const bool replay = j.seq >= 0;
     // decode: query b reads sequence b; replay: the ids the append step writes
     int32_t* q_seq = replay ? reinterpret_cast<int32_t*>(base + W.qseq) : nullptr;
@@ -634,8 +641,17 @@ static csa2_status enqueue_stack(const StackJob& j, const CacheView& cv, const S
         if (e != hipSuccess) return CSA2_ERR_HIP;
         LocalView lv;
         check_local(&j.local[l], &lv);
-        e = launch_sparse_attn(cv, j.q[l], j.q_pos, q_seq, S, cur, k, lv, j.sm_scale, j.out[l],
-                               atws, s);
+        hipEvent_t a0 = nullptr, a1 = nullptr;
+        if (j.attn_events && j.attn_events[2 * l] && j.attn_events[2 * l + 1]) {
+            hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(s, &cap) != hipSuccess) return CSA2_ERR_HIP;
+            if (cap == hipStreamCaptureStatusNone) {  // a plan ignores them
+                a0 = (hipEvent_t)j.attn_events[2 * l];
+                a1 = (hipEvent_t)j.attn_events[2 * l + 1];
+            }
+        }
+        e = launch_sparse_attn_parts(cv, j.q[l], j.q_pos, q_seq, S, cur, k, lv, j.sm_scale,
+                                     j.out[l], actr, apart, s, a0, a1);
         if (e != hipSuccess) return CSA2_ERR_HIP;
     }
     return CSA2_OK;

@@ -127,7 +127,20 @@ constexpr int32_t kManyQueries = 64;
 // Per-query arrival counters sit 256 bytes apart, so the workgroups of
 // different queries never contend for one cache line.
 constexpr int64_t kCtrStride = 64;
-size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window);
+// The split form's workspace: a fixed block of per-query counters (one for
+// each query a split call can have), then the per-chunk partials.  The
+// counters' addresses depend on nothing but the query index, so a workspace
+// serves calls of any shape without being cleared again (every call leaves
+// its counters zero).
+constexpr size_t kAttnCtrBytes = (size_t)kManyQueries * kCtrStride * sizeof(uint32_t);
+size_t attn_part_bytes(int32_t nq, int32_t k, int32_t window);
+size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window);  // 0, or kAttnCtrBytes + partials
+// ctr: kAttnCtrBytes (zero, left zero); part: attn_part_bytes.
+hipError_t launch_sparse_attn_parts(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
+                                    const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,
+                                    const LocalView& loc, float sm_scale, uint16_t* out,
+                                    uint32_t* ctr, float* part, hipStream_t s,
+                                    hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
                               const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,
                               const LocalView& loc, float sm_scale, uint16_t* out, void* ws,

@@ -25,6 +25,8 @@
 // to the workspace and the last chunk to finish (a per-query counter)
 // combines all of them in chunk order, so results do not depend on
 // scheduling.
+#include <hip/hip_ext.h>
+
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
 
@@ -845,43 +847,59 @@ static int32_t attn_chunks(int32_t k, int32_t window) {
     return std::max(std::max((k + kWgEntries - 1) / kWgEntries, (window + kBlk - 1) / kBlk), 1);
 }
 
-size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window) {
+size_t attn_part_bytes(int32_t nq, int32_t k, int32_t window) {
     const int64_t nc = attn_chunks(k, window);
     if (nc <= 1 || nq >= kManyQueries) return 0;
-    return (size_t)nq * nc * kHeads * (kHeadDim + 2) * sizeof(float) + (size_t)nq * kCtrStride * sizeof(uint32_t);
+    return (size_t)nq * nc * kHeads * (kHeadDim + 2) * sizeof(float);
+}
+
+size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window) {
+    const size_t part = attn_part_bytes(nq, k, window);
+    return part ? kAttnCtrBytes + part : 0;
 }
 
 hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
                               const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,
                               const LocalView& loc, float sm_scale, uint16_t* out, void* ws,
                               hipStream_t s) {
+    char* base = static_cast<char*>(ws);
+    return launch_sparse_attn_parts(c, q, q_pos, q_seq, nq, sel, k, loc, sm_scale, out,
+                                    reinterpret_cast<uint32_t*>(base),
+                                    base ? reinterpret_cast<float*>(base + kAttnCtrBytes) : nullptr, s);
+}
+
+hipError_t launch_sparse_attn_parts(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
+                                    const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,
+                                    const LocalView& loc, float sm_scale, uint16_t* out,
+                                    uint32_t* ctr, float* part, hipStream_t s, hipEvent_t ev0,
+                                    hipEvent_t ev1) {
     if (nq == 0) return hipSuccess;
     if (nq >= kManyQueries) {  // enough queries to fill the GPU one workgroup each
         const bool few = nq < 256;  // fewer queries than CUs
         if (c.fp4 == 2 && few)
-            hipLaunchKernelGGL((k_attn_loop<1, kLWFew>), dim3((uint32_t)nq), dim3(kLWFew * 64), 0, s, c, q,
+            hipExtLaunchKernelGGL((k_attn_loop<1, kLWFew>), dim3((uint32_t)nq), dim3(kLWFew * 64), 0, s, ev0, ev1, 0, c, q,
                                q_pos, q_seq, sel, k, loc, sm_scale, out);
         else if (c.fp4 == 2)
-            hipLaunchKernelGGL((k_attn_loop<1, kLW>), dim3((uint32_t)nq), dim3(kLW * 64), 0, s, c, q, q_pos,
+            hipExtLaunchKernelGGL((k_attn_loop<1, kLW>), dim3((uint32_t)nq), dim3(kLW * 64), 0, s, ev0, ev1, 0, c, q, q_pos,
                                q_seq, sel, k, loc, sm_scale, out);
         else if (few)
-            hipLaunchKernelGGL((k_attn_loop<0, kLWFew>), dim3((uint32_t)nq), dim3(kLWFew * 64), 0, s, c, q,
+            hipExtLaunchKernelGGL((k_attn_loop<0, kLWFew>), dim3((uint32_t)nq), dim3(kLWFew * 64), 0, s, ev0, ev1, 0, c, q,
                                q_pos, q_seq, sel, k, loc, sm_scale, out);
         else
-            hipLaunchKernelGGL((k_attn_loop<0, kLW>), dim3((uint32_t)nq), dim3(kLW * 64), 0, s, c, q, q_pos,
+            hipExtLaunchKernelGGL((k_attn_loop<0, kLW>), dim3((uint32_t)nq), dim3(kLW * 64), 0, s, ev0, ev1, 0, c, q, q_pos,
                                q_seq, sel, k, loc, sm_scale, out);
         return hipGetLastError();
     }
     int32_t nc = attn_chunks(k, loc.window);
     if (nc < 1) nc = 1;
-    float* ws_o = static_cast<float*>(ws);
+    float* ws_o = nc > 1 ? part : nullptr;
     float* ws_ml = nc > 1 ? ws_o + (size_t)nq * nc * kHeads * kHeadDim : nullptr;
-    uint32_t* ctr = nc > 1 ? reinterpret_cast<uint32_t*>(ws_ml + (size_t)nq * nc * kHeads * 2) : nullptr;
+    if (nc <= 1) ctr = nullptr;
     if (c.fp4 == 2)
-        hipLaunchKernelGGL(k_attn_chunk<1>, dim3((uint32_t)nc, (uint32_t)nq), dim3(kThreads), 0, s, c,
+        hipExtLaunchKernelGGL(k_attn_chunk<1>, dim3((uint32_t)nc, (uint32_t)nq), dim3(kThreads), 0, s, ev0, ev1, 0, c,
                            q, q_pos, q_seq, sel, k, loc, sm_scale, nc, ws_o, ws_ml, ctr, out);
     else
-        hipLaunchKernelGGL(k_attn_chunk<0>, dim3((uint32_t)nc, (uint32_t)nq), dim3(kThreads), 0, s, c,
+        hipExtLaunchKernelGGL(k_attn_chunk<0>, dim3((uint32_t)nc, (uint32_t)nq), dim3(kThreads), 0, s, ev0, ev1, 0, c,
                            q, q_pos, q_seq, sel, k, loc, sm_scale, nc, ws_o, ws_ml, ctr, out);
     return hipGetLastError();
 }

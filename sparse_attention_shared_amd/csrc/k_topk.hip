@@ -25,6 +25,8 @@
 // launches, chunks then one workgroup per row.
 // The workspace's counters and histogram reset themselves, so it must be
 // zero-filled before its first use and is left zero-filled by every call.
+#include <algorithm>
+
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
 #include "csa2_select.h"
@@ -414,10 +416,19 @@ __global__ __launch_bounds__(kLongNT) void k_topk_keep(const float* __restrict__
 
 static int32_t long_chunks(int64_t n) { return (int32_t)((n + kChunk - 1) / kChunk); }
 
+// Row records first, at least kMinRowStates of them, so their addresses
+// depend only on the row index: a workspace cleared once serves calls of any
+// row length with up to kMinRowStates rows (each call leaves its records
+// zero); the chunks' kept keys follow, as scratch.
+constexpr int32_t kMinRowStates = 64;
+static size_t row_state_bytes(int32_t nq) {
+    return (size_t)std::max(nq, kMinRowStates) * sizeof(RowState);
+}
+
 size_t topk_ws_bytes(int32_t nq, int64_t n, int32_t, int32_t) {
     if (n <= kSmallMax) return 0;
     const size_t nc = (size_t)long_chunks(n);
-    return (size_t)nq * (sizeof(RowState) + nc * kChunk * sizeof(Cand) + nc * sizeof(int32_t)) + 256;
+    return row_state_bytes(nq) + (size_t)nq * (nc * kChunk * sizeof(Cand) + nc * sizeof(int32_t)) + 256;
 }
 
 hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, const int32_t* ids,
@@ -439,7 +450,7 @@ hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, c
     char* base = static_cast<char*>(ws);
     LongWs w;
     w.st = reinterpret_cast<RowState*>(base);
-    w.keep = reinterpret_cast<Cand*>(base + (size_t)nq * sizeof(RowState));
+    w.keep = reinterpret_cast<Cand*>(base + row_state_bytes(nq));
     w.nkeep = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(w.keep) +
                                          (size_t)nq * nc * kChunk * sizeof(Cand));
     const int32_t kk2 = out2 ? k2 : 0;

@@ -11,6 +11,9 @@ Rules (parity bar):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import torch
 
@@ -97,3 +100,15 @@ def attn_check(gpu_out: np.ndarray, ref: np.ndarray, what=""):
     bad = err > ATOL + RTOL * np.abs(ref)
     assert not bad.any(), "%s: %d bad, max abs err %.3g" % (what, int(bad.sum()), err.max())
     return float(err.max())
+
+
+def par_map(fn, items):
+    """fn over items on one thread per available core (the oracle's C calls
+    release the GIL); results in order, the first exception re-raised."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    n = max(1, min(16, n))
+    with cf.ThreadPoolExecutor(max_workers=n) as ex:
+        return list(ex.map(fn, items))

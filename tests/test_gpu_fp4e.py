@@ -139,3 +139,40 @@ def test_replay_on_e4m3_cache():
     lk, lv = _rings_after(sp, x, 0, k_new, v_new)
     err = check_replay(sp, x, 0, outs, sels, pl, lk, lv, range(n))
     log("replay e4m3 max abs err", err)
+
+
+def test_page_configuration_full_size():
+    """The pages' own configuration at the 20-layer workload's full size: FP4
+    with E4M3 per 16, top-512, SWA 128, the 1 Full / 4 Reindex / 15 Reuse
+    schedule, batch 4 at 131072 tokens with an 8192-position pool, and the
+    decode append of every sequence's position; every layer of every
+    sequence through the cascade."""
+    base = synth.config(3)
+    sp = synth.Spec(**{**base.__dict__, "name": "page configuration", "kv_format": "fp4e",
+                       "k": 512, "schedule": synth.page_schedule_20(), "seed": 1013})
+    log("page configuration:", sp.n_seq, "x", sp.t_cap)
+    x = synth.make_inputs(sp)
+    d = DevInputs(x)
+    rng = np.random.default_rng(1014)
+    f = synth.f32_to_bf16_bits
+    L, S = sp.n_layers, sp.n_seq
+    kv_new = f(rng.standard_normal((S, 256)).astype(np.float32))
+    kidx_new = f(rng.standard_normal((S, 64)).astype(np.float32))
+    k_new = f(rng.standard_normal((L, S, 128)).astype(np.float32))
+    v_new = f(rng.standard_normal((L, S, 128)).astype(np.float32))
+    outs, sels, pool = csa2.stack_run(
+        d.cache, list(sp.schedule), d.q_pos, d.q,
+        [d.q_idx[l] if sp.schedule[l] != synth.REUSE else None for l in range(L)],
+        d.local, sp.k, sp.pool, sp.block,
+        append=(dev16(kv_new), dev16(kidx_new), [dev16(k_new[l]) for l in range(L)],
+                [dev16(v_new[l]) for l in range(L)]))
+    torch.cuda.synchronize()
+    kv2, ki2, lk2, lv2 = oracle.append(x.kv, x.k_idx, x.local_k, x.local_v, x.q_pos, kv_new,
+                                       kidx_new, k_new, v_new)
+    bi = np.arange(S)
+    t = x.q_pos.astype(np.int64)
+    oc, os_ = oracle.fp4e_pack(kv2[bi, t])
+    assert np.array_equal(host(d.codes)[bi, t], oc) and np.array_equal(host(d.scales)[bi, t], os_)
+    x2 = synth.Inputs(sp, kv2, ki2, x.q, x.q_idx, lk2, lv2, x.q_pos, x.q_seq, x.needle_pos)
+    err = check_stack(sp, x2, d, outs, sels, pool)
+    log("page configuration full size max abs err", err)

@@ -1,8 +1,8 @@
 """GPU parity of the prefill-chunk indexer (MFMA scores and the fused top-k
 that never writes the score rows) against the oracle: ragged query tiles, rows
 shorter than k, rows whose candidate list overflows (the exact recompute
-path), exact ties, and the 4096-query workload at full size on sampled
-queries."""
+path), exact ties, and the 4096-query workload at full size (every query's
+selection and output)."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +10,7 @@ import torch
 import oracle
 import synth
 import sparse_attention_shared_amd as csa2
-from gpu_util import DevInputs, attn_check, boundary_check, dev16, dev32, host
+from gpu_util import DevInputs, attn_check, boundary_check, dev16, dev32, host, par_map
 
 pytestmark = pytest.mark.gpu
 
@@ -117,8 +117,10 @@ def test_prefill_topk_exact_ties():
         assert chosen == [int(v) for v in ref if v >= 0], "row %d differs from the oracle" % i
 
 
-def test_prefill_workload_full_size_sampled():
-    """The 4096-query prefill chunk: fused top-k then attention, as timed."""
+def test_prefill_workload_full_size_all_queries():
+    """The 4096-query prefill chunk, fused top-k then attention as timed: every
+    query's selection against the oracle's ranking and every query's output
+    against the oracle's attention on that selection."""
     sp = synth.config(5)
     log("workload 5", sp.name)
     x = synth.make_inputs(sp)
@@ -129,14 +131,23 @@ def test_prefill_workload_full_size_sampled():
     torch.cuda.synchronize()
     gsel = host(sel)
     gout = host(out)
-    sample = np.unique(np.concatenate([[0, 1, 63, 64, nq - 1],
-                                       np.random.default_rng(5).choice(nq, 27)]))
-    for i in sample:
-        t = sp.q_pos[i]
-        s = oracle.scores(x.q_idx[0, i], x.k_idx[0, :t + 1])
-        boundary_check(gsel[i], np.arange(t + 1, dtype=np.int32), s, sp.k, "prefill q%d" % i)
+    tiles = range(0, nq, 64)
+
+    def rows(i0):
+        for i in range(i0, min(i0 + 64, nq)):
+            t = sp.q_pos[i]
+            s = oracle.scores(x.q_idx[0, i], x.k_idx[0, :t + 1])
+            boundary_check(gsel[i], np.arange(t + 1, dtype=np.int32), s, sp.k, "prefill q%d" % i)
+
+    par_map(rows, tiles)
+    log("prefill: all %d selections checked" % nq)
     c = oracle.Cache(x.kv, x.k_idx, fp4=True)
-    ref = oracle.attend(c, x.q_pos[sample], x.q_seq[sample], x.q[0, sample], gsel[sample],
-                        x.local_k[0], x.local_v[0], sp.window, sp.lo)
-    err = attn_check(gout[sample], ref, "prefill attention")
-    log("prefill sampled max abs err", err)
+
+    def att(i0):
+        sl = slice(i0, min(i0 + 64, nq))
+        ref = oracle.attend(c, x.q_pos[sl], x.q_seq[sl], x.q[0, sl], gsel[sl], x.local_k[0],
+                            x.local_v[0], sp.window, sp.lo)
+        return attn_check(gout[sl], ref, "prefill attention q%d.." % i0)
+
+    err = max(par_map(att, tiles))
+    log("prefill all %d queries max abs err" % nq, err)
