@@ -60,7 +60,8 @@ typedef enum {
     CSA2_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the size query returned */
     CSA2_ERR_UNSUPPORTED = 5, /* current device is not gfx950 */
     CSA2_ERR_NO_DEVICE = 6,   /* no HIP device visible */
-    CSA2_ERR_HIP = 7          /* the HIP runtime refused a launch */
+    CSA2_ERR_HIP = 7,         /* the HIP runtime refused a launch */
+    CSA2_ERR_TOO_LARGE = 8    /* beyond the fixed scratch of csa2_sparse_attn_noalloc */
 } csa2_status;
 
 typedef enum { CSA2_MODE_FULL = 0, CSA2_MODE_REINDEX = 1, CSA2_MODE_REUSE = 2 } csa2_mode;
@@ -285,6 +286,25 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, const i
                              const csa2_local *local, float sm_scale, uint16_t *out, void *ws,
                              size_t ws_bytes, void *stream);
 csa2_status csa2_sparse_attn_workspace(int32_t nq, int32_t k, int32_t window, size_t *bytes);
+
+/* csa2_sparse_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation).  It allocates nothing and calls no allocating
+ * routine: the split form's counters and partials live in one fixed device
+ * array per GPU inside the library (4 MiB + 16 KiB, held until the process
+ * ends), whose counters each call clears with a small kernel on `stream`
+ * before using them.  Same arguments, results and rules as csa2_sparse_attn
+ * otherwise (bit-identical outputs).  Limit: the partials of nq queries times
+ * chunks-per-query must fit 4 MiB -- nq * max(ceil(k / 256), ceil(window /
+ * 32)) <= 504 when nq < 64 (e.g. 63 queries at k = 2048, window 128); from 64
+ * queries on no scratch is used and any size is accepted.  Larger calls
+ * return CSA2_ERR_TOO_LARGE and enqueue nothing.  Every call on a GPU shares
+ * its array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. */
+csa2_status csa2_sparse_attn_noalloc(const csa2_cache *cache, const uint16_t *q,
+                                     const int32_t *q_pos, const int32_t *q_seq, int32_t nq,
+                                     const int32_t *sel, int32_t k, const csa2_local *local,
+                                     float sm_scale, uint16_t *out, void *stream);
 
 /* ------------------------------------------------------------ layer stack */
 

@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_sparse_attn.argtypes = [ctypes.POINTER(csa2_cache), _P, _P, _P, _i32, _P, _i32,
                                        ctypes.POINTER(csa2_local), _f32, _P, _P, _sz, _P]
         L.csa2_sparse_attn_workspace.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_sz)]
+        L.csa2_sparse_attn_noalloc.argtypes = [ctypes.POINTER(csa2_cache), _P, _P, _P, _i32, _P,
+                                               _i32, ctypes.POINTER(csa2_local), _f32, _P, _P]
         L.csa2_stack_workspace.argtypes = [ctypes.POINTER(csa2_stack_desc), ctypes.POINTER(_sz)]
         L.csa2_stack_run.argtypes = [ctypes.POINTER(csa2_stack_desc), _P, _sz, _P]
         L.csa2_stack_plan_create.argtypes = [ctypes.POINTER(csa2_stack_desc), _P, _sz,
@@ -104,6 +106,7 @@ def lib() -> ctypes.CDLL:
                   "csa2_append", "csa2_compress", "csa2_index_score", "csa2_prefill_score",
                   "csa2_prefill_topk", "csa2_prefill_topk_workspace", "csa2_topk",
                   "csa2_topk_workspace", "csa2_expand_blocks", "csa2_sparse_attn",
+                  "csa2_sparse_attn_noalloc",
                   "csa2_sparse_attn_workspace", "csa2_stack_workspace", "csa2_stack_run",
                   "csa2_stack_plan_create", "csa2_stack_plan_launch", "csa2_stack_plan_destroy",
                   "csa2_replay_workspace", "csa2_replay_run"):
@@ -372,6 +375,22 @@ def sparse_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, q_seq: Optio
         ctypes.byref(cache.c), _ptr(_bits16(q)), _ptr(_i32t(q_pos)), _ptr(_i32t(q_seq)), nq,
         _ptr(_i32t(sel)), k, ctypes.byref(local.c), float(sm_scale), _ptr(out), _ptr(ws),
         ws.numel() if ws is not None else 0, _stream()))
+    return out
+
+
+def sparse_attn_noalloc(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor,
+                        q_seq: Optional[torch.Tensor], sel: torch.Tensor, local: Local,
+                        sm_scale: float = HEAD_DIM ** -0.5,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """csa2_sparse_attn_noalloc: the same attention without a workspace (the
+    library's fixed per-GPU scratch; calls on one GPU must not overlap)."""
+    nq = int(q_pos.shape[0])
+    k = int(sel.shape[1]) if sel is not None else 0
+    if out is None:
+        out = torch.empty((nq, HEADS, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    _check("csa2_sparse_attn_noalloc", lib().csa2_sparse_attn_noalloc(
+        ctypes.byref(cache.c), _ptr(_bits16(q)), _ptr(_i32t(q_pos)), _ptr(_i32t(q_seq)), nq,
+        _ptr(_i32t(sel)), k, ctypes.byref(local.c), float(sm_scale), _ptr(out), _stream()))
     return out
 
 

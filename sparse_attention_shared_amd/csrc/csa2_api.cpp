@@ -218,6 +218,7 @@ const char* csa2_status_str(csa2_status s) {
         case CSA2_ERR_UNSUPPORTED: return "device is not gfx950";
         case CSA2_ERR_NO_DEVICE: return "no HIP device";
         case CSA2_ERR_HIP: return "HIP launch error";
+        case CSA2_ERR_TOO_LARGE: return "call larger than the allocation-free scratch";
     }
     return "unknown status";
 }
@@ -399,6 +400,24 @@ csa2_status csa2_sparse_attn(const csa2_cache* cache, const uint16_t* q, const i
     if (csa2_status st = device_ok()) return st;
     return from_hip(launch_sparse_attn(cv, q, q_pos, q_seq, nq, sel, k, lv, sm_scale, out, ws,
                                        (hipStream_t)stream));
+}
+
+csa2_status csa2_sparse_attn_noalloc(const csa2_cache* cache, const uint16_t* q,
+                                     const int32_t* q_pos, const int32_t* q_seq, int32_t nq,
+                                     const int32_t* sel, int32_t k, const csa2_local* local,
+                                     float sm_scale, uint16_t* out, void* stream) {
+    CacheView cv;
+    LocalView lv;
+    if (csa2_status st = check_cache(cache, true, false, &cv)) return st;
+    if (csa2_status st = check_local(local, &lv)) return st;
+    if (nq < 0 || k < 0 || nq > 65535) return CSA2_ERR_SHAPE;
+    if (nq > 0 && (!q || !q_pos || !out || !aligned16(q))) return CSA2_ERR_INVALID_ARG;
+    if (nq > 0 && k > 0 && !sel) return CSA2_ERR_INVALID_ARG;
+    if (attn_part_bytes(nq, k, lv.window) > kStaticScratchBytes - kAttnCtrBytes)
+        return CSA2_ERR_TOO_LARGE;
+    if (csa2_status st = device_ok()) return st;
+    return from_hip(launch_sparse_attn_static(cv, q, q_pos, q_seq, nq, sel, k, lv, sm_scale, out,
+                                              (hipStream_t)stream));
 }
 
 // What one stack run needs, from a decode descriptor (one query per

@@ -141,6 +141,14 @@ hipError_t launch_sparse_attn_parts(const CacheView& c, const uint16_t* q, const
                                     const LocalView& loc, float sm_scale, uint16_t* out,
                                     uint32_t* ctr, float* part, hipStream_t s,
                                     hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+// The allocation-free form: counters and partials in a fixed device array of
+// kStaticScratchBytes (partials of up to 504 query-chunks, e.g. 63 queries of
+// 8 chunks); a larger call returns hipErrorInvalidValue.
+constexpr size_t kStaticScratchBytes = kAttnCtrBytes + ((size_t)4 << 20);
+hipError_t launch_sparse_attn_static(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
+                                     const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,
+                                     const LocalView& loc, float sm_scale, uint16_t* out,
+                                     hipStream_t s);
 hipError_t launch_sparse_attn(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
                               const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,
                               const LocalView& loc, float sm_scale, uint16_t* out, void* ws,

@@ -27,6 +27,8 @@
 // scheduling.
 #include <hip/hip_ext.h>
 
+#include <atomic>
+
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
 
@@ -902,6 +904,63 @@ hipError_t launch_sparse_attn_parts(const CacheView& c, const uint16_t* q, const
         hipExtLaunchKernelGGL(k_attn_chunk<0>, dim3((uint32_t)nc, (uint32_t)nq), dim3(kThreads), 0, s, ev0, ev1, 0, c,
                            q, q_pos, q_seq, sel, k, loc, sm_scale, nc, ws_o, ws_ml, ctr, out);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free form (for callers that cannot allocate: code under graph
+// capture, serving loops): the split kernel's counters and partials live in
+// one file-scope device array per GPU, held until the process ends.  Its
+// address is looked up once per device with hipGetSymbolAddress (the array's
+// name in host code is not a device address) and passed to the kernels like
+// a caller's workspace.  Every call on a GPU uses the same array, so calls
+// that overlap on one GPU race.
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+
+// The scratch array's device address on the current device.
+hipError_t scratch_ptr(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+// Zero n words (a kernel, so that a captured graph holds no memset node).
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* __restrict__ p, int32_t n) {
+    const int32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_sparse_attn_static(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
+                                     const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,
+                                     const LocalView& loc, float sm_scale, uint16_t* out,
+                                     hipStream_t s) {
+    if (attn_part_bytes(nq, k, loc.window) > kStaticScratchBytes - kAttnCtrBytes)
+        return hipErrorInvalidValue;  // the caller checks this first
+    void* base = nullptr;
+    if (hipError_t e = scratch_ptr(&base)) return e;
+    uint32_t* ctr = static_cast<uint32_t*>(base);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(base) + kAttnCtrBytes);
+    if (attn_part_bytes(nq, k, loc.window) > 0) {
+        // the counters must start at zero whatever an earlier call left
+        constexpr int32_t nw = (int32_t)(kAttnCtrBytes / sizeof(uint32_t));
+        hipLaunchKernelGGL(k_zero_words, dim3((nw + 255) / 256), dim3(256), 0, s, ctr, nw);
+        if (hipError_t e = hipGetLastError()) return e;
+    }
+    return launch_sparse_attn_parts(c, q, q_pos, q_seq, nq, sel, k, loc, sm_scale, out, ctr, part, s);
 }
 
 }  // namespace csa2

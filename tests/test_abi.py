@@ -13,7 +13,7 @@ from sparse_attention_shared_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, INVALID, SHAPE, SCHEDULE, WORKSPACE, UNSUPPORTED, NO_DEVICE, HIP = range(8)
+OK, INVALID, SHAPE, SCHEDULE, WORKSPACE, UNSUPPORTED, NO_DEVICE, HIP, TOO_LARGE = range(9)
 
 
 def declared_functions():
@@ -38,8 +38,8 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings():
     L = csa2.lib()
-    for s in range(8):
-        assert L.csa2_status_str(s)
+    for s in range(9):
+        assert L.csa2_status_str(s) and L.csa2_status_str(s) != b"unknown status"
     assert L.csa2_status_str(99) == b"unknown status"
 
 
@@ -316,3 +316,26 @@ def test_compression_rate_validation():
     assert L.csa2_compress(FAKE, -1, 2, 256, FAKE, None) == SHAPE
     assert L.csa2_compress(None, 4, 2, 256, FAKE, None) == INVALID
     assert L.csa2_compress(FAKE_ODD, 4, 2, 256, FAKE, None) == INVALID
+
+
+def test_noalloc_attention_limit():
+    """The allocation-free attention refuses, before any device work, calls
+    whose partials exceed its fixed 4 MiB: nq * chunks <= 504 below 64
+    queries, any size from 64 queries on (no scratch is used)."""
+    L = csa2.lib()
+    c = _cache(n_seq=64, t_cap=5000)
+    loc = _lib.csa2_local(FAKE, FAKE, 128, 128, 0)
+    bp = ctypes.byref
+    # 63 queries x 16 chunks (k = 4096) = 1008 > 504
+    assert L.csa2_sparse_attn_noalloc(bp(c), FAKE, FAKE, None, 63, FAKE, 4096, bp(loc), 0.1,
+                                      FAKE, None) == TOO_LARGE
+    # 63 queries x 8 chunks fits; so does any call from 64 queries on
+    for nq, k in ((63, 2048), (64, 4096), (2, 2048)):
+        st = L.csa2_sparse_attn_noalloc(bp(c), FAKE, FAKE, None, nq, FAKE, k, bp(loc), 0.1, FAKE,
+                                        None)
+        assert st in (OK, NO_DEVICE) and st != TOO_LARGE
+        if not torch.cuda.is_available():
+            assert st == NO_DEVICE
+    # the usual validation comes first
+    assert L.csa2_sparse_attn_noalloc(bp(c), None, FAKE, None, 2, FAKE, 8, bp(loc), 0.1, FAKE,
+                                      None) == INVALID
