@@ -317,34 +317,30 @@ class DecodeSetup:
 
 
 def time_decode(setup, steps, warmup, kernel_events=True, graph=False):
-    """Times `steps` decode steps after `warmup`; returns (Timer, attention
-    launch durations in ms, scan durations in ms)."""
+    """Times `steps` decode steps after `warmup` (the value: no event inside a
+    step), then, with kernel_events, the same number of steps again in which
+    each step times the scan and ONE layer's attention launch (layer i % L at
+    step i) with the kernel's own start and end events.  Bracketing a launch
+    makes that launch ~1 us slower and costs the host ~20 us (every launch of
+    a step bracketed left the GPU waiting for the host: 0.68 vs 0.30 ms), so
+    the timed steps carry none.  Returns (Timer, attention launch durations
+    in ms, scan durations in ms, Timer of the kernel-timing steps or None)."""
     import torch
     import sparse_attention_shared_amd as csa2
     sp = setup.sp
     L = sp.n_layers
     tm = Timer(steps)
-    attn_ms, scan_ms = [], []
+    attn_ms, scan_ms, tk = [], [], None
+
+    def one_layer(i):
+        e = [None] * (2 * L)
+        e[2 * (i % L)], e[2 * (i % L) + 1] = _events(2)
+        return e
+
     if not graph:
-        # each step times the scan and ONE layer's attention launch (layer
-        # i % L at step i): bracketing a launch with events costs the host
-        # ~20 us, and every launch of a step bracketed leaves the GPU waiting
-        # for the host (measured 0.68 vs 0.30 ms per step)
-        def one_layer(i):
-            e = [None] * (2 * L)
-            e[2 * (i % L)], e[2 * (i % L) + 1] = _events(2)
-            return e
-        aev = [one_layer(i) for i in range(steps)] if kernel_events else None
-        sev = [_events(2) for _ in range(steps)] if kernel_events else None
         for i in range(warmup):
             setup.step(i)
-        torch.cuda.synchronize()
-        tm.run(lambda i: setup.step(i, sev[i] if sev else None, aev[i] if aev else None), steps)
-        if kernel_events:
-            for i in range(steps):
-                l = i % L
-                attn_ms.append(aev[i][2 * l].elapsed_time(aev[i][2 * l + 1]))
-                scan_ms.append(sev[i][0].elapsed_time(sev[i][1]))
+        tm.run(setup.step, steps)
     else:
         plans = [csa2.StackPlan(c, sp.schedule, setup.q_pos, setup.q, setup.q_idx, setup.local,
                                 sp.k, sp.pool, sp.block, out=setup.out, append=setup.app)
@@ -354,19 +350,19 @@ def time_decode(setup, steps, warmup, kernel_events=True, graph=False):
         tm.run(lambda i: plans[i % len(plans)].launch(), steps)
         for pl in plans:
             pl.close()
-        if kernel_events:
-            # events inside a graph do not bracket its kernels: the kernels
-            # are timed on host-launched steps of the same stack afterwards
-            n = min(steps, 40)
-            aev = [_events(2 * L) for _ in range(n)]
-            sev = [_events(2) for _ in range(n)]
-            for i in range(n):
-                setup.step(i, sev[i], aev[i])
-            torch.cuda.synchronize()
-            for i in range(n):
-                attn_ms += [aev[i][2 * l].elapsed_time(aev[i][2 * l + 1]) for l in range(L)]
-                scan_ms.append(sev[i][0].elapsed_time(sev[i][1]))
-    return tm, attn_ms, scan_ms
+    if kernel_events:
+        # events recorded inside a graph do not bracket its kernels, so the
+        # kernels are always timed on host-launched steps of the same stack
+        n = max(steps, L)
+        aev = [one_layer(i) for i in range(n)]
+        sev = [_events(2) for _ in range(n)]
+        tk = Timer(n)
+        tk.run(lambda i: setup.step(i, sev[i], aev[i]), n)
+        for i in range(n):
+            l = i % L
+            attn_ms.append(aev[i][2 * l].elapsed_time(aev[i][2 * l + 1]))
+            scan_ms.append(sev[i][0].elapsed_time(sev[i][1]))
+    return tm, attn_ms, scan_ms, tk
 
 
 def decode_record(setup, tm, attn_ms, scan_ms, row):
@@ -475,7 +471,7 @@ def extra_decode(cid, steps, warmup, oracle_budget):
     sp = synth.config(cid)
     row = {"bf16": 512, "fp4": 136, "fp4e": 144}[sp.kv_format]
     st = DecodeSetup(sp, copies=2 if cid == 4 else 4, append=False)
-    tm, attn_ms, scan_ms = time_decode(st, steps, warmup)
+    tm, attn_ms, scan_ms, _ = time_decode(st, steps, warmup)
     rec = decode_record(st, tm, attn_ms, scan_ms, row)
     rec["unit"] = "tokens/s"
     rec["workload"] = sp.name
@@ -649,8 +645,9 @@ def main():
     row = 136 if args.kv == "fp4" else 144
     print("generating inputs ...", file=sys.stderr, flush=True)
     st = DecodeSetup(sp, args.copies, not args.no_append)
-    tm, attn_ms, scan_ms = time_decode(st, args.steps, args.warmup,
-                                       kernel_events=not args.no_kernel_events, graph=args.graph)
+    tm, attn_ms, scan_ms, tk = time_decode(st, args.steps, args.warmup,
+                                           kernel_events=not args.no_kernel_events,
+                                           graph=args.graph)
     rec = decode_record(st, tm, attn_ms, scan_ms, row)
     B = sp.n_seq
     kern = rec.pop("kernels")
@@ -669,6 +666,9 @@ def main():
             "launch_ms": kk["launch_ms_mean"],
             "algorithmic_bytes_per_launch": kk["algorithmic_bytes_per_launch"],
             "share_of_step": kk["ms_per_step"] / rec["ms_per_step"],
+            "timing": "kernel's own start/end events on one bracketed launch per step, over "
+                      "%d steps right after the timed ones (their step: %.4f ms)" % (
+                          len(attn_ms), tk.ms),
         }
     result = {
         "metric": METRIC,

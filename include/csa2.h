@@ -87,8 +87,9 @@ typedef enum { CSA2_KV_BF16 = 0, CSA2_KV_FP4 = 1, CSA2_KV_FP4_E4M3 = 2 } csa2_kv
  * decoder's cache); 2 — entry j combines positions 2j and 2j + 1 (the
  * encoder's rate; see csa2_compress), and a query at position t reads only
  * entries whose whole group is at or before t, i.e. j <= (t + 1) / 2 - 1.
- * q_pos arguments stay token positions (the window reads positions).  The
- * prefill calls and the replay take m <= 1 only (CSA2_ERR_UNSUPPORTED). */
+ * q_pos arguments stay token positions (the window reads positions); every
+ * call, the prefill-chunk calls and the bounded replay included, applies
+ * that entry bound. */
 typedef struct {
     int32_t format;           /* csa2_kv_format */
     int32_t n_seq;
@@ -215,8 +216,9 @@ csa2_status csa2_index_score(const csa2_cache *cache, const uint16_t *q_idx, con
 /* Dense indexer scores of a prefill chunk: nq queries, all on sequence `seq`,
  * each at its own position q_pos[i] ("CED...", "Why Prefill Recomputes a
  * Recent Segment", Fig. 6: the recent positions pass through the decoder
- * again; each one selects like a decode query).  scores[i][t] for t < t_cap,
- * -inf for t > q_pos[i].  The product Q_I K_I^T runs on MFMA (bf16 in, fp32
+ * again; each one selects like a decode query).  scores[i][t] for entries
+ * t < t_cap, -inf past the query's last readable entry (t > q_pos[i] when
+ * m <= 1; t > (q_pos[i] + 1) / 2 - 1 when m = 2).  The product Q_I K_I^T runs on MFMA (bf16 in, fp32
  * accumulation); q_idx: bf16 [nq][64]; scores: float, row stride ld_scores
  * >= t_cap. */
 csa2_status csa2_prefill_score(const csa2_cache *cache, int32_t seq, const uint16_t *q_idx,
@@ -226,8 +228,9 @@ csa2_status csa2_prefill_score(const csa2_cache *cache, int32_t seq, const uint1
 /* Indexer top-k of a prefill chunk ("CED...", "Why Prefill Recomputes a
  * Recent Segment", Fig. 6, with the selection of "Selecting Positions and
  * Reading Values with Attention", Fig. 4): nq queries on sequence `seq`, query
- * i at position q_pos[i], choose the k positions p <= q_pos[i] with the largest
- * q_idx[i] . k_idx[seq][p] (ties: lower position first), written ascending to
+ * i at position q_pos[i], choose the k entries p it may read (p <= q_pos[i], or
+ * with m = 2 p <= (q_pos[i] + 1) / 2 - 1) with the largest
+ * q_idx[i] . k_idx[seq][p] (ties: lower entry first), written ascending to
  * sel[i][0..k), -1 padded.  The same selection as csa2_index_score followed by
  * csa2_topk on each row, computed without materialising the score rows: the
  * product runs on MFMA and only a candidate superset of the top-k is kept.

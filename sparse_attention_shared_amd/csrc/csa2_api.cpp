@@ -318,7 +318,6 @@ csa2_status csa2_prefill_score(const csa2_cache* cache, int32_t seq, const uint1
                                void* stream) {
     CacheView cv;
     if (csa2_status st = check_cache(cache, false, true, &cv)) return st;
-    if (cv.msh) return CSA2_ERR_UNSUPPORTED;  // prefill kernels read one position per entry
     if (nq < 0 || seq < 0 || seq >= cv.n_seq || ld_scores < cv.t_cap) return CSA2_ERR_SHAPE;
     if (nq > 65535 * 64) return CSA2_ERR_SHAPE;
     if (nq > 0 && (!q_idx || !q_pos || !scores || !aligned16(q_idx))) return CSA2_ERR_INVALID_ARG;
@@ -338,7 +337,6 @@ csa2_status csa2_prefill_topk(const csa2_cache* cache, int32_t seq, const uint16
                               size_t ws_bytes, void* stream) {
     CacheView cv;
     if (csa2_status st = check_cache(cache, false, true, &cv)) return st;
-    if (cv.msh) return CSA2_ERR_UNSUPPORTED;
     if (nq < 0 || seq < 0 || seq >= cv.n_seq || k < 1 || k > kPfMaxK || cv.t_cap > kPfMaxT)
         return CSA2_ERR_SHAPE;
     if (nq == 0) return CSA2_OK;
@@ -545,7 +543,6 @@ static csa2_status check_replay(const csa2_replay_desc* d, CacheView* cv, int32_
         return CSA2_ERR_INVALID_ARG;
     if (d->n_layers <= 0) return CSA2_ERR_SHAPE;
     if (csa2_status st = check_cache(d->cache, true, true, cv)) return st;
-    if (cv->msh) return CSA2_ERR_UNSUPPORTED;
     if (d->seq < 0 || d->seq >= cv->n_seq) return CSA2_ERR_SHAPE;
     if (d->n <= 0 || d->n > 65535) return CSA2_ERR_SHAPE;
     return check_job(replay_job(d), max_window);

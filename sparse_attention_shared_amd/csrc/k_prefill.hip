@@ -45,6 +45,13 @@ __device__ __forceinline__ int64_t pf_clamp_pos(int64_t p, int64_t t_cap) {
     return p < 0 ? -1 : (p >= t_cap ? t_cap - 1 : p);
 }
 
+// The last entry a query at position p may read: an entry of 2^msh positions
+// counts once its whole group is at or before p (msh 0: the position itself);
+// -1 for a negative position.  Every kernel below works on entries.
+__device__ __forceinline__ int64_t pf_last_entry(int64_t p, int32_t msh) {
+    return p < 0 ? -1 : ((p + 1) >> msh) - 1;
+}
+
 // Query fragments of the tile's kPfQ queries (B operand): lane column n16 of
 // block i is query q0 + 16 i + n16, dims 32 kb + 8 g .. + 8.
 __device__ __forceinline__ void pf_load_q(const uint16_t* __restrict__ q_idx, int32_t nq,
@@ -87,7 +94,7 @@ __device__ __forceinline__ pf_f32x4 pf_tile(const pf_bf16x8 (&kf)[2], const pf_b
 // largest and smallest of them over the tile (wave-uniform).  The loads are
 // unconditional (index clamped to nq - 1), so all of them are in flight at once.
 __device__ __forceinline__ void pf_tile_pos(const int32_t* __restrict__ q_pos, int32_t nq,
-                                            int64_t t_cap, int64_t q0, int n16,
+                                            int64_t t_cap, int32_t msh, int64_t q0, int n16,
                                             int32_t (&pos)[kPfQB], int32_t& tmax, int32_t& tmin) {
     int32_t raw[kPfQB];
 #pragma unroll
@@ -100,7 +107,7 @@ __device__ __forceinline__ void pf_tile_pos(const int32_t* __restrict__ q_pos, i
 #pragma unroll
     for (int i = 0; i < kPfQB; ++i) {
         const int64_t qq = q0 + 16 * i + n16;
-        pos[i] = qq < nq ? (int32_t)pf_clamp_pos(raw[i], t_cap) : -1;
+        pos[i] = qq < nq ? (int32_t)pf_clamp_pos(pf_last_entry(raw[i], msh), t_cap) : -1;
         tmax = max(tmax, pos[i]);
         tmin = min(tmin, pos[i]);
     }
@@ -210,7 +217,8 @@ __device__ __forceinline__ void pf_tile_frag(const uint32_t* buf, int n16, int g
 __global__ __launch_bounds__(256) void k_pf_cmax(const uint16_t* __restrict__ kseq, int32_t t_cap,
                                                  const uint16_t* __restrict__ q_idx,
                                                  const int32_t* __restrict__ q_pos, int32_t nq,
-                                                 uint32_t* __restrict__ cmax, int64_t ldc) {
+                                                 int32_t msh, uint32_t* __restrict__ cmax,
+                                                 int64_t ldc) {
     __shared__ uint32_t tile[2][kPfTileWords];
     __shared__ int32_t wmax[4];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(256) void k_pf_cmax(const uint16_t* __restrict__ ks
     const int64_t q0 = (int64_t)blockIdx.x * kPfWQ + wave * kPfQ;  // this wave's queries
     const int32_t span0 = (int32_t)blockIdx.y * (kPfCStride * kPfCSteps);
     int32_t tmax, tmin, pos[kPfQB];
-    pf_tile_pos(q_pos, nq, t_cap, min(q0, (int64_t)nq - 1), n16, pos, tmax, tmin);
+    pf_tile_pos(q_pos, nq, t_cap, msh, min(q0, (int64_t)nq - 1), n16, pos, tmax, tmin);
     if (q0 >= nq) tmax = -1;  // a wave past the last query computes nothing
     if (lane == 0) wmax[wave] = tmax;
     __syncthreads();
@@ -310,14 +318,14 @@ struct PfThrLds {
 // grid nq, 256 threads, dynamic LDS ldc keys.
 __global__ __launch_bounds__(256) void k_pf_thresh(const uint32_t* __restrict__ cmax, int64_t ldc,
                                                    const int32_t* __restrict__ q_pos,
-                                                   int64_t t_cap, int32_t k,
+                                                   int32_t msh, int64_t t_cap, int32_t k,
                                                    float* __restrict__ thr_f,
                                                    uint32_t* __restrict__ thr_k,
                                                    uint32_t* __restrict__ cnt) {
     extern __shared__ uint32_t pf_keys[];
     __shared__ PfThrLds sh;
     const int q = blockIdx.x, tid = threadIdx.x;
-    const int64_t t = pf_clamp_pos(q_pos[q], t_cap);
+    const int64_t t = pf_clamp_pos(pf_last_entry(q_pos[q], msh), t_cap);
     const int64_t nc = pf_nchunks(t);
     const int32_t m = pf_sample_rank(k);
     uint32_t thr = 1u;  // fewer sampled chunks than m: every valid position is a candidate
@@ -408,7 +416,7 @@ __device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int 
 __global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ kseq, int32_t t_cap,
                                                    const uint16_t* __restrict__ q_idx,
                                                    const int32_t* __restrict__ q_pos, int32_t nq,
-                                                   const float* __restrict__ thr_f,
+                                                   int32_t msh, const float* __restrict__ thr_f,
                                                    const uint32_t* __restrict__ thr_k,
                                                    uint32_t* __restrict__ cnt,
                                                    uint2* __restrict__ cand, int32_t cap) {
@@ -419,11 +427,11 @@ __global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ 
     const int64_t q0 = (int64_t)blockIdx.x * kPfQ;
     const int32_t span0 = (int32_t)blockIdx.y * kPfFiltSpan;
     int32_t tmax, tmin, pos[kPfQB];
-    pf_tile_pos(q_pos, nq, t_cap, q0, n16, pos, tmax, tmin);
+    pf_tile_pos(q_pos, nq, t_cap, msh, q0, n16, pos, tmax, tmin);
     if (span0 > tmax) return;  // uniform over the workgroup
     if (tid < kPfQ) {
         const int64_t qq = q0 + tid;
-        sh.pos[tid] = qq < nq ? (int32_t)pf_clamp_pos(q_pos[qq], t_cap) : -1;
+        sh.pos[tid] = qq < nq ? (int32_t)pf_clamp_pos(pf_last_entry(q_pos[qq], msh), t_cap) : -1;
         sh.thr[tid] = qq < nq ? thr_k[qq] : 0xFFFFFFFFu;
         sh.n[tid] = 0;
     }
@@ -570,14 +578,15 @@ __global__ __launch_bounds__(kPfSelNT) void k_pf_select(const uint16_t* __restri
                                                         int64_t t_cap,
                                                         const uint16_t* __restrict__ q_idx,
                                                         const int32_t* __restrict__ q_pos,
-                                                        int32_t k, const uint32_t* __restrict__ cnt,
+                                                        int32_t msh, int32_t k,
+                                                        const uint32_t* __restrict__ cnt,
                                                         const uint2* __restrict__ cand, int32_t cap,
                                                         int32_t* __restrict__ sel) {
     extern __shared__ uint32_t pf_bits[];
     __shared__ PfSelLds sh;
     const int q = blockIdx.x, tid = threadIdx.x;
     int32_t* dst = sel + (int64_t)q * k;
-    const int64_t t = pf_clamp_pos(q_pos[q], t_cap);
+    const int64_t t = pf_clamp_pos(pf_last_entry(q_pos[q], msh), t_cap);
     if (t < 0) {
         for (int i = tid; i < k; i += kPfSelNT) dst[i] = -1;
         return;
@@ -669,7 +678,8 @@ __global__ __launch_bounds__(kPfSelNT) void k_pf_select(const uint16_t* __restri
 __global__ __launch_bounds__(256) void k_score_mq(const uint16_t* __restrict__ kseq, int64_t t_cap,
                                                   const uint16_t* __restrict__ q_idx,
                                                   const int32_t* __restrict__ q_pos, int32_t nq,
-                                                  float* __restrict__ scores, int64_t ld) {
+                                                  int32_t msh, float* __restrict__ scores,
+                                                  int64_t ld) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n16 = lane & 15, g = lane >> 4;
     const int64_t q0 = (int64_t)blockIdx.y * 64;
@@ -680,7 +690,7 @@ __global__ __launch_bounds__(256) void k_score_mq(const uint16_t* __restrict__ k
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t qq = q0 + 16 * i + n16;
-        const int64_t p = qq < nq ? q_pos[qq] : -1;
+        const int64_t p = qq < nq ? pf_last_entry(q_pos[qq], msh) : -1;
         tmax = p > tmax ? p : tmax;
     }
 #pragma unroll
@@ -710,7 +720,7 @@ __global__ __launch_bounds__(256) void k_score_mq(const uint16_t* __restrict__ k
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t qr = q0 + 16 * i + 4 * g + r;
-            pos[i][r] = qr < nq ? q_pos[qr] : -1;
+            pos[i][r] = qr < nq ? (int32_t)pf_last_entry(q_pos[qr], msh) : -1;
         }
     }
 #pragma unroll
@@ -748,8 +758,8 @@ hipError_t launch_score_mq(const CacheView& c, int32_t seq, const uint16_t* q_id
     if (nq == 0) return hipSuccess;
     const uint16_t* kseq = c.k_idx + (int64_t)seq * c.t_cap * kIdxDim;
     dim3 grid((uint32_t)((c.t_cap + 255) / 256), (uint32_t)((nq + 63) / 64));
-    hipLaunchKernelGGL(k_score_mq, grid, dim3(256), 0, s, kseq, c.t_cap, q_idx, q_pos, nq, scores,
-                       ld);
+    hipLaunchKernelGGL(k_score_mq, grid, dim3(256), 0, s, kseq, c.t_cap, q_idx, q_pos, nq, c.msh,
+                       scores, ld);
     return hipGetLastError();
 }
 
@@ -778,16 +788,16 @@ hipError_t launch_prefill_topk(const CacheView& c, int32_t seq, const uint16_t* 
     const uint16_t* kseq = c.k_idx + (int64_t)seq * c.t_cap * kIdxDim;
     const dim3 grid((uint32_t)((nq + kPfWQ - 1) / kPfWQ),
                     (uint32_t)((c.t_cap + kPfCStride * kPfCSteps - 1) / (kPfCStride * kPfCSteps)));
-    hipLaunchKernelGGL(k_pf_cmax, grid, dim3(256), 0, s, kseq, (int32_t)c.t_cap, q_idx, q_pos, nq, cmax,
-                       ldc);
+    hipLaunchKernelGGL(k_pf_cmax, grid, dim3(256), 0, s, kseq, (int32_t)c.t_cap, q_idx, q_pos, nq, c.msh,
+                       cmax, ldc);
     hipLaunchKernelGGL(k_pf_thresh, dim3(nq), dim3(256), (size_t)ldc * 4, s, cmax, ldc, q_pos,
-                       c.t_cap, k, thr_f, thr_k, cnt);
+                       c.msh, c.t_cap, k, thr_f, thr_k, cnt);
     const dim3 fgrid((uint32_t)((nq + kPfQ - 1) / kPfQ), (uint32_t)((c.t_cap + kPfFiltSpan - 1) / kPfFiltSpan));
-    hipLaunchKernelGGL(k_pf_filter, fgrid, dim3(256), 0, s, kseq, (int32_t)c.t_cap, q_idx, q_pos, nq, thr_f,
-                       thr_k, cnt, cand, kPfCap);
+    hipLaunchKernelGGL(k_pf_filter, fgrid, dim3(256), 0, s, kseq, (int32_t)c.t_cap, q_idx, q_pos, nq, c.msh,
+                       thr_f, thr_k, cnt, cand, kPfCap);
     const size_t nw = (size_t)((c.t_cap + 31) / 32);
     hipLaunchKernelGGL(k_pf_select, dim3(nq), dim3(kPfSelNT), nw * 4 + nw * 2, s, kseq, c.t_cap,
-                       q_idx, q_pos, k, cnt, cand, kPfCap, sel);
+                       q_idx, q_pos, c.msh, k, cnt, cand, kPfCap, sel);
     return hipGetLastError();
 }
 

@@ -1,8 +1,9 @@
 """GPU parity of sequence compression ("CED", section "What Does the Sequence
 Compression Rate Reduce?"): csa2_compress bit-exact against the oracle's mean
 of pairs, and a cache of m = 2 entries through attention, the decode stack
-(scan, pool, Reindex, blockwise) and the append, against the oracle with the
-same rate (a query reads only entries whose whole group is at or before it)."""
+(scan, pool, Reindex, blockwise), the append, the prefill-chunk scores and
+top-k and the bounded replay, against the oracle with the same rate (a query
+reads only entries whose whole group is at or before it)."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +11,7 @@ import torch
 import oracle
 import synth
 import sparse_attention_shared_amd as csa2
-from gpu_util import attn_check, dev16, dev32, host
+from gpu_util import DevInputs, attn_check, boundary_check, dev16, dev32, host
 from test_gpu_parity import check_stack
 
 pytestmark = pytest.mark.gpu
@@ -137,3 +138,70 @@ def test_append_writes_an_entry_when_a_group_completes():
     lk = x.local_k[0].copy()
     lk[np.arange(3), pos % 16] = k_new[0]
     assert np.array_equal(host(local.k), lk)
+
+
+def _m2_prefill_case(T_pos, nq, seed, extra):
+    rng = np.random.default_rng(seed)
+    pos = np.concatenate([np.asarray(extra, np.int64), rng.integers(0, T_pos, nq - len(extra))])
+    sp = synth.Spec("m2-prefill", n_seq=1, t_cap=T_pos, q_pos=[int(p) for p in pos],
+                    q_seq=[0] * nq, kv_format="fp4", k=8, window=8, local_cap=16, seed=seed)
+    return _m2_inputs(sp)
+
+
+def test_prefill_score_and_topk_on_compressed_cache():
+    """The prefill-chunk calls on m = 2 entries: even and odd positions, the
+    first two positions (no complete group at 0), rows shorter than k."""
+    T_pos, nq, k = 2 * 20000, 70, 512
+    extra = [0, 1, 2, 3, 2 * k - 2, 2 * k - 1, 2 * k, 20001, 20002, T_pos - 2, T_pos - 1]
+    x, xe, cache, _ = _m2_prefill_case(T_pos, nq, 23, extra)
+    q_idx, q_pos = dev16(x.q_idx[0]), dev32(x.q_pos)
+    sc = host(csa2.prefill_score(cache, 0, q_idx, q_pos))
+    g = host(csa2.prefill_topk(cache, 0, q_idx, q_pos, k))
+    torch.cuda.synchronize()
+    k64 = (xe.k_idx[0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    q64 = (x.q_idx[0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for i, p in enumerate(x.q_pos):
+        te = (int(p) + 1) // 2 - 1  # the last complete entry
+        assert np.all(np.isneginf(sc[i, te + 1:])), "row %d: entries past %d must be -inf" % (i, te)
+        if te < 0:
+            assert (g[i] == -1).all(), "row %d: no complete entry, nothing selected" % i
+            continue
+        ref = oracle.scores(x.q_idx[0, i], xe.k_idx[0, :te + 1]).astype(np.float64)
+        bound = 64 * 2.0 ** -24 * np.abs(k64[:te + 1] * q64[i]).sum(axis=1) + 2.0 ** -24 * np.abs(ref)
+        assert np.all(np.abs(sc[i, :te + 1] - ref) <= bound), "row %d scores" % i
+        boundary_check(g[i], np.arange(te + 1, dtype=np.int32), ref.astype(np.float32), k,
+                       "m=2 prefill q%d t=%d" % (i, p))
+
+
+@pytest.mark.parametrize("schedule,pool", [("repeat", 256), ("full", 0)])
+def test_replay_on_compressed_cache(schedule, pool):
+    """The bounded replay over m = 2 entries: materialised Full rows with a
+    pool and Reindex, and the fused Full top-k; the window reads positions."""
+    from test_gpu_replay import _rings_after, check_replay
+    n, T_pos = 70, 2 * 3000
+    sched = (synth.repeating_schedule(6) if schedule == "repeat"
+             else [synth.FULL, synth.REUSE, synth.FULL])
+    sp = synth.Spec("m2-replay", n_seq=2, t_cap=T_pos, q_pos=list(range(T_pos - n, T_pos)),
+                    q_seq=[1] * n, kv_format="fp4", k=64, window=32, pool=pool, schedule=sched,
+                    local_cap=128, lo=T_pos - n, seed=29)
+    x, xe, cache, _ = _m2_inputs(sp)
+    L = sp.n_layers
+    rng = np.random.default_rng(30)
+    f = synth.f32_to_bf16_bits
+    k_new = f(rng.standard_normal((L, n, 128)).astype(np.float32))
+    v_new = f(rng.standard_normal((L, n, 128)).astype(np.float32))
+    local = [csa2.Local(dev16(x.local_k[l]), dev16(x.local_v[l]), sp.window, sp.lo) for l in range(L)]
+    outs, sels, pl = csa2.replay_run(cache, list(sched), 1, dev32(x.q_pos),
+                                     [dev16(x.q[l]) for l in range(L)],
+                                     [dev16(x.q_idx[l]) if sched[l] != synth.REUSE else None
+                                      for l in range(L)],
+                                     local, sp.k, sp.pool,
+                                     local_k=[dev16(k_new[l]) for l in range(L)],
+                                     local_v=[dev16(v_new[l]) for l in range(L)])
+    torch.cuda.synchronize()
+    lk, lv = _rings_after(sp, x, 1, k_new, v_new)
+    for l in range(L):
+        assert np.array_equal(host(local[l].k), lk[l]), "ring K layer %d" % l
+    sp_e = synth.Spec(**{**sp.__dict__, "t_cap": T_pos // 2})
+    err = check_replay(sp_e, xe, 1, outs, sels, pl, lk, lv, range(n), rate=2)
+    log("m=2 replay %s max abs err" % schedule, err)

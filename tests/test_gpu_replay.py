@@ -65,15 +65,17 @@ def _rings_after(sp, x, seq, k_new, v_new):
     return lk, lv
 
 
-def check_replay(sp, x, seq, outs, sels, pool, lk, lv, sample):
-    c = oracle_cache(sp, x.kv, x.k_idx)
+def check_replay(sp, x, seq, outs, sels, pool, lk, lv, sample, rate=1):
+    """With rate > 1, x.kv / x.k_idx hold entries of `rate` positions and a
+    query at t reads entries 0 .. (t + 1) / rate - 1."""
+    c = oracle_cache(sp, x.kv, x.k_idx, rate)
     sels = [host(s) for s in sels]
     outs = [host(o) for o in outs]
     pool = host(pool) if pool is not None else None
     worst = 0.0
     for l, m in enumerate(sp.schedule):
         for i in sample:
-            t = sp.q_pos[i]
+            t = (sp.q_pos[i] + 1) // rate - 1  # the last readable entry
             g = sels[l][i]
             assert np.all(g <= t), "causal"
             if m == synth.REUSE:
