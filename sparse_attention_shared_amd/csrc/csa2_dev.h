@@ -150,14 +150,10 @@ __device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t n) {
     return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
 }
 
-// A lighter hand-off for data that is written and read only through these
-// agent-coherent accesses (agent-scope atomic stores and loads, which write
-// through and re-fetch past the per-XCD L2s): each thread waits for its own
-// stores to complete (hand_off_wait), then after a barrier thread 0 arrives
-// with a relaxed add, so no L2 write-back or invalidate is needed on either
-// side.  Each cache line of the handed-over data is written by one workgroup.
-// Over 16-64 workgroups per group the arrival costs far less than the
-// acquire-release one (0.3 vs 1.8 us at 32).
+// Agent-scope relaxed atomic stores and loads: the data handed over through
+// arrive_last_release is written and read with them (sc1 accesses, which
+// neither leave dirty lines in a per-XCD L2 nor read a stale one); the
+// release and acquire of the arrival order them.
 template <typename T>
 __device__ __forceinline__ void store_coherent(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -168,11 +164,23 @@ __device__ __forceinline__ T load_coherent(const T* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Waits until this thread's memory operations have completed.
 __device__ __forceinline__ void hand_off_wait() { __builtin_amdgcn_s_waitcnt(0); }
 
-__device__ __forceinline__ bool arrive_last_coherent(uint32_t* ctr, uint32_t n) {
-    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+// Last-arrival counter with the release on every arrival and the acquire
+// only where it is needed: each add is a release, so it heads a release
+// sequence (every later add on the counter continues it); the arrival that
+// returns true has read the value of the add before it, so its acquire fence
+// synchronises with every member's release.  Called by thread 0 after a
+// barrier that follows the workgroup's stores; a barrier after the call
+// extends the acquire to the workgroup.
+__device__ __forceinline__ bool arrive_last_release(uint32_t* ctr, uint32_t n) {
+    const bool last =
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return last;
 }
+
 
 // XCD-aware remap of a flat workgroup id: the hardware deals consecutive ids
 // round-robin over the 8 XCDs; this makes each XCD own a contiguous range of

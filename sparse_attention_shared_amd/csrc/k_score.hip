@@ -149,10 +149,11 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint16_t* __restrict__
 // Reindex layers (rescore the Full layer's pool with the layer's own indexer
 // query and keep the top k, "What Full, Reindex, and Reuse Share", Fig. 5).
 // MODE 0, grid (ceil(n_cand / sel_keys<R>()), nq): every workgroup scores
-// sel_keys<R>() candidates into `scores` (handed over with agent-coherent
-// stores); the last one of a query to finish (per-query counter `ctr`, reset on
-// exit) selects the top k of all n_cand <= kSelMaxCand candidates.  For a
-// handful of queries (decode).
+// sel_keys<R>() candidates into `scores` (agent-scope atomic stores, read back
+// with agent-scope atomic loads); every arrival on the per-query counter `ctr`
+// (reset on exit) is a release and the last one, after an acquire fence,
+// selects the top k of all n_cand <= kSelMaxCand candidates.  For a handful of
+// queries (decode).
 // MODE 1, same grid: the scores alone (plain stores); MODE 2, grid (1, nq),
 // launched after it: one workgroup per query selects.  For many queries, where
 // leaving the selections to the last arrivals would pile them onto whichever
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
     if (MODE == 0) {
         hand_off_wait();  // this thread's score stores are complete
         __syncthreads();
-        if (threadIdx.x == 0) last = arrive_last_coherent(&ctr[qi * kCtrStride], gridDim.x);
+        if (threadIdx.x == 0) last = arrive_last_release(&ctr[qi * kCtrStride], gridDim.x);
         __syncthreads();
         if (!last) return;
     }

@@ -116,11 +116,11 @@ __global__ __launch_bounds__(kLongNT) void k_topk_hist(const float* __restrict__
             if (v) atomicAdd(&st->hist[i], (uint32_t)v);
         }
         if (MODE == 1) return;
-        // the row histogram is built and read by device atomics alone, so the
-        // arrival needs no release or acquire: only this thread's adds complete
+        // the row histogram is built and read by device atomics; the
+        // release of every arrival and the acquire of the last order them
         hand_off_wait();
         __syncthreads();
-        if (tid == 0) last = arrive_last_coherent(&st->ctr_hist, (uint32_t)nc);
+        if (tid == 0) last = arrive_last_release(&st->ctr_hist, (uint32_t)nc);
         __syncthreads();
         if (!last) return;
     }
