@@ -106,6 +106,25 @@ __device__ __forceinline__ void row_scales(const uint8_t* sp, int g, uint32_t& s
     }
 }
 
+// The dwords of a row's scales that hold the lane's K and V blocks, loaded
+// as they are (row_scale_bits takes the lane's bits out of them).
+template <int SF>
+__device__ __forceinline__ void row_scale_words(const uint8_t* sp, int g, uint32_t& wk, uint32_t& wv) {
+    if (SF == 0) {
+        const uint2 sc = *reinterpret_cast<const uint2*>(sp);
+        wk = sc.x;
+        wv = sc.y;
+    } else {
+        wk = *reinterpret_cast<const uint32_t*>(sp + 4 * (g >> 1));
+        wv = *reinterpret_cast<const uint32_t*>(sp + 8 + 4 * (g >> 1));
+    }
+}
+
+template <int SF>
+__device__ __forceinline__ uint32_t row_scale_bits(uint32_t w, int g) {
+    return SF ? (w >> (16 * (g & 1))) & 0xFFFFu : (w >> (8 * g)) & 0xFFu;
+}
+
 template <int SF>
 __device__ __forceinline__ DqScale dw_scale(uint32_t bits, int kb) {
     if (SF == 0) return DqScale{e8m0_value(bits), 1.f};
@@ -161,7 +180,7 @@ __device__ __forceinline__ uint32_t dq_pair(uint32_t w, DqScale d, int sel) {
 
 struct RowRaw {  // the FP4 data one lane loads for one entry
     uint4 k, v;
-    uint32_t sk, sv;  // scale bytes of the lane's K and V blocks
+    uint32_t sk, sv;  // scale bits of the lane's K and V blocks, or the dwords holding them
 };
 
 struct AttnLds {
@@ -582,8 +601,7 @@ __global__ __launch_bounds__(LW * 64) void k_attn_loop(CacheView c, const uint16
     // maximum passes it by more than 8, so most tiles skip the rescale and
     // p = 2^(s zs - m_run) stays below 2^8 (exact up to bf16/fp32 rounding:
     // the softmax does not depend on the reference).
-    auto consume = [&](const bf16x8_t (&kf)[2][4], uint64_t vm0, uint64_t vm1) {
-        float sv[2][4];  // raw scores
+    auto scores = [&](const bf16x8_t (&kf)[2][4], float (&sv)[2][4]) {  // raw scores
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             f32x4_t z = {0.f, 0.f, 0.f, 0.f};
@@ -592,6 +610,8 @@ __global__ __launch_bounds__(LW * 64) void k_attn_loop(CacheView c, const uint16
 #pragma unroll
             for (int r = 0; r < 4; ++r) sv[u][r] = z[r];
         }
+    };
+    auto consume = [&](float (&sv)[2][4], uint64_t vm0, uint64_t vm1) {
         if ((vm0 & vm1) != 0xFFFFull) {  // some slot of the tile is empty: -inf
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -654,57 +674,70 @@ __global__ __launch_bounds__(LW * 64) void k_attn_loop(CacheView c, const uint16
     // its codes are finite and its p is 0, so it adds nothing.
     const int32_t t32 = (int32_t)tg;  // entries fit 32 bits (t_cap <= 2^24)
     // Row offsets stay 32-bit (entries < 2^24, so entry * 128 < 2^31) over a
-    // uniform base, which the loads take as scalar base + vector offset.
+    // uniform base, which the loads take as scalar base + vector offset.  The
+    // scale dwords are kept as loaded (sk, sv hold whole words here) and
+    // their bits taken out only when the tile is decoded: touching a load's
+    // result makes the wave wait for it and, the counter being in order, for
+    // every load before it, so doing it here would wait out the prefetch.
     auto fetch = [&](int32_t j, RowRaw& r) {
         const bool ok = j >= 0 && j <= t32;
         const uint32_t jj = ok ? (uint32_t)j : 0u;
         const uint32_t off = jj * (uint32_t)kRowCodes + 16u * (uint32_t)g;
         r.k = *reinterpret_cast<const uint4*>(codes + off);
         r.v = *reinterpret_cast<const uint4*>(codes + off + 64u);
-        uint32_t sk, sv;
-        row_scales<SF>(scl + jj * (uint32_t)row_scale_bytes<SF>(), g, sk, sv);
-        r.sk = ok ? sk : unit_scale_bits<SF>();
-        r.sv = ok ? sv : unit_scale_bits<SF>();
+        row_scale_words<SF>(scl + jj * (uint32_t)row_scale_bytes<SF>(), g, r.sk, r.sv);
     };
     {
         // two row buffers, used alternately (the loop is unrolled by two), so
         // the rows in flight never have to be copied into the decode registers
         RowRaw ra[2], rb[2];
         int32_t jc[2] = {-1, -1}, jn[2] = {-1, -1};
+        // every slot of these tiles is below k: the selection row is read
+        // through a uniform base and a 32-bit slot index, with no check
+        const int32_t* selq = sel + (int64_t)qi * k;
         int tile = wave;
         if (tile < n_fast) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                jc[u] = sel_of((int64_t)tile * 32 + 2 * n16 + u);
+                jc[u] = selq[tile * 32 + 2 * n16 + u];
                 fetch(jc[u], ra[u]);
             }
             if (tile + LW < n_fast) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) jn[u] = sel_of((int64_t)(tile + LW) * 32 + 2 * n16 + u);
+                for (int u = 0; u < 2; ++u) jn[u] = selq[(tile + LW) * 32 + 2 * n16 + u];
             }
         }
         // one tile from cur; the next tile's rows go to nxt
         auto step = [&](const RowRaw (&cur)[2], RowRaw (&nxt)[2], int tl) {
             const uint64_t vm0 = __ballot(jc[0] >= 0 && jc[0] <= t32) & 0xFFFFull;
             const uint64_t vm1 = __ballot(jc[1] >= 0 && jc[1] <= t32) & 0xFFFFull;
+            uint32_t sk[2], sv[2];  // the lane's scale bits; 1 for an empty slot
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bool ok = jc[u] >= 0 && jc[u] <= t32;
+                sk[u] = ok ? row_scale_bits<SF>(cur[u].sk, g) : unit_scale_bits<SF>();
+                sv[u] = ok ? row_scale_bits<SF>(cur[u].sv, g) : unit_scale_bits<SF>();
+            }
             bf16x8_t kf[2][4];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const uint32_t w[4] = {cur[u].k.x, cur[u].k.y, cur[u].k.z, cur[u].k.w};
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const DqScale sc = dw_scale<SF>(cur[u].sk, kb);
+                    const DqScale sc = dw_scale<SF>(sk[u], kb);
                     kf[u][kb] = as_bf16x8(dq_pair<SF>(w[kb], sc, 0), dq_pair<SF>(w[kb], sc, 1),
                                           dq_pair<SF>(w[kb], sc, 2), dq_pair<SF>(w[kb], sc, 3));
                 }
             }
+            float sc4[2][4];
+            scores(kf, sc4);  // K is dead from here on
 #pragma unroll
             for (int u = 0; u < 2; ++u) {  // V rows of slots 2 n16 + u, dims 32 g .. + 32
                 const uint32_t wv[4] = {cur[u].v.x, cur[u].v.y, cur[u].v.z, cur[u].v.w};
                 uint32_t d[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    d[i] = dq_pair<SF>(wv[i >> 2], dw_scale<SF>(cur[u].sv, i >> 2), i & 3);
+                    d[i] = dq_pair<SF>(wv[i >> 2], dw_scale<SF>(sv[u], i >> 2), i & 3);
                 vr_store_row(vr, 2 * n16 + u, g, d);
             }
             const int next = tl + LW;
@@ -716,10 +749,10 @@ __global__ __launch_bounds__(LW * 64) void k_attn_loop(CacheView c, const uint16
                 }
                 if (next + LW < n_fast) {
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) jn[u] = sel_of((int64_t)(next + LW) * 32 + 2 * n16 + u);
+                    for (int u = 0; u < 2; ++u) jn[u] = selq[(next + LW) * 32 + 2 * n16 + u];
                 }
             }
-            consume(kf, vm0, vm1);
+            consume(sc4, vm0, vm1);
         };
         for (; tile < n_fast; tile += 2 * LW) {
             step(ra, rb, tile);
@@ -801,7 +834,9 @@ __global__ __launch_bounds__(LW * 64) void k_attn_loop(CacheView c, const uint16
         }
         vr_store_row(vr, 2 * n16, g, vd[0]);
         vr_store_row(vr, 2 * n16 + 1, g, vd[1]);
-        consume(kf, vm0, vm1);
+        float sc4[2][4];
+        scores(kf, sc4);
+        consume(sc4, vm0, vm1);
     }
     // ---- combine the waves
     l_part += __shfl_xor(l_part, 16, 64);

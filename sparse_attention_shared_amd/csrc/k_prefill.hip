@@ -31,8 +31,11 @@ namespace csa2 {
 typedef __attribute__((ext_vector_type(8))) __bf16 pf_bf16x8;
 typedef __attribute__((ext_vector_type(4))) float pf_f32x4;
 
-constexpr int kPfQB = 8;        // 16-query blocks per wave
+constexpr int kPfQB = 4;        // 16-query blocks per wave
 constexpr int kPfQ = 16 * kPfQB; // queries per workgroup tile (every wave takes all of them)
+// 64 queries a tile keep the filter within 128 VGPRs and its LDS within a
+// quarter of the CU's, so four of its workgroups (four waves per SIMD) share
+// a CU: the latency of the candidate hand-offs is hidden by the other waves.
 constexpr int kPfCStride = 512; // positions between sampled 64-position steps
 constexpr int kPfCSteps = 4;    // sampled steps per chunk-maximum workgroup
 constexpr int kPfFiltSpan = 4096;  // positions per filter workgroup
@@ -177,7 +180,7 @@ __device__ __forceinline__ void pf_cmax_step(const pf_bf16x8 (&kf)[4][2],
     }
 }
 
-// The cmax workgroup's four waves take different query tiles (4 x 128
+// The cmax workgroup's four waves take different query tiles (4 x kPfQ
 // queries) over the same sampled positions, so each 64-position key tile is
 // loaded from global memory once and read by all four waves from LDS.  Rows are
 // padded to 144 bytes: the 16 lanes of a lane group read 16 rows at one
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(256) void k_pf_thresh(const uint32_t* __restrict__ 
 // Pre-filter granularity: a lane's four scores of one tile (one query, four
 // consecutive positions) are queued together when any of them passes, so one
 // wave-wide compaction serves four compares.
-constexpr int kPfQueue = 576;  // per-wave queue entries: one j-block (8 x 64) past the drain mark
+constexpr int kPfQueue = kPfQB * 64 + 64;  // per-wave queue entries: one j-block past the drain mark
 
 struct PfFiltLds {
     uint2 buf[kPfQ][kPfLB];          // per-query candidates of this workgroup
@@ -413,7 +416,7 @@ __device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int 
 
 // grid (ceil(nq / kPfQ), ceil(t_cap / kPfFiltSpan)), 256 threads.  cand: [nq][cap]
 // (position, key); cnt: [nq].
-__global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ kseq, int32_t t_cap,
+__global__ __launch_bounds__(256, 4) void k_pf_filter(const uint16_t* __restrict__ kseq, int32_t t_cap,
                                                    const uint16_t* __restrict__ q_idx,
                                                    const int32_t* __restrict__ q_pos, int32_t nq,
                                                    int32_t msh, const float* __restrict__ thr_f,
@@ -509,22 +512,25 @@ __global__ __launch_bounds__(256) void k_pf_filter(const uint16_t* __restrict__ 
             }
         }
         if (s % kSegSteps == kSegSteps - 1 || s == nsteps - 1) {  // uniform: flush the lists
+            // the barriers order LDS only (lds_barrier): the next step's key
+            // fragments stay in flight, and the list stores to global memory
+            // need no order within the launch
             pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
             qn = 0;
-            __syncthreads();
+            lds_barrier();
             if (tid < kPfQ) {
                 const int m = min(sh.n[tid], kPfLB);
                 sh.base[tid] = m > 0 ? (int)atomicAdd(&cnt[q0 + tid], (uint32_t)m) : 0;
             }
-            __syncthreads();
+            lds_barrier();
             for (int e = tid; e < kPfQ * kPfLB; e += 256) {
                 const int ql = e / kPfLB, j = e % kPfLB;
                 if (j < min(sh.n[ql], kPfLB) && sh.base[ql] + j < cap)
                     cand[(q0 + ql) * cap + sh.base[ql] + j] = sh.buf[ql][j];
             }
-            __syncthreads();
+            lds_barrier();
             if (tid < kPfQ) sh.n[tid] = 0;
-            __syncthreads();
+            lds_barrier();
         }
     }
 }
