@@ -115,20 +115,19 @@ __device__ __forceinline__ void wave_find_bucket(const int* hist, int nb, int re
     }
 }
 
-// Exact (tau, need) of the kk-th key among the selectable keys K(0..m).  The
-// top `known` bits (0 or 12) are shared by every key that can reach the kk-th
-// place (the caller already resolved them, `prefix` holds them); K is called
-// once per slot and digit pass, so it may recompute keys.  The remaining bits are
-// resolved in digits of 12, 12 and 8 bits, highest first, stopping as soon as
-// a whole bucket is taken.  hist needs kHistWords ints, res 4 ints of LDS.
-// NT threads; every thread returns the same result.
-template <int NT, class KeyFn>
-__device__ void kth_fn(KeyFn K, int64_t m, int kk, int known, uint32_t prefix, int* hist, int* res,
-                       uint32_t& tau, int& need) {
+// Exact (tau, need) of the kk-th key among a workgroup's selectable keys.
+// The top `known` bits (0 or 12) are shared by every key that can reach the
+// kk-th place (the caller already resolved them, `prefix` holds them).  The
+// remaining bits are resolved in digits of 12, 12 and 8 bits, highest first,
+// stopping as soon as a whole bucket is taken.  add(mask, prefix, shift, dm)
+// adds this thread's keys k with k != 0 and (k & mask) == prefix to
+// hist[hidx((k >> shift) & dm)]; it runs once per digit.  hist needs
+// kHistWords ints, res 4 ints of LDS.  NT threads; every thread returns the
+// same result.
+template <int NT, class AddFn>
+__device__ void kth_core(AddFn add, int kk, int known, uint32_t prefix, int* hist, int* res,
+                         uint32_t& tau, int& need) {
     const int tid = threadIdx.x;
-    tau = 0u;
-    need = 0;
-    if (m <= 0 || kk <= 0) return;
     uint32_t mask = 0u;
     if (known > 0) {
         mask = 0xFFFFFFFFu << (32 - known);
@@ -144,15 +143,7 @@ __device__ void kth_fn(KeyFn K, int64_t m, int kk, int known, uint32_t prefix, i
         const uint32_t dm = (uint32_t)nb - 1u;
         for (int i = tid; i < hidx(nb); i += NT) hist[i] = 0;
         __syncthreads();
-        for (int64_t i0 = tid; i0 < m; i0 += 4 * NT) {
-            uint32_t kv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) kv[u] = (i0 + u * NT < m) ? K(i0 + u * NT) : 0u;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (kv[u] && (kv[u] & mask) == prefix)
-                    atomicAdd(&hist[hidx((int)((kv[u] >> shift) & dm))], 1);
-        }
+        add(mask, prefix, shift, dm);
         __syncthreads();
         if (tid < 64) wave_find_bucket(hist, nb, rem, res);
         __syncthreads();
@@ -169,7 +160,7 @@ __device__ void kth_fn(KeyFn K, int64_t m, int kk, int known, uint32_t prefix, i
         mask |= dm << shift;
         rem -= above;
         if (cnt == rem) {  // the whole bucket is taken: every key >= prefix
-            tau = prefix - 1u;
+            tau = prefix ? prefix - 1u : 0u;  // prefix 0: every selectable (nonzero) key
             need = 0;
             return;
         }
@@ -177,6 +168,99 @@ __device__ void kth_fn(KeyFn K, int64_t m, int kk, int known, uint32_t prefix, i
     }
     tau = prefix;
     need = rem;
+}
+
+// kth_core over the keys K(0..m): K is called once per slot and digit pass,
+// so it may recompute keys.
+template <int NT, class KeyFn>
+__device__ void kth_fn(KeyFn K, int64_t m, int kk, int known, uint32_t prefix, int* hist, int* res,
+                       uint32_t& tau, int& need) {
+    tau = 0u;
+    need = 0;
+    if (m <= 0 || kk <= 0) return;
+    const int tid = threadIdx.x;
+    kth_core<NT>(
+        [&](uint32_t mask, uint32_t pre, int shift, uint32_t dm) {
+            for (int64_t i0 = tid; i0 < m; i0 += 4 * NT) {
+                uint32_t kv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) kv[u] = (i0 + u * NT < m) ? K(i0 + u * NT) : 0u;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (kv[u] && (kv[u] & mask) == pre)
+                        atomicAdd(&hist[hidx((int)((kv[u] >> shift) & dm))], 1);
+            }
+        },
+        kk, known, prefix, hist, res, tau, need);
+}
+
+// kth_core over PER keys a thread holds in registers (0 = not selectable),
+// with a short cut after the first 12-bit digit: when the bucket holding the
+// kk-th key has at most 64 keys, one wave ranks them directly instead of
+// running the remaining digits.  small needs 64 words and res 5 ints of LDS
+// (besides hist).  NT threads; every thread returns the same result.
+template <int NT, int PER>
+__device__ void kth_regs(const uint32_t (&kv)[PER], int kk, int* hist, int* res, uint32_t* small,
+                         uint32_t& tau, int& need) {
+    const int tid = threadIdx.x;
+    tau = 0u;
+    need = 0;
+    if (kk <= 0) return;
+    for (int i = tid; i < hidx(4096); i += NT) hist[i] = 0;
+    if (tid < 64) small[tid] = 0u;
+    if (tid == 0) res[4] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+        if (kv[u]) atomicAdd(&hist[hidx((int)(kv[u] >> 20))], 1);
+    __syncthreads();
+    if (tid < 64) wave_find_bucket(hist, 4096, kk, res);
+    __syncthreads();
+    const int total = res[3], above = res[1], cnt = res[2];
+    const uint32_t bucket = (uint32_t)res[0];
+    if (total < kk) return;  // fewer selectable keys than kk: every one (tau 0)
+    const int rem = kk - above;
+    const uint32_t prefix = bucket << 20;
+    if (cnt == rem) {  // the whole bucket is taken
+        tau = prefix ? prefix - 1u : 0u;
+        return;
+    }
+    if (cnt > 64) {  // many keys share the bucket: the remaining digits
+        __syncthreads();  // every thread has read res
+        kth_core<NT>(
+            [&](uint32_t mask, uint32_t pre, int shift, uint32_t dm) {
+#pragma unroll
+                for (int u = 0; u < PER; ++u)
+                    if (kv[u] && (kv[u] & mask) == pre) atomicAdd(&hist[hidx((int)((kv[u] >> shift) & dm))], 1);
+            },
+            rem, 12, prefix, hist, res, tau, need);
+        return;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+        if (kv[u] && (kv[u] >> 20) == bucket) small[atomicAdd(&res[4], 1)] = kv[u];
+    __syncthreads();
+    if (tid < 64) {
+        // the rem-th largest key x of the bucket: gt < rem <= ge.  When every
+        // key equal to x is taken, tau = x - 1 and need = 0.
+        const uint32_t x = small[tid];  // 0 past the bucket's keys
+        const uint4* sv = reinterpret_cast<const uint4*>(small);
+        int gt = 0, ge = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint4 y = sv[j];
+            gt += (int)(y.x > x) + (int)(y.y > x) + (int)(y.z > x) + (int)(y.w > x);
+            ge += (int)(y.x >= x) + (int)(y.y >= x) + (int)(y.z >= x) + (int)(y.w >= x);
+        }
+        if (x != 0u && gt < rem && rem <= ge) {  // lanes holding equal keys write the same
+            const int nd = rem - gt;
+            res[0] = (int)(nd == ge - gt ? x - 1u : x);
+            res[1] = nd == ge - gt ? 0 : nd;
+        }
+    }
+    __syncthreads();
+    tau = (uint32_t)res[0];
+    need = res[1];
 }
 
 // kth_fn over keys held in LDS.

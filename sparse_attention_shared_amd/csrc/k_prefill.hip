@@ -22,6 +22,8 @@
 //              so every top-k position is on it.  A query with fewer (an
 //              unlucky sample) or with more than the list holds (ties) is
 //              resolved exactly by recomputing its scores.
+#include <algorithm>
+
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
 #include "csa2_select.h"
@@ -536,27 +538,34 @@ __global__ __launch_bounds__(256, 4) void k_pf_filter(const uint16_t* __restrict
 }
 
 // ---- 4. select ---------------------------------------------------------------
+// Per query: the candidates' keys stay in registers for the exact radix
+// select of (tau, need); then two bitmaps over the query's positions put the
+// chosen ones in order -- A marks keys above tau, B keys equal to it, of
+// which the `need` lowest positions are taken -- and one scan over the words
+// writes them ascending.  The radix histogram and the bitmaps share the
+// dynamic LDS (the histogram is dead once tau is known).
 struct PfSelLds {
-    alignas(16) int hist[kHistWords];
-    uint32_t skey[kPfCap];
-    int32_t spos[kPfCap];
-    int tmp[kPfSelNT / 64 + 1];
+    alignas(16) uint32_t small[64];
+    int tmp[2 * (kPfSelNT / 64 + 1)];
     int wtmp[2 * kPfSelNT / 64];
-    int res[4];
+    int res[8];
 };
 
 // Exact top-k of one query by recomputing its scores (VALU dot products): the
 // path of a query whose candidate list overflowed.
 __device__ void pf_select_recompute(const uint16_t* __restrict__ kseq, const uint16_t* __restrict__ qr,
-                                    int64_t t, int32_t k, int32_t* __restrict__ dst, PfSelLds& sh) {
-    float qf[kIdxDim];
+                                    int64_t t, int32_t k, int32_t* __restrict__ dst, int* hist,
+                                    PfSelLds& sh) {
+    // the query stays packed (two bf16 a word): half the registers of fp32,
+    // the same products
+    uint32_t qw[kIdxDim / 2];
 #pragma unroll
     for (int d = 0; d < kIdxDim; d += 8) {
         const uint4 v = *reinterpret_cast<const uint4*>(qr + d);
-        qf[d + 0] = bf16_lo(v.x); qf[d + 1] = bf16_hi(v.x);
-        qf[d + 2] = bf16_lo(v.y); qf[d + 3] = bf16_hi(v.y);
-        qf[d + 4] = bf16_lo(v.z); qf[d + 5] = bf16_hi(v.z);
-        qf[d + 6] = bf16_lo(v.w); qf[d + 7] = bf16_hi(v.w);
+        qw[d / 2 + 0] = v.x;
+        qw[d / 2 + 1] = v.y;
+        qw[d / 2 + 2] = v.z;
+        qw[d / 2 + 3] = v.w;
     }
     auto K = [&](int64_t i) -> uint32_t {
         if (i > t) return 0u;
@@ -565,22 +574,29 @@ __device__ void pf_select_recompute(const uint16_t* __restrict__ kseq, const uin
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
             const uint4 v = row[w];
-            s = fmaf(qf[8 * w + 0], bf16_lo(v.x), s); s = fmaf(qf[8 * w + 1], bf16_hi(v.x), s);
-            s = fmaf(qf[8 * w + 2], bf16_lo(v.y), s); s = fmaf(qf[8 * w + 3], bf16_hi(v.y), s);
-            s = fmaf(qf[8 * w + 4], bf16_lo(v.z), s); s = fmaf(qf[8 * w + 5], bf16_hi(v.z), s);
-            s = fmaf(qf[8 * w + 6], bf16_lo(v.w), s); s = fmaf(qf[8 * w + 7], bf16_hi(v.w), s);
+            const uint32_t kw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                s = fmaf(bf16_lo(qw[4 * w + h]), bf16_lo(kw[h]), s);
+                s = fmaf(bf16_hi(qw[4 * w + h]), bf16_hi(kw[h]), s);
+            }
         }
         return score_key(s);
     };
     uint32_t tau;
     int need;
-    kth_fn<kPfSelNT>(K, t + 1, k, 0, 0u, sh.hist, sh.res, tau, need);
+    kth_fn<kPfSelNT>(K, t + 1, k, 0, 0u, hist, sh.res, tau, need);
     ordered_write<kPfSelNT>(K, t + 1, tau, need, nullptr, k, dst, sh.wtmp);
 }
 
-// grid nq, 512 threads, dynamic LDS: bitmap [nw] words then [nw] u16 prefixes,
-// nw = ceil(t_cap / 32).
-__global__ __launch_bounds__(kPfSelNT) void k_pf_select(const uint16_t* __restrict__ kseq,
+// Dynamic LDS of k_pf_select: the radix histogram or the two bitmaps.
+size_t pf_select_lds_bytes(int64_t t_cap) {
+    const size_t nw = (size_t)((t_cap + 31) / 32);
+    return std::max((size_t)kHistWords, 2 * nw) * sizeof(uint32_t);
+}
+
+// grid nq, 512 threads, dynamic LDS pf_select_lds_bytes(t_cap).
+__global__ __launch_bounds__(kPfSelNT, 6) void k_pf_select(const uint16_t* __restrict__ kseq,
                                                         int64_t t_cap,
                                                         const uint16_t* __restrict__ q_idx,
                                                         const int32_t* __restrict__ q_pos,
@@ -588,8 +604,9 @@ __global__ __launch_bounds__(kPfSelNT) void k_pf_select(const uint16_t* __restri
                                                         const uint32_t* __restrict__ cnt,
                                                         const uint2* __restrict__ cand, int32_t cap,
                                                         int32_t* __restrict__ sel) {
-    extern __shared__ uint32_t pf_bits[];
+    extern __shared__ uint32_t pf_dyn[];
     __shared__ PfSelLds sh;
+    int* hist = reinterpret_cast<int*>(pf_dyn);
     const int q = blockIdx.x, tid = threadIdx.x;
     int32_t* dst = sel + (int64_t)q * k;
     const int64_t t = pf_clamp_pos(pf_last_entry(q_pos[q], msh), t_cap);
@@ -600,13 +617,9 @@ __global__ __launch_bounds__(kPfSelNT) void k_pf_select(const uint16_t* __restri
     const uint32_t n = cnt[q];
     // too many candidates for the list, or too few to certify the selection
     if (n > (uint32_t)cap || ((int64_t)n < k && (int64_t)n < t + 1)) {
-        pf_select_recompute(kseq, q_idx + (int64_t)q * kIdxDim, t, k, dst, sh);
+        pf_select_recompute(kseq, q_idx + (int64_t)q * kIdxDim, t, k, dst, hist, sh);
         return;
     }
-    const int nw = (int)(t / 32 + 1);
-    uint16_t* wpre = reinterpret_cast<uint16_t*>(pf_bits + ((t_cap + 31) / 32));
-    for (int w = tid; w < nw; w += kPfSelNT) pf_bits[w] = 0u;
-    __syncthreads();
     constexpr int PER = kPfCap / kPfSelNT;
     uint2 cv[PER];
     const uint2* src = cand + (int64_t)q * cap;
@@ -614,31 +627,6 @@ __global__ __launch_bounds__(kPfSelNT) void k_pf_select(const uint16_t* __restri
     for (int u = 0; u < PER; ++u) {
         const int i = tid + u * kPfSelNT;
         cv[u] = i < (int)n ? src[i] : make_uint2(0xFFFFFFFFu, 0u);
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u)
-        if (cv[u].x != 0xFFFFFFFFu) atomicOr(&pf_bits[cv[u].x >> 5], 1u << (cv[u].x & 31));
-    __syncthreads();
-    // set bits before each word: contiguous words per thread, one block scan
-    const int wpt = (nw + kPfSelNT - 1) / kPfSelNT;
-    const int w0 = min(nw, tid * wpt), w1 = min(nw, w0 + wpt);
-    int mine = 0;
-    for (int w = w0; w < w1; ++w) mine += __popc(pf_bits[w]);
-    int total;
-    int run = block_excl_scan<kPfSelNT>(mine, sh.tmp, &total);
-    for (int w = w0; w < w1; ++w) {
-        wpre[w] = (uint16_t)run;
-        run += __popc(pf_bits[w]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        if (cv[u].x != 0xFFFFFFFFu) {
-            const uint32_t p = cv[u].x, w = p >> 5;
-            const int rank = wpre[w] + __popc(pf_bits[w] & ((1u << (p & 31)) - 1u));
-            sh.skey[rank] = cv[u].y;
-            sh.spos[rank] = (int32_t)p;
-        }
     }
     // every candidate is at or above the threshold, so their keys share
     // their top bits; the radix works on the bits below that common prefix
@@ -666,13 +654,73 @@ __global__ __launch_bounds__(kPfSelNT) void k_pf_select(const uint16_t* __restri
         kmin = min(kmin, (uint32_t)sh.wtmp[w]);
         kmax = max(kmax, (uint32_t)sh.wtmp[kPfSelNT / 64 + w]);
     }
-    __syncthreads();  // wtmp is reused by the ordered write
     const int sp = kmin <= kmax ? min(31, __clz((int)(kmin ^ kmax))) : 0;
-    auto K = [&](int64_t i) { return (sh.skey[i] << sp) | 1u; };
+    uint32_t kv[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) kv[u] = cv[u].x != 0xFFFFFFFFu ? (cv[u].y << sp) | 1u : 0u;
     uint32_t tau;
     int need;
-    kth_fn<kPfSelNT>(K, (int64_t)n, k, 0, 0u, sh.hist, sh.res, tau, need);
-    ordered_write<kPfSelNT>(K, (int64_t)n, tau, need, sh.spos, k, dst, sh.wtmp);
+    kth_regs<kPfSelNT, PER>(kv, k, hist, sh.res, sh.small, tau, need);
+    // bitmap A (positions 0..t) of the chosen keys takes the histogram's
+    // place; aux holds the keys equal to tau (ties, taken lowest position
+    // first), then A's word prefixes
+    const int nw = (int)(t / 32 + 1);
+    uint32_t* bma = pf_dyn;
+    uint32_t* aux = pf_dyn + nw;
+    for (int w = tid; w < (need > 0 ? 2 * nw : nw); w += kPfSelNT) pf_dyn[w] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const uint32_t p = cv[u].x;  // a candidate's position is <= t
+        if (kv[u] > tau)
+            atomicOr(&bma[p >> 5], 1u << (p & 31));
+        else if (need > 0 && kv[u] == tau && kv[u] != 0u)
+            atomicOr(&aux[p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+    // contiguous words per thread, so one scan orders them
+    const int wpt = (nw + kPfSelNT - 1) / kPfSelNT;
+    const int w0 = min(nw, tid * wpt), w1 = min(nw, w0 + wpt);
+    if (need > 0) {  // uniform: the `need` lowest tied positions join A
+        int cb = 0;
+        for (int w = w0; w < w1; ++w) cb += __popc(aux[w]);
+        int tb;
+        int eq = block_excl_scan<kPfSelNT>(cb, sh.tmp, &tb);
+        for (int w = w0; w < w1 && eq < need; ++w) {
+            uint32_t e = aux[w], m = bma[w];
+            while (e != 0u && eq < need) {
+                const uint32_t low = e & (0u - e);
+                m |= low;
+                e ^= low;
+                ++eq;
+            }
+            bma[w] = m;
+        }
+        __syncthreads();
+    }
+    int ca = 0;
+    for (int w = w0; w < w1; ++w) ca += __popc(bma[w]);
+    int chosen;
+    int run = block_excl_scan<kPfSelNT>(ca, sh.tmp, &chosen);
+    for (int w = w0; w < w1; ++w) {  // aux: chosen positions before word w
+        const uint32_t m = bma[w];
+        aux[w] = (uint32_t)run;
+        run += __popc(m);
+    }
+    __syncthreads();
+    // each chosen candidate's place is its rank among the chosen positions
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const uint32_t p = cv[u].x;
+        if (kv[u] > tau || (need > 0 && kv[u] == tau && kv[u] != 0u)) {
+            const uint32_t m = bma[p >> 5];
+            if ((m >> (p & 31)) & 1u) {
+                const int rank = (int)aux[p >> 5] + __popc(m & ((1u << (p & 31)) - 1u));
+                if (rank < k) dst[rank] = (int32_t)p;
+            }
+        }
+    }
+    for (int i = min(chosen, k) + tid; i < k; i += kPfSelNT) dst[i] = -1;
 }
 
 // Multi-query scores of a prefill chunk on one sequence: S = Q_I K_I^T, a
@@ -801,8 +849,7 @@ hipError_t launch_prefill_topk(const CacheView& c, int32_t seq, const uint16_t* 
     const dim3 fgrid((uint32_t)((nq + kPfQ - 1) / kPfQ), (uint32_t)((c.t_cap + kPfFiltSpan - 1) / kPfFiltSpan));
     hipLaunchKernelGGL(k_pf_filter, fgrid, dim3(256), 0, s, kseq, (int32_t)c.t_cap, q_idx, q_pos, nq, c.msh,
                        thr_f, thr_k, cnt, cand, kPfCap);
-    const size_t nw = (size_t)((c.t_cap + 31) / 32);
-    hipLaunchKernelGGL(k_pf_select, dim3(nq), dim3(kPfSelNT), nw * 4 + nw * 2, s, kseq, c.t_cap,
+    hipLaunchKernelGGL(k_pf_select, dim3(nq), dim3(kPfSelNT), pf_select_lds_bytes(c.t_cap), s, kseq, c.t_cap,
                        q_idx, q_pos, c.msh, k, cnt, cand, kPfCap, sel);
     return hipGetLastError();
 }
