@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void k_pf_thresh(const uint32_t* __restrict__ 
 // Pre-filter granularity: a lane's four scores of one tile (one query, four
 // consecutive positions) are queued together when any of them passes, so one
 // wave-wide compaction serves four compares.
-constexpr int kPfQueue = kPfQB * 64 + 64;  // per-wave queue entries: one j-block past the drain mark
+constexpr int kPfQueue = kPfQB * 64 + 64;  // per-wave ring: a j-block at most, plus < 64 left by a drain
 
 struct PfFiltLds {
     uint2 buf[kPfQ][kPfLB];          // per-query candidates of this workgroup
@@ -379,14 +379,15 @@ struct PfFiltLds {
     uint32_t thr[kPfQ];
 };
 
-// Exact test of the wave's queued scores (causal mask, key >= thr); the ones
-// that pass go to their query's list.
-__device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int qn, int64_t q0,
-                                         uint32_t* __restrict__ cnt, uint2* __restrict__ cand,
-                                         int32_t cap) {
-    for (int e = lane; e < qn; e += 64) {
-        const uint4 sc = sh.qscore[wave][e];
-        const uint32_t tag = sh.qtag[wave][e];
+// Exact test of `count` queued entries from ring slot `head` (causal mask,
+// key >= thr); the scores that pass go to their query's list.
+__device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int head, int count,
+                                         int64_t q0, uint32_t* __restrict__ cnt,
+                                         uint2* __restrict__ cand, int32_t cap) {
+    for (int e = lane; e < count; e += 64) {
+        const int r = head + e < kPfQueue ? head + e : head + e - kPfQueue;
+        const uint4 sc = sh.qscore[wave][r];
+        const uint32_t tag = sh.qtag[wave][r];
         const int ql = (int)(tag & 127u);
         const int32_t t0 = (int32_t)(tag >> 7);
         const int32_t lim = sh.pos[ql];
@@ -458,7 +459,9 @@ __global__ __launch_bounds__(256, 4) void k_pf_filter(const uint16_t* __restrict
     // flush), computing only the steps that hold a position <= tmax.
     constexpr int kSegSteps = kPfFiltSeg / 256;
     const int nsteps = min(kPfFiltSpan / 256, (min(tmax, t_cap - 1) - span0) / 256 + 1);
-    int qn = 0;  // entries in this wave's queue (wave-uniform)
+    // the wave's queue is a ring: qh its first entry, qn its entries
+    // (wave-uniform); drains take whole batches of 64, one entry a lane
+    int qh = 0, qn = 0;
     pf_bf16x8 kn[4][2];
     pf_load_k(kseq, t_cap, span0 + wave * 64, n16, g, kn);
     for (int s = 0; s < nsteps; ++s) {
@@ -494,22 +497,28 @@ __global__ __launch_bounds__(256, 4) void k_pf_filter(const uint16_t* __restrict
                 const int incl = wave_scan_dpp(mine);
                 const int tot = __builtin_amdgcn_readlane(incl, 63);
                 if (tot) {  // wave-uniform
-                    int off = qn + incl - mine;
+                    // qh + qn + incl < 2 kPfQueue: one wrap at most
+                    int off = qh + qn + incl - mine;
 #pragma unroll
                     for (int i = 0; i < kPfQB; ++i) {
                         if ((bits >> i) & 1u) {
-                            sh.qscore[wave][off] =
+                            const int r = off < kPfQueue ? off : off - kPfQueue;
+                            sh.qscore[wave][r] =
                                 make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
                                            __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
-                            sh.qtag[wave][off] = tag + 16u * i;
+                            sh.qtag[wave][r] = tag + 16u * i;
                             ++off;
                         }
                     }
                     qn += tot;
                 }
-                if (qn > kPfQueue - kPfQB * 64) {  // room for the next j-block's entries
-                    pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
-                    qn = 0;
+                if (qn >= 64) {  // whole batches; fewer than 64 entries stay, so the
+                                 // next j-block's (at most kPfQB * 64) still fit
+                    const int nb = qn & ~63;
+                    pf_drain(sh, wave, lane, qh, nb, q0, cnt, cand, cap);
+                    qh += nb;
+                    if (qh >= kPfQueue) qh -= kPfQueue;
+                    qn -= nb;
                 }
             }
         }
@@ -517,7 +526,8 @@ __global__ __launch_bounds__(256, 4) void k_pf_filter(const uint16_t* __restrict
             // the barriers order LDS only (lds_barrier): the next step's key
             // fragments stay in flight, and the list stores to global memory
             // need no order within the launch
-            pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
+            pf_drain(sh, wave, lane, qh, qn, q0, cnt, cand, cap);
+            qh = 0;
             qn = 0;
             lds_barrier();
             if (tid < kPfQ) {
