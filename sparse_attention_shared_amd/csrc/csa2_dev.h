@@ -60,6 +60,28 @@ __device__ __forceinline__ float sum8(float v) {
     return v;
 }
 
+// Lane l combined with lane l ^ 16 (or l ^ 32) without going through LDS:
+// v_permlane16_swap / v_permlane32_swap of a value with itself leave x[l] in
+// one result and x[l ^ 16] (x[l ^ 32]) in the other, in an order that
+// depends on the row; max and + take them in either order.  Every lane of
+// the wave must be active.  (In the prefill loop these beat an LDS
+// shuffle; in the latency-bound decode kernel the shuffle measured faster.)
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
 // row broadcasts (no LDS traffic).
 __device__ __forceinline__ int wave_scan_dpp(int x) {

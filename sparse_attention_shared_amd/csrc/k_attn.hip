@@ -623,8 +623,7 @@ __global__ __launch_bounds__(LW * 64) void k_attn_loop(CacheView c, const uint16
         mt = fmaxf(fmaxf(mt, sv[0][2]), sv[0][3]);
         mt = fmaxf(fmaxf(mt, sv[1][0]), sv[1][1]);
         mt = fmaxf(fmaxf(mt, sv[1][2]), sv[1][3]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = max_xor32(max_xor16(mt));
         const float ms = mt * zs;            // zs > 0: the scaled tile maximum
         const bool bump = ms > m_run + 8.f;  // m_run = -inf: any valid slot
         if (__ballot(bump)) {
@@ -839,8 +838,7 @@ __global__ __launch_bounds__(LW * 64) void k_attn_loop(CacheView c, const uint16
         consume(sc4, vm0, vm1);
     }
     // ---- combine the waves
-    l_part += __shfl_xor(l_part, 16, 64);
-    l_part += __shfl_xor(l_part, 32, 64);
+    l_part = sum_xor32(sum_xor16(l_part));
     if (g == 0) {
         sh.m[wave][n16] = m_run;
         sh.l[wave][n16] = l_part;
