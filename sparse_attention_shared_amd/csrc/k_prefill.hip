@@ -367,7 +367,10 @@ __global__ __launch_bounds__(256) void k_pf_thresh(const uint32_t* __restrict__ 
 // Pre-filter granularity: a lane's four scores of one tile (one query, four
 // consecutive positions) are queued together when any of them passes, so one
 // wave-wide compaction serves four compares.
-constexpr int kPfQueue = kPfQB * 64 + 64;  // per-wave ring: a j-block at most, plus < 64 left by a drain
+constexpr int kPfQG = kPfQB % 4 == 0 ? 4 : 3;  // query blocks per queue write
+static_assert(kPfQB % kPfQG == 0, "query blocks come in whole queue groups");
+constexpr int kPfQueue = kPfQG * 64 + 64;  // per-wave ring: a group at most, plus < 64 left by a drain
+constexpr int kPfFiltMinWaves = kPfQB <= 4 ? 4 : (kPfQB <= 6 ? 3 : 2);  // per SIMD (VGPR budget)
 
 struct PfFiltLds {
     uint2 buf[kPfQ][kPfLB];          // per-query candidates of this workgroup
@@ -419,7 +422,7 @@ __device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int 
 
 // grid (ceil(nq / kPfQ), ceil(t_cap / kPfFiltSpan)), 256 threads.  cand: [nq][cap]
 // (position, key); cnt: [nq].
-__global__ __launch_bounds__(256, 4) void k_pf_filter(const uint16_t* __restrict__ kseq, int32_t t_cap,
+__global__ __launch_bounds__(256, kPfFiltMinWaves) void k_pf_filter(const uint16_t* __restrict__ kseq, int32_t t_cap,
                                                    const uint16_t* __restrict__ q_idx,
                                                    const int32_t* __restrict__ q_pos, int32_t nq,
                                                    int32_t msh, const float* __restrict__ thr_f,
@@ -493,32 +496,38 @@ __global__ __launch_bounds__(256, 4) void k_pf_filter(const uint16_t* __restrict
                     mx = fmaxf(fmaxf(mx, c[i][2]), c[i][3]);
                     bits |= (uint32_t)(mx >= th[i]) << i;
                 }
-                const int mine = __popc(bits);
-                const int incl = wave_scan_dpp(mine);
-                const int tot = __builtin_amdgcn_readlane(incl, 63);
-                if (tot) {  // wave-uniform
-                    // qh + qn + incl < 2 kPfQueue: one wrap at most
-                    int off = qh + qn + incl - mine;
+                // the blocks enter the queue kPfQG at a time, each group
+                // followed by the drain of whole batches
 #pragma unroll
-                    for (int i = 0; i < kPfQB; ++i) {
-                        if ((bits >> i) & 1u) {
-                            const int r = off < kPfQueue ? off : off - kPfQueue;
-                            sh.qscore[wave][r] =
-                                make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
-                                           __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
-                            sh.qtag[wave][r] = tag + 16u * i;
-                            ++off;
+                for (int h = 0; h < kPfQB / kPfQG; ++h) {
+                    const uint32_t hb = (bits >> (kPfQG * h)) & ((1u << kPfQG) - 1u);
+                    const int mine = __popc(hb);
+                    const int incl = wave_scan_dpp(mine);
+                    const int tot = __builtin_amdgcn_readlane(incl, 63);
+                    if (tot) {  // wave-uniform
+                        // qh + qn + incl < 2 kPfQueue: one wrap at most
+                        int off = qh + qn + incl - mine;
+#pragma unroll
+                        for (int i = kPfQG * h; i < kPfQG * (h + 1); ++i) {
+                            if ((bits >> i) & 1u) {
+                                const int r = off < kPfQueue ? off : off - kPfQueue;
+                                sh.qscore[wave][r] =
+                                    make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
+                                               __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
+                                sh.qtag[wave][r] = tag + 16u * i;
+                                ++off;
+                            }
                         }
+                        qn += tot;
                     }
-                    qn += tot;
-                }
-                if (qn >= 64) {  // whole batches; fewer than 64 entries stay, so the
-                                 // next j-block's (at most kPfQB * 64) still fit
-                    const int nb = qn & ~63;
-                    pf_drain(sh, wave, lane, qh, nb, q0, cnt, cand, cap);
-                    qh += nb;
-                    if (qh >= kPfQueue) qh -= kPfQueue;
-                    qn -= nb;
+                    if (qn >= 64) {  // whole batches; fewer than 64 entries stay, so
+                                     // the next group's (at most kPfQG * 64) still fit
+                        const int nb = qn & ~63;
+                        pf_drain(sh, wave, lane, qh, nb, q0, cnt, cand, cap);
+                        qh += nb;
+                        if (qh >= kPfQueue) qh -= kPfQueue;
+                        qn -= nb;
+                    }
                 }
             }
         }
