@@ -76,10 +76,13 @@ __device__ __forceinline__ void pf_load_q(const uint16_t* __restrict__ q_idx, in
 // query masks those positions, so no branch guards the loads.
 __device__ __forceinline__ void pf_load_k(const uint16_t* __restrict__ kseq, int32_t t_cap,
                                           int32_t t0, int n16, int g, pf_bf16x8 (&b)[4][2]) {
+    // byte offsets stay 32-bit (t_cap <= 2^24 rows of 128 B) over the
+    // wave-uniform base
+    const char* base = reinterpret_cast<const char*>(kseq);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int32_t tt = min(t0 + 16 * j + n16, t_cap - 1);
-        const uint4* row = reinterpret_cast<const uint4*>(kseq + (int64_t)tt * kIdxDim + 8 * g);
+        const uint32_t tt = (uint32_t)min(t0 + 16 * j + n16, t_cap - 1);
+        const uint4* row = reinterpret_cast<const uint4*>(base + (tt * 128u + 16u * (uint32_t)g));
         b[j][0] = __builtin_bit_cast(pf_bf16x8, row[0]);
         b[j][1] = __builtin_bit_cast(pf_bf16x8, row[4]);
     }
@@ -123,32 +126,6 @@ __device__ __forceinline__ void pf_tile_pos(const int32_t* __restrict__ q_pos, i
     }
     tmax = __builtin_amdgcn_readfirstlane(tmax);  // wave-uniform: scalar registers
     tmin = __builtin_amdgcn_readfirstlane(tmin);
-}
-
-// Runs f(kf, t0) over this wave's steps t0 = t_first + 256 s (s < SPAN /
-// 256, t0 < t_cap, t0 <= tmax).  The next step's key fragments are loaded
-// while the current step computes; the load is issued on every step (rows are
-// clamped, so it stays in bounds), which keeps the number of loads in flight
-// the same on every path and the compiler's wait before the MFMAs covers only
-// the fragments of the current step.  One copy of the body keeps the kernel
-// small enough for the instruction cache.
-template <int SPAN, class StepFn>
-__device__ __forceinline__ void pf_sweep(const uint16_t* __restrict__ kseq, int32_t t_cap,
-                                         int32_t t_first, int32_t tmax, int n16, int g, StepFn f) {
-    auto valid = [&](int32_t t, int s) { return s < SPAN / 256 && t < t_cap && t <= tmax; };
-    if (!valid(t_first, 0)) return;
-    pf_bf16x8 kn[4][2];
-    pf_load_k(kseq, t_cap, t_first, n16, g, kn);
-    for (int32_t t0 = t_first, s = 0; valid(t0, s); t0 += 256, ++s) {
-        pf_bf16x8 kf[4][2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            kf[j][0] = kn[j][0];
-            kf[j][1] = kn[j][1];
-        }
-        pf_load_k(kseq, t_cap, t0 + 256, n16, g, kn);
-        f(kf, t0);
-    }
 }
 
 // ---- 1. sampled chunk maxima -------------------------------------------
@@ -379,7 +356,7 @@ struct PfFiltLds {
     int n[kPfQ];
     int base[kPfQ];
     int32_t pos[kPfQ];
-    uint32_t thr[kPfQ];
+    float thf[kPfQ];
 };
 
 // Exact test of `count` queued entries from ring slot `head` (causal mask,
@@ -394,14 +371,14 @@ __device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int 
         const int ql = (int)(tag & 127u);
         const int32_t t0 = (int32_t)(tag >> 7);
         const int32_t lim = sh.pos[ql];
-        const uint32_t thr = sh.thr[ql];
-        const uint32_t v[4] = {sc.x, sc.y, sc.z, sc.w};
-        uint32_t key[4], okm = 0u;
+        // key(s) >= thr is s >= key_float(thr) for every score that is not a
+        // NaN (the keys order scores as floats do, -0 and +0 alike)
+        const float thf = sh.thf[ql];
+        const float v[4] = {__uint_as_float(sc.x), __uint_as_float(sc.y), __uint_as_float(sc.z),
+                            __uint_as_float(sc.w)};
+        uint32_t okm = 0u;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            key[r] = score_key(__uint_as_float(v[r]));
-            okm |= (uint32_t)(t0 + r <= lim && key[r] >= thr) << r;
-        }
+        for (int r = 0; r < 4; ++r) okm |= (uint32_t)(t0 + r <= lim && v[r] >= thf) << r;
         if (okm == 0u) continue;
         // one list reservation for all of the entry's passing positions
         const int slot0 = atomicAdd(&sh.n[ql], __popc(okm));
@@ -410,11 +387,12 @@ __device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int 
             if (!((okm >> r) & 1u)) continue;
             const int slot = slot0 + __popc(okm & ((1u << r) - 1u));
             const int32_t tt = t0 + r;
+            const uint32_t key = score_key(v[r]);
             if (slot < kPfLB) {
-                sh.buf[ql][slot] = make_uint2((uint32_t)tt, key[r]);
+                sh.buf[ql][slot] = make_uint2((uint32_t)tt, key);
             } else {  // this workgroup's list of the query is full: straight to its global list
                 const uint32_t gs = atomicAdd(&cnt[q0 + ql], 1u);
-                if (gs < (uint32_t)cap) cand[(q0 + ql) * cap + gs] = make_uint2((uint32_t)tt, key[r]);
+                if (gs < (uint32_t)cap) cand[(q0 + ql) * cap + gs] = make_uint2((uint32_t)tt, key);
             }
         }
     }
@@ -426,7 +404,6 @@ __global__ __launch_bounds__(256, kPfFiltMinWaves) void k_pf_filter(const uint16
                                                    const uint16_t* __restrict__ q_idx,
                                                    const int32_t* __restrict__ q_pos, int32_t nq,
                                                    int32_t msh, const float* __restrict__ thr_f,
-                                                   const uint32_t* __restrict__ thr_k,
                                                    uint32_t* __restrict__ cnt,
                                                    uint2* __restrict__ cand, int32_t cap) {
     __shared__ PfFiltLds sh;
@@ -441,7 +418,7 @@ __global__ __launch_bounds__(256, kPfFiltMinWaves) void k_pf_filter(const uint16
     if (tid < kPfQ) {
         const int64_t qq = q0 + tid;
         sh.pos[tid] = qq < nq ? (int32_t)pf_clamp_pos(pf_last_entry(q_pos[qq], msh), t_cap) : -1;
-        sh.thr[tid] = qq < nq ? thr_k[qq] : 0xFFFFFFFFu;
+        sh.thf[tid] = qq < nq ? thr_f[qq] : __builtin_inff();
         sh.n[tid] = 0;
     }
     float th[kPfQB];
@@ -867,7 +844,7 @@ hipError_t launch_prefill_topk(const CacheView& c, int32_t seq, const uint16_t* 
                        c.msh, c.t_cap, k, thr_f, thr_k, cnt);
     const dim3 fgrid((uint32_t)((nq + kPfQ - 1) / kPfQ), (uint32_t)((c.t_cap + kPfFiltSpan - 1) / kPfFiltSpan));
     hipLaunchKernelGGL(k_pf_filter, fgrid, dim3(256), 0, s, kseq, (int32_t)c.t_cap, q_idx, q_pos, nq, c.msh,
-                       thr_f, thr_k, cnt, cand, kPfCap);
+                       thr_f, cnt, cand, kPfCap);
     hipLaunchKernelGGL(k_pf_select, dim3(nq), dim3(kPfSelNT), pf_select_lds_bytes(c.t_cap), s, kseq, c.t_cap,
                        q_idx, q_pos, c.msh, k, cnt, cand, kPfCap, sel);
     return hipGetLastError();
