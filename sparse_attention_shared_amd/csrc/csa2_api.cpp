@@ -106,10 +106,9 @@ csa2_status check_append_local(const csa2_local& l, const uint16_t* kn, const ui
 // rows = n_seq with seq = -1 (decode: row b is sequence b's new position), or
 // the rows of one sequence's replayed segment (seq >= 0); q_seq_out, when set,
 // receives each row's sequence.
-hipError_t enqueue_append(const CacheView& cv, int32_t rows, int32_t seq, const int32_t* pos,
-                          const uint16_t* kv, const uint16_t* kidx, int32_t n_local,
-                          const csa2_local* local, const uint16_t* const* kn,
-                          const uint16_t* const* vn, int32_t* q_seq_out, hipStream_t s) {
+// The arguments of one append launch, without local layers.
+static AppendArgs append_args(const CacheView& cv, int32_t seq, const int32_t* pos,
+                              const uint16_t* kv, const uint16_t* kidx, int32_t* q_seq_out) {
     AppendArgs a{};
     a.pos = pos;
     a.seq = seq;
@@ -127,19 +126,35 @@ hipError_t enqueue_append(const CacheView& cv, int32_t rows, int32_t seq, const 
         a.bf16 = static_cast<uint16_t*>(data);
     }
     a.k_idx = const_cast<uint16_t*>(cv.k_idx);
+    return a;
+}
+
+// Adds local layers l.. to a (skipping layers without new rows) until it
+// holds kMaxAppendLayers; returns the first layer left out.
+static int32_t append_locals(AppendArgs& a, int32_t l, int32_t n_local, const csa2_local* local,
+                             const uint16_t* const* kn, const uint16_t* const* vn) {
+    a.n_local = 0;
+    for (; l < n_local && a.n_local < kMaxAppendLayers; ++l) {
+        if (!kn[l] && !vn[l]) continue;
+        AppendLocal& d = a.local[a.n_local++];
+        d.k = const_cast<uint16_t*>(local[l].k);
+        d.v = const_cast<uint16_t*>(local[l].v);
+        d.k_new = kn[l];
+        d.v_new = vn[l];
+        d.cap = local[l].cap;
+    }
+    return l;
+}
+
+hipError_t enqueue_append(const CacheView& cv, int32_t rows, int32_t seq, const int32_t* pos,
+                          const uint16_t* kv, const uint16_t* kidx, int32_t n_local,
+                          const csa2_local* local, const uint16_t* const* kn,
+                          const uint16_t* const* vn, int32_t* q_seq_out, hipStream_t s) {
+    AppendArgs a = append_args(cv, seq, pos, kv, kidx, q_seq_out);
     bool first = true;
     int32_t l = 0;
     do {
-        a.n_local = 0;
-        for (; l < n_local && a.n_local < kMaxAppendLayers; ++l) {
-            if (!kn[l] && !vn[l]) continue;
-            AppendLocal& d = a.local[a.n_local++];
-            d.k = const_cast<uint16_t*>(local[l].k);
-            d.v = const_cast<uint16_t*>(local[l].v);
-            d.k_new = kn[l];
-            d.v_new = vn[l];
-            d.cap = local[l].cap;
-        }
+        l = append_locals(a, l, n_local, local, kn, vn);
         if (first || a.n_local > 0) {
             if (hipError_t e = launch_append(a, rows, s)) return e;
         }
@@ -600,9 +615,19 @@ static csa2_status enqueue_stack(const StackJob& j, const CacheView& cv, const S
         if (e == hipSuccess) e = launch_topk(pscores, S, P, P, pool, k, dst, 0, nullptr, tkws, s);
         return e;
     };
+    // decode: an append whose rows fit one launch runs inside layer 0's
+    // tokenwise scan (the scan takes each query's new key from the rows)
+    AppendArgs fused_app{};
+    bool fuse_append = false;
+    if (!replay && j.app_kv && j.app_kidx && j.n_layers > 0 && j.modes[0] == CSA2_MODE_FULL &&
+        B == 1) {
+        fused_app = append_args(cv, -1, j.q_pos, j.app_kv, j.app_kidx, nullptr);
+        const int32_t nl = j.app_k ? j.n_layers : 0;
+        fuse_append = append_locals(fused_app, 0, nl, j.local, j.app_k, j.app_v) >= nl;
+    }
     // decode append of the new positions, or the segment's ring rows (the
     // replay always launches it: it also writes the sequence ids)
-    if (j.app_kv || replay) {
+    if ((j.app_kv || replay) && !fuse_append) {
         const int32_t nl = j.app_k ? j.n_layers : 0;
         if (enqueue_append(cv, S, j.seq, j.q_pos, j.app_kv, j.app_kidx, nl, j.local, j.app_k,
                            j.app_v, q_seq, s) != hipSuccess)
@@ -630,9 +655,14 @@ static csa2_status enqueue_stack(const StackJob& j, const CacheView& cv, const S
             if (m == CSA2_MODE_FULL && fused_full) {
                 e = launch_prefill_topk(cv, j.seq, j.q_idx[l], j.q_pos, S, k, dst, base + W.pf, s);
             } else if (m == CSA2_MODE_FULL && B == 1) {
-                e = replay ? launch_score_mq(cv, j.seq, j.q_idx[l], j.q_pos, S, scores, cv.t_cap, s)
-                           : launch_score_dense(cv, j.q_idx[l], j.q_pos, q_seq, S, 1, scores,
-                                                cv.t_cap, s, ev0, ev1);
+                if (replay)
+                    e = launch_score_mq(cv, j.seq, j.q_idx[l], j.q_pos, S, scores, cv.t_cap, s);
+                else if (l == 0 && fuse_append)
+                    e = launch_score_dense_append(cv, j.q_idx[l], j.q_pos, S, scores, cv.t_cap,
+                                                  fused_app, s, ev0, ev1);
+                else
+                    e = launch_score_dense(cv, j.q_idx[l], j.q_pos, q_seq, S, 1, scores, cv.t_cap,
+                                           s, ev0, ev1);
                 if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)j.scan_events[1], s);
                 if (e == hipSuccess)
                     e = launch_topk(scores, S, cv.t_cap, cv.t_cap, nullptr, k, dst, P, P ? pool : nullptr,

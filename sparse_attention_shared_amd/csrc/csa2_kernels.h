@@ -74,6 +74,13 @@ hipError_t launch_score_dense(const CacheView& c, const uint16_t* q_idx, const i
                               const int32_t* q_seq, int32_t nq, int32_t block, float* scores,
                               int64_t ld, hipStream_t s, hipEvent_t ev0 = nullptr,
                               hipEvent_t ev1 = nullptr);
+// The decode step's first tokenwise scan (query b on sequence b, one per
+// sequence) with the step's append (one launch's worth of layers) in the same
+// launch: the scan reads each query's new key from the append rows.
+hipError_t launch_score_dense_append(const CacheView& c, const uint16_t* q_idx,
+                                     const int32_t* q_pos, int32_t nq, float* scores, int64_t ld,
+                                     const AppendArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr,
+                                     hipEvent_t ev1 = nullptr);
 // Candidate scores: scores[i][j] = score of position cand[i][j].
 hipError_t launch_score_cand(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
                              const int32_t* q_seq, int32_t nq, const int32_t* cand, int64_t n_cand,

@@ -11,8 +11,11 @@
 // eight partial dots are summed with three lane exchanges.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+
 #include "csa2_dev.h"
 #include "csa2_kernels.h"
+#include "csa2_pack.h"
 #include "csa2_select.h"
 
 namespace csa2 {
@@ -39,19 +42,23 @@ __device__ __forceinline__ void load_q8(const uint16_t* q, float* qf) {
     qf[6] = bf16_lo(v.w); qf[7] = bf16_hi(v.w);
 }
 
-// grid: (ceil(t_cap / 256), nq).  Lane (grp, sub) of a wave handles bytes
-// [16 sub, 16 sub + 16) of key base + 8 r + grp in round r.
+// One 256-key tile of query qi's dense scores (tile index bx).  Lane (grp,
+// sub) of a wave handles bytes [16 sub, 16 sub + 16) of key base + 8 r + grp
+// in round r.  app_kidx (or null): the decode append's new indexer keys
+// ([nq][64]); entry te of query qi -- the one its own position completes, which
+// the append writes in the same launch -- is read from there instead of the
+// cache.
 template <int BLOCK>
-__global__ __launch_bounds__(256) void k_score_dense(const uint16_t* __restrict__ k_idx,
-                                                     int32_t n_seq, int64_t t_cap, int32_t msh,
-                                                     const uint16_t* __restrict__ q_idx,
-                                                     const int32_t* __restrict__ q_pos,
-                                                     const int32_t* __restrict__ q_seq,
-                                                     float* __restrict__ scores, int64_t ld) {
-    const int qi = blockIdx.y;
+__device__ __forceinline__ void score_dense_tile(const uint16_t* __restrict__ k_idx, int32_t n_seq,
+                                                 int64_t t_cap, int32_t msh,
+                                                 const uint16_t* __restrict__ q_idx,
+                                                 const int32_t* __restrict__ q_pos,
+                                                 const int32_t* __restrict__ q_seq,
+                                                 float* __restrict__ scores, int64_t ld, int qi,
+                                                 int bx, const uint16_t* __restrict__ app_kidx) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane & 7, grp = lane >> 3;
-    const int64_t base = (int64_t)blockIdx.x * kScoreTile + wave * 64;
+    const int64_t base = (int64_t)bx * kScoreTile + wave * 64;
     float* srow = scores + (int64_t)qi * ld;
     const int32_t seq = q_seq ? q_seq[qi] : qi;
     // the last entry the query may read: entries of 2^msh positions count
@@ -72,11 +79,25 @@ __global__ __launch_bounds__(256) void k_score_dense(const uint16_t* __restrict_
     float qf[8];
     load_q8(q_idx + (int64_t)qi * kIdxDim + sub * 8, qf);
     const uint4* kb = reinterpret_cast<const uint4*>(k_idx) + (int64_t)seq * t_cap * 8;
+    int64_t te = -1;  // the entry the append writes for this query, if any
+    if (app_kidx) {
+        const int32_t p = q_pos[qi];
+        if (p >= 0 && p < (t_cap << msh) && ((p + 1) & ((1 << msh) - 1)) == 0) te = ((p + 1) >> msh) - 1;
+    }
     uint4 kv[8];
+    if (te >= base && te < base + 64) {  // wave-uniform: this wave holds the new entry
+        const uint4* ka = reinterpret_cast<const uint4*>(app_kidx + (int64_t)qi * kIdxDim);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int64_t tok = base + r * 8 + grp;
-        kv[r] = (tok <= t) ? kb[tok * 8 + sub] : make_uint4(0, 0, 0, 0);
+        for (int r = 0; r < 8; ++r) {
+            const int64_t tok = base + r * 8 + grp;
+            kv[r] = tok == te ? ka[sub] : (tok <= t ? kb[tok * 8 + sub] : make_uint4(0, 0, 0, 0));
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int64_t tok = base + r * 8 + grp;
+            kv[r] = (tok <= t) ? kb[tok * 8 + sub] : make_uint4(0, 0, 0, 0);
+        }
     }
     float s[8];
 #pragma unroll
@@ -98,6 +119,42 @@ __global__ __launch_bounds__(256) void k_score_dense(const uint16_t* __restrict_
         m = fmaxf(m, __shfl_xor(m, 32, 64));
         if (lane == 0) srow[base / 64] = m;
     }
+}
+
+// grid: (ceil(t_cap / 256), nq).
+template <int BLOCK>
+__global__ __launch_bounds__(256) void k_score_dense(const uint16_t* __restrict__ k_idx,
+                                                     int32_t n_seq, int64_t t_cap, int32_t msh,
+                                                     const uint16_t* __restrict__ q_idx,
+                                                     const int32_t* __restrict__ q_pos,
+                                                     const int32_t* __restrict__ q_seq,
+                                                     float* __restrict__ scores, int64_t ld) {
+    score_dense_tile<BLOCK>(k_idx, n_seq, t_cap, msh, q_idx, q_pos, q_seq, scores, ld, blockIdx.y,
+                            blockIdx.x, nullptr);
+}
+
+// The decode step's first indexer scan and its append in one launch ("CED",
+// section "Why Prefill Recomputes a Recent Segment": the new position's global
+// KV and every layer's local row are appended before the layers read them).
+// grid: (max(tiles, nq (1 + groups)), nq + 1): rows 0 .. nq-1 are the scan
+// (query b reads sequence b); in row nq, workgroup x < nq (1 + groups) does
+// the append's workgroup (x % nq, x / nq).  The scan takes query b's new key
+// from the append's rows, so it needs no order against the append's writes;
+// later launches read the appended rows.
+__global__ __launch_bounds__(256) void k_score_dense_append(const uint16_t* __restrict__ k_idx,
+                                                            int32_t n_seq, int64_t t_cap, int32_t msh,
+                                                            const uint16_t* __restrict__ q_idx,
+                                                            const int32_t* __restrict__ q_pos,
+                                                            float* __restrict__ scores, int64_t ld,
+                                                            AppendArgs a, int32_t groups) {
+    const int nq = (int)gridDim.y - 1;
+    if ((int)blockIdx.y == nq) {
+        const int x = blockIdx.x;
+        if (x < nq * (1 + groups)) append_rows(a, x % nq, x / nq);
+        return;
+    }
+    score_dense_tile<1>(k_idx, n_seq, t_cap, msh, q_idx, q_pos, nullptr, scores, ld, blockIdx.y,
+                        blockIdx.x, a.kidx);
 }
 
 // grid: (ceil(n_cand / 256), nq).  Same lane layout; key c of the tile is
@@ -267,6 +324,19 @@ hipError_t launch_score_dense(const CacheView& c, const uint16_t* q_idx, const i
     else
         hipExtLaunchKernelGGL(k_score_dense<64>, grid, dim3(256), 0, s, ev0, ev1, 0, c.k_idx, c.n_seq,
                               c.t_cap, c.msh, q_idx, q_pos, q_seq, scores, ld);
+    return hipGetLastError();
+}
+
+hipError_t launch_score_dense_append(const CacheView& c, const uint16_t* q_idx,
+                                     const int32_t* q_pos, int32_t nq, float* scores, int64_t ld,
+                                     const AppendArgs& a, hipStream_t s, hipEvent_t ev0,
+                                     hipEvent_t ev1) {
+    if (nq == 0 || c.t_cap == 0) return hipSuccess;
+    const int32_t groups = (a.n_local + kAppendLayersPerWg - 1) / kAppendLayersPerWg;
+    const int64_t tiles = (c.t_cap + kScoreTile - 1) / kScoreTile;
+    dim3 grid((uint32_t)std::max<int64_t>(tiles, (int64_t)nq * (1 + groups)), (uint32_t)nq + 1);
+    hipExtLaunchKernelGGL(k_score_dense_append, grid, dim3(256), 0, s, ev0, ev1, 0, c.k_idx, c.n_seq,
+                          c.t_cap, c.msh, q_idx, q_pos, scores, ld, a, groups);
     return hipGetLastError();
 }
 
