@@ -1,6 +1,7 @@
 // csa2_pack.h -- device routines of the FP4 pack and of the decode append,
-// shared by the pack kernels and by the indexer scan that runs the append in
-// its own launch.  Internal header: not part of the C ABI.
+// shared by the pack kernels and by the indexer scan, which can run the
+// append's workgroups inside its launch.  Internal header: not part of the C
+// ABI.
 #pragma once
 
 #include "csa2_dev.h"
@@ -86,13 +87,13 @@ __device__ __forceinline__ uint32_t e2m1_code_scaled(uint32_t a, float s) {
 // Segment": after a token is chosen, every layer updates its local state and
 // the global KV of the new position is appended); also the ring rows of a
 // replayed segment ("Why Prefill Recomputes a Recent Segment"), where every
-// row belongs to one sequence.  Grid (rows, 1 + layer groups): workgroup
-// (b, 0) packs (or copies) row b's global K | V, one element per thread, and
-// copies its indexer key; in workgroup (b, g > 0) each wave copies one
+// row belongs to one sequence.  Work items (rows, 1 + layer groups), one
+// workgroup each: (b, 0) packs (or copies) row b's global K | V, one element
+// per thread, and copies its indexer key; in (b, g > 0) each wave copies one
 // 256-byte local row (K or V of one layer), 4 bytes per lane, so the ring
-// descriptor is wave-uniform.  Every thread issues the position load and its source load
-// before it waits for either (`hold`), so a launch costs about two memory
-// round trips.
+// descriptor is wave-uniform.  Every thread issues the position load and its
+// source load before it waits for either (`hold`), so the work costs about
+// two memory round trips.
 constexpr int kAppendLayersPerWg = 2;
 
 template <typename T>
