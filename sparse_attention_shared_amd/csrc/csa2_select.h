@@ -236,26 +236,49 @@ __device__ void kth_regs(const uint32_t (&kv)[PER], int kk, int* hist, int* res,
             rem, 12, prefix, hist, res, tau, need);
         return;
     }
+    // the bucket's keys into `small`: one reservation per wave (a wave scan
+    // of the lanes' counts), not one LDS atomic per key
+    int mine = 0;
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
-        if (kv[u] && (kv[u] >> 20) == bucket) small[atomicAdd(&res[4], 1)] = kv[u];
+    for (int u = 0; u < PER; ++u) mine += (kv[u] && (kv[u] >> 20) == bucket) ? 1 : 0;
+    const int incl = wave_scan_dpp(mine);
+    const int wtot = __builtin_amdgcn_readlane(incl, 63);
+    if (wtot) {  // wave-uniform
+        int base = 0;
+        if ((tid & 63) == 63) base = atomicAdd(&res[4], wtot);
+        int at = __builtin_amdgcn_readlane(base, 63) + incl - mine;
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+            if (kv[u] && (kv[u] >> 20) == bucket) small[at++] = kv[u];
+    }
     __syncthreads();
     if (tid < 64) {
-        // the rem-th largest key x of the bucket: gt < rem <= ge.  When every
-        // key equal to x is taken, tau = x - 1 and need = 0.
+        // the rem-th largest key of the bucket, one bit at a time from the
+        // top of the 20 bits below the bucket's digit: `act` holds the lanes
+        // still matching the prefix v; when fewer than r of them have the
+        // bit set, all of those are larger than the answer (r drops by
+        // their count), else the answer has the bit.  At the end `act` holds
+        // the keys equal to v and rem - r keys are larger.  When every key
+        // equal to v is taken, tau = v - 1 and need = 0.
         const uint32_t x = small[tid];  // 0 past the bucket's keys
-        const uint4* sv = reinterpret_cast<const uint4*>(small);
-        int gt = 0, ge = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const uint4 y = sv[j];
-            gt += (int)(y.x > x) + (int)(y.y > x) + (int)(y.z > x) + (int)(y.w > x);
-            ge += (int)(y.x >= x) + (int)(y.y >= x) + (int)(y.z >= x) + (int)(y.w >= x);
+        uint64_t act = __ballot(x != 0u);
+        uint32_t v = bucket << 20;
+        int r = rem;
+        for (int b = 19; b >= 0; --b) {
+            const uint64_t ones = __ballot((x >> b) & 1u) & act;
+            const int c = __popcll(ones);
+            if (c >= r) {
+                act = ones;
+                v |= 1u << b;
+            } else {
+                r -= c;
+                act &= ~ones;
+            }
         }
-        if (x != 0u && gt < rem && rem <= ge) {  // lanes holding equal keys write the same
-            const int nd = rem - gt;
-            res[0] = (int)(nd == ge - gt ? x - 1u : x);
-            res[1] = nd == ge - gt ? 0 : nd;
+        if (tid == 0) {
+            const int eq = __popcll(act);
+            res[0] = (int)(r == eq ? v - 1u : v);
+            res[1] = r == eq ? 0 : r;
         }
     }
     __syncthreads();

@@ -627,7 +627,8 @@ __global__ __launch_bounds__(kPfSelNT, 6) void k_pf_select(const uint16_t* __res
     // every candidate is at or above the threshold, so their keys share
     // their top bits; the radix works on the bits below that common prefix
     // (shifted up; the set low bit keeps every key nonzero and the order
-    // unchanged), so its first digit spreads over the whole histogram
+    // unchanged; with no common bit the keys stay as they are, never 0),
+    // so its first digit spreads over the whole histogram
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
     for (int u = 0; u < PER; ++u)
@@ -653,7 +654,7 @@ __global__ __launch_bounds__(kPfSelNT, 6) void k_pf_select(const uint16_t* __res
     const int sp = kmin <= kmax ? min(31, __clz((int)(kmin ^ kmax))) : 0;
     uint32_t kv[PER];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) kv[u] = cv[u].x != 0xFFFFFFFFu ? (cv[u].y << sp) | 1u : 0u;
+    for (int u = 0; u < PER; ++u) kv[u] = cv[u].x != 0xFFFFFFFFu ? (sp ? (cv[u].y << sp) | 1u : cv[u].y) : 0u;
     uint32_t tau;
     int need;
     kth_regs<kPfSelNT, PER>(kv, k, hist, sh.res, sh.small, tau, need);
