@@ -27,6 +27,8 @@ top-2048 positions (csa2_prefill_topk) and attending to them plus its window
 (csa2_sparse_attn), reported as query positions per second.  With --workload
 replay it times the bounded replay of the last 128 positions of one
 131072-token sequence through the same 20-layer stack (csa2_replay_run).
+With --workload config1, config2 or config4 it times that single-layer
+decode workload alone (the record the default line carries for it).
 
 Prints one JSON line.
 """
@@ -655,7 +657,11 @@ def main():
     ap.add_argument("--kv", choices=["fp4", "fp4e"], default="fp4",
                     help="fp4: one E8M0 scale per 32 channels; fp4e: one E4M3 scale per 16")
     ap.add_argument("--topk", type=int, default=0, help="selected entries per layer (default 2048)")
-    ap.add_argument("--workload", choices=["decode", "prefill", "replay"], default="decode")
+    ap.add_argument("--workload", choices=["decode", "prefill", "replay", "config1", "config2",
+                                           "config4"], default="decode",
+                    help="decode: the 20-layer stack (the metric); configN: one of the "
+                         "single-layer decode workloads alone (its record, as in "
+                         "extra_workloads, for profiling)")
     ap.add_argument("--graph", action="store_true",
                     help="replay a recorded stack (HIP graph) per step instead of host launches")
     ap.add_argument("--no-append", action="store_true",
@@ -681,6 +687,12 @@ def main():
         return
     if args.workload == "replay":
         bench_replay(args)
+        return
+    if args.workload.startswith("config"):
+        rec = extra_decode(int(args.workload[-1]), args.steps, args.warmup,
+                           0 if args.no_cpu_baseline else 3.0)
+        rec.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "data": "synthetic"})
+        print(json.dumps(rec), flush=True)
         return
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 18  # float32 elements

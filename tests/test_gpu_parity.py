@@ -137,6 +137,29 @@ def test_topk_bit_exact_on_identical_scores(n, k, k2):
     del ids
 
 
+@pytest.mark.parametrize("k,k2", [(200, 0), (700, 1000)])
+def test_topk_one_workgroup_sampled_floor(k, k2):
+    """Rows of 16384 slots with k < n / 16 take the sampled floor (a 1/8
+    sample's histogram bounds the keys the full pass counts): normal scores
+    (the floor holds); every eighth slot -- the sampled ones -- far above
+    the rest (the floor is too high and the row is counted whole); ties
+    around the k-th key; half the slots -inf."""
+    n, nq = 16384, 4
+    rng = np.random.default_rng(41 + k)
+    s = (rng.standard_normal((nq, n)) * 8).astype(np.float32)
+    s[1, ::8] += np.float32(100)
+    s[2] = (rng.integers(-20, 21, size=n) * 0.5).astype(np.float32)
+    s[3, rng.random(n) < 0.5] = -np.inf
+    g, g2 = csa2.topk(torch.from_numpy(s).cuda(), k, k2=k2)
+    g, g2 = host(g), (host(g2) if k2 else None)
+    for i in range(nq):
+        sv = np.where(np.isneginf(s[i]), np.float32(0), s[i])
+        ids_i = np.where(np.isneginf(s[i]), -1, np.arange(n)).astype(np.int32)
+        assert np.array_equal(g[i], oracle.topk(sv, k, ids_i)), i
+        if k2:
+            assert np.array_equal(g2[i], oracle.topk(sv, k2, ids_i)), i
+
+
 @pytest.mark.parametrize("n,k,k2", [(9000, 300, 0), (50000, 500, 3000)])  # one workgroup; long path
 def test_topk_through_ascending_ids_with_empty_slots(n, k, k2):
     rng = np.random.default_rng(7)
