@@ -198,7 +198,7 @@ StackWs stack_ws_layout(int32_t n_seq, int64_t t_cap, int32_t k, int32_t pool, i
     const int32_t nbsel = block > 1 ? pool / block : 0;
     const bool fused = replay && replay_fused_full(t_cap, k, pool, block);
     w.actr = take(kAttnCtrBytes);
-    w.ctr = take((size_t)std::max(n_seq, kManyQueries) * kCtrStride * sizeof(uint32_t));
+    w.ctr = take((size_t)std::max(n_seq, kCtrBlockQueries) * kCtrStride * sizeof(uint32_t));
     size_t tk = topk_ws_bytes(n_seq, t_cap, k, pool);
     if (block > 1) tk = std::max(tk, topk_ws_bytes(n_seq, nb, nbsel, 0));
     if (pool > 0) tk = std::max(tk, topk_ws_bytes(n_seq, pool, k, 0));

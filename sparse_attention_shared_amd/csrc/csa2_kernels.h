@@ -125,11 +125,19 @@ hipError_t launch_expand_blocks(const int32_t* blocks, int32_t nq, int32_t nb, i
 
 // From this many queries on, attention runs one workgroup per query (no
 // workspace); below it, each query is split over several workgroups.  The
-// split kernel holds ~105 KB of LDS (one workgroup per CU) and takes ~9
-// workgroups per query, so from ~64 queries on it needs three or more waves
-// of workgroups and the one-per-query loop is faster (measured: 128 queries
-// with k = 2048, W = 128 take 64 us split, 39 us in the loop).
-constexpr int32_t kManyQueries = 64;
+// split kernel holds ~105 KB of LDS (one workgroup per CU) and its last
+// chunk of each query merges the others, so its time grows with the queries
+// while the one-per-query loop stays flat until the queries fill the CUs.
+// Measured per call (k = 2048, W = 128: 8 chunks a query), split vs loop:
+// 8 queries 20.9 / 25.0 us, 16: 22.9 / 25.1, 24: 27.2 / 25.2, 48: 39.2 /
+// 25.6, 128: 71.8 / 27.1; with k = 512 (4 chunks): 8 queries 17.8 / 18.8,
+// 16: 19.1 / 18.3, 32: 21.3 / 18.2.
+constexpr int32_t kManyQueries = 16;
+// Queries a block of per-query counters covers (the split attention's, the
+// stack's Reindex select's): the blocks keep this size for any call, so a
+// workspace's layout does not depend on the number of queries up to it.
+constexpr int32_t kCtrBlockQueries = 64;
+static_assert(kCtrBlockQueries >= kManyQueries, "every split call's counters fit the block");
 
 // Per-query arrival counters sit 256 bytes apart, so the workgroups of
 // different queries never contend for one cache line.
@@ -139,7 +147,7 @@ constexpr int64_t kCtrStride = 64;
 // counters' addresses depend on nothing but the query index, so a workspace
 // serves calls of any shape without being cleared again (every call leaves
 // its counters zero).
-constexpr size_t kAttnCtrBytes = (size_t)kManyQueries * kCtrStride * sizeof(uint32_t);
+constexpr size_t kAttnCtrBytes = (size_t)kCtrBlockQueries * kCtrStride * sizeof(uint32_t);
 size_t attn_part_bytes(int32_t nq, int32_t k, int32_t window);
 size_t attn_ws_bytes(int32_t nq, int32_t k, int32_t window);  // 0, or kAttnCtrBytes + partials
 // ctr: kAttnCtrBytes (zero, left zero); part: attn_part_bytes.
@@ -149,8 +157,8 @@ hipError_t launch_sparse_attn_parts(const CacheView& c, const uint16_t* q, const
                                     uint32_t* ctr, float* part, hipStream_t s,
                                     hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // The allocation-free form: counters and partials in a fixed device array of
-// kStaticScratchBytes (partials of up to 504 query-chunks, e.g. 63 queries of
-// 8 chunks); a larger call returns hipErrorInvalidValue.
+// kStaticScratchBytes (partials of up to 504 query-chunks, e.g. 15 queries of
+// 33 chunks); a larger call returns hipErrorInvalidValue.
 constexpr size_t kStaticScratchBytes = kAttnCtrBytes + ((size_t)4 << 20);
 hipError_t launch_sparse_attn_static(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
                                      const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,

@@ -909,7 +909,7 @@ hipError_t launch_sparse_attn_parts(const CacheView& c, const uint16_t* q, const
                                     uint32_t* ctr, float* part, hipStream_t s, hipEvent_t ev0,
                                     hipEvent_t ev1) {
     if (nq == 0) return hipSuccess;
-    if (nq >= kManyQueries) {  // enough queries to fill the GPU one workgroup each
+    if (nq >= kManyQueries) {  // one workgroup per query (see kManyQueries)
         const bool few = nq < 256;  // fewer queries than CUs
         if (c.fp4 == 2 && few)
             hipExtLaunchKernelGGL((k_attn_loop<1, kLWFew>), dim3((uint32_t)nq), dim3(kLWFew * 64), 0, s, ev0, ev1, 0, c, q,

@@ -200,9 +200,9 @@ def test_sparse_attn_on_oracle_selection(kv, window, lo, cap):
 @pytest.mark.parametrize("kv,window,lo,cap,nq", [
     ("fp4", 40, 0, 64, 300), ("bf16", 40, 0, 64, 300), ("fp4", 0, 0, 64, 300),
     ("fp4", 64, 4090, 64, 300),
-    ("fp4", 40, 0, 64, 64), ("fp4", 40, 0, 64, 63)])  # both sides of the layout switch
+    ("fp4", 40, 0, 64, 16), ("fp4", 40, 0, 64, 15), ("fp4", 128, 0, 256, 48)])  # around the layout switch
 def test_sparse_attn_many_queries(kv, window, lo, cap, nq):
-    """From 64 queries on, one workgroup per query (the prefill layout), below
+    """From 16 queries on, one workgroup per query (the prefill layout), below
     it split workgroups; k = 96 puts the selection/window boundary inside a
     32-entry tile."""
     rng = np.random.default_rng(77)
@@ -297,6 +297,23 @@ def test_stack_small_ragged_and_deterministic():
         assert torch.equal(outs[l].view(torch.int16), outs2[l].view(torch.int16))
         assert torch.equal(sels[l], sels2[l])
     assert torch.equal(pool, pool2)
+
+
+def test_stack_batch_of_24_runs_one_workgroup_per_query():
+    """24 sequences: the stack's attention takes the one-workgroup-per-query
+    form (no split, no partials), the selection kernels their few-row forms."""
+    rng = np.random.default_rng(43)
+    n = 24
+    q_pos = [int(v) for v in rng.integers(200, 3001, n)]
+    q_pos[0] = 3000
+    sp = synth.Spec("stack-b24", n_seq=n, t_cap=3001, q_pos=q_pos, q_seq=list(range(n)),
+                    kv_format="fp4", k=256, window=64, pool=512,
+                    schedule=synth.repeating_schedule(6), local_cap=96, seed=47)
+    x = synth.make_inputs(sp)
+    d = DevInputs(x)
+    outs, sels, pool = run_stack(sp, x, d)
+    err = check_stack(sp, x, d, outs, sels, pool)
+    log("stack batch 24 max abs err", err)
 
 
 def test_stack_pool_not_a_multiple_of_32():

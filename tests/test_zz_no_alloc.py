@@ -57,8 +57,8 @@ def test_noalloc_matches_workspace_form_on_two_calls():
 def test_noalloc_rejects_calls_beyond_its_scratch():
     d, sel, _ = _case(2, 64, 16, 210)
     loc = d.local[0]
-    big = torch.zeros((63, 4096), dtype=torch.int32, device="cuda") - 1
-    q = torch.zeros((63, 16, 128), dtype=torch.bfloat16, device="cuda")
-    pos = torch.full((63,), 100, dtype=torch.int32, device="cuda")
+    big = torch.zeros((15, 8704), dtype=torch.int32, device="cuda") - 1  # 15 x 34 chunks > 504
+    q = torch.zeros((15, 16, 128), dtype=torch.bfloat16, device="cuda")
+    pos = torch.full((15,), 100, dtype=torch.int32, device="cuda")
     with pytest.raises(csa2.Csa2Error, match="allocation-free scratch"):
         csa2.sparse_attn_noalloc(d.cache, q, pos, None, big, loc)
