@@ -343,11 +343,11 @@ __global__ __launch_bounds__(256) void k_pf_thresh(const uint32_t* __restrict__ 
 // ---- 3. filter ---------------------------------------------------------------
 // Pre-filter granularity: a lane's four scores of one tile (one query, four
 // consecutive positions) are queued together when any of them passes, so one
-// wave-wide compaction serves four compares.
-constexpr int kPfQG = kPfQB % 4 == 0 ? 4 : 3;  // query blocks per queue write
-static_assert(kPfQB % kPfQG == 0, "query blocks come in whole queue groups");
-constexpr int kPfQueue = kPfQG * 64 + 64;  // per-wave ring: a group at most, plus < 64 left by a drain
+// wave-wide compaction (a ballot) serves four compares.
+constexpr int kPfQueue = kPfQB * 64 + 64;  // per-wave queue: one tile row's entries at most, plus < 64 left by a drain
 constexpr int kPfFiltMinWaves = kPfQB <= 4 ? 4 : (kPfQB <= 6 ? 3 : 2);  // per SIMD (VGPR budget)
+
+static_assert(kPfQ * 4 == 256 && kPfLB % 4 == 0, "the list copy takes four threads a query");
 
 struct PfFiltLds {
     uint2 buf[kPfQ][kPfLB];          // per-query candidates of this workgroup
@@ -359,15 +359,14 @@ struct PfFiltLds {
     float thf[kPfQ];
 };
 
-// Exact test of `count` queued entries from ring slot `head` (causal mask,
-// key >= thr); the scores that pass go to their query's list.
-__device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int head, int count,
+// Exact test of the first `count` queued entries (causal mask, key >= thr);
+// the scores that pass go to their query's list.
+__device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int count,
                                          int64_t q0, uint32_t* __restrict__ cnt,
                                          uint2* __restrict__ cand, int32_t cap) {
     for (int e = lane; e < count; e += 64) {
-        const int r = head + e < kPfQueue ? head + e : head + e - kPfQueue;
-        const uint4 sc = sh.qscore[wave][r];
-        const uint32_t tag = sh.qtag[wave][r];
+        const uint4 sc = sh.qscore[wave][e];
+        const uint32_t tag = sh.qtag[wave][e];
         const int ql = (int)(tag & 127u);
         const int32_t t0 = (int32_t)(tag >> 7);
         const int32_t lim = sh.pos[ql];
@@ -380,21 +379,22 @@ __device__ __forceinline__ void pf_drain(PfFiltLds& sh, int wave, int lane, int 
 #pragma unroll
         for (int r = 0; r < 4; ++r) okm |= (uint32_t)(t0 + r <= lim && v[r] >= thf) << r;
         if (okm == 0u) continue;
-        // one list reservation for all of the entry's passing positions
-        const int slot0 = atomicAdd(&sh.n[ql], __popc(okm));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (!((okm >> r) & 1u)) continue;
-            const int slot = slot0 + __popc(okm & ((1u << r) - 1u));
-            const int32_t tt = t0 + r;
-            const uint32_t key = score_key(v[r]);
+        // one list reservation for all of the entry's passing positions, then
+        // one pass per passing position (most entries have one)
+        int slot = atomicAdd(&sh.n[ql], __popc(okm));
+        do {
+            const int r = __builtin_ctz(okm);
+            okm &= okm - 1u;
+            const float vr = r == 0 ? v[0] : (r == 1 ? v[1] : (r == 2 ? v[2] : v[3]));
+            const uint2 ent = make_uint2((uint32_t)(t0 + r), score_key(vr));
             if (slot < kPfLB) {
-                sh.buf[ql][slot] = make_uint2((uint32_t)tt, key);
+                sh.buf[ql][slot] = ent;
             } else {  // this workgroup's list of the query is full: straight to its global list
                 const uint32_t gs = atomicAdd(&cnt[q0 + ql], 1u);
-                if (gs < (uint32_t)cap) cand[(q0 + ql) * cap + gs] = make_uint2((uint32_t)tt, key);
+                if (gs < (uint32_t)cap) cand[(q0 + ql) * cap + gs] = ent;
             }
-        }
+            ++slot;
+        } while (okm != 0u);
     }
 }
 
@@ -439,9 +439,9 @@ __global__ __launch_bounds__(256, kPfFiltMinWaves) void k_pf_filter(const uint16
     // flush), computing only the steps that hold a position <= tmax.
     constexpr int kSegSteps = kPfFiltSeg / 256;
     const int nsteps = min(kPfFiltSpan / 256, (min(tmax, t_cap - 1) - span0) / 256 + 1);
-    // the wave's queue is a ring: qh its first entry, qn its entries
-    // (wave-uniform); drains take whole batches of 64, one entry a lane
-    int qh = 0, qn = 0;
+    // the wave's queue holds qn entries from slot 0 (wave-uniform); drains
+    // take whole batches of 64, one entry a lane, and move the rest to the front
+    int qn = 0;
     pf_bf16x8 kn[4][2];
     pf_load_k(kseq, t_cap, span0 + wave * 64, n16, g, kn);
     for (int s = 0; s < nsteps; ++s) {
@@ -461,49 +461,45 @@ __global__ __launch_bounds__(256, kPfFiltMinWaves) void k_pf_filter(const uint16
                 for (int i = 0; i < kPfQB; ++i) c[i] = pf_tile(kf[j], qf[i]);
                 const uint32_t tag = (((uint32_t)t0 + 16u * j + 4u * g) << 7) | (uint32_t)n16;
                 // float pre-filter (passes every finite key >= thr: the largest
-                // of the four scores against the threshold's float): one bit
-                // per query block, then one wave scan places the lane's
-                // passing tiles in the queue
-                uint32_t bits = 0u;
+                // of the four scores against the threshold's float), one query
+                // block at a time: a ballot of the passing lanes, and each
+                // passing lane's queue slot is qn + the number of passing
+                // lanes below it (qn < 64 before the first block, so every
+                // slot is below kPfQueue)
 #pragma unroll
                 for (int i = 0; i < kPfQB; ++i) {
                     // max3 chains from a canonical value (no canonicalising
                     // of the MFMA results)
                     float mx = fmaxf(fmaxf(-__builtin_inff(), c[i][0]), c[i][1]);
                     mx = fmaxf(fmaxf(mx, c[i][2]), c[i][3]);
-                    bits |= (uint32_t)(mx >= th[i]) << i;
-                }
-                // the blocks enter the queue kPfQG at a time, each group
-                // followed by the drain of whole batches
-#pragma unroll
-                for (int h = 0; h < kPfQB / kPfQG; ++h) {
-                    const uint32_t hb = (bits >> (kPfQG * h)) & ((1u << kPfQG) - 1u);
-                    const int mine = __popc(hb);
-                    const int incl = wave_scan_dpp(mine);
-                    const int tot = __builtin_amdgcn_readlane(incl, 63);
-                    if (tot) {  // wave-uniform
-                        // qh + qn + incl < 2 kPfQueue: one wrap at most
-                        int off = qh + qn + incl - mine;
-#pragma unroll
-                        for (int i = kPfQG * h; i < kPfQG * (h + 1); ++i) {
-                            if ((bits >> i) & 1u) {
-                                const int r = off < kPfQueue ? off : off - kPfQueue;
-                                sh.qscore[wave][r] =
-                                    make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
-                                               __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
-                                sh.qtag[wave][r] = tag + 16u * i;
-                                ++off;
-                            }
+                    const bool pass = mx >= th[i];
+                    const uint64_t pm = __ballot(pass);
+                    if (pm != 0ull) {  // wave-uniform
+                        if (pass) {
+                            const int below = (int)__builtin_amdgcn_mbcnt_hi(
+                                (uint32_t)(pm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)pm, 0u));
+                            const int r = qn + below;
+                            sh.qscore[wave][r] =
+                                make_uint4(__float_as_uint(c[i][0]), __float_as_uint(c[i][1]),
+                                           __float_as_uint(c[i][2]), __float_as_uint(c[i][3]));
+                            sh.qtag[wave][r] = tag + 16u * i;
                         }
-                        qn += tot;
+                        qn += (int)__popcll(pm);
                     }
-                    if (qn >= 64) {  // whole batches; fewer than 64 entries stay, so
-                                     // the next group's (at most kPfQG * 64) still fit
-                        const int nb = qn & ~63;
-                        pf_drain(sh, wave, lane, qh, nb, q0, cnt, cand, cap);
-                        qh += nb;
-                        if (qh >= kPfQueue) qh -= kPfQueue;
-                        qn -= nb;
+                }
+                if (qn >= 64) {  // whole batches; fewer than 64 entries stay, so
+                                 // the next tile row's (at most kPfQB * 64) still fit
+                    const int nb = qn & ~63;
+                    pf_drain(sh, wave, lane, nb, q0, cnt, cand, cap);
+                    qn -= nb;
+                    // the rest to the front: lane l reads slot nb + l and
+                    // writes slot l, which only lane l read in the drain (the
+                    // wave's LDS accesses complete in order)
+                    if (lane < qn) {
+                        const uint4 a = sh.qscore[wave][nb + lane];
+                        const uint32_t tg = sh.qtag[wave][nb + lane];
+                        sh.qscore[wave][lane] = a;
+                        sh.qtag[wave][lane] = tg;
                     }
                 }
             }
@@ -511,20 +507,28 @@ __global__ __launch_bounds__(256, kPfFiltMinWaves) void k_pf_filter(const uint16
         if (s % kSegSteps == kSegSteps - 1 || s == nsteps - 1) {  // uniform: flush the lists
             // the barriers order LDS only (lds_barrier): the next step's key
             // fragments stay in flight, and the list stores to global memory
-            // need no order within the launch
-            pf_drain(sh, wave, lane, qh, qn, q0, cnt, cand, cap);
-            qh = 0;
-            qn = 0;
+            // need no order within the launch.  Queued entries wait for the
+            // next segment's lists, except at the end of the span.
+            if (s == nsteps - 1) {
+                pf_drain(sh, wave, lane, qn, q0, cnt, cand, cap);
+                qn = 0;
+            }
             lds_barrier();
             if (tid < kPfQ) {
                 const int m = min(sh.n[tid], kPfLB);
-                sh.base[tid] = m > 0 ? (int)atomicAdd(&cnt[q0 + tid], (uint32_t)m) : 0;
+                // the tile's counters through a uniform base (scalar registers)
+                uint32_t* cq = cnt + __builtin_amdgcn_readfirstlane((int)q0);
+                sh.base[tid] = m > 0 ? (int)atomicAdd(cq + tid, (uint32_t)m) : 0;
             }
             lds_barrier();
-            for (int e = tid; e < kPfQ * kPfLB; e += 256) {
-                const int ql = e / kPfLB, j = e % kPfLB;
-                if (j < min(sh.n[ql], kPfLB) && sh.base[ql] + j < cap)
-                    cand[(q0 + ql) * cap + sh.base[ql] + j] = sh.buf[ql][j];
+            {  // four threads a query, slots tid % 4 + 4 u
+                const int ql = tid >> 2;
+                const int m = min(sh.n[ql], kPfLB), b = sh.base[ql];
+#pragma unroll
+                for (int u = 0; u < kPfLB / 4; ++u) {
+                    const int j = (tid & 3) + 4 * u;
+                    if (j < m && b + j < cap) cand[(q0 + ql) * cap + b + j] = sh.buf[ql][j];
+                }
             }
             lds_barrier();
             if (tid < kPfQ) sh.n[tid] = 0;
