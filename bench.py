@@ -368,8 +368,8 @@ class DecodeSetup:
         sp = self.sp
         csa2.stack_run(self.caches[i % len(self.caches)], sp.schedule, self.q_pos, self.q,
                        self.q_idx, self.local, sp.k, sp.pool, sp.block, want_sel=False,
-                       ws=self.ws, out=self.out, scan_events=scan_ev, attn_events=attn_ev,
-                       append=self.app)
+                       want_pool=False, ws=self.ws, out=self.out, scan_events=scan_ev,
+                       attn_events=attn_ev, append=self.app)
 
 
 def time_decode(setup, steps, warmup, kernel_events=True, graph=False):

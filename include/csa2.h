@@ -330,7 +330,7 @@ typedef struct {
     const int32_t *q_pos;              /* device int32 [n_seq] */
     int32_t k;                         /* selected global entries per layer */
     int32_t pool;                      /* pool size in positions (0: no Reindex layers) */
-    int32_t block;                     /* 1: tokenwise Full scoring; >1 blockwise */
+    int32_t block;                     /* 1: tokenwise Full scoring; 64: blockwise */
     float sm_scale;
     const uint16_t *const *q;          /* [l] -> bf16 [n_seq][16][128] */
     const uint16_t *const *q_idx;      /* [l] -> bf16 [n_seq][64]; unused (may be NULL) for Reuse */
@@ -369,8 +369,10 @@ typedef struct {
  * only before reusing it for a stack with a different n_seq above 64. */
 csa2_status csa2_stack_workspace(const csa2_stack_desc *desc, size_t *bytes);
 /* Run every layer in order on `stream`.  Validates the schedule: layer 0 must
- * be Full and Reindex needs pool > 0; k <= pool when pool > 0; with block > 1,
- * pool > 0 and pool % block == 0. */
+ * be Full and Reindex needs pool > 0; k <= pool when pool > 0; block is 1 or
+ * 64, and with 64, pool > 0 and pool % 64 == 0.  With block 64 and a pool of
+ * at most 16384 positions, pool_out is written only when given (the layers
+ * score the pool from its block ids). */
 csa2_status csa2_stack_run(const csa2_stack_desc *desc, void *ws, size_t ws_bytes, void *stream);
 
 /* A stack plan records what csa2_stack_run would enqueue, once, into a HIP

@@ -451,10 +451,11 @@ def stack_run(cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
               local: Sequence[Local], k: int, pool: int = 0, block: int = 1,
               sm_scale: float = HEAD_DIM ** -0.5, want_sel: bool = True,
               ws: Optional[torch.Tensor] = None, out: Optional[Sequence[torch.Tensor]] = None,
-              scan_events=None, append=None, attn_events=None):
+              scan_events=None, append=None, attn_events=None, want_pool: bool = True):
     """Run a decoder stack (one decode query per sequence).
 
-    Returns (out list of bf16 [n_seq][16][128], sel list or None, pool or None).
+    Returns (out list of bf16 [n_seq][16][128], sel list or None, pool or None;
+    the pool only with ``want_pool`` and pool > 0).
     ``scan_events``: optional pair of ``torch.cuda.Event(enable_timing=True)``
     recorded around layer 0's indexer scan; ``attn_events``: optional list of
     2 * n_layers such events (or None to skip a layer), receiving the start
@@ -468,7 +469,7 @@ def stack_run(cache: Cache, modes: Sequence[int], q_pos: torch.Tensor,
     if out is None:
         out = [torch.empty((S, HEADS, HEAD_DIM), dtype=torch.bfloat16, device=dev) for _ in modes]
     sel = [torch.empty((S, k), dtype=torch.int32, device=dev) for _ in modes] if want_sel else None
-    pool_out = torch.empty((S, pool), dtype=torch.int32, device=dev) if pool > 0 else None
+    pool_out = torch.empty((S, pool), dtype=torch.int32, device=dev) if pool > 0 and want_pool else None
     ev = None
     if scan_events is not None:
         ev = tuple(ctypes.c_void_p(e.cuda_event) for e in scan_events)

@@ -606,8 +606,17 @@ static csa2_status enqueue_stack(const StackJob& j, const CacheView& cv, const S
     int32_t* q_seq = replay ? reinterpret_cast<int32_t*>(base + W.qseq) : nullptr;
     const int32_t S = j.nq, k = j.k, P = j.pool, B = j.block;
     const bool fused_full = replay && replay_fused_full(cv.t_cap, k, P, B);
+    // A blockwise pool of power-of-two blocks that one scoring launch takes is
+    // rescored from its block ids (each candidate's position computed where it
+    // is read); the position list is written only for a caller's pool_out.
+    int32_t bshift = 0;
+    while (B > 1 && (1 << bshift) < B) ++bshift;
+    const bool block_pool = B > 1 && (1 << bshift) == B && P <= kFusedSelectMax;
     // score the pool with layer l's indexer query and keep the top k
     auto rescore_pool = [&](int32_t l, int32_t* dst) -> hipError_t {
+        if (block_pool)
+            return launch_score_select(cv, j.q_idx[l], j.q_pos, q_seq, S, blocks, P, pscores, ctr,
+                                       k, dst, s, bshift);
         if (P <= kFusedSelectMax)
             return launch_score_select(cv, j.q_idx[l], j.q_pos, q_seq, S, pool, P, pscores, ctr,
                                        k, dst, s);
@@ -674,7 +683,7 @@ static csa2_status enqueue_stack(const StackJob& j, const CacheView& cv, const S
                 if (around && e == hipSuccess) e = hipEventRecord((hipEvent_t)j.scan_events[1], s);
                 if (e == hipSuccess)
                     e = launch_topk(bscores, S, nb, nb, nullptr, nbsel, blocks, 0, nullptr, tkws, s);
-                if (e == hipSuccess)
+                if (e == hipSuccess && (!block_pool || j.pool_out))
                     e = launch_expand_blocks(blocks, S, nbsel, B, j.q_pos, pool, s, cv.msh);
                 if (e == hipSuccess) e = rescore_pool(l, dst);
             } else {

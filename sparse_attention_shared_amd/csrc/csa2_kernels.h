@@ -102,7 +102,9 @@ hipError_t launch_prefill_topk(const CacheView& c, int32_t seq, const uint16_t* 
                                const int32_t* q_pos, int32_t nq, int32_t k, int32_t* sel, void* ws,
                                hipStream_t s);
 
-// Candidate scores + top-k among them (n_cand <= 16384); `scores` holds nq
+// Candidate scores + top-k among them (n_cand <= 16384); with block_shift
+// b > 0, `cand` holds n_cand >> b block ids per query and candidate c is
+// position cand[c >> b] * 2^b + c % 2^b (n_cand a multiple of 2^b); `scores` holds nq
 // rows of score_select_ld(n_cand) floats (whole 128-byte lines per row, so no
 // line is written by two workgroups); `ctr` holds nq counters kCtrStride words
 // apart that must be zero and are left zero.
@@ -110,7 +112,7 @@ __host__ __device__ inline int64_t score_select_ld(int64_t n_cand) { return (n_c
 hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
                                const int32_t* q_seq, int32_t nq, const int32_t* cand,
                                int64_t n_cand, float* scores, uint32_t* ctr, int32_t k,
-                               int32_t* sel, hipStream_t s);
+                               int32_t* sel, hipStream_t s, int32_t block_shift = 0);
 constexpr int64_t kFusedSelectMax = 16384;
 
 size_t topk_ws_bytes(int32_t nq, int64_t n, int32_t k, int32_t k2);

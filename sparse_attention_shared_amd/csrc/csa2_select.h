@@ -532,7 +532,8 @@ struct WaveSelShared {
 };
 
 // Top-kk of one row of n <= NT * PER scores by one workgroup, keys in
-// registers, slot i written as ids[i].  Wave w owns slots [64 PER w,
+// registers, slot i written as ids[i] (bs > 0: as the position of slot i
+// within block ids[i >> bs] of 2^bs positions).  Wave w owns slots [64 PER w,
 // 64 PER (w + 1)); lane l holds slots 64 PER w + 64 j + l, so every wave has
 // keys when n is near NT * PER and a wave's slots ascend in (j, l).  Scores of
 // slots that can never be chosen must be -inf (key 0).
@@ -547,7 +548,7 @@ struct WaveSelShared {
 // agent-coherent stores (read with load_coherent).
 template <int NT, int PER, bool COH = false>
 __device__ __forceinline__ void wave_select(const float* s, const int32_t* ids, int n, int kk, int32_t* dst,
-                            WaveSelShared<NT>& sh) {
+                            WaveSelShared<NT>& sh, int bs = 0) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int s0 = w * 64 * PER + lane;
@@ -556,8 +557,14 @@ __device__ __forceinline__ void wave_select(const float* s, const int32_t* ids, 
 #pragma unroll
     for (int j = 0; j < PER; ++j)
         v[j] = COH ? load_coherent(&s[min(s0 + 64 * j, n - 1)]) : s[min(s0 + 64 * j, n - 1)];
+    // bs > 0: ids holds one block id per 2^bs slots, slot i being position
+    // ids[i >> bs] * 2^bs + i % 2^bs (only slots with a finite score are
+    // ever written, so an empty block's slots need no check here)
 #pragma unroll
-    for (int j = 0; j < PER; ++j) id[j] = ids[min(s0 + 64 * j, n - 1)];
+    for (int j = 0; j < PER; ++j) {
+        const int sl = min(s0 + 64 * j, n - 1);
+        id[j] = bs ? ids[sl >> bs] * (1 << bs) + (sl & ((1 << bs) - 1)) : ids[sl];
+    }
     for (int i = tid; i < kHistWords; i += NT) sh.hist[i] = 0;
     uint32_t key[PER];
 #pragma unroll

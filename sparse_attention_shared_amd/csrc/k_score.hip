@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
                                                          const int32_t* __restrict__ cand,
                                                          int64_t n_cand, float* __restrict__ scores,
                                                          uint32_t* __restrict__ ctr, int32_t k,
-                                                         int32_t* __restrict__ sel) {
+                                                         int32_t* __restrict__ sel, int32_t bs) {
     __shared__ WaveSelShared<kSelNT> sh;
     __shared__ int last;
     const int qi = blockIdx.y;
@@ -242,7 +242,9 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
     const int sub = lane & 7, grp = lane >> 3;
     const int64_t base = (int64_t)blockIdx.x * sel_keys<R>() + wave * 8 * R;
     float* srow = scores + (int64_t)qi * score_select_ld(n_cand);
-    const int32_t* crow = cand + (int64_t)qi * n_cand;
+    // bs > 0: cand holds n_cand >> bs block ids per query, candidate c being
+    // position cand[c >> bs] * 2^bs + c % 2^bs (-1 for an empty block)
+    const int32_t* crow = cand + (int64_t)qi * (n_cand >> bs);
     const int32_t seq = q_seq ? q_seq[qi] : qi;
     // the last entry the query may read: entries of 2^msh positions count
     // once their whole group is at or before the query's position
@@ -259,7 +261,11 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int64_t c = base + r * 8 + grp;
-            const int64_t tok = (c < n_cand) ? crow[c] : -1;
+            int64_t tok = -1;
+            if (c < n_cand) {
+                const int32_t id = crow[c >> bs];
+                tok = bs ? (id >= 0 ? (int64_t)id * (1 << bs) + (c & ((1 << bs) - 1)) : -1) : id;
+            }
             ok[r] = tok >= 0 && tok <= t;
             kv[r] = ok[r] ? kb[tok * 8 + sub] : make_uint4(0, 0, 0, 0);
         }
@@ -284,31 +290,33 @@ __global__ __launch_bounds__(kSelNT) void k_score_select(const uint16_t* __restr
         if (!last) return;
     }
     if (n_cand <= kSelNT * 8)  // every wave holds keys
-        wave_select<kSelNT, 8, MODE == 0>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
+        wave_select<kSelNT, 8, MODE == 0>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh, bs);
     else
-        wave_select<kSelNT, kSelMaxCand / kSelNT, MODE == 0>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh);
+        wave_select<kSelNT, kSelMaxCand / kSelNT, MODE == 0>(srow, crow, (int)n_cand, k, sel + (int64_t)qi * k, sh,
+                                                            bs);
     if (MODE == 0 && threadIdx.x == 0) ctr[qi * kCtrStride] = 0u;
 }
 
 hipError_t launch_score_select(const CacheView& c, const uint16_t* q_idx, const int32_t* q_pos,
                                const int32_t* q_seq, int32_t nq, const int32_t* cand,
                                int64_t n_cand, float* scores, uint32_t* ctr, int32_t k,
-                               int32_t* sel, hipStream_t s) {
+                               int32_t* sel, hipStream_t s, int32_t block_shift) {
     if (nq == 0 || n_cand == 0) return hipSuccess;
     if (n_cand > kSelMaxCand) return hipErrorInvalidValue;
+    if (block_shift < 0 || block_shift > 16 || (n_cand & ((1 << block_shift) - 1))) return hipErrorInvalidValue;
     const int64_t wide = (n_cand + sel_keys<8>() - 1) / sel_keys<8>();
     if (wide * nq >= 256) {  // the queries fill the GPU
         hipLaunchKernelGGL((k_score_select<8, 1>), dim3((uint32_t)wide, (uint32_t)nq), dim3(kSelNT), 0, s,
                            c.k_idx, c.n_seq, c.t_cap, c.msh, q_idx, q_pos, q_seq, cand, n_cand,
-                           scores, ctr, k, sel);
+                           scores, ctr, k, sel, block_shift);
         hipLaunchKernelGGL((k_score_select<8, 2>), dim3(1u, (uint32_t)nq), dim3(kSelNT), 0, s,
                            c.k_idx, c.n_seq, c.t_cap, c.msh, q_idx, q_pos, q_seq, cand, n_cand,
-                           scores, ctr, k, sel);
+                           scores, ctr, k, sel, block_shift);
     } else {
         const int64_t nb = (n_cand + sel_keys<2>() - 1) / sel_keys<2>();
         hipLaunchKernelGGL((k_score_select<2, 0>), dim3((uint32_t)nb, (uint32_t)nq), dim3(kSelNT), 0, s,
                            c.k_idx, c.n_seq, c.t_cap, c.msh, q_idx, q_pos, q_seq, cand, n_cand,
-                           scores, ctr, k, sel);
+                           scores, ctr, k, sel, block_shift);
     }
     return hipGetLastError();
 }

@@ -335,6 +335,8 @@ def test_stack_pool_not_a_multiple_of_32():
 
 
 def test_stack_blockwise_small():
+    """Blocks of 64 positions: the pool is rescored from its block ids, and
+    the position list written only for a caller's pool output."""
     sp = synth.Spec("blockwise-small", n_seq=2, t_cap=20000, q_pos=[19999, 12345], q_seq=[0, 1],
                     kv_format="fp4", k=128, window=16, pool=32 * 64, block=64,
                     schedule=[synth.FULL, synth.REINDEX, synth.REUSE], local_cap=16,
@@ -343,6 +345,15 @@ def test_stack_blockwise_small():
     d = DevInputs(x)
     outs, sels, pool = run_stack(sp, x, d)
     check_stack(sp, x, d, outs, sels, pool)
+    # without the pool output: the same selections and outputs, bit for bit
+    outs2, sels2, pool2 = csa2.stack_run(d.cache, list(sp.schedule), d.q_pos, d.q,
+                                         [d.q_idx[l] if sp.schedule[l] != synth.REUSE else None
+                                          for l in range(sp.n_layers)],
+                                         d.local, sp.k, sp.pool, sp.block, want_pool=False)
+    assert pool2 is None
+    for l in range(sp.n_layers):
+        assert torch.equal(sels[l], sels2[l]), "layer %d selection" % l
+        assert torch.equal(outs[l].view(torch.int16), outs2[l].view(torch.int16)), "layer %d" % l
 
 
 def test_page_schedule_small():
