@@ -347,7 +347,8 @@ __global__ __launch_bounds__(256) void k_pf_thresh(const uint32_t* __restrict__ 
 constexpr int kPfQueue = kPfQB * 64 + 64;  // per-wave queue: one tile row's entries at most, plus < 64 left by a drain
 constexpr int kPfFiltMinWaves = kPfQB <= 4 ? 4 : (kPfQB <= 6 ? 3 : 2);  // per SIMD (VGPR budget)
 
-static_assert(kPfQ * 4 == 256 && kPfLB % 4 == 0, "the list copy takes four threads a query");
+constexpr int kPfCopyT = 256 / kPfQ;  // threads copying one query's list at a flush
+static_assert(kPfCopyT * kPfQ == 256 && kPfLB % kPfCopyT == 0, "the list copy splits evenly");
 
 struct PfFiltLds {
     uint2 buf[kPfQ][kPfLB];          // per-query candidates of this workgroup
@@ -521,12 +522,12 @@ __global__ __launch_bounds__(256, kPfFiltMinWaves) void k_pf_filter(const uint16
                 sh.base[tid] = m > 0 ? (int)atomicAdd(cq + tid, (uint32_t)m) : 0;
             }
             lds_barrier();
-            {  // four threads a query, slots tid % 4 + 4 u
-                const int ql = tid >> 2;
+            {  // kPfCopyT threads a query, slots tid % kPfCopyT + kPfCopyT u
+                const int ql = tid / kPfCopyT;
                 const int m = min(sh.n[ql], kPfLB), b = sh.base[ql];
 #pragma unroll
-                for (int u = 0; u < kPfLB / 4; ++u) {
-                    const int j = (tid & 3) + 4 * u;
+                for (int u = 0; u < kPfLB / kPfCopyT; ++u) {
+                    const int j = tid % kPfCopyT + kPfCopyT * u;
                     if (j < m && b + j < cap) cand[(q0 + ql) * cap + b + j] = sh.buf[ql][j];
                 }
             }
