@@ -137,6 +137,25 @@ def test_topk_bit_exact_on_identical_scores(n, k, k2):
     del ids
 
 
+def test_topk_one_workgroup_rows_of_32768():
+    """64 rows of 32768 slots fill a quarter of the GPU with chunk
+    workgroups, so each row takes one workgroup (32 slots a thread); 3 such
+    rows take the chunked path (the case above).  Ties, -inf, -0."""
+    n, nq, k, k2 = 32768, 64, 2048, 4096
+    rng = np.random.default_rng(4242)
+    s = (rng.integers(-40, 41, size=(nq, n)) * 0.25).astype(np.float32)
+    s[rng.random((nq, n)) < 0.05] = -0.0
+    s[::3] = (rng.standard_normal((len(range(0, nq, 3)), n)) * 8).astype(np.float32)
+    s[1::5, : n // 2] = -np.inf
+    g, g2 = csa2.topk(torch.from_numpy(s).cuda(), k, k2=k2)
+    g, g2 = host(g), host(g2)
+    for i in range(nq):
+        sv = np.where(np.isneginf(s[i]), np.float32(0), s[i])
+        ids_i = np.where(np.isneginf(s[i]), -1, np.arange(n)).astype(np.int32)
+        assert np.array_equal(g[i], oracle.topk(sv, k, ids_i)), i
+        assert np.array_equal(g2[i], oracle.topk(sv, k2, ids_i)), i
+
+
 @pytest.mark.parametrize("k,k2", [(200, 0), (700, 1000)])
 def test_topk_one_workgroup_sampled_floor(k, k2):
     """Rows of 16384 slots with k < n / 16 take the sampled floor (a 1/8
