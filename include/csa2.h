@@ -251,10 +251,8 @@ csa2_status csa2_prefill_topk(const csa2_cache *cache, int32_t seq, const uint16
  * padded with -1 when fewer than k can be chosen.  When out2 != NULL the
  * first k2 >= k under the same order are also written to out2 [nq][k2]
  * (the Full layer's candidate pool, Fig. 5).  n <= 2^24.  ws: at least the
- * size returned by csa2_topk_workspace (may be 0: rows of at most 16384
- * slots, or of at most 32768 when nq * ceil(n / 8192) >= 256, take one
- * workgroup each and no workspace).  Rows taking the chunked path keep
- * per-row counters in fixed records at the start of ws (max(nq, 64)
+ * size returned by csa2_topk_workspace (may be 0).  Rows longer than 32768
+ * slots keep per-row counters in fixed records at the start of ws (max(nq, 64)
  * of them, addressed by row index only) that every call leaves zero, so a
  * workspace zero-filled once serves any later calls with nq <= 64 (any n, k,
  * k2), or with the same nq; zero-fill it again before a call with a

@@ -425,20 +425,8 @@ static size_t row_state_bytes(int32_t nq) {
     return (size_t)std::max(nq, kMinRowStates) * sizeof(RowState);
 }
 
-// Whether rows of n slots take the multi-workgroup path.  Beyond kSmallMax
-// they must; from 16 slots a thread (n > 16 kSmallNT) up to kSmallMax the
-// one-workgroup form takes a CU per row for ~20 us, so while the rows leave
-// most of the GPU idle (under 256 chunk workgroups) the chunked path is
-// faster (a decode step at T = 32768, k = 2048, per step: 4 rows -7.1 us,
-// 8: -6.9, 16: -6.6, 32: -1.5, 64 rows +4.3 us; rows of 16384 with the
-// sampled floor stay faster on one workgroup: +8 us chunked).
-static bool topk_long(int32_t nq, int64_t n) {
-    if (n > kSmallMax) return true;
-    return n > 16 * kSmallNT && (int64_t)long_chunks(n) * nq < 256;
-}
-
 size_t topk_ws_bytes(int32_t nq, int64_t n, int32_t, int32_t) {
-    if (!topk_long(nq, n)) return 0;
+    if (n <= kSmallMax) return 0;
     const size_t nc = (size_t)long_chunks(n);
     return row_state_bytes(nq) + (size_t)nq * (nc * kChunk * sizeof(Cand) + nc * sizeof(int32_t)) + 256;
 }
@@ -446,7 +434,7 @@ size_t topk_ws_bytes(int32_t nq, int64_t n, int32_t, int32_t) {
 hipError_t launch_topk(const float* scores, int32_t nq, int64_t n, int64_t ld, const int32_t* ids,
                        int32_t k, int32_t* out, int32_t k2, int32_t* out2, void* ws, hipStream_t s) {
     if (nq == 0) return hipSuccess;
-    if (!topk_long(nq, n)) {
+    if (n <= kSmallMax) {
         const dim3 g((uint32_t)nq), b(kSmallNT);
         if (n <= 16 * kSmallNT) {
             if (ids) hipLaunchKernelGGL((k_topk_small<true, 16>), g, b, 0, s, scores, n, ld, ids, k, out, k2, out2);

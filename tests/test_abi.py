@@ -165,18 +165,15 @@ def test_prefill_validation():
 
 
 def test_topk_workspace_rule():
-    """Rows of at most 16384 slots take one workgroup each (no workspace);
-    rows of up to 32768 do too once nq * ceil(n / 8192) reaches 256, and fewer
-    of them take the chunked path, which needs a workspace; longer rows always
-    do."""
+    """Rows of at most 32768 slots take one workgroup each (no workspace);
+    longer rows take the chunked path, which needs one."""
     L = csa2.lib()
     n = _lib._sz()
     def ws(nq, slots):
         assert L.csa2_topk_workspace(nq, slots, 256, 0, ctypes.byref(n)) == OK
         return n.value
     assert ws(1, 16384) == 0 and ws(300, 16384) == 0
-    assert ws(1, 32768) > 0 and ws(63, 32768) > 0
-    assert ws(64, 32768) == 0 and ws(500, 32768) == 0
+    assert ws(1, 32768) == 0 and ws(500, 32768) == 0
     assert ws(1, 32769) > 0 and ws(500, 40000) > 0
 
 

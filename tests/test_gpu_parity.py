@@ -138,9 +138,8 @@ def test_topk_bit_exact_on_identical_scores(n, k, k2):
 
 
 def test_topk_one_workgroup_rows_of_32768():
-    """64 rows of 32768 slots fill a quarter of the GPU with chunk
-    workgroups, so each row takes one workgroup (32 slots a thread); 3 such
-    rows take the chunked path (the case above).  Ties, -inf, -0."""
+    """64 rows of 32768 slots, one workgroup each (32 slots a thread), both
+    targets: ties, -inf, -0."""
     n, nq, k, k2 = 32768, 64, 2048, 4096
     rng = np.random.default_rng(4242)
     s = (rng.integers(-40, 41, size=(nq, n)) * 0.25).astype(np.float32)
