@@ -278,7 +278,7 @@ csa2_status csa2_expand_blocks(const int32_t *blocks, int32_t nq, int32_t nb, in
  * (fp32 accumulation, rounded to nearest even).  A query with no entry at
  * all gets zeros.  q_seq may be NULL (query i reads sequence i).  nq <= 65535.
  * ws: at least csa2_sparse_attn_workspace bytes: 0 when one workgroup covers
- * a query (k <= 256 and window <= 32, or nq >= 16, where each query gets one
+ * a query (k <= 256 and window <= 32, or nq >= 20, where each query gets one
  * workgroup of its own); otherwise a fixed 16 KiB block of per-query counters
  * (at the start, addressed by query index only, left zero by every call)
  * followed by per-chunk partials.  It must be zero-filled before its first
@@ -299,8 +299,8 @@ csa2_status csa2_sparse_attn_workspace(int32_t nq, int32_t k, int32_t window, si
  * before using them.  Same arguments, results and rules as csa2_sparse_attn
  * otherwise (bit-identical outputs).  Limit: the partials of nq queries times
  * chunks-per-query must fit 4 MiB -- nq * max(ceil(k / 256), ceil(window /
- * 32)) <= 504 when nq < 16 (e.g. 15 queries at k = 8192, window 128: 32
- * chunks each); from 16 queries on no scratch is used and any size is accepted.  Larger calls
+ * 32)) <= 504 when nq < 20 (e.g. 19 queries at k = 6656, window 128: 26
+ * chunks each); from 20 queries on no scratch is used and any size is accepted.  Larger calls
  * return CSA2_ERR_TOO_LARGE and enqueue nothing.  Every call on a GPU shares
  * its array: calls that overlap on one GPU (other streams, other host
  * threads) race and must be serialised by the caller. */

@@ -130,11 +130,11 @@ hipError_t launch_expand_blocks(const int32_t* blocks, int32_t nq, int32_t nb, i
 // split kernel holds ~105 KB of LDS (one workgroup per CU) and its last
 // chunk of each query merges the others, so its time grows with the queries
 // while the one-per-query loop stays flat until the queries fill the CUs.
-// Measured per call (k = 2048, W = 128: 8 chunks a query), split vs loop:
-// 8 queries 20.9 / 25.0 us, 16: 22.9 / 25.1, 24: 27.2 / 25.2, 48: 39.2 /
-// 25.6, 128: 71.8 / 27.1; with k = 512 (4 chunks): 8 queries 17.8 / 18.8,
-// 16: 19.1 / 18.3, 32: 21.3 / 18.2.
-constexpr int32_t kManyQueries = 16;
+// Measured per call, each build in its own process (k = 2048, W = 128: 8
+// chunks a query), split vs loop: 16 queries 22.8 / 25.6 us, 24: 25.5 /
+// 25.3, 32: 28.4 / 25.4, 48: 40.0 / 25.7, 128: 71.8 / 27.1; with k = 512 (4
+// chunks): 8 queries 17.8 / 18.8, 16: 19.1 / 18.3, 32: 21.3 / 18.2.
+constexpr int32_t kManyQueries = 20;
 // Queries a block of per-query counters covers (the split attention's, the
 // stack's Reindex select's): the blocks keep this size for any call, so a
 // workspace's layout does not depend on the number of queries up to it.
@@ -159,8 +159,8 @@ hipError_t launch_sparse_attn_parts(const CacheView& c, const uint16_t* q, const
                                     uint32_t* ctr, float* part, hipStream_t s,
                                     hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // The allocation-free form: counters and partials in a fixed device array of
-// kStaticScratchBytes (partials of up to 504 query-chunks, e.g. 15 queries of
-// 33 chunks); a larger call returns hipErrorInvalidValue.
+// kStaticScratchBytes (partials of up to 504 query-chunks, e.g. 19 queries of
+// 26 chunks); a larger call returns hipErrorInvalidValue.
 constexpr size_t kStaticScratchBytes = kAttnCtrBytes + ((size_t)4 << 20);
 hipError_t launch_sparse_attn_static(const CacheView& c, const uint16_t* q, const int32_t* q_pos,
                                      const int32_t* q_seq, int32_t nq, const int32_t* sel, int32_t k,

@@ -89,10 +89,10 @@ def test_score_topk_attn_validation():
     assert L.csa2_sparse_attn_workspace(2, 8, 32, ctypes.byref(n)) == OK and n.value == 0
     assert L.csa2_sparse_attn_workspace(2, 8, 128, ctypes.byref(n)) == OK and n.value > 0
     assert L.csa2_sparse_attn_workspace(2, 2048, 128, ctypes.byref(n)) == OK and n.value > 0
-    # from 16 queries on every query has a workgroup of its own
+    # from 20 queries on every query has a workgroup of its own
     m = _lib._sz()
-    assert L.csa2_sparse_attn_workspace(15, 2048, 128, ctypes.byref(m)) == OK and m.value > 0
-    assert L.csa2_sparse_attn_workspace(16, 2048, 128, ctypes.byref(m)) == OK and m.value == 0
+    assert L.csa2_sparse_attn_workspace(19, 2048, 128, ctypes.byref(m)) == OK and m.value > 0
+    assert L.csa2_sparse_attn_workspace(20, 2048, 128, ctypes.byref(m)) == OK and m.value == 0
     assert L.csa2_sparse_attn(bp(c), FAKE, FAKE, None, 2, FAKE, 2048, bp(loc), 0.1, FAKE, FAKE,
                               n.value - 1, None) == WORKSPACE
 
@@ -337,8 +337,8 @@ def test_compression_rate_validation():
 
 def test_noalloc_attention_limit():
     """The allocation-free attention refuses, before any device work, calls
-    whose partials exceed its fixed 4 MiB: nq * chunks <= 504 below 16
-    queries, any size from 16 queries on (no scratch is used)."""
+    whose partials exceed its fixed 4 MiB: nq * chunks <= 504 below 20
+    queries, any size from 20 queries on (no scratch is used)."""
     L = csa2.lib()
     c = _cache(n_seq=64, t_cap=5000)
     loc = _lib.csa2_local(FAKE, FAKE, 128, 128, 0)
@@ -346,8 +346,8 @@ def test_noalloc_attention_limit():
     # 15 queries x 34 chunks (k = 8704) = 510 > 504
     assert L.csa2_sparse_attn_noalloc(bp(c), FAKE, FAKE, None, 15, FAKE, 8704, bp(loc), 0.1,
                                       FAKE, None) == TOO_LARGE
-    # 15 queries x 32 chunks fits; so does any call from 16 queries on
-    for nq, k in ((15, 8192), (16, 8704), (2, 2048)):
+    # 15 queries x 32 chunks fits; so does any call from 20 queries on
+    for nq, k in ((15, 8192), (20, 8704), (2, 2048)):
         st = L.csa2_sparse_attn_noalloc(bp(c), FAKE, FAKE, None, nq, FAKE, k, bp(loc), 0.1, FAKE,
                                         None)
         assert st in (OK, NO_DEVICE) and st != TOO_LARGE

@@ -218,9 +218,9 @@ def test_sparse_attn_on_oracle_selection(kv, window, lo, cap):
 @pytest.mark.parametrize("kv,window,lo,cap,nq", [
     ("fp4", 40, 0, 64, 300), ("bf16", 40, 0, 64, 300), ("fp4", 0, 0, 64, 300),
     ("fp4", 64, 4090, 64, 300),
-    ("fp4", 40, 0, 64, 16), ("fp4", 40, 0, 64, 15), ("fp4", 128, 0, 256, 48)])  # around the layout switch
+    ("fp4", 40, 0, 64, 20), ("fp4", 40, 0, 64, 19), ("fp4", 128, 0, 256, 48)])  # around the layout switch
 def test_sparse_attn_many_queries(kv, window, lo, cap, nq):
-    """From 16 queries on, one workgroup per query (the prefill layout), below
+    """From 20 queries on, one workgroup per query (the prefill layout), below
     it split workgroups; k = 96 puts the selection/window boundary inside a
     32-entry tile."""
     rng = np.random.default_rng(77)
